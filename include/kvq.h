@@ -1,0 +1,240 @@
+/*
+ * kvq.h — C ABI of libkvq: KIVI-style asymmetric KV-cache quantization and
+ * decode attention over the quantized cache, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources the operations follow (web pages, cited by title and section):
+ *   [KIVI-page]  "4.4 KV Cache 量化：KIVI 2-bit 与 FP8 KV Cache"
+ *                (aiinfraguide.pages.dev), §2, §3.1–3.4, §5
+ *   [Tutorial]   "大模型量化从0到1（十三）：KV Cache 量化——长上下文为什么越跑越吃显存"
+ *                (aiot.csdn.net), §二 (attention), §四 (byte formula),
+ *                §五 (MHA/GQA), §八.4 (online critical path), §九 (KIVI),
+ *                §十 (affine / FP8 formulas, granularity, residual window)
+ *   [Interview]  "KV Cache 量化是什么？它如何降低长上下文推理显存？"
+ *                (offer.aigcbaba.com), §三 (byte formula), §四 (pipeline)
+ *   [FP8-page]   "LLM推理加速KV Cache量化压缩实战方案" (yunthe.com),
+ *                section "自定义KV Cache量化的实现路径" (per-tensor amax/448)
+ *
+ * The three operations of the pipeline (prefill → group statistics →
+ * low-bit write; decode → append + dequantize inside attention) are stated in
+ * [Tutorial] §八.4 and [Interview] §四; the grouped-plus-residual structure
+ * and its flush rule in [KIVI-page] §3.2.
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions (apply to every entry point)
+ * ---------------------------------------------------------------------------
+ * - Memory. The caller allocates and frees every device buffer (sizes from
+ *   kvq_layout_query / kvq_decode_workspace_bytes). The library never
+ *   allocates device memory, keeps no global state, and never synchronizes
+ *   the device. Pointers marked "device" must point to device memory of the
+ *   current HIP device; "host" pointers to host memory.
+ * - Streams. `stream` is a hipStream_t passed as void* (NULL = the default
+ *   stream). All device work is enqueued asynchronously on it, in call order.
+ * - State. The fill levels (n_quant, n_resid) live in the host-side
+ *   kvq_cache struct and are updated when the work is enqueued, so no call
+ *   waits for the device. All `batch` sequences have the same length.
+ * - Errors. Every argument and state check runs before anything is enqueued.
+ *   A call that returns an error enqueued nothing and changed nothing.
+ *   KVQ_ERR_DEVICE reports a failed HIP launch; then the cache state has
+ *   still been advanced for the launched work only if the launch succeeded.
+ *   No C++ exception or abort crosses this boundary.
+ * - Inputs. K/V values must be finite fp16; non-finite input is undefined
+ *   behaviour (not checked). Query values must be finite fp32.
+ * - Supported (else KVQ_ERR_UNSUPPORTED): head_dim = 128; KIVI group_size = 32,
+ *   bits ∈ {2, 4}, residual_length a multiple of group_size (0 allowed);
+ *   FP8 bits = 8; FP16 bits = 16; num_q_heads a positive multiple of
+ *   num_kv_heads.
+ *
+ * ---------------------------------------------------------------------------
+ * Numerics (bit-exact contract for KIVI codes, scales and zero-points)
+ * ---------------------------------------------------------------------------
+ * The affine quantizer of [Tutorial] §十 (q = clamp(round(x/s)+z, qmin, qmax),
+ * x̂ = (q−z)·s) is used in its min/max asymmetric form with the zero-point kept
+ * as an fp32 offset (the form the pages leave open; see the design notes):
+ *   mn, mx = min, max of the group in fp32 (exact from fp16)
+ *   s      = (mx − mn) / (2^bits − 1)          fp32, each op correctly rounded
+ *   z      = mn
+ *   code   = min(max(rint((x − mn) / s), 0), 2^bits − 1)   (rint = round half
+ *            to even; fp32 subtract and IEEE division), code = 0 when s == 0
+ *   x̂      = (float)code · s + z               (reconstruction)
+ * KIVI granularity ([KIVI-page] §2 and §3.2, [Tutorial] §九.1–九.3):
+ *   K — per channel: one (s, z) per (group of G tokens, channel); groups are
+ *       aligned to token index multiples of G from position 0.
+ *   V — per token: one (s, z) per token over its head_dim channels.
+ *
+ * FP8 E4M3 per-tensor path ([FP8-page], [Tutorial] §十 FP8 formula,
+ * [KIVI-page] §5 for the 1-4-3 layout):
+ *   s_K = amax(|K|) / 448 over the whole prefill K tensor, s_V likewise
+ *   (s = 0 when amax = 0: every code is then 0);
+ *   code = e4m3(min(max(x / s, −448), 448)) with round-to-nearest-even, OCP
+ *   "fn" encoding (no infinities; 0x7F/0xFF are NaN and never produced),
+ *   signed zero kept; x̂ = (float)e4m3_value(code) · s.
+ *   The scales are fixed at prefill; appended tokens reuse them and saturate.
+ *
+ * ---------------------------------------------------------------------------
+ * Device layouts (all arrays contiguous, row-major, little-endian)
+ * ---------------------------------------------------------------------------
+ * Let B = batch, H = num_kv_heads, D = head_dim, G = group_size, b = bits,
+ * C = capacity, NG = ceil(C / G) (group slots), CT = NG · G (token slots),
+ * Rcap = residual_length if > 0 else G.
+ * KIVI:
+ *   k_codes  uint32 [B][H][CT][D·b/32]   token t of (b,h): its D channel codes,
+ *            code of channel d in word d/(32/b) at bits [b·(d%(32/b)), +b).
+ *   v_codes  uint32 [B][H][NG][D][G·b/32] group g, channel d: the G token
+ *            codes of that channel, token j of the group in word j/(32/b) at
+ *            bits [b·(j%(32/b)), +b).
+ *   k_scale, k_zero  fp32 [B][H][NG][D]   (per group, per channel)
+ *   v_scale, v_zero  fp32 [B][H][CT]      (per token)
+ *   k_resid, v_resid fp16 [B][H][Rcap][D] the FP16 residual window; slot i
+ *            holds token n_quant + i.
+ * FP8 E4M3:
+ *   k_codes, v_codes uint8 [B][H][C][D];  tensor_scale fp32 [2] = {s_K, s_V}.
+ * FP16 (baseline, no quantization):
+ *   k_codes, v_codes fp16 [B][H][C][D].
+ * Decode I/O: q, out fp32 [B][Hq][D]. Query head hq reads KV head
+ *   hq / (Hq / H) (consecutive query heads share a KV head, [Tutorial] §五.3).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_ABI_VERSION 1
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad enum     */
+  KVQ_ERR_UNSUPPORTED = 2, /* valid but outside the supported set above     */
+  KVQ_ERR_CAPACITY = 3,    /* would exceed the configured capacity          */
+  KVQ_ERR_STATE = 4,       /* wrong fill state (prefill into a non-empty
+                              cache, decode on an empty cache)              */
+  KVQ_ERR_DEVICE = 5,      /* a HIP launch failed                           */
+  KVQ_ERR_WORKSPACE = 6    /* decode workspace missing or too small         */
+} kvq_status;
+
+typedef enum {
+  KVQ_FMT_FP16 = 0,     /* unquantized fp16 cache (baseline)                */
+  KVQ_FMT_FP8_E4M3 = 1, /* per-tensor FP8 E4M3, scale = amax / 448          */
+  KVQ_FMT_KIVI = 2      /* K per-channel / V per-token groups + FP16 window */
+} kvq_format;
+
+/* Cache configuration. The KIVI knobs mirror the pages' `nbits`,
+ * `q_group_size`, `residual_length` ([KIVI-page] §3.4; [Tutorial] §十六). */
+typedef struct {
+  int32_t format;          /* kvq_format                                      */
+  int32_t bits;            /* KIVI 2 or 4; FP8 8; FP16 16                     */
+  int32_t group_size;      /* KIVI: G = 32 (ignored otherwise)                */
+  int32_t residual_length; /* KIVI: R, multiple of G, 0 allowed (ignored else) */
+  int32_t batch;           /* B ≥ 1                                           */
+  int32_t num_kv_heads;    /* H ≥ 1                                           */
+  int32_t head_dim;        /* D = 128                                         */
+  int32_t capacity;        /* C ≥ 1: max tokens per sequence                  */
+} kvq_config;
+
+/* Bytes the caller must allocate for each device buffer (0 = unused). */
+typedef struct {
+  size_t k_codes, v_codes;
+  size_t k_scale, k_zero, v_scale, v_zero;
+  size_t k_resid, v_resid;
+  size_t tensor_scale;
+} kvq_layout;
+
+/* A cache: its configuration, the caller-owned device buffers, and the
+ * host-side fill state. Fill the pointers after kvq_cache_init; the library
+ * only reads them. n_quant = tokens in the grouped (encoded) region,
+ * n_resid = tokens in the FP16 residual window (always 0 for FP8/FP16). */
+typedef struct {
+  kvq_config cfg;
+  void* k_codes;       /* device */
+  void* v_codes;       /* device */
+  float* k_scale;      /* device, KIVI */
+  float* k_zero;       /* device, KIVI */
+  float* v_scale;      /* device, KIVI */
+  float* v_zero;       /* device, KIVI */
+  void* k_resid;       /* device, KIVI */
+  void* v_resid;       /* device, KIVI */
+  float* tensor_scale; /* device, FP8: {s_K, s_V} */
+  int64_t n_quant;
+  int32_t n_resid;
+  int32_t reserved;
+} kvq_cache;
+
+/* Sizes of every device buffer a cache with this configuration needs.
+ * Errors: INVALID_ARG (null / non-positive fields / bad format),
+ * UNSUPPORTED (outside the supported set). */
+kvq_status kvq_layout_query(const kvq_config* cfg, kvq_layout* out);
+
+/* Validates cfg (as kvq_layout_query), copies it into *cache, clears every
+ * pointer and sets the state to empty (n_quant = n_resid = 0). */
+kvq_status kvq_cache_init(kvq_cache* cache, const kvq_config* cfg);
+
+/* Marks the cache empty again (host state only; enqueues nothing). */
+kvq_status kvq_cache_reset(kvq_cache* cache);
+
+/* Prefill-time quantization ([Tutorial] §八.4, [Interview] §四; KIVI split
+ * into groups and residual per [KIVI-page] §3.2).
+ * k, v: device fp16 [B][H][seq_len][D]; read only; must not overlap the cache.
+ * KIVI: the first n_quant = G·max(0, min(⌊S/G⌋, ⌈(S−R)/G⌉)) tokens are
+ * quantized into groups, the remaining n_resid = S − n_quant (≤ Rcap) tokens
+ * are copied into the FP16 window. FP8: amax → scale → encode all S tokens.
+ * FP16: copy. Requires an empty cache (else STATE) and 1 ≤ seq_len ≤ C
+ * (else INVALID_ARG / CAPACITY). All buffers of the format must be set. */
+kvq_status kvq_prefill_quantize(kvq_cache* cache, const void* k, const void* v,
+                                int64_t seq_len, void* stream);
+
+/* Appends one token per (batch, KV head) ([KIVI-page] §3.1–3.2).
+ * k_new, v_new: device fp16 [B][H][D].
+ * KIVI: if the window is full (n_resid == Rcap) its Rcap tokens are first
+ * quantized into new groups at n_quant (n_quant += Rcap, n_resid = 0); then
+ * the token is stored in window slot n_resid. FP8: encoded with the frozen
+ * prefill scales (saturating). FP16: copied. CAPACITY when n_quant + n_resid
+ * == C. KIVI and FP16 may append to an empty cache; FP8 needs its prefill
+ * scales first (else STATE). */
+kvq_status kvq_append_token(kvq_cache* cache, const void* k_new,
+                            const void* v_new, void* stream);
+
+/* Workspace bytes kvq_decode_attention needs for any fill state of a cache
+ * with this configuration and num_q_heads query heads (0 on invalid input).
+ * The workspace holds split partials; its contents need no initialization. */
+size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t num_q_heads);
+
+/* One decode step of attention for a single query per head
+ * ([Tutorial] §二: softmax(q·Kᵀ/√D)·V over all n_quant + n_resid cached
+ * tokens; no mask; GQA mapping as stated above). K and V of the grouped
+ * region are dequantized inside the kernel; the window is read as fp16.
+ * q: device fp32 [B][Hq][D]; out: device fp32 [B][Hq][D] (written);
+ * workspace: device, ≥ kvq_decode_workspace_bytes(&cache->cfg, Hq).
+ * Errors: STATE on an empty cache, WORKSPACE if too small, UNSUPPORTED if
+ * Hq is not a multiple of H. */
+kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q,
+                                int32_t num_q_heads, float* out,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* Algorithmic bytes one decode step must read from the cache at its current
+ * fill state: codes, scales and zero-points of the grouped region plus the
+ * fp16 window (KIVI); codes plus the two scales (FP8); fp16 K and V (FP16).
+ * Query and output bytes are not included. −1 on invalid input. */
+int64_t kvq_decode_bytes(const kvq_cache* cache, int32_t num_q_heads);
+
+/* The pages' KV byte formula 2·L·B·S·H_kv·D·bytes_per_elem
+ * ([KIVI-page] §1; [Tutorial] §四; [Interview] §三). */
+double kvq_theoretical_bytes(int32_t num_layers, int32_t batch, int64_t seq_len,
+                             int32_t num_kv_heads, int32_t head_dim,
+                             double bytes_per_elem);
+
+/* Static description of a status code (never NULL). */
+const char* kvq_status_str(kvq_status status);
+
+/* KVQ_ABI_VERSION of the loaded library. */
+int32_t kvq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,198 @@
+"""Cache state machines (oracle side): prefill, append, flush, decode.
+
+KIVI ([KIVI-page] §3.1–3.2; [Tutorial] §九.3): the cache is a grouped region
+(whole groups of G tokens, K per channel, V per token, low-bit) followed by an
+FP16 residual window holding the newest tokens. New tokens enter the window;
+once it has accumulated R tokens they are all quantized, merged into the
+grouped region and the window is cleared.
+
+Readings (the pages leave these open):
+  * Prefill split: see kivi.prefill_split.
+  * Flush timing is lazy: the window is flushed when a token arrives and the
+    window is already full, so a full window of R tokens is attended in FP16
+    and the flush happens on the next append (decode appends, then attends,
+    [Tutorial] §二.1).
+  * R = 0: K needs a whole group before it has a scale ([KIVI-page] §3.1), so
+    the incomplete group (< G tokens) is the only FP16 part; the window then
+    holds up to G tokens.
+
+FP8 ([FP8-page]; [KIVI-page] §6.2 fixes the scale after it is measured): the
+per-tensor scales are computed from the prefill K and V and kept for appended
+tokens, which saturate at ±448.
+
+Every array is laid out as the device buffers are (see kivi.pack_k/pack_v):
+  k_codes uint32 [B][H][CT][D·b/32], v_codes uint32 [B][H][NG][D][G·b/32],
+  k_scale/k_zero fp32 [B][H][NG][D], v_scale/v_zero fp32 [B][H][CT],
+  k_resid/v_resid fp16 [B][H][Rcap][D], with NG = ceil(C/G), CT = NG·G.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import attention, fp8, kivi
+
+
+class KiviCache:
+    def __init__(self, batch, num_kv_heads, head_dim, bits, group, residual,
+                 capacity):
+        assert bits in (2, 4) and residual % group == 0
+        self.B, self.H, self.D = batch, num_kv_heads, head_dim
+        self.bits, self.G, self.R, self.C = bits, group, residual, capacity
+        self.Rcap = kivi.window_capacity(group, residual)
+        self.NG = -(-capacity // group)
+        self.CT = self.NG * group
+        B, H, D = batch, num_kv_heads, head_dim
+        self.k_codes = np.zeros((B, H, self.CT, D * bits // 32), np.uint32)
+        self.v_codes = np.zeros((B, H, self.NG, D, group * bits // 32), np.uint32)
+        self.k_scale = np.zeros((B, H, self.NG, D), np.float32)
+        self.k_zero = np.zeros((B, H, self.NG, D), np.float32)
+        self.v_scale = np.zeros((B, H, self.CT), np.float32)
+        self.v_zero = np.zeros((B, H, self.CT), np.float32)
+        self.k_resid = np.zeros((B, H, self.Rcap, D), np.float16)
+        self.v_resid = np.zeros((B, H, self.Rcap, D), np.float16)
+        self.n_quant = 0
+        self.n_resid = 0
+        self.flush_steps = []   # append indices (1-based) that flushed
+        self.n_appends = 0
+
+    @property
+    def n_tokens(self):
+        return self.n_quant + self.n_resid
+
+    def _quantize_groups(self, k, v, t0):
+        """Quantize fp16 k, v [B, H, T, D] (T a multiple of G) as the groups
+        starting at token t0 (a multiple of G)."""
+        T = k.shape[2]
+        g0 = t0 // self.G
+        for b in range(self.B):
+            for h in range(self.H):
+                kc, ks, kz = kivi.quantize_k(k[b, h], self.bits, self.G)
+                vc, vs, vz = kivi.quantize_v(v[b, h], self.bits)
+                self.k_codes[b, h, t0:t0 + T] = kivi.pack_k(kc, self.bits)
+                self.k_scale[b, h, g0:g0 + T // self.G] = ks
+                self.k_zero[b, h, g0:g0 + T // self.G] = kz
+                self.v_codes[b, h, g0:g0 + T // self.G] = kivi.pack_v(vc, self.bits, self.G)
+                self.v_scale[b, h, t0:t0 + T] = vs
+                self.v_zero[b, h, t0:t0 + T] = vz
+
+    def prefill(self, k, v):
+        k = np.asarray(k, np.float16)
+        v = np.asarray(v, np.float16)
+        S = k.shape[2]
+        assert self.n_tokens == 0 and 1 <= S <= self.C
+        nq, nr = kivi.prefill_split(S, self.G, self.R)
+        if nq:
+            self._quantize_groups(k[:, :, :nq], v[:, :, :nq], 0)
+        self.k_resid[:, :, :nr] = k[:, :, nq:]
+        self.v_resid[:, :, :nr] = v[:, :, nq:]
+        self.n_quant, self.n_resid = nq, nr
+
+    def append(self, k1, v1):
+        """k1, v1: fp16 [B, H, D]."""
+        assert self.n_tokens < self.C
+        self.n_appends += 1
+        if self.n_resid == self.Rcap:
+            self._quantize_groups(self.k_resid, self.v_resid, self.n_quant)
+            self.n_quant += self.Rcap
+            self.n_resid = 0
+            self.flush_steps.append(self.n_appends)
+        self.k_resid[:, :, self.n_resid] = np.asarray(k1, np.float16)
+        self.v_resid[:, :, self.n_resid] = np.asarray(v1, np.float16)
+        self.n_resid += 1
+
+    def dequantized(self):
+        """K̂, V̂ fp32 [B, H, n_tokens, D]: grouped region dequantized from the
+        packed buffers, then the fp16 window."""
+        nq, ng = self.n_quant, self.n_quant // self.G
+        Kh = np.empty((self.B, self.H, self.n_tokens, self.D), np.float32)
+        Vh = np.empty_like(Kh)
+        for b in range(self.B):
+            for h in range(self.H):
+                kc = kivi.unpack_k(self.k_codes[b, h, :nq], self.bits, self.D)
+                vc = kivi.unpack_v(self.v_codes[b, h, :ng], self.bits, self.G)
+                Kh[b, h, :nq] = kivi.dequantize_k(kc, self.k_scale[b, h, :ng],
+                                                  self.k_zero[b, h, :ng], self.G)
+                Vh[b, h, :nq] = kivi.dequantize_v(vc, self.v_scale[b, h, :nq],
+                                                  self.v_zero[b, h, :nq])
+        Kh[:, :, nq:] = self.k_resid[:, :, :self.n_resid].astype(np.float32)
+        Vh[:, :, nq:] = self.v_resid[:, :, :self.n_resid].astype(np.float32)
+        return Kh, Vh
+
+    def attention(self, q):
+        Kh, Vh = self.dequantized()
+        return attention.decode_attention(q, Kh, Vh)
+
+
+class Fp8Cache:
+    def __init__(self, batch, num_kv_heads, head_dim, capacity):
+        self.B, self.H, self.D, self.C = batch, num_kv_heads, head_dim, capacity
+        self.k_codes = np.zeros((batch, num_kv_heads, capacity, head_dim), np.uint8)
+        self.v_codes = np.zeros_like(self.k_codes)
+        self.tensor_scale = np.zeros(2, np.float32)
+        self.n_quant = 0
+        self.n_resid = 0
+
+    @property
+    def n_tokens(self):
+        return self.n_quant
+
+    def prefill(self, k, v):
+        k = np.asarray(k, np.float16)
+        v = np.asarray(v, np.float16)
+        S = k.shape[2]
+        assert self.n_quant == 0 and 1 <= S <= self.C
+        sk, sv = fp8.tensor_scale(k), fp8.tensor_scale(v)
+        self.tensor_scale[:] = (sk, sv)
+        self.k_codes[:, :, :S] = fp8.quantize(k, sk)
+        self.v_codes[:, :, :S] = fp8.quantize(v, sv)
+        self.n_quant = S
+
+    def append(self, k1, v1):
+        assert 0 < self.n_quant < self.C
+        t = self.n_quant
+        self.k_codes[:, :, t] = fp8.quantize(np.asarray(k1, np.float16), self.tensor_scale[0])
+        self.v_codes[:, :, t] = fp8.quantize(np.asarray(v1, np.float16), self.tensor_scale[1])
+        self.n_quant += 1
+
+    def dequantized(self):
+        n = self.n_quant
+        return (fp8.dequantize(self.k_codes[:, :, :n], self.tensor_scale[0]),
+                fp8.dequantize(self.v_codes[:, :, :n], self.tensor_scale[1]))
+
+    def attention(self, q):
+        Kh, Vh = self.dequantized()
+        return attention.decode_attention(q, Kh, Vh)
+
+
+class Fp16Cache:
+    def __init__(self, batch, num_kv_heads, head_dim, capacity):
+        self.B, self.H, self.D, self.C = batch, num_kv_heads, head_dim, capacity
+        self.k = np.zeros((batch, num_kv_heads, capacity, head_dim), np.float16)
+        self.v = np.zeros_like(self.k)
+        self.n_quant = 0
+        self.n_resid = 0
+
+    @property
+    def n_tokens(self):
+        return self.n_quant
+
+    def prefill(self, k, v):
+        S = k.shape[2]
+        assert self.n_quant == 0 and 1 <= S <= self.C
+        self.k[:, :, :S] = k
+        self.v[:, :, :S] = v
+        self.n_quant = S
+
+    def append(self, k1, v1):
+        assert self.n_quant < self.C
+        self.k[:, :, self.n_quant] = k1
+        self.v[:, :, self.n_quant] = v1
+        self.n_quant += 1
+
+    def dequantized(self):
+        n = self.n_quant
+        return (self.k[:, :, :n].astype(np.float32), self.v[:, :, :n].astype(np.float32))
+
+    def attention(self, q):
+        Kh, Vh = self.dequantized()
+        return attention.decode_attention(q, Kh, Vh)

@@ -1,0 +1,152 @@
+"""Pins of the oracle's cache state machines (prefill split, lazy flush,
+residual semantics, group locality, FP8 frozen scale)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import attention, cache, fp8, kivi
+
+D = 128
+
+
+def _kv(B, H, T, seed=0):
+    k = synth.make_k(B, H, 0, T, D, seed).numpy()
+    v = synth.make_v(B, H, 0, T, D, seed).numpy()
+    return k, v
+
+
+def test_tiny_mha_split():
+    """S = 256, G = 32, R = 128 → 4 quantized groups + 128 FP16 tokens (the
+    tiny MHA workload's statement)."""
+    k, v = _kv(1, 1, 256)
+    c = cache.KiviCache(1, 1, D, 2, 32, 128, 256)
+    c.prefill(k, v)
+    assert (c.n_quant, c.n_resid) == (128, 128)
+    assert np.array_equal(c.k_resid[0, 0], k[0, 0, 128:])
+
+
+def test_all_residual_equals_fp16_attention():
+    """R ≥ S: nothing is quantized, so KIVI attention is FP16 attention."""
+    k, v = _kv(2, 2, 100)
+    q = synth.make_q(2, 4, D).numpy()
+    ck = cache.KiviCache(2, 2, D, 2, 32, 128, 300)
+    ck.prefill(k, v)
+    cf = cache.Fp16Cache(2, 2, D, 300)
+    cf.prefill(k, v)
+    assert ck.n_quant == 0
+    assert np.array_equal(ck.attention(q), cf.attention(q))
+
+
+def test_r0_no_window_when_aligned():
+    k, v = _kv(1, 1, 96)
+    c = cache.KiviCache(1, 1, D, 2, 32, 0, 200)
+    c.prefill(k, v)
+    assert (c.n_quant, c.n_resid) == (96, 0)
+    # the window of an R = 0 cache holds the incomplete group and flushes at G
+    k2 = synth.make_k(1, 1, 96, 96 + 33, D).numpy()
+    v2 = synth.make_v(1, 1, 96, 96 + 33, D).numpy()
+    for i in range(33):
+        c.append(k2[:, :, i], v2[:, :, i])
+    assert (c.n_quant, c.n_resid) == (128, 1) and c.flush_steps == [33]
+
+
+def test_residual_changes_the_result():
+    """R = 128 keeps the newest tokens exact, R = 0 quantizes them: the two
+    caches differ exactly in those tokens."""
+    k, v = _kv(1, 1, 256)
+    c128 = cache.KiviCache(1, 1, D, 2, 32, 128, 256)
+    c0 = cache.KiviCache(1, 1, D, 2, 32, 0, 256)
+    c128.prefill(k, v)
+    c0.prefill(k, v)
+    K128, _ = c128.dequantized()
+    K0, _ = c0.dequantized()
+    assert np.array_equal(K128[..., :128, :], K0[..., :128, :])
+    assert np.array_equal(K128[..., 128:, :], k[..., 128:, :].astype(np.float32))
+    assert not np.array_equal(K0[..., 128:, :], k[..., 128:, :].astype(np.float32))
+
+
+def test_streaming_flush_schedule_32k():
+    """Prefill 32768 then 256 appends (G = 32, R = 128): flushes at appends 1
+    and 129, final state (32896, 128)."""
+    S, steps = 32768, 256
+    k = synth.make_k(1, 1, 0, S + steps, D).numpy()
+    v = synth.make_v(1, 1, 0, S + steps, D).numpy()
+    c = cache.KiviCache(1, 1, D, 2, 32, 128, S + steps)
+    c.prefill(k[:, :, :S], v[:, :, :S])
+    assert (c.n_quant, c.n_resid) == (32640, 128)
+    for i in range(steps):
+        c.append(k[:, :, S + i], v[:, :, S + i])
+    assert c.flush_steps == [1, 129]
+    assert (c.n_quant, c.n_resid) == (32896, 128)
+    # group locality: a fresh prefill of the same tokens has identical groups
+    c2 = cache.KiviCache(1, 1, D, 2, 32, 128, S + steps)
+    c2.prefill(k, v)
+    assert c2.n_quant == 32896
+    n = c.n_quant
+    assert np.array_equal(c.k_codes[..., :n, :], c2.k_codes[..., :n, :])
+    assert np.array_equal(c.k_scale, c2.k_scale) and np.array_equal(c.k_zero, c2.k_zero)
+    assert np.array_equal(c.v_codes, c2.v_codes)
+    assert np.array_equal(c.v_scale, c2.v_scale) and np.array_equal(c.v_zero, c2.v_zero)
+    assert np.array_equal(c.k_resid, c2.k_resid) and np.array_equal(c.v_resid, c2.v_resid)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_group_locality_ragged(bits):
+    k, v = _kv(2, 3, 300)
+    a = cache.KiviCache(2, 3, D, bits, 32, 64, 300)
+    a.prefill(k[:, :, :100], v[:, :, :100])
+    for t in range(100, 300):
+        a.append(k[:, :, t], v[:, :, t])
+    b = cache.KiviCache(2, 3, D, bits, 32, 64, 300)
+    b.prefill(k, v)
+    n = min(a.n_quant, b.n_quant)
+    assert n >= 224
+    assert np.array_equal(a.k_codes[:, :, :n], b.k_codes[:, :, :n])
+    assert np.array_equal(a.v_scale[:, :, :n], b.v_scale[:, :, :n])
+    assert np.array_equal(a.v_codes[:, :, :n // 32], b.v_codes[:, :, :n // 32])
+    assert np.array_equal(a.k_scale[:, :, :n // 32], b.k_scale[:, :, :n // 32])
+
+
+def test_dequantized_matches_unpacked_codes():
+    """The cache's packed state decodes to the same values as quantizing the
+    tokens directly."""
+    k, v = _kv(1, 2, 256)
+    c = cache.KiviCache(1, 2, D, 2, 32, 128, 256)
+    c.prefill(k, v)
+    Kh, Vh = c.dequantized()
+    for h in range(2):
+        kc, ks, kz = kivi.quantize_k(k[0, h, :128], 2, 32)
+        vc, vs, vz = kivi.quantize_v(v[0, h, :128], 2)
+        assert np.array_equal(Kh[0, h, :128], kivi.dequantize_k(kc, ks, kz, 32))
+        assert np.array_equal(Vh[0, h, :128], kivi.dequantize_v(vc, vs, vz))
+
+
+def test_fp8_scale_frozen_after_prefill():
+    k, v = _kv(1, 2, 64)
+    c = cache.Fp8Cache(1, 2, D, 80)
+    c.prefill(k, v)
+    sk = c.tensor_scale[0]
+    assert sk == fp8.tensor_scale(k)
+    big = np.full((1, 2, D), 60000.0, np.float16)
+    c.append(big, big)
+    assert c.tensor_scale[0] == sk
+    assert np.all(c.k_codes[:, :, 64] == 0x7E)            # saturated to +448
+
+
+def test_synth_distributions():
+    """The generator draws the stated shapes: K channel factors with 2 ×10
+    outlier channels per KV head, V per-token factors."""
+    f = synth.k_channel_factors(4, D).numpy()
+    out = synth.outlier_channels(4, D)
+    for h, (a, b) in enumerate(out):
+        assert a != b
+        ratio = f[h] / np.exp(synth.normal(0, synth.STREAM_KF,
+                                           torch.arange(h * D, (h + 1) * D)).numpy())
+        assert np.allclose(ratio[[a, b]], 10.0) and np.allclose(np.delete(ratio, [a, b]), 1.0)
+    # streaming token t is element t of the prefill stream
+    k_all = synth.make_k(2, 2, 0, 40, D)
+    k_tail = synth.make_k(2, 2, 33, 40, D)
+    assert torch.equal(k_all[:, :, 33:], k_tail)
+    n = synth.normal(0, 0, torch.arange(200_000)).numpy()
+    assert abs(n.mean()) < 0.01 and abs(n.std() - 1) < 0.01
