@@ -26,7 +26,9 @@
  *   kvq_layout_query / kvq_decode_workspace_bytes). The library never
  *   allocates device memory, keeps no global state, and never synchronizes
  *   the device. Pointers marked "device" must point to device memory of the
- *   current HIP device; "host" pointers to host memory.
+ *   current HIP device; "host" pointers to host memory. Every device pointer
+ *   (cache buffers, inputs, outputs, workspace) must be 16-byte aligned
+ *   (else KVQ_ERR_INVALID_ARG, or KVQ_ERR_WORKSPACE for the workspace).
  * - Streams. `stream` is a hipStream_t passed as void* (NULL = the default
  *   stream). All device work is enqueued asynchronously on it, in call order.
  * - State. The fill levels (n_quant, n_resid) live in the host-side
@@ -36,10 +38,14 @@
  *   A call that returns an error enqueued nothing and changed nothing.
  *   KVQ_ERR_DEVICE reports a failed HIP launch; then the cache state has
  *   still been advanced for the launched work only if the launch succeeded.
- *   No C++ exception or abort crosses this boundary.
+ *   No C++ exception or abort crosses this boundary. A fill state the state
+ *   machine cannot reach (n_quant < 0, KIVI n_quant not a multiple of G,
+ *   n_resid > Rcap, n_quant + n_resid > C, ...) is rejected with
+ *   KVQ_ERR_STATE by every call that reads it.
  * - Inputs. K/V values must be finite fp16; non-finite input is undefined
  *   behaviour (not checked). Query values must be finite fp32.
- * - Supported (else KVQ_ERR_UNSUPPORTED): head_dim = 128; KIVI group_size = 32,
+ * - Supported (else KVQ_ERR_UNSUPPORTED): head_dim = 128; batch · num_kv_heads
+ *   ≤ 65535; KIVI group_size = 32,
  *   bits ∈ {2, 4}, residual_length a multiple of group_size (0 allowed);
  *   FP8 bits = 8; FP16 bits = 16; num_q_heads a positive multiple of
  *   num_kv_heads.
@@ -87,7 +93,9 @@
  *   k_resid, v_resid fp16 [B][H][Rcap][D] the FP16 residual window; slot i
  *            holds token n_quant + i.
  * FP8 E4M3:
- *   k_codes, v_codes uint8 [B][H][C][D];  tensor_scale fp32 [2] = {s_K, s_V}.
+ *   k_codes, v_codes uint8 [B][H][C][D];
+ *   tensor_scale fp32 [4] = {s_K, s_V, amax_K, amax_V} (the amax slots are
+ *   scratch of the prefill reduction).
  * FP16 (baseline, no quantization):
  *   k_codes, v_codes fp16 [B][H][C][D].
  * Decode I/O: q, out fp32 [B][Hq][D]. Query head hq reads KV head
@@ -157,7 +165,7 @@ typedef struct {
   float* v_zero;       /* device, KIVI */
   void* k_resid;       /* device, KIVI */
   void* v_resid;       /* device, KIVI */
-  float* tensor_scale; /* device, FP8: {s_K, s_V} */
+  float* tensor_scale; /* device, FP8: {s_K, s_V, amax_K, amax_V} */
   int64_t n_quant;
   int32_t n_resid;
   int32_t reserved;

@@ -1,0 +1,269 @@
+"""Python binding of libkvq (KIVI / FP8 KV-cache quantization and decode
+attention on MI355X).
+
+Argument marshalling only: every function below forwards to the C ABI of the
+same name in include/kvq.h, and every step of the path runs in the HIP
+kernels of libkvq.so. torch is used for device memory and streams. Importing
+this module fails loudly if libkvq.so has not been built
+(`python -m kv_cache_quantization_quant_amd.build`).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, byref, c_double, c_int32, c_int64, c_size_t, c_void_p
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
+
+KVQ_OK = 0
+KVQ_ERR_INVALID_ARG = 1
+KVQ_ERR_UNSUPPORTED = 2
+KVQ_ERR_CAPACITY = 3
+KVQ_ERR_STATE = 4
+KVQ_ERR_DEVICE = 5
+KVQ_ERR_WORKSPACE = 6
+
+KVQ_FMT_FP16 = 0
+KVQ_FMT_FP8_E4M3 = 1
+KVQ_FMT_KIVI = 2
+
+FORMATS = {"fp16": KVQ_FMT_FP16, "fp8": KVQ_FMT_FP8_E4M3, "kivi": KVQ_FMT_KIVI}
+
+
+class KvqConfig(ctypes.Structure):
+    _fields_ = [("format", c_int32), ("bits", c_int32), ("group_size", c_int32),
+                ("residual_length", c_int32), ("batch", c_int32),
+                ("num_kv_heads", c_int32), ("head_dim", c_int32), ("capacity", c_int32)]
+
+
+class KvqLayout(ctypes.Structure):
+    _fields_ = [(n, c_size_t) for n in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale",
+                                         "v_zero", "k_resid", "v_resid", "tensor_scale")]
+
+
+class KvqCache(ctypes.Structure):
+    _fields_ = [("cfg", KvqConfig),
+                ("k_codes", c_void_p), ("v_codes", c_void_p),
+                ("k_scale", c_void_p), ("k_zero", c_void_p),
+                ("v_scale", c_void_p), ("v_zero", c_void_p),
+                ("k_resid", c_void_p), ("v_resid", c_void_p),
+                ("tensor_scale", c_void_p),
+                ("n_quant", c_int64), ("n_resid", c_int32), ("reserved", c_int32)]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {kvq_status_str(status)} (status {status})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"libkvq.so not found at {_LIB_PATH}; build it with "
+                          "`python -m kv_cache_quantization_quant_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    sig = {
+        "kvq_abi_version": (c_int32, []),
+        "kvq_status_str": (ctypes.c_char_p, [c_int32]),
+        "kvq_layout_query": (c_int32, [POINTER(KvqConfig), POINTER(KvqLayout)]),
+        "kvq_cache_init": (c_int32, [POINTER(KvqCache), POINTER(KvqConfig)]),
+        "kvq_cache_reset": (c_int32, [POINTER(KvqCache)]),
+        "kvq_prefill_quantize": (c_int32, [POINTER(KvqCache), c_void_p, c_void_p, c_int64,
+                                           c_void_p]),
+        "kvq_append_token": (c_int32, [POINTER(KvqCache), c_void_p, c_void_p, c_void_p]),
+        "kvq_decode_workspace_bytes": (c_size_t, [POINTER(KvqConfig), c_int32]),
+        "kvq_decode_attention": (c_int32, [POINTER(KvqCache), c_void_p, c_int32, c_void_p,
+                                           c_void_p, c_size_t, c_void_p]),
+        "kvq_decode_bytes": (c_int64, [POINTER(KvqCache), c_int32]),
+        "kvq_theoretical_bytes": (c_double, [c_int32, c_int32, c_int64, c_int32, c_int32,
+                                             c_double]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+ABI_SYMBOLS = ("kvq_abi_version", "kvq_status_str", "kvq_layout_query", "kvq_cache_init",
+               "kvq_cache_reset", "kvq_prefill_quantize", "kvq_append_token",
+               "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_bytes",
+               "kvq_theoretical_bytes")
+
+
+# ------------------------------------------------- one-to-one ABI wrappers ---
+
+def kvq_abi_version() -> int:
+    return lib.kvq_abi_version()
+
+
+def kvq_status_str(status: int) -> str:
+    return lib.kvq_status_str(status).decode()
+
+
+def kvq_layout_query(cfg: KvqConfig) -> tuple[int, KvqLayout]:
+    out = KvqLayout()
+    return lib.kvq_layout_query(byref(cfg), byref(out)), out
+
+
+def kvq_cache_init(cache: KvqCache, cfg: KvqConfig) -> int:
+    return lib.kvq_cache_init(byref(cache), byref(cfg))
+
+
+def kvq_cache_reset(cache: KvqCache) -> int:
+    return lib.kvq_cache_reset(byref(cache))
+
+
+def kvq_prefill_quantize(cache: KvqCache, k_ptr: int, v_ptr: int, seq_len: int,
+                         stream: int | None) -> int:
+    return lib.kvq_prefill_quantize(byref(cache), k_ptr, v_ptr, seq_len, stream)
+
+
+def kvq_append_token(cache: KvqCache, k_ptr: int, v_ptr: int, stream: int | None) -> int:
+    return lib.kvq_append_token(byref(cache), k_ptr, v_ptr, stream)
+
+
+def kvq_decode_workspace_bytes(cfg: KvqConfig, num_q_heads: int) -> int:
+    return lib.kvq_decode_workspace_bytes(byref(cfg), num_q_heads)
+
+
+def kvq_decode_attention(cache: KvqCache, q_ptr: int, num_q_heads: int, out_ptr: int,
+                         ws_ptr: int, ws_bytes: int, stream: int | None) -> int:
+    return lib.kvq_decode_attention(byref(cache), q_ptr, num_q_heads, out_ptr, ws_ptr,
+                                    ws_bytes, stream)
+
+
+def kvq_decode_bytes(cache: KvqCache, num_q_heads: int) -> int:
+    return lib.kvq_decode_bytes(byref(cache), num_q_heads)
+
+
+def kvq_theoretical_bytes(num_layers, batch, seq_len, num_kv_heads, head_dim,
+                          bytes_per_elem) -> float:
+    return lib.kvq_theoretical_bytes(num_layers, batch, seq_len, num_kv_heads, head_dim,
+                                     bytes_per_elem)
+
+
+def make_config(fmt: str = "kivi", bits: int | None = None, group_size: int = 32,
+                residual_length: int = 128, batch: int = 1, num_kv_heads: int = 1,
+                head_dim: int = 128, capacity: int = 256) -> KvqConfig:
+    if bits is None:
+        bits = {"kivi": 2, "fp8": 8, "fp16": 16}[fmt]
+    return KvqConfig(FORMATS[fmt], bits, group_size, residual_length, batch, num_kv_heads,
+                     head_dim, capacity)
+
+
+def _check(status: int, what: str):
+    if status != KVQ_OK:
+        raise KvqError(status, what)
+
+
+def _stream_handle(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+# ------------------------------------------ torch-owned cache (plumbing) ---
+
+class DeviceCache:
+    """A cache whose device buffers are torch tensors (memory plumbing only);
+    every operation is a call into libkvq on the given (or current) stream."""
+
+    _BUFFERS = ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero",
+                "k_resid", "v_resid", "tensor_scale")
+
+    def __init__(self, cfg: KvqConfig, device="cuda"):
+        self.cfg = cfg
+        st, self.layout = kvq_layout_query(cfg)
+        _check(st, "kvq_layout_query")
+        self.cache = KvqCache()
+        _check(kvq_cache_init(self.cache, cfg), "kvq_cache_init")
+        self.buffers = {}
+        for name in self._BUFFERS:
+            nbytes = getattr(self.layout, name)
+            if nbytes:
+                t = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+                self.buffers[name] = t
+                setattr(self.cache, name, t.data_ptr())
+        self.device = device
+
+    # fill state
+    @property
+    def n_quant(self) -> int:
+        return self.cache.n_quant
+
+    @property
+    def n_resid(self) -> int:
+        return self.cache.n_resid
+
+    def reset(self):
+        _check(kvq_cache_reset(self.cache), "kvq_cache_reset")
+
+    def prefill(self, k: torch.Tensor, v: torch.Tensor, stream=None):
+        """k, v: contiguous fp16 [B, H, S, D] on the device."""
+        assert k.dtype == torch.float16 and v.dtype == torch.float16
+        assert k.is_contiguous() and v.is_contiguous() and k.shape == v.shape
+        _check(kvq_prefill_quantize(self.cache, k.data_ptr(), v.data_ptr(), k.shape[2],
+                                    _stream_handle(stream)), "kvq_prefill_quantize")
+
+    def append(self, k1: torch.Tensor, v1: torch.Tensor, stream=None):
+        """k1, v1: contiguous fp16 [B, H, D] on the device."""
+        assert k1.dtype == torch.float16 and k1.is_contiguous() and v1.is_contiguous()
+        _check(kvq_append_token(self.cache, k1.data_ptr(), v1.data_ptr(),
+                                _stream_handle(stream)), "kvq_append_token")
+
+    def workspace_bytes(self, num_q_heads: int) -> int:
+        return kvq_decode_workspace_bytes(self.cfg, num_q_heads)
+
+    def make_workspace(self, num_q_heads: int) -> torch.Tensor:
+        n = self.workspace_bytes(num_q_heads)
+        if n == 0:
+            raise KvqError(KVQ_ERR_INVALID_ARG, "kvq_decode_workspace_bytes")
+        return torch.empty(n, dtype=torch.uint8, device=self.device)
+
+    def decode(self, q: torch.Tensor, out: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """q: contiguous fp32 [B, Hq, D] → out fp32 [B, Hq, D]."""
+        assert q.dtype == torch.float32 and q.is_contiguous()
+        hq = q.shape[1]
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = self.make_workspace(hq)
+        _check(kvq_decode_attention(self.cache, q.data_ptr(), hq, out.data_ptr(),
+                                    workspace.data_ptr(), workspace.numel(),
+                                    _stream_handle(stream)), "kvq_decode_attention")
+        return out
+
+    def decode_bytes(self, num_q_heads: int) -> int:
+        return kvq_decode_bytes(self.cache, num_q_heads)
+
+    # typed views of the device buffers (for tests and inspection)
+    def view(self, name: str) -> torch.Tensor:
+        c = self.cfg
+        B, H, D, G = c.batch, c.num_kv_heads, c.head_dim, c.group_size
+        NG = -(-c.capacity // G)
+        CT = NG * G
+        Rcap = c.residual_length if c.residual_length > 0 else G
+        buf = self.buffers[name]
+        if c.format == KVQ_FMT_KIVI:
+            b = c.bits
+            shapes = {"k_codes": (torch.int32, (B, H, CT, D * b // 32)),
+                      "v_codes": (torch.int32, (B, H, NG, D, G * b // 32)),
+                      "k_scale": (torch.float32, (B, H, NG, D)),
+                      "k_zero": (torch.float32, (B, H, NG, D)),
+                      "v_scale": (torch.float32, (B, H, CT)),
+                      "v_zero": (torch.float32, (B, H, CT)),
+                      "k_resid": (torch.float16, (B, H, Rcap, D)),
+                      "v_resid": (torch.float16, (B, H, Rcap, D))}
+        elif c.format == KVQ_FMT_FP8_E4M3:
+            shapes = {"k_codes": (torch.uint8, (B, H, c.capacity, D)),
+                      "v_codes": (torch.uint8, (B, H, c.capacity, D)),
+                      "tensor_scale": (torch.float32, (4,))}
+        else:
+            shapes = {"k_codes": (torch.float16, (B, H, c.capacity, D)),
+                      "v_codes": (torch.float16, (B, H, c.capacity, D))}
+        dt, shape = shapes[name]
+        return buf.view(dt).view(shape)

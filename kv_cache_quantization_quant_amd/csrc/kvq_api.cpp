@@ -1,0 +1,463 @@
+// kvq_api.cpp — the C ABI declared in include/kvq.h: argument and state
+// validation, the KIVI fill-state machine, split planning and kernel dispatch.
+//
+// State machine ("4.4 KV Cache 量化：KIVI 2-bit 与 FP8 KV Cache", §3.1–3.2):
+// prefill fills whole groups and leaves the newest tokens (≤ R) in the FP16
+// window; an append that finds the window full first quantizes all of it into
+// new groups (lazy flush), then stores the token. With R = 0 the window holds
+// the incomplete group (capacity G), because per-channel K needs a whole group
+// before it has a scale (§3.1).
+//
+// Every check runs before any launch; a failing call changes nothing.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+using kvq::kGroup;
+using kvq::kHeadDim;
+
+// Workgroups one decode launch aims for (8 per CU on 256 CUs).
+constexpr int64_t kTargetWorkgroups = 2048;
+constexpr int64_t kMinTilesPerSplit = 4;   // one tile per wavefront at least
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+kvq_status validate_config(const kvq_config* c) {
+  if (c == nullptr) return KVQ_ERR_INVALID_ARG;
+  if (c->format != KVQ_FMT_FP16 && c->format != KVQ_FMT_FP8_E4M3 && c->format != KVQ_FMT_KIVI)
+    return KVQ_ERR_INVALID_ARG;
+  if (c->batch <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0 || c->capacity <= 0)
+    return KVQ_ERR_INVALID_ARG;
+  if (c->head_dim != kHeadDim) return KVQ_ERR_UNSUPPORTED;
+  switch (c->format) {
+    case KVQ_FMT_KIVI:
+      if (c->group_size <= 0 || c->residual_length < 0) return KVQ_ERR_INVALID_ARG;
+      if (c->group_size != kGroup) return KVQ_ERR_UNSUPPORTED;
+      if (c->bits != 2 && c->bits != 4) return KVQ_ERR_UNSUPPORTED;
+      if (c->residual_length % c->group_size != 0) return KVQ_ERR_UNSUPPORTED;
+      break;
+    case KVQ_FMT_FP8_E4M3:
+      if (c->bits != 8) return KVQ_ERR_UNSUPPORTED;
+      break;
+    default:
+      if (c->bits != 16) return KVQ_ERR_UNSUPPORTED;
+  }
+  // grid dimension y carries B·H
+  if (int64_t(c->batch) * c->num_kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
+  // keep every element index well inside int64
+  const double elems = double(c->batch) * c->num_kv_heads * (double(c->capacity) + kGroup) *
+                       c->head_dim;
+  if (elems > 9.0e15) return KVQ_ERR_UNSUPPORTED;
+  return KVQ_OK;
+}
+
+struct Dims {
+  int64_t B, H, D, C, NG, CT, Rcap, bits;
+};
+
+Dims dims_of(const kvq_config& c) {
+  Dims d;
+  d.B = c.batch;
+  d.H = c.num_kv_heads;
+  d.D = c.head_dim;
+  d.C = c.capacity;
+  d.NG = ceil_div(c.capacity, kGroup);
+  d.CT = d.NG * kGroup;
+  d.Rcap = c.residual_length > 0 ? c.residual_length : kGroup;
+  d.bits = c.bits;
+  return d;
+}
+
+kvq_status device_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE; }
+
+// Kernels use 16-byte vector loads and stores.
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool buffers_set(const kvq_cache* c) {
+  if (c->k_codes == nullptr || c->v_codes == nullptr) return false;
+  if (!aligned16(c->k_codes) || !aligned16(c->v_codes)) return false;
+  if (c->cfg.format == KVQ_FMT_KIVI) {
+    const void* p[6] = {c->k_scale, c->k_zero, c->v_scale, c->v_zero, c->k_resid, c->v_resid};
+    for (const void* x : p)
+      if (x == nullptr || !aligned16(x)) return false;
+    return true;
+  }
+  if (c->cfg.format == KVQ_FMT_FP8_E4M3)
+    return c->tensor_scale != nullptr && aligned16(c->tensor_scale);
+  return true;
+}
+
+// The host-side fill state must be one the state machine can reach; a
+// corrupted struct is rejected before it can steer a kernel out of bounds.
+bool state_ok(const kvq_cache* c, const Dims& d) {
+  if (c->n_quant < 0 || c->n_resid < 0 || c->n_quant + c->n_resid > d.C) return false;
+  if (c->cfg.format == KVQ_FMT_KIVI) return c->n_quant % kGroup == 0 && c->n_resid <= d.Rcap;
+  return c->n_resid == 0;
+}
+
+// Query heads one decode workgroup handles: the largest power of two ≤ 8
+// dividing Hq / H.
+int heads_per_chunk(int nq) {
+  for (int c = 8; c > 1; c >>= 1)
+    if (nq % c == 0) return c;
+  return 1;
+}
+
+struct Plan {
+  int tiles_per_split, n_split_main, n_split, hpc, nchunk;
+};
+
+Plan make_plan(const Dims& d, int nq, int64_t n_main, int n_win) {
+  Plan p;
+  p.hpc = heads_per_chunk(nq);
+  p.nchunk = nq / p.hpc;
+  const int64_t tiles = ceil_div(n_main, kGroup);
+  const int64_t x = d.B * d.H * p.nchunk;
+  int64_t tps = ceil_div(tiles * x, kTargetWorkgroups);
+  if (tps < kMinTilesPerSplit) tps = kMinTilesPerSplit;
+  p.tiles_per_split = int(tps);
+  p.n_split_main = int(ceil_div(tiles, tps));
+  p.n_split = p.n_split_main + (n_win > 0 ? 1 : 0);
+  return p;
+}
+
+// Upper bound of Plan::n_split over every fill state of this configuration:
+// n_split_main ≤ ⌊target / x⌋ + 1 and ≤ ⌈max tiles / 4⌉, plus the window split.
+int64_t max_splits(const Dims& d, int nq) {
+  const int hpc = heads_per_chunk(nq);
+  const int64_t x = d.B * d.H * (nq / hpc);
+  const int64_t max_tiles = d.CT / kGroup;
+  int64_t a = kTargetWorkgroups / x + 1;
+  const int64_t b = ceil_div(max_tiles, kMinTilesPerSplit);
+  if (b < a) a = b;
+  return a + 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvq_abi_version(void) { return KVQ_ABI_VERSION; }
+
+const char* kvq_status_str(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_INVALID_ARG: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVQ_ERR_CAPACITY: return "cache capacity exceeded";
+    case KVQ_ERR_STATE: return "invalid cache state for this call";
+    case KVQ_ERR_DEVICE: return "HIP launch failed";
+    case KVQ_ERR_WORKSPACE: return "decode workspace missing or too small";
+  }
+  return "unknown status";
+}
+
+kvq_status kvq_layout_query(const kvq_config* cfg, kvq_layout* out) {
+  if (out == nullptr) return KVQ_ERR_INVALID_ARG;
+  const kvq_status v = validate_config(cfg);
+  if (v != KVQ_OK) return v;
+  memset(out, 0, sizeof(*out));
+  const Dims d = dims_of(*cfg);
+  const size_t bh = size_t(d.B * d.H);
+  switch (cfg->format) {
+    case KVQ_FMT_KIVI:
+      out->k_codes = bh * d.CT * (d.D * d.bits / 32) * 4;
+      out->v_codes = bh * d.NG * d.D * (kGroup * d.bits / 32) * 4;
+      out->k_scale = out->k_zero = bh * d.NG * d.D * 4;
+      out->v_scale = out->v_zero = bh * d.CT * 4;
+      out->k_resid = out->v_resid = bh * d.Rcap * d.D * 2;
+      break;
+    case KVQ_FMT_FP8_E4M3:
+      out->k_codes = out->v_codes = bh * d.C * d.D;
+      out->tensor_scale = 4 * sizeof(float);
+      break;
+    default:
+      out->k_codes = out->v_codes = bh * d.C * d.D * 2;
+  }
+  return KVQ_OK;
+}
+
+kvq_status kvq_cache_init(kvq_cache* cache, const kvq_config* cfg) {
+  if (cache == nullptr) return KVQ_ERR_INVALID_ARG;
+  const kvq_status v = validate_config(cfg);
+  if (v != KVQ_OK) return v;
+  memset(cache, 0, sizeof(*cache));
+  cache->cfg = *cfg;
+  return KVQ_OK;
+}
+
+kvq_status kvq_cache_reset(kvq_cache* cache) {
+  if (cache == nullptr) return KVQ_ERR_INVALID_ARG;
+  const kvq_status v = validate_config(&cache->cfg);
+  if (v != KVQ_OK) return v;
+  cache->n_quant = 0;
+  cache->n_resid = 0;
+  return KVQ_OK;
+}
+
+kvq_status kvq_prefill_quantize(kvq_cache* cache, const void* k, const void* v,
+                                int64_t seq_len, void* stream) {
+  if (cache == nullptr || k == nullptr || v == nullptr) return KVQ_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned16(v)) return KVQ_ERR_INVALID_ARG;
+  const kvq_status vs = validate_config(&cache->cfg);
+  if (vs != KVQ_OK) return vs;
+  if (!buffers_set(cache)) return KVQ_ERR_INVALID_ARG;
+  if (seq_len <= 0) return KVQ_ERR_INVALID_ARG;
+  const Dims d = dims_of(cache->cfg);
+  if (!state_ok(cache, d)) return KVQ_ERR_STATE;
+  if (seq_len > d.C) return KVQ_ERR_CAPACITY;
+  if (cache->n_quant != 0 || cache->n_resid != 0) return KVQ_ERR_STATE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int bh = int(d.B * d.H);
+  const __half* kh = static_cast<const __half*>(k);
+  const __half* vh = static_cast<const __half*>(v);
+
+  if (cache->cfg.format == KVQ_FMT_KIVI) {
+    // n_quant = G·max(0, min(⌊S/G⌋, ⌈(S−R)/G⌉)); the rest stays FP16.
+    const int64_t R = cache->cfg.residual_length;
+    int64_t need = seq_len > R ? ceil_div(seq_len - R, kGroup) : 0;
+    const int64_t full = seq_len / kGroup;
+    if (need > full) need = full;
+    const int64_t nq = need * kGroup;
+    const int64_t nr = seq_len - nq;
+    kvq::KiviQuantArgs qa{};
+    qa.k_src = kh;
+    qa.v_src = vh;
+    qa.src_bh_stride = seq_len * d.D;
+    qa.n_groups = int(nq / kGroup);
+    qa.g0 = 0;
+    qa.bh_count = bh;
+    qa.bits = int(d.bits);
+    qa.NG = d.NG;
+    qa.k_codes = static_cast<uint32_t*>(cache->k_codes);
+    qa.v_codes = static_cast<uint32_t*>(cache->v_codes);
+    qa.k_scale = cache->k_scale;
+    qa.k_zero = cache->k_zero;
+    qa.v_scale = cache->v_scale;
+    qa.v_zero = cache->v_zero;
+    hipError_t e = kvq::launch_kivi_quantize(qa, s);
+    if (e != hipSuccess) return KVQ_ERR_DEVICE;
+    kvq::CopyTokensArgs ca{};
+    ca.k_src = kh + nq * d.D;
+    ca.v_src = vh + nq * d.D;
+    ca.src_bh_stride = seq_len * d.D;
+    ca.k_dst = static_cast<__half*>(cache->k_resid);
+    ca.v_dst = static_cast<__half*>(cache->v_resid);
+    ca.dst_bh_stride = d.Rcap * d.D;
+    ca.dst_t0 = 0;
+    ca.n_tokens = nr;
+    ca.bh_count = bh;
+    e = kvq::launch_copy_tokens(ca, s);
+    if (e != hipSuccess) return KVQ_ERR_DEVICE;
+    cache->n_quant = nq;
+    cache->n_resid = int32_t(nr);
+    return KVQ_OK;
+  }
+  if (cache->cfg.format == KVQ_FMT_FP8_E4M3) {
+    kvq::Fp8QuantArgs fa{};
+    fa.k_src = kh;
+    fa.v_src = vh;
+    fa.src_bh_stride = seq_len * d.D;
+    fa.n_tokens = seq_len;
+    fa.k_codes = static_cast<uint8_t*>(cache->k_codes);
+    fa.v_codes = static_cast<uint8_t*>(cache->v_codes);
+    fa.dst_bh_stride = d.C * d.D;
+    fa.dst_t0 = 0;
+    fa.bh_count = bh;
+    fa.tensor_scale = cache->tensor_scale;
+    if (kvq::launch_fp8_prefill(fa, s) != hipSuccess) return KVQ_ERR_DEVICE;
+    cache->n_quant = seq_len;
+    return KVQ_OK;
+  }
+  kvq::CopyTokensArgs ca{};
+  ca.k_src = kh;
+  ca.v_src = vh;
+  ca.src_bh_stride = seq_len * d.D;
+  ca.k_dst = static_cast<__half*>(cache->k_codes);
+  ca.v_dst = static_cast<__half*>(cache->v_codes);
+  ca.dst_bh_stride = d.C * d.D;
+  ca.dst_t0 = 0;
+  ca.n_tokens = seq_len;
+  ca.bh_count = bh;
+  if (kvq::launch_copy_tokens(ca, s) != hipSuccess) return KVQ_ERR_DEVICE;
+  cache->n_quant = seq_len;
+  return KVQ_OK;
+}
+
+kvq_status kvq_append_token(kvq_cache* cache, const void* k_new, const void* v_new,
+                            void* stream) {
+  if (cache == nullptr || k_new == nullptr || v_new == nullptr) return KVQ_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new)) return KVQ_ERR_INVALID_ARG;
+  const kvq_status vs = validate_config(&cache->cfg);
+  if (vs != KVQ_OK) return vs;
+  if (!buffers_set(cache)) return KVQ_ERR_INVALID_ARG;
+  const Dims d = dims_of(cache->cfg);
+  if (!state_ok(cache, d)) return KVQ_ERR_STATE;
+  if (cache->n_quant + cache->n_resid >= d.C) return KVQ_ERR_CAPACITY;
+  if (cache->cfg.format == KVQ_FMT_FP8_E4M3 && cache->n_quant == 0) return KVQ_ERR_STATE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int bh = int(d.B * d.H);
+  const __half* kh = static_cast<const __half*>(k_new);
+  const __half* vh = static_cast<const __half*>(v_new);
+
+  if (cache->cfg.format == KVQ_FMT_KIVI) {
+    if (cache->n_resid == d.Rcap) {   // lazy flush of the full window
+      kvq::KiviQuantArgs qa{};
+      qa.k_src = static_cast<const __half*>(cache->k_resid);
+      qa.v_src = static_cast<const __half*>(cache->v_resid);
+      qa.src_bh_stride = d.Rcap * d.D;
+      qa.n_groups = int(d.Rcap / kGroup);
+      qa.g0 = cache->n_quant / kGroup;
+      qa.bh_count = bh;
+      qa.bits = int(d.bits);
+      qa.NG = d.NG;
+      qa.k_codes = static_cast<uint32_t*>(cache->k_codes);
+      qa.v_codes = static_cast<uint32_t*>(cache->v_codes);
+      qa.k_scale = cache->k_scale;
+      qa.k_zero = cache->k_zero;
+      qa.v_scale = cache->v_scale;
+      qa.v_zero = cache->v_zero;
+      if (kvq::launch_kivi_quantize(qa, s) != hipSuccess) return KVQ_ERR_DEVICE;
+      cache->n_quant += d.Rcap;
+      cache->n_resid = 0;
+    }
+    kvq::CopyTokensArgs ca{};
+    ca.k_src = kh;
+    ca.v_src = vh;
+    ca.src_bh_stride = d.D;
+    ca.k_dst = static_cast<__half*>(cache->k_resid);
+    ca.v_dst = static_cast<__half*>(cache->v_resid);
+    ca.dst_bh_stride = d.Rcap * d.D;
+    ca.dst_t0 = cache->n_resid;
+    ca.n_tokens = 1;
+    ca.bh_count = bh;
+    if (kvq::launch_copy_tokens(ca, s) != hipSuccess) return KVQ_ERR_DEVICE;
+    cache->n_resid += 1;
+    return KVQ_OK;
+  }
+  if (cache->cfg.format == KVQ_FMT_FP8_E4M3) {
+    kvq::Fp8QuantArgs fa{};
+    fa.k_src = kh;
+    fa.v_src = vh;
+    fa.src_bh_stride = d.D;
+    fa.n_tokens = 1;
+    fa.k_codes = static_cast<uint8_t*>(cache->k_codes);
+    fa.v_codes = static_cast<uint8_t*>(cache->v_codes);
+    fa.dst_bh_stride = d.C * d.D;
+    fa.dst_t0 = cache->n_quant;
+    fa.bh_count = bh;
+    fa.tensor_scale = cache->tensor_scale;
+    if (kvq::launch_fp8_append(fa, s) != hipSuccess) return KVQ_ERR_DEVICE;
+    cache->n_quant += 1;
+    return KVQ_OK;
+  }
+  kvq::CopyTokensArgs ca{};
+  ca.k_src = kh;
+  ca.v_src = vh;
+  ca.src_bh_stride = d.D;
+  ca.k_dst = static_cast<__half*>(cache->k_codes);
+  ca.v_dst = static_cast<__half*>(cache->v_codes);
+  ca.dst_bh_stride = d.C * d.D;
+  ca.dst_t0 = cache->n_quant;
+  ca.n_tokens = 1;
+  ca.bh_count = bh;
+  if (kvq::launch_copy_tokens(ca, s) != hipSuccess) return KVQ_ERR_DEVICE;
+  cache->n_quant += 1;
+  return KVQ_OK;
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t num_q_heads) {
+  if (validate_config(cfg) != KVQ_OK) return 0;
+  if (num_q_heads <= 0 || num_q_heads % cfg->num_kv_heads != 0) return 0;
+  const Dims d = dims_of(*cfg);
+  const int nq = num_q_heads / cfg->num_kv_heads;
+  return size_t(d.B) * num_q_heads * max_splits(d, nq) * (kHeadDim + 2) * sizeof(float);
+}
+
+kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q, int32_t num_q_heads,
+                                float* out, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (cache == nullptr || q == nullptr || out == nullptr) return KVQ_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out)) return KVQ_ERR_INVALID_ARG;
+  const kvq_status vs = validate_config(&cache->cfg);
+  if (vs != KVQ_OK) return vs;
+  if (!buffers_set(cache)) return KVQ_ERR_INVALID_ARG;
+  if (num_q_heads <= 0) return KVQ_ERR_INVALID_ARG;
+  if (num_q_heads % cache->cfg.num_kv_heads != 0) return KVQ_ERR_UNSUPPORTED;
+  if (!state_ok(cache, dims_of(cache->cfg))) return KVQ_ERR_STATE;
+  if (cache->n_quant + cache->n_resid <= 0) return KVQ_ERR_STATE;
+  const size_t need = kvq_decode_workspace_bytes(&cache->cfg, num_q_heads);
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
+    return KVQ_ERR_WORKSPACE;
+
+  const Dims d = dims_of(cache->cfg);
+  const int nq = num_q_heads / int(d.H);
+  const bool kivi = cache->cfg.format == KVQ_FMT_KIVI;
+  const int n_win = kivi ? cache->n_resid : 0;
+  const Plan p = make_plan(d, nq, cache->n_quant, n_win);
+  if (p.n_split > max_splits(d, nq)) return KVQ_ERR_WORKSPACE;
+
+  kvq::DecodeArgs a{};
+  a.src = kivi ? (d.bits == 2 ? kvq::kSrcKivi2 : kvq::kSrcKivi4)
+               : (cache->cfg.format == KVQ_FMT_FP8_E4M3 ? kvq::kSrcFp8 : kvq::kSrcFp16);
+  a.B = int(d.B);
+  a.H = int(d.H);
+  a.Hq = num_q_heads;
+  a.nq = nq;
+  a.heads_per_chunk = p.hpc;
+  a.k_main = cache->k_codes;
+  a.v_main = cache->v_codes;
+  a.k_scale = cache->k_scale;
+  a.k_zero = cache->k_zero;
+  a.v_scale = cache->v_scale;
+  a.v_zero = cache->v_zero;
+  a.tensor_scale = cache->tensor_scale;
+  a.NG = d.NG;
+  a.main_bh_tokens = kivi ? d.CT : d.C;
+  a.n_main = cache->n_quant;
+  a.k_win = static_cast<const __half*>(cache->k_resid);
+  a.v_win = static_cast<const __half*>(cache->v_resid);
+  a.win_cap = int(d.Rcap);
+  a.n_win = n_win;
+  a.tiles_per_split = p.tiles_per_split;
+  a.n_split_main = p.n_split_main;
+  a.n_split = p.n_split;
+  a.q = q;
+  a.out = out;
+  a.ws = static_cast<float*>(workspace);
+  a.qscale = float(1.4426950408889634 / sqrt(double(kHeadDim)));
+  return device_status(kvq::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+int64_t kvq_decode_bytes(const kvq_cache* cache, int32_t num_q_heads) {
+  if (cache == nullptr || validate_config(&cache->cfg) != KVQ_OK) return -1;
+  if (num_q_heads <= 0 || num_q_heads % cache->cfg.num_kv_heads != 0) return -1;
+  const Dims d = dims_of(cache->cfg);
+  if (!state_ok(cache, d)) return -1;
+  const int64_t bh = d.B * d.H;
+  const int64_t nq = cache->n_quant;
+  if (cache->cfg.format == KVQ_FMT_KIVI) {
+    const int64_t code_bytes = nq * d.D * d.bits / 8;       // per K and per V
+    const int64_t k_meta = (nq / kGroup) * d.D * 2 * 4;     // fp32 s, z per channel
+    const int64_t v_meta = nq * 2 * 4;                      // fp32 s, z per token
+    const int64_t window = 2 * int64_t(cache->n_resid) * d.D * 2;
+    return bh * (2 * code_bytes + k_meta + v_meta + window);
+  }
+  if (cache->cfg.format == KVQ_FMT_FP8_E4M3) return 2 * bh * nq * d.D + 2 * 4;
+  return 2 * bh * nq * d.D * 2;
+}
+
+double kvq_theoretical_bytes(int32_t num_layers, int32_t batch, int64_t seq_len,
+                             int32_t num_kv_heads, int32_t head_dim, double bytes_per_elem) {
+  return 2.0 * num_layers * double(batch) * double(seq_len) * num_kv_heads * head_dim *
+         bytes_per_elem;
+}
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+// kvq_internal.h — launch parameter blocks shared by the C ABI host code
+// (kvq_api.cpp) and the HIP kernels (kvq_quant.hip, kvq_decode.hip).
+// Not part of the public interface.
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+constexpr int kHeadDim = 128;   // D
+constexpr int kGroup = 32;      // G (KIVI group = decode tile of tokens)
+
+// KIVI quantization of whole groups. Source tokens [0, n_groups·G) of each
+// (b, h) block of an fp16 [B·H][src_tokens][D] tensor are quantized into the
+// cache groups [g0, g0 + n_groups).
+struct KiviQuantArgs {
+  const __half* k_src;
+  const __half* v_src;
+  int64_t src_bh_stride;  // elements between consecutive (b, h) blocks
+  int n_groups;
+  int64_t g0;
+  int bh_count;           // B·H
+  int bits;
+  int64_t NG;             // group slots per (b, h)
+  uint32_t* k_codes;      // [B·H][NG·G][D·b/32]
+  uint32_t* v_codes;      // [B·H][NG][D][G·b/32]
+  float* k_scale;         // [B·H][NG][D]
+  float* k_zero;
+  float* v_scale;         // [B·H][NG·G]
+  float* v_zero;
+};
+
+// Strided copy of `n_tokens` tokens of K and V (fp16, D channels each) from
+// [B·H][src_tokens][D] into [B·H][dst_tokens][D] at token offset dst_t0.
+struct CopyTokensArgs {
+  const __half* k_src;
+  const __half* v_src;
+  int64_t src_bh_stride;  // elements
+  __half* k_dst;
+  __half* v_dst;
+  int64_t dst_bh_stride;  // elements
+  int64_t dst_t0;
+  int64_t n_tokens;
+  int bh_count;
+};
+
+// FP8 E4M3 per-tensor quantization.
+struct Fp8QuantArgs {
+  const __half* k_src;
+  const __half* v_src;
+  int64_t src_bh_stride;  // elements
+  int64_t n_tokens;       // tokens per (b, h) to encode
+  uint8_t* k_codes;       // [B·H][C][D]
+  uint8_t* v_codes;
+  int64_t dst_bh_stride;  // elements (C·D)
+  int64_t dst_t0;
+  int bh_count;
+  float* tensor_scale;    // {s_K, s_V, amax_K, amax_V}
+};
+
+enum SrcFormat : int { kSrcFp16 = 0, kSrcFp8 = 1, kSrcKivi2 = 2, kSrcKivi4 = 3 };
+
+// Split-K decode attention. Grid: (n_split, B·H, head_chunks).
+struct DecodeArgs {
+  int src;                // SrcFormat of the main region
+  int B, H, Hq;
+  int nq;                 // query heads per KV head (Hq / H)
+  int heads_per_chunk;    // query heads one workgroup handles
+  // main region: KIVI grouped region, or the whole FP8 / FP16 cache
+  const void* k_main;
+  const void* v_main;
+  const float* k_scale;
+  const float* k_zero;
+  const float* v_scale;
+  const float* v_zero;
+  const float* tensor_scale;
+  int64_t NG;             // KIVI group slots per (b, h)
+  int64_t main_bh_tokens; // token slots per (b, h) of the main region
+  int64_t n_main;         // tokens in the main region
+  // KIVI FP16 window
+  const __half* k_win;
+  const __half* v_win;
+  int win_cap;            // token slots per (b, h)
+  int n_win;              // tokens in the window
+  // split plan
+  int tiles_per_split;
+  int n_split_main;       // splits over the main region
+  int n_split;            // n_split_main (+1 if the window is non-empty)
+  const float* q;         // [B][Hq][D]
+  float* out;             // [B][Hq][D]
+  float* ws;              // [B][Hq][n_split][D + 2]
+  float qscale;           // log2(e) / sqrt(D)
+};
+
+hipError_t launch_kivi_quantize(const KiviQuantArgs& a, hipStream_t s);
+hipError_t launch_copy_tokens(const CopyTokensArgs& a, hipStream_t s);
+hipError_t launch_fp8_prefill(const Fp8QuantArgs& a, hipStream_t s);
+hipError_t launch_fp8_append(const Fp8QuantArgs& a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+}  // namespace kvq

@@ -107,9 +107,12 @@ def k_channel_factors(num_kv_heads: int, head_dim: int, seed: int = 0,
     return f
 
 
-def _token_index(b: int, h: int, H: int, t0: int, t1: int, device):
+def _token_index(b: int, H: int, t0: int, t1: int, device):
+    """Counter base of tokens [t0, t1) of every KV head of batch element b:
+    int64 [H, t1 - t0]."""
+    h = torch.arange(H, dtype=torch.int64, device=device)
     t = torch.arange(t0, t1, dtype=torch.int64, device=device)
-    return ((b * H + h) << _TOKEN_BITS) + t
+    return ((b * H + h[:, None]) << _TOKEN_BITS) + t[None, :]
 
 
 def make_k(batch: int, num_kv_heads: int, t0: int, t1: int, head_dim: int,
@@ -121,10 +124,9 @@ def make_k(batch: int, num_kv_heads: int, t0: int, t1: int, head_dim: int,
                       dtype=torch.float16, device=device)
     d = torch.arange(head_dim, dtype=torch.int64, device=device)
     for b in range(batch):
-        for h in range(num_kv_heads):
-            tok = _token_index(b, h, num_kv_heads, t0, t1, device)
-            idx = tok[:, None] * head_dim + d[None, :]
-            out[b, h] = _to_fp16(normal(seed, STREAM_K, idx) * f[h][None, :])
+        tok = _token_index(b, num_kv_heads, t0, t1, device)
+        idx = tok[:, :, None] * head_dim + d
+        out[b] = _to_fp16(normal(seed, STREAM_K, idx) * f[:, None, :])
     return out
 
 
@@ -136,11 +138,10 @@ def make_v(batch: int, num_kv_heads: int, t0: int, t1: int, head_dim: int,
                       dtype=torch.float16, device=device)
     d = torch.arange(head_dim, dtype=torch.int64, device=device)
     for b in range(batch):
-        for h in range(num_kv_heads):
-            tok = _token_index(b, h, num_kv_heads, t0, t1, device)
-            g = torch.exp(0.5 * normal(seed, STREAM_VF, tok))
-            idx = tok[:, None] * head_dim + d[None, :]
-            out[b, h] = _to_fp16(normal(seed, STREAM_V, idx) * g[:, None])
+        tok = _token_index(b, num_kv_heads, t0, t1, device)
+        g = torch.exp(0.5 * normal(seed, STREAM_VF, tok))
+        idx = tok[:, :, None] * head_dim + d
+        out[b] = _to_fp16(normal(seed, STREAM_V, idx) * g[:, :, None])
     return out
 
 

@@ -1,0 +1,415 @@
+"""Parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: packed codes, scales and zero-points bit-exact; FP8 codes and tensor
+scales bit-exact; decode attention within max-abs 2e-3 of the oracle's fp64
+attention over the same dequantized values. Inputs come from `synth` (seed 0)
+and are generated once, on the GPU, then copied to the host for the oracle.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import cache as ocache, fp8 as ofp8
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 2e-3
+D = 128
+
+
+@pytest.fixture(scope="module")
+def kq():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import kv_cache_quantization_quant_amd as m
+    return m
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _kv(B, H, T, device="cuda"):
+    return (synth.make_k(B, H, 0, T, D, device=device),
+            synth.make_v(B, H, 0, T, D, device=device))
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _compare_kivi_state(dc, oc, blocks=None):
+    """Bit-exact comparison of every KIVI buffer (optionally only (b, h) blocks)."""
+    names = ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero", "k_resid",
+             "v_resid")
+    for name in names:
+        g = _np(dc.view(name))
+        o = getattr(oc, name)
+        if name.endswith("codes"):
+            g = g.view(np.uint32)
+        if blocks is None:
+            assert g.shape == o.shape, name
+            assert np.array_equal(g.view(np.uint8), o.view(np.uint8)), name
+        else:
+            for i, (b, h) in enumerate(blocks):
+                assert np.array_equal(g[b, h].view(np.uint8), o[i, 0].view(np.uint8)), (name, b, h)
+    assert (dc.n_quant, dc.n_resid) == (oc.n_quant, oc.n_resid)
+
+
+def _att_err(got, ref):
+    return float(np.max(np.abs(got.astype(np.float64) - ref)))
+
+
+# ------------------------------------------------------------- small cases ---
+
+@pytest.mark.parametrize("B,H,Hq,S,bits,R,C", [
+    (1, 1, 1, 256, 2, 128, 256),      # tiny MHA workload: 4 groups + 128 FP16
+    (2, 3, 6, 200, 2, 128, 300),      # ragged prefill: 96 quantized + 104 window
+    (1, 2, 6, 77, 4, 128, 100),       # everything in the window; GQA 3
+    (3, 1, 8, 1000, 2, 0, 1000),      # R = 0, MQA
+    (1, 1, 1, 5, 2, 32, 64),          # fewer tokens than a group
+    (2, 2, 24, 640, 4, 64, 700),      # GQA 12 (chunks of 4)
+    (1, 4, 64, 300, 2, 128, 400),     # GQA 16 (chunks of 8)
+    (5, 3, 3, 2048, 4, 128, 2100),    # several splits per head
+])
+def test_kivi_prefill_and_decode(kq, B, H, Hq, S, bits, R, C):
+    _say(f"[kivi prefill/decode] B={B} H={H} Hq={Hq} S={S} bits={bits} R={R}")
+    k, v = _kv(B, H, S)
+    dc = kq.DeviceCache(kq.make_config("kivi", bits=bits, residual_length=R, batch=B,
+                                       num_kv_heads=H, capacity=C))
+    dc.prefill(k, v)
+    oc = ocache.KiviCache(B, H, D, bits, 32, R, C)
+    oc.prefill(_np(k), _np(v))
+    torch.cuda.synchronize()
+    _compare_kivi_state(dc, oc)
+    q = synth.make_q(B, Hq, D, device="cuda")
+    out = dc.decode(q)
+    torch.cuda.synchronize()
+    err = _att_err(_np(out), oc.attention(_np(q)))
+    _say(f"  max abs err {err:.3e}")
+    assert err <= ATOL
+
+
+def test_llama2_7b_layer_full(kq):
+    """B=8, 32 MHA heads, S=4096, KIVI 2-bit: every buffer and every output."""
+    cfg = synth.CONFIGS["llama2_7b_layer"]
+    B, H, Hq, S = cfg["batch"], cfg["num_kv_heads"], cfg["num_q_heads"], cfg["seq_len"]
+    _say(f"[llama2_7b_layer] B={B} H={H} S={S}")
+    k, v = _kv(B, H, S)
+    dc = kq.DeviceCache(kq.make_config("kivi", bits=2, batch=B, num_kv_heads=H, capacity=S))
+    dc.prefill(k, v)
+    oc = ocache.KiviCache(B, H, D, 2, 32, 128, S)
+    oc.prefill(_np(k), _np(v))
+    torch.cuda.synchronize()
+    _compare_kivi_state(dc, oc)
+    assert (dc.n_quant, dc.n_resid) == (3968, 128)
+    q = synth.make_q(B, Hq, D, device="cuda")
+    out = dc.decode(q)
+    err = _att_err(_np(out), oc.attention(_np(q)))
+    _say(f"  max abs err {err:.3e}")
+    assert err <= ATOL
+
+
+@pytest.mark.parametrize("bits,R", [(2, 64), (4, 128), (2, 0)])
+def test_kivi_streaming(kq, bits, R):
+    """Prefill, then appends with a decode after each: fill state, lazy flushes,
+    codes and attention match the oracle at every step."""
+    B, H, Hq, S0, steps = 2, 2, 4, 100, 150
+    C = S0 + steps
+    _say(f"[kivi streaming] bits={bits} R={R}")
+    k, v = _kv(B, H, C)
+    dc = kq.DeviceCache(kq.make_config("kivi", bits=bits, residual_length=R, batch=B,
+                                       num_kv_heads=H, capacity=C))
+    oc = ocache.KiviCache(B, H, D, bits, 32, R, C)
+    dc.prefill(k[:, :, :S0].contiguous(), v[:, :, :S0].contiguous())
+    oc.prefill(_np(k[:, :, :S0]), _np(v[:, :, :S0]))
+    ws = dc.make_workspace(Hq)
+    kn, vn = _np(k), _np(v)
+    worst = 0.0
+    for i in range(steps):
+        t = S0 + i
+        dc.append(k[:, :, t].contiguous(), v[:, :, t].contiguous())
+        oc.append(kn[:, :, t], vn[:, :, t])
+        assert (dc.n_quant, dc.n_resid) == (oc.n_quant, oc.n_resid)
+        q = synth.make_q(B, Hq, D, step=i, device="cuda")
+        out = dc.decode(q, workspace=ws)
+        worst = max(worst, _att_err(_np(out), oc.attention(_np(q))))
+    torch.cuda.synchronize()
+    _compare_kivi_state(dc, oc)
+    assert dc.n_quant > 0
+    _say(f"  worst max abs err {worst:.3e}, flushes at {oc.flush_steps}")
+    assert worst <= ATOL
+
+
+def test_append_at_capacity_is_rejected(kq):
+    k, v = _kv(1, 1, 40)
+    dc = kq.DeviceCache(kq.make_config("kivi", residual_length=32, capacity=40))
+    dc.prefill(k, v)
+    with pytest.raises(kq.KvqError) as e:
+        dc.append(k[:, :, 0].contiguous(), v[:, :, 0].contiguous())
+    assert e.value.status == kq.KVQ_ERR_CAPACITY
+    assert (dc.n_quant, dc.n_resid) == (32, 8)
+
+
+def test_deterministic(kq):
+    B, H, Hq, S = 2, 2, 8, 1500
+    k, v = _kv(B, H, S)
+    outs = []
+    for _ in range(2):
+        dc = kq.DeviceCache(kq.make_config("kivi", bits=2, batch=B, num_kv_heads=H, capacity=S))
+        dc.prefill(k, v)
+        q = synth.make_q(B, Hq, D, device="cuda")
+        outs.append((_np(dc.view("k_codes")), _np(dc.decode(q)), _np(dc.decode(q))))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1], outs[1][1]) and np.array_equal(outs[0][1], outs[0][2])
+
+
+# --------------------------------------------------------------------- FP8 ---
+
+def _all_finite_fp16(limit=None):
+    allv = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    allv = allv[np.isfinite(allv)]
+    if limit is not None:
+        allv = allv[np.abs(allv.astype(np.float32)) <= limit]
+    pad = (-len(allv)) % D
+    return np.concatenate([allv, np.zeros(pad, np.float16)])
+
+
+@pytest.mark.parametrize("limit", [None, 448.0, 1.0, 0.01])
+def test_fp8_encoder_every_fp16_value(kq, limit):
+    """Every finite fp16 value (up to ±limit) through the FP8 prefill: tensor
+    scale and every code bit-exact with the oracle."""
+    kvals = _all_finite_fp16(limit)
+    vvals = -kvals[::-1].copy()
+    S = len(kvals) // D
+    k = torch.from_numpy(kvals.reshape(1, 1, S, D)).cuda()
+    v = torch.from_numpy(vvals.reshape(1, 1, S, D)).cuda()
+    dc = kq.DeviceCache(kq.make_config("fp8", capacity=S))
+    dc.prefill(k, v)
+    oc = ocache.Fp8Cache(1, 1, D, S)
+    oc.prefill(_np(k), _np(v))
+    torch.cuda.synchronize()
+    ts = _np(dc.view("tensor_scale"))
+    assert ts[0].view(np.uint32) == oc.tensor_scale[0].view(np.uint32)
+    assert ts[1].view(np.uint32) == oc.tensor_scale[1].view(np.uint32)
+    assert np.array_equal(_np(dc.view("k_codes")), oc.k_codes)
+    assert np.array_equal(_np(dc.view("v_codes")), oc.v_codes)
+
+
+def test_fp8_decode_values(kq):
+    """The in-kernel E4M3 decode: a cache holding all 254 finite codes (scale
+    1 from amax 448) attends with one-hot queries to recover values."""
+    t = ofp8.decode_table()
+    finite = np.array([c for c in range(256) if np.isfinite(t[c])], np.uint8)
+    vals = t[finite].astype(np.float16)                 # all exact in fp16
+    S = 2
+    kv = np.zeros((1, 1, S, D), np.float16)
+    kv.reshape(-1)[:len(vals)] = vals
+    k = torch.from_numpy(kv).cuda()
+    dc = kq.DeviceCache(kq.make_config("fp8", capacity=S))
+    dc.prefill(k, k)
+    assert _np(dc.view("tensor_scale"))[0] == np.float32(1.0)
+    oc = ocache.Fp8Cache(1, 1, D, S)
+    oc.prefill(kv, kv)
+    assert np.array_equal(_np(dc.view("k_codes")), oc.k_codes)
+    q = torch.zeros(1, 1, D, device="cuda")
+    out = dc.decode(q)           # uniform attention: mean of the two V rows
+    ref = oc.attention(_np(q))
+    assert _att_err(_np(out), ref) <= 1e-6
+
+
+@pytest.mark.parametrize("B,H,Hq,S,steps", [(2, 2, 8, 700, 40), (1, 3, 3, 33, 5)])
+def test_fp8_prefill_append_decode(kq, B, H, Hq, S, steps):
+    C = S + steps
+    k, v = _kv(B, H, C)
+    k[:, :, S + steps // 2] *= 8      # appended tokens beyond amax saturate
+    dc = kq.DeviceCache(kq.make_config("fp8", batch=B, num_kv_heads=H, capacity=C))
+    oc = ocache.Fp8Cache(B, H, D, C)
+    dc.prefill(k[:, :, :S].contiguous(), v[:, :, :S].contiguous())
+    oc.prefill(_np(k[:, :, :S]), _np(v[:, :, :S]))
+    kn, vn = _np(k), _np(v)
+    worst = 0.0
+    for i in range(steps):
+        dc.append(k[:, :, S + i].contiguous(), v[:, :, S + i].contiguous())
+        oc.append(kn[:, :, S + i], vn[:, :, S + i])
+        q = synth.make_q(B, Hq, D, step=i, device="cuda")
+        worst = max(worst, _att_err(_np(dc.decode(q)), oc.attention(_np(q))))
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(dc.view("k_codes")), oc.k_codes)
+    assert np.array_equal(_np(dc.view("v_codes")), oc.v_codes)
+    assert np.array_equal(_np(dc.view("tensor_scale"))[:2], oc.tensor_scale)
+    _say(f"[fp8 stream] worst max abs err {worst:.3e}")
+    assert worst <= ATOL
+
+
+def test_fp8_all_zero_tensor(kq):
+    k = torch.zeros(1, 2, 64, D, dtype=torch.float16, device="cuda")
+    dc = kq.DeviceCache(kq.make_config("fp8", num_kv_heads=2, capacity=64))
+    dc.prefill(k, k)
+    assert not _np(dc.view("k_codes")).any()
+    assert np.all(_np(dc.view("tensor_scale"))[:2] == 0)
+    out = dc.decode(synth.make_q(1, 2, D, device="cuda"))
+    assert np.all(_np(out) == 0)
+
+
+@pytest.mark.parametrize("B,H,Hq,S", [(2, 4, 16, 1000), (1, 1, 2, 31)])
+def test_fp16_decode(kq, B, H, Hq, S):
+    k, v = _kv(B, H, S)
+    dc = kq.DeviceCache(kq.make_config("fp16", batch=B, num_kv_heads=H, capacity=S + 3))
+    dc.prefill(k, v)
+    oc = ocache.Fp16Cache(B, H, D, S + 3)
+    oc.prefill(_np(k), _np(v))
+    q = synth.make_q(B, Hq, D, device="cuda")
+    assert _att_err(_np(dc.decode(q)), oc.attention(_np(q))) <= ATOL
+
+
+# -------------------------------------------- full-size workloads, sampled ---
+
+def _oracle_blocks_kivi(k, v, blocks, bits, R, C, S):
+    """Oracle cache over the sampled (b, h) blocks only (B = len(blocks), H = 1)."""
+    kb = np.stack([_np(k[b, h, :S]) for b, h in blocks])[:, None]
+    vb = np.stack([_np(v[b, h, :S]) for b, h in blocks])[:, None]
+    oc = ocache.KiviCache(len(blocks), 1, D, bits, 32, R, C)
+    oc.prefill(kb, vb)
+    return oc
+
+
+def _sampled_attention_check(out, q, oc, blocks, nq):
+    """Max abs error of the query heads of each sampled (b, h) block against
+    the oracle's attention over that block."""
+    from oracle import attention
+    Kh, Vh = oc.dequantized()
+    on, qn = _np(out), _np(q)
+    worst = 0.0
+    for i, (b, h) in enumerate(blocks):
+        ref = attention.decode_attention(qn[b:b + 1, h * nq:(h + 1) * nq],
+                                         Kh[i:i + 1], Vh[i:i + 1])
+        worst = max(worst, _att_err(on[b:b + 1, h * nq:(h + 1) * nq], ref))
+    return worst
+
+
+def test_gqa70b_32k_stream_sampled(kq):
+    """64 query / 8 KV heads, B=16, S=32768, KIVI 2-bit; prefill then 256
+    appends with attention. Sampled (b, h) blocks are checked bit-exact and
+    their query heads' outputs against the oracle along the stream."""
+    cfg = synth.CONFIGS["gqa70b_32k"]
+    B, H, Hq, S, steps = (cfg["batch"], cfg["num_kv_heads"], cfg["num_q_heads"],
+                          cfg["seq_len"], cfg["decode_steps"])
+    C = S + steps
+    nq = Hq // H
+    blocks = [(0, 0), (7, 3), (15, 7)]
+    _say(f"[gqa70b_32k] B={B} H={H} Hq={Hq} S={S} steps={steps}")
+    k, v = _kv(B, H, C)
+    dc = kq.DeviceCache(kq.make_config("kivi", bits=2, batch=B, num_kv_heads=H, capacity=C))
+    dc.prefill(k[:, :, :S].contiguous(), v[:, :, :S].contiguous())
+    oc = _oracle_blocks_kivi(k, v, blocks, 2, 128, C, S)
+    torch.cuda.synchronize()
+    _compare_kivi_state(dc, oc, blocks)
+    ws = dc.make_workspace(Hq)
+    kb = np.stack([_np(k[b, h]) for b, h in blocks])[:, None]
+    vb = np.stack([_np(v[b, h]) for b, h in blocks])[:, None]
+    check_at = {1, 2, 64, 128, 129, 130, 200, 256}
+    worst = 0.0
+    for i in range(1, steps + 1):
+        t = S + i - 1
+        dc.append(k[:, :, t].contiguous(), v[:, :, t].contiguous())
+        oc.append(kb[:, :, t], vb[:, :, t])
+        assert (dc.n_quant, dc.n_resid) == (oc.n_quant, oc.n_resid)
+        q = synth.make_q(B, Hq, D, step=i, device="cuda")
+        out = dc.decode(q, workspace=ws)
+        if i in check_at:
+            worst = max(worst, _sampled_attention_check(out, q, oc, blocks, nq))
+    torch.cuda.synchronize()
+    assert oc.flush_steps == [1, 129] and (dc.n_quant, dc.n_resid) == (32896, 128)
+    _compare_kivi_state(dc, oc, blocks)
+    _say(f"  worst sampled max abs err {worst:.3e}")
+    assert worst <= ATOL
+
+
+def test_mha_large_batch_4bit_sampled(kq):
+    cfg = synth.CONFIGS["mha_large_batch_4bit"]
+    B, H, Hq, S = cfg["batch"], cfg["num_kv_heads"], cfg["num_q_heads"], cfg["seq_len"]
+    blocks = [(0, 0), (31, 17), (63, 31)]
+    _say(f"[mha_large_batch_4bit] B={B} H={H} S={S}")
+    k, v = _kv(B, H, S)
+    dc = kq.DeviceCache(kq.make_config("kivi", bits=4, batch=B, num_kv_heads=H, capacity=S))
+    dc.prefill(k, v)
+    oc = _oracle_blocks_kivi(k, v, blocks, 4, 128, S, S)
+    torch.cuda.synchronize()
+    _compare_kivi_state(dc, oc, blocks)
+    q = synth.make_q(B, Hq, D, device="cuda")
+    out = dc.decode(q)
+    err = _sampled_attention_check(out, q, oc, blocks, 1)
+    _say(f"  sampled max abs err {err:.3e}")
+    assert err <= ATOL
+
+
+@pytest.fixture(scope="module")
+def kv_128k():
+    cfg = synth.CONFIGS["gqa_128k"]
+    B, H, S = cfg["batch"], cfg["num_kv_heads"], cfg["seq_len"]
+    return _kv(B, H, S)
+
+
+def test_gqa_128k_kivi_sampled(kq, kv_128k):
+    cfg = synth.CONFIGS["gqa_128k"]
+    B, H, Hq, S = cfg["batch"], cfg["num_kv_heads"], cfg["num_q_heads"], cfg["seq_len"]
+    k, v = kv_128k
+    blocks = [(0, 0), (2, 5), (3, 7)]
+    dc = kq.DeviceCache(kq.make_config("kivi", bits=2, batch=B, num_kv_heads=H, capacity=S))
+    dc.prefill(k, v)
+    oc = _oracle_blocks_kivi(k, v, blocks, 2, 128, S, S)
+    torch.cuda.synchronize()
+    _compare_kivi_state(dc, oc, blocks)
+    q = synth.make_q(B, Hq, D, device="cuda")
+    err = _sampled_attention_check(dc.decode(q), q, oc, blocks, Hq // H)
+    _say(f"[gqa_128k kivi] sampled max abs err {err:.3e}")
+    assert err <= ATOL
+
+
+def test_gqa_128k_fp8_sampled(kq, kv_128k):
+    cfg = synth.CONFIGS["gqa_128k"]
+    B, H, Hq, S = cfg["batch"], cfg["num_kv_heads"], cfg["num_q_heads"], cfg["seq_len"]
+    k, v = kv_128k
+    dc = kq.DeviceCache(kq.make_config("fp8", batch=B, num_kv_heads=H, capacity=S))
+    dc.prefill(k, v)
+    sk, sv = ofp8.tensor_scale(_np(k)), ofp8.tensor_scale(_np(v))   # whole-tensor amax
+    ts = _np(dc.view("tensor_scale"))
+    assert ts[0] == sk and ts[1] == sv
+    nq = Hq // H
+    q = synth.make_q(B, Hq, D, device="cuda")
+    out = _np(dc.decode(q))
+    from oracle import attention
+    worst = 0.0
+    for b, h in [(0, 0), (1, 4), (3, 7)]:
+        kc = ofp8.quantize(_np(k[b, h]), sk)
+        vc = ofp8.quantize(_np(v[b, h]), sv)
+        assert np.array_equal(_np(dc.view("k_codes")[b, h]), kc)
+        assert np.array_equal(_np(dc.view("v_codes")[b, h]), vc)
+        ref = attention.decode_attention(_np(q)[b:b + 1, h * nq:(h + 1) * nq],
+                                         ofp8.dequantize(kc, sk)[None, None],
+                                         ofp8.dequantize(vc, sv)[None, None])
+        worst = max(worst, _att_err(out[b:b + 1, h * nq:(h + 1) * nq], ref))
+    _say(f"[gqa_128k fp8] sampled max abs err {worst:.3e}")
+    assert worst <= ATOL
+
+
+def test_gqa_128k_fp16_sampled(kq, kv_128k):
+    cfg = synth.CONFIGS["gqa_128k"]
+    B, H, Hq, S = cfg["batch"], cfg["num_kv_heads"], cfg["num_q_heads"], cfg["seq_len"]
+    k, v = kv_128k
+    dc = kq.DeviceCache(kq.make_config("fp16", batch=B, num_kv_heads=H, capacity=S))
+    dc.prefill(k, v)
+    nq = Hq // H
+    q = synth.make_q(B, Hq, D, device="cuda")
+    out = _np(dc.decode(q))
+    from oracle import attention
+    worst = 0.0
+    for b, h in [(0, 0), (3, 6)]:
+        ref = attention.decode_attention(_np(q)[b:b + 1, h * nq:(h + 1) * nq],
+                                         _np(k[b:b + 1, h:h + 1]), _np(v[b:b + 1, h:h + 1]))
+        worst = max(worst, _att_err(out[b:b + 1, h * nq:(h + 1) * nq], ref))
+    _say(f"[gqa_128k fp16] sampled max abs err {worst:.3e}")
+    assert worst <= ATOL
