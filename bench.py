@@ -1,0 +1,343 @@
+#!/usr/bin/env python
+"""Benchmark of the KIVI decode hot path on one MI355X.
+
+Workload (the 70B-style GQA layer at 32K context): B=16, 64 query heads,
+8 KV heads, D=128, KIVI 2-bit K and V, G=32, R=128. The 32768-token prefill is
+quantized once before timing; a step is one streamed decode step: append one
+token per (b, KV head) — with the lazy window flush when due, every 128
+appends — then decode attention of one query per head over the whole cache.
+Inputs are seeded synthetic tensors (synth), resident in HBM before timing.
+
+Printed (one JSON line): value = effective KV GB/s of the timed steps
+(Σ algorithmic decode bytes / wall time of the timed region, HIP events on the
+launch stream); roofline of the dominant kernel (decode attention, events
+around each decode launch); the CPU oracle on a bounded sample of the same
+workload; extra per-workload figures for the other configurations.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
+D = 128
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_gqa70b_32k_counters.json")
+
+
+def _log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("kvq_decode.hip", "kvq_internal.h", "kvq_api.cpp"):
+        with open(os.path.join(ROOT, "kv_cache_quantization_quant_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_counters():
+    """HBM bytes per decode launch from committed rocprofv3 PMC runs, scaled by
+    the same counters' reading for a copy of known size; None when absent or
+    taken on a different decode kernel source."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("decode_source_hash") != decode_source_hash():
+        return None
+    return c.get("traffic_bytes_per_launch")
+
+
+class Scrub:
+    """A 1 GiB buffer written between timed launches where the Infinity Cache
+    (256 MB) must not serve the next launch."""
+
+    def __init__(self, torch):
+        self.buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        self.i = 0
+
+    def __call__(self):
+        self.i += 1
+        self.buf.fill_(float(self.i))
+
+
+def time_launches(torch, fn, iters, scrub=None):
+    """Durations (µs) of `fn` launches measured with events on the current stream."""
+    out = []
+    for _ in range(iters):
+        if scrub is not None:
+            scrub()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        out.append((e0, e1))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e3 for a, b in out]
+
+
+def quantize_traffic_bytes(B, H, S, bits, n_quant, n_resid):
+    """Bytes a KIVI prefill must move: read fp16 K and V, write codes, fp32
+    scale/zero and the fp16 window."""
+    read = 2 * B * H * S * D * 2
+    ng = n_quant // 32
+    write = B * H * (2 * n_quant * D * bits // 8 + ng * D * 8 + n_quant * 8 + 2 * n_resid * D * 2)
+    return read + write
+
+
+def run_main(torch, kq, synth, args):
+    cfg = synth.CONFIGS["gqa70b_32k"]
+    B, H, Hq, S, bits = (cfg["batch"], cfg["num_kv_heads"], cfg["num_q_heads"],
+                         cfg["seq_len"], cfg["bits"])
+    n_steps = args.warmup + args.steps
+    C = S + n_steps
+    _log(f"[bench] gqa70b_32k: B={B} Hq={Hq} H={H} S={S} KIVI {bits}-bit, "
+         f"warmup={args.warmup} steps={args.steps}")
+    t0 = time.time()
+    k = synth.make_k(B, H, 0, C, D, device="cuda")
+    v = synth.make_v(B, H, 0, C, D, device="cuda")
+    kp, vp = k[:, :, :S].contiguous(), v[:, :, :S].contiguous()
+    k_new = [k[:, :, S + i].contiguous() for i in range(n_steps)]
+    v_new = [v[:, :, S + i].contiguous() for i in range(n_steps)]
+    qs = [synth.make_q(B, Hq, D, step=i, device="cuda") for i in range(n_steps)]
+    del k, v
+    torch.cuda.synchronize()
+    _log(f"[bench] inputs generated in {time.time() - t0:.1f}s")
+
+    dc = kq.DeviceCache(kq.make_config("kivi", bits=bits, batch=B, num_kv_heads=H, capacity=C))
+    ws = dc.make_workspace(Hq)
+    out = torch.empty_like(qs[0])
+
+    # prefill quantize throughput (reset + prefill, median of 5)
+    def prefill():
+        dc.reset()
+        dc.prefill(kp, vp)
+    prefill()
+    pre_us = statistics.median(time_launches(torch, prefill, 5))
+    q_bytes = quantize_traffic_bytes(B, H, S, bits, dc.n_quant, dc.n_resid)
+
+    for i in range(args.warmup):
+        dc.append(k_new[i], v_new[i])
+        dc.decode(qs[i], out=out, workspace=ws)
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    step_bytes = []
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for j in range(args.steps):
+        i = args.warmup + j
+        dc.append(k_new[i], v_new[i])
+        step_bytes.append(dc.decode_bytes(Hq))
+        ev[j][0].record()
+        dc.decode(qs[i], out=out, workspace=ws)
+        ev[j][1].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    dec_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    total_bytes = sum(step_bytes)
+    value = total_bytes / (total_ms * 1e-3) / 1e9
+    mean_dec_us = sum(dec_us) / len(dec_us)
+    achieved = (total_bytes / len(step_bytes)) / (mean_dec_us * 1e-6) / 1e9
+
+    # decode launches with the Infinity Cache scrubbed before each one
+    scrub = Scrub(torch)
+    cold = time_launches(torch, lambda: dc.decode(qs[-1], out=out, workspace=ws), 20, scrub)
+    cold_med = statistics.median(cold)
+    bytes_now = dc.decode_bytes(Hq)
+
+    res = {
+        "B": B, "Hq": Hq, "H": H, "S": S, "bits": bits,
+        "total_ms": total_ms, "wall_s": wall, "ms_per_step": total_ms / args.steps,
+        "value": value, "mean_decode_us": mean_dec_us,
+        "p50_decode_us": statistics.median(dec_us),
+        "p95_decode_us": sorted(dec_us)[int(0.95 * (len(dec_us) - 1))],
+        "decode_bytes_per_launch": total_bytes / len(step_bytes),
+        "achieved_gbs": achieved,
+        "cold_decode_us_p50": cold_med,
+        "cold_decode_gbs": bytes_now / (cold_med * 1e-6) / 1e9,
+        "prefill_quantize_us": pre_us,
+        "prefill_quantize_gbs": q_bytes / (pre_us * 1e-6) / 1e9,
+        "final_state": [dc.n_quant, dc.n_resid],
+    }
+    return res
+
+
+def run_extra(torch, kq, synth):
+    """Decode (Infinity Cache scrubbed) and prefill figures of the other
+    workloads, one decode step each."""
+    scrub = Scrub(torch)
+    out = {}
+    plan = [("llama2_7b_layer", "kivi"), ("mha_large_batch_4bit", "kivi"),
+            ("gqa_128k", "fp16"), ("gqa_128k", "fp8"), ("gqa_128k", "kivi")]
+    kv_cache = {}
+    for name, fmt in plan:
+        c = synth.CONFIGS[name]
+        B, H, Hq, S = c["batch"], c["num_kv_heads"], c["num_q_heads"], c["seq_len"]
+        if name not in kv_cache:
+            kv_cache.clear()
+            torch.cuda.empty_cache()
+            kv_cache[name] = (synth.make_k(B, H, 0, S, D, device="cuda"),
+                              synth.make_v(B, H, 0, S, D, device="cuda"))
+        k, v = kv_cache[name]
+        bits = c["bits"] if fmt == "kivi" else None
+        dc = kq.DeviceCache(kq.make_config(fmt, bits=bits, batch=B, num_kv_heads=H,
+                                           capacity=S))
+
+        def prefill():
+            dc.reset()
+            dc.prefill(k, v)
+        prefill()
+        pre = statistics.median(time_launches(torch, prefill, 3, scrub))
+        q = synth.make_q(B, Hq, D, device="cuda")
+        ws = dc.make_workspace(Hq)
+        o = torch.empty_like(q)
+        dec = statistics.median(time_launches(
+            torch, lambda: dc.decode(q, out=o, workspace=ws), 10, scrub))
+        nbytes = dc.decode_bytes(Hq)
+        out[f"{name}/{fmt}"] = {
+            "decode_us": round(dec, 2), "decode_bytes": nbytes,
+            "decode_gbs": round(nbytes / (dec * 1e-6) / 1e9, 1),
+            "decode_frac_hbm": round(nbytes / (dec * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "prefill_us": round(pre, 1)}
+        del dc, ws
+        _log(f"[bench] extra {name}/{fmt}: {out[f'{name}/{fmt}']}")
+    kv_cache.clear()
+    torch.cuda.empty_cache()
+    return out
+
+
+def _cuda_ok():
+    import torch
+    return torch.cuda.is_available()
+
+
+def run_cpu_baseline(synth):
+    """The oracle on a bounded sample of the same workload: 8 of the 128
+    (b, KV head) blocks, prefill-quantized, then 8 decode steps each
+    (append + dequantize + fp64 attention of the block's 8 query heads), on one
+    host thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import bytes_model, cache as ocache
+
+    cfg = synth.CONFIGS["gqa70b_32k"]
+    B, H, Hq, S = cfg["batch"], cfg["num_kv_heads"], cfg["num_q_heads"], cfg["seq_len"]
+    nq = Hq // H
+    blocks = [(b, h) for b in (0, 5, 10, 15) for h in (0, 7)]
+    steps = 8
+    with threadpool_limits(limits=1):
+        dev = "cuda" if _cuda_ok() else "cpu"
+        kb = np.stack([synth.make_k(1, H, 0, S + steps, D, device=dev, b0=b)[0, h].cpu().numpy()
+                       for b, h in blocks])
+        vb = np.stack([synth.make_v(1, H, 0, S + steps, D, device=dev, b0=b)[0, h].cpu().numpy()
+                       for b, h in blocks])
+        q = synth.make_q(B, Hq, D, step=0).numpy()
+        t0 = time.perf_counter()
+        oc = ocache.KiviCache(len(blocks), 1, D, 2, 32, 128, S + steps)
+        oc.prefill(kb[:, None, :S], vb[:, None, :S])
+        t_pre = time.perf_counter() - t0
+        nbytes = 0
+        t0 = time.perf_counter()
+        for i in range(steps):
+            oc.append(kb[:, None, S + i], vb[:, None, S + i])
+            qs = np.stack([q[b, h * nq:(h + 1) * nq] for b, h in blocks])   # [8 blocks, nq, D]
+            Kh, Vh = oc.dequantized()
+            from oracle import attention
+            for j in range(len(blocks)):
+                attention.decode_attention(qs[j:j + 1], Kh[j:j + 1], Vh[j:j + 1])
+            nbytes += bytes_model.decode_bytes_kivi(len(blocks), 1, D, 2, 32, oc.n_quant,
+                                                    oc.n_resid)
+        t_dec = time.perf_counter() - t0
+    return {"value": round(nbytes / t_dec / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": (f"{len(blocks)} of {B * H} (b, KV head) blocks of the 32K GQA layer, "
+                       f"{steps} decode steps each (append + dequantize + fp64 attention of "
+                       f"{nq} query heads); prefill quantize of those blocks took "
+                       f"{t_pre:.2f}s; decode {t_dec:.2f}s"),
+            "decode_s_per_block_step": round(t_dec / (steps * len(blocks)), 4)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU only; the path runs on a "
+                          "single MI355X and has no multi-GPU mode (--gpus 1)"}))
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be ≥ 1 and --warmup ≥ 0")
+
+    import torch
+
+    import kv_cache_quantization_quant_amd as kq
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    torch.cuda.set_device(0)
+    main_res = run_main(torch, kq, synth, args)
+    extra = None if args.no_extra else run_extra(torch, kq, synth)
+    cpu = None if args.no_cpu_baseline else run_cpu_baseline(synth)
+
+    traffic = traffic_from_counters()
+    achieved = main_res["achieved_gbs"]
+    line = {
+        "metric": "decode attention effective KV GB/s (% of HBM peak) and µs/step at B×S",
+        "value": round(main_res["value"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u2-codes/fp32",
+        "data": "synthetic (seeded Threefry: K channel-lognormal with 2 x10 outlier channels "
+                "per KV head, V token-lognormal, q N(0,1))",
+        "config": {"workload": "gqa70b_32k: 64 query / 8 KV heads, D=128, B=16, S=32768 "
+                               "(+ streamed tokens), KIVI 2-bit K per-channel / V per-token, "
+                               "G=32, R=128; step = append (+flush every 128) + decode",
+                   "global_batch": main_res["B"], "seq_len": main_res["S"],
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "decode attention (split + merge launches)",
+                     "bytes_per_launch": int(main_res["decode_bytes_per_launch"]),
+                     "mean_launch_us": round(main_res["mean_decode_us"], 3)},
+        "cpu_baseline": cpu,
+        "details": {k: (round(v, 3) if isinstance(v, float) else v)
+                    for k, v in main_res.items()},
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

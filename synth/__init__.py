@@ -116,29 +116,31 @@ def _token_index(b: int, H: int, t0: int, t1: int, device):
 
 
 def make_k(batch: int, num_kv_heads: int, t0: int, t1: int, head_dim: int,
-           seed: int = 0, device="cpu") -> torch.Tensor:
-    """fp16 K for tokens [t0, t1): shape [B, H, t1 - t0, D]."""
+           seed: int = 0, device="cpu", b0: int = 0) -> torch.Tensor:
+    """fp16 K for tokens [t0, t1) of batch elements [b0, b0 + B):
+    shape [B, H, t1 - t0, D]."""
     assert 0 <= t0 <= t1 < (1 << _TOKEN_BITS)
     f = k_channel_factors(num_kv_heads, head_dim, seed, device)
     out = torch.empty(batch, num_kv_heads, t1 - t0, head_dim,
                       dtype=torch.float16, device=device)
     d = torch.arange(head_dim, dtype=torch.int64, device=device)
     for b in range(batch):
-        tok = _token_index(b, num_kv_heads, t0, t1, device)
+        tok = _token_index(b0 + b, num_kv_heads, t0, t1, device)
         idx = tok[:, :, None] * head_dim + d
         out[b] = _to_fp16(normal(seed, STREAM_K, idx) * f[:, None, :])
     return out
 
 
 def make_v(batch: int, num_kv_heads: int, t0: int, t1: int, head_dim: int,
-           seed: int = 0, device="cpu") -> torch.Tensor:
-    """fp16 V for tokens [t0, t1): shape [B, H, t1 - t0, D]."""
+           seed: int = 0, device="cpu", b0: int = 0) -> torch.Tensor:
+    """fp16 V for tokens [t0, t1) of batch elements [b0, b0 + B):
+    shape [B, H, t1 - t0, D]."""
     assert 0 <= t0 <= t1 < (1 << _TOKEN_BITS)
     out = torch.empty(batch, num_kv_heads, t1 - t0, head_dim,
                       dtype=torch.float16, device=device)
     d = torch.arange(head_dim, dtype=torch.int64, device=device)
     for b in range(batch):
-        tok = _token_index(b, num_kv_heads, t0, t1, device)
+        tok = _token_index(b0 + b, num_kv_heads, t0, t1, device)
         g = torch.exp(0.5 * normal(seed, STREAM_VF, tok))
         idx = tok[:, :, None] * head_dim + d
         out[b] = _to_fp16(normal(seed, STREAM_V, idx) * g[:, :, None])
