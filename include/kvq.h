@@ -86,8 +86,10 @@
  *   k_codes  uint32 [B][H][CT][D·b/32]   token t of (b,h): its D channel codes,
  *            code of channel d in word d/(32/b) at bits [b·(d%(32/b)), +b).
  *   v_codes  uint32 [B][H][NG][D][G·b/32] group g, channel d: the G token
- *            codes of that channel, token j of the group in word j/(32/b) at
- *            bits [b·(j%(32/b)), +b).
+ *            codes of that channel, 32/b tokens per word (token j of the
+ *            group in word j/(32/b)); with i = j % (32/b), the code sits at
+ *            bits [b·(i/2), +b) when i is even and [16 + b·(i/2), +b) when i
+ *            is odd (even tokens fill the low half-word, odd the high).
  *   k_scale, k_zero  fp32 [B][H][NG][D]   (per group, per channel)
  *   v_scale, v_zero  fp32 [B][H][CT]      (per token)
  *   k_resid, v_resid fp16 [B][H][Rcap][D] the FP16 residual window; slot i

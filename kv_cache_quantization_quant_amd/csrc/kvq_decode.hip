@@ -204,7 +204,7 @@ __device__ __forceinline__ void process_tile(const DecodeArgs& a, Smem<NQ>& sm,
       for (int tt = tb; tt < tb + 8; ++tt) {
         const float s = sm.vsz[wave][0][tt];
         const float z = sm.vsz[wave][1][tt];
-        const int sh = BITS * (tt % PER);
+        const int sh = BITS * ((tt % PER) / 2) + 16 * ((tt % PER) % 2);
         const float v0 = float((w0[tt / PER] >> sh) & MASK) * s + z;
         const float v1 = float((w1[tt / PER] >> sh) & MASK) * s + z;
 #pragma unroll

@@ -138,14 +138,16 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
     *reinterpret_cast<uint2*>(kdst + 2 * j) = make_uint2(w0, w1);
   }
 
-  // ---- V codes: per channel, the group's 32 token codes packed along tokens.
+  // ---- V codes: per channel, the group's 32 token codes packed along tokens;
+  // within a word, even tokens fill the low half-word and odd tokens the high.
   uint32_t* vdst = a.v_codes + (bh * a.NG + gg) * kHeadDim * VW;
   for (int idx = tid; idx < kHeadDim * VW; idx += kThreads) {
     const int d = idx / VW;
     const int w = idx % VW;
     uint32_t word = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) word |= uint32_t(vcode[d][w * PER + i]) << (BITS * i);
+    for (int i = 0; i < PER; ++i)
+      word |= uint32_t(vcode[d][w * PER + i]) << (BITS * (i / 2) + 16 * (i % 2));
     vdst[idx] = word;
   }
 }

@@ -19,10 +19,12 @@ offset (z = mn, i.e. the integer-domain zero-point of the page formula is
              code = 0 for a constant group (s = 0)
     x̂      = float(code) · s + mn      (two roundings, no fused multiply-add)
 
-Packing (layout of the device buffers; little-endian bit order, element i of a
-32-bit word at bits [b·i, b·i + b)):
-  K: per token, its D channel codes packed along the channel axis.
-  V: per group and channel, the G token codes packed along the token axis.
+Packing (layout of the device buffers; little-endian bit order):
+  K: per token, its D channel codes packed along the channel axis; channel
+     i of a word (32/b channels per word) at bits [b·i, b·i + b).
+  V: per group and channel, the G token codes packed along the token axis,
+     32/b tokens per word; token j of a word sits in the low 16 bits when j is
+     even and in the high 16 bits when j is odd, at bit b·(j // 2) of its half.
 """
 from __future__ import annotations
 
@@ -128,6 +130,11 @@ def unpack_k(words: np.ndarray, bits: int, head_dim: int) -> np.ndarray:
     return out.reshape(T, head_dim)
 
 
+def _v_bit(j: int, bits: int) -> int:
+    """Bit offset of token j of a V word: even tokens low half, odd high half."""
+    return bits * (j // 2) + 16 * (j % 2)
+
+
 def pack_v(codes: np.ndarray, bits: int, group: int) -> np.ndarray:
     """V codes [T, D] (T a multiple of G) → uint32 [T/G, D, G·b/32], each
     channel's G token codes of a group packed along tokens."""
@@ -136,8 +143,8 @@ def pack_v(codes: np.ndarray, bits: int, group: int) -> np.ndarray:
     c = codes.astype(np.uint32).reshape(T // group, group, D).transpose(0, 2, 1)
     c = c.reshape(T // group, D, group // per, per)
     words = np.zeros((T // group, D, group // per), np.uint32)
-    for i in range(per):
-        words |= c[..., i] << np.uint32(bits * i)
+    for j in range(per):
+        words |= c[..., j] << np.uint32(_v_bit(j, bits))
     return words
 
 
@@ -146,6 +153,6 @@ def unpack_v(words: np.ndarray, bits: int, group: int) -> np.ndarray:
     per = 32 // bits
     mask = np.uint32(2 ** bits - 1)
     out = np.empty((ng, D, group // per, per), np.uint8)
-    for i in range(per):
-        out[..., i] = (words >> np.uint32(bits * i)) & mask
+    for j in range(per):
+        out[..., j] = (words >> np.uint32(_v_bit(j, bits))) & mask
     return out.reshape(ng, D, group).transpose(0, 2, 1).reshape(ng * group, D)

@@ -223,6 +223,13 @@ def test_pack_v_golden(words):
     assert w.shape == (1, 128, 2)
     assert int(w[0, 3, 0]) == int(e["word_hex"], 16)
     assert np.count_nonzero(w) == 1
+    e = words["v_4bit_channel_tokens_0_to_7"]
+    codes = np.zeros((32, 128), np.uint8)
+    codes[8:16, 5] = e["codes_by_token"]                 # channel 5, tokens 8..15: word 1
+    w = kivi.pack_v(codes, 4, 32)
+    assert w.shape == (1, 128, 4)
+    assert int(w[0, 5, 1]) == int(e["word_hex"], 16)
+    assert np.count_nonzero(w) == 1
 
 
 @pytest.mark.parametrize("bits", [2, 4])
