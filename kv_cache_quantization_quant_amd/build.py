@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libkvq.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["kvq_api.cpp", "kvq_quant.hip", "kvq_decode.hip"]
+SOURCES = ["kvq_api.cpp", "kvq_quant.hip", "kvq_decode.hip", "kvq_decode_mfma.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

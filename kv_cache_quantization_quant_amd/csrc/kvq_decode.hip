@@ -247,7 +247,7 @@ __device__ __forceinline__ void process_tile(const DecodeArgs& a, Smem<NQ>& sm,
 template <int SRC, int NQ>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   __shared__ Smem<NQ> sm;
-  const int split = blockIdx.x;
+  const int split = int(blockIdx.x) + a.split_offset;
   const int bh = blockIdx.y;
   const int b = bh / a.H;
   const int h_kv = bh % a.H;
@@ -344,8 +344,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
 }
 
 template <int SRC>
-hipError_t launch_src(const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid(a.n_split, a.B * a.H, a.nq / a.heads_per_chunk);
+hipError_t launch_src(const DecodeArgs& a, int n_splits, hipStream_t s) {
+  const dim3 grid(n_splits, a.B * a.H, a.nq / a.heads_per_chunk);
   switch (a.heads_per_chunk) {
     case 1: decode_split_kernel<SRC, 1><<<grid, kThreads, 0, s>>>(a); break;
     case 2: decode_split_kernel<SRC, 2><<<grid, kThreads, 0, s>>>(a); break;
@@ -358,14 +358,32 @@ hipError_t launch_src(const DecodeArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
-  hipError_t e;
+// KIVI: the grouped region on the matrix cores, the FP16 window (one extra
+// split) on the vector path; FP8 / FP16: every split on the vector path.
+// Then the split merge.
+hipError_t launch_decode(const DecodeArgs& a_in, hipStream_t s) {
+  DecodeArgs a = a_in;
+  hipError_t e = hipSuccess;
   switch (a.src) {
-    case kSrcFp16: e = launch_src<kSrcFp16>(a, s); break;
-    case kSrcFp8: e = launch_src<kSrcFp8>(a, s); break;
-    case kSrcKivi2: e = launch_src<kSrcKivi2>(a, s); break;
-    case kSrcKivi4: e = launch_src<kSrcKivi4>(a, s); break;
-    default: return hipErrorInvalidValue;
+    case kSrcKivi2:
+    case kSrcKivi4:
+      a.split_offset = 0;
+      e = launch_kivi_mfma(a, s);
+      if (e == hipSuccess && a.n_split > a.n_split_main) {
+        a.split_offset = a.n_split_main;
+        e = a.src == kSrcKivi2 ? launch_src<kSrcKivi2>(a, 1, s) : launch_src<kSrcKivi4>(a, 1, s);
+      }
+      break;
+    case kSrcFp16:
+      a.split_offset = 0;
+      e = launch_src<kSrcFp16>(a, a.n_split, s);
+      break;
+    case kSrcFp8:
+      a.split_offset = 0;
+      e = launch_src<kSrcFp8>(a, a.n_split, s);
+      break;
+    default:
+      return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
   decode_merge_kernel<<<a.B * a.Hq, 64, 0, s>>>(a);

@@ -88,6 +88,7 @@ struct DecodeArgs {
   int tiles_per_split;
   int n_split_main;       // splits over the main region
   int n_split;            // n_split_main (+1 if the window is non-empty)
+  int split_offset;       // first split index a launch covers (grid.x from here)
   const float* q;         // [B][Hq][D]
   float* out;             // [B][Hq][D]
   float* ws;              // [B][Hq][n_split][D + 2]
@@ -99,5 +100,6 @@ hipError_t launch_copy_tokens(const CopyTokensArgs& a, hipStream_t s);
 hipError_t launch_fp8_prefill(const Fp8QuantArgs& a, hipStream_t s);
 hipError_t launch_fp8_append(const Fp8QuantArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t s);
 
 }  // namespace kvq
