@@ -28,6 +28,8 @@ COMMON = [
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     # no packed-FP32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs (no AGPR copies around VALU work)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"),
 ]

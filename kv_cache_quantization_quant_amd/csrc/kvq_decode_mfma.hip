@@ -54,6 +54,12 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // value of lane l ^ 8 (rotate by 8 inside each row of 16 lanes)
 __device__ __forceinline__ float xor8(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
@@ -75,15 +81,28 @@ __device__ __forceinline__ float head_max(float x) {
   return x;
 }
 
-__device__ __forceinline__ uint32_t f16_bits(float x) {
-  return uint32_t(__builtin_bit_cast(unsigned short, (_Float16)x));
+// {f16(a0·b0), f16(a1·b1)}: fp32 products rounded once to fp16, packed.
+__device__ __forceinline__ uint32_t mix_pair(float a0, float b0, float a1, float b1) {
+  uint32_t d;
+  asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,0,0]" : "=v"(d) : "v"(a0), "v"(b0));
+  asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel_hi:[0,0,0]" : "+v"(d) : "v"(a1), "v"(b1));
+  return d;
 }
-// fp16 high + low split of x; returns the requested term's bits.
-__device__ __forceinline__ uint32_t split_f16(float x, bool low) {
-  const _Float16 hi = (_Float16)x;
-  const float rest = x - (float)hi;
-  return low ? uint32_t(__builtin_bit_cast(unsigned short, (_Float16)rest))
-             : uint32_t(__builtin_bit_cast(unsigned short, hi));
+// {f16(a0·b0 − c.lo), f16(a1·b1 − c.hi)} with c an fp16 pair; each term is a
+// fused fp32 multiply-subtract rounded once to fp16.
+__device__ __forceinline__ uint32_t mix_pair_sub(float a0, float b0, float a1, float b1,
+                                                 uint32_t c) {
+  uint32_t d;
+  asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel_hi:[0,0,1]" : "=v"(d) : "v"(a0), "v"(b0), "v"(c));
+  asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+      : "+v"(d) : "v"(a1), "v"(b1), "v"(c));
+  return d;
+}
+// (mask & x) | (~mask & y) in one instruction
+__device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t x, uint32_t y) {
+  uint32_t d;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(d) : "v"(mask), "v"(x), "v"(y));
+  return d;
 }
 
 // ---- K code positions (see the header comment). For local k-step sl (0..3)
@@ -129,14 +148,178 @@ __device__ __forceinline__ void k_unpack(const uint32_t* w, u32x4* A) {
   }
 }
 
+// Raw data of one group for one lane (loaded one group ahead).
+template <int BITS>
+struct GroupRegs {
+  uint32_t kw[2][BITS];        // K words of tokens r and 16 + r (32 channels)
+  float4 ksz;                  // 16-byte chunk of the group's K scale | zero block
+  uint32_t vw[8][2];           // V words (tile-0 and tile-1 tokens) of channel 16n + r
+  float vs[4], vz[4];          // V scale / zero of tokens 16·part + 4u + i
+};
+
+template <int BITS>
+__device__ __forceinline__ void load_group(GroupRegs<BITS>& G, const DecodeArgs& a, int bh,
+                                           int64_t g, int lane, int r, int u, bool low) {
+  constexpr int KW = kHeadDim * BITS / 32;
+  constexpr int VW = kGroup * BITS / 32;
+  const int64_t CT = a.main_bh_tokens;
+  const uint32_t* kcodes = static_cast<const uint32_t*>(a.k_main);
+  const uint32_t* vcodes = static_cast<const uint32_t*>(a.v_main);
+#pragma unroll
+  for (int tile = 0; tile < 2; ++tile) {
+    const uint32_t* row = kcodes + (int64_t(bh) * CT + g * kGroup + 16 * tile + r) * KW + BITS * u;
+    if (BITS == 2) {
+      const uint2 x = *reinterpret_cast<const uint2*>(row);
+      G.kw[tile][0] = x.x;
+      G.kw[tile][1] = x.y;
+    } else {
+      const uint4 x = *reinterpret_cast<const uint4*>(row);
+      G.kw[tile][0] = x.x;
+      G.kw[tile][1] = x.y;
+      G.kw[tile][2] = x.z;
+      G.kw[tile][3] = x.w;
+    }
+  }
+  // lanes 0..31: scales 4l..4l+3; lanes 32..63: zero-points
+  const float* meta = (lane < 32 ? a.k_scale : a.k_zero) + (int64_t(bh) * a.NG + g) * kHeadDim;
+  G.ksz = *reinterpret_cast<const float4*>(meta + 4 * (lane & 31));
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const uint32_t* cw = vcodes + ((int64_t(bh) * a.NG + g) * kHeadDim + 16 * n + r) * VW;
+    if (BITS == 2) {
+      const uint2 x = *reinterpret_cast<const uint2*>(cw);
+      G.vw[n][0] = x.x;
+      G.vw[n][1] = x.y;
+    } else {
+      G.vw[n][0] = cw[u / 2];
+      G.vw[n][1] = cw[2 + u / 2];
+    }
+  }
+  const int64_t tok0 = int64_t(bh) * CT + g * kGroup + (low ? 16 : 0) + 4 * u;
+  const float4 s4 = *reinterpret_cast<const float4*>(a.v_scale + tok0);
+  const float4 z4 = *reinterpret_cast<const float4*>(a.v_zero + tok0);
+  G.vs[0] = s4.x; G.vs[1] = s4.y; G.vs[2] = s4.z; G.vs[3] = s4.w;
+  G.vz[0] = z4.x; G.vz[1] = z4.y; G.vz[2] = z4.z; G.vz[3] = z4.w;
+}
+
+// Per-lane state of one wavefront across its groups.
+struct WaveAcc {
+  float m_ref, l_acc, pz_acc;
+  f32x4 cv[8];
+  f32x4 cones;
+};
+
+template <int BITS>
+__device__ __forceinline__ void process_group(const GroupRegs<BITS>& G, WaveAcc& W,
+                                              float* ksz_lds, int lane, int u,
+                                              const float (&qf)[4][8], const float (&qz)[16],
+                                              uint32_t selmask, bool low, uint32_t vsh,
+                                              uint32_t vm0, uint32_t vm1, uint32_t magic) {
+  // ---- stage the group's K scales (ksz_lds[0..127]) and zero-points
+  // (ksz_lds[128..255]) in this wavefront's LDS slot
+  wave_sync();
+  *reinterpret_cast<float4*>(ksz_lds + 4 * lane) = G.ksz;
+  wave_sync();
+  const float* ks = ksz_lds + 32 * u;
+  const float* kz = ksz_lds + 128 + 32 * u + (low ? 16 : 0);
+  // ---- z-term Σ_d q_d·z[g, d] of head hs (8 lanes × 16 channels)
+  float zt = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) zt = fmaf(qz[c], kz[c], zt);
+  zt = head_sum(zt);
+  const float c0 = low ? 0.0f : zt * kTwoM24;
+  f32x4 s0 = f32x4{c0, c0, c0, c0}, s1 = s0;
+  // ---- scores, one k-step (32 channels) at a time
+  u32x4 A0[4], A1[4];
+  k_unpack<BITS>(G.kw[0], A0);
+  k_unpack<BITS>(G.kw[1], A1);
+#pragma unroll
+  for (int sl = 0; sl < 4; ++sl) {
+    uint32_t d[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int j0 = 2 * p, j1 = 2 * p + 1;
+      const float a0 = qf[sl][j0], b0 = ks[k_channel<BITS>(sl, j0)];
+      const float a1 = qf[sl][j1], b1 = ks[k_channel<BITS>(sl, j1)];
+      const uint32_t hi = mix_pair(a0, b0, a1, b1);
+      d[p] = mix_pair_sub(a0, b0, a1, b1, hi & selmask);
+    }
+    const u32x4 bq = u32x4{d[0], d[1], d[2], d[3]};
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(A0[sl]), as_f16x8(bq), s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(A1[sl]), as_f16x8(bq), s1, 0, 0, 0);
+  }
+  // ---- both parts of the head's score; this lane keeps tile `low`
+  float sc[4];                                  // scores × 2^-24
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float send = low ? s0[i] : s1[i];
+    const float mine = low ? s1[i] : s0[i];
+    sc[i] = mine + xor8(send);
+  }
+  // ---- online softmax (log2 domain)
+  const float lmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) * kTwo24;
+  if (__any(lmax > W.m_ref + kLazy)) {           // wave-uniform, rare
+    const float m_new = fmaxf(W.m_ref, head_max(lmax));
+    const float alpha = exp2f(W.m_ref - m_new);
+    W.l_acc *= alpha;
+    W.pz_acc *= alpha;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) W.cv[n] *= alpha;
+    W.cones *= alpha;
+    W.m_ref = m_new;
+  }
+  float pp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float p = exp2f(fmaf(sc[i], kTwo24, -W.m_ref));
+    W.l_acc += p;
+    W.pz_acc = fmaf(p, G.vz[i], W.pz_acc);
+    pp[i] = p * ((BITS == 2 && i >= 2) ? G.vs[i] * 0.25f : G.vs[i]);
+  }
+  // ---- bf16 high / low terms of P' (truncation split), exchanged with lane ^ 8
+  uint32_t keep[2], send[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const float x0 = pp[2 * p], x1 = pp[2 * p + 1];
+    const float l0 = x0 - __uint_as_float(__float_as_uint(x0) & 0xFFFF0000u);
+    const float l1 = x1 - __uint_as_float(__float_as_uint(x1) & 0xFFFF0000u);
+    const uint32_t hpair = __builtin_amdgcn_perm(__float_as_uint(x1), __float_as_uint(x0), 0x07060302u);
+    const uint32_t lpair = __builtin_amdgcn_perm(__float_as_uint(l1), __float_as_uint(l0), 0x07060302u);
+    keep[p] = low ? lpair : hpair;
+    send[p] = low ? hpair : lpair;
+  }
+  const uint32_t recv0 = xor8u(send[0]), recv1 = xor8u(send[1]);
+  const u32x4 bp = low ? u32x4{recv0, recv1, keep[0], keep[1]}
+                       : u32x4{keep[0], keep[1], recv0, recv1};
+  // ---- P·V: 8 tiles of 16 channels, codes in the mantissa of 128.0
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    uint32_t d[4];
+    if (BITS == 2) {
+      const uint32_t w0 = G.vw[n][0] >> vsh, w1 = G.vw[n][1] >> vsh;
+      d[0] = bfi(vm0, w0, magic);
+      d[1] = bfi(vm1, w0, magic);
+      d[2] = bfi(vm0, w1, magic);
+      d[3] = bfi(vm1, w1, magic);
+    } else {
+      d[0] = bfi(vm0, G.vw[n][0] >> vsh, magic);
+      d[1] = bfi(vm0, G.vw[n][0] >> (vsh + 4), magic);
+      d[2] = bfi(vm0, G.vw[n][1] >> vsh, magic);
+      d[3] = bfi(vm0, G.vw[n][1] >> (vsh + 4), magic);
+    }
+    W.cv[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{d[0], d[1], d[2], d[3]}),
+                                                       as_bf16x8(bp), W.cv[n], 0, 0, 0);
+  }
+  const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  W.cones = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ones), as_bf16x8(bp), W.cones,
+                                                    0, 0, 0);
+}
+
 template <int BITS>
 __global__ __launch_bounds__(kThreads) void kivi_mfma_split_kernel(DecodeArgs a) {
-  constexpr int KW = kHeadDim * BITS / 32;     // K words per token
-  constexpr int VW = kGroup * BITS / 32;       // V words per (group, channel)
-  constexpr int LW = 32 * BITS / 32;           // K words per lane (32 channels)
-
   __shared__ float mo[kWaves][8][kHeadDim];
   __shared__ float ml[kWaves][8][2];
+  __shared__ float ksz_slot[kWaves][2 * kHeadDim];
 
   const int split = blockIdx.x;
   const int bh = blockIdx.y;
@@ -151,7 +334,6 @@ __global__ __launch_bounds__(kThreads) void kivi_mfma_split_kernel(DecodeArgs a)
   const int u = lane >> 4;
   const int hs = r & 7;
   const bool low = r >= 8;
-  const int64_t CT = a.main_bh_tokens;
 
   // ---- per-lane constants: this lane's 32 channels [32u, 32u+32) of head hs
   float qf[4][8];          // q_d·log2e/√D / f, by (k-step, k-slot)
@@ -165,195 +347,58 @@ __global__ __launch_bounds__(kThreads) void kivi_mfma_split_kernel(DecodeArgs a)
       for (int j = 0; j < 8; ++j)
         qf[sl][j] = valid ? qrow[k_channel<BITS>(sl, j)] * a.qscale / k_factor<BITS>(sl, j) : 0.0f;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) qz[c] = valid ? qrow[16 * (low ? 1 : 0) + c] * a.qscale : 0.0f;
+    for (int c = 0; c < 16; ++c) qz[c] = valid ? qrow[(low ? 16 : 0) + c] * a.qscale : 0.0f;
   }
-  // V: lane tokens 16·tile + 4u + i; factor f' and shift of the code fields
-  float vfac[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    vfac[i] = (BITS == 2) ? ((i / 2) ? 0.25f : 1.0f) : 1.0f;
+  const uint32_t selmask = low ? 0xFFFFFFFFu : 0u;
   const uint32_t vsh = (BITS == 2) ? uint32_t(4 * u) : uint32_t(8 * (u % 2));
-  const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  const uint32_t vm0 = (BITS == 2) ? 0x00030003u : 0x000F000Fu;
+  const uint32_t vm1 = 0x000C000Cu;
+  const uint32_t magic = 0x43004300u;
 
-  float m_ref = -INFINITY;
-  float l_acc = 0.0f, pz_acc = 0.0f;
-  f32x4 cv[8];
+  WaveAcc W;
+  W.m_ref = -INFINITY;
+  W.l_acc = 0.0f;
+  W.pz_acc = 0.0f;
 #pragma unroll
-  for (int n = 0; n < 8; ++n) cv[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 cones = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < 8; ++n) W.cv[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  W.cones = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int64_t n_groups = a.n_main / kGroup;
   const int64_t g0 = int64_t(split) * a.tiles_per_split;
   const int64_t g1 = min(g0 + int64_t(a.tiles_per_split), n_groups);
-  const uint32_t* kcodes = static_cast<const uint32_t*>(a.k_main);
-  const uint32_t* vcodes = static_cast<const uint32_t*>(a.v_main);
-
-  for (int64_t g = g0 + wave; g < g1; g += kWaves) {
-    // ---------------------------------------------------------------- loads
-    uint32_t kw[2][LW];
-#pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
-      const uint32_t* row = kcodes + (int64_t(bh) * CT + g * kGroup + 16 * tile + r) * KW + LW * u;
-      if (BITS == 2) {
-        const uint2 x = *reinterpret_cast<const uint2*>(row);
-        kw[tile][0] = x.x;
-        kw[tile][1] = x.y;
-      } else {
-        const uint4 x = *reinterpret_cast<const uint4*>(row);
-        kw[tile][0] = x.x;
-        kw[tile][1] = x.y;
-        kw[tile][2] = x.z;
-        kw[tile][3] = x.w;
-      }
+  // groups g0 + wave, g0 + wave + 4, ...; the next one is loaded while the
+  // current one is processed (index clamped to the range, so the load is
+  // always issued and always in bounds)
+  int64_t g = g0 + wave;
+  if (g < g1) {
+    GroupRegs<BITS> A, B;
+    float* slot = ksz_slot[wave];
+    load_group<BITS>(A, a, bh, g, lane, r, u, low);
+    while (true) {
+      load_group<BITS>(B, a, bh, min(g + kWaves, g1 - 1), lane, r, u, low);
+      process_group<BITS>(A, W, slot, lane, u, qf, qz, selmask, low, vsh, vm0, vm1, magic);
+      g += kWaves;
+      if (g >= g1) break;
+      load_group<BITS>(A, a, bh, min(g + kWaves, g1 - 1), lane, r, u, low);
+      process_group<BITS>(B, W, slot, lane, u, qf, qz, selmask, low, vsh, vm0, vm1, magic);
+      g += kWaves;
+      if (g >= g1) break;
     }
-    const float* ksp = a.k_scale + (int64_t(bh) * a.NG + g) * kHeadDim + 32 * u;
-    const float* kzp = a.k_zero + (int64_t(bh) * a.NG + g) * kHeadDim + 32 * u + 16 * (low ? 1 : 0);
-    float ks[32], kz[16];
-#pragma unroll
-    for (int c = 0; c < 32; c += 4) {
-      const float4 x = *reinterpret_cast<const float4*>(ksp + c);
-      ks[c] = x.x; ks[c + 1] = x.y; ks[c + 2] = x.z; ks[c + 3] = x.w;
-    }
-#pragma unroll
-    for (int c = 0; c < 16; c += 4) {
-      const float4 x = *reinterpret_cast<const float4*>(kzp + c);
-      kz[c] = x.x; kz[c + 1] = x.y; kz[c + 2] = x.z; kz[c + 3] = x.w;
-    }
-    uint32_t vw[8][2];
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const uint32_t* cw = vcodes + ((int64_t(bh) * a.NG + g) * kHeadDim + 16 * n + r) * VW;
-      if (BITS == 2) {
-        const uint2 x = *reinterpret_cast<const uint2*>(cw);
-        vw[n][0] = x.x;
-        vw[n][1] = x.y;
-      } else {
-        vw[n][0] = cw[u / 2];
-        vw[n][1] = cw[2 + u / 2];
-      }
-    }
-    const int64_t tok0 = int64_t(bh) * CT + g * kGroup + 16 * (low ? 1 : 0) + 4 * u;
-    const float4 vs4 = *reinterpret_cast<const float4*>(a.v_scale + tok0);
-    const float4 vz4 = *reinterpret_cast<const float4*>(a.v_zero + tok0);
-
-    // --------------------------------------------------------- scores (QK)
-    u32x4 bq[4];
-#pragma unroll
-    for (int sl = 0; sl < 4; ++sl) {
-      uint32_t d[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int j0 = 2 * p, j1 = 2 * p + 1;
-        const float x0 = qf[sl][j0] * ks[k_channel<BITS>(sl, j0)];
-        const float x1 = qf[sl][j1] * ks[k_channel<BITS>(sl, j1)];
-        d[p] = split_f16(x0, low) | (split_f16(x1, low) << 16);
-      }
-      bq[sl] = u32x4{d[0], d[1], d[2], d[3]};
-    }
-    float zt = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) zt = fmaf(qz[c], kz[c], zt);
-    zt = head_sum(zt);                          // Σ_d q_d·z[g,d] for head hs
-    const float c0 = low ? 0.0f : zt * kTwoM24;
-    f32x4 s0 = f32x4{c0, c0, c0, c0}, s1 = s0;
-    {
-      u32x4 A0[4], A1[4];
-      k_unpack<BITS>(kw[0], A0);
-      k_unpack<BITS>(kw[1], A1);
-#pragma unroll
-      for (int sl = 0; sl < 4; ++sl) {
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(A0[sl]), as_f16x8(bq[sl]), s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(A1[sl]), as_f16x8(bq[sl]), s1, 0, 0, 0);
-      }
-    }
-    // high + low parts: lane keeps tile `low` (tokens 16·low + 4u + i)
-    float sc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float send = low ? s0[i] : s1[i];
-      const float mine = low ? s1[i] : s0[i];
-      sc[i] = (mine + xor8(send)) * kTwo24;
-    }
-
-    // ------------------------------------------------------ online softmax
-    float lmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    if (__any(lmax > m_ref + kLazy)) {          // wave-uniform slow path
-      const float gm = head_max(lmax);
-      const float m_new = fmaxf(m_ref, gm);
-      const float alpha = exp2f(m_ref - m_new);
-      l_acc *= alpha;
-      pz_acc *= alpha;
-#pragma unroll
-      for (int n = 0; n < 8; ++n) cv[n] *= alpha;
-      cones *= alpha;
-      m_ref = m_new;
-    }
-    float pp[4];
-    const float vsa[4] = {vs4.x, vs4.y, vs4.z, vs4.w};
-    const float vza[4] = {vz4.x, vz4.y, vz4.z, vz4.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = exp2f(sc[i] - m_ref);
-      l_acc += p;
-      pz_acc = fmaf(p, vza[i], pz_acc);
-      pp[i] = p * vsa[i] * vfac[i];
-    }
-    // bf16 high / low terms of P' (truncation split), exchanged with lane ^ 8
-    uint32_t keep[2], send[2];
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      uint32_t hb[2], lb[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const uint32_t xb = __float_as_uint(pp[2 * p + e]);
-        hb[e] = xb & 0xFFFF0000u;
-        lb[e] = __float_as_uint(pp[2 * p + e] - __uint_as_float(hb[e])) & 0xFFFF0000u;
-      }
-      const uint32_t hpair = (hb[0] >> 16) | hb[1];
-      const uint32_t lpair = (lb[0] >> 16) | lb[1];
-      keep[p] = low ? lpair : hpair;
-      send[p] = low ? hpair : lpair;
-    }
-    const uint32_t recv0 = xor8u(send[0]), recv1 = xor8u(send[1]);
-    // k-slots 0..3: tile 0 tokens 4u..4u+3; k-slots 4..7: tile 1 tokens
-    const u32x4 bp = low ? u32x4{recv0, recv1, keep[0], keep[1]}
-                         : u32x4{keep[0], keep[1], recv0, recv1};
-
-    // ------------------------------------------------------------ P·V
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      uint32_t d[4];
-      if (BITS == 2) {
-        const uint32_t w0 = vw[n][0] >> vsh, w1 = vw[n][1] >> vsh;
-        d[0] = (w0 & 0x00030003u) | 0x43004300u;
-        d[1] = (w0 & 0x000C000Cu) | 0x43004300u;
-        d[2] = (w1 & 0x00030003u) | 0x43004300u;
-        d[3] = (w1 & 0x000C000Cu) | 0x43004300u;
-      } else {
-        d[0] = ((vw[n][0] >> vsh) & 0x000F000Fu) | 0x43004300u;
-        d[1] = ((vw[n][0] >> (vsh + 4)) & 0x000F000Fu) | 0x43004300u;
-        d[2] = ((vw[n][1] >> vsh) & 0x000F000Fu) | 0x43004300u;
-        d[3] = ((vw[n][1] >> (vsh + 4)) & 0x000F000Fu) | 0x43004300u;
-      }
-      cv[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{d[0], d[1], d[2], d[3]}),
-                                                       as_bf16x8(bp), cv[n], 0, 0, 0);
-    }
-    cones = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ones), as_bf16x8(bp), cones, 0, 0, 0);
   }
 
   // ---- wave epilogue: head totals, offset removal, high + low columns
-  const float l_tot = head_sum(l_acc);
-  const float pz_tot = head_sum(pz_acc);
-  const float off = 128.0f * (cones[0] + xor8(cones[0]));
+  const float l_tot = head_sum(W.l_acc);
+  const float pz_tot = head_sum(W.pz_acc);
+  const float off = 128.0f * (W.cones[0] + xor8(W.cones[0]));
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
     f32x4 o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = cv[n][i] + xor8(cv[n][i]) - off + pz_tot;
+    for (int i = 0; i < 4; ++i) o[i] = W.cv[n][i] + xor8(W.cv[n][i]) - off + pz_tot;
     if (!low) *reinterpret_cast<f32x4*>(&mo[wave][hs][16 * n + 4 * u]) = o;
   }
   if (lane < 8) {
-    ml[wave][hs][0] = m_ref;
+    ml[wave][hs][0] = W.m_ref;
     ml[wave][hs][1] = l_tot;
   }
   __syncthreads();
