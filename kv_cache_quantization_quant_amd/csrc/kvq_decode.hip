@@ -323,24 +323,32 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// out[b, hq, :] = Σ_s o_s·2^(m_s − M) / Σ_s l_s·2^(m_s − M), one wave per (b, hq).
+// out[b, hq, :] = Σ_s o_s·2^(m_s − M) / Σ_s l_s·2^(m_s − M), one wave per
+// (b, hq): the split maxima and sums are read by all lanes at once, then the
+// weighted partial outputs with independent loads.
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const int64_t row = blockIdx.x;   // b·Hq + hq
   const int lane = threadIdx.x;
   const float* part = a.ws + row * a.n_split * kPart;
-  float M = -INFINITY;
-  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, part[s * kPart + kHeadDim]);
-  float o0 = 0.0f, o1 = 0.0f, L = 0.0f;
+  float mloc = -INFINITY;
+  for (int s = lane; s < a.n_split; s += 64) mloc = fmaxf(mloc, part[s * kPart + kHeadDim]);
+  const float M = wave_max(mloc);
+  float lloc = 0.0f;
+  for (int s = lane; s < a.n_split; s += 64) {
+    const float ms = part[s * kPart + kHeadDim];
+    if (ms != -INFINITY) lloc = fmaf(exp2f(ms - M), part[s * kPart + kHeadDim + 1], lloc);
+  }
+  const float L = wave_sum(lloc);
+  float o0 = 0.0f, o1 = 0.0f;
+#pragma unroll 8
   for (int s = 0; s < a.n_split; ++s) {
     const float ms = part[s * kPart + kHeadDim];
-    if (ms == -INFINITY) continue;
-    const float f = exp2f(ms - M);
-    L = fmaf(f, part[s * kPart + kHeadDim + 1], L);
-    o0 = fmaf(f, part[s * kPart + 2 * lane], o0);
-    o1 = fmaf(f, part[s * kPart + 2 * lane + 1], o1);
+    const float2 os = *reinterpret_cast<const float2*>(part + s * kPart + 2 * lane);
+    const float f = ms == -INFINITY ? 0.0f : exp2f(ms - M);
+    o0 = fmaf(f, os.x, o0);
+    o1 = fmaf(f, os.y, o1);
   }
-  float2 r = make_float2(o0 / L, o1 / L);
-  *reinterpret_cast<float2*>(a.out + row * kHeadDim + 2 * lane) = r;
+  *reinterpret_cast<float2*>(a.out + row * kHeadDim + 2 * lane) = make_float2(o0 / L, o1 / L);
 }
 
 template <int SRC>
@@ -358,9 +366,8 @@ hipError_t launch_src(const DecodeArgs& a, int n_splits, hipStream_t s) {
 
 }  // namespace
 
-// KIVI: the grouped region on the matrix cores, the FP16 window (one extra
-// split) on the vector path; FP8 / FP16: every split on the vector path.
-// Then the split merge.
+// KIVI: the grouped region and the FP16 window (one extra split) on the
+// matrix cores; FP8 / FP16: every split on the vector path. Then the merge.
 hipError_t launch_decode(const DecodeArgs& a_in, hipStream_t s) {
   DecodeArgs a = a_in;
   hipError_t e = hipSuccess;
@@ -369,10 +376,6 @@ hipError_t launch_decode(const DecodeArgs& a_in, hipStream_t s) {
     case kSrcKivi4:
       a.split_offset = 0;
       e = launch_kivi_mfma(a, s);
-      if (e == hipSuccess && a.n_split > a.n_split_main) {
-        a.split_offset = a.n_split_main;
-        e = a.src == kSrcKivi2 ? launch_src<kSrcKivi2>(a, 1, s) : launch_src<kSrcKivi4>(a, 1, s);
-      }
       break;
     case kSrcFp16:
       a.split_offset = 0;

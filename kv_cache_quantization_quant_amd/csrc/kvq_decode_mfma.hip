@@ -315,6 +315,97 @@ __device__ __forceinline__ void process_group(const GroupRegs<BITS>& G, WaveAcc&
                                                     0, 0, 0);
 }
 
+
+// One 32-token tile of the FP16 window ("4.4 KV Cache 量化：KIVI 2-bit 与 FP8
+// KV Cache", §3.2: the newest tokens stay unquantized). Scores: A = K values
+// (fp16, exact), B = fp16 high/low terms of q·log2e/√D (channels 32s + 8u + j
+// in k-step s). Values: V enters as two exact bf16 terms (fp16 has 11
+// significant bits, a bf16 pair holds 16), P' = p as a bf16 high/low pair.
+// Tokens past n_win are masked (score −∞, value 0).
+__device__ __forceinline__ void process_window_tile(const DecodeArgs& a, WaveAcc& W, int bh,
+                                                    int64_t tile, const u32x4 (&bqw)[4],
+                                                    int r, int u, bool low) {
+  const __half* kw = a.k_win + (int64_t(bh) * a.win_cap + tile * kGroup) * kHeadDim;
+  const __half* vwp = a.v_win + (int64_t(bh) * a.win_cap + tile * kGroup) * kHeadDim;
+  const int n_in = int(min<int64_t>(kGroup, a.n_win - tile * kGroup));
+  f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+  for (int sl = 0; sl < 4; ++sl) {
+    const uint4 k0 = *reinterpret_cast<const uint4*>(kw + r * kHeadDim + 32 * sl + 8 * u);
+    const uint4 k1 = *reinterpret_cast<const uint4*>(kw + (16 + r) * kHeadDim + 32 * sl + 8 * u);
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(u32x4{k0.x, k0.y, k0.z, k0.w}),
+                                                as_f16x8(bqw[sl]), s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(u32x4{k1.x, k1.y, k1.z, k1.w}),
+                                                as_f16x8(bqw[sl]), s1, 0, 0, 0);
+  }
+  float sc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // the cross-lane add runs in every lane (its partner may hold a masked
+    // token); the mask is applied afterwards
+    const float send = low ? s0[i] : s1[i];
+    const float mine = low ? s1[i] : s0[i];
+    const float both = mine + xor8(send);
+    const int t = (low ? 16 : 0) + 4 * u + i;
+    sc[i] = t < n_in ? both : -INFINITY;
+  }
+  const float lmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+  if (__any(lmax > W.m_ref + kLazy)) {
+    const float m_new = fmaxf(W.m_ref, head_max(lmax));
+    const float alpha = exp2f(W.m_ref - m_new);
+    W.l_acc *= alpha;
+    W.pz_acc *= alpha;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) W.cv[n] *= alpha;
+    W.cones *= alpha;
+    W.m_ref = m_new;
+  }
+  float pp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pp[i] = exp2f(sc[i] - W.m_ref);          // 0 for masked tokens
+    W.l_acc += pp[i];
+  }
+  uint32_t keep[2], send[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const float x0 = pp[2 * p], x1 = pp[2 * p + 1];
+    const float l0 = x0 - __uint_as_float(__float_as_uint(x0) & 0xFFFF0000u);
+    const float l1 = x1 - __uint_as_float(__float_as_uint(x1) & 0xFFFF0000u);
+    const uint32_t hpair = __builtin_amdgcn_perm(__float_as_uint(x1), __float_as_uint(x0), 0x07060302u);
+    const uint32_t lpair = __builtin_amdgcn_perm(__float_as_uint(l1), __float_as_uint(l0), 0x07060302u);
+    keep[p] = low ? lpair : hpair;
+    send[p] = low ? hpair : lpair;
+  }
+  const uint32_t recv0 = xor8u(send[0]), recv1 = xor8u(send[1]);
+  const u32x4 bp = low ? u32x4{recv0, recv1, keep[0], keep[1]}
+                       : u32x4{keep[0], keep[1], recv0, recv1};
+  // V^T tiles: lane (r, u) needs channel 16n + r at tokens 4u + j (j < 4) and
+  // 16 + 4u + j - 4; masked tokens read as 0.
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = (j < 4) ? 4 * u + j : 16 + 4 * u + (j - 4);
+      v[j] = t < n_in ? __half2float(vwp[t * kHeadDim + 16 * n + r]) : 0.0f;
+    }
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float x0 = v[2 * p], x1 = v[2 * p + 1];
+      const float l0 = x0 - __uint_as_float(__float_as_uint(x0) & 0xFFFF0000u);
+      const float l1 = x1 - __uint_as_float(__float_as_uint(x1) & 0xFFFF0000u);
+      hi[p] = __builtin_amdgcn_perm(__float_as_uint(x1), __float_as_uint(x0), 0x07060302u);
+      lo[p] = __builtin_amdgcn_perm(__float_as_uint(l1), __float_as_uint(l0), 0x07060302u);
+    }
+    W.cv[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{hi[0], hi[1], hi[2], hi[3]}),
+                                                       as_bf16x8(bp), W.cv[n], 0, 0, 0);
+    W.cv[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{lo[0], lo[1], lo[2], lo[3]}),
+                                                       as_bf16x8(bp), W.cv[n], 0, 0, 0);
+  }
+}
+
 template <int BITS>
 __global__ __launch_bounds__(kThreads) void kivi_mfma_split_kernel(DecodeArgs a) {
   __shared__ float mo[kWaves][8][kHeadDim];
@@ -363,27 +454,51 @@ __global__ __launch_bounds__(kThreads) void kivi_mfma_split_kernel(DecodeArgs a)
   for (int n = 0; n < 8; ++n) W.cv[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   W.cones = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int64_t n_groups = a.n_main / kGroup;
-  const int64_t g0 = int64_t(split) * a.tiles_per_split;
-  const int64_t g1 = min(g0 + int64_t(a.tiles_per_split), n_groups);
-  // groups g0 + wave, g0 + wave + 4, ...; the next one is loaded while the
-  // current one is processed (index clamped to the range, so the load is
-  // always issued and always in bounds)
-  int64_t g = g0 + wave;
-  if (g < g1) {
-    GroupRegs<BITS> A, B;
-    float* slot = ksz_slot[wave];
-    load_group<BITS>(A, a, bh, g, lane, r, u, low);
-    while (true) {
-      load_group<BITS>(B, a, bh, min(g + kWaves, g1 - 1), lane, r, u, low);
-      process_group<BITS>(A, W, slot, lane, u, qf, qz, selmask, low, vsh, vm0, vm1, magic);
-      g += kWaves;
-      if (g >= g1) break;
-      load_group<BITS>(A, a, bh, min(g + kWaves, g1 - 1), lane, r, u, low);
-      process_group<BITS>(B, W, slot, lane, u, qf, qz, selmask, low, vsh, vm0, vm1, magic);
-      g += kWaves;
-      if (g >= g1) break;
+  if (split < a.n_split_main) {
+    const int64_t n_groups = a.n_main / kGroup;
+    const int64_t g0 = int64_t(split) * a.tiles_per_split;
+    const int64_t g1 = min(g0 + int64_t(a.tiles_per_split), n_groups);
+    // groups g0 + wave, g0 + wave + 4, ...; the next one is loaded while the
+    // current one is processed (index clamped to the range, so the load is
+    // always issued and always in bounds)
+    int64_t g = g0 + wave;
+    if (g < g1) {
+      GroupRegs<BITS> A, B;
+      float* slot = ksz_slot[wave];
+      load_group<BITS>(A, a, bh, g, lane, r, u, low);
+      while (true) {
+        load_group<BITS>(B, a, bh, min(g + kWaves, g1 - 1), lane, r, u, low);
+        process_group<BITS>(A, W, slot, lane, u, qf, qz, selmask, low, vsh, vm0, vm1, magic);
+        g += kWaves;
+        if (g >= g1) break;
+        load_group<BITS>(A, a, bh, min(g + kWaves, g1 - 1), lane, r, u, low);
+        process_group<BITS>(B, W, slot, lane, u, qf, qz, selmask, low, vsh, vm0, vm1, magic);
+        g += kWaves;
+        if (g >= g1) break;
+      }
     }
+  } else {
+    // the FP16 window: q·log2e/√D as fp16 high/low terms, channel 32s + 8u + j
+    u32x4 bqw[4];
+    {
+      const bool valid = hs < nh;
+      const float* qrow = a.q + (int64_t(b) * a.Hq + hq0 + (valid ? hs : 0)) * kHeadDim;
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        uint32_t d[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float x0 = valid ? qrow[32 * sl + 8 * u + 2 * p] * a.qscale : 0.0f;
+          const float x1 = valid ? qrow[32 * sl + 8 * u + 2 * p + 1] * a.qscale : 0.0f;
+          const uint32_t hi = mix_pair(x0, 1.0f, x1, 1.0f);
+          d[p] = mix_pair_sub(x0, 1.0f, x1, 1.0f, hi & selmask);
+        }
+        bqw[sl] = u32x4{d[0], d[1], d[2], d[3]};
+      }
+    }
+    const int64_t n_tiles = (a.n_win + kGroup - 1) / kGroup;
+    for (int64_t tile = wave; tile < n_tiles; tile += kWaves)
+      process_window_tile(a, W, bh, tile, bqw, r, u, low);
   }
 
   // ---- wave epilogue: head totals, offset removal, high + low columns
@@ -432,8 +547,7 @@ __global__ __launch_bounds__(kThreads) void kivi_mfma_split_kernel(DecodeArgs a)
 }  // namespace
 
 hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t s) {
-  if (a.n_split_main <= 0) return hipSuccess;
-  const dim3 grid(a.n_split_main, a.B * a.H, a.nq / a.heads_per_chunk);
+  const dim3 grid(a.n_split, a.B * a.H, a.nq / a.heads_per_chunk);
   if (a.src == kSrcKivi2) {
     kivi_mfma_split_kernel<2><<<grid, kThreads, 0, s>>>(a);
   } else {
