@@ -5,7 +5,7 @@ Argument marshalling only: every function below forwards to the C ABI of the
 same name in include/kvq.h, and every step of the path runs in the HIP
 kernels of libkvq.so. torch is used for device memory and streams. Importing
 this module fails loudly if libkvq.so has not been built
-(`python -m kv_cache_quantization_quant_amd.build`).
+(`python kv_cache_quantization_quant_amd/build.py`).
 """
 from __future__ import annotations
 
@@ -62,7 +62,7 @@ class KvqError(RuntimeError):
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"libkvq.so not found at {_LIB_PATH}; build it with "
-                          "`python -m kv_cache_quantization_quant_amd.build`")
+                          "`python kv_cache_quantization_quant_amd/build.py`")
     lib = ctypes.CDLL(_LIB_PATH)
     sig = {
         "kvq_abi_version": (c_int32, []),

@@ -1,6 +1,7 @@
 """Builds libkvq.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
-Usage: python -m kv_cache_quantization_quant_amd.build   (or build.build()).
+Usage: python kv_cache_quantization_quant_amd/build.py   (or build.build()); it does not
+import the package, so a stale library never blocks a rebuild.
 Always recompiles every source; objects go to _build/ next to this file.
 """
 from __future__ import annotations

@@ -1,5 +1,5 @@
 // kvq_decode_mfma.hip — decode attention over the KIVI grouped region on the
-// gfx950 matrix cores (MFMA 16x16x32).
+// gfx950 matrix cores (MFMA 16x16x32), fed by asynchronous global→LDS loads.
 //
 // Attention as in "大模型量化从0到1（十三）：KV Cache 量化", §二 (score = q·k̂/√D,
 // softmax, Σ p·v̂), over KIVI groups ("4.4 KV Cache 量化：KIVI 2-bit 与 FP8 KV
@@ -9,22 +9,29 @@
 //   q·k̂_t = Σ_d (q_d·s[g,d])·c[t,d] + Σ_d q_d·z[g,d]          (K per channel)
 //   Σ_t p_t·v̂_t[d] = Σ_t (p_t·s_t)·c[t,d] + Σ_t p_t·z_t         (V per token)
 //
-// One wavefront processes one 32-token group at a time; lane l has r = l%16,
-// u = l/16, head slot hs = r%8 (up to 8 query heads of one KV head), and
-// part = r/8 (0: high, 1: low half of a two-term split).
+// Data movement. Each wavefront owns a ring of LDS stages, one 32-token group
+// per stage (K codes, V codes, K scale | zero, V scale | zero: 3328 bytes at
+// 2 bits, 5376 at 4 bits), filled by global_load_lds (one instruction moves
+// 1 KiB, no VGPRs involved) up to three groups ahead of the group in work.
+//
+// One wavefront processes one group at a time; lane l has r = l%16, u = l/16,
+// head slot hs = r%8 (up to 8 query heads of one KV head) and part = r/8.
+// A lane's channels are the 16 channels 32u + 16·part + (0..15).
 //
 // Scores, Sᵀ[token][col] = Σ_d code[token][d] · Q'[d][col], as f16 MFMA:
 //   A = K codes of token 16·tile + r as exact small fp16 integers, made by the
 //       gfx950 scaled conversions (2-bit codes as fp4 E2M1 nibbles c/2 scaled
-//       by 2, 4-bit codes as fp8 E4M3 bytes c·2⁻⁹ scaled by 2⁹), B = Q' for
-//       column r: head hs, the fp16 high (part 0) or low (part 1) term of
-//       q_d·s[g,d]·log2(e)/√D. C starts at the head's z-term Σ_d q_d·z[g,d].
-//       The two parts of a head sit in columns hs and hs+8 of the same lane
-//       row; a DPP rotate adds them. The operands are normal fp16 numbers on
-//       purpose: the matrix core aligns the 32 products of a k-step to the
-//       largest product built from the operands' exponent fields, so a
-//       subnormal operand (exponent field 0, read as 2⁻¹⁴) would cost up to
-//       ten bits of the sum's precision.
+//       by 2, 4-bit codes as fp8 E4M3 bytes c·2⁻⁹ scaled by 2⁹). The operands
+//       are normal fp16 numbers on purpose: the matrix core aligns the 32
+//       products of a k-step to the largest product built from the operands'
+//       exponent fields, so a subnormal operand (exponent field 0, read as
+//       2⁻¹⁴) would cost up to ten bits of the sum's precision.
+//   B = Q' for column r: head hs, the fp16 high (part 0) or low (part 1) term
+//       of q_d·s[g,d]·log2(e)/√D. Each lane splits the products of its own 16
+//       channels into both terms, and a bank-masked DPP swap with lane l ^ 8
+//       hands the high terms to part 0 and the low terms to part 1.
+//   C starts at the z-term Σ_d q_d·z[g,d] of the lane's half of the channels;
+//   adding columns hs and hs+8 (DPP rotate by 8) completes both sums.
 // The Sᵀ accumulator layout (lane holds column r, tokens 4u..4u+3 of a tile)
 // is exactly the B-operand layout of the value product, so no transpose is
 // needed:
@@ -57,32 +64,52 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+// LDS stage of one group (byte offsets).
+template <int BITS>
+struct Stage {
+  static constexpr int kCodeBytes = kGroup * kHeadDim * BITS / 8;   // K codes (= V codes)
+  static constexpr int kKc = 0;
+  static constexpr int kVc = kCodeBytes;
+  static constexpr int kKsz = 2 * kCodeBytes;            // 128 fp32 scales, 128 zero-points
+  static constexpr int kVsz = kKsz + 2 * kHeadDim * 4;   // 32 fp32 scales, 32 zero-points
+  static constexpr int kBytes = kVsz + 2 * kGroup * 4;
+  static constexpr int kDepth = BITS == 2 ? 4 : 3;       // stages per wavefront
+  static constexpr int kLoads = 2 * (kCodeBytes / 1024) + 2;   // DMA instructions per group
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // value of lane l ^ 8 (rotate by 8 inside each row of 16 lanes)
 __device__ __forceinline__ float xor8(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
 }
-__device__ __forceinline__ uint32_t xor8u(uint32_t x) {
-  return uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x128, 0xF, 0xF, false));
+// src of lane l ^ 8 where BANKS enables lane l (bank b = lanes 4b..4b+3 of a
+// row: 0x3 = part 0, 0xC = part 1); the other lanes keep old
+template <int BANKS>
+__device__ __forceinline__ uint32_t from_partner(uint32_t old, uint32_t src) {
+  return uint32_t(__builtin_amdgcn_update_dpp(int(old), int(src), 0x128, 0xF, BANKS, false));
 }
+// sum over the lanes l ^ 16 and l ^ 32 (gfx950 permlane swaps)
+__device__ __forceinline__ float sum_x16_x32(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float max_x16_x32(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+// 2^x on the transcendental unit (results below 2^-126 flush to 0)
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // sum / max over the 8 lanes sharing l % 8 (xor 8, 16, 32)
-__device__ __forceinline__ float head_sum(float x) {
-  x += xor8(x);
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
-}
-__device__ __forceinline__ float head_max(float x) {
-  x = fmaxf(x, xor8(x));
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
-}
+__device__ __forceinline__ float head_sum(float x) { return sum_x16_x32(x + xor8(x)); }
+__device__ __forceinline__ float head_max(float x) { return max_x16_x32(fmaxf(x, xor8(x))); }
 
 // {f16(a0·b0), f16(a1·b1)}: fp32 products rounded once to fp16, packed.
 __device__ __forceinline__ uint32_t mix_pair(float a0, float b0, float a1, float b1) {
@@ -111,15 +138,15 @@ __device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t x, uint32_t y) {
 // ---- K code positions. The conversions turn one byte (two fp4 nibbles) or
 // one half-word (two fp8 bytes) into an fp16 pair, so in k-step sl the k-slots
 // j = 0..7 of a lane whose 32 channels start at 32·u hold channels
-// 8·sl + {0, 2, 1, 3, 4, 6, 5, 7}[j] (for both widths):
+// 8·sl + kslot_channel(j), kslot_channel = {0, 2, 1, 3, 4, 6, 5, 7} (both widths):
 //   2-bit: word sl/2; m0 = w & 0x33333333 has code 2n in nibble n, m1 =
 //          (w >> 2) & 0x33333333 code 2n+1; byte k of m0 / m1 gives codes
 //          {4k, 4k+2} / {4k+1, 4k+3}; k-step sl uses bytes 2·(sl%2) + {0, 1}.
 //   4-bit: word sl; m0 = w & 0x0F0F0F0F has code 2n in byte n, m1 =
 //          (w >> 4) & 0x0F0F0F0F code 2n+1; half-word 0 / 1 of m0 gives codes
 //          {0, 2} / {4, 6}, of m1 {1, 3} / {5, 7}.
-__device__ __forceinline__ constexpr int k_channel(int sl, int j) {
-  return 8 * sl + 4 * (j / 4) + (j / 2) % 2 + 2 * (j % 2);
+__device__ __forceinline__ constexpr int kslot_channel(int j) {
+  return 4 * (j / 4) + (j / 2) % 2 + 2 * (j % 2);
 }
 
 __device__ __forceinline__ uint32_t fp4x2_to_f16x2(uint32_t w, int byte) {
@@ -140,80 +167,32 @@ __device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t w, bool high) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// A operand of one token: 4 k-steps × 4 dwords of fp16 code pairs.
+// Code masks of one token's K words (2-bit: 2 words → 4 masks; 4-bit: 4 words
+// → 8 masks) and the A operand of k-step sl from them.
 template <int BITS>
-__device__ __forceinline__ void k_unpack(const uint32_t* w, u32x4* A) {
-  if (BITS == 2) {
+__device__ __forceinline__ void k_masks(const uint32_t (&w)[BITS], uint32_t (&m)[2 * BITS]) {
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const uint32_t m0 = w[x] & 0x33333333u, m1 = (w[x] >> 2) & 0x33333333u;
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        A[2 * x + h] = u32x4{fp4x2_to_f16x2(m0, 2 * h), fp4x2_to_f16x2(m1, 2 * h),
-                             fp4x2_to_f16x2(m0, 2 * h + 1), fp4x2_to_f16x2(m1, 2 * h + 1)};
-    }
-  } else {
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const uint32_t m0 = w[x] & 0x0F0F0F0Fu, m1 = (w[x] >> 4) & 0x0F0F0F0Fu;
-      A[x] = u32x4{fp8x2_to_f16x2(m0, false), fp8x2_to_f16x2(m1, false),
-                   fp8x2_to_f16x2(m0, true), fp8x2_to_f16x2(m1, true)};
+  for (int x = 0; x < BITS; ++x) {
+    if (BITS == 2) {
+      m[2 * x] = w[x] & 0x33333333u;
+      m[2 * x + 1] = (w[x] >> 2) & 0x33333333u;
+    } else {
+      m[2 * x] = w[x] & 0x0F0F0F0Fu;
+      m[2 * x + 1] = (w[x] >> 4) & 0x0F0F0F0Fu;
     }
   }
 }
-
-// Raw data of one group for one lane (loaded one group ahead).
 template <int BITS>
-struct GroupRegs {
-  uint32_t kw[2][BITS];        // K words of tokens r and 16 + r (32 channels)
-  float4 ksz;                  // 16-byte chunk of the group's K scale | zero block
-  uint32_t vw[8][2];           // V words (tile-0 and tile-1 tokens) of channel 16n + r
-  float vs[4], vz[4];          // V scale / zero of tokens 16·part + 4u + i
-};
-
-template <int BITS>
-__device__ __forceinline__ void load_group(GroupRegs<BITS>& G, const DecodeArgs& a, int bh,
-                                           int64_t g, int lane, int r, int u, bool low) {
-  constexpr int KW = kHeadDim * BITS / 32;
-  constexpr int VW = kGroup * BITS / 32;
-  const int64_t CT = a.main_bh_tokens;
-  const uint32_t* kcodes = static_cast<const uint32_t*>(a.k_main);
-  const uint32_t* vcodes = static_cast<const uint32_t*>(a.v_main);
-#pragma unroll
-  for (int tile = 0; tile < 2; ++tile) {
-    const uint32_t* row = kcodes + (int64_t(bh) * CT + g * kGroup + 16 * tile + r) * KW + BITS * u;
-    if (BITS == 2) {
-      const uint2 x = *reinterpret_cast<const uint2*>(row);
-      G.kw[tile][0] = x.x;
-      G.kw[tile][1] = x.y;
-    } else {
-      const uint4 x = *reinterpret_cast<const uint4*>(row);
-      G.kw[tile][0] = x.x;
-      G.kw[tile][1] = x.y;
-      G.kw[tile][2] = x.z;
-      G.kw[tile][3] = x.w;
-    }
+__device__ __forceinline__ u32x4 k_operand(const uint32_t (&m)[2 * BITS], int sl) {
+  if (BITS == 2) {
+    const uint32_t m0 = m[2 * (sl / 2)], m1 = m[2 * (sl / 2) + 1];
+    const int k = 2 * (sl % 2);
+    return u32x4{fp4x2_to_f16x2(m0, k), fp4x2_to_f16x2(m1, k), fp4x2_to_f16x2(m0, k + 1),
+                 fp4x2_to_f16x2(m1, k + 1)};
   }
-  // lanes 0..31: scales 4l..4l+3; lanes 32..63: zero-points
-  const float* meta = (lane < 32 ? a.k_scale : a.k_zero) + (int64_t(bh) * a.NG + g) * kHeadDim;
-  G.ksz = *reinterpret_cast<const float4*>(meta + 4 * (lane & 31));
-#pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    const uint32_t* cw = vcodes + ((int64_t(bh) * a.NG + g) * kHeadDim + 16 * n + r) * VW;
-    if (BITS == 2) {
-      const uint2 x = *reinterpret_cast<const uint2*>(cw);
-      G.vw[n][0] = x.x;
-      G.vw[n][1] = x.y;
-    } else {
-      G.vw[n][0] = cw[u / 2];
-      G.vw[n][1] = cw[2 + u / 2];
-    }
-  }
-  const int64_t tok0 = int64_t(bh) * CT + g * kGroup + (low ? 16 : 0) + 4 * u;
-  const float4 s4 = *reinterpret_cast<const float4*>(a.v_scale + tok0);
-  const float4 z4 = *reinterpret_cast<const float4*>(a.v_zero + tok0);
-  G.vs[0] = s4.x; G.vs[1] = s4.y; G.vs[2] = s4.z; G.vs[3] = s4.w;
-  G.vz[0] = z4.x; G.vz[1] = z4.y; G.vz[2] = z4.z; G.vz[3] = z4.w;
+  const uint32_t m0 = m[2 * sl], m1 = m[2 * sl + 1];
+  return u32x4{fp8x2_to_f16x2(m0, false), fp8x2_to_f16x2(m1, false), fp8x2_to_f16x2(m0, true),
+               fp8x2_to_f16x2(m1, true)};
 }
 
 // Per-lane state of one wavefront across its groups.
@@ -223,58 +202,12 @@ struct WaveAcc {
   f32x4 cones;
 };
 
-template <int BITS>
-__device__ __forceinline__ void process_group(const GroupRegs<BITS>& G, WaveAcc& W,
-                                              float* ksz_lds, int lane, int u,
-                                              const float (&qf)[4][8], const float (&qz)[16],
-                                              uint32_t selmask, bool low, uint32_t vsh,
-                                              uint32_t vm0, uint32_t vm1, uint32_t magic) {
-  // ---- stage the group's K scales (ksz_lds[0..127]) and zero-points
-  // (ksz_lds[128..255]) in this wavefront's LDS slot
-  wave_sync();
-  *reinterpret_cast<float4*>(ksz_lds + 4 * lane) = G.ksz;
-  wave_sync();
-  const float* ks = ksz_lds + 32 * u;
-  const float* kz = ksz_lds + 128 + 32 * u + (low ? 16 : 0);
-  // ---- z-term Σ_d q_d·z[g, d] of head hs (8 lanes × 16 channels)
-  float zt = 0.0f;
-#pragma unroll
-  for (int c = 0; c < 16; ++c) zt = fmaf(qz[c], kz[c], zt);
-  zt = head_sum(zt);
-  const float c0 = low ? 0.0f : zt;
-  f32x4 s0 = f32x4{c0, c0, c0, c0}, s1 = s0;
-  // ---- scores, one k-step (32 channels) at a time
-  u32x4 A0[4], A1[4];
-  k_unpack<BITS>(G.kw[0], A0);
-  k_unpack<BITS>(G.kw[1], A1);
-#pragma unroll
-  for (int sl = 0; sl < 4; ++sl) {
-    uint32_t d[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int j0 = 2 * p, j1 = 2 * p + 1;
-      const float a0 = qf[sl][j0], b0 = ks[k_channel(sl, j0)];
-      const float a1 = qf[sl][j1], b1 = ks[k_channel(sl, j1)];
-      const uint32_t hi = mix_pair(a0, b0, a1, b1);
-      d[p] = mix_pair_sub(a0, b0, a1, b1, hi & selmask);
-    }
-    const u32x4 bq = u32x4{d[0], d[1], d[2], d[3]};
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(A0[sl]), as_f16x8(bq), s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(A1[sl]), as_f16x8(bq), s1, 0, 0, 0);
-  }
-  // ---- both parts of the head's score; this lane keeps tile `low`
-  float sc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float send = low ? s0[i] : s1[i];
-    const float mine = low ? s1[i] : s0[i];
-    sc[i] = mine + xor8(send);
-  }
-  // ---- online softmax (log2 domain)
+// Softmax step for four scores, then P'·V for one group or window tile.
+__device__ __forceinline__ void rescale_if_needed(WaveAcc& W, const float (&sc)[4]) {
   const float lmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
   if (__any(lmax > W.m_ref + kLazy)) {           // wave-uniform, rare
     const float m_new = fmaxf(W.m_ref, head_max(lmax));
-    const float alpha = exp2f(W.m_ref - m_new);
+    const float alpha = fast_exp2(W.m_ref - m_new);
     W.l_acc *= alpha;
     W.pz_acc *= alpha;
 #pragma unroll
@@ -282,44 +215,143 @@ __device__ __forceinline__ void process_group(const GroupRegs<BITS>& G, WaveAcc&
     W.cones *= alpha;
     W.m_ref = m_new;
   }
-  float pp[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float p = exp2f(sc[i] - W.m_ref);
-    W.l_acc += p;
-    W.pz_acc = fmaf(p, G.vz[i], W.pz_acc);
-    pp[i] = p * ((BITS == 2 && i >= 2) ? G.vs[i] * 0.25f : G.vs[i]);
-  }
-  // ---- bf16 high / low terms of P' (truncation split), exchanged with lane ^ 8
-  uint32_t keep[2], send[2];
+}
+
+// bf16 high / low terms of four P' values; part 0 ends with the high terms of
+// tile 0 (own) and tile 1 (partner's), part 1 with the low terms of tile 0
+// (partner's) and tile 1 (own): the B operand of the value products.
+__device__ __forceinline__ u32x4 p_operand(const float (&pp)[4]) {
+  uint32_t hp[2], lp[2];
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const float x0 = pp[2 * p], x1 = pp[2 * p + 1];
     const float l0 = x0 - __uint_as_float(__float_as_uint(x0) & 0xFFFF0000u);
     const float l1 = x1 - __uint_as_float(__float_as_uint(x1) & 0xFFFF0000u);
-    const uint32_t hpair = __builtin_amdgcn_perm(__float_as_uint(x1), __float_as_uint(x0), 0x07060302u);
-    const uint32_t lpair = __builtin_amdgcn_perm(__float_as_uint(l1), __float_as_uint(l0), 0x07060302u);
-    keep[p] = low ? lpair : hpair;
-    send[p] = low ? hpair : lpair;
+    hp[p] = __builtin_amdgcn_perm(__float_as_uint(x1), __float_as_uint(x0), 0x07060302u);
+    lp[p] = __builtin_amdgcn_perm(__float_as_uint(l1), __float_as_uint(l0), 0x07060302u);
   }
-  const uint32_t recv0 = xor8u(send[0]), recv1 = xor8u(send[1]);
-  const u32x4 bp = low ? u32x4{recv0, recv1, keep[0], keep[1]}
-                       : u32x4{keep[0], keep[1], recv0, recv1};
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const uint32_t t = lp[p];
+    lp[p] = from_partner<0x3>(lp[p], hp[p]);
+    hp[p] = from_partner<0xC>(hp[p], t);
+  }
+  return u32x4{hp[0], hp[1], lp[0], lp[1]};
+}
+
+template <int BITS>
+__device__ __forceinline__ void process_group(const uint8_t* st, WaveAcc& W, int r, int u,
+                                              bool low, const float (&q16)[16], uint32_t vsh,
+                                              uint32_t vm0, uint32_t vm1, uint32_t magic) {
+  using S = Stage<BITS>;
+  const float* ksz = reinterpret_cast<const float*>(st + S::kKsz) + 32 * u + (low ? 16 : 0);
+  // ---- z-term of this lane's 16 channels, summed over the four lane groups u
+  float zt = 0.0f;
+#pragma unroll
+  for (int c4 = 0; c4 < 4; ++c4) {
+    const float4 z = *reinterpret_cast<const float4*>(ksz + kHeadDim + 4 * c4);
+    zt = fmaf(q16[4 * c4], z.x, zt);
+    zt = fmaf(q16[4 * c4 + 1], z.y, zt);
+    zt = fmaf(q16[4 * c4 + 2], z.z, zt);
+    zt = fmaf(q16[4 * c4 + 3], z.w, zt);
+  }
+  zt = sum_x16_x32(zt);
+  f32x4 s0 = f32x4{zt, zt, zt, zt}, s1 = s0;
+  // ---- K codes of tokens r and 16 + r, channels 32u..32u+31
+  uint32_t w0[BITS], w1[BITS];
+  {
+    const uint8_t* kc = st + S::kKc;
+    constexpr int kRow = kHeadDim * BITS / 8;
+    if (BITS == 2) {
+      const uint2 x = *reinterpret_cast<const uint2*>(kc + r * kRow + 8 * u);
+      const uint2 y = *reinterpret_cast<const uint2*>(kc + (16 + r) * kRow + 8 * u);
+      w0[0] = x.x; w0[1] = x.y; w1[0] = y.x; w1[1] = y.y;
+    } else {
+      const uint4 x = *reinterpret_cast<const uint4*>(kc + r * kRow + 16 * u);
+      const uint4 y = *reinterpret_cast<const uint4*>(kc + (16 + r) * kRow + 16 * u);
+      w0[0] = x.x; w0[1] = x.y; w0[2] = x.z; w0[3] = x.w;
+      w1[0] = y.x; w1[1] = y.y; w1[2] = y.z; w1[3] = y.w;
+    }
+  }
+  uint32_t m0[2 * BITS], m1[2 * BITS];
+  k_masks<BITS>(w0, m0);
+  k_masks<BITS>(w1, m1);
+  // ---- scores: local k-step h is global k-step h (part 0) or 2 + h (part 1)
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float ks[8];
+    {
+      const float4 a = *reinterpret_cast<const float4*>(ksz + 8 * h);
+      const float4 b = *reinterpret_cast<const float4*>(ksz + 8 * h + 4);
+      ks[0] = a.x; ks[1] = a.y; ks[2] = a.z; ks[3] = a.w;
+      ks[4] = b.x; ks[5] = b.y; ks[6] = b.z; ks[7] = b.w;
+    }
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int c0 = kslot_channel(2 * p), c1 = kslot_channel(2 * p + 1);
+      const float a0 = q16[8 * h + c0], b0 = ks[c0], a1 = q16[8 * h + c1], b1 = ks[c1];
+      hi[p] = mix_pair(a0, b0, a1, b1);
+      lo[p] = mix_pair_sub(a0, b0, a1, b1, hi[p]);
+    }
+    // part 0 takes the partner's high terms (k-step 2 + h), part 1 the
+    // partner's low terms (k-step h)
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t t = lo[p];
+      lo[p] = from_partner<0x3>(lo[p], hi[p]);
+      hi[p] = from_partner<0xC>(hi[p], t);
+    }
+    const u32x4 bh = u32x4{hi[0], hi[1], hi[2], hi[3]};
+    const u32x4 bl = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(k_operand<BITS>(m0, h)), as_f16x8(bh), s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(k_operand<BITS>(m1, h)), as_f16x8(bh), s1, 0, 0, 0);
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(k_operand<BITS>(m0, 2 + h)), as_f16x8(bl), s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(k_operand<BITS>(m1, 2 + h)), as_f16x8(bl), s1, 0, 0, 0);
+  }
+  // ---- both columns of the head; part 0 keeps tile 0, part 1 tile 1
+  float sc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float t0 = s0[i] + xor8(s0[i]);
+    const float t1 = s1[i] + xor8(s1[i]);
+    sc[i] = low ? t1 : t0;
+  }
+  rescale_if_needed(W, sc);
+  // ---- probabilities, V scale / zero of tokens 16·part + 4u + i
+  const float* vsz = reinterpret_cast<const float*>(st + S::kVsz) + (low ? 16 : 0) + 4 * u;
+  const float4 vs = *reinterpret_cast<const float4*>(vsz);
+  const float4 vz = *reinterpret_cast<const float4*>(vsz + kGroup);
+  const float vsa[4] = {vs.x, vs.y, vs.z, vs.w};
+  const float vza[4] = {vz.x, vz.y, vz.z, vz.w};
+  float pp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float p = fast_exp2(sc[i] - W.m_ref);
+    W.l_acc += p;
+    W.pz_acc = fmaf(p, vza[i], W.pz_acc);
+    pp[i] = p * ((BITS == 2 && i >= 2) ? vsa[i] * 0.25f : vsa[i]);
+  }
+  const u32x4 bp = p_operand(pp);
   // ---- P·V: 8 tiles of 16 channels, codes in the mantissa of 128.0
+  const uint8_t* vc = st + S::kVc;
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
     uint32_t d[4];
     if (BITS == 2) {
-      const uint32_t w0 = G.vw[n][0] >> vsh, w1 = G.vw[n][1] >> vsh;
-      d[0] = bfi(vm0, w0, magic);
-      d[1] = bfi(vm1, w0, magic);
-      d[2] = bfi(vm0, w1, magic);
-      d[3] = bfi(vm1, w1, magic);
+      const uint2 x = *reinterpret_cast<const uint2*>(vc + (16 * n + r) * 8);
+      const uint32_t v0 = x.x >> vsh, v1 = x.y >> vsh;
+      d[0] = bfi(vm0, v0, magic);
+      d[1] = bfi(vm1, v0, magic);
+      d[2] = bfi(vm0, v1, magic);
+      d[3] = bfi(vm1, v1, magic);
     } else {
-      d[0] = bfi(vm0, G.vw[n][0] >> vsh, magic);
-      d[1] = bfi(vm0, G.vw[n][0] >> (vsh + 4), magic);
-      d[2] = bfi(vm0, G.vw[n][1] >> vsh, magic);
-      d[3] = bfi(vm0, G.vw[n][1] >> (vsh + 4), magic);
+      const uint32_t* cw = reinterpret_cast<const uint32_t*>(vc + (16 * n + r) * 16);
+      const uint32_t v0 = cw[u / 2], v1 = cw[2 + u / 2];
+      d[0] = bfi(vm0, v0 >> vsh, magic);
+      d[1] = bfi(vm0, v0 >> (vsh + 4), magic);
+      d[2] = bfi(vm0, v1 >> vsh, magic);
+      d[3] = bfi(vm0, v1 >> (vsh + 4), magic);
     }
     W.cv[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{d[0], d[1], d[2], d[3]}),
                                                        as_bf16x8(bp), W.cv[n], 0, 0, 0);
@@ -328,7 +360,6 @@ __device__ __forceinline__ void process_group(const GroupRegs<BITS>& G, WaveAcc&
   W.cones = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ones), as_bf16x8(bp), W.cones,
                                                     0, 0, 0);
 }
-
 
 // One 32-token tile of the FP16 window ("4.4 KV Cache 量化：KIVI 2-bit 与 FP8
 // KV Cache", §3.2: the newest tokens stay unquantized). Scores: A = K values
@@ -363,37 +394,14 @@ __device__ __forceinline__ void process_window_tile(const DecodeArgs& a, WaveAcc
     const int t = (low ? 16 : 0) + 4 * u + i;
     sc[i] = t < n_in ? both : -INFINITY;
   }
-  const float lmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-  if (__any(lmax > W.m_ref + kLazy)) {
-    const float m_new = fmaxf(W.m_ref, head_max(lmax));
-    const float alpha = exp2f(W.m_ref - m_new);
-    W.l_acc *= alpha;
-    W.pz_acc *= alpha;
-#pragma unroll
-    for (int n = 0; n < 8; ++n) W.cv[n] *= alpha;
-    W.cones *= alpha;
-    W.m_ref = m_new;
-  }
+  rescale_if_needed(W, sc);
   float pp[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    pp[i] = exp2f(sc[i] - W.m_ref);          // 0 for masked tokens
+    pp[i] = fast_exp2(sc[i] - W.m_ref);      // 0 for masked tokens
     W.l_acc += pp[i];
   }
-  uint32_t keep[2], send[2];
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const float x0 = pp[2 * p], x1 = pp[2 * p + 1];
-    const float l0 = x0 - __uint_as_float(__float_as_uint(x0) & 0xFFFF0000u);
-    const float l1 = x1 - __uint_as_float(__float_as_uint(x1) & 0xFFFF0000u);
-    const uint32_t hpair = __builtin_amdgcn_perm(__float_as_uint(x1), __float_as_uint(x0), 0x07060302u);
-    const uint32_t lpair = __builtin_amdgcn_perm(__float_as_uint(l1), __float_as_uint(l0), 0x07060302u);
-    keep[p] = low ? lpair : hpair;
-    send[p] = low ? hpair : lpair;
-  }
-  const uint32_t recv0 = xor8u(send[0]), recv1 = xor8u(send[1]);
-  const u32x4 bp = low ? u32x4{recv0, recv1, keep[0], keep[1]}
-                       : u32x4{keep[0], keep[1], recv0, recv1};
+  const u32x4 bp = p_operand(pp);
   // V^T tiles: lane (r, u) needs channel 16n + r at tokens 4u + j (j < 4) and
   // 16 + 4u + j - 4; masked tokens read as 0.
 #pragma unroll
@@ -420,11 +428,30 @@ __device__ __forceinline__ void process_window_tile(const DecodeArgs& a, WaveAcc
   }
 }
 
+// Asynchronous loads of group g into an LDS stage: per lane 16 bytes of K
+// codes and of V codes per KiB, then 16 bytes of K scale (lanes 0..31) or
+// zero-point (32..63), then 4 bytes of V scale or zero-point. The per-lane
+// sources already include the lane's offset; one instruction each.
+template <int BITS>
+__device__ __forceinline__ void issue_group(uint8_t* st, int64_t g, const uint8_t* kc,
+                                            const uint8_t* vc, const float* ksz,
+                                            const float* vsz) {
+  using S = Stage<BITS>;
+#pragma unroll
+  for (int c = 0; c < S::kCodeBytes / 1024; ++c) {
+    __builtin_amdgcn_global_load_lds(kc + g * S::kCodeBytes + 1024 * c, st + S::kKc + 1024 * c,
+                                     16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vc + g * S::kCodeBytes + 1024 * c, st + S::kVc + 1024 * c,
+                                     16, 0, 0);
+  }
+  __builtin_amdgcn_global_load_lds(ksz + g * kHeadDim, st + S::kKsz, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(vsz + g * kGroup, st + S::kVsz, 4, 0, 0);
+}
+
 template <int BITS>
 __global__ __launch_bounds__(kThreads) void kivi_mfma_split_kernel(DecodeArgs a) {
-  __shared__ float mo[kWaves][8][kHeadDim];
-  __shared__ float ml[kWaves][8][2];
-  __shared__ float ksz_slot[kWaves][2 * kHeadDim];
+  using S = Stage<BITS>;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][S::kDepth][S::kBytes];
 
   const int split = blockIdx.x;
   const int bh = blockIdx.y;
@@ -433,28 +460,13 @@ __global__ __launch_bounds__(kThreads) void kivi_mfma_split_kernel(DecodeArgs a)
   const int hq0 = h_kv * a.nq + int(blockIdx.z) * a.heads_per_chunk;
   const int nh = min(a.heads_per_chunk, a.nq - int(blockIdx.z) * a.heads_per_chunk);
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int r = lane & 15;
   const int u = lane >> 4;
   const int hs = r & 7;
   const bool low = r >= 8;
 
-  // ---- per-lane constants: this lane's 32 channels [32u, 32u+32) of head hs
-  float qf[4][8];          // q_d·log2e/√D, by (k-step, k-slot)
-  float qz[16];            // q_d·log2e/√D for the z-term: channels 32u + 16·part + c
-  {
-    const bool valid = hs < nh;
-    const float* qrow = a.q + (int64_t(b) * a.Hq + hq0 + (valid ? hs : 0)) * kHeadDim + 32 * u;
-#pragma unroll
-    for (int sl = 0; sl < 4; ++sl)
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        qf[sl][j] = valid ? qrow[k_channel(sl, j)] * a.qscale : 0.0f;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) qz[c] = valid ? qrow[(low ? 16 : 0) + c] * a.qscale : 0.0f;
-  }
-  const uint32_t selmask = low ? 0xFFFFFFFFu : 0u;
   const uint32_t vsh = (BITS == 2) ? uint32_t(4 * u) : uint32_t(8 * (u % 2));
   const uint32_t vm0 = (BITS == 2) ? 0x00030003u : 0x000F000Fu;
   const uint32_t vm1 = 0x000C000Cu;
@@ -469,41 +481,72 @@ __global__ __launch_bounds__(kThreads) void kivi_mfma_split_kernel(DecodeArgs a)
   W.cones = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (split < a.n_split_main) {
+    // q_d·log2e/√D of this lane's channels 32u + 16·part + c
+    float q16[16];
+    {
+      // head slots past the chunk read head 0 and get weight 0
+      const bool valid = hs < nh;
+      const float qs = valid ? a.qscale : 0.0f;
+      const float4* qrow = reinterpret_cast<const float4*>(
+          a.q + (int64_t(b) * a.Hq + hq0 + (valid ? hs : 0)) * kHeadDim + 32 * u + (low ? 16 : 0));
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const float4 x = qrow[c4];
+        q16[4 * c4] = x.x * qs;
+        q16[4 * c4 + 1] = x.y * qs;
+        q16[4 * c4 + 2] = x.z * qs;
+        q16[4 * c4 + 3] = x.w * qs;
+      }
+    }
     const int64_t n_groups = a.n_main / kGroup;
     const int64_t g0 = int64_t(split) * a.tiles_per_split;
     const int64_t g1 = min(g0 + int64_t(a.tiles_per_split), n_groups);
-    // groups g0 + wave, g0 + wave + 4, ...; the next one is loaded while the
-    // current one is processed (index clamped to the range, so the load is
-    // always issued and always in bounds)
-    int64_t g = g0 + wave;
-    if (g < g1) {
-      GroupRegs<BITS> A, B;
-      float* slot = ksz_slot[wave];
-      load_group<BITS>(A, a, bh, g, lane, r, u, low);
-      while (true) {
-        load_group<BITS>(B, a, bh, min(g + kWaves, g1 - 1), lane, r, u, low);
-        process_group<BITS>(A, W, slot, lane, u, qf, qz, selmask, low, vsh, vm0, vm1, magic);
-        g += kWaves;
-        if (g >= g1) break;
-        load_group<BITS>(A, a, bh, min(g + kWaves, g1 - 1), lane, r, u, low);
-        process_group<BITS>(B, W, slot, lane, u, qf, qz, selmask, low, vsh, vm0, vm1, magic);
-        g += kWaves;
-        if (g >= g1) break;
+    // this wavefront's groups: g0 + wave + kWaves·i, i < n_mine
+    const int n_mine = g1 - g0 > wave ? int((g1 - g0 - wave + kWaves - 1) / kWaves) : 0;
+    const uint8_t* kc = static_cast<const uint8_t*>(a.k_main) +
+                        int64_t(bh) * a.main_bh_tokens * (kHeadDim * BITS / 8) + 16 * lane;
+    const uint8_t* vc = static_cast<const uint8_t*>(a.v_main) +
+                        int64_t(bh) * a.NG * S::kCodeBytes + 16 * lane;
+    // lanes 0..31 fetch scales, lanes 32..63 zero-points (one instruction each)
+    const float* ksz = (lane < 32 ? a.k_scale : a.k_zero) + int64_t(bh) * a.NG * kHeadDim +
+                       4 * (lane & 31);
+    const float* vsz = (lane < 32 ? a.v_scale : a.v_zero) + int64_t(bh) * a.main_bh_tokens +
+                       (lane & 31);
+#pragma unroll
+    for (int i = 0; i < S::kDepth - 1; ++i)
+      if (i < n_mine)
+        issue_group<BITS>(&ring[wave][i % S::kDepth][0], g0 + wave + int64_t(kWaves) * i, kc, vc, ksz, vsz);
+    for (int i = 0; i < n_mine; ++i) {
+      if (i + S::kDepth - 1 < n_mine) {
+        // the stage being refilled was read by the previous group: its LDS
+        // reads are complete before the new data can land
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int j = i + S::kDepth - 1;
+        issue_group<BITS>(&ring[wave][j % S::kDepth][0], g0 + wave + int64_t(kWaves) * j, kc, vc, ksz, vsz);
       }
+      // wait until this group's loads are done (loads complete in order)
+      const int ahead = min(S::kDepth - 1, n_mine - 1 - i);
+      if (ahead >= 3) wait_vmem<3 * S::kLoads>();
+      else if (ahead == 2) wait_vmem<2 * S::kLoads>();
+      else if (ahead == 1) wait_vmem<S::kLoads>();
+      else wait_vmem<0>();
+      process_group<BITS>(&ring[wave][i % S::kDepth][0], W, r, u, low, q16, vsh, vm0, vm1, magic);
     }
   } else {
     // the FP16 window: q·log2e/√D as fp16 high/low terms, channel 32s + 8u + j
     u32x4 bqw[4];
     {
+      const uint32_t selmask = low ? 0xFFFFFFFFu : 0u;
       const bool valid = hs < nh;
+      const float qs = valid ? a.qscale : 0.0f;
       const float* qrow = a.q + (int64_t(b) * a.Hq + hq0 + (valid ? hs : 0)) * kHeadDim;
 #pragma unroll
       for (int sl = 0; sl < 4; ++sl) {
         uint32_t d[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const float x0 = valid ? qrow[32 * sl + 8 * u + 2 * p] * a.qscale : 0.0f;
-          const float x1 = valid ? qrow[32 * sl + 8 * u + 2 * p + 1] * a.qscale : 0.0f;
+          const float x0 = qrow[32 * sl + 8 * u + 2 * p] * qs;
+          const float x1 = qrow[32 * sl + 8 * u + 2 * p + 1] * qs;
           const uint32_t hi = mix_pair(x0, 1.0f, x1, 1.0f);
           d[p] = mix_pair_sub(x0, 1.0f, x1, 1.0f, hi & selmask);
         }
@@ -515,7 +558,10 @@ __global__ __launch_bounds__(kThreads) void kivi_mfma_split_kernel(DecodeArgs a)
       process_window_tile(a, W, bh, tile, bqw, r, u, low);
   }
 
-  // ---- wave epilogue: head totals, offset removal, high + low columns
+  // ---- wave epilogue: head totals, offset removal, high + low columns. The
+  // wave's own ring stages hold its results (all its loads have completed).
+  float* mo = reinterpret_cast<float*>(&ring[wave][0][0]);     // [8][kHeadDim]
+  float* ml = mo + 8 * kHeadDim;                                 // [8][2]
   const float l_tot = head_sum(W.l_acc);
   const float pz_tot = head_sum(W.pz_acc);
   const float off = 128.0f * (W.cones[0] + xor8(W.cones[0]));
@@ -524,11 +570,11 @@ __global__ __launch_bounds__(kThreads) void kivi_mfma_split_kernel(DecodeArgs a)
     f32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = W.cv[n][i] + xor8(W.cv[n][i]) - off + pz_tot;
-    if (!low) *reinterpret_cast<f32x4*>(&mo[wave][hs][16 * n + 4 * u]) = o;
+    if (!low) *reinterpret_cast<f32x4*>(&mo[hs * kHeadDim + 16 * n + 4 * u]) = o;
   }
   if (lane < 8) {
-    ml[wave][hs][0] = W.m_ref;
-    ml[wave][hs][1] = l_tot;
+    ml[2 * hs] = W.m_ref;
+    ml[2 * hs + 1] = l_tot;
   }
   __syncthreads();
 
@@ -538,15 +584,20 @@ __global__ __launch_bounds__(kThreads) void kivi_mfma_split_kernel(DecodeArgs a)
     const int d = i % kHeadDim;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml[w][h][0]);
+    for (int w = 0; w < kWaves; ++w) {
+      const float* mlw = reinterpret_cast<const float*>(&ring[w][0][0]) + 8 * kHeadDim;
+      M = fmaxf(M, mlw[2 * h]);
+    }
     float O = 0.0f, L = 0.0f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float mw = ml[w][h][0];
+        const float* mow = reinterpret_cast<const float*>(&ring[w][0][0]);
+        const float* mlw = mow + 8 * kHeadDim;
+        const float mw = mlw[2 * h];
         const float f = mw == -INFINITY ? 0.0f : exp2f(mw - M);
-        O = fmaf(f, mo[w][h][d], O);
-        L = fmaf(f, ml[w][h][1], L);
+        O = fmaf(f, mow[h * kHeadDim + d], O);
+        L = fmaf(f, mlw[2 * h + 1], L);
       }
     }
     float* part = a.ws + ((int64_t(b) * a.Hq + hq0 + h) * a.n_split + split) * kPart;
