@@ -3,10 +3,13 @@
 
 Workload (the 70B-style GQA layer at 32K context): B=16, 64 query heads,
 8 KV heads, D=128, KIVI 2-bit K and V, G=32, R=128. The 32768-token prefill is
-quantized once before timing; a step is one streamed decode step: append one
-token per (b, KV head) — with the lazy window flush when due, every 128
-appends — then decode attention of one query per head over the whole cache.
-Inputs are seeded synthetic tensors (synth), resident in HBM before timing.
+quantized once before timing; a step is one streamed decode step of one layer:
+append one token per (b, KV head) — with the lazy window flush when due, every
+128 appends — then decode attention of one query per head over the whole
+cache. The steps cycle through LAYERS independent layer caches of that shape,
+as consecutive layers of a model do, so that no step finds its cache in the
+256 MB Infinity Cache. Inputs are seeded synthetic tensors (synth), resident
+in HBM before timing.
 
 Printed (one JSON line): value = effective KV GB/s of the timed steps
 (Σ algorithmic decode bytes / wall time of the timed region, HIP events on the
@@ -31,6 +34,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 D = 128
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_gqa70b_32k_counters.json")
+LAYERS = 4                     # layer caches the timed steps cycle through (4 × 441 MB)
 
 
 def _log(*a):
@@ -39,7 +43,7 @@ def _log(*a):
 
 def decode_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("kvq_decode.hip", "kvq_internal.h", "kvq_api.cpp"):
+    for f in ("kvq_decode.hip", "kvq_decode_mfma.hip", "kvq_internal.h", "kvq_api.cpp"):
         with open(os.path.join(ROOT, "kv_cache_quantization_quant_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -60,16 +64,16 @@ def traffic_from_counters():
 
 
 class Scrub:
-    """A 1 GiB buffer written between timed launches where the Infinity Cache
-    (256 MB) must not serve the next launch."""
+    """A 1 GiB buffer read between timed launches where the Infinity Cache
+    (256 MB) must not serve the next launch. Reading (not writing) leaves no
+    dirty lines whose write-back would be charged to the next launch."""
 
     def __init__(self, torch):
-        self.buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-        self.i = 0
+        self.buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        self.acc = torch.zeros((), dtype=torch.float32, device="cuda")
 
     def __call__(self):
-        self.i += 1
-        self.buf.fill_(float(self.i))
+        self.acc += self.buf.sum()
 
 
 def time_launches(torch, fn, iters, scrub=None):
@@ -102,12 +106,12 @@ def run_main(torch, kq, synth, args):
     B, H, Hq, S, bits = (cfg["batch"], cfg["num_kv_heads"], cfg["num_q_heads"],
                          cfg["seq_len"], cfg["bits"])
     n_steps = args.warmup + args.steps
-    C = S + n_steps
+    C = S + -(-n_steps // LAYERS)
     _log(f"[bench] gqa70b_32k: B={B} Hq={Hq} H={H} S={S} KIVI {bits}-bit, "
-         f"warmup={args.warmup} steps={args.steps}")
+         f"{LAYERS} layer caches, warmup={args.warmup} steps={args.steps}")
     t0 = time.time()
-    k = synth.make_k(B, H, 0, C, D, device="cuda")
-    v = synth.make_v(B, H, 0, C, D, device="cuda")
+    k = synth.make_k(B, H, 0, S + n_steps, D, device="cuda")
+    v = synth.make_v(B, H, 0, S + n_steps, D, device="cuda")
     kp, vp = k[:, :, :S].contiguous(), v[:, :, :S].contiguous()
     k_new = [k[:, :, S + i].contiguous() for i in range(n_steps)]
     v_new = [v[:, :, S + i].contiguous() for i in range(n_steps)]
@@ -116,7 +120,9 @@ def run_main(torch, kq, synth, args):
     torch.cuda.synchronize()
     _log(f"[bench] inputs generated in {time.time() - t0:.1f}s")
 
-    dc = kq.DeviceCache(kq.make_config("kivi", bits=bits, batch=B, num_kv_heads=H, capacity=C))
+    cfg_c = kq.make_config("kivi", bits=bits, batch=B, num_kv_heads=H, capacity=C)
+    layers = [kq.DeviceCache(cfg_c) for _ in range(LAYERS)]
+    dc = layers[0]
     ws = dc.make_workspace(Hq)
     out = torch.empty_like(qs[0])
 
@@ -127,10 +133,15 @@ def run_main(torch, kq, synth, args):
     prefill()
     pre_us = statistics.median(time_launches(torch, prefill, 5))
     q_bytes = quantize_traffic_bytes(B, H, S, bits, dc.n_quant, dc.n_resid)
+    for c in layers[1:]:
+        c.prefill(kp, vp)
+    del kp, vp
 
+    # step i works on layer i % LAYERS
     for i in range(args.warmup):
-        dc.append(k_new[i], v_new[i])
-        dc.decode(qs[i], out=out, workspace=ws)
+        c = layers[i % LAYERS]
+        c.append(k_new[i], v_new[i])
+        c.decode(qs[i], out=out, workspace=ws)
     torch.cuda.synchronize()
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -143,10 +154,11 @@ def run_main(torch, kq, synth, args):
     start.record()
     for j in range(args.steps):
         i = args.warmup + j
-        dc.append(k_new[i], v_new[i])
-        step_bytes.append(dc.decode_bytes(Hq))
+        c = layers[i % LAYERS]
+        c.append(k_new[i], v_new[i])
+        step_bytes.append(c.decode_bytes(Hq))
         ev[j][0].record()
-        dc.decode(qs[i], out=out, workspace=ws)
+        c.decode(qs[i], out=out, workspace=ws)
         ev[j][1].record()
     end.record()
     torch.cuda.synchronize()
@@ -159,10 +171,12 @@ def run_main(torch, kq, synth, args):
     achieved = (total_bytes / len(step_bytes)) / (mean_dec_us * 1e-6) / 1e9
 
     # decode launches with the Infinity Cache scrubbed before each one
-    scrub = Scrub(torch)
-    cold = time_launches(torch, lambda: dc.decode(qs[-1], out=out, workspace=ws), 20, scrub)
-    cold_med = statistics.median(cold)
+    cold_med = None
     bytes_now = dc.decode_bytes(Hq)
+    if not args.no_cold:
+        scrub = Scrub(torch)
+        cold = time_launches(torch, lambda: dc.decode(qs[-1], out=out, workspace=ws), 20, scrub)
+        cold_med = statistics.median(cold)
 
     res = {
         "B": B, "Hq": Hq, "H": H, "S": S, "bits": bits,
@@ -173,10 +187,11 @@ def run_main(torch, kq, synth, args):
         "decode_bytes_per_launch": total_bytes / len(step_bytes),
         "achieved_gbs": achieved,
         "cold_decode_us_p50": cold_med,
-        "cold_decode_gbs": bytes_now / (cold_med * 1e-6) / 1e9,
+        "cold_decode_gbs": None if cold_med is None else bytes_now / (cold_med * 1e-6) / 1e9,
         "prefill_quantize_us": pre_us,
         "prefill_quantize_gbs": q_bytes / (pre_us * 1e-6) / 1e9,
-        "final_state": [dc.n_quant, dc.n_resid],
+        "layers": LAYERS,
+        "final_state": [[c.n_quant, c.n_resid] for c in layers],
     }
     return res
 
@@ -284,6 +299,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the scrubbed single-launch decode timing (profiling runs)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the run, copy a device buffer of this many MiB (a known-size "
+                         "transfer that calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -303,6 +323,14 @@ def main():
     main_res = run_main(torch, kq, synth, args)
     extra = None if args.no_extra else run_extra(torch, kq, synth)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(synth)
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 18                      # float32 elements
+        src = torch.full((n,), 1.0, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     traffic = traffic_from_counters()
     achieved = main_res["achieved_gbs"]
@@ -322,7 +350,8 @@ def main():
                 "per KV head, V token-lognormal, q N(0,1))",
         "config": {"workload": "gqa70b_32k: 64 query / 8 KV heads, D=128, B=16, S=32768 "
                                "(+ streamed tokens), KIVI 2-bit K per-channel / V per-token, "
-                               "G=32, R=128; step = append (+flush every 128) + decode",
+                               "G=32, R=128; step = append (+flush every 128) + decode of one "
+                               "layer, steps cycling through 4 layer caches",
                    "global_batch": main_res["B"], "seq_len": main_res["S"],
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
