@@ -74,7 +74,7 @@ struct Stage {
   static constexpr int kVsz = kKsz + 2 * kHeadDim * 4;   // 32 fp32 scales, 32 zero-points
   static constexpr int kBytes = kVsz + 2 * kGroup * 4;
   static constexpr int kDepth = BITS == 2 ? 4 : 3;       // stages per wavefront
-  static constexpr int kLoads = 2 * (kCodeBytes / 1024) + 2;   // DMA instructions per group
+  static constexpr int kLoads = 2 * (kCodeBytes / 1024) + 4;   // DMA instructions per group
 };
 
 template <int N>
@@ -245,19 +245,8 @@ __device__ __forceinline__ void process_group(const uint8_t* st, WaveAcc& W, int
                                               uint32_t vm0, uint32_t vm1, uint32_t magic) {
   using S = Stage<BITS>;
   const float* ksz = reinterpret_cast<const float*>(st + S::kKsz) + 32 * u + (low ? 16 : 0);
-  // ---- z-term of this lane's 16 channels, summed over the four lane groups u
-  float zt = 0.0f;
-#pragma unroll
-  for (int c4 = 0; c4 < 4; ++c4) {
-    const float4 z = *reinterpret_cast<const float4*>(ksz + kHeadDim + 4 * c4);
-    zt = fmaf(q16[4 * c4], z.x, zt);
-    zt = fmaf(q16[4 * c4 + 1], z.y, zt);
-    zt = fmaf(q16[4 * c4 + 2], z.z, zt);
-    zt = fmaf(q16[4 * c4 + 3], z.w, zt);
-  }
-  zt = sum_x16_x32(zt);
-  f32x4 s0 = f32x4{zt, zt, zt, zt}, s1 = s0;
-  // ---- K codes of tokens r and 16 + r, channels 32u..32u+31
+  // ---- LDS reads first: K codes of tokens r and 16 + r (channels 32u..32u+31),
+  // K scale and zero-point of this lane's 16 channels
   uint32_t w0[BITS], w1[BITS];
   {
     const uint8_t* kc = st + S::kKc;
@@ -273,24 +262,35 @@ __device__ __forceinline__ void process_group(const uint8_t* st, WaveAcc& W, int
       w1[0] = y.x; w1[1] = y.y; w1[2] = y.z; w1[3] = y.w;
     }
   }
+  float ks[16], kz[16];
+#pragma unroll
+  for (int c4 = 0; c4 < 4; ++c4) {
+    const float4 a = *reinterpret_cast<const float4*>(ksz + 4 * c4);
+    ks[4 * c4] = a.x; ks[4 * c4 + 1] = a.y; ks[4 * c4 + 2] = a.z; ks[4 * c4 + 3] = a.w;
+  }
+#pragma unroll
+  for (int c4 = 0; c4 < 4; ++c4) {
+    const float4 z = *reinterpret_cast<const float4*>(ksz + kHeadDim + 4 * c4);
+    kz[4 * c4] = z.x; kz[4 * c4 + 1] = z.y; kz[4 * c4 + 2] = z.z; kz[4 * c4 + 3] = z.w;
+  }
   uint32_t m0[2 * BITS], m1[2 * BITS];
   k_masks<BITS>(w0, m0);
   k_masks<BITS>(w1, m1);
+  // ---- z-term of this lane's 16 channels, summed over the four lane groups u
+  float zt = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) zt = fmaf(q16[c], kz[c], zt);
+  zt = sum_x16_x32(zt);
+  f32x4 s0 = f32x4{zt, zt, zt, zt}, s1 = s0;
   // ---- scores: local k-step h is global k-step h (part 0) or 2 + h (part 1)
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    float ks[8];
-    {
-      const float4 a = *reinterpret_cast<const float4*>(ksz + 8 * h);
-      const float4 b = *reinterpret_cast<const float4*>(ksz + 8 * h + 4);
-      ks[0] = a.x; ks[1] = a.y; ks[2] = a.z; ks[3] = a.w;
-      ks[4] = b.x; ks[5] = b.y; ks[6] = b.z; ks[7] = b.w;
-    }
     uint32_t hi[4], lo[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int c0 = kslot_channel(2 * p), c1 = kslot_channel(2 * p + 1);
-      const float a0 = q16[8 * h + c0], b0 = ks[c0], a1 = q16[8 * h + c1], b1 = ks[c1];
+      const float a0 = q16[8 * h + c0], b0 = ks[8 * h + c0];
+      const float a1 = q16[8 * h + c1], b1 = ks[8 * h + c1];
       hi[p] = mix_pair(a0, b0, a1, b1);
       lo[p] = mix_pair_sub(a0, b0, a1, b1, hi[p]);
     }
@@ -428,24 +428,60 @@ __device__ __forceinline__ void process_window_tile(const DecodeArgs& a, WaveAcc
   }
 }
 
-// Asynchronous loads of group g into an LDS stage: per lane 16 bytes of K
-// codes and of V codes per KiB, then 16 bytes of K scale (lanes 0..31) or
-// zero-point (32..63), then 4 bytes of V scale or zero-point. The per-lane
-// sources already include the lane's offset; one instruction each.
+// Asynchronous global→LDS copies (global_load_lds): lane i's 16 or 4 bytes
+// land at lds + 16·i or lds + 4·i. They are issued from inline asm so that the
+// compiler does not model them: it cannot tell the ring's stages apart and
+// would otherwise wait for every copy in flight (vmcnt(0)) before each LDS
+// read. The kernel orders them itself with s_waitcnt vmcnt (copies complete in
+// issue order). M0 carries the LDS address and is restored afterwards.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)(p)));
+}
+// 16 bytes per lane from base + voff (base wave-uniform)
+__device__ __forceinline__ void dma16(void* lds, const void* base, uint32_t voff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved) : "s"(lds_addr(lds)), "v"(voff), "s"(base) : "memory");
+}
+// 4 bytes per lane from base + voff (base wave-uniform)
+__device__ __forceinline__ void dma4(void* lds, const void* base, uint32_t voff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "global_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved) : "s"(lds_addr(lds)), "v"(voff), "s"(base) : "memory");
+}
+
+// Loads of group g into an LDS stage: K codes and V codes (1 KiB per
+// instruction), K scales (lanes 0..31) and K zero-points (lanes 32..63) into
+// [scales | zero-points], V scales and V zero-points likewise. Every
+// instruction is issued with all 64 lanes or exactly half of them, so each
+// group is Stage::kLoads instructions.
 template <int BITS>
-__device__ __forceinline__ void issue_group(uint8_t* st, int64_t g, const uint8_t* kc,
-                                            const uint8_t* vc, const float* ksz,
-                                            const float* vsz) {
+__device__ __forceinline__ void issue_group(uint8_t* st, int64_t g, const DecodeArgs& a, int bh,
+                                            int lane) {
   using S = Stage<BITS>;
+  const uint8_t* kc = static_cast<const uint8_t*>(a.k_main) +
+                      (int64_t(bh) * a.main_bh_tokens + g * kGroup) * (kHeadDim * BITS / 8);
+  const uint8_t* vc = static_cast<const uint8_t*>(a.v_main) + (int64_t(bh) * a.NG + g) * S::kCodeBytes;
 #pragma unroll
   for (int c = 0; c < S::kCodeBytes / 1024; ++c) {
-    __builtin_amdgcn_global_load_lds(kc + g * S::kCodeBytes + 1024 * c, st + S::kKc + 1024 * c,
-                                     16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vc + g * S::kCodeBytes + 1024 * c, st + S::kVc + 1024 * c,
-                                     16, 0, 0);
+    dma16(st + S::kKc + 1024 * c, kc + 1024 * c, 16 * lane);
+    dma16(st + S::kVc + 1024 * c, vc + 1024 * c, 16 * lane);
   }
-  __builtin_amdgcn_global_load_lds(ksz + g * kHeadDim, st + S::kKsz, 16, 0, 0);
-  __builtin_amdgcn_global_load_lds(vsz + g * kGroup, st + S::kVsz, 4, 0, 0);
+  const int64_t kg = (int64_t(bh) * a.NG + g) * kHeadDim;
+  const int64_t vg = int64_t(bh) * a.main_bh_tokens + g * kGroup;
+  // lanes 32..63 land 512 (128) bytes after lane 0, on the zero-points
+  if (lane < 32) {
+    dma16(st + S::kKsz, a.k_scale + kg, 16 * lane);
+    dma4(st + S::kVsz, a.v_scale + vg, 4 * lane);
+  } else {
+    dma16(st + S::kKsz, a.k_zero + kg, 16 * (lane - 32));
+    dma4(st + S::kVsz, a.v_zero + vg, 4 * (lane - 32));
+  }
 }
 
 template <int BITS>
@@ -503,26 +539,17 @@ __global__ __launch_bounds__(kThreads) void kivi_mfma_split_kernel(DecodeArgs a)
     const int64_t g1 = min(g0 + int64_t(a.tiles_per_split), n_groups);
     // this wavefront's groups: g0 + wave + kWaves·i, i < n_mine
     const int n_mine = g1 - g0 > wave ? int((g1 - g0 - wave + kWaves - 1) / kWaves) : 0;
-    const uint8_t* kc = static_cast<const uint8_t*>(a.k_main) +
-                        int64_t(bh) * a.main_bh_tokens * (kHeadDim * BITS / 8) + 16 * lane;
-    const uint8_t* vc = static_cast<const uint8_t*>(a.v_main) +
-                        int64_t(bh) * a.NG * S::kCodeBytes + 16 * lane;
-    // lanes 0..31 fetch scales, lanes 32..63 zero-points (one instruction each)
-    const float* ksz = (lane < 32 ? a.k_scale : a.k_zero) + int64_t(bh) * a.NG * kHeadDim +
-                       4 * (lane & 31);
-    const float* vsz = (lane < 32 ? a.v_scale : a.v_zero) + int64_t(bh) * a.main_bh_tokens +
-                       (lane & 31);
 #pragma unroll
     for (int i = 0; i < S::kDepth - 1; ++i)
       if (i < n_mine)
-        issue_group<BITS>(&ring[wave][i % S::kDepth][0], g0 + wave + int64_t(kWaves) * i, kc, vc, ksz, vsz);
+        issue_group<BITS>(&ring[wave][i % S::kDepth][0], g0 + wave + int64_t(kWaves) * i, a, bh, lane);
     for (int i = 0; i < n_mine; ++i) {
       if (i + S::kDepth - 1 < n_mine) {
         // the stage being refilled was read by the previous group: its LDS
         // reads are complete before the new data can land
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         const int j = i + S::kDepth - 1;
-        issue_group<BITS>(&ring[wave][j % S::kDepth][0], g0 + wave + int64_t(kWaves) * j, kc, vc, ksz, vsz);
+        issue_group<BITS>(&ring[wave][j % S::kDepth][0], g0 + wave + int64_t(kWaves) * j, a, bh, lane);
       }
       // wait until this group's loads are done (loads complete in order)
       const int ahead = min(S::kDepth - 1, n_mine - 1 - i);
