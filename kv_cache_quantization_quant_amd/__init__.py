@@ -15,7 +15,10 @@ from ctypes import POINTER, byref, c_double, c_int32, c_int64, c_size_t, c_void_
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
+# KVQ_LIB names another build of the same library (e.g. one compiled with
+# different tuning macros); by default the in-tree libkvq.so is loaded.
+_LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                      "libkvq.so")
 
 KVQ_OK = 0
 KVQ_ERR_INVALID_ARG = 1

@@ -24,7 +24,10 @@ using kvq::kGroup;
 using kvq::kHeadDim;
 
 // Workgroups one decode launch aims for (8 per CU on 256 CUs).
-constexpr int64_t kTargetWorkgroups = 2048;
+#ifndef KVQ_TARGET_WORKGROUPS
+#define KVQ_TARGET_WORKGROUPS 2048
+#endif
+constexpr int64_t kTargetWorkgroups = KVQ_TARGET_WORKGROUPS;
 constexpr int64_t kMinTilesPerSplit = 4;   // one tile per wavefront at least
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -53,6 +53,17 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+// ring stages per wavefront (2-bit / 4-bit) and the occupancy the register
+// allocation targets (wavefronts per SIMD)
+#ifndef KVQ_RING_STAGES_2BIT
+#define KVQ_RING_STAGES_2BIT 4
+#endif
+#ifndef KVQ_RING_STAGES_4BIT
+#define KVQ_RING_STAGES_4BIT 3
+#endif
+#ifndef KVQ_DECODE_WAVES_PER_SIMD
+#define KVQ_DECODE_WAVES_PER_SIMD 3
+#endif
 constexpr int kPart = kHeadDim + 2;
 constexpr float kLazy = 16.0f;                 // log2-domain slack before rescaling
 
@@ -73,8 +84,10 @@ struct Stage {
   static constexpr int kKsz = 2 * kCodeBytes;            // 128 fp32 scales, 128 zero-points
   static constexpr int kVsz = kKsz + 2 * kHeadDim * 4;   // 32 fp32 scales, 32 zero-points
   static constexpr int kBytes = kVsz + 2 * kGroup * 4;
-  static constexpr int kDepth = BITS == 2 ? 4 : 3;       // stages per wavefront
+  static constexpr int kDepth = BITS == 2 ? KVQ_RING_STAGES_2BIT : KVQ_RING_STAGES_4BIT;
+  static_assert(kDepth >= 3 && kDepth <= 4, "one or two groups in flight ahead");
   static constexpr int kLoads = 2 * (kCodeBytes / 1024) + 4;   // DMA instructions per group
+  static constexpr int kSecond = kCodeBytes;   // M0 of the second copy block (V codes on)
 };
 
 template <int N>
@@ -239,10 +252,16 @@ __device__ __forceinline__ u32x4 p_operand(const float (&pp)[4]) {
   return u32x4{hp[0], hp[1], lp[0], lp[1]};
 }
 
+// A group runs in three phases. The main loop overlaps the scores of group i
+// with the value products of group i - 1 (independent instruction streams in
+// one basic block), then turns the scores of group i into probabilities.
+
+// Scores of the four tokens this lane keeps (log2 units), and the V scale /
+// zero-point of those tokens (16·part + 4u + i).
 template <int BITS>
-__device__ __forceinline__ void process_group(const uint8_t* st, WaveAcc& W, int r, int u,
-                                              bool low, const float (&q16)[16], uint32_t vsh,
-                                              uint32_t vm0, uint32_t vm1, uint32_t magic) {
+__device__ __forceinline__ void group_scores(const uint8_t* st, int r, int u, bool low,
+                                             const float (&q16)[16], float (&sc)[4], float4& vs,
+                                             float4& vz) {
   using S = Stage<BITS>;
   const float* ksz = reinterpret_cast<const float*>(st + S::kKsz) + 32 * u + (low ? 16 : 0);
   // ---- LDS reads first: K codes of tokens r and 16 + r (channels 32u..32u+31),
@@ -310,18 +329,23 @@ __device__ __forceinline__ void process_group(const uint8_t* st, WaveAcc& W, int
     s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(k_operand<BITS>(m1, 2 + h)), as_f16x8(bl), s1, 0, 0, 0);
   }
   // ---- both columns of the head; part 0 keeps tile 0, part 1 tile 1
-  float sc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float t0 = s0[i] + xor8(s0[i]);
     const float t1 = s1[i] + xor8(s1[i]);
     sc[i] = low ? t1 : t0;
   }
-  rescale_if_needed(W, sc);
-  // ---- probabilities, V scale / zero of tokens 16·part + 4u + i
   const float* vsz = reinterpret_cast<const float*>(st + S::kVsz) + (low ? 16 : 0) + 4 * u;
-  const float4 vs = *reinterpret_cast<const float4*>(vsz);
-  const float4 vz = *reinterpret_cast<const float4*>(vsz + kGroup);
+  vs = *reinterpret_cast<const float4*>(vsz);
+  vz = *reinterpret_cast<const float4*>(vsz + kGroup);
+}
+
+// Online-softmax step for the group's scores; returns the B operand P' of its
+// value products (V scale, and the 1/4 of the 2-bit codes in bits 2..3, folded).
+template <int BITS>
+__device__ __forceinline__ u32x4 group_probs(WaveAcc& W, const float (&sc)[4], float4 vs,
+                                             float4 vz) {
+  rescale_if_needed(W, sc);
   const float vsa[4] = {vs.x, vs.y, vs.z, vs.w};
   const float vza[4] = {vz.x, vz.y, vz.z, vz.w};
   float pp[4];
@@ -332,8 +356,16 @@ __device__ __forceinline__ void process_group(const uint8_t* st, WaveAcc& W, int
     W.pz_acc = fmaf(p, vza[i], W.pz_acc);
     pp[i] = p * ((BITS == 2 && i >= 2) ? vsa[i] * 0.25f : vsa[i]);
   }
-  const u32x4 bp = p_operand(pp);
-  // ---- P·V: 8 tiles of 16 channels, codes in the mantissa of 128.0
+  return p_operand(pp);
+}
+
+// P'·V of one group: 8 tiles of 16 channels, codes in the mantissa of 128.0,
+// plus the column sums of P' that remove the 128 offset.
+template <int BITS>
+__device__ __forceinline__ void group_values(const uint8_t* st, WaveAcc& W, u32x4 bp, int r,
+                                             int u, uint32_t vsh, uint32_t vm0, uint32_t vm1,
+                                             uint32_t magic) {
+  using S = Stage<BITS>;
   const uint8_t* vc = st + S::kVc;
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
@@ -429,63 +461,135 @@ __device__ __forceinline__ void process_window_tile(const DecodeArgs& a, WaveAcc
 }
 
 // Asynchronous global→LDS copies (global_load_lds): lane i's 16 or 4 bytes
-// land at lds + 16·i or lds + 4·i. They are issued from inline asm so that the
-// compiler does not model them: it cannot tell the ring's stages apart and
-// would otherwise wait for every copy in flight (vmcnt(0)) before each LDS
-// read. The kernel orders them itself with s_waitcnt vmcnt (copies complete in
-// issue order). M0 carries the LDS address and is restored afterwards.
+// land at M0 + offset + 16·i (or 4·i); the immediate offset moves the global
+// address by the same amount, so every global base below is biased by minus
+// the stage offset its copy lands at. The copies are issued from inline asm so
+// that the compiler does not model them: it cannot tell the ring's stages
+// apart and would otherwise wait for every copy in flight (vmcnt(0)) before
+// each LDS read. The kernel orders them itself with s_waitcnt vmcnt (copies
+// complete in issue order). They are non-temporal (nt): the cache is streamed
+// once per decode, and the streaming hint is worth about a fifth of the
+// achievable HBM read rate. M0 and EXEC are restored at the end of each block.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)(p)));
 }
-// 16 bytes per lane from base + voff (base wave-uniform)
-__device__ __forceinline__ void dma16(void* lds, const void* base, uint32_t voff) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved) : "s"(lds_addr(lds)), "v"(voff), "s"(base) : "memory");
-}
-// 4 bytes per lane from base + voff (base wave-uniform)
-__device__ __forceinline__ void dma4(void* lds, const void* base, uint32_t voff) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-      "global_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved) : "s"(lds_addr(lds)), "v"(voff), "s"(base) : "memory");
-}
 
-// Loads of group g into an LDS stage: K codes and V codes (1 KiB per
-// instruction), K scales (lanes 0..31) and K zero-points (lanes 32..63) into
-// [scales | zero-points], V scales and V zero-points likewise. Every
-// instruction is issued with all 64 lanes or exactly half of them, so each
-// group is Stage::kLoads instructions.
+// Wave-uniform, offset-biased sources of the next group a wavefront loads.
+struct GroupSrc {
+  const uint8_t* kc;   // K codes
+  const uint8_t* vc;   // V codes
+  const uint8_t* ks;   // K scales, read by lanes 0..31
+  const uint8_t* kz;   // K zero-points, read by lanes 32..63
+  const uint8_t* vs;   // V scales, lanes 0..31
+  const uint8_t* vz;   // V zero-points, lanes 32..63
+};
+
 template <int BITS>
-__device__ __forceinline__ void issue_group(uint8_t* st, int64_t g, const DecodeArgs& a, int bh,
-                                            int lane) {
+__device__ __forceinline__ GroupSrc group_src(const DecodeArgs& a, int bh, int64_t g) {
   using S = Stage<BITS>;
-  const uint8_t* kc = static_cast<const uint8_t*>(a.k_main) +
-                      (int64_t(bh) * a.main_bh_tokens + g * kGroup) * (kHeadDim * BITS / 8);
-  const uint8_t* vc = static_cast<const uint8_t*>(a.v_main) + (int64_t(bh) * a.NG + g) * S::kCodeBytes;
-#pragma unroll
-  for (int c = 0; c < S::kCodeBytes / 1024; ++c) {
-    dma16(st + S::kKc + 1024 * c, kc + 1024 * c, 16 * lane);
-    dma16(st + S::kVc + 1024 * c, vc + 1024 * c, 16 * lane);
-  }
-  const int64_t kg = (int64_t(bh) * a.NG + g) * kHeadDim;
-  const int64_t vg = int64_t(bh) * a.main_bh_tokens + g * kGroup;
-  // lanes 32..63 land 512 (128) bytes after lane 0, on the zero-points
-  if (lane < 32) {
-    dma16(st + S::kKsz, a.k_scale + kg, 16 * lane);
-    dma4(st + S::kVsz, a.v_scale + vg, 4 * lane);
+  const int64_t kg = (int64_t(bh) * a.NG + g) * kHeadDim * 4;           // bytes
+  const int64_t vg = (int64_t(bh) * a.main_bh_tokens + g * kGroup) * 4;
+  GroupSrc P;
+  P.kc = static_cast<const uint8_t*>(a.k_main) +
+         (int64_t(bh) * a.main_bh_tokens + g * kGroup) * (kHeadDim * BITS / 8) - S::kKc;
+  P.vc = static_cast<const uint8_t*>(a.v_main) + (int64_t(bh) * a.NG + g) * S::kCodeBytes -
+         (S::kVc - S::kSecond);
+  P.ks = reinterpret_cast<const uint8_t*>(a.k_scale) + kg - (S::kKsz - S::kSecond);
+  P.kz = reinterpret_cast<const uint8_t*>(a.k_zero) + kg - (S::kKsz - S::kSecond);
+  P.vs = reinterpret_cast<const uint8_t*>(a.v_scale) + vg - (S::kVsz - S::kSecond);
+  P.vz = reinterpret_cast<const uint8_t*>(a.v_zero) + vg - (S::kVsz - S::kSecond);
+  return P;
+}
+// the same wavefront's next group, kWaves groups later
+template <int BITS>
+__device__ __forceinline__ void advance(GroupSrc& P) {
+  using S = Stage<BITS>;
+  P.kc += int64_t(kWaves) * S::kCodeBytes;
+  P.vc += int64_t(kWaves) * S::kCodeBytes;
+  P.ks += int64_t(kWaves) * kHeadDim * 4;
+  P.kz += int64_t(kWaves) * kHeadDim * 4;
+  P.vs += int64_t(kWaves) * kGroup * 4;
+  P.vz += int64_t(kWaves) * kGroup * 4;
+}
+
+// Copies of one group into stage st: K codes (block 1, M0 = st), then V
+// codes, K scale | zero and V scale | zero (block 2, M0 = st + kSecond).
+// v16 = 16·lane, h16 = 16·(lane % 32), h4 = 4·(lane % 32). Stage::kLoads
+// instructions per group.
+template <int BITS>
+__device__ __forceinline__ void issue_group(uint8_t* st, const GroupSrc& P, uint32_t v16,
+                                            uint32_t h16, uint32_t h4) {
+  using S = Stage<BITS>;
+  uint32_t m;
+  uint64_t e;
+  if (BITS == 2) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, %6 nt\n\t"
+        "s_mov_b32 m0, %9\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, %7 offset:%13 nt\n\t"
+        "s_mov_b64 %1, exec\n\t"
+        "s_mov_b32 exec_hi, 0\n\t"
+        "global_load_lds_dwordx4 %4, %8 offset:%14 nt\n\t"
+        "global_load_lds_dword %5, %10 offset:%15 nt\n\t"
+        "s_mov_b64 exec, %1\n\t"
+        "s_mov_b32 exec_lo, 0\n\t"
+        "global_load_lds_dwordx4 %4, %11 offset:%14 nt\n\t"
+        "global_load_lds_dword %5, %12 offset:%15 nt\n\t"
+        "s_mov_b64 exec, %1\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(m), "=&s"(e)
+        : "s"(lds_addr(st)), "v"(v16), "v"(h16), "v"(h4), "s"(P.kc), "s"(P.vc), "s"(P.ks),
+          "s"(lds_addr(st + S::kSecond)), "s"(P.vs), "s"(P.kz), "s"(P.vz),
+          "i"(S::kVc - S::kSecond), "i"(S::kKsz - S::kSecond), "i"(S::kVsz - S::kSecond)
+        : "memory");
   } else {
-    dma16(st + S::kKsz, a.k_zero + kg, 16 * (lane - 32));
-    dma4(st + S::kVsz, a.v_zero + vg, 4 * (lane - 32));
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, %6 nt\n\t"
+        "global_load_lds_dwordx4 %3, %6 offset:1024 nt\n\t"
+        "s_mov_b32 m0, %9\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, %7 offset:%13 nt\n\t"
+        "global_load_lds_dwordx4 %3, %7 offset:%16 nt\n\t"
+        "s_mov_b64 %1, exec\n\t"
+        "s_mov_b32 exec_hi, 0\n\t"
+        "global_load_lds_dwordx4 %4, %8 offset:%14 nt\n\t"
+        "global_load_lds_dword %5, %10 offset:%15 nt\n\t"
+        "s_mov_b64 exec, %1\n\t"
+        "s_mov_b32 exec_lo, 0\n\t"
+        "global_load_lds_dwordx4 %4, %11 offset:%14 nt\n\t"
+        "global_load_lds_dword %5, %12 offset:%15 nt\n\t"
+        "s_mov_b64 exec, %1\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(m), "=&s"(e)
+        : "s"(lds_addr(st)), "v"(v16), "v"(h16), "v"(h4), "s"(P.kc), "s"(P.vc), "s"(P.ks),
+          "s"(lds_addr(st + S::kSecond)), "s"(P.vs), "s"(P.kz), "s"(P.vz),
+          "i"(S::kVc - S::kSecond), "i"(S::kKsz - S::kSecond), "i"(S::kVsz - S::kSecond),
+          "i"(S::kVc - S::kSecond + 1024)
+        : "memory");
   }
 }
 
+// Wait until at most `ahead` groups' copies are in flight.
 template <int BITS>
-__global__ __launch_bounds__(kThreads) void kivi_mfma_split_kernel(DecodeArgs a) {
+__device__ __forceinline__ void wait_groups(int ahead) {
+  using S = Stage<BITS>;
+  if (ahead >= 2) wait_vmem<2 * S::kLoads>();
+  else if (ahead == 1) wait_vmem<S::kLoads>();
+  else wait_vmem<0>();
+}
+
+template <int BITS>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(BITS == 2 ? KVQ_DECODE_WAVES_PER_SIMD : 2))) void kivi_mfma_split_kernel(
+    DecodeArgs a) {
   using S = Stage<BITS>;
   __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][S::kDepth][S::kBytes];
 
@@ -539,25 +643,55 @@ __global__ __launch_bounds__(kThreads) void kivi_mfma_split_kernel(DecodeArgs a)
     const int64_t g1 = min(g0 + int64_t(a.tiles_per_split), n_groups);
     // this wavefront's groups: g0 + wave + kWaves·i, i < n_mine
     const int n_mine = g1 - g0 > wave ? int((g1 - g0 - wave + kWaves - 1) / kWaves) : 0;
+    // Group i of this wavefront is g0 + wave + kWaves·i, in stage i % kDepth.
+    // Loads run kAhead groups ahead; group i + kAhead refills the stage of
+    // group i - 2, whose value products ran in the previous iteration.
+    constexpr int kAhead = S::kDepth - 2;
+    const uint32_t v16 = 16u * lane, h16 = 16u * (lane & 31), h4 = 4u * (lane & 31);
+    GroupSrc P = group_src<BITS>(a, bh, g0 + wave);
+    uint8_t* ring_w = &ring[wave][0][0];
 #pragma unroll
-    for (int i = 0; i < S::kDepth - 1; ++i)
-      if (i < n_mine)
-        issue_group<BITS>(&ring[wave][i % S::kDepth][0], g0 + wave + int64_t(kWaves) * i, a, bh, lane);
-    for (int i = 0; i < n_mine; ++i) {
-      if (i + S::kDepth - 1 < n_mine) {
-        // the stage being refilled was read by the previous group: its LDS
-        // reads are complete before the new data can land
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        const int j = i + S::kDepth - 1;
-        issue_group<BITS>(&ring[wave][j % S::kDepth][0], g0 + wave + int64_t(kWaves) * j, a, bh, lane);
+    for (int j = 0; j < kAhead; ++j) {
+      if (j < n_mine) {
+        issue_group<BITS>(ring_w + j * S::kBytes, P, v16, h16, h4);
+        advance<BITS>(P);
       }
-      // wait until this group's loads are done (loads complete in order)
-      const int ahead = min(S::kDepth - 1, n_mine - 1 - i);
-      if (ahead >= 3) wait_vmem<3 * S::kLoads>();
-      else if (ahead == 2) wait_vmem<2 * S::kLoads>();
-      else if (ahead == 1) wait_vmem<S::kLoads>();
-      else wait_vmem<0>();
-      process_group<BITS>(&ring[wave][i % S::kDepth][0], W, r, u, low, q16, vsh, vm0, vm1, magic);
+    }
+    if (n_mine > 0) {
+      float sc[4];
+      float4 vs, vz;
+      if (kAhead < n_mine) {
+        issue_group<BITS>(ring_w + kAhead * S::kBytes, P, v16, h16, h4);
+        advance<BITS>(P);
+        wait_vmem<kAhead * S::kLoads>();
+      } else {
+        wait_groups<BITS>(n_mine - 1);
+      }
+      group_scores<BITS>(ring_w, r, u, low, q16, sc, vs, vz);
+      u32x4 bp_prev = group_probs<BITS>(W, sc, vs, vz);
+      int i = 1;
+      // steady state: a group is loaded every iteration, one fixed wait
+      for (; i + kAhead < n_mine; ++i) {
+        // the refilled stage was last read two groups ago; its reads are done
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        issue_group<BITS>(ring_w + ((i + kAhead) % S::kDepth) * S::kBytes, P, v16, h16, h4);
+        advance<BITS>(P);
+        wait_vmem<kAhead * S::kLoads>();
+        group_scores<BITS>(ring_w + (i % S::kDepth) * S::kBytes, r, u, low, q16, sc, vs, vz);
+        group_values<BITS>(ring_w + ((i - 1) % S::kDepth) * S::kBytes, W, bp_prev, r, u, vsh,
+                           vm0, vm1, magic);
+        bp_prev = group_probs<BITS>(W, sc, vs, vz);
+      }
+      // the last kAhead groups: nothing left to load
+      for (; i < n_mine; ++i) {
+        wait_groups<BITS>(n_mine - 1 - i);
+        group_scores<BITS>(ring_w + (i % S::kDepth) * S::kBytes, r, u, low, q16, sc, vs, vz);
+        group_values<BITS>(ring_w + ((i - 1) % S::kDepth) * S::kBytes, W, bp_prev, r, u, vsh,
+                           vm0, vm1, magic);
+        bp_prev = group_probs<BITS>(W, sc, vs, vz);
+      }
+      group_values<BITS>(ring_w + ((n_mine - 1) % S::kDepth) * S::kBytes, W, bp_prev, r, u, vsh,
+                         vm0, vm1, magic);
     }
   } else {
     // the FP16 window: q·log2e/√D as fp16 high/low terms, channel 32s + 8u + j
