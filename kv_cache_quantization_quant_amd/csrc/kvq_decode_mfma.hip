@@ -252,54 +252,92 @@ __device__ __forceinline__ u32x4 p_operand(const float (&pp)[4]) {
   return u32x4{hp[0], hp[1], lp[0], lp[1]};
 }
 
-// A group runs in three phases. The main loop overlaps the scores of group i
-// with the value products of group i - 1 (independent instruction streams in
-// one basic block), then turns the scores of group i into probabilities.
+// A group runs in three phases: scores, probabilities, value products. Each
+// iteration of the main loop first issues all of its LDS reads (the V codes
+// of group i - 1, the K codes and scales of group i), then computes the
+// scores of group i and the value products of group i - 1 (independent
+// instruction streams in one basic block), then turns the scores of group i
+// into probabilities.
 
-// Scores of the four tokens this lane keeps (log2 units), and the V scale /
-// zero-point of those tokens (16·part + 4u + i).
+// LDS data of one group for one lane: K codes of tokens r and 16 + r
+// (channels 32u..32u+31), K scale and zero-point of the lane's 16 channels,
+// V scale and zero-point of the tokens it keeps (16·part + 4u + i).
 template <int BITS>
-__device__ __forceinline__ void group_scores(const uint8_t* st, int r, int u, bool low,
-                                             const float (&q16)[16], float (&sc)[4], float4& vs,
-                                             float4& vz) {
-  using S = Stage<BITS>;
-  const float* ksz = reinterpret_cast<const float*>(st + S::kKsz) + 32 * u + (low ? 16 : 0);
-  // ---- LDS reads first: K codes of tokens r and 16 + r (channels 32u..32u+31),
-  // K scale and zero-point of this lane's 16 channels
+struct KLoad {
   uint32_t w0[BITS], w1[BITS];
-  {
-    const uint8_t* kc = st + S::kKc;
-    constexpr int kRow = kHeadDim * BITS / 8;
+  float4 ks[4], kz[4];
+  float4 vs, vz;
+};
+// V code words of channel 16n + r (n = 0..7) that lane group u needs
+struct VLoad {
+  uint32_t w[8][2];
+};
+
+template <int BITS>
+__device__ __forceinline__ void load_k(const uint8_t* st, int r, int u, bool low, KLoad<BITS>& K) {
+  using S = Stage<BITS>;
+  const uint8_t* kc = st + S::kKc;
+  constexpr int kRow = kHeadDim * BITS / 8;
+  if (BITS == 2) {
+    const uint2 x = *reinterpret_cast<const uint2*>(kc + r * kRow + 8 * u);
+    const uint2 y = *reinterpret_cast<const uint2*>(kc + (16 + r) * kRow + 8 * u);
+    K.w0[0] = x.x; K.w0[1] = x.y; K.w1[0] = y.x; K.w1[1] = y.y;
+  } else {
+    const uint4 x = *reinterpret_cast<const uint4*>(kc + r * kRow + 16 * u);
+    const uint4 y = *reinterpret_cast<const uint4*>(kc + (16 + r) * kRow + 16 * u);
+    K.w0[0] = x.x; K.w0[1] = x.y; K.w0[2] = x.z; K.w0[3] = x.w;
+    K.w1[0] = y.x; K.w1[1] = y.y; K.w1[2] = y.z; K.w1[3] = y.w;
+  }
+  const float4* ksz = reinterpret_cast<const float4*>(st + S::kKsz) + 8 * u + (low ? 4 : 0);
+#pragma unroll
+  for (int c4 = 0; c4 < 4; ++c4) K.kz[c4] = ksz[kHeadDim / 4 + c4];
+#pragma unroll
+  for (int c4 = 0; c4 < 4; ++c4) K.ks[c4] = ksz[c4];
+  const float4* vsz = reinterpret_cast<const float4*>(st + S::kVsz) + (low ? 4 : 0) + u;
+  K.vs = vsz[0];
+  K.vz = vsz[kGroup / 4];
+}
+
+template <int BITS>
+__device__ __forceinline__ void load_v(const uint8_t* st, int r, int u, VLoad& V) {
+  using S = Stage<BITS>;
+  const uint8_t* vc = st + S::kVc;
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
     if (BITS == 2) {
-      const uint2 x = *reinterpret_cast<const uint2*>(kc + r * kRow + 8 * u);
-      const uint2 y = *reinterpret_cast<const uint2*>(kc + (16 + r) * kRow + 8 * u);
-      w0[0] = x.x; w0[1] = x.y; w1[0] = y.x; w1[1] = y.y;
+      const uint2 x = *reinterpret_cast<const uint2*>(vc + (16 * n + r) * 8);
+      V.w[n][0] = x.x;
+      V.w[n][1] = x.y;
     } else {
-      const uint4 x = *reinterpret_cast<const uint4*>(kc + r * kRow + 16 * u);
-      const uint4 y = *reinterpret_cast<const uint4*>(kc + (16 + r) * kRow + 16 * u);
-      w0[0] = x.x; w0[1] = x.y; w0[2] = x.z; w0[3] = x.w;
-      w1[0] = y.x; w1[1] = y.y; w1[2] = y.z; w1[3] = y.w;
+      const uint32_t* cw = reinterpret_cast<const uint32_t*>(vc + (16 * n + r) * 16);
+      V.w[n][0] = cw[u / 2];
+      V.w[n][1] = cw[2 + u / 2];
     }
   }
-  float ks[16], kz[16];
-#pragma unroll
-  for (int c4 = 0; c4 < 4; ++c4) {
-    const float4 a = *reinterpret_cast<const float4*>(ksz + 4 * c4);
-    ks[4 * c4] = a.x; ks[4 * c4 + 1] = a.y; ks[4 * c4 + 2] = a.z; ks[4 * c4 + 3] = a.w;
-  }
-#pragma unroll
-  for (int c4 = 0; c4 < 4; ++c4) {
-    const float4 z = *reinterpret_cast<const float4*>(ksz + kHeadDim + 4 * c4);
-    kz[4 * c4] = z.x; kz[4 * c4 + 1] = z.y; kz[4 * c4 + 2] = z.z; kz[4 * c4 + 3] = z.w;
-  }
+}
+
+__device__ __forceinline__ float f4_at(const float4 (&v)[4], int i) {
+  const float4 x = v[i / 4];
+  return (i % 4 == 0) ? x.x : (i % 4 == 1) ? x.y : (i % 4 == 2) ? x.z : x.w;
+}
+
+// Scores of the four tokens this lane keeps (log2 units).
+template <int BITS>
+__device__ __forceinline__ void group_scores(const KLoad<BITS>& K, bool low,
+                                             const float (&q16)[16], float (&sc)[4]) {
   uint32_t m0[2 * BITS], m1[2 * BITS];
-  k_masks<BITS>(w0, m0);
-  k_masks<BITS>(w1, m1);
+  k_masks<BITS>(K.w0, m0);
+  k_masks<BITS>(K.w1, m1);
   // ---- z-term of this lane's 16 channels, summed over the four lane groups u
-  float zt = 0.0f;
+  // (four independent partial sums: a 16-long dependent chain would stall)
+  float zp[4];
 #pragma unroll
-  for (int c = 0; c < 16; ++c) zt = fmaf(q16[c], kz[c], zt);
-  zt = sum_x16_x32(zt);
+  for (int j = 0; j < 4; ++j) {
+    const float4 z = K.kz[j];
+    zp[j] = fmaf(q16[4 * j + 3], z.w, fmaf(q16[4 * j + 2], z.z,
+                 fmaf(q16[4 * j + 1], z.y, q16[4 * j] * z.x)));
+  }
+  const float zt = sum_x16_x32((zp[0] + zp[1]) + (zp[2] + zp[3]));
   f32x4 s0 = f32x4{zt, zt, zt, zt}, s1 = s0;
   // ---- scores: local k-step h is global k-step h (part 0) or 2 + h (part 1)
 #pragma unroll
@@ -307,9 +345,9 @@ __device__ __forceinline__ void group_scores(const uint8_t* st, int r, int u, bo
     uint32_t hi[4], lo[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const int c0 = kslot_channel(2 * p), c1 = kslot_channel(2 * p + 1);
-      const float a0 = q16[8 * h + c0], b0 = ks[8 * h + c0];
-      const float a1 = q16[8 * h + c1], b1 = ks[8 * h + c1];
+      const int c0 = 8 * h + kslot_channel(2 * p), c1 = 8 * h + kslot_channel(2 * p + 1);
+      const float a0 = q16[c0], b0 = f4_at(K.ks, c0);
+      const float a1 = q16[c1], b1 = f4_at(K.ks, c1);
       hi[p] = mix_pair(a0, b0, a1, b1);
       lo[p] = mix_pair_sub(a0, b0, a1, b1, hi[p]);
     }
@@ -335,9 +373,6 @@ __device__ __forceinline__ void group_scores(const uint8_t* st, int r, int u, bo
     const float t1 = s1[i] + xor8(s1[i]);
     sc[i] = low ? t1 : t0;
   }
-  const float* vsz = reinterpret_cast<const float*>(st + S::kVsz) + (low ? 16 : 0) + 4 * u;
-  vs = *reinterpret_cast<const float4*>(vsz);
-  vz = *reinterpret_cast<const float4*>(vsz + kGroup);
 }
 
 // Online-softmax step for the group's scores; returns the B operand P' of its
@@ -362,24 +397,19 @@ __device__ __forceinline__ u32x4 group_probs(WaveAcc& W, const float (&sc)[4], f
 // P'·V of one group: 8 tiles of 16 channels, codes in the mantissa of 128.0,
 // plus the column sums of P' that remove the 128 offset.
 template <int BITS>
-__device__ __forceinline__ void group_values(const uint8_t* st, WaveAcc& W, u32x4 bp, int r,
-                                             int u, uint32_t vsh, uint32_t vm0, uint32_t vm1,
-                                             uint32_t magic) {
-  using S = Stage<BITS>;
-  const uint8_t* vc = st + S::kVc;
+__device__ __forceinline__ void group_values(const VLoad& V, WaveAcc& W, u32x4 bp, uint32_t vsh,
+                                             uint32_t vm0, uint32_t vm1, uint32_t magic) {
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
     uint32_t d[4];
     if (BITS == 2) {
-      const uint2 x = *reinterpret_cast<const uint2*>(vc + (16 * n + r) * 8);
-      const uint32_t v0 = x.x >> vsh, v1 = x.y >> vsh;
+      const uint32_t v0 = V.w[n][0] >> vsh, v1 = V.w[n][1] >> vsh;
       d[0] = bfi(vm0, v0, magic);
       d[1] = bfi(vm1, v0, magic);
       d[2] = bfi(vm0, v1, magic);
       d[3] = bfi(vm1, v1, magic);
     } else {
-      const uint32_t* cw = reinterpret_cast<const uint32_t*>(vc + (16 * n + r) * 16);
-      const uint32_t v0 = cw[u / 2], v1 = cw[2 + u / 2];
+      const uint32_t v0 = V.w[n][0], v1 = V.w[n][1];
       d[0] = bfi(vm0, v0 >> vsh, magic);
       d[1] = bfi(vm0, v0 >> (vsh + 4), magic);
       d[2] = bfi(vm0, v1 >> vsh, magic);
@@ -659,7 +689,6 @@ __attribute__((amdgpu_waves_per_eu(BITS == 2 ? KVQ_DECODE_WAVES_PER_SIMD : 2))) 
     }
     if (n_mine > 0) {
       float sc[4];
-      float4 vs, vz;
       if (kAhead < n_mine) {
         issue_group<BITS>(ring_w + kAhead * S::kBytes, P, v16, h16, h4);
         advance<BITS>(P);
@@ -667,8 +696,11 @@ __attribute__((amdgpu_waves_per_eu(BITS == 2 ? KVQ_DECODE_WAVES_PER_SIMD : 2))) 
       } else {
         wait_groups<BITS>(n_mine - 1);
       }
-      group_scores<BITS>(ring_w, r, u, low, q16, sc, vs, vz);
-      u32x4 bp_prev = group_probs<BITS>(W, sc, vs, vz);
+      KLoad<BITS> K;
+      VLoad V;
+      load_k<BITS>(ring_w, r, u, low, K);
+      group_scores<BITS>(K, low, q16, sc);
+      u32x4 bp_prev = group_probs<BITS>(W, sc, K.vs, K.vz);
       int i = 1;
       // steady state: a group is loaded every iteration, one fixed wait
       for (; i + kAhead < n_mine; ++i) {
@@ -677,21 +709,27 @@ __attribute__((amdgpu_waves_per_eu(BITS == 2 ? KVQ_DECODE_WAVES_PER_SIMD : 2))) 
         issue_group<BITS>(ring_w + ((i + kAhead) % S::kDepth) * S::kBytes, P, v16, h16, h4);
         advance<BITS>(P);
         wait_vmem<kAhead * S::kLoads>();
-        group_scores<BITS>(ring_w + (i % S::kDepth) * S::kBytes, r, u, low, q16, sc, vs, vz);
-        group_values<BITS>(ring_w + ((i - 1) % S::kDepth) * S::kBytes, W, bp_prev, r, u, vsh,
-                           vm0, vm1, magic);
-        bp_prev = group_probs<BITS>(W, sc, vs, vz);
+        load_v<BITS>(ring_w + ((i - 1) % S::kDepth) * S::kBytes, r, u, V);
+        load_k<BITS>(ring_w + (i % S::kDepth) * S::kBytes, r, u, low, K);
+        // keep every LDS read of the iteration ahead of the arithmetic
+        __builtin_amdgcn_sched_barrier(0);
+        group_scores<BITS>(K, low, q16, sc);
+        group_values<BITS>(V, W, bp_prev, vsh, vm0, vm1, magic);
+        bp_prev = group_probs<BITS>(W, sc, K.vs, K.vz);
       }
       // the last kAhead groups: nothing left to load
       for (; i < n_mine; ++i) {
         wait_groups<BITS>(n_mine - 1 - i);
-        group_scores<BITS>(ring_w + (i % S::kDepth) * S::kBytes, r, u, low, q16, sc, vs, vz);
-        group_values<BITS>(ring_w + ((i - 1) % S::kDepth) * S::kBytes, W, bp_prev, r, u, vsh,
-                           vm0, vm1, magic);
-        bp_prev = group_probs<BITS>(W, sc, vs, vz);
+        load_v<BITS>(ring_w + ((i - 1) % S::kDepth) * S::kBytes, r, u, V);
+        load_k<BITS>(ring_w + (i % S::kDepth) * S::kBytes, r, u, low, K);
+        // keep every LDS read of the iteration ahead of the arithmetic
+        __builtin_amdgcn_sched_barrier(0);
+        group_scores<BITS>(K, low, q16, sc);
+        group_values<BITS>(V, W, bp_prev, vsh, vm0, vm1, magic);
+        bp_prev = group_probs<BITS>(W, sc, K.vs, K.vz);
       }
-      group_values<BITS>(ring_w + ((n_mine - 1) % S::kDepth) * S::kBytes, W, bp_prev, r, u, vsh,
-                         vm0, vm1, magic);
+      load_v<BITS>(ring_w + ((n_mine - 1) % S::kDepth) * S::kBytes, r, u, V);
+      group_values<BITS>(V, W, bp_prev, vsh, vm0, vm1, magic);
     }
   } else {
     // the FP16 window: q·log2e/√D as fp16 high/low terms, channel 32s + 8u + j
