@@ -141,6 +141,17 @@ __device__ __forceinline__ uint32_t mix_pair_sub(float a0, float b0, float a1, f
       : "+v"(d) : "v"(a1), "v"(b1), "v"(c));
   return d;
 }
+// fp16 high and low terms of x0 and x1, packed: high = x rounded toward zero
+// to fp16 (in fp16's normal range that is x with its fp32 mantissa cut to 10
+// bits), low = the exact remainder rounded toward zero; together 22
+// significant bits. Only 4-byte instructions (the mixed-precision FMA form
+// costs about three of them on gfx950). Requires |x| < 65504.
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x0, x1));
+  const float r0 = x0 - __uint_as_float(__float_as_uint(x0) & 0xFFFFE000u);
+  const float r1 = x1 - __uint_as_float(__float_as_uint(x1) & 0xFFFFE000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+}
 // (mask & x) | (~mask & y) in one instruction
 __device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t x, uint32_t y) {
   uint32_t d;
@@ -346,10 +357,7 @@ __device__ __forceinline__ void group_scores(const KLoad<BITS>& K, bool low,
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int c0 = 8 * h + kslot_channel(2 * p), c1 = 8 * h + kslot_channel(2 * p + 1);
-      const float a0 = q16[c0], b0 = f4_at(K.ks, c0);
-      const float a1 = q16[c1], b1 = f4_at(K.ks, c1);
-      hi[p] = mix_pair(a0, b0, a1, b1);
-      lo[p] = mix_pair_sub(a0, b0, a1, b1, hi[p]);
+      split_pair(q16[c0] * f4_at(K.ks, c0), q16[c1] * f4_at(K.ks, c1), hi[p], lo[p]);
     }
     // part 0 takes the partner's high terms (k-step 2 + h), part 1 the
     // partner's low terms (k-step h)
