@@ -94,12 +94,15 @@
  *   v_scale, v_zero  fp32 [B][H][CT]      (per token)
  *   k_resid, v_resid fp16 [B][H][Rcap][D] the FP16 residual window; slot i
  *            holds token n_quant + i.
- * FP8 E4M3:
- *   k_codes, v_codes uint8 [B][H][C][D];
- *   tensor_scale fp32 [4] = {s_K, s_V, amax_K, amax_V} (the amax slots are
- *   scratch of the prefill reduction).
- * FP16 (baseline, no quantization):
- *   k_codes, v_codes fp16 [B][H][C][D].
+ * FP8 E4M3 and FP16 (baseline, no quantization) use tiles of T = 32 tokens,
+ * NT = ceil(C / T), CTT = NT · T:
+ *   k_codes  [B][H][CTT][D]   token rows (uint8 E4M3 codes, or fp16 values);
+ *   v_codes  [B][H][NT][D][T] tile g, channel d: the values of tokens
+ *            g·T .. g·T + T − 1 (element (t, d) at [t / T][d][t % T]);
+ *            slots between the last prefilled token and the end of its tile
+ *            are written as zero.
+ *   tensor_scale (FP8 only) fp32 [4] = {s_K, s_V, amax_K, amax_V} (the amax
+ *   slots are scratch of the prefill reduction).
  * Decode I/O: q, out fp32 [B][Hq][D]. Query head hq reads KV head
  *   hq / (Hq / H) (consecutive query heads share a KV head, [Tutorial] §五.3).
  */

@@ -262,11 +262,13 @@ class DeviceCache:
                       "k_resid": (torch.float16, (B, H, Rcap, D)),
                       "v_resid": (torch.float16, (B, H, Rcap, D))}
         elif c.format == KVQ_FMT_FP8_E4M3:
-            shapes = {"k_codes": (torch.uint8, (B, H, c.capacity, D)),
-                      "v_codes": (torch.uint8, (B, H, c.capacity, D)),
+            NT = -(-c.capacity // 32)
+            shapes = {"k_codes": (torch.uint8, (B, H, NT * 32, D)),
+                      "v_codes": (torch.uint8, (B, H, NT, D, 32)),
                       "tensor_scale": (torch.float32, (4,))}
         else:
-            shapes = {"k_codes": (torch.float16, (B, H, c.capacity, D)),
-                      "v_codes": (torch.float16, (B, H, c.capacity, D))}
+            NT = -(-c.capacity // 32)
+            shapes = {"k_codes": (torch.float16, (B, H, NT * 32, D)),
+                      "v_codes": (torch.float16, (B, H, NT, D, 32))}
         dt, shape = shapes[name]
         return buf.view(dt).view(shape)

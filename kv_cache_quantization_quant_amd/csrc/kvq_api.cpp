@@ -105,6 +105,24 @@ bool state_ok(const kvq_cache* c, const Dims& d) {
   return c->n_resid == 0;
 }
 
+// V of an FP8 / FP16 cache: source tokens [0, n) of an fp16 [B·H][..][D]
+// tensor (bh stride in elements) into cache tokens [t0, t0 + n).
+kvq::VTileArgs v_tile_args(const kvq_cache* c, const Dims& d, const __half* v,
+                           int64_t src_bh_stride, int64_t n, int64_t t0, bool zero_tail) {
+  kvq::VTileArgs a{};
+  a.v_src = v;
+  a.src_bh_stride = src_bh_stride;
+  a.n_tokens = n;
+  a.dst_t0 = t0;
+  a.v_dst = c->v_codes;
+  a.NT = d.NG;
+  a.bh_count = int(d.B * d.H);
+  a.fp8 = c->cfg.format == KVQ_FMT_FP8_E4M3 ? 1 : 0;
+  a.zero_tail = zero_tail ? 1 : 0;
+  a.tensor_scale = c->tensor_scale;
+  return a;
+}
+
 // Query heads one decode workgroup handles: the largest power of two ≤ 8
 // dividing Hq / H.
 int heads_per_chunk(int nq) {
@@ -178,11 +196,11 @@ kvq_status kvq_layout_query(const kvq_config* cfg, kvq_layout* out) {
       out->k_resid = out->v_resid = bh * d.Rcap * d.D * 2;
       break;
     case KVQ_FMT_FP8_E4M3:
-      out->k_codes = out->v_codes = bh * d.C * d.D;
+      out->k_codes = out->v_codes = bh * d.CT * d.D;
       out->tensor_scale = 4 * sizeof(float);
       break;
     default:
-      out->k_codes = out->v_codes = bh * d.C * d.D * 2;
+      out->k_codes = out->v_codes = bh * d.CT * d.D * 2;
   }
   return KVQ_OK;
 }
@@ -270,12 +288,15 @@ kvq_status kvq_prefill_quantize(kvq_cache* cache, const void* k, const void* v,
     fa.src_bh_stride = seq_len * d.D;
     fa.n_tokens = seq_len;
     fa.k_codes = static_cast<uint8_t*>(cache->k_codes);
-    fa.v_codes = static_cast<uint8_t*>(cache->v_codes);
-    fa.dst_bh_stride = d.C * d.D;
+    fa.v_codes = nullptr;                       // V goes to tiles below
+    fa.dst_bh_stride = d.CT * d.D;
     fa.dst_t0 = 0;
     fa.bh_count = bh;
     fa.tensor_scale = cache->tensor_scale;
     if (kvq::launch_fp8_prefill(fa, s) != hipSuccess) return KVQ_ERR_DEVICE;
+    if (kvq::launch_v_tiles(v_tile_args(cache, d, vh, seq_len * d.D, seq_len, 0, true), s) !=
+        hipSuccess)
+      return KVQ_ERR_DEVICE;
     cache->n_quant = seq_len;
     return KVQ_OK;
   }
@@ -284,12 +305,15 @@ kvq_status kvq_prefill_quantize(kvq_cache* cache, const void* k, const void* v,
   ca.v_src = vh;
   ca.src_bh_stride = seq_len * d.D;
   ca.k_dst = static_cast<__half*>(cache->k_codes);
-  ca.v_dst = static_cast<__half*>(cache->v_codes);
-  ca.dst_bh_stride = d.C * d.D;
+  ca.v_dst = nullptr;                           // V goes to tiles below
+  ca.dst_bh_stride = d.CT * d.D;
   ca.dst_t0 = 0;
   ca.n_tokens = seq_len;
   ca.bh_count = bh;
   if (kvq::launch_copy_tokens(ca, s) != hipSuccess) return KVQ_ERR_DEVICE;
+  if (kvq::launch_v_tiles(v_tile_args(cache, d, vh, seq_len * d.D, seq_len, 0, true), s) !=
+      hipSuccess)
+    return KVQ_ERR_DEVICE;
   cache->n_quant = seq_len;
   return KVQ_OK;
 }
@@ -352,12 +376,15 @@ kvq_status kvq_append_token(kvq_cache* cache, const void* k_new, const void* v_n
     fa.src_bh_stride = d.D;
     fa.n_tokens = 1;
     fa.k_codes = static_cast<uint8_t*>(cache->k_codes);
-    fa.v_codes = static_cast<uint8_t*>(cache->v_codes);
-    fa.dst_bh_stride = d.C * d.D;
+    fa.v_codes = nullptr;
+    fa.dst_bh_stride = d.CT * d.D;
     fa.dst_t0 = cache->n_quant;
     fa.bh_count = bh;
     fa.tensor_scale = cache->tensor_scale;
     if (kvq::launch_fp8_append(fa, s) != hipSuccess) return KVQ_ERR_DEVICE;
+    if (kvq::launch_v_tiles(v_tile_args(cache, d, vh, d.D, 1, cache->n_quant, false), s) !=
+        hipSuccess)
+      return KVQ_ERR_DEVICE;
     cache->n_quant += 1;
     return KVQ_OK;
   }
@@ -366,12 +393,15 @@ kvq_status kvq_append_token(kvq_cache* cache, const void* k_new, const void* v_n
   ca.v_src = vh;
   ca.src_bh_stride = d.D;
   ca.k_dst = static_cast<__half*>(cache->k_codes);
-  ca.v_dst = static_cast<__half*>(cache->v_codes);
-  ca.dst_bh_stride = d.C * d.D;
+  ca.v_dst = nullptr;
+  ca.dst_bh_stride = d.CT * d.D;
   ca.dst_t0 = cache->n_quant;
   ca.n_tokens = 1;
   ca.bh_count = bh;
   if (kvq::launch_copy_tokens(ca, s) != hipSuccess) return KVQ_ERR_DEVICE;
+  if (kvq::launch_v_tiles(v_tile_args(cache, d, vh, d.D, 1, cache->n_quant, false), s) !=
+      hipSuccess)
+    return KVQ_ERR_DEVICE;
   cache->n_quant += 1;
   return KVQ_OK;
 }
@@ -423,7 +453,7 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q, int32_t 
   a.v_zero = cache->v_zero;
   a.tensor_scale = cache->tensor_scale;
   a.NG = d.NG;
-  a.main_bh_tokens = kivi ? d.CT : d.C;
+  a.main_bh_tokens = d.CT;
   a.n_main = cache->n_quant;
   a.k_win = static_cast<const __half*>(cache->k_resid);
   a.v_win = static_cast<const __half*>(cache->v_resid);

@@ -227,9 +227,10 @@ struct WaveAcc {
 };
 
 // Softmax step for four scores, then P'·V for one group or window tile.
-__device__ __forceinline__ void rescale_if_needed(WaveAcc& W, const float (&sc)[4]) {
+__device__ __forceinline__ void rescale_if_needed(WaveAcc& W, const float (&sc)[4],
+                                                  float lazy = kLazy) {
   const float lmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-  if (__any(lmax > W.m_ref + kLazy)) {           // wave-uniform, rare
+  if (__any(lmax > W.m_ref + lazy)) {            // wave-uniform, rare
     const float m_new = fmaxf(W.m_ref, head_max(lmax));
     const float alpha = fast_exp2(W.m_ref - m_new);
     W.l_acc *= alpha;
@@ -513,6 +514,63 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)(p)));
 }
 
+// Wave epilogue and workgroup merge, shared by the decode kernels: head
+// totals, removal of the 128 offset of the value codes (zero when unused),
+// high + low columns, times oscale; then the four wave states are merged
+// through LDS (each wave's results go to the start of its own ring region,
+// `wave_stride` bytes apart) into this split's partial (o[D], m, l).
+__device__ __forceinline__ void wave_epilogue_and_merge(const DecodeArgs& a, const WaveAcc& W,
+                                                        uint8_t* ring, size_t wave_stride,
+                                                        int wave, int lane, int hs, int u,
+                                                        bool low, int tid, int b, int hq0,
+                                                        int nh, int split, float oscale) {
+  float* mo = reinterpret_cast<float*>(ring + wave * wave_stride);     // [8][kHeadDim]
+  float* ml = mo + 8 * kHeadDim;                                         // [8][2]
+  const float l_tot = head_sum(W.l_acc);
+  const float pz_tot = head_sum(W.pz_acc);
+  const float off = 128.0f * (W.cones[0] + xor8(W.cones[0]));
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    f32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = (W.cv[n][i] + xor8(W.cv[n][i]) - off + pz_tot) * oscale;
+    if (!low) *reinterpret_cast<f32x4*>(&mo[hs * kHeadDim + 16 * n + 4 * u]) = o;
+  }
+  if (lane < 8) {
+    ml[2 * hs] = W.m_ref;
+    ml[2 * hs + 1] = l_tot;
+  }
+  __syncthreads();
+  for (int i = tid; i < nh * kHeadDim; i += kThreads) {
+    const int h = i / kHeadDim;
+    const int d = i % kHeadDim;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float* mlw = reinterpret_cast<const float*>(ring + w * wave_stride) + 8 * kHeadDim;
+      M = fmaxf(M, mlw[2 * h]);
+    }
+    float O = 0.0f, L = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float* mow = reinterpret_cast<const float*>(ring + w * wave_stride);
+        const float* mlw = mow + 8 * kHeadDim;
+        const float mw = mlw[2 * h];
+        const float f = mw == -INFINITY ? 0.0f : exp2f(mw - M);
+        O = fmaf(f, mow[h * kHeadDim + d], O);
+        L = fmaf(f, mlw[2 * h + 1], L);
+      }
+    }
+    float* part = a.ws + ((int64_t(b) * a.Hq + hq0 + h) * a.n_split + split) * kPart;
+    part[d] = O;
+    if (d == 0) {
+      part[kHeadDim] = M;
+      part[kHeadDim + 1] = L;
+    }
+  }
+}
+
 // Wave-uniform, offset-biased sources of the next group a wavefront loads.
 struct GroupSrc {
   const uint8_t* kc;   // K codes
@@ -765,58 +823,238 @@ __attribute__((amdgpu_waves_per_eu(BITS == 2 ? KVQ_DECODE_WAVES_PER_SIMD : 2))) 
       process_window_tile(a, W, bh, tile, bqw, r, u, low);
   }
 
-  // ---- wave epilogue: head totals, offset removal, high + low columns. The
-  // wave's own ring stages hold its results (all its loads have completed).
-  float* mo = reinterpret_cast<float*>(&ring[wave][0][0]);     // [8][kHeadDim]
-  float* ml = mo + 8 * kHeadDim;                                 // [8][2]
-  const float l_tot = head_sum(W.l_acc);
-  const float pz_tot = head_sum(W.pz_acc);
-  const float off = 128.0f * (W.cones[0] + xor8(W.cones[0]));
-#pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    f32x4 o;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = W.cv[n][i] + xor8(W.cv[n][i]) - off + pz_tot;
-    if (!low) *reinterpret_cast<f32x4*>(&mo[hs * kHeadDim + 16 * n + 4 * u]) = o;
-  }
-  if (lane < 8) {
-    ml[2 * hs] = W.m_ref;
-    ml[2 * hs + 1] = l_tot;
-  }
-  __syncthreads();
+  wave_epilogue_and_merge(a, W, &ring[0][0][0], sizeof(ring[0]), wave, lane, hs, u, low, tid,
+                          b, hq0, nh, split, 1.0f);
+}
 
-  // ---- merge the four wave states, write this split's partials
-  for (int i = tid; i < nh * kHeadDim; i += kThreads) {
-    const int h = i / kHeadDim;
-    const int d = i % kHeadDim;
-    float M = -INFINITY;
+// ===================================================================== FP8 / FP16
+// Decode over the FP8 and FP16 caches ("大模型量化从0到1（十三）：KV Cache 量化", §二
+// and §十 FP8 formula: x̂ = e4m3_value(code) · s_tensor), same split-K
+// structure and online softmax as the KIVI kernel, 32-token tiles streamed
+// through an LDS ring. K rows [CT][D] and V tiles [D][32] enter the f16
+// matrix cores directly (FP8 codes through the exact E4M3 → fp16 scaled
+// conversion): scores A = K rows, B = q·log2(e)/√D (·s_K) as a constant fp16
+// high/low pair; values A = V tile rows, B = p as an fp16 high/low pair, so
+// p must stay below fp16's maximum: the reference maximum is raised when a
+// score exceeds it by 14 (p ≤ 2^14). s_V scales the output at the end.
+
+constexpr float kLazyDense = 14.0f;
+
+template <int SRC>
+struct DenseStage {
+  static constexpr int kElem = SRC == kSrcFp16 ? 2 : 1;
+  static constexpr int kRows = kGroup * kHeadDim * kElem;   // K rows (= V tile) of a tile
+  static constexpr int kBytes = 2 * kRows;
+  static constexpr int kDepth = SRC == kSrcFp16 ? 2 : 3;    // stages per wavefront
+  static constexpr int kLoads = kBytes / 1024;              // copies per tile
+};
+
+// one 16-byte-per-lane copy (1 KiB per wavefront), M0 saved and restored
+__device__ __forceinline__ void dma_kib(void* lds, const void* base, uint32_t voff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3 nt\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved) : "s"(lds_addr(lds)), "v"(voff), "s"(base) : "memory");
+}
+
+template <int SRC>
+__device__ __forceinline__ void issue_tile(uint8_t* st, const DecodeArgs& a, int bh, int64_t tile,
+                                           uint32_t v16) {
+  using S = DenseStage<SRC>;
+  const uint8_t* kr = static_cast<const uint8_t*>(a.k_main) +
+                      (int64_t(bh) * a.main_bh_tokens + tile * kGroup) * kHeadDim * S::kElem;
+  const uint8_t* vt = static_cast<const uint8_t*>(a.v_main) +
+                      (int64_t(bh) * a.NG + tile) * int64_t(S::kRows);
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float* mlw = reinterpret_cast<const float*>(&ring[w][0][0]) + 8 * kHeadDim;
-      M = fmaxf(M, mlw[2 * h]);
-    }
-    float O = 0.0f, L = 0.0f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float* mow = reinterpret_cast<const float*>(&ring[w][0][0]);
-        const float* mlw = mow + 8 * kHeadDim;
-        const float mw = mlw[2 * h];
-        const float f = mw == -INFINITY ? 0.0f : exp2f(mw - M);
-        O = fmaf(f, mow[h * kHeadDim + d], O);
-        L = fmaf(f, mlw[2 * h + 1], L);
-      }
-    }
-    float* part = a.ws + ((int64_t(b) * a.Hq + hq0 + h) * a.n_split + split) * kPart;
-    part[d] = O;
-    if (d == 0) {
-      part[kHeadDim] = M;
-      part[kHeadDim + 1] = L;
-    }
+  for (int c = 0; c < S::kRows / 1024; ++c) {
+    dma_kib(st + 1024 * c, kr + 1024 * c, v16);
+    dma_kib(st + S::kRows + 1024 * c, vt + 1024 * c, v16);
   }
 }
 
+// fp16 pair from two E4M3 bytes (half-word `high` of w), exact
+__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w, bool high) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f16x2 r = high ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)
+                       : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// fp16 high / low terms of four p values; part 0 ends with the high terms of
+// tile 0 (own) and tile 1 (partner's), part 1 with the low terms of tile 0
+// (partner's) and tile 1 (own).
+__device__ __forceinline__ u32x4 p_operand_f16(const float (&pp)[4]) {
+  uint32_t hp[2], lp[2];
+  split_pair(pp[0], pp[1], hp[0], lp[0]);
+  split_pair(pp[2], pp[3], hp[1], lp[1]);
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const uint32_t t = lp[p];
+    lp[p] = from_partner<0x3>(lp[p], hp[p]);
+    hp[p] = from_partner<0xC>(hp[p], t);
+  }
+  return u32x4{hp[0], hp[1], lp[0], lp[1]};
+}
+
+template <int SRC>
+__device__ __forceinline__ void process_dense_tile(const uint8_t* st, WaveAcc& W, int n_in,
+                                                   const u32x4 (&bq)[4], int r, int u,
+                                                   bool low) {
+  using S = DenseStage<SRC>;
+  // ---- scores
+  f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+  for (int sl = 0; sl < 4; ++sl) {
+    u32x4 a0, a1;
+    if (SRC == kSrcFp16) {
+      const uint4 x = *reinterpret_cast<const uint4*>(st + (r * kHeadDim + 32 * sl + 8 * u) * 2);
+      const uint4 y =
+          *reinterpret_cast<const uint4*>(st + ((16 + r) * kHeadDim + 32 * sl + 8 * u) * 2);
+      a0 = u32x4{x.x, x.y, x.z, x.w};
+      a1 = u32x4{y.x, y.y, y.z, y.w};
+    } else {
+      const uint2 x = *reinterpret_cast<const uint2*>(st + r * kHeadDim + 32 * sl + 8 * u);
+      const uint2 y = *reinterpret_cast<const uint2*>(st + (16 + r) * kHeadDim + 32 * sl + 8 * u);
+      a0 = u32x4{e4m3x2_to_f16x2(x.x, false), e4m3x2_to_f16x2(x.x, true),
+                 e4m3x2_to_f16x2(x.y, false), e4m3x2_to_f16x2(x.y, true)};
+      a1 = u32x4{e4m3x2_to_f16x2(y.x, false), e4m3x2_to_f16x2(y.x, true),
+                 e4m3x2_to_f16x2(y.y, false), e4m3x2_to_f16x2(y.y, true)};
+    }
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a0), as_f16x8(bq[sl]), s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a1), as_f16x8(bq[sl]), s1, 0, 0, 0);
+  }
+  float sc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // the cross-lane add runs in every lane; tokens past n_in are masked after
+    const float t0 = s0[i] + xor8(s0[i]);
+    const float t1 = s1[i] + xor8(s1[i]);
+    const int t = (low ? 16 : 0) + 4 * u + i;
+    sc[i] = t < n_in ? (low ? t1 : t0) : -INFINITY;
+  }
+  rescale_if_needed(W, sc, kLazyDense);
+  float pp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pp[i] = fast_exp2(sc[i] - W.m_ref);       // 0 for masked tokens
+    W.l_acc += pp[i];
+  }
+  const u32x4 bp = p_operand_f16(pp);
+  // ---- values: row 16n + r of the V tile, tokens 4u..4u+3 and 16+4u..16+4u+3
+  const uint8_t* vt = st + S::kRows;
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    u32x4 av;
+    if (SRC == kSrcFp16) {
+      const uint8_t* row = vt + (16 * n + r) * kGroup * 2;
+      const uint2 x = *reinterpret_cast<const uint2*>(row + 8 * u);
+      const uint2 y = *reinterpret_cast<const uint2*>(row + 32 + 8 * u);
+      av = u32x4{x.x, x.y, y.x, y.y};
+    } else {
+      const uint8_t* row = vt + (16 * n + r) * kGroup;
+      const uint32_t x = *reinterpret_cast<const uint32_t*>(row + 4 * u);
+      const uint32_t y = *reinterpret_cast<const uint32_t*>(row + 16 + 4 * u);
+      av = u32x4{e4m3x2_to_f16x2(x, false), e4m3x2_to_f16x2(x, true),
+                 e4m3x2_to_f16x2(y, false), e4m3x2_to_f16x2(y, true)};
+    }
+    W.cv[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(av), as_f16x8(bp), W.cv[n], 0, 0, 0);
+  }
+}
+
+template <int SRC>
+__global__ __launch_bounds__(kThreads) void dense_mfma_split_kernel(DecodeArgs a) {
+  using S = DenseStage<SRC>;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][S::kDepth][S::kBytes];
+
+  const int split = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int b = bh / a.H;
+  const int h_kv = bh % a.H;
+  const int hq0 = h_kv * a.nq + int(blockIdx.z) * a.heads_per_chunk;
+  const int nh = min(a.heads_per_chunk, a.nq - int(blockIdx.z) * a.heads_per_chunk);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int r = lane & 15;
+  const int u = lane >> 4;
+  const int hs = r & 7;
+  const bool low = r >= 8;
+
+  const float sk = SRC == kSrcFp8 ? a.tensor_scale[0] : 1.0f;
+  const float sv = SRC == kSrcFp8 ? a.tensor_scale[1] : 1.0f;
+  // B of the scores: q·log2e/√D (·s_K) as fp16 high (part 0) / low (part 1)
+  // terms, channel 32s + 8u + j in k-step s
+  u32x4 bq[4];
+  {
+    const bool valid = hs < nh;
+    const float qs = valid ? a.qscale * sk : 0.0f;
+    const float* qrow = a.q + (int64_t(b) * a.Hq + hq0 + (valid ? hs : 0)) * kHeadDim;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      uint32_t d[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        uint32_t hi, lo;
+        split_pair(qrow[32 * sl + 8 * u + 2 * p] * qs, qrow[32 * sl + 8 * u + 2 * p + 1] * qs,
+                   hi, lo);
+        d[p] = low ? lo : hi;
+      }
+      bq[sl] = u32x4{d[0], d[1], d[2], d[3]};
+    }
+  }
+
+  WaveAcc W;
+  W.m_ref = -INFINITY;
+  W.l_acc = 0.0f;
+  W.pz_acc = 0.0f;
+#pragma unroll
+  for (int n = 0; n < 8; ++n) W.cv[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  W.cones = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t n_tiles = (a.n_main + kGroup - 1) / kGroup;
+  const int64_t g0 = int64_t(split) * a.tiles_per_split;
+  const int64_t g1 = min(g0 + int64_t(a.tiles_per_split), n_tiles);
+  // this wavefront's tiles: g0 + wave + kWaves·i, i < n_mine
+  const int n_mine = g1 - g0 > wave ? int((g1 - g0 - wave + kWaves - 1) / kWaves) : 0;
+  constexpr int kAhead = S::kDepth - 1;
+  const uint32_t v16 = 16u * lane;
+  uint8_t* ring_w = &ring[wave][0][0];
+#pragma unroll
+  for (int j = 0; j < kAhead; ++j)
+    if (j < n_mine) issue_tile<SRC>(ring_w + j * S::kBytes, a, bh, g0 + wave + int64_t(kWaves) * j, v16);
+  for (int i = 0; i < n_mine; ++i) {
+    if (i + kAhead < n_mine) {
+      // the refilled stage was read by the previous tile; its reads are done
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const int j = i + kAhead;
+      issue_tile<SRC>(ring_w + (j % S::kDepth) * S::kBytes, a, bh, g0 + wave + int64_t(kWaves) * j,
+                      v16);
+    }
+    const int ahead = min(kAhead, n_mine - 1 - i);
+    if (ahead >= 2) wait_vmem<2 * S::kLoads>();
+    else if (ahead == 1) wait_vmem<S::kLoads>();
+    else wait_vmem<0>();
+    const int64_t tile = g0 + wave + int64_t(kWaves) * i;
+    const int n_in = int(min<int64_t>(kGroup, a.n_main - tile * kGroup));
+    process_dense_tile<SRC>(ring_w + (i % S::kDepth) * S::kBytes, W, n_in, bq, r, u, low);
+  }
+
+  wave_epilogue_and_merge(a, W, &ring[0][0][0], sizeof(ring[0]), wave, lane, hs, u, low, tid,
+                          b, hq0, nh, split, sv);
+}
+
 }  // namespace
+
+hipError_t launch_dense_mfma(const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid(a.n_split, a.B * a.H, a.nq / a.heads_per_chunk);
+  if (a.src == kSrcFp16) {
+    dense_mfma_split_kernel<kSrcFp16><<<grid, kThreads, 0, s>>>(a);
+  } else {
+    dense_mfma_split_kernel<kSrcFp8><<<grid, kThreads, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(a.n_split, a.B * a.H, a.nq / a.heads_per_chunk);

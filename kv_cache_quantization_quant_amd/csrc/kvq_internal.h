@@ -46,14 +46,33 @@ struct CopyTokensArgs {
   int bh_count;
 };
 
+// V of the FP8 / FP16 caches in tiles of kGroup tokens: tile g of (b, h) is
+// [D][kGroup] (one row of the tile's tokens per channel). Writes source tokens
+// [0, n_tokens) of each (b, h) block of an fp16 [B·H][src_tokens][D] tensor
+// to cache tokens [dst_t0, dst_t0 + n_tokens), as fp16 or as E4M3 codes with
+// the stored V scale (tensor_scale[1]). zero_tail: also zero the slots after
+// the last written token up to the end of its tile.
+struct VTileArgs {
+  const __half* v_src;
+  int64_t src_bh_stride;  // elements
+  int64_t n_tokens;
+  int64_t dst_t0;
+  void* v_dst;            // fp16 or uint8 [B·H][NT][D][kGroup]
+  int64_t NT;             // tiles per (b, h)
+  int bh_count;
+  int fp8;                // 0: fp16 copy, 1: E4M3 encode
+  int zero_tail;
+  const float* tensor_scale;
+};
+
 // FP8 E4M3 per-tensor quantization.
 struct Fp8QuantArgs {
   const __half* k_src;
   const __half* v_src;
   int64_t src_bh_stride;  // elements
   int64_t n_tokens;       // tokens per (b, h) to encode
-  uint8_t* k_codes;       // [B·H][C][D]
-  uint8_t* v_codes;
+  uint8_t* k_codes;       // [B·H][CT][D]
+  uint8_t* v_codes;       // row-major V codes, or null (V written in tiles)
   int64_t dst_bh_stride;  // elements (C·D)
   int64_t dst_t0;
   int bh_count;
@@ -97,9 +116,11 @@ struct DecodeArgs {
 
 hipError_t launch_kivi_quantize(const KiviQuantArgs& a, hipStream_t s);
 hipError_t launch_copy_tokens(const CopyTokensArgs& a, hipStream_t s);
+hipError_t launch_v_tiles(const VTileArgs& a, hipStream_t s);
 hipError_t launch_fp8_prefill(const Fp8QuantArgs& a, hipStream_t s);
 hipError_t launch_fp8_append(const Fp8QuantArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_dense_mfma(const DecodeArgs& a, hipStream_t s);
 
 }  // namespace kvq

@@ -152,7 +152,18 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
   }
 }
 
-// Copies n_tokens tokens of K and V (16 bytes per thread).
+__device__ __forceinline__ uint32_t fp8_encode4(const float* x, float s) {
+  // t = clamp(x / s, ±448), then the hardware RNE conversion, two per call.
+  float t[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) t[e] = fminf(fmaxf(x[e] / s, -448.0f), 448.0f);
+  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], w, true);
+  return w;
+}
+
+// Copies n_tokens tokens of K and V (16 bytes per thread); V is skipped when
+// v_dst is null.
 __global__ __launch_bounds__(kThreads) void copy_tokens_kernel(CopyTokensArgs a) {
   const int64_t idx = int64_t(blockIdx.x) * kThreads + threadIdx.x;  // uint4 index
   const int bh = blockIdx.y;
@@ -163,7 +174,80 @@ __global__ __launch_bounds__(kThreads) void copy_tokens_kernel(CopyTokensArgs a)
   const int64_t s = bh * a.src_bh_stride + tok * kHeadDim + c * 8;
   const int64_t d = bh * a.dst_bh_stride + (a.dst_t0 + tok) * kHeadDim + c * 8;
   *reinterpret_cast<uint4*>(a.k_dst + d) = *reinterpret_cast<const uint4*>(a.k_src + s);
-  *reinterpret_cast<uint4*>(a.v_dst + d) = *reinterpret_cast<const uint4*>(a.v_src + s);
+  if (a.v_dst != nullptr)
+    *reinterpret_cast<uint4*>(a.v_dst + d) = *reinterpret_cast<const uint4*>(a.v_src + s);
+}
+
+// V of the FP8 / FP16 caches, one workgroup per (tile, b·h): the tile's
+// tokens are read token-major into LDS and written channel-major (a row of
+// the tile's kGroup tokens per channel), as fp16 or as E4M3 codes (the FP8
+// encoding of the row-major path: clamp to ±448, then RNE).
+__global__ __launch_bounds__(kThreads) void v_tile_kernel(VTileArgs a) {
+  __shared__ float tile[kGroup][kHeadDim + 1];
+  const int bh = blockIdx.y;
+  const int64_t g = a.dst_t0 / kGroup + blockIdx.x;
+  const int64_t t_first = g * kGroup;
+  const int64_t lo = max(a.dst_t0, t_first);
+  const int64_t hi = min(a.dst_t0 + a.n_tokens, t_first + kGroup);
+  const int64_t wr_hi = a.zero_tail ? t_first + kGroup : hi;
+  const int tid = threadIdx.x;
+  {
+    // thread: token j of the tile, channels 16·(tid % 8) + [0, 16)
+    const int j = tid / 8, c0 = 16 * (tid % 8);
+    const int64_t t = t_first + j;
+    if (t >= lo && t < hi) {
+      const __half* src = a.v_src + bh * a.src_bh_stride + (t - a.dst_t0) * kHeadDim + c0;
+      float f[16];
+      halves_to_float(*reinterpret_cast<const uint4*>(src), f);
+      halves_to_float(*reinterpret_cast<const uint4*>(src + 8), f + 8);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) tile[j][c0 + e] = f[e];
+    }
+  }
+  __syncthreads();
+  // thread: channel d, tokens j0 + [0, 16)
+  const int d = tid / 2, j0 = 16 * (tid % 2);
+  const float sv = a.fp8 ? a.tensor_scale[1] : 1.0f;
+  float x[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int64_t t = t_first + j0 + k;
+    x[k] = (t >= lo && t < hi) ? tile[j0 + k][d] : 0.0f;
+  }
+  const int64_t row = ((int64_t(bh) * a.NT + g) * kHeadDim + d) * kGroup + j0;
+  const bool full = lo <= t_first + j0 && t_first + j0 + 16 <= wr_hi;
+  if (a.fp8) {
+    uint8_t* dst = static_cast<uint8_t*>(a.v_dst) + row;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (sv != 0.0f) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w[q] = fp8_encode4(x + 4 * q, sv);
+    }
+    if (full) {
+      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+      for (int k = 0; k < 16; ++k) {
+        const int64_t t = t_first + j0 + k;
+        if (t >= lo && t < wr_hi) dst[k] = uint8_t(w[k / 4] >> (8 * (k % 4)));
+      }
+    }
+  } else {
+    __half* dst = static_cast<__half*>(a.v_dst) + row;
+    if (full) {
+      uint32_t w[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        w[q] = uint32_t(__half_as_ushort(__float2half(x[2 * q]))) |
+               (uint32_t(__half_as_ushort(__float2half(x[2 * q + 1]))) << 16);
+      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4*>(dst + 8) = make_uint4(w[4], w[5], w[6], w[7]);
+    } else {
+      for (int k = 0; k < 16; ++k) {
+        const int64_t t = t_first + j0 + k;
+        if (t >= lo && t < wr_hi) dst[k] = __float2half(x[k]);
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------------- FP8 ---
@@ -207,15 +291,6 @@ __global__ __launch_bounds__(kThreads) void fp8_amax_kernel(Fp8QuantArgs a) {
   }
 }
 
-__device__ __forceinline__ uint32_t fp8_encode4(const float* x, float s) {
-  // t = clamp(x / s, ±448), then the hardware RNE conversion, two per call.
-  float t[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) t[e] = fminf(fmaxf(x[e] / s, -448.0f), 448.0f);
-  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], w, true);
-  return w;
-}
 
 // Encodes n_tokens tokens per (b, h). FROM_AMAX: the prefill pass, scales come
 // from the amax slots and are stored; otherwise the stored scales are reused.
@@ -248,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void fp8_encode_kernel(Fp8QuantArgs a) {
   if (sk != 0.0f) ck = make_uint2(fp8_encode4(fk, sk), fp8_encode4(fk + 4, sk));
   if (sv != 0.0f) cv = make_uint2(fp8_encode4(fv, sv), fp8_encode4(fv + 4, sv));
   *reinterpret_cast<uint2*>(a.k_codes + d) = ck;
-  *reinterpret_cast<uint2*>(a.v_codes + d) = cv;
+  if (a.v_codes != nullptr) *reinterpret_cast<uint2*>(a.v_codes + d) = cv;
 }
 
 }  // namespace
@@ -269,6 +344,15 @@ hipError_t launch_copy_tokens(const CopyTokensArgs& a, hipStream_t s) {
   const int64_t chunks = a.n_tokens * (kHeadDim / 8);
   dim3 grid(unsigned((chunks + kThreads - 1) / kThreads), a.bh_count);
   copy_tokens_kernel<<<grid, kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_v_tiles(const VTileArgs& a, hipStream_t s) {
+  if (a.n_tokens <= 0) return hipSuccess;
+  const int64_t first = a.dst_t0 / kGroup;
+  const int64_t last = (a.dst_t0 + a.n_tokens - 1) / kGroup;
+  dim3 grid(unsigned(last - first + 1), a.bh_count);
+  v_tile_kernel<<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

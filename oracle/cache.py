@@ -24,6 +24,9 @@ Every array is laid out as the device buffers are (see kivi.pack_k/pack_v):
   k_codes uint32 [B][H][CT][D·b/32], v_codes uint32 [B][H][NG][D][G·b/32],
   k_scale/k_zero fp32 [B][H][NG][D], v_scale/v_zero fp32 [B][H][CT],
   k_resid/v_resid fp16 [B][H][Rcap][D], with NG = ceil(C/G), CT = NG·G.
+FP8 and FP16 caches use tiles of T = 32 tokens: K [B][H][CT][D] (token rows,
+CT = ceil(C/T)·T) and V [B][H][NT][D][T] (per tile, one row of its T tokens per
+channel); slots that hold no token are zero.
 """
 from __future__ import annotations
 
@@ -123,11 +126,33 @@ class KiviCache:
         return attention.decode_attention(q, Kh, Vh)
 
 
+TILE = 32   # tokens per V tile of the FP8 / FP16 layouts
+
+
+def tile_rows(x, n_tiles):
+    """[..., T_tokens, D] token rows → [..., n_tiles, D, TILE] tiles (zero
+    padded): element (t, d) goes to tile t // TILE, row d, column t % TILE."""
+    x = np.asarray(x)
+    t = x.shape[-2]
+    pad = np.zeros(x.shape[:-2] + (n_tiles * TILE - t, x.shape[-1]), x.dtype)
+    y = np.concatenate([x, pad], axis=-2)
+    y = y.reshape(x.shape[:-2] + (n_tiles, TILE, x.shape[-1]))
+    return np.swapaxes(y, -1, -2).copy()
+
+
+def untile_rows(y, n_tokens):
+    """Inverse of tile_rows for the first n_tokens tokens."""
+    x = np.swapaxes(np.asarray(y), -1, -2)
+    x = x.reshape(y.shape[:-3] + (y.shape[-3] * TILE, y.shape[-2]))
+    return x[..., :n_tokens, :]
+
+
 class Fp8Cache:
     def __init__(self, batch, num_kv_heads, head_dim, capacity):
         self.B, self.H, self.D, self.C = batch, num_kv_heads, head_dim, capacity
-        self.k_codes = np.zeros((batch, num_kv_heads, capacity, head_dim), np.uint8)
-        self.v_codes = np.zeros_like(self.k_codes)
+        self.NT = -(-capacity // TILE)
+        self.k_codes = np.zeros((batch, num_kv_heads, self.NT * TILE, head_dim), np.uint8)
+        self.v_codes = np.zeros((batch, num_kv_heads, self.NT, head_dim, TILE), np.uint8)
         self.tensor_scale = np.zeros(2, np.float32)
         self.n_quant = 0
         self.n_resid = 0
@@ -144,20 +169,21 @@ class Fp8Cache:
         sk, sv = fp8.tensor_scale(k), fp8.tensor_scale(v)
         self.tensor_scale[:] = (sk, sv)
         self.k_codes[:, :, :S] = fp8.quantize(k, sk)
-        self.v_codes[:, :, :S] = fp8.quantize(v, sv)
+        self.v_codes[:] = tile_rows(fp8.quantize(v, sv), self.NT)
         self.n_quant = S
 
     def append(self, k1, v1):
         assert 0 < self.n_quant < self.C
         t = self.n_quant
         self.k_codes[:, :, t] = fp8.quantize(np.asarray(k1, np.float16), self.tensor_scale[0])
-        self.v_codes[:, :, t] = fp8.quantize(np.asarray(v1, np.float16), self.tensor_scale[1])
+        self.v_codes[:, :, t // TILE, :, t % TILE] = fp8.quantize(np.asarray(v1, np.float16),
+                                                                   self.tensor_scale[1])
         self.n_quant += 1
 
     def dequantized(self):
         n = self.n_quant
         return (fp8.dequantize(self.k_codes[:, :, :n], self.tensor_scale[0]),
-                fp8.dequantize(self.v_codes[:, :, :n], self.tensor_scale[1]))
+                fp8.dequantize(untile_rows(self.v_codes, n), self.tensor_scale[1]))
 
     def attention(self, q):
         Kh, Vh = self.dequantized()
@@ -167,8 +193,9 @@ class Fp8Cache:
 class Fp16Cache:
     def __init__(self, batch, num_kv_heads, head_dim, capacity):
         self.B, self.H, self.D, self.C = batch, num_kv_heads, head_dim, capacity
-        self.k = np.zeros((batch, num_kv_heads, capacity, head_dim), np.float16)
-        self.v = np.zeros_like(self.k)
+        self.NT = -(-capacity // TILE)
+        self.k = np.zeros((batch, num_kv_heads, self.NT * TILE, head_dim), np.float16)
+        self.v = np.zeros((batch, num_kv_heads, self.NT, head_dim, TILE), np.float16)
         self.n_quant = 0
         self.n_resid = 0
 
@@ -180,18 +207,20 @@ class Fp16Cache:
         S = k.shape[2]
         assert self.n_quant == 0 and 1 <= S <= self.C
         self.k[:, :, :S] = k
-        self.v[:, :, :S] = v
+        self.v[:] = tile_rows(np.asarray(v, np.float16), self.NT)
         self.n_quant = S
 
     def append(self, k1, v1):
         assert self.n_quant < self.C
-        self.k[:, :, self.n_quant] = k1
-        self.v[:, :, self.n_quant] = v1
+        t = self.n_quant
+        self.k[:, :, t] = k1
+        self.v[:, :, t // TILE, :, t % TILE] = v1
         self.n_quant += 1
 
     def dequantized(self):
         n = self.n_quant
-        return (self.k[:, :, :n].astype(np.float32), self.v[:, :, :n].astype(np.float32))
+        return (self.k[:, :, :n].astype(np.float32),
+                untile_rows(self.v, n).astype(np.float32))
 
     def attention(self, q):
         Kh, Vh = self.dequantized()

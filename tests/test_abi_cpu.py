@@ -99,10 +99,13 @@ def test_kivi_layout_matches_oracle_arrays(bits, R):
 
 
 def test_fp8_fp16_layout():
+    # FP8 / FP16: whole 32-token tiles (77 tokens -> 3 tiles = 96 slots)
     st, lay = kq.kvq_layout_query(kq.make_config("fp8", batch=2, num_kv_heads=3, capacity=77))
-    assert st == 0 and lay.k_codes == lay.v_codes == 2 * 3 * 77 * 128 and lay.tensor_scale == 16
+    assert st == 0 and lay.k_codes == lay.v_codes == 2 * 3 * 96 * 128 and lay.tensor_scale == 16
     st, lay = kq.kvq_layout_query(kq.make_config("fp16", batch=2, num_kv_heads=3, capacity=77))
-    assert st == 0 and lay.k_codes == 2 * 3 * 77 * 128 * 2 and lay.k_scale == 0
+    assert st == 0 and lay.k_codes == 2 * 3 * 96 * 128 * 2 and lay.k_scale == 0
+    oc = ocache.Fp8Cache(2, 3, 128, 77)
+    assert lay.v_codes == oc.v_codes.nbytes * 2 and lay.k_codes == oc.k_codes.nbytes * 2
 
 
 def _host_cache(cfg, n_quant=0, n_resid=0, fake_ptrs=True):

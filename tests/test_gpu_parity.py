@@ -261,8 +261,56 @@ def test_fp16_decode(kq, B, H, Hq, S):
     dc.prefill(k, v)
     oc = ocache.Fp16Cache(B, H, D, S + 3)
     oc.prefill(_np(k), _np(v))
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(dc.view("k_codes")), oc.k)
+    assert np.array_equal(_np(dc.view("v_codes")), oc.v)
     q = synth.make_q(B, Hq, D, device="cuda")
     assert _att_err(_np(dc.decode(q)), oc.attention(_np(q))) <= ATOL
+
+
+@pytest.mark.parametrize("B,H,Hq,S,steps", [(2, 2, 8, 45, 40), (1, 3, 6, 64, 3)])
+def test_fp16_prefill_append_decode(kq, B, H, Hq, S, steps):
+    """Streamed FP16 tokens across tile boundaries: tiled V layout exact,
+    attention within tolerance after every append."""
+    C = S + steps
+    k, v = _kv(B, H, C)
+    dc = kq.DeviceCache(kq.make_config("fp16", batch=B, num_kv_heads=H, capacity=C))
+    oc = ocache.Fp16Cache(B, H, D, C)
+    dc.prefill(k[:, :, :S].contiguous(), v[:, :, :S].contiguous())
+    oc.prefill(_np(k[:, :, :S]), _np(v[:, :, :S]))
+    kn, vn = _np(k), _np(v)
+    worst = 0.0
+    for i in range(steps):
+        dc.append(k[:, :, S + i].contiguous(), v[:, :, S + i].contiguous())
+        oc.append(kn[:, :, S + i], vn[:, :, S + i])
+        q = synth.make_q(B, Hq, D, step=i, device="cuda")
+        worst = max(worst, _att_err(_np(dc.decode(q)), oc.attention(_np(q))))
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(dc.view("k_codes")), oc.k)
+    assert np.array_equal(_np(dc.view("v_codes")), oc.v)
+    _say(f"[fp16 stream] worst max abs err {worst:.3e}")
+    assert worst <= ATOL
+
+
+@pytest.mark.parametrize("fmt", ["fp16", "fp8"])
+def test_dense_prefill_over_nan_memory(kq, fmt):
+    """Cache memory filled with NaN bytes before a prefill of a partial tile:
+    the slots after the last token are rewritten as zero and the masked tokens
+    of the last tile never reach the output."""
+    B, H, Hq, S = 1, 2, 4, 45
+    k, v = _kv(B, H, S)
+    dc = kq.DeviceCache(kq.make_config(fmt, batch=B, num_kv_heads=H, capacity=70))
+    for name in ("k_codes", "v_codes"):
+        dc.buffers[name].fill_(0xFF)
+    dc.prefill(k, v)
+    oc = (ocache.Fp16Cache if fmt == "fp16" else ocache.Fp8Cache)(B, H, D, 70)
+    oc.prefill(_np(k), _np(v))
+    q = synth.make_q(B, Hq, D, device="cuda")
+    out = _np(dc.decode(q))
+    assert np.all(np.isfinite(out))
+    assert _att_err(out, oc.attention(_np(q))) <= ATOL
+    vt = _np(dc.view("v_codes"))
+    assert not vt[:, :, 1, :, S - 32:].astype(np.float64).any()      # zeroed tail of tile 1
 
 
 # -------------------------------------------- full-size workloads, sampled ---
@@ -386,8 +434,8 @@ def test_gqa_128k_fp8_sampled(kq, kv_128k):
     for b, h in [(0, 0), (1, 4), (3, 7)]:
         kc = ofp8.quantize(_np(k[b, h]), sk)
         vc = ofp8.quantize(_np(v[b, h]), sv)
-        assert np.array_equal(_np(dc.view("k_codes")[b, h]), kc)
-        assert np.array_equal(_np(dc.view("v_codes")[b, h]), vc)
+        assert np.array_equal(_np(dc.view("k_codes")[b, h, :S]), kc)
+        assert np.array_equal(_np(dc.view("v_codes")[b, h]), ocache.tile_rows(vc, -(-S // 32)))
         ref = attention.decode_attention(_np(q)[b:b + 1, h * nq:(h + 1) * nq],
                                          ofp8.dequantize(kc, sk)[None, None],
                                          ofp8.dequantize(vc, sv)[None, None])

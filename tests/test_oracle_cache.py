@@ -122,6 +122,29 @@ def test_dequantized_matches_unpacked_codes():
         assert np.array_equal(Vh[0, h, :128], kivi.dequantize_v(vc, vs, vz))
 
 
+def test_fp8_fp16_tile_layout():
+    """V of the FP8 / FP16 caches sits in 32-token tiles, one row per channel:
+    element (t, d) at [t // 32][d][t % 32]; tile_rows / untile_rows invert
+    each other and unfilled slots are zero."""
+    x = np.arange(70 * D, dtype=np.float32).reshape(70, D)
+    y = cache.tile_rows(x, 3)
+    assert y.shape == (3, D, 32)
+    assert y[1, 5, 7] == x[39, 5] and y[2, 127, 5] == x[69, 127]
+    assert np.all(y[2, :, 6:] == 0)
+    assert np.array_equal(cache.untile_rows(y, 70), x)
+    k, v = _kv(1, 2, 45)
+    c = cache.Fp16Cache(1, 2, D, 70)
+    c.prefill(k, v)
+    k1 = synth.make_k(1, 2, 45, 46, D).numpy()[:, :, 0]
+    v1 = synth.make_v(1, 2, 45, 46, D).numpy()[:, :, 0]
+    c.append(k1, v1)
+    assert c.v.shape == (1, 2, 3, D, 32) and c.k.shape == (1, 2, 96, D)
+    assert np.array_equal(c.v[0, 1, 1, :, 13], v1[0, 1])          # token 45
+    assert np.array_equal(c.v[0, 0, 0, :, 3], v[0, 0, 3])
+    Kh, Vh = c.dequantized()
+    assert np.array_equal(Vh[0, 0, :45], v[0, 0].astype(np.float32))
+
+
 def test_fp8_scale_frozen_after_prefill():
     k, v = _kv(1, 2, 64)
     c = cache.Fp8Cache(1, 2, D, 80)
