@@ -845,7 +845,7 @@ struct DenseStage {
   static constexpr int kElem = SRC == kSrcFp16 ? 2 : 1;
   static constexpr int kRows = kGroup * kHeadDim * kElem;   // K rows (= V tile) of a tile
   static constexpr int kBytes = 2 * kRows;
-  static constexpr int kDepth = SRC == kSrcFp16 ? 2 : 3;    // stages per wavefront
+  static constexpr int kDepth = 2;                          // stages per wavefront
   static constexpr int kLoads = kBytes / 1024;              // copies per tile
 };
 

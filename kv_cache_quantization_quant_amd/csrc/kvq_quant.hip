@@ -40,20 +40,80 @@ __device__ __forceinline__ void halves_to_float(const uint4& raw, float* f) {
   }
 }
 
+// ---- fast exact quotient. The code is rint(RN((x − min) / s)). With r within
+// about one ulp of 1/s, p = RN((x − min)·r) lies within 1.5·2⁻²³·Q of the exact
+// quotient Q ≤ 2^b − 1 < 16, so |p − RN(Q)| < 2⁻¹⁸. Unless p is within 2⁻¹⁶ of
+// a half-integer (a possible rounding tie), rint(p) is the code; the rare lanes
+// with such a value redo their codes with the correctly rounded division.
+constexpr float kTieEdge = 0.5f - 1.0f / 65536.0f;
+
+// 1/s to within about an ulp (one Newton step on the hardware estimate);
+// 0 when s == 0, which makes every code 0 as the quantizer requires.
+__device__ __forceinline__ float quant_recip(float s) {
+  if (s == 0.0f) return 0.0f;
+  const float r = __builtin_amdgcn_rcpf(s);
+  return fmaf(r, fmaf(-s, r, 1.0f), r);
+}
+
+// rint((x − mn)·r) as a float (0 ≤ code ≤ 2^b − 1); `dev` keeps the largest
+// |p − rint(p)| seen, so that dev > kTieEdge flags a possible rounding tie.
+__device__ __forceinline__ float fast_code(float x, float mn, float r, float& dev) {
+  const float p = (x - mn) * r;
+  const float c = rintf(p);
+  dev = fmaxf(dev, fabsf(p - c));
+  return c;
+}
+
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ h2v as_h2(uint32_t u) { return __builtin_bit_cast(h2v, u); }
+__device__ __forceinline__ uint32_t as_u(h2v h) { return __builtin_bit_cast(uint32_t, h); }
+__device__ __forceinline__ h2v h2max(h2v a, h2v b) { return __builtin_elementwise_max(a, b); }
+__device__ __forceinline__ h2v h2min(h2v a, h2v b) { return __builtin_elementwise_min(a, b); }
+
+// pack 16 codes (floats 0..2^b−1) of consecutive channels into 32-bit words,
+// channel i of a word at bits [b·i, b·i + b): 2 bits → 1 word, 4 bits → 2.
+template <int BITS>
+__device__ __forceinline__ void pack16(const float (&c)[16], uint32_t (&w)[BITS / 2]) {
+  constexpr int PER = 32 / BITS;
+#pragma unroll
+  for (int k = 0; k < BITS / 2; ++k) {
+    // two exact float sums of 8 codes each (< 2^16), then one integer merge
+    float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+    for (int i = 0; i < PER / 2; ++i) {
+      lo = fmaf(c[k * PER + i], float(1 << (BITS * i)), lo);
+      hi = fmaf(c[k * PER + PER / 2 + i], float(1 << (BITS * i)), hi);
+    }
+    w[k] = static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
+  }
+}
+
 // One workgroup quantizes one group (32 tokens × 128 channels) of K and of V
-// for one (b, h). Thread (t = tid / 8, j = tid % 8) holds channels
-// [16j, 16j + 16) of token t: the loads cover 256 contiguous bytes per token.
+// for one (b, h). Loads: thread (t = tid / 8, j = tid % 8) holds channels
+// [16j, 16j + 16) of token t (256 contiguous bytes per token).
+//   V: per-token min / max over the 8 threads of a token (packed fp16 max of
+//      (x, −x), DPP exchanges), codes in registers, one word (two at 4 bits)
+//      of 16 channel codes per thread into an LDS transpose, from which each
+//      thread assembles V words along tokens.
+//   K: the tile goes through LDS; wavefront w takes channels [32w, 32w + 32),
+//      lane (pair c = l % 16, quarter u = l / 16) reduces tokens [8u, 8u + 8)
+//      of channels 32w + 2c, +1, then the four quarters are combined; codes of
+//      the thread's 16 channels follow from the per-channel scale and zero.
 template <int BITS>
 __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a) {
   constexpr int PER = 32 / BITS;           // codes per 32-bit word
-  constexpr int KW = kHeadDim / PER;       // K words per token
+  constexpr int KW = kHeadDim / PER;       // K words per token (= V transpose rows)
   constexpr int VW = kGroup / PER;         // V words per (group, channel)
+  constexpr int TW = BITS / 2;             // words of one thread's 16 codes
   constexpr float QMAX = float((1 << BITS) - 1);
+  constexpr int kRow = kGroup + 8;         // padded transpose row (words)
 
-  __shared__ __half tile_k[kGroup][kHeadDim];
-  __shared__ float s_k[kHeadDim];
-  __shared__ float z_k[kHeadDim];
-  __shared__ uint8_t vcode[kHeadDim][kGroup + 4];
+  __shared__ __attribute__((aligned(16))) __half tile_k[kGroup][kHeadDim];
+  __shared__ __attribute__((aligned(16))) float s_k[kHeadDim];
+  __shared__ __attribute__((aligned(16))) float z_k[kHeadDim];
+  __shared__ __attribute__((aligned(16))) float r_k[kHeadDim];
+  __shared__ __attribute__((aligned(16))) uint32_t vt[KW][kRow];   // [channel word][token]
 
   const int g = blockIdx.x;
   const int bh = blockIdx.y;
@@ -71,84 +131,136 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
   *reinterpret_cast<uint4*>(&tile_k[t][j * 16]) = k0;
   *reinterpret_cast<uint4*>(&tile_k[t][j * 16 + 8]) = k1;
 
-  // ---- V: per-token statistics over the 128 channels (8 consecutive lanes).
-  float vx[16];
-  halves_to_float(v0, vx);
-  halves_to_float(v1, vx + 8);
-  float vmn = vx[0], vmx = vx[0];
+  // ---- V statistics: (max, max of −x) of the 16 values, then over the 8
+  // threads of the token (xor 1, xor 2 inside a quad, then the half-row mirror).
+  const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  h2v mx2 = as_h2(vw[0]), mn2 = mx2;
 #pragma unroll
-  for (int i = 1; i < 16; ++i) {
-    vmn = fminf(vmn, vx[i]);
-    vmx = fmaxf(vmx, vx[i]);
+  for (int i = 1; i < 8; ++i) {
+    mx2 = h2max(mx2, as_h2(vw[i]));
+    mn2 = h2min(mn2, as_h2(vw[i]));
   }
-#pragma unroll
-  for (int off = 1; off < 8; off <<= 1) {
-    vmn = fminf(vmn, __shfl_xor(vmn, off));
-    vmx = fmaxf(vmx, __shfl_xor(vmx, off));
-  }
+  // (max, −min) of the thread's 16 values in one fp16 pair
+  h2v mm = h2max(h2v{mx2[0], -mn2[0]}, h2v{mx2[1], -mn2[1]});
+  mm = h2max(mm, as_h2(uint32_t(__builtin_amdgcn_mov_dpp(int(as_u(mm)), 0xB1, 0xF, 0xF, false))));
+  mm = h2max(mm, as_h2(uint32_t(__builtin_amdgcn_mov_dpp(int(as_u(mm)), 0x4E, 0xF, 0xF, false))));
+  mm = h2max(mm, as_h2(uint32_t(__builtin_amdgcn_mov_dpp(int(as_u(mm)), 0x141, 0xF, 0xF, false))));
+  const float vmx = float(mm[0]);
+  const float vmn = -float(mm[1]);
   const float vs = (vmx - vmn) / QMAX;
   if (j == 0) {
     a.v_scale[bh * CT + gg * kGroup + t] = vs;
     a.v_zero[bh * CT + gg * kGroup + t] = vmn;
   }
+
+  // ---- V codes of the thread's 16 channels → the LDS transpose
+  {
+    float vx[16], c[16];
+    halves_to_float(v0, vx);
+    halves_to_float(v1, vx + 8);
+    const float vr = quant_recip(vs);
+    float dev = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) vcode[j * 16 + i][t] = uint8_t(affine_code(vx[i], vmn, vs, QMAX));
+    for (int i = 0; i < 16; ++i) c[i] = fast_code(vx[i], vmn, vr, dev);
+    if (dev > kTieEdge) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c[i] = float(affine_code(vx[i], vmn, vs, QMAX));
+    }
+    uint32_t w[TW];
+    pack16<BITS>(c, w);
+#pragma unroll
+    for (int k = 0; k < TW; ++k) vt[TW * j + k][t] = w[k];
+  }
   __syncthreads();
 
-  // ---- K: per-channel statistics over the group's 32 tokens.
-  if (tid < kHeadDim) {
-    const int d = tid;
-    float mn = __half2float(tile_k[0][d]);
-    float mx = mn;
-#pragma unroll 8
-    for (int tt = 1; tt < kGroup; ++tt) {
-      const float x = __half2float(tile_k[tt][d]);
-      mn = fminf(mn, x);
-      mx = fmaxf(mx, x);
+  // ---- K statistics: wavefront w, channels 32w + 2c and 32w + 2c + 1
+  {
+    const int wv = tid >> 6;
+    const int c = tid & 15;
+    const int u = (tid >> 4) & 3;
+    const int d0 = 32 * wv + 2 * c;
+    h2v kmx = as_h2(*reinterpret_cast<const uint32_t*>(&tile_k[8 * u][d0])), kmn = kmx;
+#pragma unroll
+    for (int tt = 1; tt < 8; ++tt) {
+      const h2v x = as_h2(*reinterpret_cast<const uint32_t*>(&tile_k[8 * u + tt][d0]));
+      kmx = h2max(kmx, x);
+      kmn = h2min(kmn, x);
     }
-    const float s = (mx - mn) / QMAX;
-    s_k[d] = s;
-    z_k[d] = mn;
-    a.k_scale[(bh * a.NG + gg) * kHeadDim + d] = s;
-    a.k_zero[(bh * a.NG + gg) * kHeadDim + d] = mn;
+    // combine the four quarters (lanes l ^ 16, l ^ 32)
+#pragma unroll
+    for (int step = 0; step < 2; ++step) {
+      const auto px = step == 0
+          ? __builtin_amdgcn_permlane16_swap(as_u(kmx), as_u(kmx), false, false)
+          : __builtin_amdgcn_permlane32_swap(as_u(kmx), as_u(kmx), false, false);
+      const auto pn = step == 0
+          ? __builtin_amdgcn_permlane16_swap(as_u(kmn), as_u(kmn), false, false)
+          : __builtin_amdgcn_permlane32_swap(as_u(kmn), as_u(kmn), false, false);
+      kmx = h2max(as_h2(px[0]), as_h2(px[1]));
+      kmn = h2min(as_h2(pn[0]), as_h2(pn[1]));
+    }
+    const float mn0 = float(kmn[0]), mn1 = float(kmn[1]);
+    const float s0 = (float(kmx[0]) - mn0) / QMAX;
+    const float s1 = (float(kmx[1]) - mn1) / QMAX;
+    if (u == 0) {
+      const int64_t o = (bh * a.NG + gg) * kHeadDim + d0;
+      *reinterpret_cast<float2*>(a.k_scale + o) = make_float2(s0, s1);
+      *reinterpret_cast<float2*>(a.k_zero + o) = make_float2(mn0, mn1);
+      *reinterpret_cast<float2*>(&s_k[d0]) = make_float2(s0, s1);
+      *reinterpret_cast<float2*>(&z_k[d0]) = make_float2(mn0, mn1);
+      *reinterpret_cast<float2*>(&r_k[d0]) = make_float2(quant_recip(s0), quant_recip(s1));
+    }
+  }
+
+  // ---- V words: per channel, the group's 32 token codes packed along tokens;
+  // within a word, even tokens fill the low half-word and odd tokens the high.
+  uint32_t* vdst = a.v_codes + (bh * a.NG + gg) * kHeadDim * VW;
+#pragma unroll
+  for (int rep = 0; rep < (kHeadDim * VW) / kThreads; ++rep) {
+    const int idx = rep * kThreads + tid;
+    const int d = idx / VW;
+    const int w = idx % VW;
+    const uint32_t* row = &vt[d / PER][w * PER];
+    const int sh = BITS * (d % PER);
+    uint32_t word = 0;
+#pragma unroll
+    for (int q4 = 0; q4 < PER / 4; ++q4) {
+      const uint4 x = *reinterpret_cast<const uint4*>(row + 4 * q4);
+      const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * q4 + e;
+        word |= ((xs[e] >> sh) & ((1u << BITS) - 1)) << (BITS * (i / 2) + 16 * (i % 2));
+      }
+    }
+    vdst[idx] = word;
   }
   __syncthreads();
 
   // ---- K codes: token t, channels [16j, 16j + 16), packed along channels.
-  float kx[16];
+  float kx[16], c[16];
   halves_to_float(k0, kx);
   halves_to_float(k1, kx + 8);
-  uint32_t w0 = 0, w1 = 0;
+  float dev = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int d = j * 16 + i;
-    const uint32_t c = affine_code(kx[i], z_k[d], s_k[d], QMAX);
-    if (BITS == 2) {
-      w0 |= c << (2 * i);
-    } else if (i < 8) {
-      w0 |= c << (4 * i);
-    } else {
-      w1 |= c << (4 * (i - 8));
-    }
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const float4 z = *reinterpret_cast<const float4*>(&z_k[16 * j + 4 * q4]);
+    const float4 r = *reinterpret_cast<const float4*>(&r_k[16 * j + 4 * q4]);
+    c[4 * q4 + 0] = fast_code(kx[4 * q4 + 0], z.x, r.x, dev);
+    c[4 * q4 + 1] = fast_code(kx[4 * q4 + 1], z.y, r.y, dev);
+    c[4 * q4 + 2] = fast_code(kx[4 * q4 + 2], z.z, r.z, dev);
+    c[4 * q4 + 3] = fast_code(kx[4 * q4 + 3], z.w, r.w, dev);
   }
+  if (dev > kTieEdge) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c[i] = float(affine_code(kx[i], z_k[16 * j + i], s_k[16 * j + i], QMAX));
+  }
+  uint32_t w[TW];
+  pack16<BITS>(c, w);
   uint32_t* kdst = a.k_codes + (bh * CT + gg * kGroup + t) * KW;
   if (BITS == 2) {
-    kdst[j] = w0;
+    kdst[j] = w[0];
   } else {
-    *reinterpret_cast<uint2*>(kdst + 2 * j) = make_uint2(w0, w1);
-  }
-
-  // ---- V codes: per channel, the group's 32 token codes packed along tokens;
-  // within a word, even tokens fill the low half-word and odd tokens the high.
-  uint32_t* vdst = a.v_codes + (bh * a.NG + gg) * kHeadDim * VW;
-  for (int idx = tid; idx < kHeadDim * VW; idx += kThreads) {
-    const int d = idx / VW;
-    const int w = idx % VW;
-    uint32_t word = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      word |= uint32_t(vcode[d][w * PER + i]) << (BITS * (i / 2) + 16 * (i % 2));
-    vdst[idx] = word;
+    *reinterpret_cast<uint2*>(kdst + 2 * j) = make_uint2(w[0], w[TW - 1]);
   }
 }
 

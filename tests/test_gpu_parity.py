@@ -92,6 +92,52 @@ def test_kivi_prefill_and_decode(kq, B, H, Hq, S, bits, R, C):
     assert err <= ATOL
 
 
+def _tie_heavy(B, H, S, bits, seed):
+    """fp16 K/V whose groups and tokens put many values exactly on, or one
+    fp16 step beside, the rounding ties (k + 1/2)·s of the quantizer, plus
+    constant groups and groups spanning the whole fp16 range."""
+    rng = np.random.default_rng(seed)
+    qmax = 2 ** bits - 1
+    shape = (B, H, S, D)
+    e = rng.integers(-12, 4, size=shape).astype(np.float64)
+    k = rng.integers(0, 2 * qmax + 1, size=shape) / 2.0            # multiples of 1/2
+    x = (k - qmax / 2.0) * 2.0 ** e                                  # ties at odd k
+    x16 = x.astype(np.float16)
+    nudge = rng.integers(-1, 2, size=shape).astype(np.int16)         # one fp16 step
+    x16 = np.where(rng.random(shape) < 0.3,
+                   (x16.view(np.int16) + nudge).view(np.float16), x16)
+    x16 = np.where(np.isfinite(x16), x16, np.float16(0))
+    # per-token / per-group endpoints that make s a power of two times 1
+    x16[..., 0] = np.float16(-qmax / 2.0)
+    x16[..., 1] = np.float16(qmax / 2.0)
+    x16[:, :, 0:32, :] = np.float16(1.5)                             # constant group
+    x16[:, :, 32:64, 5] = np.float16(-65504.0)
+    x16[:, :, 40, 5] = np.float16(65504.0)
+    x16[:, :, 64:96, 7] = np.float16(2.0 ** -24)                     # subnormal range
+    x16[:, :, 70, 7] = np.float16(3 * 2.0 ** -24)
+    return x16
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_kivi_quantize_rounding_ties(kq, bits):
+    """Codes, scales and zero-points bit-exact on inputs full of exact and
+    near rounding ties (where the reciprocal shortcut must defer to the
+    correctly rounded division), constant and extreme-range groups."""
+    B, H, S = 2, 3, 512
+    _say(f"[kivi ties] bits={bits} B={B} H={H} S={S}")
+    kn = _tie_heavy(B, H, S, bits, 1)
+    vn = _tie_heavy(B, H, S, bits, 2)
+    k = torch.from_numpy(kn).cuda()
+    v = torch.from_numpy(vn).cuda()
+    dc = kq.DeviceCache(kq.make_config("kivi", bits=bits, residual_length=0, batch=B,
+                                       num_kv_heads=H, capacity=S))
+    dc.prefill(k, v)
+    oc = ocache.KiviCache(B, H, D, bits, 32, 0, S)
+    oc.prefill(kn, vn)
+    torch.cuda.synchronize()
+    _compare_kivi_state(dc, oc)
+
+
 def test_llama2_7b_layer_full(kq):
     """B=8, 32 MHA heads, S=4096, KIVI 2-bit: every buffer and every output."""
     cfg = synth.CONFIGS["llama2_7b_layer"]
