@@ -16,6 +16,8 @@
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -264,11 +266,23 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
   }
 }
 
-__device__ __forceinline__ uint32_t fp8_encode4(const float* x, float s) {
+// x / s correctly rounded, from rs = RN(1 / s) (one IEEE division per
+// thread): q = RN(x·rs) is within an ulp of x / s, the residual x − q·s is
+// exact in one fma, and RN(q + residual·rs) is the correctly rounded quotient
+// (Markstein's theorem for round-to-nearest; no overflow or underflow occurs
+// for fp16 x and a tensor scale amax / 448 ≥ 2⁻²⁴ / 448). The quotient takes
+// the sign of x, which keeps −0 / s = −0 (the sum above would give +0).
+__device__ __forceinline__ float div_by_scale(float x, float s, float rs) {
+  const float q = x * rs;
+  const float res = fmaf(-q, s, x);
+  return __builtin_copysignf(fmaf(res, rs, q), x);
+}
+
+__device__ __forceinline__ uint32_t fp8_encode4(const float* x, float s, float rs) {
   // t = clamp(x / s, ±448), then the hardware RNE conversion, two per call.
   float t[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) t[e] = fminf(fmaxf(x[e] / s, -448.0f), 448.0f);
+  for (int e = 0; e < 4; ++e) t[e] = fminf(fmaxf(div_by_scale(x[e], s, rs), -448.0f), 448.0f);
   uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], w, true);
   return w;
@@ -332,8 +346,9 @@ __global__ __launch_bounds__(kThreads) void v_tile_kernel(VTileArgs a) {
     uint8_t* dst = static_cast<uint8_t*>(a.v_dst) + row;
     uint32_t w[4] = {0u, 0u, 0u, 0u};
     if (sv != 0.0f) {
+      const float rsv = 1.0f / sv;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) w[q] = fp8_encode4(x + 4 * q, sv);
+      for (int q = 0; q < 4; ++q) w[q] = fp8_encode4(x + 4 * q, sv, rsv);
     }
     if (full) {
       *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
@@ -371,38 +386,55 @@ __global__ void fp8_clear_amax_kernel(float* ts) {
   }
 }
 
-// amax(|K|) and amax(|V|) over the source tokens; non-negative fp32 values
-// order like their bit patterns, so an unsigned atomic max suffices.
+// amax(|K|) and amax(|V|) over the source tokens: grid (blocks per (b, h),
+// B·H), each thread a running packed-fp16 max of |x| (exact: the maximum of
+// fp16 magnitudes is one of them); non-negative fp32 values order like their
+// bit patterns, so an unsigned atomic max combines the wavefronts.
 __global__ __launch_bounds__(kThreads) void fp8_amax_kernel(Fp8QuantArgs a) {
-  constexpr int kChunks = kHeadDim / 8;
-  const int64_t per_bh = a.n_tokens * kChunks;
-  const int64_t total = per_bh * a.bh_count;
-  float mk = 0.0f, mv = 0.0f;
-  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < total;
-       i += int64_t(gridDim.x) * kThreads) {
-    const int64_t bh = i / per_bh;
-    const int64_t r = i % per_bh;
-    const int64_t s = bh * a.src_bh_stride + (r / kChunks) * kHeadDim + (r % kChunks) * 8;
-    float fk[8], fv[8];
-    halves_to_float(*reinterpret_cast<const uint4*>(a.k_src + s), fk);
-    halves_to_float(*reinterpret_cast<const uint4*>(a.v_src + s), fv);
+  constexpr int kChunks = kHeadDim / 8;                 // uint4 per token
+  const int64_t n = a.n_tokens * kChunks;               // consecutive uint4 per (b, h)
+  const __half* ks = a.k_src + int64_t(blockIdx.y) * a.src_bh_stride;
+  const __half* vs = a.v_src + int64_t(blockIdx.y) * a.src_bh_stride;
+  h2v mk = h2v{0, 0}, mv = h2v{0, 0};
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  // four chunks of K and of V per step, all eight loads in flight together
+  constexpr int kUnroll = 4;
+  int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
+    uint4 k[kUnroll], v[kUnroll];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      mk = fmaxf(mk, fabsf(fk[e]));
-      mv = fmaxf(mv, fabsf(fv[e]));
+    for (int u = 0; u < kUnroll; ++u) {
+      k[u] = *reinterpret_cast<const uint4*>(ks + 8 * (i + u * stride));
+      v[u] = *reinterpret_cast<const uint4*>(vs + 8 * (i + u * stride));
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      mk = h2max(h2max(mk, as_h2(k[u].x & 0x7FFF7FFFu)), as_h2(k[u].y & 0x7FFF7FFFu));
+      mk = h2max(h2max(mk, as_h2(k[u].z & 0x7FFF7FFFu)), as_h2(k[u].w & 0x7FFF7FFFu));
+      mv = h2max(h2max(mv, as_h2(v[u].x & 0x7FFF7FFFu)), as_h2(v[u].y & 0x7FFF7FFFu));
+      mv = h2max(h2max(mv, as_h2(v[u].z & 0x7FFF7FFFu)), as_h2(v[u].w & 0x7FFF7FFFu));
     }
   }
+  for (; i < n; i += stride) {
+    const uint4 k = *reinterpret_cast<const uint4*>(ks + 8 * i);
+    const uint4 v = *reinterpret_cast<const uint4*>(vs + 8 * i);
+    mk = h2max(h2max(mk, as_h2(k.x & 0x7FFF7FFFu)), as_h2(k.y & 0x7FFF7FFFu));
+    mk = h2max(h2max(mk, as_h2(k.z & 0x7FFF7FFFu)), as_h2(k.w & 0x7FFF7FFFu));
+    mv = h2max(h2max(mv, as_h2(v.x & 0x7FFF7FFFu)), as_h2(v.y & 0x7FFF7FFFu));
+    mv = h2max(h2max(mv, as_h2(v.z & 0x7FFF7FFFu)), as_h2(v.w & 0x7FFF7FFFu));
+  }
+  float fk = fmaxf(float(mk[0]), float(mk[1]));
+  float fv = fmaxf(float(mv[0]), float(mv[1]));
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
-    mk = fmaxf(mk, __shfl_xor(mk, off));
-    mv = fmaxf(mv, __shfl_xor(mv, off));
+    fk = fmaxf(fk, __shfl_xor(fk, off));
+    fv = fmaxf(fv, __shfl_xor(fv, off));
   }
   if ((threadIdx.x & 63) == 0) {
-    atomicMax(reinterpret_cast<unsigned int*>(a.tensor_scale + 2), __float_as_uint(mk));
-    atomicMax(reinterpret_cast<unsigned int*>(a.tensor_scale + 3), __float_as_uint(mv));
+    atomicMax(reinterpret_cast<unsigned int*>(a.tensor_scale + 2), __float_as_uint(fk));
+    atomicMax(reinterpret_cast<unsigned int*>(a.tensor_scale + 3), __float_as_uint(fv));
   }
 }
-
 
 // Encodes n_tokens tokens per (b, h). FROM_AMAX: the prefill pass, scales come
 // from the amax slots and are stored; otherwise the stored scales are reused.
@@ -428,14 +460,24 @@ __global__ __launch_bounds__(kThreads) void fp8_encode_kernel(Fp8QuantArgs a) {
   const int c = int(idx % kChunks);
   const int64_t s = bh * a.src_bh_stride + tok * kHeadDim + c * 8;
   const int64_t d = bh * a.dst_bh_stride + (a.dst_t0 + tok) * kHeadDim + c * 8;
-  float fk[8], fv[8];
+  float fk[8];
   halves_to_float(*reinterpret_cast<const uint4*>(a.k_src + s), fk);
-  halves_to_float(*reinterpret_cast<const uint4*>(a.v_src + s), fv);
-  uint2 ck = make_uint2(0u, 0u), cv = make_uint2(0u, 0u);
-  if (sk != 0.0f) ck = make_uint2(fp8_encode4(fk, sk), fp8_encode4(fk + 4, sk));
-  if (sv != 0.0f) cv = make_uint2(fp8_encode4(fv, sv), fp8_encode4(fv + 4, sv));
+  uint2 ck = make_uint2(0u, 0u);
+  if (sk != 0.0f) {
+    const float rsk = 1.0f / sk;
+    ck = make_uint2(fp8_encode4(fk, sk, rsk), fp8_encode4(fk + 4, sk, rsk));
+  }
   *reinterpret_cast<uint2*>(a.k_codes + d) = ck;
-  if (a.v_codes != nullptr) *reinterpret_cast<uint2*>(a.v_codes + d) = cv;
+  if (a.v_codes != nullptr) {
+    float fv[8];
+    halves_to_float(*reinterpret_cast<const uint4*>(a.v_src + s), fv);
+    uint2 cv = make_uint2(0u, 0u);
+    if (sv != 0.0f) {
+      const float rsv = 1.0f / sv;
+      cv = make_uint2(fp8_encode4(fv, sv, rsv), fp8_encode4(fv + 4, sv, rsv));
+    }
+    *reinterpret_cast<uint2*>(a.v_codes + d) = cv;
+  }
 }
 
 }  // namespace
@@ -472,10 +514,11 @@ hipError_t launch_fp8_prefill(const Fp8QuantArgs& a, hipStream_t s) {
   fp8_clear_amax_kernel<<<1, 64, 0, s>>>(a.tensor_scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t chunks = a.n_tokens * (kHeadDim / 8) * a.bh_count;
-  int64_t blocks = (chunks + kThreads - 1) / kThreads;
-  if (blocks > 4096) blocks = 4096;
-  fp8_amax_kernel<<<unsigned(blocks), kThreads, 0, s>>>(a);
+  // about 4096 workgroups in all, at most one per 256 chunks of a (b, h)
+  const int64_t per_bh_chunks = a.n_tokens * (kHeadDim / 8);
+  int64_t per_bh = (4096 + a.bh_count - 1) / a.bh_count;
+  per_bh = std::max<int64_t>(1, std::min<int64_t>(per_bh, (per_bh_chunks + kThreads - 1) / kThreads));
+  fp8_amax_kernel<<<dim3(unsigned(per_bh), a.bh_count), kThreads, 0, s>>>(a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid(unsigned((a.n_tokens * (kHeadDim / 8) + kThreads - 1) / kThreads), a.bh_count);

@@ -244,6 +244,27 @@ def test_fp8_encoder_every_fp16_value(kq, limit):
     assert np.array_equal(_np(dc.view("v_codes")), oc.v_codes)
 
 
+def test_fp8_encoder_random_scales(kq):
+    """Tensor scales from 16 random magnitudes (amax from 2^-10 to 2^15), every
+    value of the tensor drawn across [-amax, amax] so that quotients x / s
+    fall between all E4M3 grid points: codes bit-exact with the oracle."""
+    rng = np.random.default_rng(7)
+    S = 512
+    for i in range(16):
+        amax = np.float16(2.0 ** rng.uniform(-10, 15))
+        k = (rng.uniform(-1, 1, size=(1, 1, S, D)) * float(amax)).astype(np.float16)
+        v = (rng.uniform(-1, 1, size=(1, 1, S, D)) * float(amax)).astype(np.float16)
+        k[0, 0, 3, 7] = amax
+        v[0, 0, 5, 1] = -amax
+        dc = kq.DeviceCache(kq.make_config("fp8", capacity=S))
+        dc.prefill(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+        oc = ocache.Fp8Cache(1, 1, D, S)
+        oc.prefill(k, v)
+        torch.cuda.synchronize()
+        assert np.array_equal(_np(dc.view("k_codes")), oc.k_codes), (i, float(amax))
+        assert np.array_equal(_np(dc.view("v_codes")), oc.v_codes), (i, float(amax))
+
+
 def test_fp8_decode_values(kq):
     """The in-kernel E4M3 decode: a cache holding all 254 finite codes (scale
     1 from amax 448) attends with one-hot queries to recover values."""
