@@ -137,15 +137,27 @@ def run_main(torch, kq, synth, args):
         c.prefill(kp, vp)
     del kp, vp
 
-    # step i works on layer i % LAYERS
+    # step i works on layer i % LAYERS; with every layer prefilled to a full
+    # window, the first append of each layer flushes 128 tokens into 4 groups
+    warm_flush = []
     for i in range(args.warmup):
         c = layers[i % LAYERS]
+        flushes = c.n_resid == c.cfg.residual_length
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
         c.append(k_new[i], v_new[i])
+        e1.record()
+        if flushes:
+            warm_flush.append((e0, e1))
         c.decode(qs[i], out=out, workspace=ws)
     torch.cuda.synchronize()
+    warm_flush_us = [a.elapsed_time(b) * 1e3 for a, b in warm_flush]
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
+    ev_app = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    flush_step = []
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     step_bytes = []
@@ -155,6 +167,8 @@ def run_main(torch, kq, synth, args):
     for j in range(args.steps):
         i = args.warmup + j
         c = layers[i % LAYERS]
+        flush_step.append(c.n_resid == c.cfg.residual_length)   # this append flushes
+        ev_app[j].record()
         c.append(k_new[i], v_new[i])
         step_bytes.append(c.decode_bytes(Hq))
         ev[j][0].record()
@@ -165,6 +179,9 @@ def run_main(torch, kq, synth, args):
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(end)
     dec_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    app_us = [a.elapsed_time(b[0]) * 1e3 for a, b in zip(ev_app, ev)]
+    plain_app = [u for u, f in zip(app_us, flush_step) if not f]
+    flush_app = [u for u, f in zip(app_us, flush_step) if f] + warm_flush_us
     total_bytes = sum(step_bytes)
     value = total_bytes / (total_ms * 1e-3) / 1e9
     mean_dec_us = sum(dec_us) / len(dec_us)
@@ -188,6 +205,10 @@ def run_main(torch, kq, synth, args):
         "achieved_gbs": achieved,
         "cold_decode_us_p50": cold_med,
         "cold_decode_gbs": None if cold_med is None else bytes_now / (cold_med * 1e-6) / 1e9,
+        "append_us_p50": statistics.median(plain_app) if plain_app else None,
+        "flush_append_us_mean": statistics.mean(flush_app) if flush_app else None,
+        "flush_steps": len(flush_app),
+        "append_plus_decode_us_mean": statistics.mean(a + d for a, d in zip(app_us, dec_us)),
         "prefill_quantize_us": pre_us,
         "prefill_quantize_gbs": q_bytes / (pre_us * 1e-6) / 1e9,
         "layers": LAYERS,
@@ -204,6 +225,7 @@ def run_extra(torch, kq, synth):
     plan = [("llama2_7b_layer", "kivi"), ("mha_large_batch_4bit", "kivi"),
             ("gqa_128k", "fp16"), ("gqa_128k", "fp8"), ("gqa_128k", "kivi")]
     kv_cache = {}
+    outs = {}                      # gqa_128k decode outputs, same K/V and q
     for name, fmt in plan:
         c = synth.CONFIGS[name]
         B, H, Hq, S = c["batch"], c["num_kv_heads"], c["num_q_heads"], c["seq_len"]
@@ -227,6 +249,8 @@ def run_extra(torch, kq, synth):
         o = torch.empty_like(q)
         dec = statistics.median(time_launches(
             torch, lambda: dc.decode(q, out=o, workspace=ws), 10, scrub))
+        if name == "gqa_128k":
+            outs[fmt] = o.double().cpu()
         nbytes = dc.decode_bytes(Hq)
         out[f"{name}/{fmt}"] = {
             "decode_us": round(dec, 2), "decode_bytes": nbytes,
@@ -237,6 +261,15 @@ def run_extra(torch, kq, synth):
         _log(f"[bench] extra {name}/{fmt}: {out[f'{name}/{fmt}']}")
     kv_cache.clear()
     torch.cuda.empty_cache()
+    # accuracy side report: FP8 and KIVI attention against FP16 attention
+    ref = outs["fp16"]
+    acc = {}
+    for fmt in ("fp8", "kivi"):
+        d = outs[fmt] - ref
+        acc[fmt] = {"max_abs": float(d.abs().max()),
+                    "rel_l2": float(d.norm() / ref.norm())}
+    out["gqa_128k/accuracy_vs_fp16"] = acc
+    _log(f"[bench] gqa_128k accuracy vs fp16: {acc}")
     return out
 
 
