@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -36,12 +37,32 @@ COMMON = [
 ]
 
 
+def _scratch_kernels(remarks: str) -> list[str]:
+    """Kernels whose resource-usage remark reports scratch (spilled registers
+    or stack): such a kernel issues vector-memory instructions the decode
+    kernels' hand-counted `s_waitcnt vmcnt` waits do not expect."""
+    bad, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name and int(m.group(1)) > 0:
+            bad.append(f"{name} ({m.group(1)} bytes/lane)")
+    return bad
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC, *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    if src.endswith(".hip"):
+        cmd.append("-Rpass-analysis=kernel-resource-usage")
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+    bad = _scratch_kernels(r.stderr)
+    if bad:
+        raise RuntimeError(f"{src}: kernels using scratch memory: {', '.join(bad)}")
     return obj
 
 

@@ -223,3 +223,24 @@ def test_prefill_split_matches_oracle_cpu_only():
     for S, expect in [(256, (128, 128)), (4096, (3968, 128)), (32768, (32640, 128)),
                       (8192, (8064, 128)), (131072, (130944, 128))]:
         assert okivi.prefill_split(S, 32, 128) == expect
+
+
+def test_build_rejects_scratch_kernels():
+    """The build's guard against kernels that spill to scratch (their
+    scratch accesses would be counted by the decode kernels' hand-written
+    vector-memory waits): the remark parser flags exactly the kernels with a
+    non-zero scratch size."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "kvq_build", os.path.join(ROOT, "kv_cache_quantization_quant_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    remarks = "\n".join([
+        "k.hip:1:1: remark: Function Name: _Z3onev [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:1:1: remark:     VGPRs: 168 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:1:1: remark:     ScratchSize [bytes/lane]: 16 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:9:1: remark: Function Name: _Z3twov [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:9:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    assert b._scratch_kernels(remarks) == ["_Z3onev (16 bytes/lane)"]
+    assert b._scratch_kernels("") == []
