@@ -35,12 +35,17 @@
 // The Sᵀ accumulator layout (lane holds column r, tokens 4u..4u+3 of a tile)
 // is exactly the B-operand layout of the value product, so no transpose is
 // needed:
-//   Oᵀ[d][col] = Σ_t (128 + f'·code[t][d]) · P'[t][col]   (bf16 MFMA, 8 tiles
-//       of 16 channels), with A = codes OR-ed into the mantissa of 128.0 and
-//       B = P' = p_t·s_t/f' as a bf16 high + low split (columns hs, hs+8);
-//   Σ_t P'[t][col] from one more MFMA with A = 1 removes the 128 offset.
+//   Oᵀ[d][col] = Σ_t (o_t + code[t][d]) · P'[t][col]   (bf16 MFMA, 8 tiles
+//       of 16 channels), with A = codes OR-ed into the mantissa of a bf16
+//       power of two o_t whose last mantissa step at the code's bit position
+//       is 1 (128.0 for codes in bits 0..1 or 0..3, 32.0 for codes in bits
+//       2..3) and B = P' = p_t·s_t as a bf16 high + low split (columns hs,
+//       hs+8); Σ_t o_t·P'[t][col] from one more MFMA (A = o_t / 128, then
+//       times 128) removes them.
 // Online softmax in the log2 domain with a per-head reference maximum that
-// is only raised (with rescaling) when a score exceeds it by more than 16.
+// is only raised (with rescaling) when a score exceeds it by more than 16;
+// after a wavefront's first group the score accumulator starts at −m_ref, so
+// the scores come out relative to it.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -242,6 +247,25 @@ __device__ __forceinline__ void rescale_if_needed(WaveAcc& W, const float (&sc)[
   }
 }
 
+// The same step for scores already taken relative to the reference maximum
+// (the score accumulator starts at −m_ref): the threshold is the constant
+// slack, and a raise by d shifts the reference and the four scores by d.
+__device__ __forceinline__ void rescale_rel(WaveAcc& W, float (&sc)[4]) {
+  const float lmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+  if (__any(lmax > kLazy)) {                     // wave-uniform, rare
+    const float d = fmaxf(0.0f, head_max(lmax));
+    const float alpha = fast_exp2(-d);
+    W.l_acc *= alpha;
+    W.pz_acc *= alpha;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) W.cv[n] *= alpha;
+    W.cones *= alpha;
+    W.m_ref += d;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] -= d;
+  }
+}
+
 // bf16 high / low terms of four P' values; part 0 ends with the high terms of
 // tile 0 (own) and tile 1 (partner's), part 1 with the low terms of tile 0
 // (partner's) and tile 1 (own): the B operand of the value products.
@@ -336,7 +360,8 @@ __device__ __forceinline__ float f4_at(const float4 (&v)[4], int i) {
 // Scores of the four tokens this lane keeps (log2 units).
 template <int BITS>
 __device__ __forceinline__ void group_scores(const KLoad<BITS>& K, bool low,
-                                             const float (&q16)[16], float (&sc)[4]) {
+                                             const float (&q16)[16], float m_part,
+                                             float (&sc)[4]) {
   uint32_t m0[2 * BITS], m1[2 * BITS];
   k_masks<BITS>(K.w0, m0);
   k_masks<BITS>(K.w1, m1);
@@ -349,7 +374,9 @@ __device__ __forceinline__ void group_scores(const KLoad<BITS>& K, bool low,
     zp[j] = fmaf(q16[4 * j + 3], z.w, fmaf(q16[4 * j + 2], z.z,
                  fmaf(q16[4 * j + 1], z.y, q16[4 * j] * z.x)));
   }
-  const float zt = sum_x16_x32((zp[0] + zp[1]) + (zp[2] + zp[3]));
+  // part 0 also carries −m_ref (m_part), so that the scores come out relative
+  // to the reference maximum
+  const float zt = sum_x16_x32((zp[0] + zp[1]) + (zp[2] + zp[3])) - m_part;
   f32x4 s0 = f32x4{zt, zt, zt, zt}, s1 = s0;
   // ---- scores: local k-step h is global k-step h (part 0) or 2 + h (part 1)
 #pragma unroll
@@ -385,38 +412,46 @@ __device__ __forceinline__ void group_scores(const KLoad<BITS>& K, bool low,
 }
 
 // Online-softmax step for the group's scores; returns the B operand P' of its
-// value products (V scale, and the 1/4 of the 2-bit codes in bits 2..3, folded).
-template <int BITS>
-__device__ __forceinline__ u32x4 group_probs(WaveAcc& W, const float (&sc)[4], float4 vs,
-                                             float4 vz) {
-  rescale_if_needed(W, sc);
+// value products (p times the V scale). REL: the scores are relative to the
+// reference maximum already; otherwise (the first group of a wavefront) they
+// are absolute.
+template <int BITS, bool REL>
+__device__ __forceinline__ u32x4 group_probs(WaveAcc& W, float (&sc)[4], float4 vs, float4 vz) {
+  if (REL) {
+    rescale_rel(W, sc);
+  } else {
+    rescale_if_needed(W, sc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] -= W.m_ref;
+  }
   const float vsa[4] = {vs.x, vs.y, vs.z, vs.w};
   const float vza[4] = {vz.x, vz.y, vz.z, vz.w};
   float pp[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float p = fast_exp2(sc[i] - W.m_ref);
+    const float p = fast_exp2(sc[i]);
     W.l_acc += p;
     W.pz_acc = fmaf(p, vza[i], W.pz_acc);
-    pp[i] = p * ((BITS == 2 && i >= 2) ? vsa[i] * 0.25f : vsa[i]);
+    pp[i] = p * vsa[i];
   }
   return p_operand(pp);
 }
 
-// P'·V of one group: 8 tiles of 16 channels, codes in the mantissa of 128.0,
-// plus the column sums of P' that remove the 128 offset.
+// P'·V of one group: 8 tiles of 16 channels, codes in the mantissa of 128.0
+// or 32.0, plus the offset-weighted column sums of P' that remove the offsets.
 template <int BITS>
 __device__ __forceinline__ void group_values(const VLoad& V, WaveAcc& W, u32x4 bp, uint32_t vsh,
-                                             uint32_t vm0, uint32_t vm1, uint32_t magic) {
+                                             uint32_t vm0, uint32_t vm1, uint32_t magic,
+                                             uint32_t magic32) {
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
     uint32_t d[4];
     if (BITS == 2) {
       const uint32_t v0 = V.w[n][0] >> vsh, v1 = V.w[n][1] >> vsh;
       d[0] = bfi(vm0, v0, magic);
-      d[1] = bfi(vm1, v0, magic);
+      d[1] = bfi(vm1, v0, magic32);
       d[2] = bfi(vm0, v1, magic);
-      d[3] = bfi(vm1, v1, magic);
+      d[3] = bfi(vm1, v1, magic32);
     } else {
       const uint32_t v0 = V.w[n][0], v1 = V.w[n][1];
       d[0] = bfi(vm0, v0 >> vsh, magic);
@@ -427,8 +462,12 @@ __device__ __forceinline__ void group_values(const VLoad& V, WaveAcc& W, u32x4 b
     W.cv[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{d[0], d[1], d[2], d[3]}),
                                                        as_bf16x8(bp), W.cv[n], 0, 0, 0);
   }
-  const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-  W.cones = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ones), as_bf16x8(bp), W.cones,
+  // each k-slot's code offset over 128 (1, or 1/4 for the 2-bit codes in
+  // bits 2..3, whose offset is 32): 128 times this product is what the codes
+  // carry on top of their values
+  const uint32_t o1 = BITS == 2 ? 0x3E803E80u : 0x3F803F80u;
+  const u32x4 offs = u32x4{0x3F803F80u, o1, 0x3F803F80u, o1};
+  W.cones = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(offs), as_bf16x8(bp), W.cones,
                                                     0, 0, 0);
 }
 
@@ -515,7 +554,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // Wave epilogue and workgroup merge, shared by the decode kernels: head
-// totals, removal of the 128 offset of the value codes (zero when unused),
+// totals, removal of the offsets of the value codes (zero when unused),
 // high + low columns, times oscale; then the four wave states are merged
 // through LDS (each wave's results go to the start of its own ring region,
 // `wave_stride` bytes apart) into this split's partial (o[D], m, l).
@@ -706,7 +745,8 @@ __attribute__((amdgpu_waves_per_eu(BITS == 2 ? KVQ_DECODE_WAVES_PER_SIMD : 2))) 
   const uint32_t vsh = (BITS == 2) ? uint32_t(4 * u) : uint32_t(8 * (u % 2));
   const uint32_t vm0 = (BITS == 2) ? 0x00030003u : 0x000F000Fu;
   const uint32_t vm1 = 0x000C000Cu;
-  const uint32_t magic = 0x43004300u;
+  const uint32_t magic = 0x43004300u;     // bf16 128.0: codes in bits 0..3 count 1
+  const uint32_t magic32 = 0x42004200u;   // bf16 32.0: codes in bits 2..3 count 1
 
   WaveAcc W;
   W.m_ref = -INFINITY;
@@ -765,8 +805,8 @@ __attribute__((amdgpu_waves_per_eu(BITS == 2 ? KVQ_DECODE_WAVES_PER_SIMD : 2))) 
       KLoad<BITS> K;
       VLoad V;
       load_k<BITS>(ring_w, r, u, low, K);
-      group_scores<BITS>(K, low, q16, sc);
-      u32x4 bp_prev = group_probs<BITS>(W, sc, K.vs, K.vz);
+      group_scores<BITS>(K, low, q16, 0.0f, sc);
+      u32x4 bp_prev = group_probs<BITS, false>(W, sc, K.vs, K.vz);
       int i = 1;
       // steady state: a group is loaded every iteration, one fixed wait
       for (; i + kAhead < n_mine; ++i) {
@@ -779,9 +819,9 @@ __attribute__((amdgpu_waves_per_eu(BITS == 2 ? KVQ_DECODE_WAVES_PER_SIMD : 2))) 
         load_k<BITS>(ring_w + (i % S::kDepth) * S::kBytes, r, u, low, K);
         // keep every LDS read of the iteration ahead of the arithmetic
         __builtin_amdgcn_sched_barrier(0);
-        group_scores<BITS>(K, low, q16, sc);
-        group_values<BITS>(V, W, bp_prev, vsh, vm0, vm1, magic);
-        bp_prev = group_probs<BITS>(W, sc, K.vs, K.vz);
+        group_scores<BITS>(K, low, q16, low ? 0.0f : W.m_ref, sc);
+        group_values<BITS>(V, W, bp_prev, vsh, vm0, vm1, magic, magic32);
+        bp_prev = group_probs<BITS, true>(W, sc, K.vs, K.vz);
       }
       // the last kAhead groups: nothing left to load
       for (; i < n_mine; ++i) {
@@ -790,12 +830,12 @@ __attribute__((amdgpu_waves_per_eu(BITS == 2 ? KVQ_DECODE_WAVES_PER_SIMD : 2))) 
         load_k<BITS>(ring_w + (i % S::kDepth) * S::kBytes, r, u, low, K);
         // keep every LDS read of the iteration ahead of the arithmetic
         __builtin_amdgcn_sched_barrier(0);
-        group_scores<BITS>(K, low, q16, sc);
-        group_values<BITS>(V, W, bp_prev, vsh, vm0, vm1, magic);
-        bp_prev = group_probs<BITS>(W, sc, K.vs, K.vz);
+        group_scores<BITS>(K, low, q16, low ? 0.0f : W.m_ref, sc);
+        group_values<BITS>(V, W, bp_prev, vsh, vm0, vm1, magic, magic32);
+        bp_prev = group_probs<BITS, true>(W, sc, K.vs, K.vz);
       }
       load_v<BITS>(ring_w + ((n_mine - 1) % S::kDepth) * S::kBytes, r, u, V);
-      group_values<BITS>(V, W, bp_prev, vsh, vm0, vm1, magic);
+      group_values<BITS>(V, W, bp_prev, vsh, vm0, vm1, magic, magic32);
     }
   } else {
     // the FP16 window: q·log2e/√D as fp16 high/low terms, channel 32s + 8u + j
