@@ -30,29 +30,39 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // out[b, hq, :] = Σ_s o_s·2^(m_s − M) / Σ_s l_s·2^(m_s − M), one wave per
-// (b, hq): the split maxima and sums are read by all lanes at once, then the
-// weighted partial outputs with independent loads.
+// (b, hq). The loads are issued together: lane s reads split s's (m, l), and
+// every lane reads its two channels of up to kBatch partial outputs at once,
+// so a head costs about one memory round trip per kBatch splits.
+constexpr int kBatch = 32;
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const int64_t row = blockIdx.x;   // b·Hq + hq
   const int lane = threadIdx.x;
   const float* part = a.ws + row * a.n_split * kPart;
-  float mloc = -INFINITY;
-  for (int s = lane; s < a.n_split; s += 64) mloc = fmaxf(mloc, part[s * kPart + kHeadDim]);
-  const float M = wave_max(mloc);
-  float lloc = 0.0f;
-  for (int s = lane; s < a.n_split; s += 64) {
-    const float ms = part[s * kPart + kHeadDim];
-    if (ms != -INFINITY) lloc = fmaf(exp2f(ms - M), part[s * kPart + kHeadDim + 1], lloc);
-  }
-  const float L = wave_sum(lloc);
-  float o0 = 0.0f, o1 = 0.0f;
-#pragma unroll 8
-  for (int s = 0; s < a.n_split; ++s) {
-    const float ms = part[s * kPart + kHeadDim];
-    const float2 os = *reinterpret_cast<const float2*>(part + s * kPart + 2 * lane);
-    const float f = ms == -INFINITY ? 0.0f : exp2f(ms - M);
-    o0 = fmaf(f, os.x, o0);
-    o1 = fmaf(f, os.y, o1);
+  float M = -INFINITY, L = 0.0f, o0 = 0.0f, o1 = 0.0f;
+  for (int s0 = 0; s0 < a.n_split; s0 += kBatch) {
+    const int n = min(kBatch, a.n_split - s0);
+    float2 os[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (j < n) os[j] = *reinterpret_cast<const float2*>(part + (s0 + j) * kPart + 2 * lane);
+    float2 ml = make_float2(-INFINITY, 0.0f);
+    if (lane < n) ml = *reinterpret_cast<const float2*>(part + (s0 + lane) * kPart + kHeadDim);
+    // this batch's maximum, then everything so far relative to the new one
+    const float Mb = fmaxf(M, wave_max(ml.x));
+    const float fl = ml.x == -INFINITY ? 0.0f : exp2f(ml.x - Mb);
+    const float fo = M == -INFINITY ? 0.0f : exp2f(M - Mb);
+    L = L * fo + wave_sum(fl * ml.y);
+    o0 *= fo;
+    o1 *= fo;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (j < n) {
+        const float f = __shfl(fl, j);
+        o0 = fmaf(f, os[j].x, o0);
+        o1 = fmaf(f, os[j].y, o1);
+      }
+    }
+    M = Mb;
   }
   *reinterpret_cast<float2*>(a.out + row * kHeadDim + 2 * lane) = make_float2(o0 / L, o1 / L);
 }
