@@ -9,9 +9,9 @@ after `--`):
      known size calibrates the two counters.
 Writes decode_gqa70b_32k_kernel_stats.txt, decode_gqa70b_32k_counters.txt and
 decode_gqa70b_32k_counters.json (read by bench.py for roofline.traffic, keyed by
-a hash of the decode sources) to gpurun_out/profiles/, from where they are
-copied into profiles/. Raw profiler output stays under gpurun_out/prof_*.
-Run on the GPU machine: python profile_counters.py
+a hash of the decode sources) to OUT/profiles/ (OUT below), to be copied into
+profiles/; raw profiler output stays under OUT/prof_*.
+Run on a machine with the GPU: python profile_counters.py
 """
 from __future__ import annotations
 
@@ -28,6 +28,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 OUT = os.path.join(ROOT, "gpurun_out")
 PROF = os.path.join(OUT, "profiles")          # copied into profiles/ afterwards
+# the kernel-trace pass times the bench's own default steps (so that its
+# average decode duration compares with the bench line); the counter passes,
+# which serialize every dispatch they count, use a short run
+BENCH_STATS = ["python3", os.path.join(ROOT, "bench.py"), "--steps", "256", "--warmup", "16",
+               "--no-cpu-baseline", "--no-extra", "--no-cold"]
 BENCH = ["python3", os.path.join(ROOT, "bench.py"), "--steps", "16", "--warmup", "4",
          "--no-cpu-baseline", "--no-extra", "--no-cold"]
 COPY_MIB = 1024
@@ -35,10 +40,10 @@ DECODE = "kivi_mfma_split_kernel<2>"
 MERGE = "decode_merge_kernel"
 
 
-def run(tag, prof_args, extra=()):
+def run(tag, prof_args, extra=(), bench=BENCH):
     d = os.path.join(OUT, f"prof_{tag}")
     cmd = ["rocprofv3", *prof_args, "--output-format", "csv", "-d", d, "-o", "run", "--",
-           *BENCH, *extra]
+           *bench, *extra]
     print("[profile] " + " ".join(cmd), flush=True)
     with open(os.path.join(OUT, f"prof_{tag}.log"), "w") as log:
         r = subprocess.run(cmd, stdout=log, stderr=subprocess.STDOUT, timeout=300,
@@ -66,7 +71,7 @@ def write_stats_summary(csv_path, cmd, out_path):
     srows.sort(key=lambda r: -float(r["TotalDurationNs"]))
     ours = [r for r in srows if "kvq::" in r["Name"]]
     rest = [r for r in srows if "kvq::" not in r["Name"]][:5]
-    lines = ["# rocprofv3 kernel stats, gqa70b_32k decode (bench.py, 16 timed + 4 warmup steps, "
+    lines = ["# rocprofv3 kernel stats, gqa70b_32k decode (bench.py, 256 timed + 16 warmup steps, "
              "4 layer caches)",
              f"# command: {cmd}",
              f"# {'kernel':62s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}"]
@@ -110,7 +115,7 @@ def main():
     os.makedirs(PROF, exist_ok=True)
     from bench import decode_source_hash
 
-    d1, c1 = run("stats", ["--kernel-trace", "--stats"])
+    d1, c1 = run("stats", ["--kernel-trace", "--stats"], bench=BENCH_STATS)
     stats = glob.glob(os.path.join(d1, "**", "*kernel_stats.csv"), recursive=True)[0]
     write_stats_summary(stats, rel(c1), os.path.join(PROF, "decode_gqa70b_32k_kernel_stats.txt"))
 
