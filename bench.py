@@ -222,11 +222,12 @@ def run_extra(torch, kq, synth):
     workloads, one decode step each."""
     scrub = Scrub(torch)
     out = {}
-    plan = [("llama2_7b_layer", "kivi"), ("mha_large_batch_4bit", "kivi"),
-            ("gqa_128k", "fp16"), ("gqa_128k", "fp8"), ("gqa_128k", "kivi")]
+    plan = [("llama2_7b_layer", "kivi", 32), ("mha_large_batch_4bit", "kivi", 32),
+            ("gqa70b_32k", "kivi", 64), ("gqa70b_32k", "kivi", 128),
+            ("gqa_128k", "fp16", 32), ("gqa_128k", "fp8", 32), ("gqa_128k", "kivi", 32)]
     kv_cache = {}
     outs = {}                      # gqa_128k decode outputs, same K/V and q
-    for name, fmt in plan:
+    for name, fmt, G in plan:
         c = synth.CONFIGS[name]
         B, H, Hq, S = c["batch"], c["num_kv_heads"], c["num_q_heads"], c["seq_len"]
         if name not in kv_cache:
@@ -236,8 +237,8 @@ def run_extra(torch, kq, synth):
                               synth.make_v(B, H, 0, S, D, device="cuda"))
         k, v = kv_cache[name]
         bits = c["bits"] if fmt == "kivi" else None
-        dc = kq.DeviceCache(kq.make_config(fmt, bits=bits, batch=B, num_kv_heads=H,
-                                           capacity=S))
+        dc = kq.DeviceCache(kq.make_config(fmt, bits=bits, group_size=G, batch=B,
+                                           num_kv_heads=H, capacity=S))
 
         def prefill():
             dc.reset()
@@ -252,13 +253,14 @@ def run_extra(torch, kq, synth):
         if name == "gqa_128k":
             outs[fmt] = o.double().cpu()
         nbytes = dc.decode_bytes(Hq)
-        out[f"{name}/{fmt}"] = {
+        key = f"{name}/{fmt}" + (f"_g{G}" if G != 32 else "")
+        out[key] = {
             "decode_us": round(dec, 2), "decode_bytes": nbytes,
             "decode_gbs": round(nbytes / (dec * 1e-6) / 1e9, 1),
             "decode_frac_hbm": round(nbytes / (dec * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "prefill_us": round(pre, 1)}
         del dc, ws
-        _log(f"[bench] extra {name}/{fmt}: {out[f'{name}/{fmt}']}")
+        _log(f"[bench] extra {key}: {out[key]}")
     kv_cache.clear()
     torch.cuda.empty_cache()
     # accuracy side report: FP8 and KIVI attention against FP16 attention

@@ -45,8 +45,9 @@
  * - Inputs. K/V values must be finite fp16; non-finite input is undefined
  *   behaviour (not checked). Query values must be finite fp32.
  * - Supported (else KVQ_ERR_UNSUPPORTED): head_dim = 128; batch · num_kv_heads
- *   ≤ 65535; KIVI group_size = 32,
- *   bits ∈ {2, 4}, residual_length a multiple of group_size (0 allowed);
+ *   ≤ 65535; KIVI group_size ∈ {32, 64, 128} ([KIVI-page] §3.4 names 32
+ *   and compares 64 and 128), bits ∈ {2, 4}, residual_length a multiple of
+ *   group_size (0 allowed);
  *   FP8 bits = 8; FP16 bits = 16; num_q_heads a positive multiple of
  *   num_kv_heads.
  *
@@ -81,15 +82,17 @@
  * ---------------------------------------------------------------------------
  * Let B = batch, H = num_kv_heads, D = head_dim, G = group_size, b = bits,
  * C = capacity, NG = ceil(C / G) (group slots), CT = NG · G (token slots),
- * Rcap = residual_length if > 0 else G.
+ * NT = CT / 32 (32-token tiles), Rcap = residual_length if > 0 else G.
  * KIVI:
  *   k_codes  uint32 [B][H][CT][D·b/32]   token t of (b,h): its D channel codes,
  *            code of channel d in word d/(32/b) at bits [b·(d%(32/b)), +b).
- *   v_codes  uint32 [B][H][NG][D][G·b/32] group g, channel d: the G token
- *            codes of that channel, 32/b tokens per word (token j of the
- *            group in word j/(32/b)); with i = j % (32/b), the code sits at
- *            bits [b·(i/2), +b) when i is even and [16 + b·(i/2), +b) when i
- *            is odd (even tokens fill the low half-word, odd the high).
+ *   v_codes  uint32 [B][H][NT][D][32·b/32] tile g (tokens 32g .. 32g + 31),
+ *            channel d: the 32 token codes of that channel, 32/b tokens per
+ *            word (token j of the tile in word j/(32/b)); with
+ *            i = j % (32/b), the code sits at bits [b·(i/2), +b) when i is
+ *            even and [16 + b·(i/2), +b) when i is odd (even tokens fill the
+ *            low half-word, odd the high). V is quantized per token, so the
+ *            tile size does not depend on G.
  *   k_scale, k_zero  fp32 [B][H][NG][D]   (per group, per channel)
  *   v_scale, v_zero  fp32 [B][H][CT]      (per token)
  *   k_resid, v_resid fp16 [B][H][Rcap][D] the FP16 residual window; slot i
@@ -140,7 +143,7 @@ typedef enum {
 typedef struct {
   int32_t format;          /* kvq_format                                      */
   int32_t bits;            /* KIVI 2 or 4; FP8 8; FP16 16                     */
-  int32_t group_size;      /* KIVI: G = 32 (ignored otherwise)                */
+  int32_t group_size;      /* KIVI: G ∈ {32, 64, 128} (ignored otherwise)      */
   int32_t residual_length; /* KIVI: R, multiple of G, 0 allowed (ignored else) */
   int32_t batch;           /* B ≥ 1                                           */
   int32_t num_kv_heads;    /* H ≥ 1                                           */

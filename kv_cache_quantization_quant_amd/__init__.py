@@ -254,7 +254,7 @@ class DeviceCache:
         if c.format == KVQ_FMT_KIVI:
             b = c.bits
             shapes = {"k_codes": (torch.int32, (B, H, CT, D * b // 32)),
-                      "v_codes": (torch.int32, (B, H, NG, D, G * b // 32)),
+                      "v_codes": (torch.int32, (B, H, CT // 32, D, 32 * b // 32)),
                       "k_scale": (torch.float32, (B, H, NG, D)),
                       "k_zero": (torch.float32, (B, H, NG, D)),
                       "v_scale": (torch.float32, (B, H, CT)),

@@ -42,7 +42,8 @@ kvq_status validate_config(const kvq_config* c) {
   switch (c->format) {
     case KVQ_FMT_KIVI:
       if (c->group_size <= 0 || c->residual_length < 0) return KVQ_ERR_INVALID_ARG;
-      if (c->group_size != kGroup) return KVQ_ERR_UNSUPPORTED;
+      if (c->group_size != 32 && c->group_size != 64 && c->group_size != 128)
+        return KVQ_ERR_UNSUPPORTED;
       if (c->bits != 2 && c->bits != 4) return KVQ_ERR_UNSUPPORTED;
       if (c->residual_length % c->group_size != 0) return KVQ_ERR_UNSUPPORTED;
       break;
@@ -55,14 +56,16 @@ kvq_status validate_config(const kvq_config* c) {
   // grid dimension y carries B·H
   if (int64_t(c->batch) * c->num_kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
   // keep every element index well inside int64
-  const double elems = double(c->batch) * c->num_kv_heads * (double(c->capacity) + kGroup) *
+  const double elems = double(c->batch) * c->num_kv_heads * (double(c->capacity) + 128) *
                        c->head_dim;
   if (elems > 9.0e15) return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;
 }
 
+// G: tokens per K scale group (KIVI), or the 32-token tile (FP8 / FP16);
+// NG = ⌈C/G⌉ group slots, CT = NG·G token slots, NT = CT/32 tiles of 32 tokens.
 struct Dims {
-  int64_t B, H, D, C, NG, CT, Rcap, bits;
+  int64_t B, H, D, C, G, NG, CT, NT, Rcap, bits;
 };
 
 Dims dims_of(const kvq_config& c) {
@@ -71,9 +74,11 @@ Dims dims_of(const kvq_config& c) {
   d.H = c.num_kv_heads;
   d.D = c.head_dim;
   d.C = c.capacity;
-  d.NG = ceil_div(c.capacity, kGroup);
-  d.CT = d.NG * kGroup;
-  d.Rcap = c.residual_length > 0 ? c.residual_length : kGroup;
+  d.G = c.format == KVQ_FMT_KIVI ? c.group_size : kGroup;
+  d.NG = ceil_div(c.capacity, d.G);
+  d.CT = d.NG * d.G;
+  d.NT = d.CT / kGroup;
+  d.Rcap = c.residual_length > 0 ? c.residual_length : d.G;
   d.bits = c.bits;
   return d;
 }
@@ -101,7 +106,7 @@ bool buffers_set(const kvq_cache* c) {
 // corrupted struct is rejected before it can steer a kernel out of bounds.
 bool state_ok(const kvq_cache* c, const Dims& d) {
   if (c->n_quant < 0 || c->n_resid < 0 || c->n_quant + c->n_resid > d.C) return false;
-  if (c->cfg.format == KVQ_FMT_KIVI) return c->n_quant % kGroup == 0 && c->n_resid <= d.Rcap;
+  if (c->cfg.format == KVQ_FMT_KIVI) return c->n_quant % d.G == 0 && c->n_resid <= d.Rcap;
   return c->n_resid == 0;
 }
 
@@ -115,7 +120,7 @@ kvq::VTileArgs v_tile_args(const kvq_cache* c, const Dims& d, const __half* v,
   a.n_tokens = n;
   a.dst_t0 = t0;
   a.v_dst = c->v_codes;
-  a.NT = d.NG;
+  a.NT = d.NT;
   a.bh_count = int(d.B * d.H);
   a.fp8 = c->cfg.format == KVQ_FMT_FP8_E4M3 ? 1 : 0;
   a.zero_tail = zero_tail ? 1 : 0;
@@ -190,7 +195,7 @@ kvq_status kvq_layout_query(const kvq_config* cfg, kvq_layout* out) {
   switch (cfg->format) {
     case KVQ_FMT_KIVI:
       out->k_codes = bh * d.CT * (d.D * d.bits / 32) * 4;
-      out->v_codes = bh * d.NG * d.D * (kGroup * d.bits / 32) * 4;
+      out->v_codes = bh * d.NT * d.D * (kGroup * d.bits / 32) * 4;
       out->k_scale = out->k_zero = bh * d.NG * d.D * 4;
       out->v_scale = out->v_zero = bh * d.CT * 4;
       out->k_resid = out->v_resid = bh * d.Rcap * d.D * 2;
@@ -243,20 +248,22 @@ kvq_status kvq_prefill_quantize(kvq_cache* cache, const void* k, const void* v,
   if (cache->cfg.format == KVQ_FMT_KIVI) {
     // n_quant = G·max(0, min(⌊S/G⌋, ⌈(S−R)/G⌉)); the rest stays FP16.
     const int64_t R = cache->cfg.residual_length;
-    int64_t need = seq_len > R ? ceil_div(seq_len - R, kGroup) : 0;
-    const int64_t full = seq_len / kGroup;
+    int64_t need = seq_len > R ? ceil_div(seq_len - R, d.G) : 0;
+    const int64_t full = seq_len / d.G;
     if (need > full) need = full;
-    const int64_t nq = need * kGroup;
+    const int64_t nq = need * d.G;
     const int64_t nr = seq_len - nq;
     kvq::KiviQuantArgs qa{};
     qa.k_src = kh;
     qa.v_src = vh;
     qa.src_bh_stride = seq_len * d.D;
-    qa.n_groups = int(nq / kGroup);
+    qa.n_groups = int(nq / d.G);
     qa.g0 = 0;
     qa.bh_count = bh;
     qa.bits = int(d.bits);
     qa.NG = d.NG;
+    qa.NT = d.NT;
+    qa.group = int(d.G);
     qa.k_codes = static_cast<uint32_t*>(cache->k_codes);
     qa.v_codes = static_cast<uint32_t*>(cache->v_codes);
     qa.k_scale = cache->k_scale;
@@ -340,11 +347,13 @@ kvq_status kvq_append_token(kvq_cache* cache, const void* k_new, const void* v_n
       qa.k_src = static_cast<const __half*>(cache->k_resid);
       qa.v_src = static_cast<const __half*>(cache->v_resid);
       qa.src_bh_stride = d.Rcap * d.D;
-      qa.n_groups = int(d.Rcap / kGroup);
-      qa.g0 = cache->n_quant / kGroup;
+      qa.n_groups = int(d.Rcap / d.G);
+      qa.g0 = cache->n_quant / d.G;
       qa.bh_count = bh;
       qa.bits = int(d.bits);
       qa.NG = d.NG;
+      qa.NT = d.NT;
+      qa.group = int(d.G);
       qa.k_codes = static_cast<uint32_t*>(cache->k_codes);
       qa.v_codes = static_cast<uint32_t*>(cache->v_codes);
       qa.k_scale = cache->k_scale;
@@ -453,6 +462,8 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q, int32_t 
   a.v_zero = cache->v_zero;
   a.tensor_scale = cache->tensor_scale;
   a.NG = d.NG;
+  a.NT = d.NT;
+  a.gshift = d.G == 128 ? 2 : d.G == 64 ? 1 : 0;
   a.main_bh_tokens = d.CT;
   a.n_main = cache->n_quant;
   a.k_win = static_cast<const __half*>(cache->k_resid);
@@ -478,7 +489,7 @@ int64_t kvq_decode_bytes(const kvq_cache* cache, int32_t num_q_heads) {
   const int64_t nq = cache->n_quant;
   if (cache->cfg.format == KVQ_FMT_KIVI) {
     const int64_t code_bytes = nq * d.D * d.bits / 8;       // per K and per V
-    const int64_t k_meta = (nq / kGroup) * d.D * 2 * 4;     // fp32 s, z per channel
+    const int64_t k_meta = (nq / d.G) * d.D * 2 * 4;        // fp32 s, z per channel
     const int64_t v_meta = nq * 2 * 4;                      // fp32 s, z per token
     const int64_t window = 2 * int64_t(cache->n_resid) * d.D * 2;
     return bh * (2 * code_bytes + k_meta + v_meta + window);

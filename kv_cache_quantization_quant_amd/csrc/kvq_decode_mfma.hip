@@ -620,15 +620,17 @@ struct GroupSrc {
   const uint8_t* vz;   // V zero-points, lanes 32..63
 };
 
+// Sources of 32-token tile g; its K scales and zero-points are those of
+// group g >> gshift (G = 32 << gshift tokens share them).
 template <int BITS>
 __device__ __forceinline__ GroupSrc group_src(const DecodeArgs& a, int bh, int64_t g) {
   using S = Stage<BITS>;
-  const int64_t kg = (int64_t(bh) * a.NG + g) * kHeadDim * 4;           // bytes
+  const int64_t kg = (int64_t(bh) * a.NG + (g >> a.gshift)) * kHeadDim * 4;   // bytes
   const int64_t vg = (int64_t(bh) * a.main_bh_tokens + g * kGroup) * 4;
   GroupSrc P;
   P.kc = static_cast<const uint8_t*>(a.k_main) +
          (int64_t(bh) * a.main_bh_tokens + g * kGroup) * (kHeadDim * BITS / 8) - S::kKc;
-  P.vc = static_cast<const uint8_t*>(a.v_main) + (int64_t(bh) * a.NG + g) * S::kCodeBytes -
+  P.vc = static_cast<const uint8_t*>(a.v_main) + (int64_t(bh) * a.NT + g) * S::kCodeBytes -
          (S::kVc - S::kSecond);
   P.ks = reinterpret_cast<const uint8_t*>(a.k_scale) + kg - (S::kKsz - S::kSecond);
   P.kz = reinterpret_cast<const uint8_t*>(a.k_zero) + kg - (S::kKsz - S::kSecond);
@@ -636,14 +638,15 @@ __device__ __forceinline__ GroupSrc group_src(const DecodeArgs& a, int bh, int64
   P.vz = reinterpret_cast<const uint8_t*>(a.v_zero) + vg - (S::kVsz - S::kSecond);
   return P;
 }
-// the same wavefront's next group, kWaves groups later
+// the same wavefront's next tile, kWaves tiles later (kWaves >> gshift K
+// scale groups later: kWaves·32 is a multiple of every G)
 template <int BITS>
-__device__ __forceinline__ void advance(GroupSrc& P) {
+__device__ __forceinline__ void advance(GroupSrc& P, int gshift) {
   using S = Stage<BITS>;
   P.kc += int64_t(kWaves) * S::kCodeBytes;
   P.vc += int64_t(kWaves) * S::kCodeBytes;
-  P.ks += int64_t(kWaves) * kHeadDim * 4;
-  P.kz += int64_t(kWaves) * kHeadDim * 4;
+  P.ks += int64_t(kWaves >> gshift) * kHeadDim * 4;
+  P.kz += int64_t(kWaves >> gshift) * kHeadDim * 4;
   P.vs += int64_t(kWaves) * kGroup * 4;
   P.vz += int64_t(kWaves) * kGroup * 4;
 }
@@ -790,14 +793,14 @@ __attribute__((amdgpu_waves_per_eu(BITS == 2 ? KVQ_DECODE_WAVES_PER_SIMD : 2))) 
     for (int j = 0; j < kAhead; ++j) {
       if (j < n_mine) {
         issue_group<BITS>(ring_w + j * S::kBytes, P, v16, h16, h4);
-        advance<BITS>(P);
+        advance<BITS>(P, a.gshift);
       }
     }
     if (n_mine > 0) {
       float sc[4];
       if (kAhead < n_mine) {
         issue_group<BITS>(ring_w + kAhead * S::kBytes, P, v16, h16, h4);
-        advance<BITS>(P);
+        advance<BITS>(P, a.gshift);
         wait_vmem<kAhead * S::kLoads>();
       } else {
         wait_groups<BITS>(n_mine - 1);
@@ -813,7 +816,7 @@ __attribute__((amdgpu_waves_per_eu(BITS == 2 ? KVQ_DECODE_WAVES_PER_SIMD : 2))) 
         // the refilled stage was last read two groups ago; its reads are done
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         issue_group<BITS>(ring_w + ((i + kAhead) % S::kDepth) * S::kBytes, P, v16, h16, h4);
-        advance<BITS>(P);
+        advance<BITS>(P, a.gshift);
         wait_vmem<kAhead * S::kLoads>();
         load_v<BITS>(ring_w + ((i - 1) % S::kDepth) * S::kBytes, r, u, V);
         load_k<BITS>(ring_w + (i % S::kDepth) * S::kBytes, r, u, low, K);
@@ -905,7 +908,7 @@ __device__ __forceinline__ void issue_tile(uint8_t* st, const DecodeArgs& a, int
   const uint8_t* kr = static_cast<const uint8_t*>(a.k_main) +
                       (int64_t(bh) * a.main_bh_tokens + tile * kGroup) * kHeadDim * S::kElem;
   const uint8_t* vt = static_cast<const uint8_t*>(a.v_main) +
-                      (int64_t(bh) * a.NG + tile) * int64_t(S::kRows);
+                      (int64_t(bh) * a.NT + tile) * int64_t(S::kRows);
 #pragma unroll
   for (int c = 0; c < S::kRows / 1024; ++c) {
     dma_kib(st + 1024 * c, kr + 1024 * c, v16);

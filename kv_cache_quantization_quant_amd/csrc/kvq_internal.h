@@ -10,7 +10,7 @@
 namespace kvq {
 
 constexpr int kHeadDim = 128;   // D
-constexpr int kGroup = 32;      // G (KIVI group = decode tile of tokens)
+constexpr int kGroup = 32;      // tokens per decode tile and per KIVI V code tile (the KIVI group when G = 32)
 
 // KIVI quantization of whole groups. Source tokens [0, n_groups·G) of each
 // (b, h) block of an fp16 [B·H][src_tokens][D] tensor are quantized into the
@@ -24,8 +24,10 @@ struct KiviQuantArgs {
   int bh_count;           // B·H
   int bits;
   int64_t NG;             // group slots per (b, h)
+  int64_t NT;             // 32-token V tiles per (b, h) (NG·G/32)
+  int group;              // G: 32, 64 or 128 tokens per K scale group
   uint32_t* k_codes;      // [B·H][NG·G][D·b/32]
-  uint32_t* v_codes;      // [B·H][NG][D][G·b/32]
+  uint32_t* v_codes;      // [B·H][NT][D][32·b/32]
   float* k_scale;         // [B·H][NG][D]
   float* k_zero;
   float* v_scale;         // [B·H][NG·G]
@@ -96,6 +98,8 @@ struct DecodeArgs {
   const float* v_zero;
   const float* tensor_scale;
   int64_t NG;             // KIVI group slots per (b, h)
+  int64_t NT;             // 32-token tiles per (b, h) (KIVI V codes; FP8 / FP16 V tiles)
+  int gshift;             // log2(G / 32): tile t uses the K scales of group t >> gshift
   int64_t main_bh_tokens; // token slots per (b, h) of the main region
   int64_t n_main;         // tokens in the main region
   // KIVI FP16 window

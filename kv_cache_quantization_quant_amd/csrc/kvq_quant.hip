@@ -91,72 +91,78 @@ __device__ __forceinline__ void pack16(const float (&c)[16], uint32_t (&w)[BITS 
   }
 }
 
-// One workgroup quantizes one group (32 tokens × 128 channels) of K and of V
-// for one (b, h). Loads: thread (t = tid / 8, j = tid % 8) holds channels
-// [16j, 16j + 16) of token t (256 contiguous bytes per token).
-//   V: per-token min / max over the 8 threads of a token (packed fp16 max of
-//      (x, −x), DPP exchanges), codes in registers, one word (two at 4 bits)
-//      of 16 channel codes per thread into an LDS transpose, from which each
-//      thread assembles V words along tokens.
-//   K: the tile goes through LDS; wavefront w takes channels [32w, 32w + 32),
-//      lane (pair c = l % 16, quarter u = l / 16) reduces tokens [8u, 8u + 8)
-//      of channels 32w + 2c, +1, then the four quarters are combined; codes of
-//      the thread's 16 channels follow from the per-channel scale and zero.
-template <int BITS>
+// One workgroup quantizes one group of G = 32·NS tokens (NS sub-tiles of 32
+// tokens × 128 channels) of K and of V for one (b, h). Loads: thread
+// (t = tid / 8, j = tid % 8) holds channels [16j, 16j + 16) of token t of each
+// sub-tile (256 contiguous bytes per token).
+//   V (per token): min / max over the 8 threads of a token (packed fp16 max
+//      of (x, −x), DPP exchanges), codes in registers, one word (two at 4
+//      bits) of 16 channel codes per thread into an LDS transpose, from which
+//      each thread assembles the sub-tile's V words along tokens.
+//   K (per channel over the G tokens): the group goes through LDS; wavefront
+//      w takes channels [32w, 32w + 32), lane (pair c = l % 16, quarter
+//      u = l / 16) reduces rows [u·G/4, (u+1)·G/4) of channels 32w + 2c, +1,
+//      then the four quarters are combined; codes of the thread's 16 channels
+//      follow from the per-channel scale and zero.
+template <int BITS, int NS>
 __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a) {
+  constexpr int G = NS * kGroup;           // tokens per group
   constexpr int PER = 32 / BITS;           // codes per 32-bit word
   constexpr int KW = kHeadDim / PER;       // K words per token (= V transpose rows)
-  constexpr int VW = kGroup / PER;         // V words per (group, channel)
+  constexpr int VW = kGroup / PER;         // V words per (32-token tile, channel)
   constexpr int TW = BITS / 2;             // words of one thread's 16 codes
   constexpr float QMAX = float((1 << BITS) - 1);
   constexpr int kRow = kGroup + 8;         // padded transpose row (words)
 
-  __shared__ __attribute__((aligned(16))) __half tile_k[kGroup][kHeadDim];
+  __shared__ __attribute__((aligned(16))) __half tile_k[G][kHeadDim];
   __shared__ __attribute__((aligned(16))) float s_k[kHeadDim];
   __shared__ __attribute__((aligned(16))) float z_k[kHeadDim];
   __shared__ __attribute__((aligned(16))) float r_k[kHeadDim];
-  __shared__ __attribute__((aligned(16))) uint32_t vt[KW][kRow];   // [channel word][token]
+  __shared__ __attribute__((aligned(16))) uint32_t vt[NS][KW][kRow];   // [sub][channel word][token]
 
   const int g = blockIdx.x;
   const int bh = blockIdx.y;
   const int tid = threadIdx.x;
   const int t = tid >> 3;
   const int j = tid & 7;
-  const int64_t gg = a.g0 + g;
-  const int64_t CT = a.NG * kGroup;
+  const int64_t gg = a.g0 + g;             // cache group
+  const int64_t CT = a.NG * G;
 
-  const int64_t src = bh * a.src_bh_stride + int64_t(g * kGroup + t) * kHeadDim + j * 16;
-  const uint4 k0 = *reinterpret_cast<const uint4*>(a.k_src + src);
-  const uint4 k1 = *reinterpret_cast<const uint4*>(a.k_src + src + 8);
-  const uint4 v0 = *reinterpret_cast<const uint4*>(a.v_src + src);
-  const uint4 v1 = *reinterpret_cast<const uint4*>(a.v_src + src + 8);
-  *reinterpret_cast<uint4*>(&tile_k[t][j * 16]) = k0;
-  *reinterpret_cast<uint4*>(&tile_k[t][j * 16 + 8]) = k1;
-
-  // ---- V statistics: (max, max of −x) of the 16 values, then over the 8
-  // threads of the token (xor 1, xor 2 inside a quad, then the half-row mirror).
-  const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-  h2v mx2 = as_h2(vw[0]), mn2 = mx2;
+  uint4 kr[NS][2];                         // the thread's K values of each sub-tile
 #pragma unroll
-  for (int i = 1; i < 8; ++i) {
-    mx2 = h2max(mx2, as_h2(vw[i]));
-    mn2 = h2min(mn2, as_h2(vw[i]));
-  }
-  // (max, −min) of the thread's 16 values in one fp16 pair
-  h2v mm = h2max(h2v{mx2[0], -mn2[0]}, h2v{mx2[1], -mn2[1]});
-  mm = h2max(mm, as_h2(uint32_t(__builtin_amdgcn_mov_dpp(int(as_u(mm)), 0xB1, 0xF, 0xF, false))));
-  mm = h2max(mm, as_h2(uint32_t(__builtin_amdgcn_mov_dpp(int(as_u(mm)), 0x4E, 0xF, 0xF, false))));
-  mm = h2max(mm, as_h2(uint32_t(__builtin_amdgcn_mov_dpp(int(as_u(mm)), 0x141, 0xF, 0xF, false))));
-  const float vmx = float(mm[0]);
-  const float vmn = -float(mm[1]);
-  const float vs = (vmx - vmn) / QMAX;
-  if (j == 0) {
-    a.v_scale[bh * CT + gg * kGroup + t] = vs;
-    a.v_zero[bh * CT + gg * kGroup + t] = vmn;
-  }
+  for (int sub = 0; sub < NS; ++sub) {
+    const int tr = sub * kGroup + t;       // token row within the group
+    const int64_t src = bh * a.src_bh_stride + (int64_t(g) * G + tr) * kHeadDim + j * 16;
+    kr[sub][0] = *reinterpret_cast<const uint4*>(a.k_src + src);
+    kr[sub][1] = *reinterpret_cast<const uint4*>(a.k_src + src + 8);
+    const uint4 v0 = *reinterpret_cast<const uint4*>(a.v_src + src);
+    const uint4 v1 = *reinterpret_cast<const uint4*>(a.v_src + src + 8);
+    *reinterpret_cast<uint4*>(&tile_k[tr][j * 16]) = kr[sub][0];
+    *reinterpret_cast<uint4*>(&tile_k[tr][j * 16 + 8]) = kr[sub][1];
 
-  // ---- V codes of the thread's 16 channels → the LDS transpose
-  {
+    // ---- V statistics: (max, max of −x) of the 16 values, then over the 8
+    // threads of the token (xor 1, xor 2 inside a quad, then the half-row mirror).
+    const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    h2v mx2 = as_h2(vw[0]), mn2 = mx2;
+#pragma unroll
+    for (int i = 1; i < 8; ++i) {
+      mx2 = h2max(mx2, as_h2(vw[i]));
+      mn2 = h2min(mn2, as_h2(vw[i]));
+    }
+    // (max, −min) of the thread's 16 values in one fp16 pair
+    h2v mm = h2max(h2v{mx2[0], -mn2[0]}, h2v{mx2[1], -mn2[1]});
+    mm = h2max(mm, as_h2(uint32_t(__builtin_amdgcn_mov_dpp(int(as_u(mm)), 0xB1, 0xF, 0xF, false))));
+    mm = h2max(mm, as_h2(uint32_t(__builtin_amdgcn_mov_dpp(int(as_u(mm)), 0x4E, 0xF, 0xF, false))));
+    mm = h2max(mm, as_h2(uint32_t(__builtin_amdgcn_mov_dpp(int(as_u(mm)), 0x141, 0xF, 0xF, false))));
+    const float vmx = float(mm[0]);
+    const float vmn = -float(mm[1]);
+    const float vs = (vmx - vmn) / QMAX;
+    if (j == 0) {
+      a.v_scale[bh * CT + gg * G + tr] = vs;
+      a.v_zero[bh * CT + gg * G + tr] = vmn;
+    }
+
+    // ---- V codes of the thread's 16 channels → the LDS transpose
     float vx[16], c[16];
     halves_to_float(v0, vx);
     halves_to_float(v1, vx + 8);
@@ -171,20 +177,22 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
     uint32_t w[TW];
     pack16<BITS>(c, w);
 #pragma unroll
-    for (int k = 0; k < TW; ++k) vt[TW * j + k][t] = w[k];
+    for (int k = 0; k < TW; ++k) vt[sub][TW * j + k][t] = w[k];
   }
   __syncthreads();
 
-  // ---- K statistics: wavefront w, channels 32w + 2c and 32w + 2c + 1
+  // ---- K statistics over the G rows: wavefront w, channels 32w + 2c, +1
   {
     const int wv = tid >> 6;
     const int c = tid & 15;
     const int u = (tid >> 4) & 3;
     const int d0 = 32 * wv + 2 * c;
-    h2v kmx = as_h2(*reinterpret_cast<const uint32_t*>(&tile_k[8 * u][d0])), kmn = kmx;
+    constexpr int kRowsPerQuarter = G / 4;
+    h2v kmx = as_h2(*reinterpret_cast<const uint32_t*>(&tile_k[u * kRowsPerQuarter][d0])),
+        kmn = kmx;
 #pragma unroll
-    for (int tt = 1; tt < 8; ++tt) {
-      const h2v x = as_h2(*reinterpret_cast<const uint32_t*>(&tile_k[8 * u + tt][d0]));
+    for (int tt = 1; tt < kRowsPerQuarter; ++tt) {
+      const h2v x = as_h2(*reinterpret_cast<const uint32_t*>(&tile_k[u * kRowsPerQuarter + tt][d0]));
       kmx = h2max(kmx, x);
       kmn = h2min(kmn, x);
     }
@@ -213,56 +221,68 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
     }
   }
 
-  // ---- V words: per channel, the group's 32 token codes packed along tokens;
-  // within a word, even tokens fill the low half-word and odd tokens the high.
-  uint32_t* vdst = a.v_codes + (bh * a.NG + gg) * kHeadDim * VW;
+  // ---- V words: per (tile, channel), the tile's 32 token codes packed along
+  // tokens; within a word, even tokens fill the low half-word and odd tokens
+  // the high.
 #pragma unroll
-  for (int rep = 0; rep < (kHeadDim * VW) / kThreads; ++rep) {
-    const int idx = rep * kThreads + tid;
-    const int d = idx / VW;
-    const int w = idx % VW;
-    const uint32_t* row = &vt[d / PER][w * PER];
-    const int sh = BITS * (d % PER);
-    uint32_t word = 0;
+  for (int sub = 0; sub < NS; ++sub) {
+    uint32_t* vdst = a.v_codes + (bh * a.NT + gg * NS + sub) * kHeadDim * VW;
 #pragma unroll
-    for (int q4 = 0; q4 < PER / 4; ++q4) {
-      const uint4 x = *reinterpret_cast<const uint4*>(row + 4 * q4);
-      const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+    for (int rep = 0; rep < (kHeadDim * VW) / kThreads; ++rep) {
+      const int idx = rep * kThreads + tid;
+      const int d = idx / VW;
+      const int w = idx % VW;
+      const uint32_t* row = &vt[sub][d / PER][w * PER];
+      const int sh = BITS * (d % PER);
+      uint32_t word = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * q4 + e;
-        word |= ((xs[e] >> sh) & ((1u << BITS) - 1)) << (BITS * (i / 2) + 16 * (i % 2));
+      for (int q4 = 0; q4 < PER / 4; ++q4) {
+        const uint4 x = *reinterpret_cast<const uint4*>(row + 4 * q4);
+        const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * q4 + e;
+          word |= ((xs[e] >> sh) & ((1u << BITS) - 1)) << (BITS * (i / 2) + 16 * (i % 2));
+        }
       }
+      vdst[idx] = word;
     }
-    vdst[idx] = word;
   }
   __syncthreads();
 
-  // ---- K codes: token t, channels [16j, 16j + 16), packed along channels.
-  float kx[16], c[16];
-  halves_to_float(k0, kx);
-  halves_to_float(k1, kx + 8);
-  float dev = 0.0f;
+  // ---- K codes: token 32·sub + t, channels [16j, 16j + 16), packed along channels.
+  float4 zq[4], rq[4];
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
-    const float4 z = *reinterpret_cast<const float4*>(&z_k[16 * j + 4 * q4]);
-    const float4 r = *reinterpret_cast<const float4*>(&r_k[16 * j + 4 * q4]);
-    c[4 * q4 + 0] = fast_code(kx[4 * q4 + 0], z.x, r.x, dev);
-    c[4 * q4 + 1] = fast_code(kx[4 * q4 + 1], z.y, r.y, dev);
-    c[4 * q4 + 2] = fast_code(kx[4 * q4 + 2], z.z, r.z, dev);
-    c[4 * q4 + 3] = fast_code(kx[4 * q4 + 3], z.w, r.w, dev);
+    zq[q4] = *reinterpret_cast<const float4*>(&z_k[16 * j + 4 * q4]);
+    rq[q4] = *reinterpret_cast<const float4*>(&r_k[16 * j + 4 * q4]);
   }
-  if (dev > kTieEdge) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) c[i] = float(affine_code(kx[i], z_k[16 * j + i], s_k[16 * j + i], QMAX));
-  }
-  uint32_t w[TW];
-  pack16<BITS>(c, w);
-  uint32_t* kdst = a.k_codes + (bh * CT + gg * kGroup + t) * KW;
-  if (BITS == 2) {
-    kdst[j] = w[0];
-  } else {
-    *reinterpret_cast<uint2*>(kdst + 2 * j) = make_uint2(w[0], w[TW - 1]);
+  for (int sub = 0; sub < NS; ++sub) {
+    float kx[16], c[16];
+    halves_to_float(kr[sub][0], kx);
+    halves_to_float(kr[sub][1], kx + 8);
+    float dev = 0.0f;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      c[4 * q4 + 0] = fast_code(kx[4 * q4 + 0], zq[q4].x, rq[q4].x, dev);
+      c[4 * q4 + 1] = fast_code(kx[4 * q4 + 1], zq[q4].y, rq[q4].y, dev);
+      c[4 * q4 + 2] = fast_code(kx[4 * q4 + 2], zq[q4].z, rq[q4].z, dev);
+      c[4 * q4 + 3] = fast_code(kx[4 * q4 + 3], zq[q4].w, rq[q4].w, dev);
+    }
+    if (dev > kTieEdge) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        c[i] = float(affine_code(kx[i], z_k[16 * j + i], s_k[16 * j + i], QMAX));
+    }
+    uint32_t w[TW];
+    pack16<BITS>(c, w);
+    uint32_t* kdst = a.k_codes + (bh * CT + gg * G + sub * kGroup + t) * KW;
+    if (BITS == 2) {
+      kdst[j] = w[0];
+    } else {
+      *reinterpret_cast<uint2*>(kdst + 2 * j) = make_uint2(w[0], w[TW - 1]);
+    }
   }
 }
 
@@ -485,10 +505,17 @@ __global__ __launch_bounds__(kThreads) void fp8_encode_kernel(Fp8QuantArgs a) {
 hipError_t launch_kivi_quantize(const KiviQuantArgs& a, hipStream_t s) {
   if (a.n_groups <= 0) return hipSuccess;
   dim3 grid(a.n_groups, a.bh_count);
+  const int ns = a.group / kGroup;
   if (a.bits == 2) {
-    kivi_quantize_kernel<2><<<grid, kThreads, 0, s>>>(a);
+    if (ns == 1) kivi_quantize_kernel<2, 1><<<grid, kThreads, 0, s>>>(a);
+    else if (ns == 2) kivi_quantize_kernel<2, 2><<<grid, kThreads, 0, s>>>(a);
+    else if (ns == 4) kivi_quantize_kernel<2, 4><<<grid, kThreads, 0, s>>>(a);
+    else return hipErrorInvalidValue;
   } else {
-    kivi_quantize_kernel<4><<<grid, kThreads, 0, s>>>(a);
+    if (ns == 1) kivi_quantize_kernel<4, 1><<<grid, kThreads, 0, s>>>(a);
+    else if (ns == 2) kivi_quantize_kernel<4, 2><<<grid, kThreads, 0, s>>>(a);
+    else if (ns == 4) kivi_quantize_kernel<4, 4><<<grid, kThreads, 0, s>>>(a);
+    else return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

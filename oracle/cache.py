@@ -21,9 +21,12 @@ per-tensor scales are computed from the prefill K and V and kept for appended
 tokens, which saturate at ±448.
 
 Every array is laid out as the device buffers are (see kivi.pack_k/pack_v):
-  k_codes uint32 [B][H][CT][D·b/32], v_codes uint32 [B][H][NG][D][G·b/32],
+  k_codes uint32 [B][H][CT][D·b/32], v_codes uint32 [B][H][NT][D][32·b/32],
   k_scale/k_zero fp32 [B][H][NG][D], v_scale/v_zero fp32 [B][H][CT],
-  k_resid/v_resid fp16 [B][H][Rcap][D], with NG = ceil(C/G), CT = NG·G.
+  k_resid/v_resid fp16 [B][H][Rcap][D], with NG = ceil(C/G), CT = NG·G and
+  NT = CT/32. V is quantized per token, so its codes are packed in tiles of
+  VT = 32 tokens whatever the group size (G = 32, 64 or 128 sets only how many
+  tokens share one K scale and zero-point per channel).
 FP8 and FP16 caches use tiles of T = 32 tokens: K [B][H][CT][D] (token rows,
 CT = ceil(C/T)·T) and V [B][H][NT][D][T] (per tile, one row of its T tokens per
 channel); slots that hold no token are zero.
@@ -34,11 +37,13 @@ import numpy as np
 
 from . import attention, fp8, kivi
 
+VT = 32          # tokens per packed V tile (KIVI)
+
 
 class KiviCache:
     def __init__(self, batch, num_kv_heads, head_dim, bits, group, residual,
                  capacity):
-        assert bits in (2, 4) and residual % group == 0
+        assert bits in (2, 4) and residual % group == 0 and group % VT == 0
         self.B, self.H, self.D = batch, num_kv_heads, head_dim
         self.bits, self.G, self.R, self.C = bits, group, residual, capacity
         self.Rcap = kivi.window_capacity(group, residual)
@@ -46,7 +51,8 @@ class KiviCache:
         self.CT = self.NG * group
         B, H, D = batch, num_kv_heads, head_dim
         self.k_codes = np.zeros((B, H, self.CT, D * bits // 32), np.uint32)
-        self.v_codes = np.zeros((B, H, self.NG, D, group * bits // 32), np.uint32)
+        self.NT = self.CT // VT
+        self.v_codes = np.zeros((B, H, self.NT, D, VT * bits // 32), np.uint32)
         self.k_scale = np.zeros((B, H, self.NG, D), np.float32)
         self.k_zero = np.zeros((B, H, self.NG, D), np.float32)
         self.v_scale = np.zeros((B, H, self.CT), np.float32)
@@ -74,7 +80,7 @@ class KiviCache:
                 self.k_codes[b, h, t0:t0 + T] = kivi.pack_k(kc, self.bits)
                 self.k_scale[b, h, g0:g0 + T // self.G] = ks
                 self.k_zero[b, h, g0:g0 + T // self.G] = kz
-                self.v_codes[b, h, g0:g0 + T // self.G] = kivi.pack_v(vc, self.bits, self.G)
+                self.v_codes[b, h, t0 // VT:(t0 + T) // VT] = kivi.pack_v(vc, self.bits, VT)
                 self.v_scale[b, h, t0:t0 + T] = vs
                 self.v_zero[b, h, t0:t0 + T] = vz
 
@@ -112,7 +118,7 @@ class KiviCache:
         for b in range(self.B):
             for h in range(self.H):
                 kc = kivi.unpack_k(self.k_codes[b, h, :nq], self.bits, self.D)
-                vc = kivi.unpack_v(self.v_codes[b, h, :ng], self.bits, self.G)
+                vc = kivi.unpack_v(self.v_codes[b, h, :nq // VT], self.bits, VT)
                 Kh[b, h, :nq] = kivi.dequantize_k(kc, self.k_scale[b, h, :ng],
                                                   self.k_zero[b, h, :ng], self.G)
                 Vh[b, h, :nq] = kivi.dequantize_v(vc, self.v_scale[b, h, :nq],

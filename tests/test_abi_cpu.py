@@ -57,8 +57,12 @@ def test_status_strings():
     (dict(capacity=0), kq.KVQ_ERR_INVALID_ARG),
     (dict(bits=3), kq.KVQ_ERR_UNSUPPORTED),
     (dict(bits=8), kq.KVQ_ERR_UNSUPPORTED),
-    (dict(group_size=64), kq.KVQ_ERR_UNSUPPORTED),
+    (dict(group_size=48), kq.KVQ_ERR_UNSUPPORTED),
+    (dict(group_size=256), kq.KVQ_ERR_UNSUPPORTED),
     (dict(group_size=0), kq.KVQ_ERR_INVALID_ARG),
+    (dict(group_size=64, residual_length=96), kq.KVQ_ERR_UNSUPPORTED),
+    (dict(group_size=64), 0),
+    (dict(group_size=128, residual_length=256), 0),
     (dict(residual_length=48), kq.KVQ_ERR_UNSUPPORTED),
     (dict(residual_length=-32), kq.KVQ_ERR_INVALID_ARG),
     (dict(batch=300, num_kv_heads=300), kq.KVQ_ERR_UNSUPPORTED),
@@ -84,14 +88,14 @@ def test_format_validation():
 
 
 @pytest.mark.parametrize("bits", [2, 4])
-@pytest.mark.parametrize("R", [0, 128])
-def test_kivi_layout_matches_oracle_arrays(bits, R):
+@pytest.mark.parametrize("G,R", [(32, 0), (32, 128), (64, 64), (128, 0), (128, 256)])
+def test_kivi_layout_matches_oracle_arrays(bits, G, R):
     B, H, C = 3, 5, 1000
-    cfg = kq.make_config("kivi", bits=bits, residual_length=R, batch=B, num_kv_heads=H,
-                         capacity=C)
+    cfg = kq.make_config("kivi", bits=bits, group_size=G, residual_length=R, batch=B,
+                         num_kv_heads=H, capacity=C)
     st, lay = kq.kvq_layout_query(cfg)
     assert st == 0
-    oc = ocache.KiviCache(B, H, 128, bits, 32, R, C)
+    oc = ocache.KiviCache(B, H, 128, bits, G, R, C)
     for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero",
                  "k_resid", "v_resid"):
         assert getattr(lay, name) == getattr(oc, name).nbytes, name

@@ -189,6 +189,44 @@ def test_kivi_streaming(kq, bits, R):
     assert worst <= ATOL
 
 
+@pytest.mark.parametrize("G,bits,R,B,H,Hq,S0,steps", [
+    (64, 2, 64, 2, 2, 8, 300, 140),       # flushes of one 64-token group
+    (128, 4, 128, 1, 3, 6, 500, 140),     # GQA 2, 4-bit
+    (64, 4, 0, 2, 1, 4, 256, 70),         # R = 0: the window is the open group
+    (128, 2, 256, 1, 2, 16, 1000, 30),    # longer window, GQA 8
+])
+def test_kivi_group_sizes(kq, G, bits, R, B, H, Hq, S0, steps):
+    """G = 64 and 128 ([KIVI-page] §3.4): one K scale per channel spans G
+    tokens, V codes stay in 32-token tiles. Prefill, appends with lazy
+    flushes and decodes: every buffer bit-exact, attention within the bound."""
+    C = S0 + steps
+    _say(f"[kivi G={G}] bits={bits} R={R} B={B} H={H} Hq={Hq} S0={S0} steps={steps}")
+    k, v = _kv(B, H, C)
+    dc = kq.DeviceCache(kq.make_config("kivi", bits=bits, group_size=G, residual_length=R,
+                                       batch=B, num_kv_heads=H, capacity=C))
+    oc = ocache.KiviCache(B, H, D, bits, G, R, C)
+    dc.prefill(k[:, :, :S0].contiguous(), v[:, :, :S0].contiguous())
+    oc.prefill(_np(k[:, :, :S0]), _np(v[:, :, :S0]))
+    torch.cuda.synchronize()
+    _compare_kivi_state(dc, oc)
+    ws = dc.make_workspace(Hq)
+    kn, vn = _np(k), _np(v)
+    worst = 0.0
+    for i in range(steps):
+        t = S0 + i
+        dc.append(k[:, :, t].contiguous(), v[:, :, t].contiguous())
+        oc.append(kn[:, :, t], vn[:, :, t])
+        assert (dc.n_quant, dc.n_resid) == (oc.n_quant, oc.n_resid)
+        if i % 10 == 9 or i == steps - 1:
+            q = synth.make_q(B, Hq, D, step=i, device="cuda")
+            out = dc.decode(q, workspace=ws)
+            worst = max(worst, _att_err(_np(out), oc.attention(_np(q))))
+    torch.cuda.synchronize()
+    _compare_kivi_state(dc, oc)
+    _say(f"  worst max abs err {worst:.3e}, flushes at {oc.flush_steps}")
+    assert oc.flush_steps and worst <= ATOL
+
+
 def test_append_at_capacity_is_rejected(kq):
     k, v = _kv(1, 1, 40)
     dc = kq.DeviceCache(kq.make_config("kivi", residual_length=32, capacity=40))

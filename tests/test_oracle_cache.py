@@ -91,21 +91,52 @@ def test_streaming_flush_schedule_32k():
     assert np.array_equal(c.k_resid, c2.k_resid) and np.array_equal(c.v_resid, c2.v_resid)
 
 
-@pytest.mark.parametrize("bits", [2, 4])
-def test_group_locality_ragged(bits):
-    k, v = _kv(2, 3, 300)
-    a = cache.KiviCache(2, 3, D, bits, 32, 64, 300)
+@pytest.mark.parametrize("bits,G,R", [(2, 32, 64), (4, 32, 64), (2, 64, 64), (4, 128, 128),
+                                       (2, 64, 256)])
+def test_group_locality_ragged(bits, G, R):
+    k, v = _kv(2, 3, 600)
+    a = cache.KiviCache(2, 3, D, bits, G, R, 600)
     a.prefill(k[:, :, :100], v[:, :, :100])
-    for t in range(100, 300):
+    for t in range(100, 600):
         a.append(k[:, :, t], v[:, :, t])
-    b = cache.KiviCache(2, 3, D, bits, 32, 64, 300)
+    b = cache.KiviCache(2, 3, D, bits, G, R, 600)
     b.prefill(k, v)
     n = min(a.n_quant, b.n_quant)
-    assert n >= 224
+    assert n >= 600 - 2 * R - G and n % G == 0
     assert np.array_equal(a.k_codes[:, :, :n], b.k_codes[:, :, :n])
     assert np.array_equal(a.v_scale[:, :, :n], b.v_scale[:, :, :n])
     assert np.array_equal(a.v_codes[:, :, :n // 32], b.v_codes[:, :, :n // 32])
-    assert np.array_equal(a.k_scale[:, :, :n // 32], b.k_scale[:, :, :n // 32])
+    assert np.array_equal(a.k_scale[:, :, :n // G], b.k_scale[:, :, :n // G])
+
+
+@pytest.mark.parametrize("G", [64, 128])
+def test_k_scale_spans_the_whole_group(G):
+    """With G = 64 or 128 one K scale and zero-point per channel cover all G
+    tokens of a group (checked against plain per-slice minima and maxima of
+    the input), while V stays per token and its codes stay in 32-token tiles:
+    a group whose halves have very different ranges gets one shared scale."""
+    k, v = _kv(1, 1, 4 * G)
+    k = k.copy()
+    k[0, 0, G // 2:G] *= 8          # second half of group 0 spans a wider range
+    c = cache.KiviCache(1, 1, D, 2, G, 0, 4 * G)
+    c.prefill(k, v)
+    assert c.n_quant == 4 * G and c.k_scale.shape == (1, 1, 4, D)
+    assert c.v_codes.shape == (1, 1, 4 * G // 32, D, 2)
+    x = k[0, 0].astype(np.float32)
+    for g in range(4):
+        mn = x[g * G:(g + 1) * G].min(axis=0)
+        mx = x[g * G:(g + 1) * G].max(axis=0)
+        assert np.array_equal(c.k_zero[0, 0, g], mn)
+        assert np.array_equal(c.k_scale[0, 0, g], (mx - mn) / np.float32(3))
+    # V: per-token range, whatever G is
+    xv = v[0, 0].astype(np.float32)
+    assert np.array_equal(c.v_zero[0, 0, :4 * G], xv.min(axis=1))
+    Kh, Vh = c.dequantized()
+    # every K value within half a step of its group's scale (+ fp32 slack)
+    err = np.abs(Kh[0, 0] - x)
+    for g in range(4):
+        s = c.k_scale[0, 0, g]
+        assert np.all(err[g * G:(g + 1) * G] <= s / 2 + 1e-6 * np.abs(x[g * G:(g + 1) * G]) + 1e-7)
 
 
 def test_dequantized_matches_unpacked_codes():
