@@ -222,12 +222,16 @@ def run_extra(torch, kq, synth):
     workloads, one decode step each."""
     scrub = Scrub(torch)
     out = {}
-    plan = [("llama2_7b_layer", "kivi", 32), ("mha_large_batch_4bit", "kivi", 32),
-            ("gqa70b_32k", "kivi", 64), ("gqa70b_32k", "kivi", 128),
-            ("gqa_128k", "fp16", 32), ("gqa_128k", "fp8", 32), ("gqa_128k", "kivi", 32)]
+    # (workload, format, G, K bits, V bits); None: the workload's bit width
+    plan = [("llama2_7b_layer", "kivi", 32, None, None),
+            ("mha_large_batch_4bit", "kivi", 32, None, None),
+            ("gqa70b_32k", "kivi", 64, None, None), ("gqa70b_32k", "kivi", 128, None, None),
+            ("gqa70b_32k", "kivi", 32, 4, 2), ("gqa70b_32k", "kivi", 32, 2, 4),
+            ("gqa_128k", "fp16", 32, None, None), ("gqa_128k", "fp8", 32, None, None),
+            ("gqa_128k", "kivi", 32, None, None)]
     kv_cache = {}
     outs = {}                      # gqa_128k decode outputs, same K/V and q
-    for name, fmt, G in plan:
+    for name, fmt, G, kbits, vbits in plan:
         c = synth.CONFIGS[name]
         B, H, Hq, S = c["batch"], c["num_kv_heads"], c["num_q_heads"], c["seq_len"]
         if name not in kv_cache:
@@ -236,9 +240,9 @@ def run_extra(torch, kq, synth):
             kv_cache[name] = (synth.make_k(B, H, 0, S, D, device="cuda"),
                               synth.make_v(B, H, 0, S, D, device="cuda"))
         k, v = kv_cache[name]
-        bits = c["bits"] if fmt == "kivi" else None
+        bits = (kbits or c["bits"]) if fmt == "kivi" else None
         dc = kq.DeviceCache(kq.make_config(fmt, bits=bits, group_size=G, batch=B,
-                                           num_kv_heads=H, capacity=S))
+                                           num_kv_heads=H, capacity=S, v_bits=vbits or 0))
 
         def prefill():
             dc.reset()
@@ -253,7 +257,8 @@ def run_extra(torch, kq, synth):
         if name == "gqa_128k":
             outs[fmt] = o.double().cpu()
         nbytes = dc.decode_bytes(Hq)
-        key = f"{name}/{fmt}" + (f"_g{G}" if G != 32 else "")
+        key = (f"{name}/{fmt}" + (f"_g{G}" if G != 32 else "") +
+               (f"_k{kbits}v{vbits}" if vbits else ""))
         out[key] = {
             "decode_us": round(dec, 2), "decode_bytes": nbytes,
             "decode_gbs": round(nbytes / (dec * 1e-6) / 1e9, 1),

@@ -46,8 +46,8 @@
  *   behaviour (not checked). Query values must be finite fp32.
  * - Supported (else KVQ_ERR_UNSUPPORTED): head_dim = 128; batch · num_kv_heads
  *   ≤ 65535; KIVI group_size ∈ {32, 64, 128} ([KIVI-page] §3.4 names 32
- *   and compares 64 and 128), bits ∈ {2, 4}, residual_length a multiple of
- *   group_size (0 allowed);
+ *   and compares 64 and 128), bits ∈ {2, 4} and v_bits ∈ {0, 2, 4} (K and V
+ *   bit widths), residual_length a multiple of group_size (0 allowed);
  *   FP8 bits = 8; FP16 bits = 16; num_q_heads a positive multiple of
  *   num_kv_heads.
  *
@@ -80,19 +80,20 @@
  * ---------------------------------------------------------------------------
  * Device layouts (all arrays contiguous, row-major, little-endian)
  * ---------------------------------------------------------------------------
- * Let B = batch, H = num_kv_heads, D = head_dim, G = group_size, b = bits,
+ * Let B = batch, H = num_kv_heads, D = head_dim, G = group_size, b = bits
+ * (K), b_V = v_bits if > 0 else bits (V),
  * C = capacity, NG = ceil(C / G) (group slots), CT = NG · G (token slots),
  * NT = CT / 32 (32-token tiles), Rcap = residual_length if > 0 else G.
  * KIVI:
  *   k_codes  uint32 [B][H][CT][D·b/32]   token t of (b,h): its D channel codes,
  *            code of channel d in word d/(32/b) at bits [b·(d%(32/b)), +b).
- *   v_codes  uint32 [B][H][NT][D][32·b/32] tile g (tokens 32g .. 32g + 31),
- *            channel d: the 32 token codes of that channel, 32/b tokens per
- *            word (token j of the tile in word j/(32/b)); with
- *            i = j % (32/b), the code sits at bits [b·(i/2), +b) when i is
- *            even and [16 + b·(i/2), +b) when i is odd (even tokens fill the
- *            low half-word, odd the high). V is quantized per token, so the
- *            tile size does not depend on G.
+ *   v_codes  uint32 [B][H][NT][D][32·b_V/32] tile g (tokens 32g .. 32g + 31),
+ *            channel d: the 32 token codes of that channel, 32/b_V tokens
+ *            per word (token j of the tile in word j/(32/b_V)); with
+ *            i = j % (32/b_V), the code sits at bits [b_V·(i/2), +b_V) when
+ *            i is even and [16 + b_V·(i/2), +b_V) when i is odd (even tokens
+ *            fill the low half-word, odd the high). V is quantized per token,
+ *            so the tile size does not depend on G.
  *   k_scale, k_zero  fp32 [B][H][NG][D]   (per group, per channel)
  *   v_scale, v_zero  fp32 [B][H][CT]      (per token)
  *   k_resid, v_resid fp16 [B][H][Rcap][D] the FP16 residual window; slot i
@@ -119,7 +120,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 1
+#define KVQ_ABI_VERSION 2
 
 typedef enum {
   KVQ_OK = 0,
@@ -149,6 +150,9 @@ typedef struct {
   int32_t num_kv_heads;    /* H ≥ 1                                           */
   int32_t head_dim;        /* D = 128                                         */
   int32_t capacity;        /* C ≥ 1: max tokens per sequence                  */
+  int32_t v_bits;          /* KIVI: V's bit width, 2 or 4; 0 = same as bits
+                              (K 4-bit with V 2-bit and the reverse are the
+                              mixed widths of [KIVI-page] §3.4); ignored else */
 } kvq_config;
 
 /* Bytes the caller must allocate for each device buffer (0 = unused). */

@@ -28,6 +28,8 @@ KVQ_ERR_STATE = 4
 KVQ_ERR_DEVICE = 5
 KVQ_ERR_WORKSPACE = 6
 
+ABI_VERSION = 2        # KVQ_ABI_VERSION of include/kvq.h
+
 KVQ_FMT_FP16 = 0
 KVQ_FMT_FP8_E4M3 = 1
 KVQ_FMT_KIVI = 2
@@ -38,7 +40,8 @@ FORMATS = {"fp16": KVQ_FMT_FP16, "fp8": KVQ_FMT_FP8_E4M3, "kivi": KVQ_FMT_KIVI}
 class KvqConfig(ctypes.Structure):
     _fields_ = [("format", c_int32), ("bits", c_int32), ("group_size", c_int32),
                 ("residual_length", c_int32), ("batch", c_int32),
-                ("num_kv_heads", c_int32), ("head_dim", c_int32), ("capacity", c_int32)]
+                ("num_kv_heads", c_int32), ("head_dim", c_int32), ("capacity", c_int32),
+                ("v_bits", c_int32)]
 
 
 class KvqLayout(ctypes.Structure):
@@ -87,6 +90,10 @@ def _load():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    # the structs below must match the library's
+    if lib.kvq_abi_version() != ABI_VERSION:
+        raise ImportError(f"{_LIB_PATH} has ABI version {lib.kvq_abi_version()}, this binding "
+                          f"expects {ABI_VERSION}; rebuild it")
     return lib
 
 
@@ -151,11 +158,12 @@ def kvq_theoretical_bytes(num_layers, batch, seq_len, num_kv_heads, head_dim,
 
 def make_config(fmt: str = "kivi", bits: int | None = None, group_size: int = 32,
                 residual_length: int = 128, batch: int = 1, num_kv_heads: int = 1,
-                head_dim: int = 128, capacity: int = 256) -> KvqConfig:
+                head_dim: int = 128, capacity: int = 256, v_bits: int = 0) -> KvqConfig:
+    """v_bits: KIVI V bit width (0 = same as bits)."""
     if bits is None:
         bits = {"kivi": 2, "fp8": 8, "fp16": 16}[fmt]
     return KvqConfig(FORMATS[fmt], bits, group_size, residual_length, batch, num_kv_heads,
-                     head_dim, capacity)
+                     head_dim, capacity, v_bits)
 
 
 def _check(status: int, what: str):
@@ -253,8 +261,9 @@ class DeviceCache:
         buf = self.buffers[name]
         if c.format == KVQ_FMT_KIVI:
             b = c.bits
+            bv = c.v_bits if c.v_bits > 0 else c.bits
             shapes = {"k_codes": (torch.int32, (B, H, CT, D * b // 32)),
-                      "v_codes": (torch.int32, (B, H, CT // 32, D, 32 * b // 32)),
+                      "v_codes": (torch.int32, (B, H, CT // 32, D, 32 * bv // 32)),
                       "k_scale": (torch.float32, (B, H, NG, D)),
                       "k_zero": (torch.float32, (B, H, NG, D)),
                       "v_scale": (torch.float32, (B, H, CT)),

@@ -45,6 +45,7 @@ kvq_status validate_config(const kvq_config* c) {
       if (c->group_size != 32 && c->group_size != 64 && c->group_size != 128)
         return KVQ_ERR_UNSUPPORTED;
       if (c->bits != 2 && c->bits != 4) return KVQ_ERR_UNSUPPORTED;
+      if (c->v_bits != 0 && c->v_bits != 2 && c->v_bits != 4) return KVQ_ERR_UNSUPPORTED;
       if (c->residual_length % c->group_size != 0) return KVQ_ERR_UNSUPPORTED;
       break;
     case KVQ_FMT_FP8_E4M3:
@@ -65,7 +66,7 @@ kvq_status validate_config(const kvq_config* c) {
 // G: tokens per K scale group (KIVI), or the 32-token tile (FP8 / FP16);
 // NG = ⌈C/G⌉ group slots, CT = NG·G token slots, NT = CT/32 tiles of 32 tokens.
 struct Dims {
-  int64_t B, H, D, C, G, NG, CT, NT, Rcap, bits;
+  int64_t B, H, D, C, G, NG, CT, NT, Rcap, bits, vbits;
 };
 
 Dims dims_of(const kvq_config& c) {
@@ -80,6 +81,7 @@ Dims dims_of(const kvq_config& c) {
   d.NT = d.CT / kGroup;
   d.Rcap = c.residual_length > 0 ? c.residual_length : d.G;
   d.bits = c.bits;
+  d.vbits = (c.format == KVQ_FMT_KIVI && c.v_bits > 0) ? c.v_bits : c.bits;
   return d;
 }
 
@@ -195,7 +197,7 @@ kvq_status kvq_layout_query(const kvq_config* cfg, kvq_layout* out) {
   switch (cfg->format) {
     case KVQ_FMT_KIVI:
       out->k_codes = bh * d.CT * (d.D * d.bits / 32) * 4;
-      out->v_codes = bh * d.NT * d.D * (kGroup * d.bits / 32) * 4;
+      out->v_codes = bh * d.NT * d.D * (kGroup * d.vbits / 32) * 4;
       out->k_scale = out->k_zero = bh * d.NG * d.D * 4;
       out->v_scale = out->v_zero = bh * d.CT * 4;
       out->k_resid = out->v_resid = bh * d.Rcap * d.D * 2;
@@ -261,6 +263,7 @@ kvq_status kvq_prefill_quantize(kvq_cache* cache, const void* k, const void* v,
     qa.g0 = 0;
     qa.bh_count = bh;
     qa.bits = int(d.bits);
+    qa.vbits = int(d.vbits);
     qa.NG = d.NG;
     qa.NT = d.NT;
     qa.group = int(d.G);
@@ -351,6 +354,7 @@ kvq_status kvq_append_token(kvq_cache* cache, const void* k_new, const void* v_n
       qa.g0 = cache->n_quant / d.G;
       qa.bh_count = bh;
       qa.bits = int(d.bits);
+      qa.vbits = int(d.vbits);
       qa.NG = d.NG;
       qa.NT = d.NT;
       qa.group = int(d.G);
@@ -449,6 +453,8 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q, int32_t 
   kvq::DecodeArgs a{};
   a.src = kivi ? (d.bits == 2 ? kvq::kSrcKivi2 : kvq::kSrcKivi4)
                : (cache->cfg.format == KVQ_FMT_FP8_E4M3 ? kvq::kSrcFp8 : kvq::kSrcFp16);
+  a.kbits = int(d.bits);
+  a.vbits = int(d.vbits);
   a.B = int(d.B);
   a.H = int(d.H);
   a.Hq = num_q_heads;
@@ -488,11 +494,11 @@ int64_t kvq_decode_bytes(const kvq_cache* cache, int32_t num_q_heads) {
   const int64_t bh = d.B * d.H;
   const int64_t nq = cache->n_quant;
   if (cache->cfg.format == KVQ_FMT_KIVI) {
-    const int64_t code_bytes = nq * d.D * d.bits / 8;       // per K and per V
+    const int64_t code_bytes = nq * d.D * (d.bits + d.vbits) / 8;   // K and V codes
     const int64_t k_meta = (nq / d.G) * d.D * 2 * 4;        // fp32 s, z per channel
     const int64_t v_meta = nq * 2 * 4;                      // fp32 s, z per token
     const int64_t window = 2 * int64_t(cache->n_resid) * d.D * 2;
-    return bh * (2 * code_bytes + k_meta + v_meta + window);
+    return bh * (code_bytes + k_meta + v_meta + window);
   }
   if (cache->cfg.format == KVQ_FMT_FP8_E4M3) return 2 * bh * nq * d.D + 2 * 4;
   return 2 * bh * nq * d.D * 2;

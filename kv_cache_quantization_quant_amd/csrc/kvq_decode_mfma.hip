@@ -80,19 +80,22 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// LDS stage of one group (byte offsets).
-template <int BITS>
+// LDS stage of one 32-token tile (byte offsets), K codes at KB bits and V
+// codes at VB bits.
+template <int KB, int VB>
 struct Stage {
-  static constexpr int kCodeBytes = kGroup * kHeadDim * BITS / 8;   // K codes (= V codes)
+  static constexpr int kKBytes = kGroup * kHeadDim * KB / 8;   // K codes
+  static constexpr int kVBytes = kGroup * kHeadDim * VB / 8;   // V codes
   static constexpr int kKc = 0;
-  static constexpr int kVc = kCodeBytes;
-  static constexpr int kKsz = 2 * kCodeBytes;            // 128 fp32 scales, 128 zero-points
+  static constexpr int kVc = kKBytes;
+  static constexpr int kKsz = kKBytes + kVBytes;         // 128 fp32 scales, 128 zero-points
   static constexpr int kVsz = kKsz + 2 * kHeadDim * 4;   // 32 fp32 scales, 32 zero-points
   static constexpr int kBytes = kVsz + 2 * kGroup * 4;
-  static constexpr int kDepth = BITS == 2 ? KVQ_RING_STAGES_2BIT : KVQ_RING_STAGES_4BIT;
+  static constexpr int kDepth = (KB == 2 && VB == 2) ? KVQ_RING_STAGES_2BIT : KVQ_RING_STAGES_4BIT;
   static_assert(kDepth >= 3 && kDepth <= 4, "one or two groups in flight ahead");
-  static constexpr int kLoads = 2 * (kCodeBytes / 1024) + 4;   // DMA instructions per group
-  static constexpr int kSecond = kCodeBytes;   // M0 of the second copy block (V codes on)
+  static constexpr int kLoads = (kKBytes + kVBytes) / 1024 + 4;   // DMA instructions per tile
+  static constexpr int kSecond = kKBytes;   // M0 of the second copy block (V codes on)
+  static_assert(kVsz - kSecond < 4096, "copy offsets fit the 12-bit immediate");
 };
 
 template <int N>
@@ -309,9 +312,9 @@ struct VLoad {
   uint32_t w[8][2];
 };
 
-template <int BITS>
+template <int BITS, int VB>
 __device__ __forceinline__ void load_k(const uint8_t* st, int r, int u, bool low, KLoad<BITS>& K) {
-  using S = Stage<BITS>;
+  using S = Stage<BITS, VB>;
   const uint8_t* kc = st + S::kKc;
   constexpr int kRow = kHeadDim * BITS / 8;
   if (BITS == 2) {
@@ -334,9 +337,9 @@ __device__ __forceinline__ void load_k(const uint8_t* st, int r, int u, bool low
   K.vz = vsz[kGroup / 4];
 }
 
-template <int BITS>
+template <int KB, int BITS>
 __device__ __forceinline__ void load_v(const uint8_t* st, int r, int u, VLoad& V) {
-  using S = Stage<BITS>;
+  using S = Stage<KB, BITS>;
   const uint8_t* vc = st + S::kVc;
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
@@ -622,15 +625,15 @@ struct GroupSrc {
 
 // Sources of 32-token tile g; its K scales and zero-points are those of
 // group g >> gshift (G = 32 << gshift tokens share them).
-template <int BITS>
+template <int BITS, int VB>
 __device__ __forceinline__ GroupSrc group_src(const DecodeArgs& a, int bh, int64_t g) {
-  using S = Stage<BITS>;
+  using S = Stage<BITS, VB>;
   const int64_t kg = (int64_t(bh) * a.NG + (g >> a.gshift)) * kHeadDim * 4;   // bytes
   const int64_t vg = (int64_t(bh) * a.main_bh_tokens + g * kGroup) * 4;
   GroupSrc P;
   P.kc = static_cast<const uint8_t*>(a.k_main) +
          (int64_t(bh) * a.main_bh_tokens + g * kGroup) * (kHeadDim * BITS / 8) - S::kKc;
-  P.vc = static_cast<const uint8_t*>(a.v_main) + (int64_t(bh) * a.NT + g) * S::kCodeBytes -
+  P.vc = static_cast<const uint8_t*>(a.v_main) + (int64_t(bh) * a.NT + g) * S::kVBytes -
          (S::kVc - S::kSecond);
   P.ks = reinterpret_cast<const uint8_t*>(a.k_scale) + kg - (S::kKsz - S::kSecond);
   P.kz = reinterpret_cast<const uint8_t*>(a.k_zero) + kg - (S::kKsz - S::kSecond);
@@ -640,11 +643,11 @@ __device__ __forceinline__ GroupSrc group_src(const DecodeArgs& a, int bh, int64
 }
 // the same wavefront's next tile, kWaves tiles later (kWaves >> gshift K
 // scale groups later: kWaves·32 is a multiple of every G)
-template <int BITS>
+template <int BITS, int VB>
 __device__ __forceinline__ void advance(GroupSrc& P, int gshift) {
-  using S = Stage<BITS>;
-  P.kc += int64_t(kWaves) * S::kCodeBytes;
-  P.vc += int64_t(kWaves) * S::kCodeBytes;
+  using S = Stage<BITS, VB>;
+  P.kc += int64_t(kWaves) * S::kKBytes;
+  P.vc += int64_t(kWaves) * S::kVBytes;
   P.ks += int64_t(kWaves >> gshift) * kHeadDim * 4;
   P.kz += int64_t(kWaves >> gshift) * kHeadDim * 4;
   P.vs += int64_t(kWaves) * kGroup * 4;
@@ -655,80 +658,65 @@ __device__ __forceinline__ void advance(GroupSrc& P, int gshift) {
 // codes, K scale | zero and V scale | zero (block 2, M0 = st + kSecond).
 // v16 = 16·lane, h16 = 16·(lane % 32), h4 = 4·(lane % 32). Stage::kLoads
 // instructions per group.
-template <int BITS>
+// K and V code copies: one 1 KiB copy per 2 bits of width
+#define KVQ_COPY_K1 "global_load_lds_dwordx4 %3, %6 nt\n\t"
+#define KVQ_COPY_K2 KVQ_COPY_K1 "global_load_lds_dwordx4 %3, %6 offset:1024 nt\n\t"
+#define KVQ_COPY_V1 "global_load_lds_dwordx4 %3, %7 offset:%13 nt\n\t"
+#define KVQ_COPY_V2 KVQ_COPY_V1 "global_load_lds_dwordx4 %3, %7 offset:%16 nt\n\t"
+#define KVQ_ISSUE_TILE(KCOPY, VCOPY)                                                          \
+  asm volatile("s_mov_b32 %0, m0\n\t"                                                         \
+               "s_mov_b32 m0, %2\n\t"                                                         \
+               "s_nop 0\n\t" KCOPY                                                            \
+               "s_mov_b32 m0, %9\n\t"                                                         \
+               "s_nop 0\n\t" VCOPY                                                            \
+               "s_mov_b64 %1, exec\n\t"                                                       \
+               "s_mov_b32 exec_hi, 0\n\t"                                                     \
+               "global_load_lds_dwordx4 %4, %8 offset:%14 nt\n\t"                             \
+               "global_load_lds_dword %5, %10 offset:%15 nt\n\t"                              \
+               "s_mov_b64 exec, %1\n\t"                                                       \
+               "s_mov_b32 exec_lo, 0\n\t"                                                     \
+               "global_load_lds_dwordx4 %4, %11 offset:%14 nt\n\t"                            \
+               "global_load_lds_dword %5, %12 offset:%15 nt\n\t"                              \
+               "s_mov_b64 exec, %1\n\t"                                                       \
+               "s_mov_b32 m0, %0"                                                             \
+               : "=&s"(m), "=&s"(e)                                                           \
+               : "s"(lds_addr(st)), "v"(v16), "v"(h16), "v"(h4), "s"(P.kc), "s"(P.vc),        \
+                 "s"(P.ks), "s"(lds_addr(st + S::kSecond)), "s"(P.vs), "s"(P.kz), "s"(P.vz),  \
+                 "i"(S::kVc - S::kSecond), "i"(S::kKsz - S::kSecond),                        \
+                 "i"(S::kVsz - S::kSecond), "i"(S::kVc - S::kSecond + 1024)                   \
+               : "memory")
+
+template <int KB, int VB>
 __device__ __forceinline__ void issue_group(uint8_t* st, const GroupSrc& P, uint32_t v16,
                                             uint32_t h16, uint32_t h4) {
-  using S = Stage<BITS>;
+  using S = Stage<KB, VB>;
   uint32_t m;
   uint64_t e;
-  if (BITS == 2) {
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %3, %6 nt\n\t"
-        "s_mov_b32 m0, %9\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %3, %7 offset:%13 nt\n\t"
-        "s_mov_b64 %1, exec\n\t"
-        "s_mov_b32 exec_hi, 0\n\t"
-        "global_load_lds_dwordx4 %4, %8 offset:%14 nt\n\t"
-        "global_load_lds_dword %5, %10 offset:%15 nt\n\t"
-        "s_mov_b64 exec, %1\n\t"
-        "s_mov_b32 exec_lo, 0\n\t"
-        "global_load_lds_dwordx4 %4, %11 offset:%14 nt\n\t"
-        "global_load_lds_dword %5, %12 offset:%15 nt\n\t"
-        "s_mov_b64 exec, %1\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(m), "=&s"(e)
-        : "s"(lds_addr(st)), "v"(v16), "v"(h16), "v"(h4), "s"(P.kc), "s"(P.vc), "s"(P.ks),
-          "s"(lds_addr(st + S::kSecond)), "s"(P.vs), "s"(P.kz), "s"(P.vz),
-          "i"(S::kVc - S::kSecond), "i"(S::kKsz - S::kSecond), "i"(S::kVsz - S::kSecond)
-        : "memory");
+  if constexpr (KB == 2 && VB == 2) {
+    KVQ_ISSUE_TILE(KVQ_COPY_K1, KVQ_COPY_V1);
+  } else if constexpr (KB == 4 && VB == 4) {
+    KVQ_ISSUE_TILE(KVQ_COPY_K2, KVQ_COPY_V2);
+  } else if constexpr (KB == 4) {
+    KVQ_ISSUE_TILE(KVQ_COPY_K2, KVQ_COPY_V1);
   } else {
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %3, %6 nt\n\t"
-        "global_load_lds_dwordx4 %3, %6 offset:1024 nt\n\t"
-        "s_mov_b32 m0, %9\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %3, %7 offset:%13 nt\n\t"
-        "global_load_lds_dwordx4 %3, %7 offset:%16 nt\n\t"
-        "s_mov_b64 %1, exec\n\t"
-        "s_mov_b32 exec_hi, 0\n\t"
-        "global_load_lds_dwordx4 %4, %8 offset:%14 nt\n\t"
-        "global_load_lds_dword %5, %10 offset:%15 nt\n\t"
-        "s_mov_b64 exec, %1\n\t"
-        "s_mov_b32 exec_lo, 0\n\t"
-        "global_load_lds_dwordx4 %4, %11 offset:%14 nt\n\t"
-        "global_load_lds_dword %5, %12 offset:%15 nt\n\t"
-        "s_mov_b64 exec, %1\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(m), "=&s"(e)
-        : "s"(lds_addr(st)), "v"(v16), "v"(h16), "v"(h4), "s"(P.kc), "s"(P.vc), "s"(P.ks),
-          "s"(lds_addr(st + S::kSecond)), "s"(P.vs), "s"(P.kz), "s"(P.vz),
-          "i"(S::kVc - S::kSecond), "i"(S::kKsz - S::kSecond), "i"(S::kVsz - S::kSecond),
-          "i"(S::kVc - S::kSecond + 1024)
-        : "memory");
+    KVQ_ISSUE_TILE(KVQ_COPY_K1, KVQ_COPY_V2);
   }
 }
 
 // Wait until at most `ahead` groups' copies are in flight.
-template <int BITS>
+template <int BITS, int VB>
 __device__ __forceinline__ void wait_groups(int ahead) {
-  using S = Stage<BITS>;
+  using S = Stage<BITS, VB>;
   if (ahead >= 2) wait_vmem<2 * S::kLoads>();
   else if (ahead == 1) wait_vmem<S::kLoads>();
   else wait_vmem<0>();
 }
 
-template <int BITS>
+template <int BITS, int VB>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(BITS == 2 ? KVQ_DECODE_WAVES_PER_SIMD : 2))) void kivi_mfma_split_kernel(
+__attribute__((amdgpu_waves_per_eu((BITS == 2 && VB == 2) ? KVQ_DECODE_WAVES_PER_SIMD : 2))) void kivi_mfma_split_kernel(
     DecodeArgs a) {
-  using S = Stage<BITS>;
+  using S = Stage<BITS, VB>;
   __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][S::kDepth][S::kBytes];
 
   const int split = blockIdx.x;
@@ -745,8 +733,8 @@ __attribute__((amdgpu_waves_per_eu(BITS == 2 ? KVQ_DECODE_WAVES_PER_SIMD : 2))) 
   const int hs = r & 7;
   const bool low = r >= 8;
 
-  const uint32_t vsh = (BITS == 2) ? uint32_t(4 * u) : uint32_t(8 * (u % 2));
-  const uint32_t vm0 = (BITS == 2) ? 0x00030003u : 0x000F000Fu;
+  const uint32_t vsh = (VB == 2) ? uint32_t(4 * u) : uint32_t(8 * (u % 2));
+  const uint32_t vm0 = (VB == 2) ? 0x00030003u : 0x000F000Fu;
   const uint32_t vm1 = 0x000C000Cu;
   const uint32_t magic = 0x43004300u;     // bf16 128.0: codes in bits 0..3 count 1
   const uint32_t magic32 = 0x42004200u;   // bf16 32.0: codes in bits 2..3 count 1
@@ -787,27 +775,27 @@ __attribute__((amdgpu_waves_per_eu(BITS == 2 ? KVQ_DECODE_WAVES_PER_SIMD : 2))) 
     // group i - 2, whose value products ran in the previous iteration.
     constexpr int kAhead = S::kDepth - 2;
     const uint32_t v16 = 16u * lane, h16 = 16u * (lane & 31), h4 = 4u * (lane & 31);
-    GroupSrc P = group_src<BITS>(a, bh, g0 + wave);
+    GroupSrc P = group_src<BITS, VB>(a, bh, g0 + wave);
     uint8_t* ring_w = &ring[wave][0][0];
 #pragma unroll
     for (int j = 0; j < kAhead; ++j) {
       if (j < n_mine) {
-        issue_group<BITS>(ring_w + j * S::kBytes, P, v16, h16, h4);
-        advance<BITS>(P, a.gshift);
+        issue_group<BITS, VB>(ring_w + j * S::kBytes, P, v16, h16, h4);
+        advance<BITS, VB>(P, a.gshift);
       }
     }
     if (n_mine > 0) {
       float sc[4];
       if (kAhead < n_mine) {
-        issue_group<BITS>(ring_w + kAhead * S::kBytes, P, v16, h16, h4);
-        advance<BITS>(P, a.gshift);
+        issue_group<BITS, VB>(ring_w + kAhead * S::kBytes, P, v16, h16, h4);
+        advance<BITS, VB>(P, a.gshift);
         wait_vmem<kAhead * S::kLoads>();
       } else {
-        wait_groups<BITS>(n_mine - 1);
+        wait_groups<BITS, VB>(n_mine - 1);
       }
       KLoad<BITS> K;
       VLoad V;
-      load_k<BITS>(ring_w, r, u, low, K);
+      load_k<BITS, VB>(ring_w, r, u, low, K);
       group_scores<BITS>(K, low, q16, 0.0f, sc);
       u32x4 bp_prev = group_probs<BITS, false>(W, sc, K.vs, K.vz);
       int i = 1;
@@ -815,30 +803,30 @@ __attribute__((amdgpu_waves_per_eu(BITS == 2 ? KVQ_DECODE_WAVES_PER_SIMD : 2))) 
       for (; i + kAhead < n_mine; ++i) {
         // the refilled stage was last read two groups ago; its reads are done
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        issue_group<BITS>(ring_w + ((i + kAhead) % S::kDepth) * S::kBytes, P, v16, h16, h4);
-        advance<BITS>(P, a.gshift);
+        issue_group<BITS, VB>(ring_w + ((i + kAhead) % S::kDepth) * S::kBytes, P, v16, h16, h4);
+        advance<BITS, VB>(P, a.gshift);
         wait_vmem<kAhead * S::kLoads>();
-        load_v<BITS>(ring_w + ((i - 1) % S::kDepth) * S::kBytes, r, u, V);
-        load_k<BITS>(ring_w + (i % S::kDepth) * S::kBytes, r, u, low, K);
+        load_v<BITS, VB>(ring_w + ((i - 1) % S::kDepth) * S::kBytes, r, u, V);
+        load_k<BITS, VB>(ring_w + (i % S::kDepth) * S::kBytes, r, u, low, K);
         // keep every LDS read of the iteration ahead of the arithmetic
         __builtin_amdgcn_sched_barrier(0);
         group_scores<BITS>(K, low, q16, low ? 0.0f : W.m_ref, sc);
-        group_values<BITS>(V, W, bp_prev, vsh, vm0, vm1, magic, magic32);
+        group_values<VB>(V, W, bp_prev, vsh, vm0, vm1, magic, magic32);
         bp_prev = group_probs<BITS, true>(W, sc, K.vs, K.vz);
       }
       // the last kAhead groups: nothing left to load
       for (; i < n_mine; ++i) {
-        wait_groups<BITS>(n_mine - 1 - i);
-        load_v<BITS>(ring_w + ((i - 1) % S::kDepth) * S::kBytes, r, u, V);
-        load_k<BITS>(ring_w + (i % S::kDepth) * S::kBytes, r, u, low, K);
+        wait_groups<BITS, VB>(n_mine - 1 - i);
+        load_v<BITS, VB>(ring_w + ((i - 1) % S::kDepth) * S::kBytes, r, u, V);
+        load_k<BITS, VB>(ring_w + (i % S::kDepth) * S::kBytes, r, u, low, K);
         // keep every LDS read of the iteration ahead of the arithmetic
         __builtin_amdgcn_sched_barrier(0);
         group_scores<BITS>(K, low, q16, low ? 0.0f : W.m_ref, sc);
-        group_values<BITS>(V, W, bp_prev, vsh, vm0, vm1, magic, magic32);
+        group_values<VB>(V, W, bp_prev, vsh, vm0, vm1, magic, magic32);
         bp_prev = group_probs<BITS, true>(W, sc, K.vs, K.vz);
       }
-      load_v<BITS>(ring_w + ((n_mine - 1) % S::kDepth) * S::kBytes, r, u, V);
-      group_values<BITS>(V, W, bp_prev, vsh, vm0, vm1, magic, magic32);
+      load_v<BITS, VB>(ring_w + ((n_mine - 1) % S::kDepth) * S::kBytes, r, u, V);
+      group_values<VB>(V, W, bp_prev, vsh, vm0, vm1, magic, magic32);
     }
   } else {
     // the FP16 window: q·log2e/√D as fp16 high/low terms, channel 32s + 8u + j
@@ -1101,10 +1089,16 @@ hipError_t launch_dense_mfma(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(a.n_split, a.B * a.H, a.nq / a.heads_per_chunk);
-  if (a.src == kSrcKivi2) {
-    kivi_mfma_split_kernel<2><<<grid, kThreads, 0, s>>>(a);
+  if (a.kbits == 2 && a.vbits == 2) {
+    kivi_mfma_split_kernel<2, 2><<<grid, kThreads, 0, s>>>(a);
+  } else if (a.kbits == 4 && a.vbits == 4) {
+    kivi_mfma_split_kernel<4, 4><<<grid, kThreads, 0, s>>>(a);
+  } else if (a.kbits == 4 && a.vbits == 2) {
+    kivi_mfma_split_kernel<4, 2><<<grid, kThreads, 0, s>>>(a);
+  } else if (a.kbits == 2 && a.vbits == 4) {
+    kivi_mfma_split_kernel<2, 4><<<grid, kThreads, 0, s>>>(a);
   } else {
-    kivi_mfma_split_kernel<4><<<grid, kThreads, 0, s>>>(a);
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -22,12 +22,13 @@ struct KiviQuantArgs {
   int n_groups;
   int64_t g0;
   int bh_count;           // B·H
-  int bits;
+  int bits;               // K bit width
+  int vbits;              // V bit width
   int64_t NG;             // group slots per (b, h)
   int64_t NT;             // 32-token V tiles per (b, h) (NG·G/32)
   int group;              // G: 32, 64 or 128 tokens per K scale group
   uint32_t* k_codes;      // [B·H][NG·G][D·b/32]
-  uint32_t* v_codes;      // [B·H][NT][D][32·b/32]
+  uint32_t* v_codes;      // [B·H][NT][D][32·b_V/32]
   float* k_scale;         // [B·H][NG][D]
   float* k_zero;
   float* v_scale;         // [B·H][NG·G]
@@ -86,6 +87,7 @@ enum SrcFormat : int { kSrcFp16 = 0, kSrcFp8 = 1, kSrcKivi2 = 2, kSrcKivi4 = 3 }
 // Split-K decode attention. Grid: (n_split, B·H, head_chunks).
 struct DecodeArgs {
   int src;                // SrcFormat of the main region
+  int kbits, vbits;       // KIVI K and V bit widths
   int B, H, Hq;
   int nq;                 // query heads per KV head (Hq / H)
   int heads_per_chunk;    // query heads one workgroup handles

@@ -104,21 +104,25 @@ __device__ __forceinline__ void pack16(const float (&c)[16], uint32_t (&w)[BITS 
 //      u = l / 16) reduces rows [u·G/4, (u+1)·G/4) of channels 32w + 2c, +1,
 //      then the four quarters are combined; codes of the thread's 16 channels
 //      follow from the per-channel scale and zero.
-template <int BITS, int NS>
+template <int KB, int VB, int NS>
 __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a) {
   constexpr int G = NS * kGroup;           // tokens per group
-  constexpr int PER = 32 / BITS;           // codes per 32-bit word
-  constexpr int KW = kHeadDim / PER;       // K words per token (= V transpose rows)
-  constexpr int VW = kGroup / PER;         // V words per (32-token tile, channel)
-  constexpr int TW = BITS / 2;             // words of one thread's 16 codes
-  constexpr float QMAX = float((1 << BITS) - 1);
+  constexpr int KPER = 32 / KB;            // K codes per 32-bit word
+  constexpr int KW = kHeadDim / KPER;      // K words per token
+  constexpr int KTW = KB / 2;              // words of one thread's 16 K codes
+  constexpr float KQMAX = float((1 << KB) - 1);
+  constexpr int VPER = 32 / VB;            // V codes per 32-bit word
+  constexpr int VTR = kHeadDim / VPER;     // V transpose rows (words of a token's codes)
+  constexpr int VW = kGroup / VPER;        // V words per (32-token tile, channel)
+  constexpr int VTW = VB / 2;              // words of one thread's 16 V codes
+  constexpr float VQMAX = float((1 << VB) - 1);
   constexpr int kRow = kGroup + 8;         // padded transpose row (words)
 
   __shared__ __attribute__((aligned(16))) __half tile_k[G][kHeadDim];
   __shared__ __attribute__((aligned(16))) float s_k[kHeadDim];
   __shared__ __attribute__((aligned(16))) float z_k[kHeadDim];
   __shared__ __attribute__((aligned(16))) float r_k[kHeadDim];
-  __shared__ __attribute__((aligned(16))) uint32_t vt[NS][KW][kRow];   // [sub][channel word][token]
+  __shared__ __attribute__((aligned(16))) uint32_t vt[NS][VTR][kRow];  // [sub][channel word][token]
 
   const int g = blockIdx.x;
   const int bh = blockIdx.y;
@@ -156,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
     mm = h2max(mm, as_h2(uint32_t(__builtin_amdgcn_mov_dpp(int(as_u(mm)), 0x141, 0xF, 0xF, false))));
     const float vmx = float(mm[0]);
     const float vmn = -float(mm[1]);
-    const float vs = (vmx - vmn) / QMAX;
+    const float vs = (vmx - vmn) / VQMAX;
     if (j == 0) {
       a.v_scale[bh * CT + gg * G + tr] = vs;
       a.v_zero[bh * CT + gg * G + tr] = vmn;
@@ -172,12 +176,12 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
     for (int i = 0; i < 16; ++i) c[i] = fast_code(vx[i], vmn, vr, dev);
     if (dev > kTieEdge) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) c[i] = float(affine_code(vx[i], vmn, vs, QMAX));
+      for (int i = 0; i < 16; ++i) c[i] = float(affine_code(vx[i], vmn, vs, VQMAX));
     }
-    uint32_t w[TW];
-    pack16<BITS>(c, w);
+    uint32_t w[VTW];
+    pack16<VB>(c, w);
 #pragma unroll
-    for (int k = 0; k < TW; ++k) vt[sub][TW * j + k][t] = w[k];
+    for (int k = 0; k < VTW; ++k) vt[sub][VTW * j + k][t] = w[k];
   }
   __syncthreads();
 
@@ -209,8 +213,8 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
       kmn = h2min(as_h2(pn[0]), as_h2(pn[1]));
     }
     const float mn0 = float(kmn[0]), mn1 = float(kmn[1]);
-    const float s0 = (float(kmx[0]) - mn0) / QMAX;
-    const float s1 = (float(kmx[1]) - mn1) / QMAX;
+    const float s0 = (float(kmx[0]) - mn0) / KQMAX;
+    const float s1 = (float(kmx[1]) - mn1) / KQMAX;
     if (u == 0) {
       const int64_t o = (bh * a.NG + gg) * kHeadDim + d0;
       *reinterpret_cast<float2*>(a.k_scale + o) = make_float2(s0, s1);
@@ -232,17 +236,17 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
       const int idx = rep * kThreads + tid;
       const int d = idx / VW;
       const int w = idx % VW;
-      const uint32_t* row = &vt[sub][d / PER][w * PER];
-      const int sh = BITS * (d % PER);
+      const uint32_t* row = &vt[sub][d / VPER][w * VPER];
+      const int sh = VB * (d % VPER);
       uint32_t word = 0;
 #pragma unroll
-      for (int q4 = 0; q4 < PER / 4; ++q4) {
+      for (int q4 = 0; q4 < VPER / 4; ++q4) {
         const uint4 x = *reinterpret_cast<const uint4*>(row + 4 * q4);
         const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * q4 + e;
-          word |= ((xs[e] >> sh) & ((1u << BITS) - 1)) << (BITS * (i / 2) + 16 * (i % 2));
+          word |= ((xs[e] >> sh) & ((1u << VB) - 1)) << (VB * (i / 2) + 16 * (i % 2));
         }
       }
       vdst[idx] = word;
@@ -273,15 +277,15 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
     if (dev > kTieEdge) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        c[i] = float(affine_code(kx[i], z_k[16 * j + i], s_k[16 * j + i], QMAX));
+        c[i] = float(affine_code(kx[i], z_k[16 * j + i], s_k[16 * j + i], KQMAX));
     }
-    uint32_t w[TW];
-    pack16<BITS>(c, w);
+    uint32_t w[KTW];
+    pack16<KB>(c, w);
     uint32_t* kdst = a.k_codes + (bh * CT + gg * G + sub * kGroup + t) * KW;
-    if (BITS == 2) {
+    if (KB == 2) {
       kdst[j] = w[0];
     } else {
-      *reinterpret_cast<uint2*>(kdst + 2 * j) = make_uint2(w[0], w[TW - 1]);
+      *reinterpret_cast<uint2*>(kdst + 2 * j) = make_uint2(w[0], w[KTW - 1]);
     }
   }
 }
@@ -502,21 +506,29 @@ __global__ __launch_bounds__(kThreads) void fp8_encode_kernel(Fp8QuantArgs a) {
 
 }  // namespace
 
+// launches the (K bits, V bits, NS) instance of the quantize kernel when
+// ns == NS (e becomes hipSuccess)
+template <int NS>
+static void launch_quantize_bits(const KiviQuantArgs& a, dim3 grid, hipStream_t s, int ns,
+                          hipError_t& e) {
+  if (ns != NS) return;
+  e = hipSuccess;
+  if (a.bits == 2 && a.vbits == 2) kivi_quantize_kernel<2, 2, NS><<<grid, kThreads, 0, s>>>(a);
+  else if (a.bits == 4 && a.vbits == 4) kivi_quantize_kernel<4, 4, NS><<<grid, kThreads, 0, s>>>(a);
+  else if (a.bits == 4 && a.vbits == 2) kivi_quantize_kernel<4, 2, NS><<<grid, kThreads, 0, s>>>(a);
+  else if (a.bits == 2 && a.vbits == 4) kivi_quantize_kernel<2, 4, NS><<<grid, kThreads, 0, s>>>(a);
+  else e = hipErrorInvalidValue;
+}
+
 hipError_t launch_kivi_quantize(const KiviQuantArgs& a, hipStream_t s) {
   if (a.n_groups <= 0) return hipSuccess;
   dim3 grid(a.n_groups, a.bh_count);
   const int ns = a.group / kGroup;
-  if (a.bits == 2) {
-    if (ns == 1) kivi_quantize_kernel<2, 1><<<grid, kThreads, 0, s>>>(a);
-    else if (ns == 2) kivi_quantize_kernel<2, 2><<<grid, kThreads, 0, s>>>(a);
-    else if (ns == 4) kivi_quantize_kernel<2, 4><<<grid, kThreads, 0, s>>>(a);
-    else return hipErrorInvalidValue;
-  } else {
-    if (ns == 1) kivi_quantize_kernel<4, 1><<<grid, kThreads, 0, s>>>(a);
-    else if (ns == 2) kivi_quantize_kernel<4, 2><<<grid, kThreads, 0, s>>>(a);
-    else if (ns == 4) kivi_quantize_kernel<4, 4><<<grid, kThreads, 0, s>>>(a);
-    else return hipErrorInvalidValue;
-  }
+  hipError_t e = hipErrorInvalidValue;
+  launch_quantize_bits<1>(a, grid, s, ns, e);
+  launch_quantize_bits<2>(a, grid, s, ns, e);
+  launch_quantize_bits<4>(a, grid, s, ns, e);
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 

@@ -41,18 +41,24 @@ VT = 32          # tokens per packed V tile (KIVI)
 
 
 class KiviCache:
+    """bits: K's bit width; v_bits: V's (default: the same). Mixed widths
+    (e.g. K 4-bit, V 2-bit) quantize each tensor with its own 2^b − 1 levels."""
+
     def __init__(self, batch, num_kv_heads, head_dim, bits, group, residual,
-                 capacity):
-        assert bits in (2, 4) and residual % group == 0 and group % VT == 0
+                 capacity, v_bits=None):
+        v_bits = bits if v_bits is None else v_bits
+        assert bits in (2, 4) and v_bits in (2, 4)
+        assert residual % group == 0 and group % VT == 0
         self.B, self.H, self.D = batch, num_kv_heads, head_dim
         self.bits, self.G, self.R, self.C = bits, group, residual, capacity
+        self.v_bits = v_bits
         self.Rcap = kivi.window_capacity(group, residual)
         self.NG = -(-capacity // group)
         self.CT = self.NG * group
         B, H, D = batch, num_kv_heads, head_dim
         self.k_codes = np.zeros((B, H, self.CT, D * bits // 32), np.uint32)
         self.NT = self.CT // VT
-        self.v_codes = np.zeros((B, H, self.NT, D, VT * bits // 32), np.uint32)
+        self.v_codes = np.zeros((B, H, self.NT, D, VT * v_bits // 32), np.uint32)
         self.k_scale = np.zeros((B, H, self.NG, D), np.float32)
         self.k_zero = np.zeros((B, H, self.NG, D), np.float32)
         self.v_scale = np.zeros((B, H, self.CT), np.float32)
@@ -76,11 +82,11 @@ class KiviCache:
         for b in range(self.B):
             for h in range(self.H):
                 kc, ks, kz = kivi.quantize_k(k[b, h], self.bits, self.G)
-                vc, vs, vz = kivi.quantize_v(v[b, h], self.bits)
+                vc, vs, vz = kivi.quantize_v(v[b, h], self.v_bits)
                 self.k_codes[b, h, t0:t0 + T] = kivi.pack_k(kc, self.bits)
                 self.k_scale[b, h, g0:g0 + T // self.G] = ks
                 self.k_zero[b, h, g0:g0 + T // self.G] = kz
-                self.v_codes[b, h, t0 // VT:(t0 + T) // VT] = kivi.pack_v(vc, self.bits, VT)
+                self.v_codes[b, h, t0 // VT:(t0 + T) // VT] = kivi.pack_v(vc, self.v_bits, VT)
                 self.v_scale[b, h, t0:t0 + T] = vs
                 self.v_zero[b, h, t0:t0 + T] = vz
 
@@ -118,7 +124,7 @@ class KiviCache:
         for b in range(self.B):
             for h in range(self.H):
                 kc = kivi.unpack_k(self.k_codes[b, h, :nq], self.bits, self.D)
-                vc = kivi.unpack_v(self.v_codes[b, h, :nq // VT], self.bits, VT)
+                vc = kivi.unpack_v(self.v_codes[b, h, :nq // VT], self.v_bits, VT)
                 Kh[b, h, :nq] = kivi.dequantize_k(kc, self.k_scale[b, h, :ng],
                                                   self.k_zero[b, h, :ng], self.G)
                 Vh[b, h, :nq] = kivi.dequantize_v(vc, self.v_scale[b, h, :nq],

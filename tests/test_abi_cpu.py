@@ -35,12 +35,32 @@ def test_exports_every_declared_symbol():
     assert set(kq.ABI_SYMBOLS) == set(declared)
 
 
-def test_struct_sizes_match_header():
-    # kvq_config: 8 × int32; kvq_layout: 9 × size_t; kvq_cache: cfg + 9 ptrs + i64 + 2 × i32
-    assert ctypes.sizeof(kq.KvqConfig) == 32
-    assert ctypes.sizeof(kq.KvqLayout) == 72
-    assert ctypes.sizeof(kq.KvqCache) == 32 + 9 * 8 + 8 + 8
-    assert kq.kvq_abi_version() == 1
+def test_struct_sizes_match_header(tmp_path):
+    """The ctypes structs match the C header: sizes and field offsets as a C
+    compiler lays out include/kvq.h."""
+    src = tmp_path / "layout.c"
+    fields = {"kvq_config": [f for f, _ in kq.KvqConfig._fields_],
+              "kvq_layout": [f for f, _ in kq.KvqLayout._fields_],
+              "kvq_cache": [f for f, _ in kq.KvqCache._fields_]}
+    lines = ['#include <stddef.h>', '#include <stdio.h>', '#include "kvq.h"', "int main(void) {"]
+    for st, fs in fields.items():
+        lines.append(f'  printf("{st} %zu\\n", sizeof({st}));')
+        for f in fs:
+            lines.append(f'  printf("{st}.{f} %zu\\n", offsetof({st}, {f}));')
+    lines += ["  printf(\"abi %d\\n\", KVQ_ABI_VERSION);", "  return 0;", "}"]
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o",
+                    str(exe)], check=True)
+    got = dict(line.rsplit(" ", 1) for line in
+               subprocess.run([str(exe)], capture_output=True, text=True, check=True)
+               .stdout.split("\n") if line)
+    for st, cls in (("kvq_config", kq.KvqConfig), ("kvq_layout", kq.KvqLayout),
+                    ("kvq_cache", kq.KvqCache)):
+        assert int(got[st]) == ctypes.sizeof(cls), st
+        for f in fields[st]:
+            assert int(got[f"{st}.{f}"]) == getattr(cls, f).offset, (st, f)
+    assert int(got["abi"]) == kq.kvq_abi_version() == kq.ABI_VERSION == 2
 
 
 def test_status_strings():
@@ -63,6 +83,10 @@ def test_status_strings():
     (dict(group_size=64, residual_length=96), kq.KVQ_ERR_UNSUPPORTED),
     (dict(group_size=64), 0),
     (dict(group_size=128, residual_length=256), 0),
+    (dict(v_bits=3), kq.KVQ_ERR_UNSUPPORTED),
+    (dict(v_bits=8), kq.KVQ_ERR_UNSUPPORTED),
+    (dict(bits=4, v_bits=2), 0),
+    (dict(bits=2, v_bits=4), 0),
     (dict(residual_length=48), kq.KVQ_ERR_UNSUPPORTED),
     (dict(residual_length=-32), kq.KVQ_ERR_INVALID_ARG),
     (dict(batch=300, num_kv_heads=300), kq.KVQ_ERR_UNSUPPORTED),
@@ -87,15 +111,15 @@ def test_format_validation():
     assert kq.lib.kvq_layout_query(None, None) == kq.KVQ_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits,vbits", [(2, 0), (4, 0), (4, 2), (2, 4)])
 @pytest.mark.parametrize("G,R", [(32, 0), (32, 128), (64, 64), (128, 0), (128, 256)])
-def test_kivi_layout_matches_oracle_arrays(bits, G, R):
+def test_kivi_layout_matches_oracle_arrays(bits, vbits, G, R):
     B, H, C = 3, 5, 1000
     cfg = kq.make_config("kivi", bits=bits, group_size=G, residual_length=R, batch=B,
-                         num_kv_heads=H, capacity=C)
+                         num_kv_heads=H, capacity=C, v_bits=vbits)
     st, lay = kq.kvq_layout_query(cfg)
     assert st == 0
-    oc = ocache.KiviCache(B, H, 128, bits, G, R, C)
+    oc = ocache.KiviCache(B, H, 128, bits, G, R, C, v_bits=vbits or None)
     for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero",
                  "k_resid", "v_resid"):
         assert getattr(lay, name) == getattr(oc, name).nbytes, name
@@ -123,17 +147,18 @@ def _host_cache(cfg, n_quant=0, n_resid=0, fake_ptrs=True):
     return c
 
 
-@pytest.mark.parametrize("fmt,bits", [("kivi", 2), ("kivi", 4), ("fp8", 8), ("fp16", 16)])
-def test_decode_bytes_match_oracle(fmt, bits):
+@pytest.mark.parametrize("fmt,bits,vbits", [("kivi", 2, 0), ("kivi", 4, 0), ("kivi", 4, 2),
+                                            ("kivi", 2, 4), ("fp8", 8, 0), ("fp16", 16, 0)])
+def test_decode_bytes_match_oracle(fmt, bits, vbits):
     B, H, C = 4, 8, 33024
-    cfg = kq.make_config(fmt, bits=bits, batch=B, num_kv_heads=H, capacity=C)
+    cfg = kq.make_config(fmt, bits=bits, batch=B, num_kv_heads=H, capacity=C, v_bits=vbits)
     for nq, nr in [(32640, 128), (32768, 1), (32896, 128), (0, 77)]:
         if fmt != "kivi":
             nq, nr = nq + nr, 0
         c = _host_cache(cfg, nq, nr)
         got = kq.kvq_decode_bytes(c, 64)
         if fmt == "kivi":
-            ref = bytes_model.decode_bytes_kivi(B, H, 128, bits, 32, nq, nr)
+            ref = bytes_model.decode_bytes_kivi(B, H, 128, bits, 32, nq, nr, vbits or None)
         elif fmt == "fp8":
             ref = bytes_model.decode_bytes_fp8(B, H, 128, nq)
         else:

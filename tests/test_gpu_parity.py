@@ -199,12 +199,30 @@ def test_kivi_group_sizes(kq, G, bits, R, B, H, Hq, S0, steps):
     """G = 64 and 128 ([KIVI-page] §3.4): one K scale per channel spans G
     tokens, V codes stay in 32-token tiles. Prefill, appends with lazy
     flushes and decodes: every buffer bit-exact, attention within the bound."""
+    _kivi_stream_case(kq, G, bits, 0, R, B, H, Hq, S0, steps)
+
+
+@pytest.mark.parametrize("G,bits,vbits,R,B,H,Hq,S0,steps", [
+    (32, 4, 2, 128, 2, 2, 8, 600, 70),    # K 4-bit, V 2-bit
+    (32, 2, 4, 128, 1, 3, 6, 450, 70),    # K 2-bit, V 4-bit
+    (128, 4, 2, 0, 1, 2, 16, 700, 140),   # with G = 128, R = 0
+    (64, 2, 4, 64, 2, 1, 4, 300, 70),
+])
+def test_kivi_mixed_bits(kq, G, bits, vbits, R, B, H, Hq, S0, steps):
+    """K and V at different bit widths, each 2 or 4 ([KIVI-page] §3.4): K
+    codes at K's width, V codes at V's, decode reading both. Every buffer
+    bit-exact, attention within the bound."""
+    _kivi_stream_case(kq, G, bits, vbits, R, B, H, Hq, S0, steps)
+
+
+def _kivi_stream_case(kq, G, bits, vbits, R, B, H, Hq, S0, steps):
     C = S0 + steps
-    _say(f"[kivi G={G}] bits={bits} R={R} B={B} H={H} Hq={Hq} S0={S0} steps={steps}")
+    _say(f"[kivi G={G}] bits={bits} v_bits={vbits} R={R} B={B} H={H} Hq={Hq} S0={S0} "
+         f"steps={steps}")
     k, v = _kv(B, H, C)
     dc = kq.DeviceCache(kq.make_config("kivi", bits=bits, group_size=G, residual_length=R,
-                                       batch=B, num_kv_heads=H, capacity=C))
-    oc = ocache.KiviCache(B, H, D, bits, G, R, C)
+                                       batch=B, num_kv_heads=H, capacity=C, v_bits=vbits))
+    oc = ocache.KiviCache(B, H, D, bits, G, R, C, v_bits=vbits or None)
     dc.prefill(k[:, :, :S0].contiguous(), v[:, :, :S0].contiguous())
     oc.prefill(_np(k[:, :, :S0]), _np(v[:, :, :S0]))
     torch.cuda.synchronize()

@@ -204,3 +204,26 @@ def test_synth_distributions():
     assert torch.equal(k_all[:, :, 33:], k_tail)
     n = synth.normal(0, 0, torch.arange(200_000)).numpy()
     assert abs(n.mean()) < 0.01 and abs(n.std() - 1) < 0.01
+
+
+@pytest.mark.parametrize("kb,vb", [(4, 2), (2, 4)])
+def test_mixed_bit_widths(kb, vb):
+    """K and V with their own bit widths: K codes span 2^kb − 1 levels with
+    one per-channel scale (max − min)/(2^kb − 1) per group, V codes span
+    2^vb − 1 levels per token; each reconstructs within half its own step."""
+    k, v = _kv(1, 2, 192)
+    c = cache.KiviCache(1, 2, D, kb, 32, 0, 192, v_bits=vb)
+    c.prefill(k, v)
+    assert c.k_codes.shape[-1] == D * kb // 32 and c.v_codes.shape[-1] == 32 * vb // 32
+    Kh, Vh = c.dequantized()
+    for h in range(2):
+        x = k[0, h].astype(np.float32)
+        y = v[0, h].astype(np.float32)
+        for g in range(6):
+            sl = slice(32 * g, 32 * g + 32)
+            s_k = (x[sl].max(axis=0) - x[sl].min(axis=0)) / np.float32(2 ** kb - 1)
+            assert np.array_equal(c.k_scale[0, h, g], s_k)
+            assert np.all(np.abs(Kh[0, h, sl] - x[sl]) <= s_k / 2 + 1e-6 * np.abs(x[sl]) + 1e-7)
+        s_v = (y.max(axis=1) - y.min(axis=1)) / np.float32(2 ** vb - 1)
+        assert np.array_equal(c.v_scale[0, h, :192], s_v)
+        assert np.all(np.abs(Vh[0, h] - y) <= s_v[:, None] / 2 + 1e-6 * np.abs(y) + 1e-7)
