@@ -160,12 +160,18 @@ def untile_rows(y, n_tokens):
 
 
 class Fp8Cache:
-    def __init__(self, batch, num_kv_heads, head_dim, capacity):
+    """FP8 cache: codes of the format `fmt` ("e4m3" or "e5m2"), one K and one V
+    scale per tensor, or per KV head when per_head ([Tutorial] §十八.6);
+    tensor_scale is [2] = (s_K, s_V) or [H, 2]. Scales are measured at
+    prefill and then frozen: appended tokens reuse them ([KIVI-page] §6.2)."""
+
+    def __init__(self, batch, num_kv_heads, head_dim, capacity, fmt="e4m3", per_head=False):
         self.B, self.H, self.D, self.C = batch, num_kv_heads, head_dim, capacity
+        self.fmt, self.per_head = fmt, per_head
         self.NT = -(-capacity // TILE)
         self.k_codes = np.zeros((batch, num_kv_heads, self.NT * TILE, head_dim), np.uint8)
         self.v_codes = np.zeros((batch, num_kv_heads, self.NT, head_dim, TILE), np.uint8)
-        self.tensor_scale = np.zeros(2, np.float32)
+        self.tensor_scale = np.zeros((num_kv_heads, 2) if per_head else 2, np.float32)
         self.n_quant = 0
         self.n_resid = 0
 
@@ -173,29 +179,46 @@ class Fp8Cache:
     def n_tokens(self):
         return self.n_quant
 
+    def _scales(self, which):
+        """Scale of each KV head, [H] (the one tensor scale repeated if per tensor)."""
+        ts = self.tensor_scale
+        return ts[:, which] if self.per_head else np.full(self.H, ts[which], np.float32)
+
+    def _quantize(self, x, which):
+        """x: [B, H, ...] fp16 → codes, head h with its own scale."""
+        s = self._scales(which)
+        return np.stack([fp8.quantize(x[:, h], s[h], self.fmt) for h in range(self.H)], axis=1)
+
+    def _dequantize(self, codes, which):
+        s = self._scales(which)
+        return np.stack([fp8.dequantize(codes[:, h], s[h], self.fmt) for h in range(self.H)],
+                        axis=1)
+
     def prefill(self, k, v):
         k = np.asarray(k, np.float16)
         v = np.asarray(v, np.float16)
         S = k.shape[2]
         assert self.n_quant == 0 and 1 <= S <= self.C
-        sk, sv = fp8.tensor_scale(k), fp8.tensor_scale(v)
-        self.tensor_scale[:] = (sk, sv)
-        self.k_codes[:, :, :S] = fp8.quantize(k, sk)
-        self.v_codes[:] = tile_rows(fp8.quantize(v, sv), self.NT)
+        if self.per_head:
+            self.tensor_scale[:, 0] = fp8.head_scales(k, self.fmt)
+            self.tensor_scale[:, 1] = fp8.head_scales(v, self.fmt)
+        else:
+            self.tensor_scale[:] = (fp8.tensor_scale(k, self.fmt), fp8.tensor_scale(v, self.fmt))
+        self.k_codes[:, :, :S] = self._quantize(k, 0)
+        self.v_codes[:] = tile_rows(self._quantize(v, 1), self.NT)
         self.n_quant = S
 
     def append(self, k1, v1):
         assert 0 < self.n_quant < self.C
         t = self.n_quant
-        self.k_codes[:, :, t] = fp8.quantize(np.asarray(k1, np.float16), self.tensor_scale[0])
-        self.v_codes[:, :, t // TILE, :, t % TILE] = fp8.quantize(np.asarray(v1, np.float16),
-                                                                   self.tensor_scale[1])
+        self.k_codes[:, :, t] = self._quantize(np.asarray(k1, np.float16), 0)
+        self.v_codes[:, :, t // TILE, :, t % TILE] = self._quantize(np.asarray(v1, np.float16), 1)
         self.n_quant += 1
 
     def dequantized(self):
         n = self.n_quant
-        return (fp8.dequantize(self.k_codes[:, :, :n], self.tensor_scale[0]),
-                fp8.dequantize(untile_rows(self.v_codes, n), self.tensor_scale[1]))
+        return (self._dequantize(self.k_codes[:, :, :n], 0),
+                self._dequantize(untile_rows(self.v_codes, n), 1))
 
     def attention(self, q):
         Kh, Vh = self.dequantized()

@@ -227,3 +227,27 @@ def test_mixed_bit_widths(kb, vb):
         s_v = (y.max(axis=1) - y.min(axis=1)) / np.float32(2 ** vb - 1)
         assert np.array_equal(c.v_scale[0, h, :192], s_v)
         assert np.all(np.abs(Vh[0, h] - y) <= s_v[:, None] / 2 + 1e-6 * np.abs(y) + 1e-7)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_per_head_is_per_tensor_on_each_head(fmt):
+    """Per-KV-head scales ([Tutorial] §十八.6) reduce to the per-tensor cache
+    run on each head's slice alone: same scales, same codes, after prefill and
+    after appends (scales frozen at prefill)."""
+    B, H, S, C = 2, 3, 70, 75
+    k, v = _kv(B, H, C)
+    k = k.copy()
+    k[:, 1] *= 20                                        # one wide head
+    c = cache.Fp8Cache(B, H, D, C, fmt=fmt, per_head=True)
+    c.prefill(k[:, :, :S], v[:, :, :S])
+    for t in range(S, C):
+        c.append(k[:, :, t], v[:, :, t])
+    for h in range(H):
+        r = cache.Fp8Cache(B, 1, D, C, fmt=fmt)
+        r.prefill(k[:, h:h + 1, :S], v[:, h:h + 1, :S])
+        for t in range(S, C):
+            r.append(k[:, h:h + 1, t], v[:, h:h + 1, t])
+        assert np.array_equal(c.tensor_scale[h], r.tensor_scale)
+        assert np.array_equal(c.k_codes[:, h], r.k_codes[:, 0])
+        assert np.array_equal(c.v_codes[:, h], r.v_codes[:, 0])
+    assert c.tensor_scale[1, 0] > 10 * c.tensor_scale[0, 0]
