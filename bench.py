@@ -222,16 +222,22 @@ def run_extra(torch, kq, synth):
     workloads, one decode step each."""
     scrub = Scrub(torch)
     out = {}
-    # (workload, format, G, K bits, V bits); None: the workload's bit width
-    plan = [("llama2_7b_layer", "kivi", 32, None, None),
-            ("mha_large_batch_4bit", "kivi", 32, None, None),
-            ("gqa70b_32k", "kivi", 64, None, None), ("gqa70b_32k", "kivi", 128, None, None),
-            ("gqa70b_32k", "kivi", 32, 4, 2), ("gqa70b_32k", "kivi", 32, 2, 4),
-            ("gqa_128k", "fp16", 32, None, None), ("gqa_128k", "fp8", 32, None, None),
-            ("gqa_128k", "kivi", 32, None, None)]
+    # workload, format and the knobs that differ from the workload's defaults
+    # (G = 32, the workload's bit width for K and V, per-tensor FP8 scales)
+    plan = [dict(name="llama2_7b_layer", fmt="kivi"),
+            dict(name="mha_large_batch_4bit", fmt="kivi"),
+            dict(name="gqa70b_32k", fmt="kivi", G=64), dict(name="gqa70b_32k", fmt="kivi", G=128),
+            dict(name="gqa70b_32k", fmt="kivi", kbits=4, vbits=2),
+            dict(name="gqa70b_32k", fmt="kivi", kbits=2, vbits=4),
+            dict(name="gqa_128k", fmt="fp16"), dict(name="gqa_128k", fmt="fp8"),
+            dict(name="gqa_128k", fmt="fp8", per_head=1), dict(name="gqa_128k", fmt="fp8_e5m2"),
+            dict(name="gqa_128k", fmt="kivi")]
     kv_cache = {}
     outs = {}                      # gqa_128k decode outputs, same K/V and q
-    for name, fmt, G, kbits, vbits in plan:
+    for item in plan:
+        name, fmt = item["name"], item["fmt"]
+        G, kbits, vbits = item.get("G", 32), item.get("kbits"), item.get("vbits")
+        per_head = item.get("per_head", 0)
         c = synth.CONFIGS[name]
         B, H, Hq, S = c["batch"], c["num_kv_heads"], c["num_q_heads"], c["seq_len"]
         if name not in kv_cache:
@@ -242,7 +248,8 @@ def run_extra(torch, kq, synth):
         k, v = kv_cache[name]
         bits = (kbits or c["bits"]) if fmt == "kivi" else None
         dc = kq.DeviceCache(kq.make_config(fmt, bits=bits, group_size=G, batch=B,
-                                           num_kv_heads=H, capacity=S, v_bits=vbits or 0))
+                                           num_kv_heads=H, capacity=S, v_bits=vbits or 0,
+                                           scale_per_head=per_head))
 
         def prefill():
             dc.reset()
@@ -255,10 +262,10 @@ def run_extra(torch, kq, synth):
         dec = statistics.median(time_launches(
             torch, lambda: dc.decode(q, out=o, workspace=ws), 10, scrub))
         if name == "gqa_128k":
-            outs[fmt] = o.double().cpu()
+            outs[fmt + ("_per_head" if per_head else "")] = o.double().cpu()
         nbytes = dc.decode_bytes(Hq)
         key = (f"{name}/{fmt}" + (f"_g{G}" if G != 32 else "") +
-               (f"_k{kbits}v{vbits}" if vbits else ""))
+               (f"_k{kbits}v{vbits}" if vbits else "") + ("_per_head" if per_head else ""))
         out[key] = {
             "decode_us": round(dec, 2), "decode_bytes": nbytes,
             "decode_gbs": round(nbytes / (dec * 1e-6) / 1e9, 1),
@@ -271,7 +278,7 @@ def run_extra(torch, kq, synth):
     # accuracy side report: FP8 and KIVI attention against FP16 attention
     ref = outs["fp16"]
     acc = {}
-    for fmt in ("fp8", "kivi"):
+    for fmt in ("fp8", "fp8_per_head", "fp8_e5m2", "kivi"):
         d = outs[fmt] - ref
         acc[fmt] = {"max_abs": float(d.abs().max()),
                     "rel_l2": float(d.norm() / ref.norm())}

@@ -4,11 +4,12 @@
  *
  * Sources the operations follow (web pages, cited by title and section):
  *   [KIVI-page]  "4.4 KV Cache 量化：KIVI 2-bit 与 FP8 KV Cache"
- *                (aiinfraguide.pages.dev), §2, §3.1–3.4, §5
+ *                (aiinfraguide.pages.dev), §2, §3.1–3.4, §5, §6.3
  *   [Tutorial]   "大模型量化从0到1（十三）：KV Cache 量化——长上下文为什么越跑越吃显存"
  *                (aiot.csdn.net), §二 (attention), §四 (byte formula),
  *                §五 (MHA/GQA), §八.4 (online critical path), §九 (KIVI),
- *                §十 (affine / FP8 formulas, granularity, residual window)
+ *                §十 (affine / FP8 formulas, granularity, residual window),
+ *                §十八.4 (E4M3 vs E5M2), §十八.6 (per-attention-head scales)
  *   [Interview]  "KV Cache 量化是什么？它如何降低长上下文推理显存？"
  *                (offer.aigcbaba.com), §三 (byte formula), §四 (pipeline)
  *   [FP8-page]   "LLM推理加速KV Cache量化压缩实战方案" (yunthe.com),
@@ -48,8 +49,8 @@
  *   ≤ 65535; KIVI group_size ∈ {32, 64, 128} ([KIVI-page] §3.4 names 32
  *   and compares 64 and 128), bits ∈ {2, 4} and v_bits ∈ {0, 2, 4} (K and V
  *   bit widths), residual_length a multiple of group_size (0 allowed);
- *   FP8 bits = 8; FP16 bits = 16; num_q_heads a positive multiple of
- *   num_kv_heads.
+ *   FP8 (E4M3 or E5M2) bits = 8 and scale_per_head ∈ {0, 1}; FP16 bits =
+ *   16; num_q_heads a positive multiple of num_kv_heads.
  *
  * ---------------------------------------------------------------------------
  * Numerics (bit-exact contract for KIVI codes, scales and zero-points)
@@ -68,13 +69,17 @@
  *       aligned to token index multiples of G from position 0.
  *   V — per token: one (s, z) per token over its head_dim channels.
  *
- * FP8 E4M3 per-tensor path ([FP8-page], [Tutorial] §十 FP8 formula,
- * [KIVI-page] §5 for the 1-4-3 layout):
- *   s_K = amax(|K|) / 448 over the whole prefill K tensor, s_V likewise
- *   (s = 0 when amax = 0: every code is then 0);
- *   code = e4m3(min(max(x / s, −448), 448)) with round-to-nearest-even, OCP
- *   "fn" encoding (no infinities; 0x7F/0xFF are NaN and never produced),
- *   signed zero kept; x̂ = (float)e4m3_value(code) · s.
+ * FP8 path ([FP8-page], [Tutorial] §十 FP8 formula, [KIVI-page] §5 for the
+ * 1-4-3 layout, [Tutorial] §十八.4 for E5M2), FMAX = 448 (E4M3) or 57344
+ * (E5M2):
+ *   s_K = amax(|K|) / FMAX over the whole prefill K tensor, s_V likewise
+ *   (s = 0 when amax = 0: every code is then 0); with scale_per_head, one
+ *   s_K and one s_V per KV head h, amax over all batch rows, tokens and
+ *   channels of head h ([Tutorial] §十八.6, [KIVI-page] §6.3);
+ *   code = fp8(min(max(x / s, −FMAX), FMAX)) with round-to-nearest-even,
+ *   signed zero kept. E4M3 is OCP "fn" (no infinities; 0x7F/0xFF are NaN and
+ *   never produced); E5M2 is OCP E5M2 (bias 15; infinities and NaN are never
+ *   produced). x̂ = (float)fp8_value(code) · s.
  *   The scales are fixed at prefill; appended tokens reuse them and saturate.
  *
  * ---------------------------------------------------------------------------
@@ -98,15 +103,16 @@
  *   v_scale, v_zero  fp32 [B][H][CT]      (per token)
  *   k_resid, v_resid fp16 [B][H][Rcap][D] the FP16 residual window; slot i
  *            holds token n_quant + i.
- * FP8 E4M3 and FP16 (baseline, no quantization) use tiles of T = 32 tokens,
+ * FP8 and FP16 (baseline, no quantization) use tiles of T = 32 tokens,
  * NT = ceil(C / T), CTT = NT · T:
- *   k_codes  [B][H][CTT][D]   token rows (uint8 E4M3 codes, or fp16 values);
+ *   k_codes  [B][H][CTT][D]   token rows (uint8 FP8 codes, or fp16 values);
  *   v_codes  [B][H][NT][D][T] tile g, channel d: the values of tokens
  *            g·T .. g·T + T − 1 (element (t, d) at [t / T][d][t % T]);
  *            slots between the last prefilled token and the end of its tile
  *            are written as zero.
- *   tensor_scale (FP8 only) fp32 [4] = {s_K, s_V, amax_K, amax_V} (the amax
- *   slots are scratch of the prefill reduction).
+ *   tensor_scale (FP8 only) fp32 [NS][4], NS = H with scale_per_head else 1:
+ *   row h = {s_K, s_V, amax_K, amax_V} of KV head h (or of the tensor); the
+ *   amax slots are scratch of the prefill reduction.
  * Decode I/O: q, out fp32 [B][Hq][D]. Query head hq reads KV head
  *   hq / (Hq / H) (consecutive query heads share a KV head, [Tutorial] §五.3).
  */
@@ -120,7 +126,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 2
+#define KVQ_ABI_VERSION 3
 
 typedef enum {
   KVQ_OK = 0,
@@ -135,8 +141,9 @@ typedef enum {
 
 typedef enum {
   KVQ_FMT_FP16 = 0,     /* unquantized fp16 cache (baseline)                */
-  KVQ_FMT_FP8_E4M3 = 1, /* per-tensor FP8 E4M3, scale = amax / 448          */
-  KVQ_FMT_KIVI = 2      /* K per-channel / V per-token groups + FP16 window */
+  KVQ_FMT_FP8_E4M3 = 1, /* FP8 E4M3, scale = amax / 448                     */
+  KVQ_FMT_KIVI = 2,     /* K per-channel / V per-token groups + FP16 window */
+  KVQ_FMT_FP8_E5M2 = 3  /* FP8 E5M2, scale = amax / 57344                   */
 } kvq_format;
 
 /* Cache configuration. The KIVI knobs mirror the pages' `nbits`,
@@ -153,6 +160,9 @@ typedef struct {
   int32_t v_bits;          /* KIVI: V's bit width, 2 or 4; 0 = same as bits
                               (K 4-bit with V 2-bit and the reverse are the
                               mixed widths of [KIVI-page] §3.4); ignored else */
+  int32_t scale_per_head;  /* FP8: 0 = one K and one V scale per tensor, 1 = one
+                              pair per KV head ([Tutorial] §十八.6); ignored
+                              else                                            */
 } kvq_config;
 
 /* Bytes the caller must allocate for each device buffer (0 = unused). */
@@ -177,7 +187,7 @@ typedef struct {
   float* v_zero;       /* device, KIVI */
   void* k_resid;       /* device, KIVI */
   void* v_resid;       /* device, KIVI */
-  float* tensor_scale; /* device, FP8: {s_K, s_V, amax_K, amax_V} */
+  float* tensor_scale; /* device, FP8: [NS][4] {s_K, s_V, amax_K, amax_V} */
   int64_t n_quant;
   int32_t n_resid;
   int32_t reserved;
@@ -237,7 +247,8 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q,
 
 /* Algorithmic bytes one decode step must read from the cache at its current
  * fill state: codes, scales and zero-points of the grouped region plus the
- * fp16 window (KIVI); codes plus the two scales (FP8); fp16 K and V (FP16).
+ * fp16 window (KIVI); codes plus the K and V scales, per tensor or per KV
+ * head (FP8); fp16 K and V (FP16).
  * Query and output bytes are not included. −1 on invalid input. */
 int64_t kvq_decode_bytes(const kvq_cache* cache, int32_t num_q_heads);
 

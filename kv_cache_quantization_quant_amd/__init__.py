@@ -28,20 +28,23 @@ KVQ_ERR_STATE = 4
 KVQ_ERR_DEVICE = 5
 KVQ_ERR_WORKSPACE = 6
 
-ABI_VERSION = 2        # KVQ_ABI_VERSION of include/kvq.h
+ABI_VERSION = 3        # KVQ_ABI_VERSION of include/kvq.h
 
 KVQ_FMT_FP16 = 0
 KVQ_FMT_FP8_E4M3 = 1
 KVQ_FMT_KIVI = 2
+KVQ_FMT_FP8_E5M2 = 3
 
-FORMATS = {"fp16": KVQ_FMT_FP16, "fp8": KVQ_FMT_FP8_E4M3, "kivi": KVQ_FMT_KIVI}
+FORMATS = {"fp16": KVQ_FMT_FP16, "fp8": KVQ_FMT_FP8_E4M3, "kivi": KVQ_FMT_KIVI,
+           "fp8_e5m2": KVQ_FMT_FP8_E5M2}
+FP8_FORMATS = (KVQ_FMT_FP8_E4M3, KVQ_FMT_FP8_E5M2)
 
 
 class KvqConfig(ctypes.Structure):
     _fields_ = [("format", c_int32), ("bits", c_int32), ("group_size", c_int32),
                 ("residual_length", c_int32), ("batch", c_int32),
                 ("num_kv_heads", c_int32), ("head_dim", c_int32), ("capacity", c_int32),
-                ("v_bits", c_int32)]
+                ("v_bits", c_int32), ("scale_per_head", c_int32)]
 
 
 class KvqLayout(ctypes.Structure):
@@ -158,12 +161,14 @@ def kvq_theoretical_bytes(num_layers, batch, seq_len, num_kv_heads, head_dim,
 
 def make_config(fmt: str = "kivi", bits: int | None = None, group_size: int = 32,
                 residual_length: int = 128, batch: int = 1, num_kv_heads: int = 1,
-                head_dim: int = 128, capacity: int = 256, v_bits: int = 0) -> KvqConfig:
-    """v_bits: KIVI V bit width (0 = same as bits)."""
+                head_dim: int = 128, capacity: int = 256, v_bits: int = 0,
+                scale_per_head: int = 0) -> KvqConfig:
+    """v_bits: KIVI V bit width (0 = same as bits); scale_per_head: FP8 scales
+    per KV head (1) or per tensor (0)."""
     if bits is None:
-        bits = {"kivi": 2, "fp8": 8, "fp16": 16}[fmt]
+        bits = {"kivi": 2, "fp8": 8, "fp8_e5m2": 8, "fp16": 16}[fmt]
     return KvqConfig(FORMATS[fmt], bits, group_size, residual_length, batch, num_kv_heads,
-                     head_dim, capacity, v_bits)
+                     head_dim, capacity, v_bits, scale_per_head)
 
 
 def _check(status: int, what: str):
@@ -270,11 +275,12 @@ class DeviceCache:
                       "v_zero": (torch.float32, (B, H, CT)),
                       "k_resid": (torch.float16, (B, H, Rcap, D)),
                       "v_resid": (torch.float16, (B, H, Rcap, D))}
-        elif c.format == KVQ_FMT_FP8_E4M3:
+        elif c.format in FP8_FORMATS:
             NT = -(-c.capacity // 32)
             shapes = {"k_codes": (torch.uint8, (B, H, NT * 32, D)),
                       "v_codes": (torch.uint8, (B, H, NT, D, 32)),
-                      "tensor_scale": (torch.float32, (4,))}
+                      "tensor_scale": (torch.float32,
+                                       (H, 4) if c.scale_per_head else (4,))}
         else:
             NT = -(-c.capacity // 32)
             shapes = {"k_codes": (torch.float16, (B, H, NT * 32, D)),

@@ -32,9 +32,14 @@ constexpr int64_t kMinTilesPerSplit = 4;   // one tile per wavefront at least
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+bool is_fp8(int32_t format) { return format == KVQ_FMT_FP8_E4M3 || format == KVQ_FMT_FP8_E5M2; }
+
+// KV heads with their own FP8 scale row (1: one row for the tensor)
+int64_t fp8_scale_rows(const kvq_config& c) { return c.scale_per_head ? c.num_kv_heads : 1; }
+
 kvq_status validate_config(const kvq_config* c) {
   if (c == nullptr) return KVQ_ERR_INVALID_ARG;
-  if (c->format != KVQ_FMT_FP16 && c->format != KVQ_FMT_FP8_E4M3 && c->format != KVQ_FMT_KIVI)
+  if (c->format != KVQ_FMT_FP16 && c->format != KVQ_FMT_KIVI && !is_fp8(c->format))
     return KVQ_ERR_INVALID_ARG;
   if (c->batch <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0 || c->capacity <= 0)
     return KVQ_ERR_INVALID_ARG;
@@ -49,7 +54,9 @@ kvq_status validate_config(const kvq_config* c) {
       if (c->residual_length % c->group_size != 0) return KVQ_ERR_UNSUPPORTED;
       break;
     case KVQ_FMT_FP8_E4M3:
+    case KVQ_FMT_FP8_E5M2:
       if (c->bits != 8) return KVQ_ERR_UNSUPPORTED;
+      if (c->scale_per_head != 0 && c->scale_per_head != 1) return KVQ_ERR_UNSUPPORTED;
       break;
     default:
       if (c->bits != 16) return KVQ_ERR_UNSUPPORTED;
@@ -99,8 +106,7 @@ bool buffers_set(const kvq_cache* c) {
       if (x == nullptr || !aligned16(x)) return false;
     return true;
   }
-  if (c->cfg.format == KVQ_FMT_FP8_E4M3)
-    return c->tensor_scale != nullptr && aligned16(c->tensor_scale);
+  if (is_fp8(c->cfg.format)) return c->tensor_scale != nullptr && aligned16(c->tensor_scale);
   return true;
 }
 
@@ -124,7 +130,10 @@ kvq::VTileArgs v_tile_args(const kvq_cache* c, const Dims& d, const __half* v,
   a.v_dst = c->v_codes;
   a.NT = d.NT;
   a.bh_count = int(d.B * d.H);
-  a.fp8 = c->cfg.format == KVQ_FMT_FP8_E4M3 ? 1 : 0;
+  a.H = int(d.H);
+  a.fp8 = is_fp8(c->cfg.format) ? 1 : 0;
+  a.fmt = c->cfg.format == KVQ_FMT_FP8_E5M2 ? kvq::kE5M2 : kvq::kE4M3;
+  a.scale_stride = c->cfg.scale_per_head ? 4 : 0;
   a.zero_tail = zero_tail ? 1 : 0;
   a.tensor_scale = c->tensor_scale;
   return a;
@@ -203,8 +212,9 @@ kvq_status kvq_layout_query(const kvq_config* cfg, kvq_layout* out) {
       out->k_resid = out->v_resid = bh * d.Rcap * d.D * 2;
       break;
     case KVQ_FMT_FP8_E4M3:
+    case KVQ_FMT_FP8_E5M2:
       out->k_codes = out->v_codes = bh * d.CT * d.D;
-      out->tensor_scale = 4 * sizeof(float);
+      out->tensor_scale = size_t(fp8_scale_rows(*cfg)) * 4 * sizeof(float);
       break;
     default:
       out->k_codes = out->v_codes = bh * d.CT * d.D * 2;
@@ -291,7 +301,7 @@ kvq_status kvq_prefill_quantize(kvq_cache* cache, const void* k, const void* v,
     cache->n_resid = int32_t(nr);
     return KVQ_OK;
   }
-  if (cache->cfg.format == KVQ_FMT_FP8_E4M3) {
+  if (is_fp8(cache->cfg.format)) {
     kvq::Fp8QuantArgs fa{};
     fa.k_src = kh;
     fa.v_src = vh;
@@ -302,6 +312,9 @@ kvq_status kvq_prefill_quantize(kvq_cache* cache, const void* k, const void* v,
     fa.dst_bh_stride = d.CT * d.D;
     fa.dst_t0 = 0;
     fa.bh_count = bh;
+    fa.H = int(d.H);
+    fa.fmt = cache->cfg.format == KVQ_FMT_FP8_E5M2 ? kvq::kE5M2 : kvq::kE4M3;
+    fa.per_head = cache->cfg.scale_per_head;
     fa.tensor_scale = cache->tensor_scale;
     if (kvq::launch_fp8_prefill(fa, s) != hipSuccess) return KVQ_ERR_DEVICE;
     if (kvq::launch_v_tiles(v_tile_args(cache, d, vh, seq_len * d.D, seq_len, 0, true), s) !=
@@ -338,7 +351,7 @@ kvq_status kvq_append_token(kvq_cache* cache, const void* k_new, const void* v_n
   const Dims d = dims_of(cache->cfg);
   if (!state_ok(cache, d)) return KVQ_ERR_STATE;
   if (cache->n_quant + cache->n_resid >= d.C) return KVQ_ERR_CAPACITY;
-  if (cache->cfg.format == KVQ_FMT_FP8_E4M3 && cache->n_quant == 0) return KVQ_ERR_STATE;
+  if (is_fp8(cache->cfg.format) && cache->n_quant == 0) return KVQ_ERR_STATE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int bh = int(d.B * d.H);
   const __half* kh = static_cast<const __half*>(k_new);
@@ -382,7 +395,7 @@ kvq_status kvq_append_token(kvq_cache* cache, const void* k_new, const void* v_n
     cache->n_resid += 1;
     return KVQ_OK;
   }
-  if (cache->cfg.format == KVQ_FMT_FP8_E4M3) {
+  if (is_fp8(cache->cfg.format)) {
     kvq::Fp8QuantArgs fa{};
     fa.k_src = kh;
     fa.v_src = vh;
@@ -393,6 +406,9 @@ kvq_status kvq_append_token(kvq_cache* cache, const void* k_new, const void* v_n
     fa.dst_bh_stride = d.CT * d.D;
     fa.dst_t0 = cache->n_quant;
     fa.bh_count = bh;
+    fa.H = int(d.H);
+    fa.fmt = cache->cfg.format == KVQ_FMT_FP8_E5M2 ? kvq::kE5M2 : kvq::kE4M3;
+    fa.per_head = cache->cfg.scale_per_head;
     fa.tensor_scale = cache->tensor_scale;
     if (kvq::launch_fp8_append(fa, s) != hipSuccess) return KVQ_ERR_DEVICE;
     if (kvq::launch_v_tiles(v_tile_args(cache, d, vh, d.D, 1, cache->n_quant, false), s) !=
@@ -452,7 +468,9 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q, int32_t 
 
   kvq::DecodeArgs a{};
   a.src = kivi ? (d.bits == 2 ? kvq::kSrcKivi2 : kvq::kSrcKivi4)
-               : (cache->cfg.format == KVQ_FMT_FP8_E4M3 ? kvq::kSrcFp8 : kvq::kSrcFp16);
+       : cache->cfg.format == KVQ_FMT_FP8_E4M3 ? kvq::kSrcFp8
+       : cache->cfg.format == KVQ_FMT_FP8_E5M2 ? kvq::kSrcE5M2
+                                               : kvq::kSrcFp16;
   a.kbits = int(d.bits);
   a.vbits = int(d.vbits);
   a.B = int(d.B);
@@ -467,6 +485,7 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q, int32_t 
   a.v_scale = cache->v_scale;
   a.v_zero = cache->v_zero;
   a.tensor_scale = cache->tensor_scale;
+  a.scale_stride = is_fp8(cache->cfg.format) && cache->cfg.scale_per_head ? 4 : 0;
   a.NG = d.NG;
   a.NT = d.NT;
   a.gshift = d.G == 128 ? 2 : d.G == 64 ? 1 : 0;
@@ -500,7 +519,7 @@ int64_t kvq_decode_bytes(const kvq_cache* cache, int32_t num_q_heads) {
     const int64_t window = 2 * int64_t(cache->n_resid) * d.D * 2;
     return bh * (code_bytes + k_meta + v_meta + window);
   }
-  if (cache->cfg.format == KVQ_FMT_FP8_E4M3) return 2 * bh * nq * d.D + 2 * 4;
+  if (is_fp8(cache->cfg.format)) return 2 * bh * nq * d.D + 2 * 4 * fp8_scale_rows(cache->cfg);
   return 2 * bh * nq * d.D * 2;
 }
 

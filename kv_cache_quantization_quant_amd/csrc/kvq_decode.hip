@@ -81,6 +81,7 @@ hipError_t launch_decode(const DecodeArgs& a_in, hipStream_t s) {
       break;
     case kSrcFp16:
     case kSrcFp8:
+    case kSrcE5M2:
       e = launch_dense_mfma(a, s);
       break;
     default:

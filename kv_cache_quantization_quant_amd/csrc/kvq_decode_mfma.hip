@@ -860,14 +860,16 @@ __attribute__((amdgpu_waves_per_eu((BITS == 2 && VB == 2) ? KVQ_DECODE_WAVES_PER
 
 // ===================================================================== FP8 / FP16
 // Decode over the FP8 and FP16 caches ("大模型量化从0到1（十三）：KV Cache 量化", §二
-// and §十 FP8 formula: x̂ = e4m3_value(code) · s_tensor), same split-K
-// structure and online softmax as the KIVI kernel, 32-token tiles streamed
-// through an LDS ring. K rows [CT][D] and V tiles [D][32] enter the f16
-// matrix cores directly (FP8 codes through the exact E4M3 → fp16 scaled
-// conversion): scores A = K rows, B = q·log2(e)/√D (·s_K) as a constant fp16
-// high/low pair; values A = V tile rows, B = p as an fp16 high/low pair, so
-// p must stay below fp16's maximum: the reference maximum is raised when a
-// score exceeds it by 14 (p ≤ 2^14). s_V scales the output at the end.
+// and §十 FP8 formula: x̂ = fp8_value(code) · s, s per tensor or per KV head
+// as in §十八.6), same split-K structure and online softmax as the KIVI
+// kernel, 32-token tiles streamed through an LDS ring. K rows [CT][D] and V
+// tiles [D][32] enter the f16 matrix cores directly (E4M3 codes through the
+// exact E4M3 → fp16 scaled conversion; an E5M2 code is the high byte of the
+// fp16 of the same value, placed there by a byte permute): scores A = K rows,
+// B = q·log2(e)/√D (·s_K) as a constant fp16 high/low pair; values A = V tile
+// rows, B = p as an fp16 high/low pair, so p must stay below fp16's maximum:
+// the reference maximum is raised when a score exceeds it by 14 (p ≤ 2^14).
+// s_V scales the output at the end.
 
 constexpr float kLazyDense = 14.0f;
 
@@ -912,6 +914,17 @@ __device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w, bool high) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// fp16 pair from two E5M2 bytes (half-word `high` of w), exact: each byte
+// becomes the high byte of its fp16 (selector 0x0C gives a zero byte)
+__device__ __forceinline__ uint32_t e5m2x2_to_f16x2(uint32_t w, bool high) {
+  return __builtin_amdgcn_perm(0u, w, high ? 0x030C020Cu : 0x010C000Cu);
+}
+
+template <int SRC>
+__device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t w, bool high) {
+  return SRC == kSrcE5M2 ? e5m2x2_to_f16x2(w, high) : e4m3x2_to_f16x2(w, high);
+}
+
 // fp16 high / low terms of four p values; part 0 ends with the high terms of
 // tile 0 (own) and tile 1 (partner's), part 1 with the low terms of tile 0
 // (partner's) and tile 1 (own).
@@ -930,8 +943,8 @@ __device__ __forceinline__ u32x4 p_operand_f16(const float (&pp)[4]) {
 
 template <int SRC>
 __device__ __forceinline__ void process_dense_tile(const uint8_t* st, WaveAcc& W, int n_in,
-                                                   const u32x4 (&bq)[4], int r, int u,
-                                                   bool low) {
+                                                   const u32x4 (&bq)[4], float smul, int r,
+                                                   int u, bool low) {
   using S = DenseStage<SRC>;
   // ---- scores
   f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
@@ -947,10 +960,10 @@ __device__ __forceinline__ void process_dense_tile(const uint8_t* st, WaveAcc& W
     } else {
       const uint2 x = *reinterpret_cast<const uint2*>(st + r * kHeadDim + 32 * sl + 8 * u);
       const uint2 y = *reinterpret_cast<const uint2*>(st + (16 + r) * kHeadDim + 32 * sl + 8 * u);
-      a0 = u32x4{e4m3x2_to_f16x2(x.x, false), e4m3x2_to_f16x2(x.x, true),
-                 e4m3x2_to_f16x2(x.y, false), e4m3x2_to_f16x2(x.y, true)};
-      a1 = u32x4{e4m3x2_to_f16x2(y.x, false), e4m3x2_to_f16x2(y.x, true),
-                 e4m3x2_to_f16x2(y.y, false), e4m3x2_to_f16x2(y.y, true)};
+      a0 = u32x4{fp8x2_to_f16x2<SRC>(x.x, false), fp8x2_to_f16x2<SRC>(x.x, true),
+                 fp8x2_to_f16x2<SRC>(x.y, false), fp8x2_to_f16x2<SRC>(x.y, true)};
+      a1 = u32x4{fp8x2_to_f16x2<SRC>(y.x, false), fp8x2_to_f16x2<SRC>(y.x, true),
+                 fp8x2_to_f16x2<SRC>(y.y, false), fp8x2_to_f16x2<SRC>(y.y, true)};
     }
     s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a0), as_f16x8(bq[sl]), s0, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a1), as_f16x8(bq[sl]), s1, 0, 0, 0);
@@ -958,9 +971,10 @@ __device__ __forceinline__ void process_dense_tile(const uint8_t* st, WaveAcc& W
   float sc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    // the cross-lane add runs in every lane; tokens past n_in are masked after
-    const float t0 = s0[i] + xor8(s0[i]);
-    const float t1 = s1[i] + xor8(s1[i]);
+    // the cross-lane add runs in every lane; tokens past n_in are masked after;
+    // smul (a power of two) undoes the normalisation of the score operand
+    const float t0 = (s0[i] + xor8(s0[i])) * smul;
+    const float t1 = (s1[i] + xor8(s1[i])) * smul;
     const int t = (low ? 16 : 0) + 4 * u + i;
     sc[i] = t < n_in ? (low ? t1 : t0) : -INFINITY;
   }
@@ -986,8 +1000,8 @@ __device__ __forceinline__ void process_dense_tile(const uint8_t* st, WaveAcc& W
       const uint8_t* row = vt + (16 * n + r) * kGroup;
       const uint32_t x = *reinterpret_cast<const uint32_t*>(row + 4 * u);
       const uint32_t y = *reinterpret_cast<const uint32_t*>(row + 16 + 4 * u);
-      av = u32x4{e4m3x2_to_f16x2(x, false), e4m3x2_to_f16x2(x, true),
-                 e4m3x2_to_f16x2(y, false), e4m3x2_to_f16x2(y, true)};
+      av = u32x4{fp8x2_to_f16x2<SRC>(x, false), fp8x2_to_f16x2<SRC>(x, true),
+                 fp8x2_to_f16x2<SRC>(y, false), fp8x2_to_f16x2<SRC>(y, true)};
     }
     W.cv[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(av), as_f16x8(bp), W.cv[n], 0, 0, 0);
   }
@@ -1012,14 +1026,25 @@ __global__ __launch_bounds__(kThreads) void dense_mfma_split_kernel(DecodeArgs a
   const int hs = r & 7;
   const bool low = r >= 8;
 
-  const float sk = SRC == kSrcFp8 ? a.tensor_scale[0] : 1.0f;
-  const float sv = SRC == kSrcFp8 ? a.tensor_scale[1] : 1.0f;
+  // FP8: the scale row of the tensor, or of this KV head
+  const float sk = SRC != kSrcFp16 ? a.tensor_scale[a.scale_stride * h_kv] : 1.0f;
+  const float sv = SRC != kSrcFp16 ? a.tensor_scale[a.scale_stride * h_kv + 1] : 1.0f;
   // B of the scores: q·log2e/√D (·s_K) as fp16 high (part 0) / low (part 1)
-  // terms, channel 32s + 8u + j in k-step s
+  // terms, channel 32s + 8u + j in k-step s. An FP8 scale can be small enough
+  // (amax / 57344 for E5M2, or a narrow head's scale) to push these terms
+  // into fp16's subnormal range, so for FP8 the factor log2e/√D·s_K = m·2^e
+  // enters B as its mantissa m ∈ [0.5, 1) and the scores are multiplied by
+  // 2^e afterwards (both steps exact).
+  float smul = 1.0f, qfac = a.qscale;
+  if (SRC != kSrcFp16) {
+    int e;
+    qfac = frexpf(a.qscale * sk, &e);
+    smul = ldexpf(1.0f, e);
+  }
   u32x4 bq[4];
   {
     const bool valid = hs < nh;
-    const float qs = valid ? a.qscale * sk : 0.0f;
+    const float qs = valid ? qfac : 0.0f;
     const float* qrow = a.q + (int64_t(b) * a.Hq + hq0 + (valid ? hs : 0)) * kHeadDim;
 #pragma unroll
     for (int sl = 0; sl < 4; ++sl) {
@@ -1068,7 +1093,7 @@ __global__ __launch_bounds__(kThreads) void dense_mfma_split_kernel(DecodeArgs a
     else wait_vmem<0>();
     const int64_t tile = g0 + wave + int64_t(kWaves) * i;
     const int n_in = int(min<int64_t>(kGroup, a.n_main - tile * kGroup));
-    process_dense_tile<SRC>(ring_w + (i % S::kDepth) * S::kBytes, W, n_in, bq, r, u, low);
+    process_dense_tile<SRC>(ring_w + (i % S::kDepth) * S::kBytes, W, n_in, bq, smul, r, u, low);
   }
 
   wave_epilogue_and_merge(a, W, &ring[0][0][0], sizeof(ring[0]), wave, lane, hs, u, low, tid,
@@ -1081,6 +1106,8 @@ hipError_t launch_dense_mfma(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(a.n_split, a.B * a.H, a.nq / a.heads_per_chunk);
   if (a.src == kSrcFp16) {
     dense_mfma_split_kernel<kSrcFp16><<<grid, kThreads, 0, s>>>(a);
+  } else if (a.src == kSrcE5M2) {
+    dense_mfma_split_kernel<kSrcE5M2><<<grid, kThreads, 0, s>>>(a);
   } else {
     dense_mfma_split_kernel<kSrcFp8><<<grid, kThreads, 0, s>>>(a);
   }

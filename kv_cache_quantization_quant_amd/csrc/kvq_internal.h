@@ -49,12 +49,16 @@ struct CopyTokensArgs {
   int bh_count;
 };
 
+// FP8 code formats (the cache's V tiles and K rows).
+enum Fp8Format : int { kE4M3 = 0, kE5M2 = 1 };
+
 // V of the FP8 / FP16 caches in tiles of kGroup tokens: tile g of (b, h) is
 // [D][kGroup] (one row of the tile's tokens per channel). Writes source tokens
 // [0, n_tokens) of each (b, h) block of an fp16 [B·H][src_tokens][D] tensor
-// to cache tokens [dst_t0, dst_t0 + n_tokens), as fp16 or as E4M3 codes with
-// the stored V scale (tensor_scale[1]). zero_tail: also zero the slots after
-// the last written token up to the end of its tile.
+// to cache tokens [dst_t0, dst_t0 + n_tokens), as fp16 or as FP8 codes with
+// the stored V scale of the block's KV head (tensor_scale[scale_stride·h + 1]).
+// zero_tail: also zero the slots after the last written token up to the end
+// of its tile.
 struct VTileArgs {
   const __half* v_src;
   int64_t src_bh_stride;  // elements
@@ -63,12 +67,15 @@ struct VTileArgs {
   void* v_dst;            // fp16 or uint8 [B·H][NT][D][kGroup]
   int64_t NT;             // tiles per (b, h)
   int bh_count;
-  int fp8;                // 0: fp16 copy, 1: E4M3 encode
+  int H;                  // KV heads (h = bh % H)
+  int fp8;                // 0: fp16 copy, 1: FP8 encode
+  int fmt;                // Fp8Format
+  int scale_stride;       // floats between KV heads' scale rows (0: per tensor)
   int zero_tail;
   const float* tensor_scale;
 };
 
-// FP8 E4M3 per-tensor quantization.
+// FP8 quantization, one scale pair per tensor or per KV head.
 struct Fp8QuantArgs {
   const __half* k_src;
   const __half* v_src;
@@ -79,10 +86,13 @@ struct Fp8QuantArgs {
   int64_t dst_bh_stride;  // elements (C·D)
   int64_t dst_t0;
   int bh_count;
-  float* tensor_scale;    // {s_K, s_V, amax_K, amax_V}
+  int H;                  // KV heads (h = bh % H)
+  int fmt;                // Fp8Format
+  int per_head;           // 1: row h of tensor_scale belongs to KV head h
+  float* tensor_scale;    // [per_head ? H : 1][4] {s_K, s_V, amax_K, amax_V}
 };
 
-enum SrcFormat : int { kSrcFp16 = 0, kSrcFp8 = 1, kSrcKivi2 = 2, kSrcKivi4 = 3 };
+enum SrcFormat : int { kSrcFp16 = 0, kSrcFp8 = 1, kSrcKivi2 = 2, kSrcKivi4 = 3, kSrcE5M2 = 4 };
 
 // Split-K decode attention. Grid: (n_split, B·H, head_chunks).
 struct DecodeArgs {
@@ -99,6 +109,7 @@ struct DecodeArgs {
   const float* v_scale;
   const float* v_zero;
   const float* tensor_scale;
+  int scale_stride;       // FP8: floats between KV heads' scale rows (0: per tensor)
   int64_t NG;             // KIVI group slots per (b, h)
   int64_t NT;             // 32-token tiles per (b, h) (KIVI V codes; FP8 / FP16 V tiles)
   int gshift;             // log2(G / 32): tile t uses the K scales of group t >> gshift

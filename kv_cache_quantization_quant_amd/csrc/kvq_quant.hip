@@ -1,18 +1,20 @@
 // kvq_quant.hip — cache-write kernels for gfx950: KIVI group quantization
 // (prefill and window flush), token copies into the FP16 window / FP16 cache,
-// and FP8 E4M3 per-tensor quantization.
+// and FP8 (E4M3 or E5M2) quantization with per-tensor or per-KV-head scales.
 //
 // KIVI ("4.4 KV Cache 量化：KIVI 2-bit 与 FP8 KV Cache", §2 and §3.2;
 // "大模型量化从0到1（十三）：KV Cache 量化", §九 and the affine formula of §十):
-// K gets one (scale, zero) per (group of 32 tokens, channel), V one per token.
+// K gets one (scale, zero) per (group of G tokens, channel), V one per token.
 // Quantizer, each op in fp32 and correctly rounded (no contraction; the
 // library is built with -ffp-contract=off):
 //   s = (max − min) / (2^b − 1), z = min,
 //   code = clamp(rint((x − min) / s), 0, 2^b − 1), code = 0 when s == 0.
 //
-// FP8 ("LLM推理加速KV Cache量化压缩实战方案", section 自定义KV Cache量化的实现路径):
-//   s = amax(|x|) / 448 per tensor; code = E4M3(clamp(x / s, ±448)) with the
-//   native gfx950 OCP conversion (round to nearest even).
+// FP8 ("LLM推理加速KV Cache量化压缩实战方案", section 自定义KV Cache量化的实现路径;
+// "大模型量化从0到1（十三）：KV Cache 量化", §十八.4 and §十八.6):
+//   s = amax(|x|) / FMAX per tensor or per KV head, FMAX = 448 (E4M3) or
+//   57344 (E5M2); code = fp8(clamp(x / s, ±FMAX)) with the native gfx950 OCP
+//   conversion (round to nearest even).
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -294,7 +296,7 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
 // thread): q = RN(x·rs) is within an ulp of x / s, the residual x − q·s is
 // exact in one fma, and RN(q + residual·rs) is the correctly rounded quotient
 // (Markstein's theorem for round-to-nearest; no overflow or underflow occurs
-// for fp16 x and a tensor scale amax / 448 ≥ 2⁻²⁴ / 448). The quotient takes
+// for fp16 x and a scale amax / FMAX ≥ 2⁻²⁴ / 57344). The quotient takes
 // the sign of x, which keeps −0 / s = −0 (the sum above would give +0).
 __device__ __forceinline__ float div_by_scale(float x, float s, float rs) {
   const float q = x * rs;
@@ -302,13 +304,26 @@ __device__ __forceinline__ float div_by_scale(float x, float s, float rs) {
   return __builtin_copysignf(fmaf(res, rs, q), x);
 }
 
+// Largest finite value of each FP8 format: E4M3 "fn" 1.75·2^8, E5M2 1.75·2^15.
+template <int FMT>
+constexpr float kFp8Max = FMT == kE5M2 ? 57344.0f : 448.0f;
+
+// Four codes: t = clamp(x / s, ±FMAX), then the hardware round-to-nearest-even
+// conversion (OCP E4M3 or E5M2), two per instruction.
+template <int FMT>
 __device__ __forceinline__ uint32_t fp8_encode4(const float* x, float s, float rs) {
-  // t = clamp(x / s, ±448), then the hardware RNE conversion, two per call.
+  constexpr float M = kFp8Max<FMT>;
   float t[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) t[e] = fminf(fmaxf(div_by_scale(x[e], s, rs), -448.0f), 448.0f);
-  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], w, true);
+  for (int e = 0; e < 4; ++e) t[e] = fminf(fmaxf(div_by_scale(x[e], s, rs), -M), M);
+  uint32_t w;
+  if (FMT == kE5M2) {
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(t[0], t[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(t[2], t[3], w, true);
+  } else {
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], w, true);
+  }
   return w;
 }
 
@@ -330,8 +345,9 @@ __global__ __launch_bounds__(kThreads) void copy_tokens_kernel(CopyTokensArgs a)
 
 // V of the FP8 / FP16 caches, one workgroup per (tile, b·h): the tile's
 // tokens are read token-major into LDS and written channel-major (a row of
-// the tile's kGroup tokens per channel), as fp16 or as E4M3 codes (the FP8
-// encoding of the row-major path: clamp to ±448, then RNE).
+// the tile's kGroup tokens per channel), as fp16 or as FP8 codes (the
+// encoding of the row-major path: clamp to ±FMAX, then RNE) with the V scale
+// of the block's KV head.
 __global__ __launch_bounds__(kThreads) void v_tile_kernel(VTileArgs a) {
   __shared__ float tile[kGroup][kHeadDim + 1];
   const int bh = blockIdx.y;
@@ -357,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void v_tile_kernel(VTileArgs a) {
   __syncthreads();
   // thread: channel d, tokens j0 + [0, 16)
   const int d = tid / 2, j0 = 16 * (tid % 2);
-  const float sv = a.fp8 ? a.tensor_scale[1] : 1.0f;
+  const float sv = a.fp8 ? a.tensor_scale[a.scale_stride * (bh % a.H) + 1] : 1.0f;
   float x[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
@@ -371,8 +387,13 @@ __global__ __launch_bounds__(kThreads) void v_tile_kernel(VTileArgs a) {
     uint32_t w[4] = {0u, 0u, 0u, 0u};
     if (sv != 0.0f) {
       const float rsv = 1.0f / sv;
+      if (a.fmt == kE5M2) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) w[q] = fp8_encode4(x + 4 * q, sv, rsv);
+        for (int q = 0; q < 4; ++q) w[q] = fp8_encode4<kE5M2>(x + 4 * q, sv, rsv);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = fp8_encode4<kE4M3>(x + 4 * q, sv, rsv);
+      }
     }
     if (full) {
       *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
@@ -403,17 +424,19 @@ __global__ __launch_bounds__(kThreads) void v_tile_kernel(VTileArgs a) {
 
 // ------------------------------------------------------------------- FP8 ---
 
-__global__ void fp8_clear_amax_kernel(float* ts) {
-  if (threadIdx.x == 0) {
-    ts[2] = 0.0f;
-    ts[3] = 0.0f;
+// zeroes the amax slots of `rows` scale rows
+__global__ void fp8_clear_amax_kernel(float* ts, int rows) {
+  for (int r = threadIdx.x; r < rows; r += blockDim.x) {
+    ts[4 * r + 2] = 0.0f;
+    ts[4 * r + 3] = 0.0f;
   }
 }
 
 // amax(|K|) and amax(|V|) over the source tokens: grid (blocks per (b, h),
 // B·H), each thread a running packed-fp16 max of |x| (exact: the maximum of
 // fp16 magnitudes is one of them); non-negative fp32 values order like their
-// bit patterns, so an unsigned atomic max combines the wavefronts.
+// bit patterns, so an unsigned atomic max combines the wavefronts into the
+// tensor's row, or the row of the block's KV head.
 __global__ __launch_bounds__(kThreads) void fp8_amax_kernel(Fp8QuantArgs a) {
   constexpr int kChunks = kHeadDim / 8;                 // uint4 per token
   const int64_t n = a.n_tokens * kChunks;               // consecutive uint4 per (b, h)
@@ -455,30 +478,33 @@ __global__ __launch_bounds__(kThreads) void fp8_amax_kernel(Fp8QuantArgs a) {
     fv = fmaxf(fv, __shfl_xor(fv, off));
   }
   if ((threadIdx.x & 63) == 0) {
-    atomicMax(reinterpret_cast<unsigned int*>(a.tensor_scale + 2), __float_as_uint(fk));
-    atomicMax(reinterpret_cast<unsigned int*>(a.tensor_scale + 3), __float_as_uint(fv));
+    float* row = a.tensor_scale + (a.per_head ? 4 * (int(blockIdx.y) % a.H) : 0);
+    atomicMax(reinterpret_cast<unsigned int*>(row + 2), __float_as_uint(fk));
+    atomicMax(reinterpret_cast<unsigned int*>(row + 3), __float_as_uint(fv));
   }
 }
 
 // Encodes n_tokens tokens per (b, h). FROM_AMAX: the prefill pass, scales come
-// from the amax slots and are stored; otherwise the stored scales are reused.
-template <bool FROM_AMAX>
+// from the amax slots and are stored (by the blocks of batch row 0, one per
+// scale row); otherwise the stored scales are reused.
+template <bool FROM_AMAX, int FMT>
 __global__ __launch_bounds__(kThreads) void fp8_encode_kernel(Fp8QuantArgs a) {
   constexpr int kChunks = kHeadDim / 8;
+  const int bh = blockIdx.y;
+  float* row = a.tensor_scale + (a.per_head ? 4 * (bh % a.H) : 0);
   float sk, sv;
   if (FROM_AMAX) {
-    sk = a.tensor_scale[2] / 448.0f;
-    sv = a.tensor_scale[3] / 448.0f;
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
-      a.tensor_scale[0] = sk;
-      a.tensor_scale[1] = sv;
+    sk = row[2] / kFp8Max<FMT>;
+    sv = row[3] / kFp8Max<FMT>;
+    if (blockIdx.x == 0 && bh < (a.per_head ? a.H : 1) && threadIdx.x == 0) {
+      row[0] = sk;
+      row[1] = sv;
     }
   } else {
-    sk = a.tensor_scale[0];
-    sv = a.tensor_scale[1];
+    sk = row[0];
+    sv = row[1];
   }
   const int64_t idx = int64_t(blockIdx.x) * kThreads + threadIdx.x;
-  const int bh = blockIdx.y;
   if (idx >= a.n_tokens * kChunks) return;
   const int64_t tok = idx / kChunks;
   const int c = int(idx % kChunks);
@@ -489,7 +515,7 @@ __global__ __launch_bounds__(kThreads) void fp8_encode_kernel(Fp8QuantArgs a) {
   uint2 ck = make_uint2(0u, 0u);
   if (sk != 0.0f) {
     const float rsk = 1.0f / sk;
-    ck = make_uint2(fp8_encode4(fk, sk, rsk), fp8_encode4(fk + 4, sk, rsk));
+    ck = make_uint2(fp8_encode4<FMT>(fk, sk, rsk), fp8_encode4<FMT>(fk + 4, sk, rsk));
   }
   *reinterpret_cast<uint2*>(a.k_codes + d) = ck;
   if (a.v_codes != nullptr) {
@@ -498,7 +524,7 @@ __global__ __launch_bounds__(kThreads) void fp8_encode_kernel(Fp8QuantArgs a) {
     uint2 cv = make_uint2(0u, 0u);
     if (sv != 0.0f) {
       const float rsv = 1.0f / sv;
-      cv = make_uint2(fp8_encode4(fv, sv, rsv), fp8_encode4(fv + 4, sv, rsv));
+      cv = make_uint2(fp8_encode4<FMT>(fv, sv, rsv), fp8_encode4<FMT>(fv + 4, sv, rsv));
     }
     *reinterpret_cast<uint2*>(a.v_codes + d) = cv;
   }
@@ -550,7 +576,7 @@ hipError_t launch_v_tiles(const VTileArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_fp8_prefill(const Fp8QuantArgs& a, hipStream_t s) {
-  fp8_clear_amax_kernel<<<1, 64, 0, s>>>(a.tensor_scale);
+  fp8_clear_amax_kernel<<<1, 64, 0, s>>>(a.tensor_scale, a.per_head ? a.H : 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // about 4096 workgroups in all, at most one per 256 chunks of a (b, h)
@@ -561,13 +587,15 @@ hipError_t launch_fp8_prefill(const Fp8QuantArgs& a, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid(unsigned((a.n_tokens * (kHeadDim / 8) + kThreads - 1) / kThreads), a.bh_count);
-  fp8_encode_kernel<true><<<grid, kThreads, 0, s>>>(a);
+  if (a.fmt == kE5M2) fp8_encode_kernel<true, kE5M2><<<grid, kThreads, 0, s>>>(a);
+  else fp8_encode_kernel<true, kE4M3><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_fp8_append(const Fp8QuantArgs& a, hipStream_t s) {
   dim3 grid(unsigned((a.n_tokens * (kHeadDim / 8) + kThreads - 1) / kThreads), a.bh_count);
-  fp8_encode_kernel<false><<<grid, kThreads, 0, s>>>(a);
+  if (a.fmt == kE5M2) fp8_encode_kernel<false, kE5M2><<<grid, kThreads, 0, s>>>(a);
+  else fp8_encode_kernel<false, kE4M3><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -53,9 +53,11 @@ def decode_bytes_kivi(batch: int, num_kv_heads: int, head_dim: int, bits: int,
 
 
 def decode_bytes_fp8(batch: int, num_kv_heads: int, head_dim: int,
-                     n_tokens: int) -> int:
-    """FP8: one byte per K and V element plus the two fp32 tensor scales."""
-    return 2 * batch * num_kv_heads * n_tokens * head_dim + 8
+                     n_tokens: int, per_head: bool = False) -> int:
+    """FP8: one byte per K and V element plus the fp32 K and V scales (one
+    pair per tensor, or per KV head)."""
+    return (2 * batch * num_kv_heads * n_tokens * head_dim
+            + 8 * (num_kv_heads if per_head else 1))
 
 
 def decode_bytes_fp16(batch: int, num_kv_heads: int, head_dim: int,

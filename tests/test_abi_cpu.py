@@ -60,7 +60,7 @@ def test_struct_sizes_match_header(tmp_path):
         assert int(got[st]) == ctypes.sizeof(cls), st
         for f in fields[st]:
             assert int(got[f"{st}.{f}"]) == getattr(cls, f).offset, (st, f)
-    assert int(got["abi"]) == kq.kvq_abi_version() == kq.ABI_VERSION == 2
+    assert int(got["abi"]) == kq.kvq_abi_version() == kq.ABI_VERSION == 3
 
 
 def test_status_strings():
@@ -105,6 +105,13 @@ def test_format_validation():
     cfg = kq.make_config("fp8")
     cfg.bits = 16
     assert kq.kvq_layout_query(cfg)[0] == kq.KVQ_ERR_UNSUPPORTED
+    for fmt in ("fp8", "fp8_e5m2"):
+        for per_head, expect in ((0, 0), (1, 0), (2, kq.KVQ_ERR_UNSUPPORTED),
+                                 (-1, kq.KVQ_ERR_UNSUPPORTED)):
+            cfg = kq.make_config(fmt, scale_per_head=per_head)
+            assert kq.kvq_layout_query(cfg)[0] == expect, (fmt, per_head)
+    cfg = kq.make_config("fp8_e5m2", bits=4)
+    assert kq.kvq_layout_query(cfg)[0] == kq.KVQ_ERR_UNSUPPORTED
     cfg = kq.make_config("fp16")
     cfg.format = 7
     assert kq.kvq_layout_query(cfg)[0] == kq.KVQ_ERR_INVALID_ARG
@@ -136,6 +143,20 @@ def test_fp8_fp16_layout():
     assert lay.v_codes == oc.v_codes.nbytes * 2 and lay.k_codes == oc.k_codes.nbytes * 2
 
 
+@pytest.mark.parametrize("fmt,oc_fmt", [("fp8", "e4m3"), ("fp8_e5m2", "e5m2")])
+@pytest.mark.parametrize("per_head", [0, 1])
+def test_fp8_variant_layout(fmt, oc_fmt, per_head):
+    """E5M2 uses the E4M3 layout; per-head scales take one 16-byte row per KV
+    head (the oracle's [H, 2] scales plus the two amax slots of each row)."""
+    B, H, C = 2, 5, 77
+    st, lay = kq.kvq_layout_query(kq.make_config(fmt, batch=B, num_kv_heads=H, capacity=C,
+                                                 scale_per_head=per_head))
+    assert st == 0
+    oc = ocache.Fp8Cache(B, H, 128, C, fmt=oc_fmt, per_head=bool(per_head))
+    assert lay.k_codes == oc.k_codes.nbytes and lay.v_codes == oc.v_codes.nbytes
+    assert lay.tensor_scale == 2 * oc.tensor_scale.nbytes == 16 * (H if per_head else 1)
+
+
 def _host_cache(cfg, n_quant=0, n_resid=0, fake_ptrs=True):
     c = kq.KvqCache()
     assert kq.kvq_cache_init(c, cfg) == 0
@@ -147,11 +168,14 @@ def _host_cache(cfg, n_quant=0, n_resid=0, fake_ptrs=True):
     return c
 
 
-@pytest.mark.parametrize("fmt,bits,vbits", [("kivi", 2, 0), ("kivi", 4, 0), ("kivi", 4, 2),
-                                            ("kivi", 2, 4), ("fp8", 8, 0), ("fp16", 16, 0)])
-def test_decode_bytes_match_oracle(fmt, bits, vbits):
+@pytest.mark.parametrize("fmt,bits,vbits,per_head", [
+    ("kivi", 2, 0, 0), ("kivi", 4, 0, 0), ("kivi", 4, 2, 0), ("kivi", 2, 4, 0),
+    ("fp8", 8, 0, 0), ("fp8", 8, 0, 1), ("fp8_e5m2", 8, 0, 0), ("fp8_e5m2", 8, 0, 1),
+    ("fp16", 16, 0, 0)])
+def test_decode_bytes_match_oracle(fmt, bits, vbits, per_head):
     B, H, C = 4, 8, 33024
-    cfg = kq.make_config(fmt, bits=bits, batch=B, num_kv_heads=H, capacity=C, v_bits=vbits)
+    cfg = kq.make_config(fmt, bits=bits, batch=B, num_kv_heads=H, capacity=C, v_bits=vbits,
+                         scale_per_head=per_head)
     for nq, nr in [(32640, 128), (32768, 1), (32896, 128), (0, 77)]:
         if fmt != "kivi":
             nq, nr = nq + nr, 0
@@ -159,8 +183,8 @@ def test_decode_bytes_match_oracle(fmt, bits, vbits):
         got = kq.kvq_decode_bytes(c, 64)
         if fmt == "kivi":
             ref = bytes_model.decode_bytes_kivi(B, H, 128, bits, 32, nq, nr, vbits or None)
-        elif fmt == "fp8":
-            ref = bytes_model.decode_bytes_fp8(B, H, 128, nq)
+        elif fmt.startswith("fp8"):
+            ref = bytes_model.decode_bytes_fp8(B, H, 128, nq, bool(per_head))
         else:
             ref = bytes_model.decode_bytes_fp16(B, H, 128, nq)
         assert got == ref

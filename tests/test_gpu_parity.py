@@ -279,18 +279,24 @@ def _all_finite_fp16(limit=None):
     return np.concatenate([allv, np.zeros(pad, np.float16)])
 
 
-@pytest.mark.parametrize("limit", [None, 448.0, 1.0, 0.01])
-def test_fp8_encoder_every_fp16_value(kq, limit):
-    """Every finite fp16 value (up to ±limit) through the FP8 prefill: tensor
-    scale and every code bit-exact with the oracle."""
+OC_FMT = {"fp8": "e4m3", "fp8_e5m2": "e5m2"}
+
+
+@pytest.mark.parametrize("fmt,limit", [("fp8", None), ("fp8", 448.0), ("fp8", 1.0),
+                                       ("fp8", 0.01), ("fp8_e5m2", None),
+                                       ("fp8_e5m2", 57344.0), ("fp8_e5m2", 1.0),
+                                       ("fp8_e5m2", 1e-3)])
+def test_fp8_encoder_every_fp16_value(kq, fmt, limit):
+    """Every finite fp16 value (up to ±limit) through the FP8 prefill (E4M3
+    and E5M2): tensor scale and every code bit-exact with the oracle."""
     kvals = _all_finite_fp16(limit)
     vvals = -kvals[::-1].copy()
     S = len(kvals) // D
     k = torch.from_numpy(kvals.reshape(1, 1, S, D)).cuda()
     v = torch.from_numpy(vvals.reshape(1, 1, S, D)).cuda()
-    dc = kq.DeviceCache(kq.make_config("fp8", capacity=S))
+    dc = kq.DeviceCache(kq.make_config(fmt, capacity=S))
     dc.prefill(k, v)
-    oc = ocache.Fp8Cache(1, 1, D, S)
+    oc = ocache.Fp8Cache(1, 1, D, S, fmt=OC_FMT[fmt])
     oc.prefill(_np(k), _np(v))
     torch.cuda.synchronize()
     ts = _np(dc.view("tensor_scale"))
@@ -300,10 +306,12 @@ def test_fp8_encoder_every_fp16_value(kq, limit):
     assert np.array_equal(_np(dc.view("v_codes")), oc.v_codes)
 
 
-def test_fp8_encoder_random_scales(kq):
+@pytest.mark.parametrize("fmt", ["fp8", "fp8_e5m2"])
+def test_fp8_encoder_random_scales(kq, fmt):
     """Tensor scales from 16 random magnitudes (amax from 2^-10 to 2^15), every
     value of the tensor drawn across [-amax, amax] so that quotients x / s
-    fall between all E4M3 grid points: codes bit-exact with the oracle."""
+    fall between all grid points of the format: codes bit-exact with the
+    oracle."""
     rng = np.random.default_rng(7)
     S = 512
     for i in range(16):
@@ -312,29 +320,31 @@ def test_fp8_encoder_random_scales(kq):
         v = (rng.uniform(-1, 1, size=(1, 1, S, D)) * float(amax)).astype(np.float16)
         k[0, 0, 3, 7] = amax
         v[0, 0, 5, 1] = -amax
-        dc = kq.DeviceCache(kq.make_config("fp8", capacity=S))
+        dc = kq.DeviceCache(kq.make_config(fmt, capacity=S))
         dc.prefill(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
-        oc = ocache.Fp8Cache(1, 1, D, S)
+        oc = ocache.Fp8Cache(1, 1, D, S, fmt=OC_FMT[fmt])
         oc.prefill(k, v)
         torch.cuda.synchronize()
         assert np.array_equal(_np(dc.view("k_codes")), oc.k_codes), (i, float(amax))
         assert np.array_equal(_np(dc.view("v_codes")), oc.v_codes), (i, float(amax))
 
 
-def test_fp8_decode_values(kq):
-    """The in-kernel E4M3 decode: a cache holding all 254 finite codes (scale
-    1 from amax 448) attends with one-hot queries to recover values."""
-    t = ofp8.decode_table()
+@pytest.mark.parametrize("fmt", ["fp8", "fp8_e5m2"])
+def test_fp8_decode_values(kq, fmt):
+    """The in-kernel FP8 decode: a cache holding every finite code (254 E4M3,
+    248 E5M2; scale 1 from amax = the format's maximum) attends with a zero
+    query, so the output is the mean of the two V rows' decoded values."""
+    t = ofp8.decode_table(OC_FMT[fmt])
     finite = np.array([c for c in range(256) if np.isfinite(t[c])], np.uint8)
     vals = t[finite].astype(np.float16)                 # all exact in fp16
     S = 2
     kv = np.zeros((1, 1, S, D), np.float16)
     kv.reshape(-1)[:len(vals)] = vals
     k = torch.from_numpy(kv).cuda()
-    dc = kq.DeviceCache(kq.make_config("fp8", capacity=S))
+    dc = kq.DeviceCache(kq.make_config(fmt, capacity=S))
     dc.prefill(k, k)
     assert _np(dc.view("tensor_scale"))[0] == np.float32(1.0)
-    oc = ocache.Fp8Cache(1, 1, D, S)
+    oc = ocache.Fp8Cache(1, 1, D, S, fmt=OC_FMT[fmt])
     oc.prefill(kv, kv)
     assert np.array_equal(_np(dc.view("k_codes")), oc.k_codes)
     q = torch.zeros(1, 1, D, device="cuda")
@@ -343,13 +353,25 @@ def test_fp8_decode_values(kq):
     assert _att_err(_np(out), ref) <= 1e-6
 
 
-@pytest.mark.parametrize("B,H,Hq,S,steps", [(2, 2, 8, 700, 40), (1, 3, 3, 33, 5)])
-def test_fp8_prefill_append_decode(kq, B, H, Hq, S, steps):
+@pytest.mark.parametrize("fmt,per_head,B,H,Hq,S,steps", [
+    ("fp8", 0, 2, 2, 8, 700, 40), ("fp8", 0, 1, 3, 3, 33, 5),
+    ("fp8", 1, 2, 3, 12, 300, 40),           # per-KV-head scales
+    ("fp8_e5m2", 0, 2, 2, 8, 700, 40), ("fp8_e5m2", 1, 1, 4, 16, 90, 40),
+])
+def test_fp8_prefill_append_decode(kq, fmt, per_head, B, H, Hq, S, steps):
+    """FP8 prefill, appends with the frozen scales, a decode after each:
+    codes and scales bit-exact, attention within the bound. Per-head cases
+    give one KV head's K and another's V a 16x narrower range than the rest
+    (so the shared scale would push them toward the subnormal codes)."""
     C = S + steps
     k, v = _kv(B, H, C)
     k[:, :, S + steps // 2] *= 8      # appended tokens beyond amax saturate
-    dc = kq.DeviceCache(kq.make_config("fp8", batch=B, num_kv_heads=H, capacity=C))
-    oc = ocache.Fp8Cache(B, H, D, C)
+    if per_head:
+        k[:, 1] /= 16
+        v[:, H - 1] /= 16
+    dc = kq.DeviceCache(kq.make_config(fmt, batch=B, num_kv_heads=H, capacity=C,
+                                       scale_per_head=per_head))
+    oc = ocache.Fp8Cache(B, H, D, C, fmt=OC_FMT[fmt], per_head=bool(per_head))
     dc.prefill(k[:, :, :S].contiguous(), v[:, :, :S].contiguous())
     oc.prefill(_np(k[:, :, :S]), _np(v[:, :, :S]))
     kn, vn = _np(k), _np(v)
@@ -362,19 +384,46 @@ def test_fp8_prefill_append_decode(kq, B, H, Hq, S, steps):
     torch.cuda.synchronize()
     assert np.array_equal(_np(dc.view("k_codes")), oc.k_codes)
     assert np.array_equal(_np(dc.view("v_codes")), oc.v_codes)
-    assert np.array_equal(_np(dc.view("tensor_scale"))[:2], oc.tensor_scale)
-    _say(f"[fp8 stream] worst max abs err {worst:.3e}")
+    assert np.array_equal(_np(dc.view("tensor_scale"))[..., :2], oc.tensor_scale)
+    _say(f"[{fmt} stream, per_head={per_head}] worst max abs err {worst:.3e}")
     assert worst <= ATOL
 
 
-def test_fp8_all_zero_tensor(kq):
+@pytest.mark.parametrize("fmt,per_head", [("fp8", 0), ("fp8", 1), ("fp8_e5m2", 0),
+                                          ("fp8_e5m2", 1)])
+def test_fp8_all_zero_tensor(kq, fmt, per_head):
     k = torch.zeros(1, 2, 64, D, dtype=torch.float16, device="cuda")
-    dc = kq.DeviceCache(kq.make_config("fp8", num_kv_heads=2, capacity=64))
+    dc = kq.DeviceCache(kq.make_config(fmt, num_kv_heads=2, capacity=64,
+                                       scale_per_head=per_head))
     dc.prefill(k, k)
     assert not _np(dc.view("k_codes")).any()
-    assert np.all(_np(dc.view("tensor_scale"))[:2] == 0)
+    assert np.all(_np(dc.view("tensor_scale"))[..., :2] == 0)
     out = dc.decode(synth.make_q(1, 2, D, device="cuda"))
     assert np.all(_np(out) == 0)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp8_e5m2"])
+def test_fp8_per_head_zero_head(kq, fmt):
+    """Per-head scales with one all-zero KV head: that head's scales are 0 and
+    its codes 0, the other head is encoded with its own scale; attention of
+    both matches the oracle."""
+    B, H, Hq, S = 2, 2, 4, 100
+    k, v = _kv(B, H, S)
+    k[:, 0] = 0
+    v[:, 0] = 0
+    dc = kq.DeviceCache(kq.make_config(fmt, batch=B, num_kv_heads=H, capacity=S,
+                                       scale_per_head=1))
+    dc.prefill(k, v)
+    oc = ocache.Fp8Cache(B, H, D, S, fmt=OC_FMT[fmt], per_head=True)
+    oc.prefill(_np(k), _np(v))
+    torch.cuda.synchronize()
+    ts = _np(dc.view("tensor_scale"))
+    assert np.all(ts[0, :2] == 0) and np.all(ts[1, :2] > 0)
+    assert np.array_equal(ts[:, :2], oc.tensor_scale)
+    assert np.array_equal(_np(dc.view("k_codes")), oc.k_codes)
+    assert np.array_equal(_np(dc.view("v_codes")), oc.v_codes)
+    q = synth.make_q(B, Hq, D, device="cuda")
+    assert _att_err(_np(dc.decode(q)), oc.attention(_np(q))) <= ATOL
 
 
 @pytest.mark.parametrize("B,H,Hq,S", [(2, 4, 16, 1000), (1, 1, 2, 31)])
@@ -415,7 +464,7 @@ def test_fp16_prefill_append_decode(kq, B, H, Hq, S, steps):
     assert worst <= ATOL
 
 
-@pytest.mark.parametrize("fmt", ["fp16", "fp8"])
+@pytest.mark.parametrize("fmt", ["fp16", "fp8", "fp8_e5m2"])
 def test_dense_prefill_over_nan_memory(kq, fmt):
     """Cache memory filled with NaN bytes before a prefill of a partial tile:
     the slots after the last token are rewritten as zero and the masked tokens
@@ -426,7 +475,8 @@ def test_dense_prefill_over_nan_memory(kq, fmt):
     for name in ("k_codes", "v_codes"):
         dc.buffers[name].fill_(0xFF)
     dc.prefill(k, v)
-    oc = (ocache.Fp16Cache if fmt == "fp16" else ocache.Fp8Cache)(B, H, D, 70)
+    oc = (ocache.Fp16Cache(B, H, D, 70) if fmt == "fp16"
+          else ocache.Fp8Cache(B, H, D, 70, fmt=OC_FMT[fmt]))
     oc.prefill(_np(k), _np(v))
     q = synth.make_q(B, Hq, D, device="cuda")
     out = _np(dc.decode(q))
