@@ -220,8 +220,13 @@ class Fp8Cache:
         return (self._dequantize(self.k_codes[:, :, :n], 0),
                 self._dequantize(untile_rows(self.v_codes, n), 1))
 
-    def attention(self, q):
+    def attention(self, q, fp8_query=False):
+        """Decode attention over the dequantized cache; fp8_query: the query
+        itself goes through per-head E4M3 quantization first (attention in the
+        FP8 domain, [Tutorial] §十八.7)."""
         Kh, Vh = self.dequantized()
+        if fp8_query:
+            q = fp8.dequantize_query(*fp8.quantize_query(q))
         return attention.decode_attention(q, Kh, Vh)
 
 

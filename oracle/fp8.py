@@ -25,6 +25,13 @@ Encoding ([Tutorial] §十, FP8 formula q = cast_fp8(x / s)):
 Decoding: x̂ = float(value(code)) · s in fp32 ([Tutorial] §十: cast to high
 precision, multiply by s).
 
+Attention in the FP8 domain ([Tutorial] §十八.7; [KIVI-page] §6, the tip
+after §6.3): the query is quantized too, with one scale per query head
+(q_scale has num_heads entries, [Tutorial] §十八.6). Reading: no calibrated
+scale exists here, so each decode step takes the dynamic scale of its own
+query row, s_q[b, hq] = amax_d |q[b, hq, d]| / 448 in fp32, and the E4M3
+codes follow the encoder above; scores then use q̂ = value(code) · s_q.
+
 Parity pins live in tests/test_oracle_fp8.py; only tests, the package's smoke
 check and the benchmark's CPU baseline use this module.
 """
@@ -108,3 +115,22 @@ def quantize(x: np.ndarray, s: np.float32, fmt: str = "e4m3") -> np.ndarray:
 
 def dequantize(codes: np.ndarray, s: np.float32, fmt: str = "e4m3") -> np.ndarray:
     return decode(codes, fmt) * F32(s)
+
+
+def quantize_query(q: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """E4M3 codes and per-row scales of a [B, Hq, D] fp32 query: one scale
+    per (b, query head), amax over that head's D values / 448."""
+    q = np.asarray(q, dtype=F32)
+    B, Hq, _ = q.shape
+    scales = np.zeros((B, Hq), F32)
+    codes = np.zeros(q.shape, np.uint8)
+    for b in range(B):
+        for h in range(Hq):
+            scales[b, h] = tensor_scale(q[b, h])
+            codes[b, h] = quantize(q[b, h], scales[b, h])
+    return codes, scales
+
+
+def dequantize_query(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """q̂[b, hq, d] = value(code) · s_q[b, hq] in fp32."""
+    return decode(codes) * np.asarray(scales, F32)[..., None]

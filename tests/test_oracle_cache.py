@@ -251,3 +251,23 @@ def test_fp8_per_head_is_per_tensor_on_each_head(fmt):
         assert np.array_equal(c.k_codes[:, h], r.k_codes[:, 0])
         assert np.array_equal(c.v_codes[:, h], r.v_codes[:, 0])
     assert c.tensor_scale[1, 0] > 10 * c.tensor_scale[0, 0]
+
+
+def test_fp8_query_attention_reduces_to_exact_on_grid_queries():
+    """Attention in the FP8 domain: a query whose rows are E4M3 values at a
+    power-of-two scale (amax exactly 448 · 2^-3) is unchanged by the query
+    quantization, so the result equals the plain FP8-cache attention; a
+    general query moves the output by a small amount only."""
+    B, H, Hq, S = 1, 2, 4, 96
+    k, v = _kv(B, H, S)
+    c = cache.Fp8Cache(B, H, D, S)
+    c.prefill(k, v)
+    grid = fp8.decode_table()[:0x7F]
+    rng = np.random.default_rng(4)
+    q = grid[rng.integers(0, 0x7F, (B, Hq, D))].astype(np.float32)
+    q[..., 0] = 448.0
+    q *= np.float32(2.0 ** -3)
+    assert np.array_equal(c.attention(q, fp8_query=True), c.attention(q))
+    qn = rng.normal(0, 1, (B, Hq, D)).astype(np.float32)
+    d = np.abs(c.attention(qn, fp8_query=True) - c.attention(qn)).max()
+    assert 0 < d < 0.5

@@ -184,3 +184,32 @@ def test_head_scales(fmt):
         assert s[h] == F32(amax / fmax)
     assert s[2] == F32(F32(300.0) / fmax) and s[0] < s[2] / 50
     assert np.max(s) == fp8.tensor_scale(x, fmt)
+
+
+# ------------------------------------------------- FP8-domain query ---
+
+def test_query_quantization():
+    """Per-(b, query head) E4M3 query codes ([Tutorial] §十八.7): each row is
+    the per-tensor quantizer applied to that row alone; the row's largest
+    magnitude maps to ±448 (0x7E / 0xFE); a zero row has scale 0 and codes 0;
+    q̂ stays within E4M3's half step of q."""
+    rng = np.random.default_rng(9)
+    q = rng.normal(0, 1, (3, 4, 128)).astype(F32)
+    q[1, 2] *= 1000
+    q[2, 3] = 0
+    q[0, 1, 17] = -9.5                         # this row's amax, negative
+    codes, s = fp8.quantize_query(q)
+    assert s.shape == (3, 4) and codes.shape == q.shape
+    assert s[0, 1] == F32(F32(9.5) / F32(448)) and codes[0, 1, 17] == 0xFE
+    assert s[2, 3] == 0 and not codes[2, 3].any()
+    for b in range(3):
+        for h in range(4):
+            assert np.array_equal(codes[b, h], fp8.quantize(q[b, h], fp8.tensor_scale(q[b, h])))
+    qh = fp8.dequantize_query(codes, s)
+    assert np.all(np.abs(qh - q) <= np.abs(q) * 2.0 ** -4 + s[..., None] * 2.0 ** -10 + 1e-12)
+    # a row that is already on the E4M3 grid at a power-of-two scale is exact
+    g = fp8.decode_table()[np.arange(0, 0x7F, 1)][:128].astype(F32)
+    g[-1] = 448.0
+    row = (g * F32(0.25))[None, None, :]
+    c2, s2 = fp8.quantize_query(row)
+    assert s2[0, 0] == F32(0.25) and np.array_equal(fp8.dequantize_query(c2, s2), row)
