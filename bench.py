@@ -231,6 +231,7 @@ def run_extra(torch, kq, synth):
             dict(name="gqa70b_32k", fmt="kivi", kbits=2, vbits=4),
             dict(name="gqa_128k", fmt="fp16"), dict(name="gqa_128k", fmt="fp8"),
             dict(name="gqa_128k", fmt="fp8", per_head=1), dict(name="gqa_128k", fmt="fp8_e5m2"),
+            dict(name="gqa_128k", fmt="fp8", fp8_attention=1),
             dict(name="gqa_128k", fmt="kivi")]
     kv_cache = {}
     outs = {}                      # gqa_128k decode outputs, same K/V and q
@@ -238,6 +239,7 @@ def run_extra(torch, kq, synth):
         name, fmt = item["name"], item["fmt"]
         G, kbits, vbits = item.get("G", 32), item.get("kbits"), item.get("vbits")
         per_head = item.get("per_head", 0)
+        qf8 = item.get("fp8_attention", 0)
         c = synth.CONFIGS[name]
         B, H, Hq, S = c["batch"], c["num_kv_heads"], c["num_q_heads"], c["seq_len"]
         if name not in kv_cache:
@@ -249,7 +251,7 @@ def run_extra(torch, kq, synth):
         bits = (kbits or c["bits"]) if fmt == "kivi" else None
         dc = kq.DeviceCache(kq.make_config(fmt, bits=bits, group_size=G, batch=B,
                                            num_kv_heads=H, capacity=S, v_bits=vbits or 0,
-                                           scale_per_head=per_head))
+                                           scale_per_head=per_head, fp8_attention=qf8))
 
         def prefill():
             dc.reset()
@@ -261,11 +263,12 @@ def run_extra(torch, kq, synth):
         o = torch.empty_like(q)
         dec = statistics.median(time_launches(
             torch, lambda: dc.decode(q, out=o, workspace=ws), 10, scrub))
-        if name == "gqa_128k":
-            outs[fmt + ("_per_head" if per_head else "")] = o.double().cpu()
-        nbytes = dc.decode_bytes(Hq)
         key = (f"{name}/{fmt}" + (f"_g{G}" if G != 32 else "") +
-               (f"_k{kbits}v{vbits}" if vbits else "") + ("_per_head" if per_head else ""))
+               (f"_k{kbits}v{vbits}" if vbits else "") + ("_per_head" if per_head else "") +
+               ("_fp8_attention" if qf8 else ""))
+        if name == "gqa_128k":
+            outs[key.split("/")[1]] = o.double().cpu()
+        nbytes = dc.decode_bytes(Hq)
         out[key] = {
             "decode_us": round(dec, 2), "decode_bytes": nbytes,
             "decode_gbs": round(nbytes / (dec * 1e-6) / 1e9, 1),
@@ -278,7 +281,7 @@ def run_extra(torch, kq, synth):
     # accuracy side report: FP8 and KIVI attention against FP16 attention
     ref = outs["fp16"]
     acc = {}
-    for fmt in ("fp8", "fp8_per_head", "fp8_e5m2", "kivi"):
+    for fmt in ("fp8", "fp8_per_head", "fp8_e5m2", "fp8_fp8_attention", "kivi"):
         d = outs[fmt] - ref
         acc[fmt] = {"max_abs": float(d.abs().max()),
                     "rel_l2": float(d.norm() / ref.norm())}

@@ -49,8 +49,9 @@
  *   ≤ 65535; KIVI group_size ∈ {32, 64, 128} ([KIVI-page] §3.4 names 32
  *   and compares 64 and 128), bits ∈ {2, 4} and v_bits ∈ {0, 2, 4} (K and V
  *   bit widths), residual_length a multiple of group_size (0 allowed);
- *   FP8 (E4M3 or E5M2) bits = 8 and scale_per_head ∈ {0, 1}; FP16 bits =
- *   16; num_q_heads a positive multiple of num_kv_heads.
+ *   FP8 (E4M3 or E5M2) bits = 8, scale_per_head ∈ {0, 1} and fp8_attention
+ *   ∈ {0, 1}; FP16 bits = 16; num_q_heads a positive multiple of
+ *   num_kv_heads.
  *
  * ---------------------------------------------------------------------------
  * Numerics (bit-exact contract for KIVI codes, scales and zero-points)
@@ -126,7 +127,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 3
+#define KVQ_ABI_VERSION 4
 
 typedef enum {
   KVQ_OK = 0,
@@ -162,6 +163,11 @@ typedef struct {
                               mixed widths of [KIVI-page] §3.4); ignored else */
   int32_t scale_per_head;  /* FP8: 0 = one K and one V scale per tensor, 1 = one
                               pair per KV head ([Tutorial] §十八.6); ignored
+                              else                                            */
+  int32_t fp8_attention;   /* FP8: 1 = decode quantizes the query to E4M3 per
+                              query head (kvq_quantize_query_fp8) and takes
+                              the scores in the FP8 domain ([Tutorial]
+                              §十八.7); 0 = the query stays fp32; ignored
                               else                                            */
 } kvq_config;
 
@@ -236,6 +242,9 @@ size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t num_q_heads);
  * ([Tutorial] §二: softmax(q·Kᵀ/√D)·V over all n_quant + n_resid cached
  * tokens; no mask; GQA mapping as stated above). K and V of the grouped
  * region are dequantized inside the kernel; the window is read as fp16.
+ * FP8 caches with fp8_attention = 1 attend with q̂ = e4m3_value(code) · s_q,
+ * the codes and scales kvq_quantize_query_fp8 gives for q (computed inside
+ * the decode launch, not stored): attention in the FP8 domain.
  * q: device fp32 [B][Hq][D]; out: device fp32 [B][Hq][D] (written);
  * workspace: device, ≥ kvq_decode_workspace_bytes(&cache->cfg, Hq).
  * Errors: STATE on an empty cache, WORKSPACE if too small, UNSUPPORTED if
@@ -244,6 +253,22 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q,
                                 int32_t num_q_heads, float* out,
                                 void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/* Per-query-head E4M3 quantization of decode queries, the first step of
+ * attention in the FP8 domain ([Tutorial] §十八.7; [KIVI-page] §6): one scale
+ * per (b, query head) as q_scale has one entry per head ([Tutorial] §十八.6),
+ * taken from the current query row since no calibrated scale exists here:
+ *   s[b][hq]        = amax_d |q[b][hq][d]| / 448 (fp32, IEEE division);
+ *   codes[b][hq][d] = e4m3(min(max(q / s, −448), 448)), round to nearest
+ *                     even, the cache's encoder; s = 0 gives codes 0.
+ * q: device fp32 [batch][num_q_heads][head_dim], finite; codes: device uint8,
+ * same shape; scales: device fp32 [batch][num_q_heads]. q and codes 16-byte
+ * aligned, scales 4-byte aligned (else INVALID_ARG); batch, num_q_heads ≥ 1
+ * (else INVALID_ARG), head_dim = 128 and batch·num_q_heads ≤ 2^31 − 1 (else
+ * UNSUPPORTED). Caller-owned buffers; nothing is allocated. */
+kvq_status kvq_quantize_query_fp8(const float* q, int32_t batch, int32_t num_q_heads,
+                                  int32_t head_dim, uint8_t* codes, float* scales,
+                                  void* stream);
 
 /* Algorithmic bytes one decode step must read from the cache at its current
  * fill state: codes, scales and zero-points of the grouped region plus the

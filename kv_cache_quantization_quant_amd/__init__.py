@@ -28,7 +28,7 @@ KVQ_ERR_STATE = 4
 KVQ_ERR_DEVICE = 5
 KVQ_ERR_WORKSPACE = 6
 
-ABI_VERSION = 3        # KVQ_ABI_VERSION of include/kvq.h
+ABI_VERSION = 4        # KVQ_ABI_VERSION of include/kvq.h
 
 KVQ_FMT_FP16 = 0
 KVQ_FMT_FP8_E4M3 = 1
@@ -44,7 +44,7 @@ class KvqConfig(ctypes.Structure):
     _fields_ = [("format", c_int32), ("bits", c_int32), ("group_size", c_int32),
                 ("residual_length", c_int32), ("batch", c_int32),
                 ("num_kv_heads", c_int32), ("head_dim", c_int32), ("capacity", c_int32),
-                ("v_bits", c_int32), ("scale_per_head", c_int32)]
+                ("v_bits", c_int32), ("scale_per_head", c_int32), ("fp8_attention", c_int32)]
 
 
 class KvqLayout(ctypes.Structure):
@@ -86,6 +86,8 @@ def _load():
         "kvq_decode_attention": (c_int32, [POINTER(KvqCache), c_void_p, c_int32, c_void_p,
                                            c_void_p, c_size_t, c_void_p]),
         "kvq_decode_bytes": (c_int64, [POINTER(KvqCache), c_int32]),
+        "kvq_quantize_query_fp8": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p,
+                                             c_void_p, c_void_p]),
         "kvq_theoretical_bytes": (c_double, [c_int32, c_int32, c_int64, c_int32, c_int32,
                                              c_double]),
     }
@@ -104,7 +106,7 @@ lib = _load()
 ABI_SYMBOLS = ("kvq_abi_version", "kvq_status_str", "kvq_layout_query", "kvq_cache_init",
                "kvq_cache_reset", "kvq_prefill_quantize", "kvq_append_token",
                "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_bytes",
-               "kvq_theoretical_bytes")
+               "kvq_quantize_query_fp8", "kvq_theoretical_bytes")
 
 
 # ------------------------------------------------- one-to-one ABI wrappers ---
@@ -153,6 +155,12 @@ def kvq_decode_bytes(cache: KvqCache, num_q_heads: int) -> int:
     return lib.kvq_decode_bytes(byref(cache), num_q_heads)
 
 
+def kvq_quantize_query_fp8(q_ptr: int, batch: int, num_q_heads: int, head_dim: int,
+                           codes_ptr: int, scales_ptr: int, stream: int | None) -> int:
+    return lib.kvq_quantize_query_fp8(q_ptr, batch, num_q_heads, head_dim, codes_ptr,
+                                      scales_ptr, stream)
+
+
 def kvq_theoretical_bytes(num_layers, batch, seq_len, num_kv_heads, head_dim,
                           bytes_per_elem) -> float:
     return lib.kvq_theoretical_bytes(num_layers, batch, seq_len, num_kv_heads, head_dim,
@@ -162,13 +170,26 @@ def kvq_theoretical_bytes(num_layers, batch, seq_len, num_kv_heads, head_dim,
 def make_config(fmt: str = "kivi", bits: int | None = None, group_size: int = 32,
                 residual_length: int = 128, batch: int = 1, num_kv_heads: int = 1,
                 head_dim: int = 128, capacity: int = 256, v_bits: int = 0,
-                scale_per_head: int = 0) -> KvqConfig:
+                scale_per_head: int = 0, fp8_attention: int = 0) -> KvqConfig:
     """v_bits: KIVI V bit width (0 = same as bits); scale_per_head: FP8 scales
-    per KV head (1) or per tensor (0)."""
+    per KV head (1) or per tensor (0); fp8_attention: FP8 decode with the
+    query quantized to E4M3 (1)."""
     if bits is None:
         bits = {"kivi": 2, "fp8": 8, "fp8_e5m2": 8, "fp16": 16}[fmt]
     return KvqConfig(FORMATS[fmt], bits, group_size, residual_length, batch, num_kv_heads,
-                     head_dim, capacity, v_bits, scale_per_head)
+                     head_dim, capacity, v_bits, scale_per_head, fp8_attention)
+
+
+def quantize_query_fp8(q: torch.Tensor, stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """q: contiguous fp32 [B, Hq, D] on the device → (E4M3 codes uint8
+    [B, Hq, D], scales fp32 [B, Hq])."""
+    assert q.dtype == torch.float32 and q.is_contiguous() and q.dim() == 3
+    B, Hq, D = q.shape
+    codes = torch.empty(q.shape, dtype=torch.uint8, device=q.device)
+    scales = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check(kvq_quantize_query_fp8(q.data_ptr(), B, Hq, D, codes.data_ptr(), scales.data_ptr(),
+                                  _stream_handle(stream)), "kvq_quantize_query_fp8")
+    return codes, scales
 
 
 def _check(status: int, what: str):

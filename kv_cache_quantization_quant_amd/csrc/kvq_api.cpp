@@ -57,6 +57,7 @@ kvq_status validate_config(const kvq_config* c) {
     case KVQ_FMT_FP8_E5M2:
       if (c->bits != 8) return KVQ_ERR_UNSUPPORTED;
       if (c->scale_per_head != 0 && c->scale_per_head != 1) return KVQ_ERR_UNSUPPORTED;
+      if (c->fp8_attention != 0 && c->fp8_attention != 1) return KVQ_ERR_UNSUPPORTED;
       break;
     default:
       if (c->bits != 16) return KVQ_ERR_UNSUPPORTED;
@@ -486,6 +487,7 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q, int32_t 
   a.v_zero = cache->v_zero;
   a.tensor_scale = cache->tensor_scale;
   a.scale_stride = is_fp8(cache->cfg.format) && cache->cfg.scale_per_head ? 4 : 0;
+  a.qfp8 = is_fp8(cache->cfg.format) && cache->cfg.fp8_attention ? 1 : 0;
   a.NG = d.NG;
   a.NT = d.NT;
   a.gshift = d.G == 128 ? 2 : d.G == 64 ? 1 : 0;
@@ -503,6 +505,24 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q, int32_t 
   a.ws = static_cast<float*>(workspace);
   a.qscale = float(1.4426950408889634 / sqrt(double(kHeadDim)));
   return device_status(kvq::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_quantize_query_fp8(const float* q, int32_t batch, int32_t num_q_heads,
+                                  int32_t head_dim, uint8_t* codes, float* scales,
+                                  void* stream) {
+  if (q == nullptr || codes == nullptr || scales == nullptr) return KVQ_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(codes) || (reinterpret_cast<uintptr_t>(scales) & 3u) != 0)
+    return KVQ_ERR_INVALID_ARG;
+  if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0) return KVQ_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim) return KVQ_ERR_UNSUPPORTED;
+  const int64_t rows = int64_t(batch) * num_q_heads;
+  if (rows > 0x7FFFFFFF) return KVQ_ERR_UNSUPPORTED;
+  kvq::QueryQuantArgs qa{};
+  qa.q = q;
+  qa.codes = codes;
+  qa.scales = scales;
+  qa.rows = rows;
+  return device_status(kvq::launch_query_fp8(qa, static_cast<hipStream_t>(stream)));
 }
 
 int64_t kvq_decode_bytes(const kvq_cache* cache, int32_t num_q_heads) {

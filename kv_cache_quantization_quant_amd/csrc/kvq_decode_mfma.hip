@@ -51,6 +51,7 @@
 
 #include <math.h>
 
+#include "kvq_fp8.h"
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -870,6 +871,15 @@ __attribute__((amdgpu_waves_per_eu((BITS == 2 && VB == 2) ? KVQ_DECODE_WAVES_PER
 // rows, B = p as an fp16 high/low pair, so p must stay below fp16's maximum:
 // the reference maximum is raised when a score exceeds it by 14 (p ≤ 2^14).
 // s_V scales the output at the end.
+// In the FP8 domain (§十八.7) the query is quantized to E4M3 per head inside
+// the launch (the encoder of kvq_quantize_query_fp8) and B = the query codes'
+// values, exact in fp16 (no high/low split: both B columns of a head carry the
+// same values, so each lane's own column is the whole score); s_q·s_K·log2e/√D
+// scales the fp32 result. The fp8 × fp8 products go to the f16 matrix cores,
+// where they are exact and their fp32 sums keep full precision: the FP8
+// matrix cores sum each run of 8 products aligned to the largest and drop
+// bits about 12 binary places below it (measured), and the decode is
+// memory-bound, so they would cost accuracy for no time.
 
 constexpr float kLazyDense = 14.0f;
 
@@ -941,7 +951,7 @@ __device__ __forceinline__ u32x4 p_operand_f16(const float (&pp)[4]) {
   return u32x4{hp[0], hp[1], lp[0], lp[1]};
 }
 
-template <int SRC>
+template <int SRC, bool QF8>
 __device__ __forceinline__ void process_dense_tile(const uint8_t* st, WaveAcc& W, int n_in,
                                                    const u32x4 (&bq)[4], float smul, int r,
                                                    int u, bool low) {
@@ -972,9 +982,11 @@ __device__ __forceinline__ void process_dense_tile(const uint8_t* st, WaveAcc& W
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     // the cross-lane add runs in every lane; tokens past n_in are masked after;
-    // smul (a power of two) undoes the normalisation of the score operand
-    const float t0 = (s0[i] + xor8(s0[i])) * smul;
-    const float t1 = (s1[i] + xor8(s1[i])) * smul;
+    // smul undoes the normalisation of the score operand (a power of two), or
+    // applies s_q·s_K·log2e/√D in the FP8 domain, where columns r and r + 8
+    // both hold head hs: lane r (part 0) has tile 0's scores, lane r + 8 tile 1's
+    const float t0 = (QF8 ? s0[i] : s0[i] + xor8(s0[i])) * smul;
+    const float t1 = (QF8 ? s1[i] : s1[i] + xor8(s1[i])) * smul;
     const int t = (low ? 16 : 0) + 4 * u + i;
     sc[i] = t < n_in ? (low ? t1 : t0) : -INFINITY;
   }
@@ -1007,7 +1019,7 @@ __device__ __forceinline__ void process_dense_tile(const uint8_t* st, WaveAcc& W
   }
 }
 
-template <int SRC>
+template <int SRC, bool QF8>
 __global__ __launch_bounds__(kThreads) void dense_mfma_split_kernel(DecodeArgs a) {
   using S = DenseStage<SRC>;
   __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][S::kDepth][S::kBytes];
@@ -1042,7 +1054,46 @@ __global__ __launch_bounds__(kThreads) void dense_mfma_split_kernel(DecodeArgs a
     smul = ldexpf(1.0f, e);
   }
   u32x4 bq[4];
-  {
+  if constexpr (QF8) {
+    // the query row of head hs as E4M3 codes, channel 32s + 8u + j in k-step s
+    // (byte j); lanes r and r + 8 build the same operand
+    const bool valid = hs < nh;
+    const float* qrow = a.q + (int64_t(b) * a.Hq + hq0 + (valid ? hs : 0)) * kHeadDim;
+    float x[32];
+    float amax = 0.0f;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      const float4 x0 = *reinterpret_cast<const float4*>(qrow + 32 * sl + 8 * u);
+      const float4 x1 = *reinterpret_cast<const float4*>(qrow + 32 * sl + 8 * u + 4);
+      const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        x[8 * sl + j] = valid ? xs[j] : 0.0f;
+        amax = fmaxf(amax, fabsf(x[8 * sl + j]));
+      }
+    }
+    amax = max_x16_x32(amax);                    // the row's four lane groups u
+    const float sq = amax / kFp8Max<kE4M3>;
+    const float rs = sq != 0.0f ? 1.0f / sq : 0.0f;
+    const bool tiny = sq < kTinyQueryScale;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      uint32_t w[2] = {0u, 0u};
+      if (sq != 0.0f) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float* xx = x + 8 * sl + 4 * h;
+          w[h] = fp8_pack2<kE4M3>(query_quotient(xx[0], sq, rs, tiny),
+                                  query_quotient(xx[1], sq, rs, tiny), 0u, false);
+          w[h] = fp8_pack2<kE4M3>(query_quotient(xx[2], sq, rs, tiny),
+                                  query_quotient(xx[3], sq, rs, tiny), w[h], true);
+        }
+      }
+      bq[sl] = u32x4{e4m3x2_to_f16x2(w[0], false), e4m3x2_to_f16x2(w[0], true),
+                     e4m3x2_to_f16x2(w[1], false), e4m3x2_to_f16x2(w[1], true)};
+    }
+    smul = sq * sk * a.qscale;
+  } else {
     const bool valid = hs < nh;
     const float qs = valid ? qfac : 0.0f;
     const float* qrow = a.q + (int64_t(b) * a.Hq + hq0 + (valid ? hs : 0)) * kHeadDim;
@@ -1093,7 +1144,8 @@ __global__ __launch_bounds__(kThreads) void dense_mfma_split_kernel(DecodeArgs a
     else wait_vmem<0>();
     const int64_t tile = g0 + wave + int64_t(kWaves) * i;
     const int n_in = int(min<int64_t>(kGroup, a.n_main - tile * kGroup));
-    process_dense_tile<SRC>(ring_w + (i % S::kDepth) * S::kBytes, W, n_in, bq, smul, r, u, low);
+    process_dense_tile<SRC, QF8>(ring_w + (i % S::kDepth) * S::kBytes, W, n_in, bq, smul, r,
+                                 u, low);
   }
 
   wave_epilogue_and_merge(a, W, &ring[0][0][0], sizeof(ring[0]), wave, lane, hs, u, low, tid,
@@ -1105,11 +1157,13 @@ __global__ __launch_bounds__(kThreads) void dense_mfma_split_kernel(DecodeArgs a
 hipError_t launch_dense_mfma(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(a.n_split, a.B * a.H, a.nq / a.heads_per_chunk);
   if (a.src == kSrcFp16) {
-    dense_mfma_split_kernel<kSrcFp16><<<grid, kThreads, 0, s>>>(a);
+    dense_mfma_split_kernel<kSrcFp16, false><<<grid, kThreads, 0, s>>>(a);
   } else if (a.src == kSrcE5M2) {
-    dense_mfma_split_kernel<kSrcE5M2><<<grid, kThreads, 0, s>>>(a);
+    if (a.qfp8) dense_mfma_split_kernel<kSrcE5M2, true><<<grid, kThreads, 0, s>>>(a);
+    else dense_mfma_split_kernel<kSrcE5M2, false><<<grid, kThreads, 0, s>>>(a);
   } else {
-    dense_mfma_split_kernel<kSrcFp8><<<grid, kThreads, 0, s>>>(a);
+    if (a.qfp8) dense_mfma_split_kernel<kSrcFp8, true><<<grid, kThreads, 0, s>>>(a);
+    else dense_mfma_split_kernel<kSrcFp8, false><<<grid, kThreads, 0, s>>>(a);
   }
   return hipGetLastError();
 }

@@ -110,6 +110,7 @@ struct DecodeArgs {
   const float* v_zero;
   const float* tensor_scale;
   int scale_stride;       // FP8: floats between KV heads' scale rows (0: per tensor)
+  int qfp8;               // FP8: scores in the FP8 domain (query quantized to E4M3)
   int64_t NG;             // KIVI group slots per (b, h)
   int64_t NT;             // 32-token tiles per (b, h) (KIVI V codes; FP8 / FP16 V tiles)
   int gshift;             // log2(G / 32): tile t uses the K scales of group t >> gshift
@@ -136,6 +137,15 @@ hipError_t launch_copy_tokens(const CopyTokensArgs& a, hipStream_t s);
 hipError_t launch_v_tiles(const VTileArgs& a, hipStream_t s);
 hipError_t launch_fp8_prefill(const Fp8QuantArgs& a, hipStream_t s);
 hipError_t launch_fp8_append(const Fp8QuantArgs& a, hipStream_t s);
+// Per-row E4M3 quantization of fp32 query rows of D = 128 values.
+struct QueryQuantArgs {
+  const float* q;         // [rows][D]
+  uint8_t* codes;         // [rows][D]
+  float* scales;          // [rows]
+  int64_t rows;
+};
+
+hipError_t launch_query_fp8(const QueryQuantArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_dense_mfma(const DecodeArgs& a, hipStream_t s);

@@ -20,6 +20,7 @@
 
 #include <algorithm>
 
+#include "kvq_fp8.h"
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -292,41 +293,6 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
   }
 }
 
-// x / s correctly rounded, from rs = RN(1 / s) (one IEEE division per
-// thread): q = RN(x·rs) is within an ulp of x / s, the residual x − q·s is
-// exact in one fma, and RN(q + residual·rs) is the correctly rounded quotient
-// (Markstein's theorem for round-to-nearest; no overflow or underflow occurs
-// for fp16 x and a scale amax / FMAX ≥ 2⁻²⁴ / 57344). The quotient takes
-// the sign of x, which keeps −0 / s = −0 (the sum above would give +0).
-__device__ __forceinline__ float div_by_scale(float x, float s, float rs) {
-  const float q = x * rs;
-  const float res = fmaf(-q, s, x);
-  return __builtin_copysignf(fmaf(res, rs, q), x);
-}
-
-// Largest finite value of each FP8 format: E4M3 "fn" 1.75·2^8, E5M2 1.75·2^15.
-template <int FMT>
-constexpr float kFp8Max = FMT == kE5M2 ? 57344.0f : 448.0f;
-
-// Four codes: t = clamp(x / s, ±FMAX), then the hardware round-to-nearest-even
-// conversion (OCP E4M3 or E5M2), two per instruction.
-template <int FMT>
-__device__ __forceinline__ uint32_t fp8_encode4(const float* x, float s, float rs) {
-  constexpr float M = kFp8Max<FMT>;
-  float t[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) t[e] = fminf(fmaxf(div_by_scale(x[e], s, rs), -M), M);
-  uint32_t w;
-  if (FMT == kE5M2) {
-    w = __builtin_amdgcn_cvt_pk_bf8_f32(t[0], t[1], 0, false);
-    w = __builtin_amdgcn_cvt_pk_bf8_f32(t[2], t[3], w, true);
-  } else {
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], w, true);
-  }
-  return w;
-}
-
 // Copies n_tokens tokens of K and V (16 bytes per thread); V is skipped when
 // v_dst is null.
 __global__ __launch_bounds__(kThreads) void copy_tokens_kernel(CopyTokensArgs a) {
@@ -530,6 +496,28 @@ __global__ __launch_bounds__(kThreads) void fp8_encode_kernel(Fp8QuantArgs a) {
   }
 }
 
+// Query rows to E4M3 (attention in the FP8 domain): one wavefront per row of
+// D = 128 fp32 values, two per lane; s = amax / 448 from a wavefront max.
+__global__ __launch_bounds__(kThreads) void query_fp8_kernel(QueryQuantArgs a) {
+  const int64_t row = int64_t(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= a.rows) return;                 // whole wavefronts leave together
+  const float2 x = *reinterpret_cast<const float2*>(a.q + row * kHeadDim + 2 * lane);
+  float amax = fmaxf(fabsf(x.x), fabsf(x.y));
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const float s = amax / kFp8Max<kE4M3>;
+  uint32_t w = 0u;
+  if (s != 0.0f) {
+    const float rs = 1.0f / s;
+    const bool tiny = s < kTinyQueryScale;
+    w = fp8_pack2<kE4M3>(query_quotient(x.x, s, rs, tiny), query_quotient(x.y, s, rs, tiny),
+                         0u, false);
+  }
+  *reinterpret_cast<uint16_t*>(a.codes + row * kHeadDim + 2 * lane) = uint16_t(w & 0xFFFFu);
+  if (lane == 0) a.scales[row] = s;
+}
+
 }  // namespace
 
 // launches the (K bits, V bits, NS) instance of the quantize kernel when
@@ -589,6 +577,13 @@ hipError_t launch_fp8_prefill(const Fp8QuantArgs& a, hipStream_t s) {
   dim3 grid(unsigned((a.n_tokens * (kHeadDim / 8) + kThreads - 1) / kThreads), a.bh_count);
   if (a.fmt == kE5M2) fp8_encode_kernel<true, kE5M2><<<grid, kThreads, 0, s>>>(a);
   else fp8_encode_kernel<true, kE4M3><<<grid, kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_query_fp8(const QueryQuantArgs& a, hipStream_t s) {
+  if (a.rows <= 0) return hipSuccess;
+  constexpr int kRowsPerBlock = kThreads / 64;
+  query_fp8_kernel<<<unsigned((a.rows + kRowsPerBlock - 1) / kRowsPerBlock), kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -60,7 +60,7 @@ def test_struct_sizes_match_header(tmp_path):
         assert int(got[st]) == ctypes.sizeof(cls), st
         for f in fields[st]:
             assert int(got[f"{st}.{f}"]) == getattr(cls, f).offset, (st, f)
-    assert int(got["abi"]) == kq.kvq_abi_version() == kq.ABI_VERSION == 3
+    assert int(got["abi"]) == kq.kvq_abi_version() == kq.ABI_VERSION == 4
 
 
 def test_status_strings():
@@ -112,6 +112,24 @@ def test_format_validation():
             assert kq.kvq_layout_query(cfg)[0] == expect, (fmt, per_head)
     cfg = kq.make_config("fp8_e5m2", bits=4)
     assert kq.kvq_layout_query(cfg)[0] == kq.KVQ_ERR_UNSUPPORTED
+    for flag, expect in ((1, 0), (2, kq.KVQ_ERR_UNSUPPORTED)):
+        cfg = kq.make_config("fp8", fp8_attention=flag)
+        assert kq.kvq_layout_query(cfg)[0] == expect
+
+
+def test_quantize_query_validation():
+    """Argument checks of kvq_quantize_query_fp8 (all fail before any launch;
+    the pointers are never dereferenced)."""
+    P, C, S = 0x10000, 0x20000, 0x30000
+    f = kq.kvq_quantize_query_fp8
+    assert f(None, 1, 1, 128, C, S, None) == kq.KVQ_ERR_INVALID_ARG
+    assert f(P, 1, 1, 128, None, S, None) == kq.KVQ_ERR_INVALID_ARG
+    assert f(P, 1, 1, 128, C, None, None) == kq.KVQ_ERR_INVALID_ARG
+    assert f(P + 4, 1, 1, 128, C, S, None) == kq.KVQ_ERR_INVALID_ARG     # q misaligned
+    assert f(P, 1, 1, 128, C, S + 2, None) == kq.KVQ_ERR_INVALID_ARG     # scales misaligned
+    assert f(P, 0, 1, 128, C, S, None) == kq.KVQ_ERR_INVALID_ARG
+    assert f(P, 1, -3, 128, C, S, None) == kq.KVQ_ERR_INVALID_ARG
+    assert f(P, 1, 1, 64, C, S, None) == kq.KVQ_ERR_UNSUPPORTED
     cfg = kq.make_config("fp16")
     cfg.format = 7
     assert kq.kvq_layout_query(cfg)[0] == kq.KVQ_ERR_INVALID_ARG

@@ -426,6 +426,62 @@ def test_fp8_per_head_zero_head(kq, fmt):
     assert _att_err(_np(dc.decode(q)), oc.attention(_np(q))) <= ATOL
 
 
+def test_query_fp8_codes(kq):
+    """Per-query-head E4M3 query codes and scales ([Tutorial] §十八.7)
+    bit-exact with the oracle: normal rows, a zero row, rows ×1e6 and ×1e-33
+    (a scale below 2^-100, the exact-division path), rows of exact ties."""
+    B, Hq = 3, 16
+    q = synth.make_q(B, Hq, D, step=5, device="cuda")
+    q[0, 1] = 0
+    q[1, 2] *= 1e6
+    q[2, 3] *= 1e-33
+    # ties: an amax of 448 gives scale 1, and x.5-step values sit halfway
+    # between E4M3 neighbours
+    row = torch.linspace(-448, 448, D, device="cuda")
+    row[0] = 448.0
+    row[1:17] = torch.tensor([1.0625, 1.1875, 17.0, -9.0, 0.0029296875, -0.0029296875,
+                              208.0, -240.0, 0.5 + 2 ** -6, 3.25, 44.0, -52.0,
+                              2 ** -10, 3 * 2 ** -10, -448.0, 300.0], device="cuda")
+    q[2, 5] = row
+    codes, scales = kq.quantize_query_fp8(q)
+    torch.cuda.synchronize()
+    oc_codes, oc_scales = ofp8.quantize_query(_np(q))
+    assert np.array_equal(_np(scales).view(np.uint32), oc_scales.view(np.uint32))
+    assert np.array_equal(_np(codes), oc_codes)
+    assert _np(scales)[0, 1] == 0 and not _np(codes)[0, 1].any()
+
+
+@pytest.mark.parametrize("fmt,per_head,B,H,Hq,S,steps", [
+    ("fp8", 0, 2, 2, 8, 700, 40), ("fp8", 1, 1, 3, 12, 300, 20),
+    ("fp8_e5m2", 0, 2, 2, 16, 500, 20), ("fp8", 0, 1, 1, 2, 31, 3),
+])
+def test_fp8_attention_in_fp8_domain(kq, fmt, per_head, B, H, Hq, S, steps):
+    """Decode with the query quantized to E4M3 and the scores on the FP8
+    matrix cores (E4M3 × E4M3, or E5M2 K × E4M3 q): attention within the bound
+    of the oracle's attention over the dequantized query and cache."""
+    C = S + steps
+    k, v = _kv(B, H, C)
+    dc = kq.DeviceCache(kq.make_config(fmt, batch=B, num_kv_heads=H, capacity=C,
+                                       scale_per_head=per_head, fp8_attention=1))
+    oc = ocache.Fp8Cache(B, H, D, C, fmt=OC_FMT[fmt], per_head=bool(per_head))
+    dc.prefill(k[:, :, :S].contiguous(), v[:, :, :S].contiguous())
+    oc.prefill(_np(k[:, :, :S]), _np(v[:, :, :S]))
+    kn, vn = _np(k), _np(v)
+    worst, moved = 0.0, 0.0
+    for i in range(steps):
+        dc.append(k[:, :, S + i].contiguous(), v[:, :, S + i].contiguous())
+        oc.append(kn[:, :, S + i], vn[:, :, S + i])
+        if i % 5 == 4 or i == steps - 1:
+            q = synth.make_q(B, Hq, D, step=i, device="cuda")
+            got = _np(dc.decode(q))
+            worst = max(worst, _att_err(got, oc.attention(_np(q), fp8_query=True)))
+            moved = max(moved, _att_err(got, oc.attention(_np(q))))
+    _say(f"[{fmt} fp8-domain, per_head={per_head}] worst max abs err {worst:.3e} "
+         f"(vs the fp32-query attention: {moved:.3e})")
+    assert worst <= ATOL
+    assert moved > worst          # the query quantization is really in effect
+
+
 @pytest.mark.parametrize("B,H,Hq,S", [(2, 4, 16, 1000), (1, 1, 2, 31)])
 def test_fp16_decode(kq, B, H, Hq, S):
     k, v = _kv(B, H, S)
