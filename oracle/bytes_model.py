@@ -38,16 +38,19 @@ def metadata_overhead(group: int, bits: int, scale_bytes: float,
 
 
 def decode_bytes_kivi(batch: int, num_kv_heads: int, head_dim: int, bits: int,
-                      group: int, n_quant: int, n_resid: int, v_bits: int | None = None) -> int:
+                      group: int, n_quant: int, n_resid: int, v_bits: int | None = None,
+                      v_group_channels: int | None = None) -> int:
     """Bytes one KIVI decode step reads: per (b, h), K codes n_quant·D·b/8,
     K scale+zero (n_quant/G)·D·8, V codes n_quant·D·b_V/8 (b_V = b unless
-    given), V scale+zero n_quant·8, fp16 window 2·n_resid·D·2."""
+    given), V scale+zero n_quant·8 (times D/Gc with channel sub-groups of Gc),
+    fp16 window 2·n_resid·D·2."""
     assert n_quant % group == 0
     v_bits = bits if v_bits is None else v_bits
+    n_vs = 1 if v_group_channels is None else head_dim // v_group_channels
     per_pair = (n_quant * head_dim * bits // 8            # K codes
                 + (n_quant // group) * head_dim * 8       # K scale, zero
                 + n_quant * head_dim * v_bits // 8        # V codes
-                + n_quant * 8                             # V scale, zero
+                + n_quant * 8 * n_vs                      # V scale, zero
                 + 2 * n_resid * head_dim * 2)             # K, V window
     return batch * num_kv_heads * per_pair
 

@@ -42,12 +42,17 @@ VT = 32          # tokens per packed V tile (KIVI)
 
 class KiviCache:
     """bits: K's bit width; v_bits: V's (default: the same). Mixed widths
-    (e.g. K 4-bit, V 2-bit) quantize each tensor with its own 2^b − 1 levels."""
+    (e.g. K 4-bit, V 2-bit) quantize each tensor with its own 2^b − 1 levels.
+    v_group_channels: V scales and zero-points per run of that many channels
+    of a token (default: one per token); v_scale / v_zero are then
+    [B, H, CT, D / Gc]."""
 
     def __init__(self, batch, num_kv_heads, head_dim, bits, group, residual,
-                 capacity, v_bits=None):
+                 capacity, v_bits=None, v_group_channels=None):
         v_bits = bits if v_bits is None else v_bits
         assert bits in (2, 4) and v_bits in (2, 4)
+        assert v_group_channels is None or head_dim % v_group_channels == 0
+        self.Gc = v_group_channels
         assert residual % group == 0 and group % VT == 0
         self.B, self.H, self.D = batch, num_kv_heads, head_dim
         self.bits, self.G, self.R, self.C = bits, group, residual, capacity
@@ -61,8 +66,9 @@ class KiviCache:
         self.v_codes = np.zeros((B, H, self.NT, D, VT * v_bits // 32), np.uint32)
         self.k_scale = np.zeros((B, H, self.NG, D), np.float32)
         self.k_zero = np.zeros((B, H, self.NG, D), np.float32)
-        self.v_scale = np.zeros((B, H, self.CT), np.float32)
-        self.v_zero = np.zeros((B, H, self.CT), np.float32)
+        vshape = (B, H, self.CT) if self.Gc is None else (B, H, self.CT, D // self.Gc)
+        self.v_scale = np.zeros(vshape, np.float32)
+        self.v_zero = np.zeros(vshape, np.float32)
         self.k_resid = np.zeros((B, H, self.Rcap, D), np.float16)
         self.v_resid = np.zeros((B, H, self.Rcap, D), np.float16)
         self.n_quant = 0
@@ -82,7 +88,7 @@ class KiviCache:
         for b in range(self.B):
             for h in range(self.H):
                 kc, ks, kz = kivi.quantize_k(k[b, h], self.bits, self.G)
-                vc, vs, vz = kivi.quantize_v(v[b, h], self.v_bits)
+                vc, vs, vz = kivi.quantize_v(v[b, h], self.v_bits, self.Gc)
                 self.k_codes[b, h, t0:t0 + T] = kivi.pack_k(kc, self.bits)
                 self.k_scale[b, h, g0:g0 + T // self.G] = ks
                 self.k_zero[b, h, g0:g0 + T // self.G] = kz

@@ -5,7 +5,11 @@ Method ([KIVI-page] §2, §3.2, §3.4; [Tutorial] §九.1–九.3):
     tokens, aligned to multiples of G) share one scale and zero-point per
     channel.
   * V is quantized per token: each token has one scale and zero-point over its
-    head_dim channels.
+    head_dim channels, or, as a variant, one per run of Gc consecutive channels
+    of the token (channel sub-groups [Gc·m, Gc·m + Gc); reading: the
+    per-token axis of [Tutorial] §九.2 with the group granularity of
+    [Tutorial] §十.1 applied along the channels, as the q_group_size knob of
+    the quantized caches the pages describe does).
   * Codes have 2 or 4 bits.
 
 Quantizer ([Tutorial] §十, affine formula q = clamp(round(x/s) + z, qmin, qmax),
@@ -81,16 +85,26 @@ def quantize_k(k: np.ndarray, bits: int, group: int):
     return codes.reshape(T, D), s, mn.copy()
 
 
-def quantize_v(v: np.ndarray, bits: int):
+def quantize_v(v: np.ndarray, bits: int, channel_group: int | None = None):
     """Per-token quantization of V.
 
-    v: fp16 [T, D]. Returns codes uint8 [T, D], scale fp32 [T], zero fp32 [T].
+    v: fp16 [T, D]. Returns codes uint8 [T, D], scale fp32 [T], zero fp32 [T];
+    with channel_group = Gc, one scale and zero per (token, run of Gc
+    channels): scale, zero fp32 [T, D / Gc].
     """
     x = v.astype(F32)
-    mn = x.min(axis=1)                         # over the token's channels
-    mx = x.max(axis=1)
+    if channel_group is None:
+        mn = x.min(axis=1)                     # over the token's channels
+        mx = x.max(axis=1)
+        s = _scale(mn, mx, bits)
+        codes = _codes(x, mn[:, None], s[:, None], bits)
+        return codes, s, mn.copy()
+    T, D = x.shape
+    xs = x.reshape(T, D // channel_group, channel_group)
+    mn = xs.min(axis=2)                        # over each run of Gc channels
+    mx = xs.max(axis=2)
     s = _scale(mn, mx, bits)
-    codes = _codes(x, mn[:, None], s[:, None], bits)
+    codes = _codes(xs, mn[:, :, None], s[:, :, None], bits).reshape(T, D)
     return codes, s, mn.copy()
 
 
@@ -103,7 +117,13 @@ def dequantize_k(codes: np.ndarray, scale: np.ndarray, zero: np.ndarray,
 
 
 def dequantize_v(codes: np.ndarray, scale: np.ndarray, zero: np.ndarray) -> np.ndarray:
-    """x̂[t, d] = code[t, d] · s[t] + z[t] in fp32."""
+    """x̂[t, d] = code[t, d] · s[t] + z[t] in fp32 (s[t, d // Gc] and
+    z[t, d // Gc] with channel sub-groups)."""
+    if scale.ndim == 2:
+        gc = codes.shape[1] // scale.shape[1]
+        scale = np.repeat(scale, gc, axis=1)
+        zero = np.repeat(zero, gc, axis=1)
+        return codes.astype(F32) * scale + zero
     return codes.astype(F32) * scale[:, None] + zero[:, None]
 
 

@@ -91,15 +91,17 @@ def test_streaming_flush_schedule_32k():
     assert np.array_equal(c.k_resid, c2.k_resid) and np.array_equal(c.v_resid, c2.v_resid)
 
 
-@pytest.mark.parametrize("bits,G,R", [(2, 32, 64), (4, 32, 64), (2, 64, 64), (4, 128, 128),
-                                       (2, 64, 256)])
-def test_group_locality_ragged(bits, G, R):
+@pytest.mark.parametrize("bits,G,R,Gc", [(2, 32, 64, None), (4, 32, 64, None),
+                                          (2, 64, 64, None), (4, 128, 128, None),
+                                          (2, 64, 256, None), (2, 32, 128, 32),
+                                          (4, 64, 64, 32)])
+def test_group_locality_ragged(bits, G, R, Gc):
     k, v = _kv(2, 3, 600)
-    a = cache.KiviCache(2, 3, D, bits, G, R, 600)
+    a = cache.KiviCache(2, 3, D, bits, G, R, 600, v_group_channels=Gc)
     a.prefill(k[:, :, :100], v[:, :, :100])
     for t in range(100, 600):
         a.append(k[:, :, t], v[:, :, t])
-    b = cache.KiviCache(2, 3, D, bits, G, R, 600)
+    b = cache.KiviCache(2, 3, D, bits, G, R, 600, v_group_channels=Gc)
     b.prefill(k, v)
     n = min(a.n_quant, b.n_quant)
     assert n >= 600 - 2 * R - G and n % G == 0
@@ -271,3 +273,22 @@ def test_fp8_query_attention_reduces_to_exact_on_grid_queries():
     qn = rng.normal(0, 1, (B, Hq, D)).astype(np.float32)
     d = np.abs(c.attention(qn, fp8_query=True) - c.attention(qn)).max()
     assert 0 < d < 0.5
+
+
+def test_v_subgroup_cache_layout_and_reduction():
+    """V channel sub-groups in the cache: v_scale / v_zero gain a trailing
+    D/32 axis; with Gc = D the cache equals the per-token cache."""
+    k, v = _kv(1, 2, 200)
+    c = cache.KiviCache(1, 2, D, 2, 32, 64, 200, v_group_channels=32)
+    c.prefill(k, v)
+    assert c.v_scale.shape == (1, 2, 224, 4) and c.n_quant == 160
+    w = cache.KiviCache(1, 2, D, 2, 32, 64, 200, v_group_channels=D)
+    w.prefill(k, v)
+    p = cache.KiviCache(1, 2, D, 2, 32, 64, 200)
+    p.prefill(k, v)
+    assert np.array_equal(w.v_codes, p.v_codes) and np.array_equal(w.v_scale[..., 0], p.v_scale)
+    Kh, Vh = c.dequantized()
+    Kp, Vp = p.dequantized()
+    assert np.array_equal(Kh, Kp)
+    x = v[:, :, :160].astype(np.float32)
+    assert np.abs(Vh[:, :, :160] - x).max() <= np.abs(Vp[:, :, :160] - x).max()

@@ -237,3 +237,29 @@ def test_pack_round_trip(bits):
     codes = RNG.integers(0, 2 ** bits, (96, 128)).astype(np.uint8)
     assert np.array_equal(kivi.unpack_k(kivi.pack_k(codes, bits), bits, 128), codes)
     assert np.array_equal(kivi.unpack_v(kivi.pack_v(codes, bits, 32), bits, 32), codes)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_v_channel_subgroups(bits):
+    """V per token with one scale and zero per run of 32 channels: each run's
+    scale is (max − min)/(2^b − 1) of those 32 values alone (a run with a ×50
+    outlier does not widen its neighbours' steps); Gc = D reduces to plain
+    per-token V; reconstruction within half of the run's own step."""
+    rng = np.random.default_rng(21)
+    v = rng.normal(0, 1, (40, 128)).astype(np.float16)
+    v[:, 70] *= 50                                     # outlier channel in run 2
+    c_sub, s_sub, z_sub = kivi.quantize_v(v, bits, 32)
+    assert s_sub.shape == (40, 4) and z_sub.shape == (40, 4)
+    x = v.astype(np.float32)
+    for m in range(4):
+        run = x[:, 32 * m:32 * m + 32]
+        assert np.array_equal(z_sub[:, m], run.min(axis=1))
+        assert np.array_equal(s_sub[:, m], (run.max(axis=1) - run.min(axis=1)) / np.float32(2 ** bits - 1))
+    c_all, s_all, z_all = kivi.quantize_v(v, bits)
+    assert np.all(s_sub[:, [0, 1, 3]] < s_all[:, None])   # runs without the outlier: finer
+    c_one, s_one, z_one = kivi.quantize_v(v, bits, 128)
+    assert np.array_equal(c_one, c_all) and np.array_equal(s_one[:, 0], s_all)
+    xh = kivi.dequantize_v(c_sub, s_sub, z_sub)
+    step = np.repeat(s_sub, 32, axis=1)
+    assert np.all(np.abs(xh - x) <= step / 2 + 1e-6 * np.abs(x) + 1e-7)
+    assert np.abs(xh - x)[:, :64].max() < np.abs(kivi.dequantize_v(c_all, s_all, z_all) - x)[:, :64].max()
