@@ -229,6 +229,7 @@ def run_extra(torch, kq, synth):
             dict(name="gqa70b_32k", fmt="kivi", G=64), dict(name="gqa70b_32k", fmt="kivi", G=128),
             dict(name="gqa70b_32k", fmt="kivi", kbits=4, vbits=2),
             dict(name="gqa70b_32k", fmt="kivi", kbits=2, vbits=4),
+            dict(name="gqa70b_32k", fmt="kivi", v_group_channels=32),
             dict(name="gqa_128k", fmt="fp16"), dict(name="gqa_128k", fmt="fp8"),
             dict(name="gqa_128k", fmt="fp8", per_head=1), dict(name="gqa_128k", fmt="fp8_e5m2"),
             dict(name="gqa_128k", fmt="fp8", fp8_attention=1),
@@ -240,6 +241,7 @@ def run_extra(torch, kq, synth):
         G, kbits, vbits = item.get("G", 32), item.get("kbits"), item.get("vbits")
         per_head = item.get("per_head", 0)
         qf8 = item.get("fp8_attention", 0)
+        gc = item.get("v_group_channels", 0)
         c = synth.CONFIGS[name]
         B, H, Hq, S = c["batch"], c["num_kv_heads"], c["num_q_heads"], c["seq_len"]
         if name not in kv_cache:
@@ -251,7 +253,8 @@ def run_extra(torch, kq, synth):
         bits = (kbits or c["bits"]) if fmt == "kivi" else None
         dc = kq.DeviceCache(kq.make_config(fmt, bits=bits, group_size=G, batch=B,
                                            num_kv_heads=H, capacity=S, v_bits=vbits or 0,
-                                           scale_per_head=per_head, fp8_attention=qf8))
+                                           scale_per_head=per_head, fp8_attention=qf8,
+                                           v_group_channels=gc))
 
         def prefill():
             dc.reset()
@@ -265,7 +268,7 @@ def run_extra(torch, kq, synth):
             torch, lambda: dc.decode(q, out=o, workspace=ws), 10, scrub))
         key = (f"{name}/{fmt}" + (f"_g{G}" if G != 32 else "") +
                (f"_k{kbits}v{vbits}" if vbits else "") + ("_per_head" if per_head else "") +
-               ("_fp8_attention" if qf8 else ""))
+               ("_fp8_attention" if qf8 else "") + (f"_vgc{gc}" if gc else ""))
         if name == "gqa_128k":
             outs[key.split("/")[1]] = o.double().cpu()
         nbytes = dc.decode_bytes(Hq)

@@ -48,7 +48,8 @@
  * - Supported (else KVQ_ERR_UNSUPPORTED): head_dim = 128; batch · num_kv_heads
  *   ≤ 65535; KIVI group_size ∈ {32, 64, 128} ([KIVI-page] §3.4 names 32
  *   and compares 64 and 128), bits ∈ {2, 4} and v_bits ∈ {0, 2, 4} (K and V
- *   bit widths), residual_length a multiple of group_size (0 allowed);
+ *   bit widths), v_group_channels ∈ {0, 32}, residual_length a multiple of
+ *   group_size (0 allowed);
  *   FP8 (E4M3 or E5M2) bits = 8, scale_per_head ∈ {0, 1} and fp8_attention
  *   ∈ {0, 1}; FP16 bits = 16; num_q_heads a positive multiple of
  *   num_kv_heads.
@@ -68,7 +69,10 @@
  * KIVI granularity ([KIVI-page] §2 and §3.2, [Tutorial] §九.1–九.3):
  *   K — per channel: one (s, z) per (group of G tokens, channel); groups are
  *       aligned to token index multiples of G from position 0.
- *   V — per token: one (s, z) per token over its head_dim channels.
+ *   V — per token: one (s, z) per token over its head_dim channels; with
+ *       v_group_channels = 32, one (s, z) per token and run of 32 channels
+ *       [32m, 32m + 32) (the group granularity of [Tutorial] §十.1 along the
+ *       channels of a token).
  *
  * FP8 path ([FP8-page], [Tutorial] §十 FP8 formula, [KIVI-page] §5 for the
  * 1-4-3 layout, [Tutorial] §十八.4 for E5M2), FMAX = 448 (E4M3) or 57344
@@ -101,7 +105,8 @@
  *            fill the low half-word, odd the high). V is quantized per token,
  *            so the tile size does not depend on G.
  *   k_scale, k_zero  fp32 [B][H][NG][D]   (per group, per channel)
- *   v_scale, v_zero  fp32 [B][H][CT]      (per token)
+ *   v_scale, v_zero  fp32 [B][H][CT]      (per token), or [B][H][CT][D/32]
+ *            with v_group_channels = 32 (run m of token t at [t][m])
  *   k_resid, v_resid fp16 [B][H][Rcap][D] the FP16 residual window; slot i
  *            holds token n_quant + i.
  * FP8 and FP16 (baseline, no quantization) use tiles of T = 32 tokens,
@@ -127,7 +132,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 4
+#define KVQ_ABI_VERSION 5
 
 typedef enum {
   KVQ_OK = 0,
@@ -169,6 +174,9 @@ typedef struct {
                               the scores in the FP8 domain ([Tutorial]
                               §十八.7); 0 = the query stays fp32; ignored
                               else                                            */
+  int32_t v_group_channels; /* KIVI: 0 = one V scale / zero-point per token;
+                              32 = one per token and run of 32 channels
+                              (D/32 per token); ignored else                  */
 } kvq_config;
 
 /* Bytes the caller must allocate for each device buffer (0 = unused). */

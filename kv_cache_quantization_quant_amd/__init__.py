@@ -28,7 +28,7 @@ KVQ_ERR_STATE = 4
 KVQ_ERR_DEVICE = 5
 KVQ_ERR_WORKSPACE = 6
 
-ABI_VERSION = 4        # KVQ_ABI_VERSION of include/kvq.h
+ABI_VERSION = 5        # KVQ_ABI_VERSION of include/kvq.h
 
 KVQ_FMT_FP16 = 0
 KVQ_FMT_FP8_E4M3 = 1
@@ -44,7 +44,8 @@ class KvqConfig(ctypes.Structure):
     _fields_ = [("format", c_int32), ("bits", c_int32), ("group_size", c_int32),
                 ("residual_length", c_int32), ("batch", c_int32),
                 ("num_kv_heads", c_int32), ("head_dim", c_int32), ("capacity", c_int32),
-                ("v_bits", c_int32), ("scale_per_head", c_int32), ("fp8_attention", c_int32)]
+                ("v_bits", c_int32), ("scale_per_head", c_int32), ("fp8_attention", c_int32),
+                ("v_group_channels", c_int32)]
 
 
 class KvqLayout(ctypes.Structure):
@@ -170,14 +171,17 @@ def kvq_theoretical_bytes(num_layers, batch, seq_len, num_kv_heads, head_dim,
 def make_config(fmt: str = "kivi", bits: int | None = None, group_size: int = 32,
                 residual_length: int = 128, batch: int = 1, num_kv_heads: int = 1,
                 head_dim: int = 128, capacity: int = 256, v_bits: int = 0,
-                scale_per_head: int = 0, fp8_attention: int = 0) -> KvqConfig:
+                scale_per_head: int = 0, fp8_attention: int = 0,
+                v_group_channels: int = 0) -> KvqConfig:
     """v_bits: KIVI V bit width (0 = same as bits); scale_per_head: FP8 scales
     per KV head (1) or per tensor (0); fp8_attention: FP8 decode with the
-    query quantized to E4M3 (1)."""
+    query quantized to E4M3 (1); v_group_channels: KIVI V scales per run of
+    32 channels (32) or per token (0)."""
     if bits is None:
         bits = {"kivi": 2, "fp8": 8, "fp8_e5m2": 8, "fp16": 16}[fmt]
     return KvqConfig(FORMATS[fmt], bits, group_size, residual_length, batch, num_kv_heads,
-                     head_dim, capacity, v_bits, scale_per_head, fp8_attention)
+                     head_dim, capacity, v_bits, scale_per_head, fp8_attention,
+                     v_group_channels)
 
 
 def quantize_query_fp8(q: torch.Tensor, stream=None) -> tuple[torch.Tensor, torch.Tensor]:
@@ -288,12 +292,13 @@ class DeviceCache:
         if c.format == KVQ_FMT_KIVI:
             b = c.bits
             bv = c.v_bits if c.v_bits > 0 else c.bits
+            vsh = (B, H, CT) if c.v_group_channels == 0 else (B, H, CT, D // c.v_group_channels)
             shapes = {"k_codes": (torch.int32, (B, H, CT, D * b // 32)),
                       "v_codes": (torch.int32, (B, H, CT // 32, D, 32 * bv // 32)),
                       "k_scale": (torch.float32, (B, H, NG, D)),
                       "k_zero": (torch.float32, (B, H, NG, D)),
-                      "v_scale": (torch.float32, (B, H, CT)),
-                      "v_zero": (torch.float32, (B, H, CT)),
+                      "v_scale": (torch.float32, vsh),
+                      "v_zero": (torch.float32, vsh),
                       "k_resid": (torch.float16, (B, H, Rcap, D)),
                       "v_resid": (torch.float16, (B, H, Rcap, D))}
         elif c.format in FP8_FORMATS:

@@ -51,6 +51,7 @@ kvq_status validate_config(const kvq_config* c) {
         return KVQ_ERR_UNSUPPORTED;
       if (c->bits != 2 && c->bits != 4) return KVQ_ERR_UNSUPPORTED;
       if (c->v_bits != 0 && c->v_bits != 2 && c->v_bits != 4) return KVQ_ERR_UNSUPPORTED;
+      if (c->v_group_channels != 0 && c->v_group_channels != 32) return KVQ_ERR_UNSUPPORTED;
       if (c->residual_length % c->group_size != 0) return KVQ_ERR_UNSUPPORTED;
       break;
     case KVQ_FMT_FP8_E4M3:
@@ -74,7 +75,7 @@ kvq_status validate_config(const kvq_config* c) {
 // G: tokens per K scale group (KIVI), or the 32-token tile (FP8 / FP16);
 // NG = ⌈C/G⌉ group slots, CT = NG·G token slots, NT = CT/32 tiles of 32 tokens.
 struct Dims {
-  int64_t B, H, D, C, G, NG, CT, NT, Rcap, bits, vbits;
+  int64_t B, H, D, C, G, NG, CT, NT, Rcap, bits, vbits, nvs;
 };
 
 Dims dims_of(const kvq_config& c) {
@@ -90,6 +91,8 @@ Dims dims_of(const kvq_config& c) {
   d.Rcap = c.residual_length > 0 ? c.residual_length : d.G;
   d.bits = c.bits;
   d.vbits = (c.format == KVQ_FMT_KIVI && c.v_bits > 0) ? c.v_bits : c.bits;
+  d.nvs = (c.format == KVQ_FMT_KIVI && c.v_group_channels > 0) ? c.head_dim / c.v_group_channels
+                                                              : 1;
   return d;
 }
 
@@ -209,7 +212,7 @@ kvq_status kvq_layout_query(const kvq_config* cfg, kvq_layout* out) {
       out->k_codes = bh * d.CT * (d.D * d.bits / 32) * 4;
       out->v_codes = bh * d.NT * d.D * (kGroup * d.vbits / 32) * 4;
       out->k_scale = out->k_zero = bh * d.NG * d.D * 4;
-      out->v_scale = out->v_zero = bh * d.CT * 4;
+      out->v_scale = out->v_zero = bh * d.CT * d.nvs * 4;
       out->k_resid = out->v_resid = bh * d.Rcap * d.D * 2;
       break;
     case KVQ_FMT_FP8_E4M3:
@@ -278,6 +281,7 @@ kvq_status kvq_prefill_quantize(kvq_cache* cache, const void* k, const void* v,
     qa.NG = d.NG;
     qa.NT = d.NT;
     qa.group = int(d.G);
+    qa.nvs = int(d.nvs);
     qa.k_codes = static_cast<uint32_t*>(cache->k_codes);
     qa.v_codes = static_cast<uint32_t*>(cache->v_codes);
     qa.k_scale = cache->k_scale;
@@ -372,6 +376,7 @@ kvq_status kvq_append_token(kvq_cache* cache, const void* k_new, const void* v_n
       qa.NG = d.NG;
       qa.NT = d.NT;
       qa.group = int(d.G);
+      qa.nvs = int(d.nvs);
       qa.k_codes = static_cast<uint32_t*>(cache->k_codes);
       qa.v_codes = static_cast<uint32_t*>(cache->v_codes);
       qa.k_scale = cache->k_scale;
@@ -474,6 +479,7 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q, int32_t 
                                                : kvq::kSrcFp16;
   a.kbits = int(d.bits);
   a.vbits = int(d.vbits);
+  a.nvs = int(d.nvs);
   a.B = int(d.B);
   a.H = int(d.H);
   a.Hq = num_q_heads;
@@ -535,7 +541,7 @@ int64_t kvq_decode_bytes(const kvq_cache* cache, int32_t num_q_heads) {
   if (cache->cfg.format == KVQ_FMT_KIVI) {
     const int64_t code_bytes = nq * d.D * (d.bits + d.vbits) / 8;   // K and V codes
     const int64_t k_meta = (nq / d.G) * d.D * 2 * 4;        // fp32 s, z per channel
-    const int64_t v_meta = nq * 2 * 4;                      // fp32 s, z per token
+    const int64_t v_meta = nq * 2 * 4 * d.nvs;              // fp32 s, z per token (run)
     const int64_t window = 2 * int64_t(cache->n_resid) * d.D * 2;
     return bh * (code_bytes + k_meta + v_meta + window);
   }

@@ -81,17 +81,17 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// LDS stage of one 32-token tile (byte offsets), K codes at KB bits and V
-// codes at VB bits.
-template <int KB, int VB>
+// LDS stage of one 32-token tile (byte offsets), K codes at KB bits, V
+// codes at VB bits, NVS V scales (and zero-points) per token.
+template <int KB, int VB, int NVS = 1>
 struct Stage {
   static constexpr int kKBytes = kGroup * kHeadDim * KB / 8;   // K codes
   static constexpr int kVBytes = kGroup * kHeadDim * VB / 8;   // V codes
   static constexpr int kKc = 0;
   static constexpr int kVc = kKBytes;
   static constexpr int kKsz = kKBytes + kVBytes;         // 128 fp32 scales, 128 zero-points
-  static constexpr int kVsz = kKsz + 2 * kHeadDim * 4;   // 32 fp32 scales, 32 zero-points
-  static constexpr int kBytes = kVsz + 2 * kGroup * 4;
+  static constexpr int kVsz = kKsz + 2 * kHeadDim * 4;   // 32·NVS fp32 scales, zero-points
+  static constexpr int kBytes = kVsz + 2 * kGroup * 4 * NVS;
   static constexpr int kDepth = (KB == 2 && VB == 2) ? KVQ_RING_STAGES_2BIT : KVQ_RING_STAGES_4BIT;
   static_assert(kDepth >= 3 && kDepth <= 4, "one or two groups in flight ahead");
   static constexpr int kLoads = (kKBytes + kVBytes) / 1024 + 4;   // DMA instructions per tile
@@ -133,22 +133,22 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float head_sum(float x) { return sum_x16_x32(x + xor8(x)); }
 __device__ __forceinline__ float head_max(float x) { return max_x16_x32(fmaxf(x, xor8(x))); }
 
-// {f16(a0·b0), f16(a1·b1)}: fp32 products rounded once to fp16, packed.
-__device__ __forceinline__ uint32_t mix_pair(float a0, float b0, float a1, float b1) {
-  uint32_t d;
-  asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,0,0]" : "=v"(d) : "v"(a0), "v"(b0));
-  asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel_hi:[0,0,0]" : "+v"(d) : "v"(a1), "v"(b1));
-  return d;
+// VALU helpers are plain C or compiler builtins, never inline asm: a matrix
+// core instruction that reads a VGPR needs two wait states after the VALU
+// instruction that wrote it, and the compiler only inserts them for
+// instructions it emitted itself (an inline-asm v_bfi_b32 one slot before an
+// MFMA reading its result fed that MFMA a stale register).
+
+// {f16(x0), f16(x1)}, round to nearest even, packed
+__device__ __forceinline__ uint32_t pack_rn(float x0, float x1) {
+  return __builtin_bit_cast(uint32_t, __floats2half2_rn(x0, x1));
 }
-// {f16(a0·b0 − c.lo), f16(a1·b1 − c.hi)} with c an fp16 pair; each term is a
-// fused fp32 multiply-subtract rounded once to fp16.
-__device__ __forceinline__ uint32_t mix_pair_sub(float a0, float b0, float a1, float b1,
-                                                 uint32_t c) {
-  uint32_t d;
-  asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel_hi:[0,0,1]" : "=v"(d) : "v"(a0), "v"(b0), "v"(c));
-  asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
-      : "+v"(d) : "v"(a1), "v"(b1), "v"(c));
-  return d;
+// {f16(x0 − c.lo), f16(x1 − c.hi)} with c an fp16 pair that is 0 or the
+// pack_rn of (x0, x1): the fp32 difference is exact, so each term is rounded
+// once
+__device__ __forceinline__ uint32_t pack_rn_sub(float x0, float x1, uint32_t c) {
+  const __half2 h = __builtin_bit_cast(__half2, c);
+  return pack_rn(x0 - __low2float(h), x1 - __high2float(h));
 }
 // fp16 high and low terms of x0 and x1, packed: high = x rounded toward zero
 // to fp16 (in fp16's normal range that is x with its fp32 mantissa cut to 10
@@ -161,11 +161,9 @@ __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uin
   const float r1 = x1 - __uint_as_float(__float_as_uint(x1) & 0xFFFFE000u);
   lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
 }
-// (mask & x) | (~mask & y) in one instruction
+// (mask & x) | (~mask & y): one v_bfi_b32
 __device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t x, uint32_t y) {
-  uint32_t d;
-  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(d) : "v"(mask), "v"(x), "v"(y));
-  return d;
+  return (mask & x) | (~mask & y);
 }
 
 // ---- K code positions. The conversions turn one byte (two fp4 nibbles) or
@@ -228,25 +226,32 @@ __device__ __forceinline__ u32x4 k_operand(const uint32_t (&m)[2 * BITS], int sl
                fp8x2_to_f16x2(m1, true)};
 }
 
-// Per-lane state of one wavefront across its groups.
-struct WaveAcc {
-  float m_ref, l_acc, pz_acc;
+// Per-lane state of one wavefront across its groups; NVS V scales per token
+// (runs of 128 / NVS channels) keep one zero-point sum and one offset sum each.
+template <int NVS = 1>
+struct WaveAccT {
+  float m_ref, l_acc, pz_acc[NVS];
   f32x4 cv[8];
-  f32x4 cones;
+  f32x4 cones[NVS];
 };
+using WaveAcc = WaveAccT<1>;
 
 // Softmax step for four scores, then P'·V for one group or window tile.
-__device__ __forceinline__ void rescale_if_needed(WaveAcc& W, const float (&sc)[4],
+template <int NVS>
+__device__ __forceinline__ void rescale_if_needed(WaveAccT<NVS>& W, const float (&sc)[4],
                                                   float lazy = kLazy) {
   const float lmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
   if (__any(lmax > W.m_ref + lazy)) {            // wave-uniform, rare
     const float m_new = fmaxf(W.m_ref, head_max(lmax));
     const float alpha = fast_exp2(W.m_ref - m_new);
     W.l_acc *= alpha;
-    W.pz_acc *= alpha;
 #pragma unroll
     for (int n = 0; n < 8; ++n) W.cv[n] *= alpha;
-    W.cones *= alpha;
+#pragma unroll
+    for (int j = 0; j < NVS; ++j) {
+      W.pz_acc[j] *= alpha;
+      W.cones[j] *= alpha;
+    }
     W.m_ref = m_new;
   }
 }
@@ -254,16 +259,20 @@ __device__ __forceinline__ void rescale_if_needed(WaveAcc& W, const float (&sc)[
 // The same step for scores already taken relative to the reference maximum
 // (the score accumulator starts at −m_ref): the threshold is the constant
 // slack, and a raise by d shifts the reference and the four scores by d.
-__device__ __forceinline__ void rescale_rel(WaveAcc& W, float (&sc)[4]) {
+template <int NVS>
+__device__ __forceinline__ void rescale_rel(WaveAccT<NVS>& W, float (&sc)[4]) {
   const float lmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
   if (__any(lmax > kLazy)) {                     // wave-uniform, rare
     const float d = fmaxf(0.0f, head_max(lmax));
     const float alpha = fast_exp2(-d);
     W.l_acc *= alpha;
-    W.pz_acc *= alpha;
 #pragma unroll
     for (int n = 0; n < 8; ++n) W.cv[n] *= alpha;
-    W.cones *= alpha;
+#pragma unroll
+    for (int j = 0; j < NVS; ++j) {
+      W.pz_acc[j] *= alpha;
+      W.cones[j] *= alpha;
+    }
     W.m_ref += d;
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[i] -= d;
@@ -301,21 +310,24 @@ __device__ __forceinline__ u32x4 p_operand(const float (&pp)[4]) {
 
 // LDS data of one group for one lane: K codes of tokens r and 16 + r
 // (channels 32u..32u+31), K scale and zero-point of the lane's 16 channels,
-// V scale and zero-point of the tokens it keeps (16·part + 4u + i).
-template <int BITS>
+// V scale and zero-point of the tokens it keeps (16·part + 4u + i): vs[0]
+// holds the four tokens' scales (NVS = 1), or vs[i] token i's four run
+// scales (NVS = 4).
+template <int BITS, int NVS = 1>
 struct KLoad {
   uint32_t w0[BITS], w1[BITS];
   float4 ks[4], kz[4];
-  float4 vs, vz;
+  float4 vs[NVS], vz[NVS];
 };
 // V code words of channel 16n + r (n = 0..7) that lane group u needs
 struct VLoad {
   uint32_t w[8][2];
 };
 
-template <int BITS, int VB>
-__device__ __forceinline__ void load_k(const uint8_t* st, int r, int u, bool low, KLoad<BITS>& K) {
-  using S = Stage<BITS, VB>;
+template <int BITS, int VB, int NVS>
+__device__ __forceinline__ void load_k(const uint8_t* st, int r, int u, bool low,
+                                       KLoad<BITS, NVS>& K) {
+  using S = Stage<BITS, VB, NVS>;
   const uint8_t* kc = st + S::kKc;
   constexpr int kRow = kHeadDim * BITS / 8;
   if (BITS == 2) {
@@ -333,14 +345,24 @@ __device__ __forceinline__ void load_k(const uint8_t* st, int r, int u, bool low
   for (int c4 = 0; c4 < 4; ++c4) K.kz[c4] = ksz[kHeadDim / 4 + c4];
 #pragma unroll
   for (int c4 = 0; c4 < 4; ++c4) K.ks[c4] = ksz[c4];
-  const float4* vsz = reinterpret_cast<const float4*>(st + S::kVsz) + (low ? 4 : 0) + u;
-  K.vs = vsz[0];
-  K.vz = vsz[kGroup / 4];
+  if (NVS == 1) {
+    const float4* vsz = reinterpret_cast<const float4*>(st + S::kVsz) + (low ? 4 : 0) + u;
+    K.vs[0] = vsz[0];
+    K.vz[0] = vsz[kGroup / 4];
+  } else {
+    // token-major [32][NVS]: the lane's four tokens are NVS float4 each
+    const float4* vsz = reinterpret_cast<const float4*>(st + S::kVsz) + (low ? 16 : 0) + 4 * u;
+#pragma unroll
+    for (int i = 0; i < NVS; ++i) {
+      K.vs[i] = vsz[i];
+      K.vz[i] = vsz[kGroup * NVS / 4 + i];
+    }
+  }
 }
 
-template <int KB, int BITS>
+template <int KB, int BITS, int NVS>
 __device__ __forceinline__ void load_v(const uint8_t* st, int r, int u, VLoad& V) {
-  using S = Stage<KB, BITS>;
+  using S = Stage<KB, BITS, NVS>;
   const uint8_t* vc = st + S::kVc;
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
@@ -362,8 +384,8 @@ __device__ __forceinline__ float f4_at(const float4 (&v)[4], int i) {
 }
 
 // Scores of the four tokens this lane keeps (log2 units).
-template <int BITS>
-__device__ __forceinline__ void group_scores(const KLoad<BITS>& K, bool low,
+template <int BITS, int NVS>
+__device__ __forceinline__ void group_scores(const KLoad<BITS, NVS>& K, bool low,
                                              const float (&q16)[16], float m_part,
                                              float (&sc)[4]) {
   uint32_t m0[2 * BITS], m1[2 * BITS];
@@ -415,12 +437,17 @@ __device__ __forceinline__ void group_scores(const KLoad<BITS>& K, bool low,
   }
 }
 
-// Online-softmax step for the group's scores; returns the B operand P' of its
-// value products (p times the V scale). REL: the scores are relative to the
-// reference maximum already; otherwise (the first group of a wavefront) they
-// are absolute.
-template <int BITS, bool REL>
-__device__ __forceinline__ u32x4 group_probs(WaveAcc& W, float (&sc)[4], float4 vs, float4 vz) {
+// Online-softmax step for the group's scores; sets the B operands P' of its
+// value products (p times the V scale, one per run of V channels with its
+// own scale). REL: the scores are relative to the reference maximum already;
+// otherwise (the first group of a wavefront) they are absolute.
+__device__ __forceinline__ float f4c(float4 x, int c) {
+  return c == 0 ? x.x : c == 1 ? x.y : c == 2 ? x.z : x.w;
+}
+template <int BITS, bool REL, int NVS>
+__device__ __forceinline__ void group_probs(WaveAccT<NVS>& W, float (&sc)[4],
+                                            const float4 (&vs)[NVS], const float4 (&vz)[NVS],
+                                            u32x4 (&bp)[NVS]) {
   if (REL) {
     rescale_rel(W, sc);
   } else {
@@ -428,23 +455,44 @@ __device__ __forceinline__ u32x4 group_probs(WaveAcc& W, float (&sc)[4], float4 
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[i] -= W.m_ref;
   }
-  const float vsa[4] = {vs.x, vs.y, vs.z, vs.w};
-  const float vza[4] = {vz.x, vz.y, vz.z, vz.w};
-  float pp[4];
+  if constexpr (NVS == 1) {
+    const float vsa[4] = {vs[0].x, vs[0].y, vs[0].z, vs[0].w};
+    const float vza[4] = {vz[0].x, vz[0].y, vz[0].z, vz[0].w};
+    float pp[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float p = fast_exp2(sc[i]);
-    W.l_acc += p;
-    W.pz_acc = fmaf(p, vza[i], W.pz_acc);
-    pp[i] = p * vsa[i];
+    for (int i = 0; i < 4; ++i) {
+      const float p = fast_exp2(sc[i]);
+      W.l_acc += p;
+      W.pz_acc[0] = fmaf(p, vza[i], W.pz_acc[0]);
+      pp[i] = p * vsa[i];
+    }
+    bp[0] = p_operand(pp);
+  } else {
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = fast_exp2(sc[i]);
+      W.l_acc += p[i];
+    }
+#pragma unroll
+    for (int j = 0; j < NVS; ++j) {
+      // token i's scale of run j is component j of vs[i]
+      float pp[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        W.pz_acc[j] = fmaf(p[i], f4c(vz[i], j), W.pz_acc[j]);
+        pp[i] = p[i] * f4c(vs[i], j);
+      }
+      bp[j] = p_operand(pp);
+    }
   }
-  return p_operand(pp);
 }
 
 // P'·V of one group: 8 tiles of 16 channels, codes in the mantissa of 128.0
 // or 32.0, plus the offset-weighted column sums of P' that remove the offsets.
-template <int BITS>
-__device__ __forceinline__ void group_values(const VLoad& V, WaveAcc& W, u32x4 bp, uint32_t vsh,
+template <int BITS, int NVS>
+__device__ __forceinline__ void group_values(const VLoad& V, WaveAccT<NVS>& W,
+                                             const u32x4 (&bp)[NVS], uint32_t vsh,
                                              uint32_t vm0, uint32_t vm1, uint32_t magic,
                                              uint32_t magic32) {
 #pragma unroll
@@ -463,16 +511,20 @@ __device__ __forceinline__ void group_values(const VLoad& V, WaveAcc& W, u32x4 b
       d[2] = bfi(vm0, v1 >> vsh, magic);
       d[3] = bfi(vm0, v1 >> (vsh + 4), magic);
     }
+    // channels 16n..16n+15 lie in run n·NVS/8
     W.cv[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{d[0], d[1], d[2], d[3]}),
-                                                       as_bf16x8(bp), W.cv[n], 0, 0, 0);
+                                                       as_bf16x8(bp[n * NVS / 8]), W.cv[n], 0,
+                                                       0, 0);
   }
   // each k-slot's code offset over 128 (1, or 1/4 for the 2-bit codes in
   // bits 2..3, whose offset is 32): 128 times this product is what the codes
   // carry on top of their values
   const uint32_t o1 = BITS == 2 ? 0x3E803E80u : 0x3F803F80u;
   const u32x4 offs = u32x4{0x3F803F80u, o1, 0x3F803F80u, o1};
-  W.cones = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(offs), as_bf16x8(bp), W.cones,
-                                                    0, 0, 0);
+#pragma unroll
+  for (int j = 0; j < NVS; ++j)
+    W.cones[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(offs), as_bf16x8(bp[j]),
+                                                         W.cones[j], 0, 0, 0);
 }
 
 // One 32-token tile of the FP16 window ("4.4 KV Cache 量化：KIVI 2-bit 与 FP8
@@ -481,7 +533,8 @@ __device__ __forceinline__ void group_values(const VLoad& V, WaveAcc& W, u32x4 b
 // in k-step s). Values: V enters as two exact bf16 terms (fp16 has 11
 // significant bits, a bf16 pair holds 16), P' = p as a bf16 high/low pair.
 // Tokens past n_win are masked (score −∞, value 0).
-__device__ __forceinline__ void process_window_tile(const DecodeArgs& a, WaveAcc& W, int bh,
+template <int NVS>
+__device__ __forceinline__ void process_window_tile(const DecodeArgs& a, WaveAccT<NVS>& W, int bh,
                                                     int64_t tile, const u32x4 (&bqw)[4],
                                                     int r, int u, bool low) {
   const __half* kw = a.k_win + (int64_t(bh) * a.win_cap + tile * kGroup) * kHeadDim;
@@ -562,7 +615,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // high + low columns, times oscale; then the four wave states are merged
 // through LDS (each wave's results go to the start of its own ring region,
 // `wave_stride` bytes apart) into this split's partial (o[D], m, l).
-__device__ __forceinline__ void wave_epilogue_and_merge(const DecodeArgs& a, const WaveAcc& W,
+template <int NVS>
+__device__ __forceinline__ void wave_epilogue_and_merge(const DecodeArgs& a, const WaveAccT<NVS>& W,
                                                         uint8_t* ring, size_t wave_stride,
                                                         int wave, int lane, int hs, int u,
                                                         bool low, int tid, int b, int hq0,
@@ -570,13 +624,18 @@ __device__ __forceinline__ void wave_epilogue_and_merge(const DecodeArgs& a, con
   float* mo = reinterpret_cast<float*>(ring + wave * wave_stride);     // [8][kHeadDim]
   float* ml = mo + 8 * kHeadDim;                                         // [8][2]
   const float l_tot = head_sum(W.l_acc);
-  const float pz_tot = head_sum(W.pz_acc);
-  const float off = 128.0f * (W.cones[0] + xor8(W.cones[0]));
+  float pz_tot[NVS], off[NVS];     // zero-point sum and code offsets, per V run
+#pragma unroll
+  for (int j = 0; j < NVS; ++j) {
+    pz_tot[j] = head_sum(W.pz_acc[j]);
+    off[j] = 128.0f * (W.cones[j][0] + xor8(W.cones[j][0]));
+  }
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
     f32x4 o;
+    const int j = n * NVS / 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = (W.cv[n][i] + xor8(W.cv[n][i]) - off + pz_tot) * oscale;
+    for (int i = 0; i < 4; ++i) o[i] = (W.cv[n][i] + xor8(W.cv[n][i]) - off[j] + pz_tot[j]) * oscale;
     if (!low) *reinterpret_cast<f32x4*>(&mo[hs * kHeadDim + 16 * n + 4 * u]) = o;
   }
   if (lane < 8) {
@@ -626,11 +685,11 @@ struct GroupSrc {
 
 // Sources of 32-token tile g; its K scales and zero-points are those of
 // group g >> gshift (G = 32 << gshift tokens share them).
-template <int BITS, int VB>
+template <int BITS, int VB, int NVS>
 __device__ __forceinline__ GroupSrc group_src(const DecodeArgs& a, int bh, int64_t g) {
-  using S = Stage<BITS, VB>;
+  using S = Stage<BITS, VB, NVS>;
   const int64_t kg = (int64_t(bh) * a.NG + (g >> a.gshift)) * kHeadDim * 4;   // bytes
-  const int64_t vg = (int64_t(bh) * a.main_bh_tokens + g * kGroup) * 4;
+  const int64_t vg = (int64_t(bh) * a.main_bh_tokens + g * kGroup) * 4 * NVS;
   GroupSrc P;
   P.kc = static_cast<const uint8_t*>(a.k_main) +
          (int64_t(bh) * a.main_bh_tokens + g * kGroup) * (kHeadDim * BITS / 8) - S::kKc;
@@ -644,15 +703,15 @@ __device__ __forceinline__ GroupSrc group_src(const DecodeArgs& a, int bh, int64
 }
 // the same wavefront's next tile, kWaves tiles later (kWaves >> gshift K
 // scale groups later: kWaves·32 is a multiple of every G)
-template <int BITS, int VB>
+template <int BITS, int VB, int NVS>
 __device__ __forceinline__ void advance(GroupSrc& P, int gshift) {
-  using S = Stage<BITS, VB>;
+  using S = Stage<BITS, VB, NVS>;
   P.kc += int64_t(kWaves) * S::kKBytes;
   P.vc += int64_t(kWaves) * S::kVBytes;
   P.ks += int64_t(kWaves >> gshift) * kHeadDim * 4;
   P.kz += int64_t(kWaves >> gshift) * kHeadDim * 4;
-  P.vs += int64_t(kWaves) * kGroup * 4;
-  P.vz += int64_t(kWaves) * kGroup * 4;
+  P.vs += int64_t(kWaves) * kGroup * 4 * NVS;
+  P.vz += int64_t(kWaves) * kGroup * 4 * NVS;
 }
 
 // Copies of one group into stage st: K codes (block 1, M0 = st), then V
@@ -664,7 +723,13 @@ __device__ __forceinline__ void advance(GroupSrc& P, int gshift) {
 #define KVQ_COPY_K2 KVQ_COPY_K1 "global_load_lds_dwordx4 %3, %6 offset:1024 nt\n\t"
 #define KVQ_COPY_V1 "global_load_lds_dwordx4 %3, %7 offset:%13 nt\n\t"
 #define KVQ_COPY_V2 KVQ_COPY_V1 "global_load_lds_dwordx4 %3, %7 offset:%16 nt\n\t"
-#define KVQ_ISSUE_TILE(KCOPY, VCOPY)                                                          \
+// V scales and zero-points of a tile: 128 B each (one dword per lane), or
+// 512 B each with four scales per token (16 bytes per lane)
+#define KVQ_COPY_VS1 "global_load_lds_dword %5, %10 offset:%15 nt\n\t"
+#define KVQ_COPY_VZ1 "global_load_lds_dword %5, %12 offset:%15 nt\n\t"
+#define KVQ_COPY_VS4 "global_load_lds_dwordx4 %4, %10 offset:%15 nt\n\t"
+#define KVQ_COPY_VZ4 "global_load_lds_dwordx4 %4, %12 offset:%15 nt\n\t"
+#define KVQ_ISSUE_TILE(KCOPY, VCOPY, VSCOPY, VZCOPY)                                          \
   asm volatile("s_mov_b32 %0, m0\n\t"                                                         \
                "s_mov_b32 m0, %2\n\t"                                                         \
                "s_nop 0\n\t" KCOPY                                                            \
@@ -672,12 +737,10 @@ __device__ __forceinline__ void advance(GroupSrc& P, int gshift) {
                "s_nop 0\n\t" VCOPY                                                            \
                "s_mov_b64 %1, exec\n\t"                                                       \
                "s_mov_b32 exec_hi, 0\n\t"                                                     \
-               "global_load_lds_dwordx4 %4, %8 offset:%14 nt\n\t"                             \
-               "global_load_lds_dword %5, %10 offset:%15 nt\n\t"                              \
+               "global_load_lds_dwordx4 %4, %8 offset:%14 nt\n\t" VSCOPY                      \
                "s_mov_b64 exec, %1\n\t"                                                       \
                "s_mov_b32 exec_lo, 0\n\t"                                                     \
-               "global_load_lds_dwordx4 %4, %11 offset:%14 nt\n\t"                            \
-               "global_load_lds_dword %5, %12 offset:%15 nt\n\t"                              \
+               "global_load_lds_dwordx4 %4, %11 offset:%14 nt\n\t" VZCOPY                     \
                "s_mov_b64 exec, %1\n\t"                                                       \
                "s_mov_b32 m0, %0"                                                             \
                : "=&s"(m), "=&s"(e)                                                           \
@@ -687,37 +750,50 @@ __device__ __forceinline__ void advance(GroupSrc& P, int gshift) {
                  "i"(S::kVsz - S::kSecond), "i"(S::kVc - S::kSecond + 1024)                   \
                : "memory")
 
-template <int KB, int VB>
+template <int KB, int VB, int NVS>
 __device__ __forceinline__ void issue_group(uint8_t* st, const GroupSrc& P, uint32_t v16,
                                             uint32_t h16, uint32_t h4) {
-  using S = Stage<KB, VB>;
+  using S = Stage<KB, VB, NVS>;
   uint32_t m;
   uint64_t e;
-  if constexpr (KB == 2 && VB == 2) {
-    KVQ_ISSUE_TILE(KVQ_COPY_K1, KVQ_COPY_V1);
-  } else if constexpr (KB == 4 && VB == 4) {
-    KVQ_ISSUE_TILE(KVQ_COPY_K2, KVQ_COPY_V2);
-  } else if constexpr (KB == 4) {
-    KVQ_ISSUE_TILE(KVQ_COPY_K2, KVQ_COPY_V1);
+  if constexpr (NVS == 1) {
+    if constexpr (KB == 2 && VB == 2) {
+      KVQ_ISSUE_TILE(KVQ_COPY_K1, KVQ_COPY_V1, KVQ_COPY_VS1, KVQ_COPY_VZ1);
+    } else if constexpr (KB == 4 && VB == 4) {
+      KVQ_ISSUE_TILE(KVQ_COPY_K2, KVQ_COPY_V2, KVQ_COPY_VS1, KVQ_COPY_VZ1);
+    } else if constexpr (KB == 4) {
+      KVQ_ISSUE_TILE(KVQ_COPY_K2, KVQ_COPY_V1, KVQ_COPY_VS1, KVQ_COPY_VZ1);
+    } else {
+      KVQ_ISSUE_TILE(KVQ_COPY_K1, KVQ_COPY_V2, KVQ_COPY_VS1, KVQ_COPY_VZ1);
+    }
   } else {
-    KVQ_ISSUE_TILE(KVQ_COPY_K1, KVQ_COPY_V2);
+    static_assert(NVS == 4, "four V scales per token (runs of 32 channels)");
+    if constexpr (KB == 2 && VB == 2) {
+      KVQ_ISSUE_TILE(KVQ_COPY_K1, KVQ_COPY_V1, KVQ_COPY_VS4, KVQ_COPY_VZ4);
+    } else if constexpr (KB == 4 && VB == 4) {
+      KVQ_ISSUE_TILE(KVQ_COPY_K2, KVQ_COPY_V2, KVQ_COPY_VS4, KVQ_COPY_VZ4);
+    } else if constexpr (KB == 4) {
+      KVQ_ISSUE_TILE(KVQ_COPY_K2, KVQ_COPY_V1, KVQ_COPY_VS4, KVQ_COPY_VZ4);
+    } else {
+      KVQ_ISSUE_TILE(KVQ_COPY_K1, KVQ_COPY_V2, KVQ_COPY_VS4, KVQ_COPY_VZ4);
+    }
   }
 }
 
 // Wait until at most `ahead` groups' copies are in flight.
-template <int BITS, int VB>
+template <int BITS, int VB, int NVS>
 __device__ __forceinline__ void wait_groups(int ahead) {
-  using S = Stage<BITS, VB>;
+  using S = Stage<BITS, VB, NVS>;
   if (ahead >= 2) wait_vmem<2 * S::kLoads>();
   else if (ahead == 1) wait_vmem<S::kLoads>();
   else wait_vmem<0>();
 }
 
-template <int BITS, int VB>
+template <int BITS, int VB, int NVS>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu((BITS == 2 && VB == 2) ? KVQ_DECODE_WAVES_PER_SIMD : 2))) void kivi_mfma_split_kernel(
+__attribute__((amdgpu_waves_per_eu((BITS == 2 && VB == 2 && NVS == 1) ? KVQ_DECODE_WAVES_PER_SIMD : 2))) void kivi_mfma_split_kernel(
     DecodeArgs a) {
-  using S = Stage<BITS, VB>;
+  using S = Stage<BITS, VB, NVS>;
   __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][S::kDepth][S::kBytes];
 
   const int split = blockIdx.x;
@@ -735,18 +811,25 @@ __attribute__((amdgpu_waves_per_eu((BITS == 2 && VB == 2) ? KVQ_DECODE_WAVES_PER
   const bool low = r >= 8;
 
   const uint32_t vsh = (VB == 2) ? uint32_t(4 * u) : uint32_t(8 * (u % 2));
-  const uint32_t vm0 = (VB == 2) ? 0x00030003u : 0x000F000Fu;
-  const uint32_t vm1 = 0x000C000Cu;
-  const uint32_t magic = 0x43004300u;     // bf16 128.0: codes in bits 0..3 count 1
-  const uint32_t magic32 = 0x42004200u;   // bf16 32.0: codes in bits 2..3 count 1
+  uint32_t vm0 = (VB == 2) ? 0x00030003u : 0x000F000Fu;
+  uint32_t vm1 = 0x000C000Cu;
+  uint32_t magic = 0x43004300u;           // bf16 128.0: codes in bits 0..3 count 1
+  uint32_t magic32 = 0x42004200u;         // bf16 32.0: codes in bits 2..3 count 1
+  // registers the compiler cannot fold (an empty asm, no instruction): with
+  // the constants known it splits each bit insert into an and plus an or;
+  // with them opaque it selects one v_bfi_b32 and still tracks its hazards
+  asm("" : "+v"(vm0), "+v"(vm1), "+v"(magic), "+v"(magic32));
 
-  WaveAcc W;
+  WaveAccT<NVS> W;
   W.m_ref = -INFINITY;
   W.l_acc = 0.0f;
-  W.pz_acc = 0.0f;
 #pragma unroll
   for (int n = 0; n < 8; ++n) W.cv[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  W.cones = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < NVS; ++j) {
+    W.pz_acc[j] = 0.0f;
+    W.cones[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   if (split < a.n_split_main) {
     // q_d·log2e/√D of this lane's channels 32u + 16·part + c
@@ -776,58 +859,60 @@ __attribute__((amdgpu_waves_per_eu((BITS == 2 && VB == 2) ? KVQ_DECODE_WAVES_PER
     // group i - 2, whose value products ran in the previous iteration.
     constexpr int kAhead = S::kDepth - 2;
     const uint32_t v16 = 16u * lane, h16 = 16u * (lane & 31), h4 = 4u * (lane & 31);
-    GroupSrc P = group_src<BITS, VB>(a, bh, g0 + wave);
+    GroupSrc P = group_src<BITS, VB, NVS>(a, bh, g0 + wave);
     uint8_t* ring_w = &ring[wave][0][0];
 #pragma unroll
     for (int j = 0; j < kAhead; ++j) {
       if (j < n_mine) {
-        issue_group<BITS, VB>(ring_w + j * S::kBytes, P, v16, h16, h4);
-        advance<BITS, VB>(P, a.gshift);
+        issue_group<BITS, VB, NVS>(ring_w + j * S::kBytes, P, v16, h16, h4);
+        advance<BITS, VB, NVS>(P, a.gshift);
       }
     }
     if (n_mine > 0) {
       float sc[4];
       if (kAhead < n_mine) {
-        issue_group<BITS, VB>(ring_w + kAhead * S::kBytes, P, v16, h16, h4);
-        advance<BITS, VB>(P, a.gshift);
+        issue_group<BITS, VB, NVS>(ring_w + kAhead * S::kBytes, P, v16, h16, h4);
+        advance<BITS, VB, NVS>(P, a.gshift);
         wait_vmem<kAhead * S::kLoads>();
       } else {
-        wait_groups<BITS, VB>(n_mine - 1);
+        wait_groups<BITS, VB, NVS>(n_mine - 1);
       }
-      KLoad<BITS> K;
+      KLoad<BITS, NVS> K;
       VLoad V;
-      load_k<BITS, VB>(ring_w, r, u, low, K);
-      group_scores<BITS>(K, low, q16, 0.0f, sc);
-      u32x4 bp_prev = group_probs<BITS, false>(W, sc, K.vs, K.vz);
+      load_k<BITS, VB, NVS>(ring_w, r, u, low, K);
+      group_scores<BITS, NVS>(K, low, q16, 0.0f, sc);
+      u32x4 bp_prev[NVS];
+      group_probs<BITS, false, NVS>(W, sc, K.vs, K.vz, bp_prev);
       int i = 1;
       // steady state: a group is loaded every iteration, one fixed wait
       for (; i + kAhead < n_mine; ++i) {
         // the refilled stage was last read two groups ago; its reads are done
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        issue_group<BITS, VB>(ring_w + ((i + kAhead) % S::kDepth) * S::kBytes, P, v16, h16, h4);
-        advance<BITS, VB>(P, a.gshift);
+        issue_group<BITS, VB, NVS>(ring_w + ((i + kAhead) % S::kDepth) * S::kBytes, P, v16, h16,
+                                   h4);
+        advance<BITS, VB, NVS>(P, a.gshift);
         wait_vmem<kAhead * S::kLoads>();
-        load_v<BITS, VB>(ring_w + ((i - 1) % S::kDepth) * S::kBytes, r, u, V);
-        load_k<BITS, VB>(ring_w + (i % S::kDepth) * S::kBytes, r, u, low, K);
+        load_v<BITS, VB, NVS>(ring_w + ((i - 1) % S::kDepth) * S::kBytes, r, u, V);
+        load_k<BITS, VB, NVS>(ring_w + (i % S::kDepth) * S::kBytes, r, u, low, K);
         // keep every LDS read of the iteration ahead of the arithmetic
         __builtin_amdgcn_sched_barrier(0);
-        group_scores<BITS>(K, low, q16, low ? 0.0f : W.m_ref, sc);
-        group_values<VB>(V, W, bp_prev, vsh, vm0, vm1, magic, magic32);
-        bp_prev = group_probs<BITS, true>(W, sc, K.vs, K.vz);
+        group_scores<BITS, NVS>(K, low, q16, low ? 0.0f : W.m_ref, sc);
+        group_values<VB, NVS>(V, W, bp_prev, vsh, vm0, vm1, magic, magic32);
+        group_probs<BITS, true, NVS>(W, sc, K.vs, K.vz, bp_prev);
       }
       // the last kAhead groups: nothing left to load
       for (; i < n_mine; ++i) {
-        wait_groups<BITS, VB>(n_mine - 1 - i);
-        load_v<BITS, VB>(ring_w + ((i - 1) % S::kDepth) * S::kBytes, r, u, V);
-        load_k<BITS, VB>(ring_w + (i % S::kDepth) * S::kBytes, r, u, low, K);
+        wait_groups<BITS, VB, NVS>(n_mine - 1 - i);
+        load_v<BITS, VB, NVS>(ring_w + ((i - 1) % S::kDepth) * S::kBytes, r, u, V);
+        load_k<BITS, VB, NVS>(ring_w + (i % S::kDepth) * S::kBytes, r, u, low, K);
         // keep every LDS read of the iteration ahead of the arithmetic
         __builtin_amdgcn_sched_barrier(0);
-        group_scores<BITS>(K, low, q16, low ? 0.0f : W.m_ref, sc);
-        group_values<VB>(V, W, bp_prev, vsh, vm0, vm1, magic, magic32);
-        bp_prev = group_probs<BITS, true>(W, sc, K.vs, K.vz);
+        group_scores<BITS, NVS>(K, low, q16, low ? 0.0f : W.m_ref, sc);
+        group_values<VB, NVS>(V, W, bp_prev, vsh, vm0, vm1, magic, magic32);
+        group_probs<BITS, true, NVS>(W, sc, K.vs, K.vz, bp_prev);
       }
-      load_v<BITS, VB>(ring_w + ((n_mine - 1) % S::kDepth) * S::kBytes, r, u, V);
-      group_values<VB>(V, W, bp_prev, vsh, vm0, vm1, magic, magic32);
+      load_v<BITS, VB, NVS>(ring_w + ((n_mine - 1) % S::kDepth) * S::kBytes, r, u, V);
+      group_values<VB, NVS>(V, W, bp_prev, vsh, vm0, vm1, magic, magic32);
     }
   } else {
     // the FP16 window: q·log2e/√D as fp16 high/low terms, channel 32s + 8u + j
@@ -844,8 +929,8 @@ __attribute__((amdgpu_waves_per_eu((BITS == 2 && VB == 2) ? KVQ_DECODE_WAVES_PER
         for (int p = 0; p < 4; ++p) {
           const float x0 = qrow[32 * sl + 8 * u + 2 * p] * qs;
           const float x1 = qrow[32 * sl + 8 * u + 2 * p + 1] * qs;
-          const uint32_t hi = mix_pair(x0, 1.0f, x1, 1.0f);
-          d[p] = mix_pair_sub(x0, 1.0f, x1, 1.0f, hi & selmask);
+          const uint32_t hi = pack_rn(x0, x1);
+          d[p] = pack_rn_sub(x0, x1, hi & selmask);
         }
         bqw[sl] = u32x4{d[0], d[1], d[2], d[3]};
       }
@@ -1114,10 +1199,10 @@ __global__ __launch_bounds__(kThreads) void dense_mfma_split_kernel(DecodeArgs a
   WaveAcc W;
   W.m_ref = -INFINITY;
   W.l_acc = 0.0f;
-  W.pz_acc = 0.0f;
+  W.pz_acc[0] = 0.0f;
 #pragma unroll
   for (int n = 0; n < 8; ++n) W.cv[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  W.cones = f32x4{0.f, 0.f, 0.f, 0.f};
+  W.cones[0] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int64_t n_tiles = (a.n_main + kGroup - 1) / kGroup;
   const int64_t g0 = int64_t(split) * a.tiles_per_split;
@@ -1168,20 +1253,28 @@ hipError_t launch_dense_mfma(const DecodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid(a.n_split, a.B * a.H, a.nq / a.heads_per_chunk);
+// launches the (K bits, V bits) instance with NVS V scales per token
+template <int NVS>
+static hipError_t launch_kivi_nvs(const DecodeArgs& a, dim3 grid, hipStream_t s) {
   if (a.kbits == 2 && a.vbits == 2) {
-    kivi_mfma_split_kernel<2, 2><<<grid, kThreads, 0, s>>>(a);
+    kivi_mfma_split_kernel<2, 2, NVS><<<grid, kThreads, 0, s>>>(a);
   } else if (a.kbits == 4 && a.vbits == 4) {
-    kivi_mfma_split_kernel<4, 4><<<grid, kThreads, 0, s>>>(a);
+    kivi_mfma_split_kernel<4, 4, NVS><<<grid, kThreads, 0, s>>>(a);
   } else if (a.kbits == 4 && a.vbits == 2) {
-    kivi_mfma_split_kernel<4, 2><<<grid, kThreads, 0, s>>>(a);
+    kivi_mfma_split_kernel<4, 2, NVS><<<grid, kThreads, 0, s>>>(a);
   } else if (a.kbits == 2 && a.vbits == 4) {
-    kivi_mfma_split_kernel<2, 4><<<grid, kThreads, 0, s>>>(a);
+    kivi_mfma_split_kernel<2, 4, NVS><<<grid, kThreads, 0, s>>>(a);
   } else {
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid(a.n_split, a.B * a.H, a.nq / a.heads_per_chunk);
+  if (a.nvs == 1) return launch_kivi_nvs<1>(a, grid, s);
+  if (a.nvs == 4) return launch_kivi_nvs<4>(a, grid, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace kvq

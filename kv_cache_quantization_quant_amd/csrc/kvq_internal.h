@@ -27,11 +27,12 @@ struct KiviQuantArgs {
   int64_t NG;             // group slots per (b, h)
   int64_t NT;             // 32-token V tiles per (b, h) (NG·G/32)
   int group;              // G: 32, 64 or 128 tokens per K scale group
+  int nvs;                // V scales per token: 1, or 4 (runs of 32 channels)
   uint32_t* k_codes;      // [B·H][NG·G][D·b/32]
   uint32_t* v_codes;      // [B·H][NT][D][32·b_V/32]
   float* k_scale;         // [B·H][NG][D]
   float* k_zero;
-  float* v_scale;         // [B·H][NG·G]
+  float* v_scale;         // [B·H][NG·G][nvs]
   float* v_zero;
 };
 
@@ -98,6 +99,7 @@ enum SrcFormat : int { kSrcFp16 = 0, kSrcFp8 = 1, kSrcKivi2 = 2, kSrcKivi4 = 3, 
 struct DecodeArgs {
   int src;                // SrcFormat of the main region
   int kbits, vbits;       // KIVI K and V bit widths
+  int nvs;                // KIVI V scales per token (1, or 4: runs of 32 channels)
   int B, H, Hq;
   int nq;                 // query heads per KV head (Hq / H)
   int heads_per_chunk;    // query heads one workgroup handles

@@ -98,8 +98,9 @@ __device__ __forceinline__ void pack16(const float (&c)[16], uint32_t (&w)[BITS 
 // tokens × 128 channels) of K and of V for one (b, h). Loads: thread
 // (t = tid / 8, j = tid % 8) holds channels [16j, 16j + 16) of token t of each
 // sub-tile (256 contiguous bytes per token).
-//   V (per token): min / max over the 8 threads of a token (packed fp16 max
-//      of (x, −x), DPP exchanges), codes in registers, one word (two at 4
+//   V (per token): min / max over the 8 threads of a token, or over the 2
+//      threads of each run of 32 channels (packed fp16 max of (x, −x), DPP
+//      exchanges), codes in registers, one word (two at 4
 //      bits) of 16 channel codes per thread into an LDS transpose, from which
 //      each thread assembles the sub-tile's V words along tokens.
 //   K (per channel over the G tokens): the group goes through LDS; wavefront
@@ -148,7 +149,9 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
     *reinterpret_cast<uint4*>(&tile_k[tr][j * 16 + 8]) = kr[sub][1];
 
     // ---- V statistics: (max, max of −x) of the 16 values, then over the 8
-    // threads of the token (xor 1, xor 2 inside a quad, then the half-row mirror).
+    // threads of the token (xor 1, xor 2 inside a quad, then the half-row
+    // mirror), or over the 2 threads of a run of 32 channels (xor 1) when V
+    // has a scale per run (nvs = 4).
     const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     h2v mx2 = as_h2(vw[0]), mn2 = mx2;
 #pragma unroll
@@ -159,14 +162,18 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
     // (max, −min) of the thread's 16 values in one fp16 pair
     h2v mm = h2max(h2v{mx2[0], -mn2[0]}, h2v{mx2[1], -mn2[1]});
     mm = h2max(mm, as_h2(uint32_t(__builtin_amdgcn_mov_dpp(int(as_u(mm)), 0xB1, 0xF, 0xF, false))));
-    mm = h2max(mm, as_h2(uint32_t(__builtin_amdgcn_mov_dpp(int(as_u(mm)), 0x4E, 0xF, 0xF, false))));
-    mm = h2max(mm, as_h2(uint32_t(__builtin_amdgcn_mov_dpp(int(as_u(mm)), 0x141, 0xF, 0xF, false))));
+    if (a.nvs == 1) {
+      mm = h2max(mm, as_h2(uint32_t(__builtin_amdgcn_mov_dpp(int(as_u(mm)), 0x4E, 0xF, 0xF, false))));
+      mm = h2max(mm, as_h2(uint32_t(__builtin_amdgcn_mov_dpp(int(as_u(mm)), 0x141, 0xF, 0xF, false))));
+    }
     const float vmx = float(mm[0]);
     const float vmn = -float(mm[1]);
     const float vs = (vmx - vmn) / VQMAX;
-    if (j == 0) {
-      a.v_scale[bh * CT + gg * G + tr] = vs;
-      a.v_zero[bh * CT + gg * G + tr] = vmn;
+    // one thread per token (nvs = 1) or per run of 32 channels (nvs = 4)
+    if (a.nvs == 1 ? j == 0 : (j & 1) == 0) {
+      const int64_t o = (bh * CT + gg * G + tr) * a.nvs + (a.nvs == 1 ? 0 : j / 2);
+      a.v_scale[o] = vs;
+      a.v_zero[o] = vmn;
     }
 
     // ---- V codes of the thread's 16 channels → the LDS transpose

@@ -60,7 +60,7 @@ def test_struct_sizes_match_header(tmp_path):
         assert int(got[st]) == ctypes.sizeof(cls), st
         for f in fields[st]:
             assert int(got[f"{st}.{f}"]) == getattr(cls, f).offset, (st, f)
-    assert int(got["abi"]) == kq.kvq_abi_version() == kq.ABI_VERSION == 4
+    assert int(got["abi"]) == kq.kvq_abi_version() == kq.ABI_VERSION == 5
 
 
 def test_status_strings():
@@ -87,6 +87,9 @@ def test_status_strings():
     (dict(v_bits=8), kq.KVQ_ERR_UNSUPPORTED),
     (dict(bits=4, v_bits=2), 0),
     (dict(bits=2, v_bits=4), 0),
+    (dict(v_group_channels=32), 0),
+    (dict(v_group_channels=64), kq.KVQ_ERR_UNSUPPORTED),
+    (dict(v_group_channels=-32), kq.KVQ_ERR_UNSUPPORTED),
     (dict(residual_length=48), kq.KVQ_ERR_UNSUPPORTED),
     (dict(residual_length=-32), kq.KVQ_ERR_INVALID_ARG),
     (dict(batch=300, num_kv_heads=300), kq.KVQ_ERR_UNSUPPORTED),
@@ -136,15 +139,17 @@ def test_quantize_query_validation():
     assert kq.lib.kvq_layout_query(None, None) == kq.KVQ_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("bits,vbits", [(2, 0), (4, 0), (4, 2), (2, 4)])
+@pytest.mark.parametrize("bits,vbits,gc", [(2, 0, 0), (4, 0, 0), (4, 2, 0), (2, 4, 0),
+                                           (2, 0, 32), (4, 2, 32)])
 @pytest.mark.parametrize("G,R", [(32, 0), (32, 128), (64, 64), (128, 0), (128, 256)])
-def test_kivi_layout_matches_oracle_arrays(bits, vbits, G, R):
+def test_kivi_layout_matches_oracle_arrays(bits, vbits, gc, G, R):
     B, H, C = 3, 5, 1000
     cfg = kq.make_config("kivi", bits=bits, group_size=G, residual_length=R, batch=B,
-                         num_kv_heads=H, capacity=C, v_bits=vbits)
+                         num_kv_heads=H, capacity=C, v_bits=vbits, v_group_channels=gc)
     st, lay = kq.kvq_layout_query(cfg)
     assert st == 0
-    oc = ocache.KiviCache(B, H, 128, bits, G, R, C, v_bits=vbits or None)
+    oc = ocache.KiviCache(B, H, 128, bits, G, R, C, v_bits=vbits or None,
+                          v_group_channels=gc or None)
     for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero",
                  "k_resid", "v_resid"):
         assert getattr(lay, name) == getattr(oc, name).nbytes, name
@@ -188,19 +193,22 @@ def _host_cache(cfg, n_quant=0, n_resid=0, fake_ptrs=True):
 
 @pytest.mark.parametrize("fmt,bits,vbits,per_head", [
     ("kivi", 2, 0, 0), ("kivi", 4, 0, 0), ("kivi", 4, 2, 0), ("kivi", 2, 4, 0),
+    ("kivi", 2, 0, 32),      # per_head column carries v_group_channels for KIVI
     ("fp8", 8, 0, 0), ("fp8", 8, 0, 1), ("fp8_e5m2", 8, 0, 0), ("fp8_e5m2", 8, 0, 1),
     ("fp16", 16, 0, 0)])
 def test_decode_bytes_match_oracle(fmt, bits, vbits, per_head):
     B, H, C = 4, 8, 33024
     cfg = kq.make_config(fmt, bits=bits, batch=B, num_kv_heads=H, capacity=C, v_bits=vbits,
-                         scale_per_head=per_head)
+                         scale_per_head=per_head if fmt != "kivi" else 0,
+                         v_group_channels=per_head if fmt == "kivi" else 0)
     for nq, nr in [(32640, 128), (32768, 1), (32896, 128), (0, 77)]:
         if fmt != "kivi":
             nq, nr = nq + nr, 0
         c = _host_cache(cfg, nq, nr)
         got = kq.kvq_decode_bytes(c, 64)
         if fmt == "kivi":
-            ref = bytes_model.decode_bytes_kivi(B, H, 128, bits, 32, nq, nr, vbits or None)
+            ref = bytes_model.decode_bytes_kivi(B, H, 128, bits, 32, nq, nr, vbits or None,
+                                                per_head or None)
         elif fmt.startswith("fp8"):
             ref = bytes_model.decode_bytes_fp8(B, H, 128, nq, bool(per_head))
         else:

@@ -215,14 +215,32 @@ def test_kivi_mixed_bits(kq, G, bits, vbits, R, B, H, Hq, S0, steps):
     _kivi_stream_case(kq, G, bits, vbits, R, B, H, Hq, S0, steps)
 
 
-def _kivi_stream_case(kq, G, bits, vbits, R, B, H, Hq, S0, steps):
+@pytest.mark.parametrize("G,bits,vbits,R,B,H,Hq,S0,steps", [
+    (32, 2, 0, 128, 2, 2, 8, 600, 70),    # the 2-bit layout, GQA 4
+    (32, 4, 0, 64, 1, 3, 6, 300, 70),     # 4-bit
+    (64, 4, 2, 64, 2, 1, 4, 256, 70),     # G = 64, mixed widths
+    (128, 2, 4, 0, 1, 2, 16, 700, 140),   # G = 128, R = 0, GQA 8
+])
+def test_kivi_v_channel_subgroups(kq, G, bits, vbits, R, B, H, Hq, S0, steps):
+    """V scales and zero-points per token and run of 32 channels: quantizer
+    buffers bit-exact, and decode (four value-product operands per tile, one
+    per run) within the bound. The first two runs of V are made 8x narrower
+    than the others, so the runs' scales really differ."""
+    _kivi_stream_case(kq, G, bits, vbits, R, B, H, Hq, S0, steps, gc=32)
+
+
+def _kivi_stream_case(kq, G, bits, vbits, R, B, H, Hq, S0, steps, gc=0):
     C = S0 + steps
-    _say(f"[kivi G={G}] bits={bits} v_bits={vbits} R={R} B={B} H={H} Hq={Hq} S0={S0} "
-         f"steps={steps}")
+    _say(f"[kivi G={G}] bits={bits} v_bits={vbits} v_group_channels={gc} R={R} B={B} H={H} "
+         f"Hq={Hq} S0={S0} steps={steps}")
     k, v = _kv(B, H, C)
+    if gc:
+        v[..., :64] /= 8
     dc = kq.DeviceCache(kq.make_config("kivi", bits=bits, group_size=G, residual_length=R,
-                                       batch=B, num_kv_heads=H, capacity=C, v_bits=vbits))
-    oc = ocache.KiviCache(B, H, D, bits, G, R, C, v_bits=vbits or None)
+                                       batch=B, num_kv_heads=H, capacity=C, v_bits=vbits,
+                                       v_group_channels=gc))
+    oc = ocache.KiviCache(B, H, D, bits, G, R, C, v_bits=vbits or None,
+                          v_group_channels=gc or None)
     dc.prefill(k[:, :, :S0].contiguous(), v[:, :, :S0].contiguous())
     oc.prefill(_np(k[:, :, :S0]), _np(v[:, :, :S0]))
     torch.cuda.synchronize()
@@ -544,11 +562,12 @@ def test_dense_prefill_over_nan_memory(kq, fmt):
 
 # -------------------------------------------- full-size workloads, sampled ---
 
-def _oracle_blocks_kivi(k, v, blocks, bits, R, C, S):
+def _oracle_blocks_kivi(k, v, blocks, bits, R, C, S, G=32, v_bits=None, gc=None):
     """Oracle cache over the sampled (b, h) blocks only (B = len(blocks), H = 1)."""
     kb = np.stack([_np(k[b, h, :S]) for b, h in blocks])[:, None]
     vb = np.stack([_np(v[b, h, :S]) for b, h in blocks])[:, None]
-    oc = ocache.KiviCache(len(blocks), 1, D, bits, 32, R, C)
+    oc = ocache.KiviCache(len(blocks), 1, D, bits, G, R, C, v_bits=v_bits,
+                          v_group_channels=gc)
     oc.prefill(kb, vb)
     return oc
 
@@ -565,6 +584,50 @@ def _sampled_attention_check(out, q, oc, blocks, nq):
                                          Kh[i:i + 1], Vh[i:i + 1])
         worst = max(worst, _att_err(on[b:b + 1, h * nq:(h + 1) * nq], ref))
     return worst
+
+
+@pytest.mark.parametrize("G,bits,vbits,gc", [
+    (32, 2, 0, 0), (32, 4, 0, 0), (32, 4, 2, 0), (32, 2, 4, 0), (64, 2, 0, 0),
+    (128, 4, 0, 0), (32, 2, 0, 32), (64, 4, 2, 32), (128, 2, 4, 32),
+])
+def test_kivi_variants_full_layer_sampled(kq, G, bits, vbits, gc):
+    """Every KIVI decode variant on the 7B-layer shape (B = 8, 32 MHA heads,
+    S = 4096): each wavefront runs several groups through its LDS ring (the
+    small parity cases give it one), so the steady-state loop of each
+    instance is checked. Sampled (b, h) blocks: state bit-exact, attention
+    within the bound; then a few appends with a flush and another decode."""
+    cfg = synth.CONFIGS["llama2_7b_layer"]
+    B, H, Hq, S = cfg["batch"], cfg["num_kv_heads"], cfg["num_q_heads"], cfg["seq_len"]
+    R, steps = 128, 130
+    C = S + steps
+    nq = Hq // H
+    blocks = [(0, 0), (3, 17), (7, 31)]
+    _say(f"[7B layer] G={G} bits={bits} v_bits={vbits} v_group_channels={gc}")
+    k, v = _kv(B, H, C)
+    if gc:
+        v[..., :64] /= 8
+    dc = kq.DeviceCache(kq.make_config("kivi", bits=bits, group_size=G, residual_length=R,
+                                       batch=B, num_kv_heads=H, capacity=C, v_bits=vbits,
+                                       v_group_channels=gc))
+    dc.prefill(k[:, :, :S].contiguous(), v[:, :, :S].contiguous())
+    oc = _oracle_blocks_kivi(k, v, blocks, bits, R, C, S, G, vbits or None, gc or None)
+    torch.cuda.synchronize()
+    _compare_kivi_state(dc, oc, blocks)
+    q = synth.make_q(B, Hq, D, device="cuda")
+    worst = _sampled_attention_check(dc.decode(q), q, oc, blocks, nq)
+    kb = np.stack([_np(k[b, h]) for b, h in blocks])[:, None]
+    vb = np.stack([_np(v[b, h]) for b, h in blocks])[:, None]
+    for i in range(steps):
+        t = S + i
+        dc.append(k[:, :, t].contiguous(), v[:, :, t].contiguous())
+        oc.append(kb[:, :, t], vb[:, :, t])
+    q = synth.make_q(B, Hq, D, step=1, device="cuda")
+    worst = max(worst, _sampled_attention_check(dc.decode(q), q, oc, blocks, nq))
+    torch.cuda.synchronize()
+    assert oc.flush_steps
+    _compare_kivi_state(dc, oc, blocks)
+    _say(f"  worst sampled max abs err {worst:.3e}")
+    assert worst <= ATOL
 
 
 def test_gqa70b_32k_stream_sampled(kq):
