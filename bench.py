@@ -43,7 +43,8 @@ def _log(*a):
 
 def decode_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("kvq_decode.hip", "kvq_decode_mfma.hip", "kvq_internal.h", "kvq_api.cpp"):
+    for f in ("kvq_decode.hip", "kvq_decode_mfma.hip", "kvq_internal.h", "kvq_fp8.h",
+              "kvq_api.cpp"):
         with open(os.path.join(ROOT, "kv_cache_quantization_quant_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
