@@ -23,11 +23,16 @@ namespace {
 using kvq::kGroup;
 using kvq::kHeadDim;
 
-// Workgroups one decode launch aims for (8 per CU on 256 CUs).
-#ifndef KVQ_TARGET_WORKGROUPS
-#define KVQ_TARGET_WORKGROUPS 2048
+// Workgroups one decode launch aims for: KVQ_SPLIT_ROUNDS full rounds of the
+// split kernel's resident workgroups on the device (one round: every block
+// starts at once, and none waits for a slot behind a long one), at most
+// kMaxTargetWorkgroups (which bounds the workspace independently of the
+// device); kFallbackWorkgroups when the runtime cannot report residency.
+#ifndef KVQ_SPLIT_ROUNDS
+#define KVQ_SPLIT_ROUNDS 1
 #endif
-constexpr int64_t kTargetWorkgroups = KVQ_TARGET_WORKGROUPS;
+constexpr int64_t kMaxTargetWorkgroups = 4096;
+constexpr int64_t kFallbackWorkgroups = 2048;
 constexpr int64_t kMinTilesPerSplit = 4;   // one tile per wavefront at least
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -155,13 +160,15 @@ struct Plan {
   int tiles_per_split, n_split_main, n_split, hpc, nchunk;
 };
 
-Plan make_plan(const Dims& d, int nq, int64_t n_main, int n_win) {
+Plan make_plan(const Dims& d, int nq, int64_t n_main, int n_win, int64_t target) {
   Plan p;
   p.hpc = heads_per_chunk(nq);
   p.nchunk = nq / p.hpc;
   const int64_t tiles = ceil_div(n_main, kGroup);
   const int64_t x = d.B * d.H * p.nchunk;
-  int64_t tps = ceil_div(tiles * x, kTargetWorkgroups);
+  if (target <= 0) target = kFallbackWorkgroups;
+  if (target > kMaxTargetWorkgroups) target = kMaxTargetWorkgroups;
+  int64_t tps = ceil_div(tiles * x, target);
   if (tps < kMinTilesPerSplit) tps = kMinTilesPerSplit;
   p.tiles_per_split = int(tps);
   p.n_split_main = int(ceil_div(tiles, tps));
@@ -175,7 +182,7 @@ int64_t max_splits(const Dims& d, int nq) {
   const int hpc = heads_per_chunk(nq);
   const int64_t x = d.B * d.H * (nq / hpc);
   const int64_t max_tiles = d.CT / kGroup;
-  int64_t a = kTargetWorkgroups / x + 1;
+  int64_t a = kMaxTargetWorkgroups / x + 1;
   const int64_t b = ceil_div(max_tiles, kMinTilesPerSplit);
   if (b < a) a = b;
   return a + 1;
@@ -469,9 +476,6 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q, int32_t 
   const int nq = num_q_heads / int(d.H);
   const bool kivi = cache->cfg.format == KVQ_FMT_KIVI;
   const int n_win = kivi ? cache->n_resid : 0;
-  const Plan p = make_plan(d, nq, cache->n_quant, n_win);
-  if (p.n_split > max_splits(d, nq)) return KVQ_ERR_WORKSPACE;
-
   kvq::DecodeArgs a{};
   a.src = kivi ? (d.bits == 2 ? kvq::kSrcKivi2 : kvq::kSrcKivi4)
        : cache->cfg.format == KVQ_FMT_FP8_E4M3 ? kvq::kSrcFp8
@@ -480,6 +484,11 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q, int32_t 
   a.kbits = int(d.bits);
   a.vbits = int(d.vbits);
   a.nvs = int(d.nvs);
+  a.qfp8 = is_fp8(cache->cfg.format) && cache->cfg.fp8_attention ? 1 : 0;
+  const Plan p = make_plan(d, nq, cache->n_quant, n_win,
+                           int64_t(kvq::decode_resident_workgroups(a)) * KVQ_SPLIT_ROUNDS);
+  if (p.n_split > max_splits(d, nq)) return KVQ_ERR_WORKSPACE;
+
   a.B = int(d.B);
   a.H = int(d.H);
   a.Hq = num_q_heads;
@@ -493,7 +502,6 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q, int32_t 
   a.v_zero = cache->v_zero;
   a.tensor_scale = cache->tensor_scale;
   a.scale_stride = is_fp8(cache->cfg.format) && cache->cfg.scale_per_head ? 4 : 0;
-  a.qfp8 = is_fp8(cache->cfg.format) && cache->cfg.fp8_attention ? 1 : 0;
   a.NG = d.NG;
   a.NT = d.NT;
   a.gshift = d.G == 128 ? 2 : d.G == 64 ? 1 : 0;

@@ -51,6 +51,8 @@
 
 #include <math.h>
 
+#include <atomic>
+
 #include "kvq_fp8.h"
 #include "kvq_internal.h"
 
@@ -673,6 +675,35 @@ __device__ __forceinline__ void wave_epilogue_and_merge(const DecodeArgs& a, con
   }
 }
 
+// Block order of the split kernels: a 1-D grid whose first B·H·chunks·n_split_main
+// blocks are the main-region splits and whose last B·H·chunks blocks (when the
+// window is non-empty) are the window splits, so the short window blocks run
+// after the long ones instead of holding resident slots among them.
+struct BlockCoord {
+  int split, bh, chunk;
+};
+__device__ __forceinline__ BlockCoord block_coord(const DecodeArgs& a) {
+  const int x = a.B * a.H * (a.nq / a.heads_per_chunk);
+  const int id = int(blockIdx.x);
+  const int n_main_blocks = a.n_split_main * x;
+  int split, rest;
+  if (id < n_main_blocks) {
+    split = id % a.n_split_main;
+    rest = id / a.n_split_main;
+  } else {
+    split = a.n_split_main;
+    rest = id - n_main_blocks;
+  }
+  BlockCoord c;
+  c.split = split;
+  c.bh = rest % (a.B * a.H);
+  c.chunk = rest / (a.B * a.H);
+  return c;
+}
+__host__ inline dim3 split_grid(const DecodeArgs& a) {
+  return dim3(unsigned(a.n_split) * unsigned(a.B * a.H) * unsigned(a.nq / a.heads_per_chunk));
+}
+
 // Wave-uniform, offset-biased sources of the next group a wavefront loads.
 struct GroupSrc {
   const uint8_t* kc;   // K codes
@@ -796,12 +827,13 @@ __attribute__((amdgpu_waves_per_eu((BITS == 2 && VB == 2 && NVS == 1) ? KVQ_DECO
   using S = Stage<BITS, VB, NVS>;
   __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][S::kDepth][S::kBytes];
 
-  const int split = blockIdx.x;
-  const int bh = blockIdx.y;
+  const BlockCoord bc = block_coord(a);
+  const int split = bc.split;
+  const int bh = bc.bh;
   const int b = bh / a.H;
   const int h_kv = bh % a.H;
-  const int hq0 = h_kv * a.nq + int(blockIdx.z) * a.heads_per_chunk;
-  const int nh = min(a.heads_per_chunk, a.nq - int(blockIdx.z) * a.heads_per_chunk);
+  const int hq0 = h_kv * a.nq + bc.chunk * a.heads_per_chunk;
+  const int nh = min(a.heads_per_chunk, a.nq - bc.chunk * a.heads_per_chunk);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -1109,12 +1141,13 @@ __global__ __launch_bounds__(kThreads) void dense_mfma_split_kernel(DecodeArgs a
   using S = DenseStage<SRC>;
   __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][S::kDepth][S::kBytes];
 
-  const int split = blockIdx.x;
-  const int bh = blockIdx.y;
+  const BlockCoord bc = block_coord(a);
+  const int split = bc.split;
+  const int bh = bc.bh;
   const int b = bh / a.H;
   const int h_kv = bh % a.H;
-  const int hq0 = h_kv * a.nq + int(blockIdx.z) * a.heads_per_chunk;
-  const int nh = min(a.heads_per_chunk, a.nq - int(blockIdx.z) * a.heads_per_chunk);
+  const int hq0 = h_kv * a.nq + bc.chunk * a.heads_per_chunk;
+  const int nh = min(a.heads_per_chunk, a.nq - bc.chunk * a.heads_per_chunk);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -1240,7 +1273,7 @@ __global__ __launch_bounds__(kThreads) void dense_mfma_split_kernel(DecodeArgs a
 }  // namespace
 
 hipError_t launch_dense_mfma(const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid(a.n_split, a.B * a.H, a.nq / a.heads_per_chunk);
+  const dim3 grid = split_grid(a);
   if (a.src == kSrcFp16) {
     dense_mfma_split_kernel<kSrcFp16, false><<<grid, kThreads, 0, s>>>(a);
   } else if (a.src == kSrcE5M2) {
@@ -1270,8 +1303,63 @@ static hipError_t launch_kivi_nvs(const DecodeArgs& a, dim3 grid, hipStream_t s)
   return hipGetLastError();
 }
 
+// Resident workgroups per compute unit of each split-kernel instance, found
+// once per process (all instances are fixed at build time; 0 = not yet known).
+template <typename Kernel>
+static int blocks_per_cu(Kernel kernel, std::atomic<int>& slot) {
+  int n = slot.load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kThreads, 0) != hipSuccess || n <= 0)
+    return 0;
+  slot.store(n, std::memory_order_relaxed);
+  return n;
+}
+
+int decode_resident_workgroups(const DecodeArgs& a) {
+  static std::atomic<int> slots[16];
+  int per_cu = 0;
+  switch (a.src) {
+    case kSrcKivi2:
+    case kSrcKivi4: {
+      const int k = (a.kbits == 4 ? 1 : 0) + (a.vbits == 4 ? 2 : 0) + (a.nvs == 4 ? 4 : 0);
+      if (a.nvs != 1 && a.nvs != 4) return 0;
+      if (a.nvs == 1) {
+        if (k == 0) per_cu = blocks_per_cu(kivi_mfma_split_kernel<2, 2, 1>, slots[k]);
+        else if (k == 1) per_cu = blocks_per_cu(kivi_mfma_split_kernel<4, 2, 1>, slots[k]);
+        else if (k == 2) per_cu = blocks_per_cu(kivi_mfma_split_kernel<2, 4, 1>, slots[k]);
+        else per_cu = blocks_per_cu(kivi_mfma_split_kernel<4, 4, 1>, slots[k]);
+      } else {
+        if (k == 4) per_cu = blocks_per_cu(kivi_mfma_split_kernel<2, 2, 4>, slots[k]);
+        else if (k == 5) per_cu = blocks_per_cu(kivi_mfma_split_kernel<4, 2, 4>, slots[k]);
+        else if (k == 6) per_cu = blocks_per_cu(kivi_mfma_split_kernel<2, 4, 4>, slots[k]);
+        else per_cu = blocks_per_cu(kivi_mfma_split_kernel<4, 4, 4>, slots[k]);
+      }
+      break;
+    }
+    case kSrcFp16:
+      per_cu = blocks_per_cu(dense_mfma_split_kernel<kSrcFp16, false>, slots[8]);
+      break;
+    case kSrcFp8:
+      per_cu = a.qfp8 ? blocks_per_cu(dense_mfma_split_kernel<kSrcFp8, true>, slots[9])
+                      : blocks_per_cu(dense_mfma_split_kernel<kSrcFp8, false>, slots[10]);
+      break;
+    case kSrcE5M2:
+      per_cu = a.qfp8 ? blocks_per_cu(dense_mfma_split_kernel<kSrcE5M2, true>, slots[11])
+                      : blocks_per_cu(dense_mfma_split_kernel<kSrcE5M2, false>, slots[12]);
+      break;
+    default:
+      return 0;
+  }
+  if (per_cu <= 0) return 0;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return cus > 0 ? cus * per_cu : 0;
+}
+
 hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid(a.n_split, a.B * a.H, a.nq / a.heads_per_chunk);
+  const dim3 grid = split_grid(a);
   if (a.nvs == 1) return launch_kivi_nvs<1>(a, grid, s);
   if (a.nvs == 4) return launch_kivi_nvs<4>(a, grid, s);
   return hipErrorInvalidValue;

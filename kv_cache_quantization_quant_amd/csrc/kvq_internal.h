@@ -95,7 +95,8 @@ struct Fp8QuantArgs {
 
 enum SrcFormat : int { kSrcFp16 = 0, kSrcFp8 = 1, kSrcKivi2 = 2, kSrcKivi4 = 3, kSrcE5M2 = 4 };
 
-// Split-K decode attention. Grid: (n_split, B·H, head_chunks).
+// Split-K decode attention. Grid: n_split · B·H · head_chunks blocks in one
+// dimension, main-region splits first and window splits last.
 struct DecodeArgs {
   int src;                // SrcFormat of the main region
   int kbits, vbits;       // KIVI K and V bit widths
@@ -149,6 +150,11 @@ struct QueryQuantArgs {
 
 hipError_t launch_query_fp8(const QueryQuantArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// Workgroups of the split kernel that a.src, a.kbits, a.vbits, a.nvs and a.qfp8
+// select that the current device holds at once (compute units × resident
+// workgroups per unit, from the kernel's register and LDS use); 0 if the
+// runtime cannot tell.
+int decode_resident_workgroups(const DecodeArgs& a);
 hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_dense_mfma(const DecodeArgs& a, hipStream_t s);
 
