@@ -32,7 +32,14 @@ using kvq::kHeadDim;
 #define KVQ_SPLIT_ROUNDS 1
 #endif
 constexpr int64_t kMaxTargetWorkgroups = 4096;
+// Time of one FP16 window tile in a wavefront, in grouped-region tiles of the
+// same wavefront: the last main split of each (b, h) runs the window too and
+// gets that much less of the grouped region.
+#ifndef KVQ_WINDOW_TILE_COST
+#define KVQ_WINDOW_TILE_COST 8
+#endif
 constexpr int64_t kFallbackWorkgroups = 2048;
+constexpr int64_t kWaves = 4;              // wavefronts per decode workgroup
 constexpr int64_t kMinTilesPerSplit = 4;   // one tile per wavefront at least
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -157,7 +164,7 @@ int heads_per_chunk(int nq) {
 }
 
 struct Plan {
-  int tiles_per_split, n_split_main, n_split, hpc, nchunk;
+  int tiles_per_split, n_split_main, n_split, win_split, hpc, nchunk;
 };
 
 Plan make_plan(const Dims& d, int nq, int64_t n_main, int n_win, int64_t target) {
@@ -168,11 +175,21 @@ Plan make_plan(const Dims& d, int nq, int64_t n_main, int n_win, int64_t target)
   const int64_t x = d.B * d.H * p.nchunk;
   if (target <= 0) target = kFallbackWorkgroups;
   if (target > kMaxTargetWorkgroups) target = kMaxTargetWorkgroups;
-  int64_t tps = ceil_div(tiles * x, target);
+  // a non-empty window joins the last main split of (b, h) when there is one
+  const bool fold = n_win > 0 && tiles > 0;
+  const int64_t win_cost =
+      fold ? kWaves * KVQ_WINDOW_TILE_COST * ceil_div(ceil_div(n_win, kGroup), kWaves) : 0;
+  int64_t tps = ceil_div((tiles + win_cost) * x, target);
   if (tps < kMinTilesPerSplit) tps = kMinTilesPerSplit;
   p.tiles_per_split = int(tps);
   p.n_split_main = int(ceil_div(tiles, tps));
-  p.n_split = p.n_split_main + (n_win > 0 ? 1 : 0);
+  if (fold) {
+    p.n_split = p.n_split_main;
+    p.win_split = p.n_split_main - 1;
+  } else {
+    p.n_split = p.n_split_main + (n_win > 0 ? 1 : 0);
+    p.win_split = n_win > 0 ? p.n_split_main : -1;
+  }
   return p;
 }
 
@@ -514,6 +531,7 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q, int32_t 
   a.tiles_per_split = p.tiles_per_split;
   a.n_split_main = p.n_split_main;
   a.n_split = p.n_split;
+  a.win_split = p.win_split;
   a.q = q;
   a.out = out;
   a.ws = static_cast<float*>(workspace);

@@ -110,11 +110,60 @@ __device__ __forceinline__ void wait_vmem() {
 __device__ __forceinline__ float xor8(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
 }
-// src of lane l ^ 8 where BANKS enables lane l (bank b = lanes 4b..4b+3 of a
-// row: 0x3 = part 0, 0xC = part 1); the other lanes keep old
-template <int BANKS>
-__device__ __forceinline__ uint32_t from_partner(uint32_t old, uint32_t src) {
-  return uint32_t(__builtin_amdgcn_update_dpp(int(old), int(src), 0x128, 0xF, BANKS, false));
+// Exchange of high and low terms between partner lanes l and l ^ 8 (part 0:
+// lanes with l % 16 < 8): afterwards hi holds {part 0: own hi, part 1:
+// partner's lo} and lo holds {part 0: partner's hi, part 1: own lo}. One
+// v_cndmask_b32 per register, its first source read from lane l ^ 8 by DPP
+// (a masked DPP move pair would need a third instruction to keep a copy).
+// The block opens with two wait states (a DPP read of a VGPR that a VALU
+// instruction just wrote) and closes with two (a matrix-core operand read of
+// a VGPR a VALU instruction just wrote): the compiler pads only around
+// instructions it emitted itself. Both masks are set with s_mov, which
+// leaves SCC alone: the compiler may hold a branch condition in SCC across
+// the block (an SCC-writing s_not here once broke a loop's exit test).
+__device__ __forceinline__ void swap_halves2(uint32_t (&hi)[2], uint32_t (&lo)[2]) {
+  uint32_t h0, h1, l0, l1;
+  asm volatile(
+      "s_nop 1\n\t"
+      "s_mov_b32 vcc_lo, 0x00ff00ff\n\t"
+      "s_mov_b32 vcc_hi, 0x00ff00ff\n\t"
+      // vcc = part 0: part 0 keeps its hi (src1), part 1 takes lo of l ^ 8 (src0)
+      "v_cndmask_b32_dpp %0, %6, %4, vcc row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_cndmask_b32_dpp %1, %7, %5, vcc row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "s_mov_b32 vcc_lo, 0xff00ff00\n\t"
+      "s_mov_b32 vcc_hi, 0xff00ff00\n\t"
+      // vcc = part 1: part 1 keeps its lo (src1), part 0 takes hi of l ^ 8 (src0)
+      "v_cndmask_b32_dpp %2, %4, %6, vcc row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_cndmask_b32_dpp %3, %5, %7, vcc row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1"
+      : "=&v"(h0), "=&v"(h1), "=&v"(l0), "=&v"(l1)
+      : "v"(hi[0]), "v"(hi[1]), "v"(lo[0]), "v"(lo[1])
+      : "vcc");
+  hi[0] = h0; hi[1] = h1; lo[0] = l0; lo[1] = l1;
+}
+__device__ __forceinline__ void swap_halves4(uint32_t (&hi)[4], uint32_t (&lo)[4]) {
+  uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+  asm volatile(
+      "s_nop 1\n\t"
+      "s_mov_b32 vcc_lo, 0x00ff00ff\n\t"
+      "s_mov_b32 vcc_hi, 0x00ff00ff\n\t"
+      "v_cndmask_b32_dpp %0, %12, %8, vcc row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_cndmask_b32_dpp %1, %13, %9, vcc row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_cndmask_b32_dpp %2, %14, %10, vcc row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_cndmask_b32_dpp %3, %15, %11, vcc row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "s_mov_b32 vcc_lo, 0xff00ff00\n\t"
+      "s_mov_b32 vcc_hi, 0xff00ff00\n\t"
+      "v_cndmask_b32_dpp %4, %8, %12, vcc row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_cndmask_b32_dpp %5, %9, %13, vcc row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_cndmask_b32_dpp %6, %10, %14, vcc row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_cndmask_b32_dpp %7, %11, %15, vcc row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1"
+      : "=&v"(h0), "=&v"(h1), "=&v"(h2), "=&v"(h3), "=&v"(l0), "=&v"(l1), "=&v"(l2), "=&v"(l3)
+      : "v"(hi[0]), "v"(hi[1]), "v"(hi[2]), "v"(hi[3]), "v"(lo[0]), "v"(lo[1]), "v"(lo[2]),
+        "v"(lo[3])
+      : "vcc");
+  hi[0] = h0; hi[1] = h1; hi[2] = h2; hi[3] = h3;
+  lo[0] = l0; lo[1] = l1; lo[2] = l2; lo[3] = l3;
 }
 // sum over the lanes l ^ 16 and l ^ 32 (gfx950 permlane swaps)
 __device__ __forceinline__ float sum_x16_x32(float x) {
@@ -294,12 +343,7 @@ __device__ __forceinline__ u32x4 p_operand(const float (&pp)[4]) {
     hp[p] = __builtin_amdgcn_perm(__float_as_uint(x1), __float_as_uint(x0), 0x07060302u);
     lp[p] = __builtin_amdgcn_perm(__float_as_uint(l1), __float_as_uint(l0), 0x07060302u);
   }
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const uint32_t t = lp[p];
-    lp[p] = from_partner<0x3>(lp[p], hp[p]);
-    hp[p] = from_partner<0xC>(hp[p], t);
-  }
+  swap_halves2(hp, lp);
   return u32x4{hp[0], hp[1], lp[0], lp[1]};
 }
 
@@ -417,12 +461,7 @@ __device__ __forceinline__ void group_scores(const KLoad<BITS, NVS>& K, bool low
     }
     // part 0 takes the partner's high terms (k-step 2 + h), part 1 the
     // partner's low terms (k-step h)
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t t = lo[p];
-      lo[p] = from_partner<0x3>(lo[p], hi[p]);
-      hi[p] = from_partner<0xC>(hi[p], t);
-    }
+    swap_halves4(hi, lo);
     const u32x4 bh = u32x4{hi[0], hi[1], hi[2], hi[3]};
     const u32x4 bl = u32x4{lo[0], lo[1], lo[2], lo[3]};
     s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(k_operand<BITS>(m0, h)), as_f16x8(bh), s0, 0, 0, 0);
@@ -595,6 +634,36 @@ __device__ __forceinline__ void process_window_tile(const DecodeArgs& a, WaveAcc
     W.cv[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{lo[0], lo[1], lo[2], lo[3]}),
                                                        as_bf16x8(bp), W.cv[n], 0, 0, 0);
   }
+}
+
+// The FP16 window tiles of (b, h): tile t goes to wavefront t % kWaves.
+template <int NVS>
+__device__ __forceinline__ void run_window(const DecodeArgs& a, WaveAccT<NVS>& W, int bh, int b,
+                                           int hq0, int nh, int hs, int r, int u, bool low,
+                                           int wave) {
+  // the FP16 window: q·log2e/√D as fp16 high/low terms, channel 32s + 8u + j
+  u32x4 bqw[4];
+  {
+    const uint32_t selmask = low ? 0xFFFFFFFFu : 0u;
+    const bool valid = hs < nh;
+    const float qs = valid ? a.qscale : 0.0f;
+    const float* qrow = a.q + (int64_t(b) * a.Hq + hq0 + (valid ? hs : 0)) * kHeadDim;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      uint32_t d[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float x0 = qrow[32 * sl + 8 * u + 2 * p] * qs;
+        const float x1 = qrow[32 * sl + 8 * u + 2 * p + 1] * qs;
+        const uint32_t hi = pack_rn(x0, x1);
+        d[p] = pack_rn_sub(x0, x1, hi & selmask);
+      }
+      bqw[sl] = u32x4{d[0], d[1], d[2], d[3]};
+    }
+  }
+  const int64_t n_tiles = (a.n_win + kGroup - 1) / kGroup;
+  for (int64_t tile = wave; tile < n_tiles; tile += kWaves)
+    process_window_tile(a, W, bh, tile, bqw, r, u, low);
 }
 
 // Asynchronous global→LDS copies (global_load_lds): lane i's 16 or 4 bytes
@@ -900,6 +969,10 @@ __attribute__((amdgpu_waves_per_eu((BITS == 2 && VB == 2 && NVS == 1) ? KVQ_DECO
         advance<BITS, VB, NVS>(P, a.gshift);
       }
     }
+    // the last main split of (b, h) also takes the window, while the first
+    // copies are in flight (its loads are ordinary ones, older than every
+    // copy waited on below, so the counted waits still hold)
+    if (split == a.win_split) run_window(a, W, bh, b, hq0, nh, hs, r, u, low, wave);
     if (n_mine > 0) {
       float sc[4];
       if (kAhead < n_mine) {
@@ -947,29 +1020,7 @@ __attribute__((amdgpu_waves_per_eu((BITS == 2 && VB == 2 && NVS == 1) ? KVQ_DECO
       group_values<VB, NVS>(V, W, bp_prev, vsh, vm0, vm1, magic, magic32);
     }
   } else {
-    // the FP16 window: q·log2e/√D as fp16 high/low terms, channel 32s + 8u + j
-    u32x4 bqw[4];
-    {
-      const uint32_t selmask = low ? 0xFFFFFFFFu : 0u;
-      const bool valid = hs < nh;
-      const float qs = valid ? a.qscale : 0.0f;
-      const float* qrow = a.q + (int64_t(b) * a.Hq + hq0 + (valid ? hs : 0)) * kHeadDim;
-#pragma unroll
-      for (int sl = 0; sl < 4; ++sl) {
-        uint32_t d[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const float x0 = qrow[32 * sl + 8 * u + 2 * p] * qs;
-          const float x1 = qrow[32 * sl + 8 * u + 2 * p + 1] * qs;
-          const uint32_t hi = pack_rn(x0, x1);
-          d[p] = pack_rn_sub(x0, x1, hi & selmask);
-        }
-        bqw[sl] = u32x4{d[0], d[1], d[2], d[3]};
-      }
-    }
-    const int64_t n_tiles = (a.n_win + kGroup - 1) / kGroup;
-    for (int64_t tile = wave; tile < n_tiles; tile += kWaves)
-      process_window_tile(a, W, bh, tile, bqw, r, u, low);
+    run_window(a, W, bh, b, hq0, nh, hs, r, u, low, wave);
   }
 
   wave_epilogue_and_merge(a, W, &ring[0][0][0], sizeof(ring[0]), wave, lane, hs, u, low, tid,
@@ -1059,12 +1110,7 @@ __device__ __forceinline__ u32x4 p_operand_f16(const float (&pp)[4]) {
   uint32_t hp[2], lp[2];
   split_pair(pp[0], pp[1], hp[0], lp[0]);
   split_pair(pp[2], pp[3], hp[1], lp[1]);
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const uint32_t t = lp[p];
-    lp[p] = from_partner<0x3>(lp[p], hp[p]);
-    hp[p] = from_partner<0xC>(hp[p], t);
-  }
+  swap_halves2(hp, lp);
   return u32x4{hp[0], hp[1], lp[0], lp[1]};
 }
 

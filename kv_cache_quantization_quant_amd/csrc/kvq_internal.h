@@ -127,7 +127,8 @@ struct DecodeArgs {
   // split plan
   int tiles_per_split;
   int n_split_main;       // splits over the main region
-  int n_split;            // n_split_main (+1 if the window is non-empty)
+  int n_split;            // n_split_main, +1 if the window has a split of its own
+  int win_split;          // split that runs the window tiles (-1: empty window)
   int split_offset;       // first split index a launch covers (grid.x from here)
   const float* q;         // [B][Hq][D]
   float* out;             // [B][Hq][D]

@@ -7,7 +7,8 @@ feeds the MFMA the register's previous contents (one accumulator tile of the
 KIVI decode came out as garbage that way). This test compiles
 kvq_decode_mfma.hip for gfx950 with the library's flags and checks, in every
 kernel, that each MFMA's A and B operands were written at least two wait
-states (instructions or s_nop slots) earlier.
+states (instructions or s_nop slots) earlier, and likewise the DPP-read
+operand of every DPP instruction.
 """
 import os
 import re
@@ -88,10 +89,76 @@ def test_every_mfma_operand_has_two_wait_states(decode_asm):
     assert not bad, "\n".join(bad[:10])
 
 
-def test_no_inline_asm_valu_in_decode_source():
-    """Inline asm in the decode kernels holds only copies, waits and M0 / EXEC
-    moves (no VALU instruction the compiler could not pad)."""
+def _dpp_gaps(body):
+    """(gap, dpp, producer) for each DPP instruction whose DPP-read source
+    (src0) a VALU instruction wrote fewer than 2 slots earlier."""
+    found = []
+    for i, t in enumerate(body):
+        if not (t.startswith("v_") and "_dpp" in t.split()[0]):
+            continue
+        ops = [o.strip(",") for o in t.split()[1:3]]
+        src = _regs(ops[1])
+        k, slots = i - 1, 0
+        while k >= 0 and slots < 2:
+            u = body[k]
+            if u.startswith(".LBB") or u.startswith("s_cbranch") or u.startswith("s_branch"):
+                break
+            if u and not u.startswith((".", ";")):
+                if u.startswith("s_nop"):
+                    slots += int(u.split()[1]) + 1
+                else:
+                    if u.startswith("v_") and _regs(u.split()[1].strip(",")) & src:
+                        found.append((slots, t, u))
+                        break
+                    slots += 1
+            k -= 1
+    return found
+
+
+def test_every_dpp_read_has_two_wait_states(decode_asm):
+    """A DPP operand read of a VGPR needs two wait states after the VALU
+    write of it; the compiler pads only its own instructions."""
+    bad = []
+    for name, body in _kernels(decode_asm).items():
+        for gap, dpp, producer in _dpp_gaps(body):
+            bad.append(f"{name[:60]}: {producer} -> {dpp} ({gap} wait states)")
+    assert not bad, "\n".join(bad[:10])
+
+
+def test_inline_asm_valu_is_padded_in_decode_source():
+    """Inline asm in the decode kernels that holds VALU instructions (the
+    DPP half swaps) opens and closes with two wait states (s_nop 1), since the
+    compiler does not pad around instructions it did not emit."""
     src = open(SRC).read()
     bodies = re.findall(r'asm(?:\s+volatile)?\s*\((.*?)\)\s*;', src, re.S)
     valu = [b for b in bodies if re.search(r'"\s*v_', b)]
-    assert not valu, valu[:3]
+    assert valu, "the half swaps are inline asm"
+    for b in valu:
+        lits = []
+        for lit in re.findall(r'"((?:[^"\\]|\\.)*)"', b):
+            if re.fullmatch(r"[=&+]*[a-z]", lit):     # first operand constraint
+                break
+            lits.append(lit)
+        text = "".join(lits).replace("\\n", "\n").replace("\\t", "")
+        instrs = [x.strip() for x in text.split("\n") if x.strip()]
+        assert instrs[0] == "s_nop 1" and instrs[-1] == "s_nop 1", instrs
+
+
+def test_inline_asm_keeps_scc_in_decode_source():
+    """The scalar instructions in the decode kernels' inline asm are moves,
+    nops and waits only: the compiler may keep a branch condition in SCC
+    across an asm block, and SALU arithmetic or logic (s_not, s_and, s_add...)
+    would overwrite it."""
+    src = open(SRC).read()
+    bodies = re.findall(r'asm(?:\s+volatile)?\s*\((.*?)\)\s*;', src, re.S)
+    allowed = {"s_mov_b32", "s_mov_b64", "s_nop", "s_waitcnt"}
+    for b in bodies:
+        for lit in re.findall(r'"((?:[^"\\]|\\.)*)"', b):
+            for ins in lit.replace("\\n", "\n").replace("\\t", "").split("\n"):
+                op = ins.strip().split(" ")[0] if ins.strip() else ""
+                if op.startswith("s_"):
+                    assert op in allowed, f"SCC-writing scalar instruction in inline asm: {ins}"
+    # the KVQ_COPY_* macros hold the copy instructions
+    for m in re.findall(r'#define KVQ_\w+\s+(.*)', src):
+        for op in re.findall(r'\b(s_[a-z0-9_]+)', m):
+            assert op in allowed, op
