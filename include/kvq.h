@@ -34,7 +34,10 @@
  *   stream). All device work is enqueued asynchronously on it, in call order.
  * - State. The fill levels (n_quant, n_resid) live in the host-side
  *   kvq_cache struct and are updated when the work is enqueued, so no call
- *   waits for the device. All `batch` sequences have the same length.
+ *   waits for the device. All `batch` sequences have the same length, unless
+ *   the cache is ragged (KIVI only; see kvq_prefill_quantize_ragged): then
+ *   each sequence b has its own fill levels seq_n_quant[b], seq_n_resid[b]
+ *   in caller-owned host arrays, and the scalar n_quant, n_resid stay 0.
  * - Errors. Every argument and state check runs before anything is enqueued.
  *   A call that returns an error enqueued nothing and changed nothing.
  *   KVQ_ERR_DEVICE reports a failed HIP launch; then the cache state has
@@ -132,7 +135,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 5
+#define KVQ_ABI_VERSION 6
 
 typedef enum {
   KVQ_OK = 0,
@@ -205,7 +208,17 @@ typedef struct {
   int64_t n_quant;
   int32_t n_resid;
   int32_t reserved;
+  /* Ragged mode (KIVI): both non-NULL, host arrays of `batch` entries owned by
+   * the caller, holding each sequence's fill levels (grouped tokens, window
+   * tokens); the library reads and updates them like n_quant and n_resid.
+   * NULL (both): every sequence has the scalar fill levels above. */
+  int64_t* seq_n_quant;
+  int32_t* seq_n_resid;
 } kvq_cache;
+
+/* Largest batch of a ragged cache (the per-sequence fill levels travel to
+ * the kernels as launch arguments). */
+#define KVQ_MAX_RAGGED_BATCH 128
 
 /* Sizes of every device buffer a cache with this configuration needs.
  * Errors: INVALID_ARG (null / non-positive fields / bad format),
@@ -216,7 +229,8 @@ kvq_status kvq_layout_query(const kvq_config* cfg, kvq_layout* out);
  * pointer and sets the state to empty (n_quant = n_resid = 0). */
 kvq_status kvq_cache_init(kvq_cache* cache, const kvq_config* cfg);
 
-/* Marks the cache empty again (host state only; enqueues nothing). */
+/* Marks the cache empty again (host state only; enqueues nothing); a
+ * ragged cache clears every sequence's fill levels. */
 kvq_status kvq_cache_reset(kvq_cache* cache);
 
 /* Prefill-time quantization ([Tutorial] §八.4, [Interview] §四; KIVI split
@@ -230,6 +244,21 @@ kvq_status kvq_cache_reset(kvq_cache* cache);
 kvq_status kvq_prefill_quantize(kvq_cache* cache, const void* k, const void* v,
                                 int64_t seq_len, void* stream);
 
+/* Prefill of a ragged batch: sequences of different lengths, each
+ * quantized as if it were alone in a batch of one (its groups start at its
+ * own token 0, its window holds its own newest tokens; [KIVI-page] §3.2 per
+ * sequence). The cache must be KIVI and ragged (seq_n_quant and seq_n_resid
+ * set; else UNSUPPORTED / INVALID_ARG), with batch ≤ KVQ_MAX_RAGGED_BATCH
+ * (else UNSUPPORTED), and every sequence empty (else STATE).
+ * k, v: device fp16 [B][H][max_len][D], sequence b in its first seq_lens[b]
+ * tokens (the rest is padding and is not read). seq_lens: host int64 [B],
+ * 1 ≤ seq_lens[b] ≤ max_len (else INVALID_ARG) and ≤ capacity (else
+ * CAPACITY). Sets seq_n_quant[b] = G·max(0, min(⌊S_b/G⌋, ⌈(S_b−R)/G⌉)) and
+ * seq_n_resid[b] = S_b − seq_n_quant[b]. */
+kvq_status kvq_prefill_quantize_ragged(kvq_cache* cache, const void* k, const void* v,
+                                       int64_t max_len, const int64_t* seq_lens,
+                                       void* stream);
+
 /* Appends one token per (batch, KV head) ([KIVI-page] §3.1–3.2).
  * k_new, v_new: device fp16 [B][H][D].
  * KIVI: if the window is full (n_resid == Rcap) its Rcap tokens are first
@@ -237,7 +266,9 @@ kvq_status kvq_prefill_quantize(kvq_cache* cache, const void* k, const void* v,
  * the token is stored in window slot n_resid. FP8: encoded with the frozen
  * prefill scales (saturating). FP16: copied. CAPACITY when n_quant + n_resid
  * == C. KIVI and FP16 may append to an empty cache; FP8 needs its prefill
- * scales first (else STATE). */
+ * scales first (else STATE). Ragged KIVI cache: every sequence appends one
+ * token; each sequence whose window is full flushes it first, alone;
+ * CAPACITY if any sequence is full. */
 kvq_status kvq_append_token(kvq_cache* cache, const void* k_new,
                             const void* v_new, void* stream);
 
@@ -255,8 +286,9 @@ size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t num_q_heads);
  * the decode launch, not stored): attention in the FP8 domain.
  * q: device fp32 [B][Hq][D]; out: device fp32 [B][Hq][D] (written);
  * workspace: device, ≥ kvq_decode_workspace_bytes(&cache->cfg, Hq).
- * Errors: STATE on an empty cache, WORKSPACE if too small, UNSUPPORTED if
- * Hq is not a multiple of H. */
+ * Ragged KIVI cache: each sequence attends over its own tokens.
+ * Errors: STATE on an empty cache (ragged: any empty sequence), WORKSPACE if
+ * too small, UNSUPPORTED if Hq is not a multiple of H. */
 kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q,
                                 int32_t num_q_heads, float* out,
                                 void* workspace, size_t workspace_bytes,
@@ -282,7 +314,8 @@ kvq_status kvq_quantize_query_fp8(const float* q, int32_t batch, int32_t num_q_h
  * fill state: codes, scales and zero-points of the grouped region plus the
  * fp16 window (KIVI); codes plus the K and V scales, per tensor or per KV
  * head (FP8); fp16 K and V (FP16).
- * Query and output bytes are not included. −1 on invalid input. */
+ * Query and output bytes are not included; a ragged cache sums its
+ * sequences. −1 on invalid input. */
 int64_t kvq_decode_bytes(const kvq_cache* cache, int32_t num_q_heads);
 
 /* The pages' KV byte formula 2·L·B·S·H_kv·D·bytes_per_elem

@@ -28,7 +28,7 @@ KVQ_ERR_STATE = 4
 KVQ_ERR_DEVICE = 5
 KVQ_ERR_WORKSPACE = 6
 
-ABI_VERSION = 5        # KVQ_ABI_VERSION of include/kvq.h
+ABI_VERSION = 6        # KVQ_ABI_VERSION of include/kvq.h
 
 KVQ_FMT_FP16 = 0
 KVQ_FMT_FP8_E4M3 = 1
@@ -60,7 +60,11 @@ class KvqCache(ctypes.Structure):
                 ("v_scale", c_void_p), ("v_zero", c_void_p),
                 ("k_resid", c_void_p), ("v_resid", c_void_p),
                 ("tensor_scale", c_void_p),
-                ("n_quant", c_int64), ("n_resid", c_int32), ("reserved", c_int32)]
+                ("n_quant", c_int64), ("n_resid", c_int32), ("reserved", c_int32),
+                ("seq_n_quant", POINTER(c_int64)), ("seq_n_resid", POINTER(c_int32))]
+
+
+MAX_RAGGED_BATCH = 128   # KVQ_MAX_RAGGED_BATCH
 
 
 class KvqError(RuntimeError):
@@ -82,6 +86,8 @@ def _load():
         "kvq_cache_reset": (c_int32, [POINTER(KvqCache)]),
         "kvq_prefill_quantize": (c_int32, [POINTER(KvqCache), c_void_p, c_void_p, c_int64,
                                            c_void_p]),
+        "kvq_prefill_quantize_ragged": (c_int32, [POINTER(KvqCache), c_void_p, c_void_p, c_int64,
+                                                  POINTER(c_int64), c_void_p]),
         "kvq_append_token": (c_int32, [POINTER(KvqCache), c_void_p, c_void_p, c_void_p]),
         "kvq_decode_workspace_bytes": (c_size_t, [POINTER(KvqConfig), c_int32]),
         "kvq_decode_attention": (c_int32, [POINTER(KvqCache), c_void_p, c_int32, c_void_p,
@@ -105,7 +111,8 @@ def _load():
 
 lib = _load()
 ABI_SYMBOLS = ("kvq_abi_version", "kvq_status_str", "kvq_layout_query", "kvq_cache_init",
-               "kvq_cache_reset", "kvq_prefill_quantize", "kvq_append_token",
+               "kvq_cache_reset", "kvq_prefill_quantize", "kvq_prefill_quantize_ragged",
+               "kvq_append_token",
                "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_bytes",
                "kvq_quantize_query_fp8", "kvq_theoretical_bytes")
 
@@ -136,6 +143,12 @@ def kvq_cache_reset(cache: KvqCache) -> int:
 def kvq_prefill_quantize(cache: KvqCache, k_ptr: int, v_ptr: int, seq_len: int,
                          stream: int | None) -> int:
     return lib.kvq_prefill_quantize(byref(cache), k_ptr, v_ptr, seq_len, stream)
+
+
+def kvq_prefill_quantize_ragged(cache: KvqCache, k_ptr: int, v_ptr: int, max_len: int,
+                                seq_lens, stream: int | None) -> int:
+    """seq_lens: a ctypes int64 array of `batch` entries (host)."""
+    return lib.kvq_prefill_quantize_ragged(byref(cache), k_ptr, v_ptr, max_len, seq_lens, stream)
 
 
 def kvq_append_token(cache: KvqCache, k_ptr: int, v_ptr: int, stream: int | None) -> int:
@@ -215,12 +228,20 @@ class DeviceCache:
     _BUFFERS = ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero",
                 "k_resid", "v_resid", "tensor_scale")
 
-    def __init__(self, cfg: KvqConfig, device="cuda"):
+    def __init__(self, cfg: KvqConfig, device="cuda", ragged: bool = False):
+        """ragged: per-sequence fill levels (KIVI; prefill with prefill_ragged)."""
         self.cfg = cfg
         st, self.layout = kvq_layout_query(cfg)
         _check(st, "kvq_layout_query")
         self.cache = KvqCache()
         _check(kvq_cache_init(self.cache, cfg), "kvq_cache_init")
+        self.ragged = ragged
+        if ragged:
+            # host arrays the library reads and updates (kept alive here)
+            self._seq_nq = (c_int64 * cfg.batch)()
+            self._seq_nr = (c_int32 * cfg.batch)()
+            self.cache.seq_n_quant = ctypes.cast(self._seq_nq, POINTER(c_int64))
+            self.cache.seq_n_resid = ctypes.cast(self._seq_nr, POINTER(c_int32))
         self.buffers = {}
         for name in self._BUFFERS:
             nbytes = getattr(self.layout, name)
@@ -239,8 +260,27 @@ class DeviceCache:
     def n_resid(self) -> int:
         return self.cache.n_resid
 
+    @property
+    def seq_n_quant(self) -> list[int]:
+        return list(self._seq_nq)
+
+    @property
+    def seq_n_resid(self) -> list[int]:
+        return list(self._seq_nr)
+
     def reset(self):
         _check(kvq_cache_reset(self.cache), "kvq_cache_reset")
+
+    def prefill_ragged(self, k: torch.Tensor, v: torch.Tensor, seq_lens, stream=None):
+        """k, v: contiguous fp16 [B, H, max_len, D] on the device, sequence b in
+        its first seq_lens[b] tokens."""
+        assert self.ragged
+        assert k.dtype == torch.float16 and v.dtype == torch.float16
+        assert k.is_contiguous() and v.is_contiguous() and k.shape == v.shape
+        lens = (c_int64 * len(seq_lens))(*[int(x) for x in seq_lens])
+        _check(kvq_prefill_quantize_ragged(self.cache, k.data_ptr(), v.data_ptr(), k.shape[2],
+                                           lens, _stream_handle(stream)),
+               "kvq_prefill_quantize_ragged")
 
     def prefill(self, k: torch.Tensor, v: torch.Tensor, stream=None):
         """k, v: contiguous fp16 [B, H, S, D] on the device."""

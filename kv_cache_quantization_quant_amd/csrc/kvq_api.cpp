@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+
+#include <algorithm>
 #include <stdint.h>
 #include <string.h>
 
@@ -126,12 +128,60 @@ bool buffers_set(const kvq_cache* c) {
   return true;
 }
 
+bool is_ragged(const kvq_cache* c) {
+  return c->seq_n_quant != nullptr && c->seq_n_resid != nullptr;
+}
+
+// One sequence's KIVI fill levels are reachable ones.
+bool kivi_levels_ok(int64_t nq, int64_t nr, const Dims& d) {
+  return nq >= 0 && nr >= 0 && nq + nr <= d.C && nq % d.G == 0 && nr <= d.Rcap;
+}
+
 // The host-side fill state must be one the state machine can reach; a
 // corrupted struct is rejected before it can steer a kernel out of bounds.
+// A ragged cache is KIVI with at most kMaxRagged sequences, zero scalar
+// levels and reachable levels per sequence (only one of the two arrays set
+// is not a state at all).
 bool state_ok(const kvq_cache* c, const Dims& d) {
+  if ((c->seq_n_quant == nullptr) != (c->seq_n_resid == nullptr)) return false;
+  if (is_ragged(c)) {
+    if (c->cfg.format != KVQ_FMT_KIVI || d.B > kvq::kMaxRagged) return false;
+    if (c->n_quant != 0 || c->n_resid != 0) return false;
+    for (int64_t b = 0; b < d.B; ++b)
+      if (!kivi_levels_ok(c->seq_n_quant[b], c->seq_n_resid[b], d)) return false;
+    return true;
+  }
   if (c->n_quant < 0 || c->n_resid < 0 || c->n_quant + c->n_resid > d.C) return false;
   if (c->cfg.format == KVQ_FMT_KIVI) return c->n_quant % d.G == 0 && c->n_resid <= d.Rcap;
   return c->n_resid == 0;
+}
+
+// n_quant of a prefill of S tokens: G·max(0, min(⌊S/G⌋, ⌈(S−R)/G⌉)).
+int64_t prefill_quant_tokens(int64_t S, int64_t R, int64_t G) {
+  int64_t need = S > R ? ceil_div(S - R, G) : 0;
+  const int64_t full = S / G;
+  if (need > full) need = full;
+  return need * G;
+}
+
+// The quantize launch block of a KIVI cache (source and group range unset).
+kvq::KiviQuantArgs kivi_quant_args(const kvq_cache* c, const Dims& d) {
+  kvq::KiviQuantArgs qa{};
+  qa.bh_count = int(d.B * d.H);
+  qa.bits = int(d.bits);
+  qa.vbits = int(d.vbits);
+  qa.NG = d.NG;
+  qa.NT = d.NT;
+  qa.group = int(d.G);
+  qa.nvs = int(d.nvs);
+  qa.H = int(d.H);
+  qa.k_codes = static_cast<uint32_t*>(c->k_codes);
+  qa.v_codes = static_cast<uint32_t*>(c->v_codes);
+  qa.k_scale = c->k_scale;
+  qa.k_zero = c->k_zero;
+  qa.v_scale = c->v_scale;
+  qa.v_zero = c->v_zero;
+  return qa;
 }
 
 // V of an FP8 / FP16 cache: source tokens [0, n) of an fp16 [B·H][..][D]
@@ -205,6 +255,36 @@ int64_t max_splits(const Dims& d, int nq) {
   return a + 1;
 }
 
+// Split plan of a ragged KIVI batch: one tile count per split over all
+// sequences, sized like make_plan from the total work (tiles plus window
+// cost) of the batch, but never more splits than the workspace bound allows
+// for the longest sequence. Sequence b uses splits [0, ⌈tiles_b / tps⌉); its
+// window joins its last one (split 0 when it has no tiles).
+Plan make_plan_ragged(const Dims& d, int nq, const kvq_cache* c, int64_t target) {
+  Plan p;
+  p.hpc = heads_per_chunk(nq);
+  p.nchunk = nq / p.hpc;
+  if (target <= 0) target = kFallbackWorkgroups;
+  if (target > kMaxTargetWorkgroups) target = kMaxTargetWorkgroups;
+  int64_t total = 0, max_tiles = 0;
+  for (int64_t b = 0; b < d.B; ++b) {
+    const int64_t tiles = c->seq_n_quant[b] / kGroup;
+    const int64_t n_win = c->seq_n_resid[b];
+    total += tiles;
+    if (n_win > 0 && tiles > 0)
+      total += kWaves * KVQ_WINDOW_TILE_COST * ceil_div(ceil_div(n_win, kGroup), kWaves);
+    max_tiles = std::max(max_tiles, tiles);
+  }
+  int64_t tps = ceil_div(total * d.H * p.nchunk, target);
+  tps = std::max(tps, ceil_div(max_tiles, max_splits(d, nq) - 1));
+  if (tps < kMinTilesPerSplit) tps = kMinTilesPerSplit;
+  p.tiles_per_split = int(tps);
+  p.n_split_main = int(ceil_div(max_tiles, tps));
+  p.n_split = std::max(p.n_split_main, 1);
+  p.win_split = -1;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -265,6 +345,13 @@ kvq_status kvq_cache_reset(kvq_cache* cache) {
   if (v != KVQ_OK) return v;
   cache->n_quant = 0;
   cache->n_resid = 0;
+  if (is_ragged(cache)) {
+    if (cache->cfg.batch > kvq::kMaxRagged) return KVQ_ERR_UNSUPPORTED;
+    for (int32_t b = 0; b < cache->cfg.batch; ++b) {
+      cache->seq_n_quant[b] = 0;
+      cache->seq_n_resid[b] = 0;
+    }
+  }
   return KVQ_OK;
 }
 
@@ -276,6 +363,7 @@ kvq_status kvq_prefill_quantize(kvq_cache* cache, const void* k, const void* v,
   if (vs != KVQ_OK) return vs;
   if (!buffers_set(cache)) return KVQ_ERR_INVALID_ARG;
   if (seq_len <= 0) return KVQ_ERR_INVALID_ARG;
+  if (is_ragged(cache)) return KVQ_ERR_INVALID_ARG;   // kvq_prefill_quantize_ragged
   const Dims d = dims_of(cache->cfg);
   if (!state_ok(cache, d)) return KVQ_ERR_STATE;
   if (seq_len > d.C) return KVQ_ERR_CAPACITY;
@@ -370,6 +458,121 @@ kvq_status kvq_prefill_quantize(kvq_cache* cache, const void* k, const void* v,
   return KVQ_OK;
 }
 
+kvq_status kvq_prefill_quantize_ragged(kvq_cache* cache, const void* k, const void* v,
+                                       int64_t max_len, const int64_t* seq_lens,
+                                       void* stream) {
+  if (cache == nullptr || k == nullptr || v == nullptr || seq_lens == nullptr)
+    return KVQ_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned16(v)) return KVQ_ERR_INVALID_ARG;
+  const kvq_status vs = validate_config(&cache->cfg);
+  if (vs != KVQ_OK) return vs;
+  if (cache->cfg.format != KVQ_FMT_KIVI) return KVQ_ERR_UNSUPPORTED;
+  if (cache->cfg.batch > kvq::kMaxRagged) return KVQ_ERR_UNSUPPORTED;
+  if (!is_ragged(cache)) return KVQ_ERR_INVALID_ARG;
+  if (!buffers_set(cache)) return KVQ_ERR_INVALID_ARG;
+  if (max_len <= 0) return KVQ_ERR_INVALID_ARG;
+  const Dims d = dims_of(cache->cfg);
+  if (!state_ok(cache, d)) return KVQ_ERR_STATE;
+  for (int64_t b = 0; b < d.B; ++b) {
+    if (seq_lens[b] <= 0 || seq_lens[b] > max_len) return KVQ_ERR_INVALID_ARG;
+  }
+  for (int64_t b = 0; b < d.B; ++b) {
+    if (seq_lens[b] > d.C) return KVQ_ERR_CAPACITY;
+    if (cache->seq_n_quant[b] != 0 || cache->seq_n_resid[b] != 0) return KVQ_ERR_STATE;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const __half* kh = static_cast<const __half*>(k);
+  const __half* vh = static_cast<const __half*>(v);
+  kvq::KiviQuantArgs qa = kivi_quant_args(cache, d);
+  qa.k_src = kh;
+  qa.v_src = vh;
+  qa.src_bh_stride = max_len * d.D;
+  qa.ragged = 1;
+  kvq::CopyTokensArgs ca{};
+  ca.k_src = kh;
+  ca.v_src = vh;
+  ca.src_bh_stride = max_len * d.D;
+  ca.k_dst = static_cast<__half*>(cache->k_resid);
+  ca.v_dst = static_cast<__half*>(cache->v_resid);
+  ca.dst_bh_stride = d.Rcap * d.D;
+  ca.bh_count = int(d.B * d.H);
+  ca.ragged = 1;
+  ca.H = int(d.H);
+  int64_t max_groups = 0, max_resid = 0;
+  for (int64_t b = 0; b < d.B; ++b) {
+    const int64_t nq = prefill_quant_tokens(seq_lens[b], cache->cfg.residual_length, d.G);
+    qa.seq.x[b] = int32_t(nq / d.G);
+    qa.seq.y[b] = 0;
+    ca.seq.x[b] = int32_t(nq);
+    ca.seq.y[b] = int32_t(seq_lens[b] - nq);
+    ca.seq.z[b] = 0;
+    max_groups = std::max(max_groups, nq / d.G);
+    max_resid = std::max(max_resid, seq_lens[b] - nq);
+  }
+  qa.n_groups = int(max_groups);
+  ca.n_tokens = max_resid;
+  if (kvq::launch_kivi_quantize(qa, s) != hipSuccess) return KVQ_ERR_DEVICE;
+  if (kvq::launch_copy_tokens(ca, s) != hipSuccess) return KVQ_ERR_DEVICE;
+  for (int64_t b = 0; b < d.B; ++b) {
+    cache->seq_n_quant[b] = int64_t(ca.seq.x[b]);
+    cache->seq_n_resid[b] = ca.seq.y[b];
+  }
+  return KVQ_OK;
+}
+
+namespace {
+
+// One token per sequence of a ragged KIVI cache; sequences with a full
+// window flush it into their own next groups first.
+kvq_status append_ragged(kvq_cache* cache, const Dims& d, const __half* kh, const __half* vh,
+                         hipStream_t s) {
+  for (int64_t b = 0; b < d.B; ++b)
+    if (cache->seq_n_quant[b] + cache->seq_n_resid[b] >= d.C) return KVQ_ERR_CAPACITY;
+  kvq::KiviQuantArgs qa = kivi_quant_args(cache, d);
+  qa.k_src = static_cast<const __half*>(cache->k_resid);
+  qa.v_src = static_cast<const __half*>(cache->v_resid);
+  qa.src_bh_stride = d.Rcap * d.D;
+  qa.ragged = 1;
+  bool any_flush = false;
+  for (int64_t b = 0; b < d.B; ++b) {
+    const bool full = cache->seq_n_resid[b] == d.Rcap;
+    qa.seq.x[b] = full ? int32_t(d.Rcap / d.G) : 0;
+    qa.seq.y[b] = int32_t(cache->seq_n_quant[b] / d.G);
+    any_flush = any_flush || full;
+  }
+  if (any_flush) {
+    qa.n_groups = int(d.Rcap / d.G);
+    if (kvq::launch_kivi_quantize(qa, s) != hipSuccess) return KVQ_ERR_DEVICE;
+    for (int64_t b = 0; b < d.B; ++b) {
+      if (qa.seq.x[b] > 0) {
+        cache->seq_n_quant[b] += d.Rcap;
+        cache->seq_n_resid[b] = 0;
+      }
+    }
+  }
+  kvq::CopyTokensArgs ca{};
+  ca.k_src = kh;
+  ca.v_src = vh;
+  ca.src_bh_stride = d.D;
+  ca.k_dst = static_cast<__half*>(cache->k_resid);
+  ca.v_dst = static_cast<__half*>(cache->v_resid);
+  ca.dst_bh_stride = d.Rcap * d.D;
+  ca.n_tokens = 1;
+  ca.bh_count = int(d.B * d.H);
+  ca.ragged = 1;
+  ca.H = int(d.H);
+  for (int64_t b = 0; b < d.B; ++b) {
+    ca.seq.x[b] = 0;
+    ca.seq.y[b] = 1;
+    ca.seq.z[b] = cache->seq_n_resid[b];
+  }
+  if (kvq::launch_copy_tokens(ca, s) != hipSuccess) return KVQ_ERR_DEVICE;
+  for (int64_t b = 0; b < d.B; ++b) cache->seq_n_resid[b] += 1;
+  return KVQ_OK;
+}
+
+}  // namespace
+
 kvq_status kvq_append_token(kvq_cache* cache, const void* k_new, const void* v_new,
                             void* stream) {
   if (cache == nullptr || k_new == nullptr || v_new == nullptr) return KVQ_ERR_INVALID_ARG;
@@ -379,12 +582,13 @@ kvq_status kvq_append_token(kvq_cache* cache, const void* k_new, const void* v_n
   if (!buffers_set(cache)) return KVQ_ERR_INVALID_ARG;
   const Dims d = dims_of(cache->cfg);
   if (!state_ok(cache, d)) return KVQ_ERR_STATE;
-  if (cache->n_quant + cache->n_resid >= d.C) return KVQ_ERR_CAPACITY;
-  if (is_fp8(cache->cfg.format) && cache->n_quant == 0) return KVQ_ERR_STATE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int bh = int(d.B * d.H);
   const __half* kh = static_cast<const __half*>(k_new);
   const __half* vh = static_cast<const __half*>(v_new);
+  if (is_ragged(cache)) return append_ragged(cache, d, kh, vh, s);
+  if (cache->n_quant + cache->n_resid >= d.C) return KVQ_ERR_CAPACITY;
+  if (is_fp8(cache->cfg.format) && cache->n_quant == 0) return KVQ_ERR_STATE;
 
   if (cache->cfg.format == KVQ_FMT_KIVI) {
     if (cache->n_resid == d.Rcap) {   // lazy flush of the full window
@@ -484,7 +688,13 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q, int32_t 
   if (num_q_heads <= 0) return KVQ_ERR_INVALID_ARG;
   if (num_q_heads % cache->cfg.num_kv_heads != 0) return KVQ_ERR_UNSUPPORTED;
   if (!state_ok(cache, dims_of(cache->cfg))) return KVQ_ERR_STATE;
-  if (cache->n_quant + cache->n_resid <= 0) return KVQ_ERR_STATE;
+  const bool ragged = is_ragged(cache);
+  if (ragged) {
+    for (int32_t b = 0; b < cache->cfg.batch; ++b)
+      if (cache->seq_n_quant[b] + cache->seq_n_resid[b] <= 0) return KVQ_ERR_STATE;
+  } else if (cache->n_quant + cache->n_resid <= 0) {
+    return KVQ_ERR_STATE;
+  }
   const size_t need = kvq_decode_workspace_bytes(&cache->cfg, num_q_heads);
   if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
     return KVQ_ERR_WORKSPACE;
@@ -502,8 +712,9 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q, int32_t 
   a.vbits = int(d.vbits);
   a.nvs = int(d.nvs);
   a.qfp8 = is_fp8(cache->cfg.format) && cache->cfg.fp8_attention ? 1 : 0;
-  const Plan p = make_plan(d, nq, cache->n_quant, n_win,
-                           int64_t(kvq::decode_resident_workgroups(a)) * KVQ_SPLIT_ROUNDS);
+  const int64_t target = int64_t(kvq::decode_resident_workgroups(a)) * KVQ_SPLIT_ROUNDS;
+  const Plan p = ragged ? make_plan_ragged(d, nq, cache, target)
+                        : make_plan(d, nq, cache->n_quant, n_win, target);
   if (p.n_split > max_splits(d, nq)) return KVQ_ERR_WORKSPACE;
 
   a.B = int(d.B);
@@ -532,6 +743,13 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q, int32_t 
   a.n_split_main = p.n_split_main;
   a.n_split = p.n_split;
   a.win_split = p.win_split;
+  if (ragged) {
+    a.ragged = 1;
+    for (int64_t b = 0; b < d.B; ++b) {
+      a.seq.x[b] = int32_t(cache->seq_n_quant[b] / kGroup);
+      a.seq.y[b] = cache->seq_n_resid[b];
+    }
+  }
   a.q = q;
   a.out = out;
   a.ws = static_cast<float*>(workspace);
@@ -565,11 +783,20 @@ int64_t kvq_decode_bytes(const kvq_cache* cache, int32_t num_q_heads) {
   const int64_t bh = d.B * d.H;
   const int64_t nq = cache->n_quant;
   if (cache->cfg.format == KVQ_FMT_KIVI) {
-    const int64_t code_bytes = nq * d.D * (d.bits + d.vbits) / 8;   // K and V codes
-    const int64_t k_meta = (nq / d.G) * d.D * 2 * 4;        // fp32 s, z per channel
-    const int64_t v_meta = nq * 2 * 4 * d.nvs;              // fp32 s, z per token (run)
-    const int64_t window = 2 * int64_t(cache->n_resid) * d.D * 2;
-    return bh * (code_bytes + k_meta + v_meta + window);
+    // per (b, h) with nq grouped and nr window tokens
+    auto per_bh = [&](int64_t q, int64_t nr) {
+      const int64_t code_bytes = q * d.D * (d.bits + d.vbits) / 8;   // K and V codes
+      const int64_t k_meta = (q / d.G) * d.D * 2 * 4;        // fp32 s, z per channel
+      const int64_t v_meta = q * 2 * 4 * d.nvs;              // fp32 s, z per token (run)
+      const int64_t window = 2 * nr * d.D * 2;
+      return code_bytes + k_meta + v_meta + window;
+    };
+    if (is_ragged(cache)) {
+      int64_t sum = 0;
+      for (int64_t b = 0; b < d.B; ++b) sum += per_bh(cache->seq_n_quant[b], cache->seq_n_resid[b]);
+      return d.H * sum;
+    }
+    return bh * per_bh(nq, cache->n_resid);
   }
   if (is_fp8(cache->cfg.format)) return 2 * bh * nq * d.D + 2 * 4 * fp8_scale_rows(cache->cfg);
   return 2 * bh * nq * d.D * 2;

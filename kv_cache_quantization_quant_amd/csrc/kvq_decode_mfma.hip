@@ -577,10 +577,10 @@ __device__ __forceinline__ void group_values(const VLoad& V, WaveAccT<NVS>& W,
 template <int NVS>
 __device__ __forceinline__ void process_window_tile(const DecodeArgs& a, WaveAccT<NVS>& W, int bh,
                                                     int64_t tile, const u32x4 (&bqw)[4],
-                                                    int r, int u, bool low) {
+                                                    int r, int u, bool low, int n_win) {
   const __half* kw = a.k_win + (int64_t(bh) * a.win_cap + tile * kGroup) * kHeadDim;
   const __half* vwp = a.v_win + (int64_t(bh) * a.win_cap + tile * kGroup) * kHeadDim;
-  const int n_in = int(min<int64_t>(kGroup, a.n_win - tile * kGroup));
+  const int n_in = int(min<int64_t>(kGroup, n_win - tile * kGroup));
   f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
   for (int sl = 0; sl < 4; ++sl) {
@@ -640,7 +640,7 @@ __device__ __forceinline__ void process_window_tile(const DecodeArgs& a, WaveAcc
 template <int NVS>
 __device__ __forceinline__ void run_window(const DecodeArgs& a, WaveAccT<NVS>& W, int bh, int b,
                                            int hq0, int nh, int hs, int r, int u, bool low,
-                                           int wave) {
+                                           int wave, int n_win) {
   // the FP16 window: q·log2e/√D as fp16 high/low terms, channel 32s + 8u + j
   u32x4 bqw[4];
   {
@@ -661,9 +661,9 @@ __device__ __forceinline__ void run_window(const DecodeArgs& a, WaveAccT<NVS>& W
       bqw[sl] = u32x4{d[0], d[1], d[2], d[3]};
     }
   }
-  const int64_t n_tiles = (a.n_win + kGroup - 1) / kGroup;
+  const int64_t n_tiles = (n_win + kGroup - 1) / kGroup;
   for (int64_t tile = wave; tile < n_tiles; tile += kWaves)
-    process_window_tile(a, W, bh, tile, bqw, r, u, low);
+    process_window_tile(a, W, bh, tile, bqw, r, u, low, n_win);
 }
 
 // Asynchronous global→LDS copies (global_load_lds): lane i's 16 or 4 bytes
@@ -932,6 +932,19 @@ __attribute__((amdgpu_waves_per_eu((BITS == 2 && VB == 2 && NVS == 1) ? KVQ_DECO
     W.cones[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // grouped tokens, window tokens and the split that runs the window: the
+  // launch's, or this sequence's in a ragged batch (its window joins its
+  // last main split, or split 0 when it has no grouped tiles)
+  int64_t n_main = a.n_main;
+  int n_win = a.n_win;
+  int win_split = a.win_split;
+  if (a.ragged) {
+    const int tiles = a.seq.x[b];
+    n_main = int64_t(tiles) * kGroup;
+    n_win = a.seq.y[b];
+    win_split = n_win <= 0 ? -1 : tiles > 0 ? (tiles + a.tiles_per_split - 1) / a.tiles_per_split - 1 : 0;
+  }
+
   if (split < a.n_split_main) {
     // q_d·log2e/√D of this lane's channels 32u + 16·part + c
     float q16[16];
@@ -950,7 +963,7 @@ __attribute__((amdgpu_waves_per_eu((BITS == 2 && VB == 2 && NVS == 1) ? KVQ_DECO
         q16[4 * c4 + 3] = x.w * qs;
       }
     }
-    const int64_t n_groups = a.n_main / kGroup;
+    const int64_t n_groups = n_main / kGroup;
     const int64_t g0 = int64_t(split) * a.tiles_per_split;
     const int64_t g1 = min(g0 + int64_t(a.tiles_per_split), n_groups);
     // this wavefront's groups: g0 + wave + kWaves·i, i < n_mine
@@ -972,7 +985,7 @@ __attribute__((amdgpu_waves_per_eu((BITS == 2 && VB == 2 && NVS == 1) ? KVQ_DECO
     // the last main split of (b, h) also takes the window, while the first
     // copies are in flight (its loads are ordinary ones, older than every
     // copy waited on below, so the counted waits still hold)
-    if (split == a.win_split) run_window(a, W, bh, b, hq0, nh, hs, r, u, low, wave);
+    if (split == win_split) run_window(a, W, bh, b, hq0, nh, hs, r, u, low, wave, n_win);
     if (n_mine > 0) {
       float sc[4];
       if (kAhead < n_mine) {
@@ -1020,7 +1033,7 @@ __attribute__((amdgpu_waves_per_eu((BITS == 2 && VB == 2 && NVS == 1) ? KVQ_DECO
       group_values<VB, NVS>(V, W, bp_prev, vsh, vm0, vm1, magic, magic32);
     }
   } else {
-    run_window(a, W, bh, b, hq0, nh, hs, r, u, low, wave);
+    run_window(a, W, bh, b, hq0, nh, hs, r, u, low, wave, n_win);
   }
 
   wave_epilogue_and_merge(a, W, &ring[0][0][0], sizeof(ring[0]), wave, lane, hs, u, low, tid,

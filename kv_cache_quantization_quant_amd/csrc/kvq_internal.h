@@ -12,6 +12,15 @@ namespace kvq {
 constexpr int kHeadDim = 128;   // D
 constexpr int kGroup = 32;      // tokens per decode tile and per KIVI V code tile (the KIVI group when G = 32)
 
+// Per-sequence counts of a ragged batch, passed by value with the launch
+// (sequence b = bh / H); the meaning of x, y, z is stated by each user.
+constexpr int kMaxRagged = 128;
+struct RaggedTable {
+  int32_t x[kMaxRagged];
+  int32_t y[kMaxRagged];
+  int32_t z[kMaxRagged];
+};
+
 // KIVI quantization of whole groups. Source tokens [0, n_groups·G) of each
 // (b, h) block of an fp16 [B·H][src_tokens][D] tensor are quantized into the
 // cache groups [g0, g0 + n_groups).
@@ -34,6 +43,11 @@ struct KiviQuantArgs {
   float* k_zero;
   float* v_scale;         // [B·H][NG·G][nvs]
   float* v_zero;
+  // ragged batch: sequence b quantizes groups [0, seq.x[b]) of its source
+  // into cache groups [seq.y[b], seq.y[b] + seq.x[b]) (n_groups, g0 unused)
+  int ragged;
+  int H;
+  RaggedTable seq;
 };
 
 // Strided copy of `n_tokens` tokens of K and V (fp16, D channels each) from
@@ -48,6 +62,11 @@ struct CopyTokensArgs {
   int64_t dst_t0;
   int64_t n_tokens;
   int bh_count;
+  // ragged batch: sequence b copies seq.y[b] tokens from source token
+  // seq.x[b] to cache token seq.z[b] (n_tokens: the largest count)
+  int ragged;
+  int H;
+  RaggedTable seq;
 };
 
 // FP8 code formats (the cache's V tiles and K rows).
@@ -134,6 +153,10 @@ struct DecodeArgs {
   float* out;             // [B][Hq][D]
   float* ws;              // [B][Hq][n_split][D + 2]
   float qscale;           // log2(e) / sqrt(D)
+  // ragged KIVI batch: sequence b has seq.x[b] 32-token tiles in its grouped
+  // region and seq.y[b] window tokens (n_main, n_win, win_split unused)
+  int ragged;
+  RaggedTable seq;
 };
 
 hipError_t launch_kivi_quantize(const KiviQuantArgs& a, hipStream_t s);

@@ -133,7 +133,12 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
   const int tid = threadIdx.x;
   const int t = tid >> 3;
   const int j = tid & 7;
-  const int64_t gg = a.g0 + g;             // cache group
+  int64_t gg = a.g0 + g;                   // cache group
+  if (a.ragged) {                          // block-uniform: the whole block leaves
+    const int b = bh / a.H;
+    if (g >= a.seq.x[b]) return;
+    gg = int64_t(a.seq.y[b]) + g;
+  }
   const int64_t CT = a.NG * G;
 
   uint4 kr[NS][2];                         // the thread's K values of each sub-tile
@@ -306,11 +311,18 @@ __global__ __launch_bounds__(kThreads) void copy_tokens_kernel(CopyTokensArgs a)
   const int64_t idx = int64_t(blockIdx.x) * kThreads + threadIdx.x;  // uint4 index
   const int bh = blockIdx.y;
   constexpr int kChunks = kHeadDim / 8;                                // uint4 per token
-  if (idx >= a.n_tokens * kChunks) return;
+  int64_t n = a.n_tokens, s0 = 0, d0 = a.dst_t0;
+  if (a.ragged) {
+    const int b = bh / a.H;
+    s0 = a.seq.x[b];
+    n = a.seq.y[b];
+    d0 = a.seq.z[b];
+  }
+  if (idx >= n * kChunks) return;
   const int64_t tok = idx / kChunks;
   const int c = int(idx % kChunks);
-  const int64_t s = bh * a.src_bh_stride + tok * kHeadDim + c * 8;
-  const int64_t d = bh * a.dst_bh_stride + (a.dst_t0 + tok) * kHeadDim + c * 8;
+  const int64_t s = bh * a.src_bh_stride + (s0 + tok) * kHeadDim + c * 8;
+  const int64_t d = bh * a.dst_bh_stride + (d0 + tok) * kHeadDim + c * 8;
   *reinterpret_cast<uint4*>(a.k_dst + d) = *reinterpret_cast<const uint4*>(a.k_src + s);
   if (a.v_dst != nullptr)
     *reinterpret_cast<uint4*>(a.v_dst + d) = *reinterpret_cast<const uint4*>(a.v_src + s);

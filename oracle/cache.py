@@ -144,6 +144,51 @@ class KiviCache:
         return attention.decode_attention(q, Kh, Vh)
 
 
+class RaggedKiviCache:
+    """A ragged batch: B sequences of their own lengths sharing one cache
+    layout. Reading (the pages state KIVI per sequence and never mix
+    sequences): each sequence is quantized, flushed and attended exactly as a
+    batch of one holding only its own tokens — its groups start at its token
+    0 and its window holds its own newest tokens — so sequence b of the
+    ragged cache is KiviCache(1, ...) run on that sequence alone. The arrays
+    below are those per-sequence caches stacked along the batch axis, the
+    layout of the device buffers."""
+
+    def __init__(self, batch, num_kv_heads, head_dim, bits, group, residual, capacity,
+                 v_bits=None, v_group_channels=None):
+        self.B = batch
+        self.seqs = [KiviCache(1, num_kv_heads, head_dim, bits, group, residual, capacity,
+                               v_bits=v_bits, v_group_channels=v_group_channels)
+                     for _ in range(batch)]
+
+    @property
+    def seq_n_quant(self):
+        return [c.n_quant for c in self.seqs]
+
+    @property
+    def seq_n_resid(self):
+        return [c.n_resid for c in self.seqs]
+
+    def prefill(self, k, v, seq_lens):
+        """k, v: fp16 [B, H, max_len, D]; sequence b is its first seq_lens[b]
+        tokens (the rest is padding, never read)."""
+        for b, c in enumerate(self.seqs):
+            S = int(seq_lens[b])
+            c.prefill(k[b:b + 1, :, :S], v[b:b + 1, :, :S])
+
+    def append(self, k1, v1):
+        """k1, v1: fp16 [B, H, D], one token per sequence."""
+        for b, c in enumerate(self.seqs):
+            c.append(k1[b:b + 1], v1[b:b + 1])
+
+    def array(self, name):
+        return np.concatenate([getattr(c, name) for c in self.seqs], axis=0)
+
+    def attention(self, q):
+        """q: fp32 [B, Hq, D] → fp64 [B, Hq, D], each row over its own sequence."""
+        return np.concatenate([c.attention(q[b:b + 1]) for b, c in enumerate(self.seqs)], axis=0)
+
+
 TILE = 32   # tokens per V tile of the FP8 / FP16 layouts
 
 

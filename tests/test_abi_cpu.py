@@ -60,7 +60,7 @@ def test_struct_sizes_match_header(tmp_path):
         assert int(got[st]) == ctypes.sizeof(cls), st
         for f in fields[st]:
             assert int(got[f"{st}.{f}"]) == getattr(cls, f).offset, (st, f)
-    assert int(got["abi"]) == kq.kvq_abi_version() == kq.ABI_VERSION == 5
+    assert int(got["abi"]) == kq.kvq_abi_version() == kq.ABI_VERSION == 6
 
 
 def test_status_strings():
@@ -324,3 +324,72 @@ def test_build_rejects_scratch_kernels():
     ])
     assert b._scratch_kernels(remarks) == ["_Z3onev (16 bytes/lane)"]
     assert b._scratch_kernels("") == []
+
+
+def _ragged_host_cache(cfg, nq=None, nr=None):
+    c = _host_cache(cfg)
+    B = cfg.batch
+    nqa = (ctypes.c_int64 * B)(*(nq or [0] * B))
+    nra = (ctypes.c_int32 * B)(*(nr or [0] * B))
+    c.seq_n_quant = ctypes.cast(nqa, ctypes.POINTER(ctypes.c_int64))
+    c.seq_n_resid = ctypes.cast(nra, ctypes.POINTER(ctypes.c_int32))
+    return c, nqa, nra
+
+
+def test_ragged_errors_before_any_launch():
+    """Ragged-batch validation (no launch happens: every call fails first)."""
+    P = 0x100000
+    cfg = kq.make_config("kivi", batch=3, num_kv_heads=2, capacity=512)
+    lens = (ctypes.c_int64 * 3)(300, 40, 129)
+    c, nqa, nra = _ragged_host_cache(cfg)
+    # not ragged / wrong format / too large a batch
+    plain = _host_cache(cfg)
+    assert kq.kvq_prefill_quantize_ragged(plain, P, P, 300, lens, None) == kq.KVQ_ERR_INVALID_ARG
+    fp8 = _host_cache(kq.make_config("fp8", batch=3, capacity=512))
+    assert kq.kvq_prefill_quantize_ragged(fp8, P, P, 300, lens, None) == kq.KVQ_ERR_UNSUPPORTED
+    big, _, _ = _ragged_host_cache(kq.make_config("kivi", batch=129, capacity=256))
+    big_lens = (ctypes.c_int64 * 129)(*([10] * 129))
+    assert kq.kvq_prefill_quantize_ragged(big, P, P, 10, big_lens, None) == kq.KVQ_ERR_UNSUPPORTED
+    # lengths
+    for bad in ([0, 40, 129], [301, 40, 129]):
+        bl = (ctypes.c_int64 * 3)(*bad)
+        assert kq.kvq_prefill_quantize_ragged(c, P, P, 300, bl, None) == kq.KVQ_ERR_INVALID_ARG
+    over = (ctypes.c_int64 * 3)(513, 40, 129)
+    assert kq.kvq_prefill_quantize_ragged(c, P, P, 600, over, None) == kq.KVQ_ERR_CAPACITY
+    assert kq.kvq_prefill_quantize_ragged(c, P + 4, P, 300, lens, None) == kq.KVQ_ERR_INVALID_ARG
+    # uniform prefill refuses a ragged cache
+    assert kq.kvq_prefill_quantize(c, P, P, 300, None) == kq.KVQ_ERR_INVALID_ARG
+    # a non-empty sequence: STATE
+    c2, _, _ = _ragged_host_cache(cfg, nq=[0, 32, 0], nr=[0, 8, 0])
+    assert kq.kvq_prefill_quantize_ragged(c2, P, P, 300, lens, None) == kq.KVQ_ERR_STATE
+    # unreachable per-sequence levels are rejected everywhere
+    c3, _, _ = _ragged_host_cache(cfg, nq=[33, 0, 0], nr=[0, 1, 1])
+    need = kq.kvq_decode_workspace_bytes(cfg, 4)
+    assert kq.kvq_decode_attention(c3, P, 4, P, P, need, None) == kq.KVQ_ERR_STATE
+    assert kq.kvq_append_token(c3, P, P, None) == kq.KVQ_ERR_STATE
+    assert kq.kvq_decode_bytes(c3, 4) == -1
+    c4, _, _ = _ragged_host_cache(cfg, nq=[0, 0, 0], nr=[0, 129, 0])
+    assert kq.kvq_append_token(c4, P, P, None) == kq.KVQ_ERR_STATE
+    # only one of the two arrays set
+    c5 = _host_cache(cfg)
+    c5.seq_n_quant = ctypes.cast(nqa, ctypes.POINTER(ctypes.c_int64))
+    assert kq.kvq_append_token(c5, P, P, None) == kq.KVQ_ERR_STATE
+    # an empty sequence cannot be attended; a full one cannot append
+    c6, _, _ = _ragged_host_cache(cfg, nq=[64, 0, 32], nr=[3, 0, 5])
+    assert kq.kvq_decode_attention(c6, P, 4, P, P, need, None) == kq.KVQ_ERR_STATE
+    c7, _, _ = _ragged_host_cache(cfg, nq=[384, 0, 32], nr=[128, 1, 5])
+    assert kq.kvq_append_token(c7, P, P, None) == kq.KVQ_ERR_CAPACITY
+    # reset clears every sequence
+    c8, nq8, nr8 = _ragged_host_cache(cfg, nq=[64, 32, 0], nr=[3, 7, 9])
+    assert kq.kvq_cache_reset(c8) == 0
+    assert list(nq8) == [0, 0, 0] and list(nr8) == [0, 0, 0]
+
+
+def test_ragged_decode_bytes_sum_sequences():
+    """A ragged cache's algorithmic bytes are the sum of its sequences' (the
+    oracle byte model of a batch of one per sequence)."""
+    cfg = kq.make_config("kivi", batch=3, num_kv_heads=8, capacity=33024)
+    nq, nr = [32640, 4096, 0], [128, 17, 99]
+    c, _, _ = _ragged_host_cache(cfg, nq=nq, nr=nr)
+    want = sum(bytes_model.decode_bytes_kivi(1, 8, 128, 2, 32, q, r) for q, r in zip(nq, nr))
+    assert kq.kvq_decode_bytes(c, 64) == want

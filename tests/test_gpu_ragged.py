@@ -1,0 +1,145 @@
+"""Parity of ragged KIVI batches (per-sequence lengths) against the oracle.
+
+The oracle of a ragged batch is one single-sequence cache per sequence
+(oracle.cache.RaggedKiviCache). Bar: every packed code, scale, zero-point and
+window value bit-exact (the whole device buffers, stacked oracle arrays);
+per-sequence fill levels equal; decode attention within max-abs 2e-3 of the
+oracle's fp64 attention over the same dequantized values.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import cache as ocache
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 2e-3
+D = 128
+NAMES = ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero", "k_resid", "v_resid")
+
+
+@pytest.fixture(scope="module")
+def kq():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import kv_cache_quantization_quant_amd as m
+    return m
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _compare(dc, oc):
+    for name in NAMES:
+        g = _np(dc.view(name))
+        o = oc.array(name)
+        if name.endswith("codes"):
+            g = g.view(np.uint32)
+        assert g.shape == o.shape, name
+        assert np.array_equal(g.view(np.uint8), o.view(np.uint8)), name
+    assert dc.seq_n_quant == oc.seq_n_quant
+    assert dc.seq_n_resid == oc.seq_n_resid
+
+
+@pytest.mark.parametrize("G,bits,vbits,gc,R,H,Hq,lens,steps", [
+    (32, 2, 0, 0, 128, 2, 8, [300, 45, 161, 128], 40),     # one sequence all window
+    (64, 4, 2, 0, 64, 1, 4, [500, 63, 200], 70),
+    (32, 2, 0, 0, 0, 2, 2, [97, 1, 32], 35),               # R = 0, a 1-token sequence
+    (32, 2, 0, 0, 128, 1, 1, [10, 20], 3),                  # no grouped tile anywhere
+    (32, 2, 0, 32, 128, 2, 16, [257, 700, 96], 30),         # V scales per 32 channels
+    (128, 2, 4, 0, 128, 2, 8, [1000, 129, 640], 20),
+    (32, 2, 0, 0, 128, 4, 32, [4096, 1000, 3000, 77, 2048, 333], 5),   # many splits
+])
+def test_ragged_prefill_append_decode(kq, G, bits, vbits, gc, R, H, Hq, lens, steps):
+    B = len(lens)
+    Smax = max(lens)
+    C = Smax + steps
+    _say(f"[ragged] G={G} bits={bits} v_bits={vbits} gc={gc} R={R} H={H} Hq={Hq} "
+         f"lens={lens} steps={steps}")
+    k = synth.make_k(B, H, 0, C, D, device="cuda")
+    v = synth.make_v(B, H, 0, C, D, device="cuda")
+    cfg = kq.make_config("kivi", bits=bits, group_size=G, residual_length=R, batch=B,
+                         num_kv_heads=H, capacity=C, v_bits=vbits, v_group_channels=gc)
+    dc = kq.DeviceCache(cfg, ragged=True)
+    oc = ocache.RaggedKiviCache(B, H, D, bits, G, R, C, v_bits=vbits or None,
+                                v_group_channels=gc or None)
+    kp, vp = k[:, :, :Smax].clone(), v[:, :, :Smax].clone()
+    for b, S in enumerate(lens):          # padding the kernels must not read
+        kp[b, :, S:] = 30000.0
+        vp[b, :, S:] = -30000.0
+    dc.prefill_ragged(kp, vp, lens)
+    oc.prefill(_np(kp), _np(vp), lens)
+    torch.cuda.synchronize()
+    _compare(dc, oc)
+    ws = dc.make_workspace(Hq)
+    q = synth.make_q(B, Hq, D, device="cuda")
+    worst = _err(dc.decode(q, workspace=ws), oc.attention(_np(q)))
+    # each sequence's next tokens follow its own last one
+    nxt = list(lens)
+    kn, vn = _np(k), _np(v)
+    for i in range(steps):
+        k1 = torch.stack([k[b, :, nxt[b]] for b in range(B)]).contiguous()
+        v1 = torch.stack([v[b, :, nxt[b]] for b in range(B)]).contiguous()
+        dc.append(k1, v1)
+        oc.append(_np(k1), _np(v1))
+        nxt = [t + 1 for t in nxt]
+        assert dc.seq_n_quant == oc.seq_n_quant and dc.seq_n_resid == oc.seq_n_resid
+        if i % 10 == 9 or i == steps - 1:
+            q = synth.make_q(B, Hq, D, step=i, device="cuda")
+            worst = max(worst, _err(dc.decode(q, workspace=ws), oc.attention(_np(q))))
+    torch.cuda.synchronize()
+    _compare(dc, oc)
+    flushes = [s.flush_steps for s in oc.seqs]
+    _say(f"  worst max abs err {worst:.3e}, flushes per sequence {flushes}")
+    assert worst <= ATOL
+    assert dc.decode_bytes(Hq) == sum(
+        kq.kvq_decode_bytes(_one_seq_cache(kq, cfg, nq, nr), Hq)
+        for nq, nr in zip(oc.seq_n_quant, oc.seq_n_resid))
+
+
+def _err(out, ref):
+    return float(np.max(np.abs(_np(out).astype(np.float64) - ref)))
+
+
+def _one_seq_cache(kq, cfg, nq, nr):
+    """A host-only batch-of-one cache at the given fill levels (for byte counts)."""
+    c1 = kq.make_config("kivi", bits=cfg.bits, group_size=cfg.group_size,
+                        residual_length=cfg.residual_length, batch=1,
+                        num_kv_heads=cfg.num_kv_heads, capacity=cfg.capacity,
+                        v_bits=cfg.v_bits, v_group_channels=cfg.v_group_channels)
+    c = kq.KvqCache()
+    assert kq.kvq_cache_init(c, c1) == 0
+    c.n_quant, c.n_resid = nq, nr
+    return c
+
+
+def test_ragged_equal_lengths_match_uniform(kq):
+    """Equal lengths: the ragged path gives the uniform path's buffers and
+    outputs bit for bit (same kernels, per-sequence counts all equal)."""
+    B, H, Hq, S, C = 3, 2, 8, 700, 760
+    k = synth.make_k(B, H, 0, C, D, device="cuda")
+    v = synth.make_v(B, H, 0, C, D, device="cuda")
+    cfg = kq.make_config("kivi", batch=B, num_kv_heads=H, capacity=C)
+    rag = kq.DeviceCache(cfg, ragged=True)
+    uni = kq.DeviceCache(cfg)
+    rag.prefill_ragged(k[:, :, :S].contiguous(), v[:, :, :S].contiguous(), [S] * B)
+    uni.prefill(k[:, :, :S].contiguous(), v[:, :, :S].contiguous())
+    for t in range(S, S + 50):
+        rag.append(k[:, :, t].contiguous(), v[:, :, t].contiguous())
+        uni.append(k[:, :, t].contiguous(), v[:, :, t].contiguous())
+    q = synth.make_q(B, Hq, D, device="cuda")
+    a, b = rag.decode(q), uni.decode(q)
+    torch.cuda.synchronize()
+    for name in NAMES:
+        assert torch.equal(rag.view(name), uni.view(name)), name
+    err = float((a - b).abs().max())
+    _say(f"[ragged == uniform] max abs diff {err:.3e}")
+    assert err <= 1e-5
