@@ -231,6 +231,8 @@ def run_extra(torch, kq, synth):
             dict(name="gqa70b_32k", fmt="kivi", kbits=4, vbits=2),
             dict(name="gqa70b_32k", fmt="kivi", kbits=2, vbits=4),
             dict(name="gqa70b_32k", fmt="kivi", v_group_channels=32),
+            # ragged batch: sequence b holds 32768 - 1920·b tokens (32768 .. 3968)
+            dict(name="gqa70b_32k", fmt="kivi", ragged=True),
             dict(name="gqa_128k", fmt="fp16"), dict(name="gqa_128k", fmt="fp8"),
             dict(name="gqa_128k", fmt="fp8", per_head=1), dict(name="gqa_128k", fmt="fp8_e5m2"),
             dict(name="gqa_128k", fmt="fp8", fp8_attention=1),
@@ -252,14 +254,19 @@ def run_extra(torch, kq, synth):
                               synth.make_v(B, H, 0, S, D, device="cuda"))
         k, v = kv_cache[name]
         bits = (kbits or c["bits"]) if fmt == "kivi" else None
+        ragged = item.get("ragged", False)
+        lens = [S - 1920 * b for b in range(B)] if ragged else None
         dc = kq.DeviceCache(kq.make_config(fmt, bits=bits, group_size=G, batch=B,
                                            num_kv_heads=H, capacity=S, v_bits=vbits or 0,
                                            scale_per_head=per_head, fp8_attention=qf8,
-                                           v_group_channels=gc))
+                                           v_group_channels=gc), ragged=ragged)
 
         def prefill():
             dc.reset()
-            dc.prefill(k, v)
+            if ragged:
+                dc.prefill_ragged(k, v, lens)
+            else:
+                dc.prefill(k, v)
         prefill()
         pre = statistics.median(time_launches(torch, prefill, 3, scrub))
         q = synth.make_q(B, Hq, D, device="cuda")
@@ -269,7 +276,8 @@ def run_extra(torch, kq, synth):
             torch, lambda: dc.decode(q, out=o, workspace=ws), 10, scrub))
         key = (f"{name}/{fmt}" + (f"_g{G}" if G != 32 else "") +
                (f"_k{kbits}v{vbits}" if vbits else "") + ("_per_head" if per_head else "") +
-               ("_fp8_attention" if qf8 else "") + (f"_vgc{gc}" if gc else ""))
+               ("_fp8_attention" if qf8 else "") + (f"_vgc{gc}" if gc else "") +
+               ("_ragged" if ragged else ""))
         if name == "gqa_128k":
             outs[key.split("/")[1]] = o.double().cpu()
         nbytes = dc.decode_bytes(Hq)

@@ -54,8 +54,8 @@
  *   bit widths), v_group_channels ∈ {0, 32}, residual_length a multiple of
  *   group_size (0 allowed);
  *   FP8 (E4M3 or E5M2) bits = 8, scale_per_head ∈ {0, 1} and fp8_attention
- *   ∈ {0, 1}; FP16 bits = 16; num_q_heads a positive multiple of
- *   num_kv_heads.
+ *   ∈ {0, 1}; FP16 bits = 16; deterministic ∈ {0, 1}; num_q_heads a
+ *   positive multiple of num_kv_heads.
  *
  * ---------------------------------------------------------------------------
  * Numerics (bit-exact contract for KIVI codes, scales and zero-points)
@@ -135,7 +135,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 6
+#define KVQ_ABI_VERSION 7
 
 typedef enum {
   KVQ_OK = 0,
@@ -180,6 +180,14 @@ typedef struct {
   int32_t v_group_channels; /* KIVI: 0 = one V scale / zero-point per token;
                               32 = one per token and run of 32 channels
                               (D/32 per token); ignored else                  */
+  int32_t deterministic;   /* 0 or 1. KIVI decode: 0 = the wavefronts of a
+                              split take its 32-token tiles from a shared
+                              counter as they go (fastest; which wavefront
+                              sums which tile varies, so outputs can differ
+                              from run to run in the last bits, always
+                              within the accuracy bound); 1 = a fixed tile
+                              order per wavefront (bitwise identical runs).
+                              FP8 / FP16 decodes are always deterministic.  */
 } kvq_config;
 
 /* Bytes the caller must allocate for each device buffer (0 = unused). */

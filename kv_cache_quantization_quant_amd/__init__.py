@@ -28,7 +28,7 @@ KVQ_ERR_STATE = 4
 KVQ_ERR_DEVICE = 5
 KVQ_ERR_WORKSPACE = 6
 
-ABI_VERSION = 6        # KVQ_ABI_VERSION of include/kvq.h
+ABI_VERSION = 7        # KVQ_ABI_VERSION of include/kvq.h
 
 KVQ_FMT_FP16 = 0
 KVQ_FMT_FP8_E4M3 = 1
@@ -45,7 +45,7 @@ class KvqConfig(ctypes.Structure):
                 ("residual_length", c_int32), ("batch", c_int32),
                 ("num_kv_heads", c_int32), ("head_dim", c_int32), ("capacity", c_int32),
                 ("v_bits", c_int32), ("scale_per_head", c_int32), ("fp8_attention", c_int32),
-                ("v_group_channels", c_int32)]
+                ("v_group_channels", c_int32), ("deterministic", c_int32)]
 
 
 class KvqLayout(ctypes.Structure):
@@ -185,16 +185,18 @@ def make_config(fmt: str = "kivi", bits: int | None = None, group_size: int = 32
                 residual_length: int = 128, batch: int = 1, num_kv_heads: int = 1,
                 head_dim: int = 128, capacity: int = 256, v_bits: int = 0,
                 scale_per_head: int = 0, fp8_attention: int = 0,
-                v_group_channels: int = 0) -> KvqConfig:
+                v_group_channels: int = 0, deterministic: int = 0) -> KvqConfig:
     """v_bits: KIVI V bit width (0 = same as bits); scale_per_head: FP8 scales
     per KV head (1) or per tensor (0); fp8_attention: FP8 decode with the
     query quantized to E4M3 (1); v_group_channels: KIVI V scales per run of
-    32 channels (32) or per token (0)."""
+    32 channels (32) or per token (0); deterministic: KIVI decode with a fixed
+    tile order per wavefront (1, bitwise reproducible) or tiles shared as the
+    wavefronts go (0, fastest)."""
     if bits is None:
         bits = {"kivi": 2, "fp8": 8, "fp8_e5m2": 8, "fp16": 16}[fmt]
     return KvqConfig(FORMATS[fmt], bits, group_size, residual_length, batch, num_kv_heads,
                      head_dim, capacity, v_bits, scale_per_head, fp8_attention,
-                     v_group_channels)
+                     v_group_channels, deterministic)
 
 
 def quantize_query_fp8(q: torch.Tensor, stream=None) -> tuple[torch.Tensor, torch.Tensor]:

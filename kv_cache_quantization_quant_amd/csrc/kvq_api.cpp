@@ -34,14 +34,14 @@ using kvq::kHeadDim;
 #define KVQ_SPLIT_ROUNDS 1
 #endif
 constexpr int64_t kMaxTargetWorkgroups = 4096;
-// Time of one FP16 window tile in a wavefront, in grouped-region tiles of the
-// same wavefront: the last main split of each (b, h) runs the window too and
-// gets that much less of the grouped region.
+// Time of one FP16 window tile in grouped-region tiles: the last main split
+// of each (b, h) runs the window too and gets that much less of the grouped
+// region (the wavefronts of a split share its tiles as they go, so the
+// window's cost spreads over all of them).
 #ifndef KVQ_WINDOW_TILE_COST
-#define KVQ_WINDOW_TILE_COST 8
+#define KVQ_WINDOW_TILE_COST 4
 #endif
 constexpr int64_t kFallbackWorkgroups = 2048;
-constexpr int64_t kWaves = 4;              // wavefronts per decode workgroup
 constexpr int64_t kMinTilesPerSplit = 4;   // one tile per wavefront at least
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -58,6 +58,7 @@ kvq_status validate_config(const kvq_config* c) {
   if (c->batch <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0 || c->capacity <= 0)
     return KVQ_ERR_INVALID_ARG;
   if (c->head_dim != kHeadDim) return KVQ_ERR_UNSUPPORTED;
+  if (c->deterministic != 0 && c->deterministic != 1) return KVQ_ERR_UNSUPPORTED;
   switch (c->format) {
     case KVQ_FMT_KIVI:
       if (c->group_size <= 0 || c->residual_length < 0) return KVQ_ERR_INVALID_ARG;
@@ -228,8 +229,10 @@ Plan make_plan(const Dims& d, int nq, int64_t n_main, int n_win, int64_t target)
   // a non-empty window joins the last main split of (b, h) when there is one
   const bool fold = n_win > 0 && tiles > 0;
   const int64_t win_cost =
-      fold ? kWaves * KVQ_WINDOW_TILE_COST * ceil_div(ceil_div(n_win, kGroup), kWaves) : 0;
+      fold ? KVQ_WINDOW_TILE_COST * ceil_div(n_win, kGroup) : 0;
   int64_t tps = ceil_div((tiles + win_cost) * x, target);
+  // no more splits per (b, h) than whole rounds of the target allow
+  if (x <= target && tiles > 0) tps = std::max(tps, ceil_div(tiles, target / x));
   if (tps < kMinTilesPerSplit) tps = kMinTilesPerSplit;
   p.tiles_per_split = int(tps);
   p.n_split_main = int(ceil_div(tiles, tps));
@@ -272,12 +275,33 @@ Plan make_plan_ragged(const Dims& d, int nq, const kvq_cache* c, int64_t target)
     const int64_t n_win = c->seq_n_resid[b];
     total += tiles;
     if (n_win > 0 && tiles > 0)
-      total += kWaves * KVQ_WINDOW_TILE_COST * ceil_div(ceil_div(n_win, kGroup), kWaves);
+      total += KVQ_WINDOW_TILE_COST * ceil_div(n_win, kGroup);
     max_tiles = std::max(max_tiles, tiles);
   }
   int64_t tps = ceil_div(total * d.H * p.nchunk, target);
   tps = std::max(tps, ceil_div(max_tiles, max_splits(d, nq) - 1));
   if (tps < kMinTilesPerSplit) tps = kMinTilesPerSplit;
+  // Each sequence's last split is a partial one, so the populated blocks can
+  // outnumber the resident slots at this size: take the smallest size (binary
+  // search; the count only falls as the size grows) whose populated blocks
+  // fit in one round, when one exists.
+  auto populated = [&](int64_t t) {
+    int64_t n = 0;
+    for (int64_t b = 0; b < d.B; ++b) {
+      const int64_t tiles = c->seq_n_quant[b] / kGroup;
+      n += tiles > 0 ? ceil_div(tiles, t) : 1;
+    }
+    return n * d.H * p.nchunk;
+  };
+  if (max_tiles > tps && populated(tps) > target && populated(max_tiles) <= target) {
+    int64_t lo = tps, hi = max_tiles;          // populated(lo) > target >= populated(hi)
+    while (hi - lo > 1) {
+      const int64_t mid = lo + (hi - lo) / 2;
+      if (populated(mid) <= target) hi = mid;
+      else lo = mid;
+    }
+    tps = hi;
+  }
   p.tiles_per_split = int(tps);
   p.n_split_main = int(ceil_div(max_tiles, tps));
   p.n_split = std::max(p.n_split_main, 1);
@@ -743,6 +767,7 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q, int32_t 
   a.n_split_main = p.n_split_main;
   a.n_split = p.n_split;
   a.win_split = p.win_split;
+  a.fixed_order = cache->cfg.deterministic;
   if (ragged) {
     a.ragged = 1;
     for (int64_t b = 0; b < d.B; ++b) {

@@ -636,8 +636,8 @@ __device__ __forceinline__ void process_window_tile(const DecodeArgs& a, WaveAcc
   }
 }
 
-// The FP16 window tiles of (b, h): tile t goes to wavefront t % kWaves.
-template <int NVS>
+// The FP16 window tiles of (b, h): tile t goes to wavefront t % NW.
+template <int NVS, int NW = kWaves>
 __device__ __forceinline__ void run_window(const DecodeArgs& a, WaveAccT<NVS>& W, int bh, int b,
                                            int hq0, int nh, int hs, int r, int u, bool low,
                                            int wave, int n_win) {
@@ -662,7 +662,7 @@ __device__ __forceinline__ void run_window(const DecodeArgs& a, WaveAccT<NVS>& W
     }
   }
   const int64_t n_tiles = (n_win + kGroup - 1) / kGroup;
-  for (int64_t tile = wave; tile < n_tiles; tile += kWaves)
+  for (int64_t tile = wave; tile < n_tiles; tile += NW)
     process_window_tile(a, W, bh, tile, bqw, r, u, low, n_win);
 }
 
@@ -686,7 +686,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // high + low columns, times oscale; then the four wave states are merged
 // through LDS (each wave's results go to the start of its own ring region,
 // `wave_stride` bytes apart) into this split's partial (o[D], m, l).
-template <int NVS>
+template <int NVS, int NW = kWaves>
 __device__ __forceinline__ void wave_epilogue_and_merge(const DecodeArgs& a, const WaveAccT<NVS>& W,
                                                         uint8_t* ring, size_t wave_stride,
                                                         int wave, int lane, int hs, int u,
@@ -714,19 +714,19 @@ __device__ __forceinline__ void wave_epilogue_and_merge(const DecodeArgs& a, con
     ml[2 * hs + 1] = l_tot;
   }
   __syncthreads();
-  for (int i = tid; i < nh * kHeadDim; i += kThreads) {
+  for (int i = tid; i < nh * kHeadDim; i += 64 * NW) {
     const int h = i / kHeadDim;
     const int d = i % kHeadDim;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float* mlw = reinterpret_cast<const float*>(ring + w * wave_stride) + 8 * kHeadDim;
       M = fmaxf(M, mlw[2 * h]);
     }
     float O = 0.0f, L = 0.0f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float* mow = reinterpret_cast<const float*>(ring + w * wave_stride);
         const float* mlw = mow + 8 * kHeadDim;
         const float mw = mlw[2 * h];
@@ -744,27 +744,22 @@ __device__ __forceinline__ void wave_epilogue_and_merge(const DecodeArgs& a, con
   }
 }
 
-// Block order of the split kernels: a 1-D grid whose first B·H·chunks·n_split_main
-// blocks are the main-region splits and whose last B·H·chunks blocks (when the
-// window is non-empty) are the window splits, so the short window blocks run
-// after the long ones instead of holding resident slots among them.
+// Block order of the split kernels: a 1-D grid, split-major — block id
+// covers split id / X of (b, h, head chunk) id % X, X = B·H·chunks. All
+// (b, h) of split 0 come first, then split 1, and so on, so the window-only
+// split (index n_split_main, when the window has a split of its own) runs
+// last, and in a ragged batch the splits past a short sequence's end (empty
+// blocks) come after the populated ones instead of holding back the first
+// round of resident workgroups.
 struct BlockCoord {
   int split, bh, chunk;
 };
 __device__ __forceinline__ BlockCoord block_coord(const DecodeArgs& a) {
   const int x = a.B * a.H * (a.nq / a.heads_per_chunk);
   const int id = int(blockIdx.x);
-  const int n_main_blocks = a.n_split_main * x;
-  int split, rest;
-  if (id < n_main_blocks) {
-    split = id % a.n_split_main;
-    rest = id / a.n_split_main;
-  } else {
-    split = a.n_split_main;
-    rest = id - n_main_blocks;
-  }
+  const int rest = id % x;
   BlockCoord c;
-  c.split = split;
+  c.split = id / x;
   c.bh = rest % (a.B * a.H);
   c.chunk = rest / (a.B * a.H);
   return c;
@@ -800,18 +795,6 @@ __device__ __forceinline__ GroupSrc group_src(const DecodeArgs& a, int bh, int64
   P.vs = reinterpret_cast<const uint8_t*>(a.v_scale) + vg - (S::kVsz - S::kSecond);
   P.vz = reinterpret_cast<const uint8_t*>(a.v_zero) + vg - (S::kVsz - S::kSecond);
   return P;
-}
-// the same wavefront's next tile, kWaves tiles later (kWaves >> gshift K
-// scale groups later: kWaves·32 is a multiple of every G)
-template <int BITS, int VB, int NVS>
-__device__ __forceinline__ void advance(GroupSrc& P, int gshift) {
-  using S = Stage<BITS, VB, NVS>;
-  P.kc += int64_t(kWaves) * S::kKBytes;
-  P.vc += int64_t(kWaves) * S::kVBytes;
-  P.ks += int64_t(kWaves >> gshift) * kHeadDim * 4;
-  P.kz += int64_t(kWaves >> gshift) * kHeadDim * 4;
-  P.vs += int64_t(kWaves) * kGroup * 4 * NVS;
-  P.vz += int64_t(kWaves) * kGroup * 4 * NVS;
 }
 
 // Copies of one group into stage st: K codes (block 1, M0 = st), then V
@@ -889,12 +872,41 @@ __device__ __forceinline__ void wait_groups(int ahead) {
   else wait_vmem<0>();
 }
 
+// Wavefronts per SIMD each KIVI instance's registers allow, and its
+// workgroup size. The wavefronts of a workgroup take the split's 32-token
+// tiles from one LDS counter, so however the SIMDs share their issue slots
+// between them (older wavefronts go first), they all run out of tiles within
+// about one tile of each other; with a fixed share per wavefront, or per
+// workgroup among several workgroups on a unit, the favoured ones finish
+// early and leave their SIMDs one wavefront deep for the rest of the launch
+// (measured: three equal workgroups per unit ended at 46, 67 and 88 µs of a
+// 91 µs launch).
 template <int BITS, int VB, int NVS>
-__global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu((BITS == 2 && VB == 2 && NVS == 1) ? KVQ_DECODE_WAVES_PER_SIMD : 2))) void kivi_mfma_split_kernel(
+constexpr int kivi_waves_per_simd() {
+  return (BITS == 2 && VB == 2 && NVS == 1) ? KVQ_DECODE_WAVES_PER_SIMD : 2;
+}
+// The 2-bit instance holds three wavefronts per SIMD, the whole unit in one
+// workgroup; the others keep four-wavefront workgroups (two per unit), since
+// a unit-sized workgroup of theirs leaves the unit idle between workgroups
+// when a launch has more (b, h) blocks than units.
+#ifndef KVQ_KIVI_UNIT_WORKGROUP
+#define KVQ_KIVI_UNIT_WORKGROUP 1
+#endif
+template <int BITS, int VB, int NVS>
+constexpr int kivi_waves() {
+  return (KVQ_KIVI_UNIT_WORKGROUP && BITS == 2 && VB == 2 && NVS == 1)
+             ? 4 * kivi_waves_per_simd<BITS, VB, NVS>()
+             : 4;
+}
+
+template <int BITS, int VB, int NVS>
+__global__ __launch_bounds__((64 * kivi_waves<BITS, VB, NVS>()))
+__attribute__((amdgpu_waves_per_eu((kivi_waves_per_simd<BITS, VB, NVS>())))) void kivi_mfma_split_kernel(
     DecodeArgs a) {
   using S = Stage<BITS, VB, NVS>;
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][S::kDepth][S::kBytes];
+  constexpr int NW = kivi_waves<BITS, VB, NVS>();
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NW][S::kDepth][S::kBytes];
+  __shared__ uint32_t next_tile;   // tiles of this split handed out so far
 
   const BlockCoord bc = block_coord(a);
   const int split = bc.split;
@@ -945,6 +957,9 @@ __attribute__((amdgpu_waves_per_eu((BITS == 2 && VB == 2 && NVS == 1) ? KVQ_DECO
     win_split = n_win <= 0 ? -1 : tiles > 0 ? (tiles + a.tiles_per_split - 1) / a.tiles_per_split - 1 : 0;
   }
 
+  if (tid == 0) next_tile = 0;
+  __syncthreads();
+
   if (split < a.n_split_main) {
     // q_d·log2e/√D of this lane's channels 32u + 16·part + c
     float q16[16];
@@ -966,35 +981,57 @@ __attribute__((amdgpu_waves_per_eu((BITS == 2 && VB == 2 && NVS == 1) ? KVQ_DECO
     const int64_t n_groups = n_main / kGroup;
     const int64_t g0 = int64_t(split) * a.tiles_per_split;
     const int64_t g1 = min(g0 + int64_t(a.tiles_per_split), n_groups);
-    // this wavefront's groups: g0 + wave + kWaves·i, i < n_mine
-    const int n_mine = g1 - g0 > wave ? int((g1 - g0 - wave + kWaves - 1) / kWaves) : 0;
-    // Group i of this wavefront is g0 + wave + kWaves·i, in stage i % kDepth.
-    // Loads run kAhead groups ahead; group i + kAhead refills the stage of
-    // group i - 2, whose value products ran in the previous iteration.
+    const uint32_t n_blk = g1 > g0 ? uint32_t(g1 - g0) : 0u;   // tiles of this split
+    // Group i of this wavefront (the i-th tile it takes) sits in stage
+    // i % kDepth. Loads run kAhead groups ahead; group i + kAhead refills the
+    // stage of group i - 2, whose value products ran in the previous
+    // iteration. n_mine, the wavefront's group count, is known once a take
+    // comes back empty (-1 until then).
     constexpr int kAhead = S::kDepth - 2;
     const uint32_t v16 = 16u * lane, h16 = 16u * (lane & 31), h4 = 4u * (lane & 31);
-    GroupSrc P = group_src<BITS, VB, NVS>(a, bh, g0 + wave);
     uint8_t* ring_w = &ring[wave][0][0];
+    // the next tile of the split, or n_blk and above when none is left:
+    // from the shared counter (unit-sized workgroups; four-wavefront ones
+    // share a unit with others, so balancing inside them gains little), or
+    // wave, wave + NW, ... in fixed order
+    constexpr bool kShare = NW > 4;
+    uint32_t taken = 0;
+    auto take = [&]() -> uint32_t {
+      if (!kShare || a.fixed_order) return uint32_t(wave) + uint32_t(NW) * taken++;
+      uint32_t t = 0;
+      if (lane == 0) t = atomicAdd(&next_tile, 1u);
+      return __builtin_amdgcn_readfirstlane(t);
+    };
+    int n_mine = -1;
 #pragma unroll
     for (int j = 0; j < kAhead; ++j) {
-      if (j < n_mine) {
-        issue_group<BITS, VB, NVS>(ring_w + j * S::kBytes, P, v16, h16, h4);
-        advance<BITS, VB, NVS>(P, a.gshift);
+      if (n_mine < 0) {
+        const uint32_t t = take();
+        if (t < n_blk) {
+          issue_group<BITS, VB, NVS>(ring_w + j * S::kBytes, group_src<BITS, VB, NVS>(a, bh, g0 + t),
+                                     v16, h16, h4);
+        } else {
+          n_mine = j;
+        }
       }
     }
     // the last main split of (b, h) also takes the window, while the first
     // copies are in flight (its loads are ordinary ones, older than every
     // copy waited on below, so the counted waits still hold)
-    if (split == win_split) run_window(a, W, bh, b, hq0, nh, hs, r, u, low, wave, n_win);
-    if (n_mine > 0) {
+    if (split == win_split) run_window<NVS, NW>(a, W, bh, b, hq0, nh, hs, r, u, low, wave, n_win);
+    if (n_mine != 0) {
       float sc[4];
-      if (kAhead < n_mine) {
-        issue_group<BITS, VB, NVS>(ring_w + kAhead * S::kBytes, P, v16, h16, h4);
-        advance<BITS, VB, NVS>(P, a.gshift);
-        wait_vmem<kAhead * S::kLoads>();
-      } else {
-        wait_groups<BITS, VB, NVS>(n_mine - 1);
+      if (n_mine < 0) {
+        const uint32_t t = take();
+        if (t < n_blk) {
+          issue_group<BITS, VB, NVS>(ring_w + kAhead * S::kBytes,
+                                     group_src<BITS, VB, NVS>(a, bh, g0 + t), v16, h16, h4);
+          wait_vmem<kAhead * S::kLoads>();
+        } else {
+          n_mine = kAhead;
+        }
       }
+      if (n_mine >= 0) wait_groups<BITS, VB, NVS>(n_mine - 1);
       KLoad<BITS, NVS> K;
       VLoad V;
       load_k<BITS, VB, NVS>(ring_w, r, u, low, K);
@@ -1002,23 +1039,32 @@ __attribute__((amdgpu_waves_per_eu((BITS == 2 && VB == 2 && NVS == 1) ? KVQ_DECO
       u32x4 bp_prev[NVS];
       group_probs<BITS, false, NVS>(W, sc, K.vs, K.vz, bp_prev);
       int i = 1;
-      // steady state: a group is loaded every iteration, one fixed wait
-      for (; i + kAhead < n_mine; ++i) {
+      // steady state: a group is loaded every iteration, one fixed wait,
+      // until the split runs out of tiles; each iteration takes the tile of
+      // the next one, so the counter's round trip overlaps the arithmetic
+      uint32_t t_next = n_mine < 0 ? take() : n_blk;
+      while (n_mine < 0) {
         // the refilled stage was last read two groups ago; its reads are done
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        issue_group<BITS, VB, NVS>(ring_w + ((i + kAhead) % S::kDepth) * S::kBytes, P, v16, h16,
-                                   h4);
-        advance<BITS, VB, NVS>(P, a.gshift);
+        if (t_next >= n_blk) {
+          n_mine = i + kAhead;
+          break;
+        }
+        issue_group<BITS, VB, NVS>(ring_w + ((i + kAhead) % S::kDepth) * S::kBytes,
+                                   group_src<BITS, VB, NVS>(a, bh, g0 + t_next), v16, h16, h4);
         wait_vmem<kAhead * S::kLoads>();
         load_v<BITS, VB, NVS>(ring_w + ((i - 1) % S::kDepth) * S::kBytes, r, u, V);
         load_k<BITS, VB, NVS>(ring_w + (i % S::kDepth) * S::kBytes, r, u, low, K);
+        t_next = take();
         // keep every LDS read of the iteration ahead of the arithmetic
         __builtin_amdgcn_sched_barrier(0);
         group_scores<BITS, NVS>(K, low, q16, low ? 0.0f : W.m_ref, sc);
         group_values<VB, NVS>(V, W, bp_prev, vsh, vm0, vm1, magic, magic32);
         group_probs<BITS, true, NVS>(W, sc, K.vs, K.vz, bp_prev);
+        ++i;
       }
-      // the last kAhead groups: nothing left to load
+      // the last kAhead groups (fewer for a wavefront with fewer groups):
+      // nothing left to load
       for (; i < n_mine; ++i) {
         wait_groups<BITS, VB, NVS>(n_mine - 1 - i);
         load_v<BITS, VB, NVS>(ring_w + ((i - 1) % S::kDepth) * S::kBytes, r, u, V);
@@ -1033,11 +1079,11 @@ __attribute__((amdgpu_waves_per_eu((BITS == 2 && VB == 2 && NVS == 1) ? KVQ_DECO
       group_values<VB, NVS>(V, W, bp_prev, vsh, vm0, vm1, magic, magic32);
     }
   } else {
-    run_window(a, W, bh, b, hq0, nh, hs, r, u, low, wave, n_win);
+    run_window<NVS, NW>(a, W, bh, b, hq0, nh, hs, r, u, low, wave, n_win);
   }
 
-  wave_epilogue_and_merge(a, W, &ring[0][0][0], sizeof(ring[0]), wave, lane, hs, u, low, tid,
-                          b, hq0, nh, split, 1.0f);
+  wave_epilogue_and_merge<NVS, NW>(a, W, &ring[0][0][0], sizeof(ring[0]), wave, lane, hs, u,
+                                   low, tid, b, hq0, nh, split, 1.0f);
 }
 
 // ===================================================================== FP8 / FP16
@@ -1349,13 +1395,13 @@ hipError_t launch_dense_mfma(const DecodeArgs& a, hipStream_t s) {
 template <int NVS>
 static hipError_t launch_kivi_nvs(const DecodeArgs& a, dim3 grid, hipStream_t s) {
   if (a.kbits == 2 && a.vbits == 2) {
-    kivi_mfma_split_kernel<2, 2, NVS><<<grid, kThreads, 0, s>>>(a);
+    kivi_mfma_split_kernel<2, 2, NVS><<<grid, 64 * kivi_waves<2, 2, NVS>(), 0, s>>>(a);
   } else if (a.kbits == 4 && a.vbits == 4) {
-    kivi_mfma_split_kernel<4, 4, NVS><<<grid, kThreads, 0, s>>>(a);
+    kivi_mfma_split_kernel<4, 4, NVS><<<grid, 64 * kivi_waves<4, 4, NVS>(), 0, s>>>(a);
   } else if (a.kbits == 4 && a.vbits == 2) {
-    kivi_mfma_split_kernel<4, 2, NVS><<<grid, kThreads, 0, s>>>(a);
+    kivi_mfma_split_kernel<4, 2, NVS><<<grid, 64 * kivi_waves<4, 2, NVS>(), 0, s>>>(a);
   } else if (a.kbits == 2 && a.vbits == 4) {
-    kivi_mfma_split_kernel<2, 4, NVS><<<grid, kThreads, 0, s>>>(a);
+    kivi_mfma_split_kernel<2, 4, NVS><<<grid, 64 * kivi_waves<2, 4, NVS>(), 0, s>>>(a);
   } else {
     return hipErrorInvalidValue;
   }
@@ -1365,10 +1411,10 @@ static hipError_t launch_kivi_nvs(const DecodeArgs& a, dim3 grid, hipStream_t s)
 // Resident workgroups per compute unit of each split-kernel instance, found
 // once per process (all instances are fixed at build time; 0 = not yet known).
 template <typename Kernel>
-static int blocks_per_cu(Kernel kernel, std::atomic<int>& slot) {
+static int blocks_per_cu(Kernel kernel, std::atomic<int>& slot, int threads = kThreads) {
   int n = slot.load(std::memory_order_relaxed);
   if (n > 0) return n;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kThreads, 0) != hipSuccess || n <= 0)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n <= 0)
     return 0;
   slot.store(n, std::memory_order_relaxed);
   return n;
@@ -1383,15 +1429,15 @@ int decode_resident_workgroups(const DecodeArgs& a) {
       const int k = (a.kbits == 4 ? 1 : 0) + (a.vbits == 4 ? 2 : 0) + (a.nvs == 4 ? 4 : 0);
       if (a.nvs != 1 && a.nvs != 4) return 0;
       if (a.nvs == 1) {
-        if (k == 0) per_cu = blocks_per_cu(kivi_mfma_split_kernel<2, 2, 1>, slots[k]);
-        else if (k == 1) per_cu = blocks_per_cu(kivi_mfma_split_kernel<4, 2, 1>, slots[k]);
-        else if (k == 2) per_cu = blocks_per_cu(kivi_mfma_split_kernel<2, 4, 1>, slots[k]);
-        else per_cu = blocks_per_cu(kivi_mfma_split_kernel<4, 4, 1>, slots[k]);
+        if (k == 0) per_cu = blocks_per_cu(kivi_mfma_split_kernel<2, 2, 1>, slots[k], 64 * kivi_waves<2, 2, 1>());
+        else if (k == 1) per_cu = blocks_per_cu(kivi_mfma_split_kernel<4, 2, 1>, slots[k], 64 * kivi_waves<4, 2, 1>());
+        else if (k == 2) per_cu = blocks_per_cu(kivi_mfma_split_kernel<2, 4, 1>, slots[k], 64 * kivi_waves<2, 4, 1>());
+        else per_cu = blocks_per_cu(kivi_mfma_split_kernel<4, 4, 1>, slots[k], 64 * kivi_waves<4, 4, 1>());
       } else {
-        if (k == 4) per_cu = blocks_per_cu(kivi_mfma_split_kernel<2, 2, 4>, slots[k]);
-        else if (k == 5) per_cu = blocks_per_cu(kivi_mfma_split_kernel<4, 2, 4>, slots[k]);
-        else if (k == 6) per_cu = blocks_per_cu(kivi_mfma_split_kernel<2, 4, 4>, slots[k]);
-        else per_cu = blocks_per_cu(kivi_mfma_split_kernel<4, 4, 4>, slots[k]);
+        if (k == 4) per_cu = blocks_per_cu(kivi_mfma_split_kernel<2, 2, 4>, slots[k], 64 * kivi_waves<2, 2, 4>());
+        else if (k == 5) per_cu = blocks_per_cu(kivi_mfma_split_kernel<4, 2, 4>, slots[k], 64 * kivi_waves<4, 2, 4>());
+        else if (k == 6) per_cu = blocks_per_cu(kivi_mfma_split_kernel<2, 4, 4>, slots[k], 64 * kivi_waves<2, 4, 4>());
+        else per_cu = blocks_per_cu(kivi_mfma_split_kernel<4, 4, 4>, slots[k], 64 * kivi_waves<4, 4, 4>());
       }
       break;
     }

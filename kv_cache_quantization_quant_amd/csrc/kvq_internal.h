@@ -148,6 +148,8 @@ struct DecodeArgs {
   int n_split_main;       // splits over the main region
   int n_split;            // n_split_main, +1 if the window has a split of its own
   int win_split;          // split that runs the window tiles (-1: empty window)
+  int fixed_order;        // KIVI: 1 = wavefront w takes tiles w, w + NW, ... of its
+                          // split (deterministic); 0 = tiles from a shared counter
   int split_offset;       // first split index a launch covers (grid.x from here)
   const float* q;         // [B][Hq][D]
   float* out;             // [B][Hq][D]

@@ -60,7 +60,7 @@ def test_struct_sizes_match_header(tmp_path):
         assert int(got[st]) == ctypes.sizeof(cls), st
         for f in fields[st]:
             assert int(got[f"{st}.{f}"]) == getattr(cls, f).offset, (st, f)
-    assert int(got["abi"]) == kq.kvq_abi_version() == kq.ABI_VERSION == 6
+    assert int(got["abi"]) == kq.kvq_abi_version() == kq.ABI_VERSION == 7
 
 
 def test_status_strings():
@@ -89,6 +89,8 @@ def test_status_strings():
     (dict(bits=2, v_bits=4), 0),
     (dict(v_group_channels=32), 0),
     (dict(v_group_channels=64), kq.KVQ_ERR_UNSUPPORTED),
+    (dict(deterministic=1), 0),
+    (dict(deterministic=2), kq.KVQ_ERR_UNSUPPORTED),
     (dict(v_group_channels=-32), kq.KVQ_ERR_UNSUPPORTED),
     (dict(residual_length=48), kq.KVQ_ERR_UNSUPPORTED),
     (dict(residual_length=-32), kq.KVQ_ERR_INVALID_ARG),

@@ -122,8 +122,9 @@ def _one_seq_cache(kq, cfg, nq, nr):
 
 
 def test_ragged_equal_lengths_match_uniform(kq):
-    """Equal lengths: the ragged path gives the uniform path's buffers and
-    outputs bit for bit (same kernels, per-sequence counts all equal)."""
+    """Equal lengths: the ragged path gives the uniform path's buffers bit
+    for bit, and its outputs up to fp32 summation order (its split plan and
+    tile order may differ; 5e-5 on outputs of magnitude up to about 10)."""
     B, H, Hq, S, C = 3, 2, 8, 700, 760
     k = synth.make_k(B, H, 0, C, D, device="cuda")
     v = synth.make_v(B, H, 0, C, D, device="cuda")
@@ -142,4 +143,4 @@ def test_ragged_equal_lengths_match_uniform(kq):
         assert torch.equal(rag.view(name), uni.view(name)), name
     err = float((a - b).abs().max())
     _say(f"[ragged == uniform] max abs diff {err:.3e}")
-    assert err <= 1e-5
+    assert err <= 5e-5
