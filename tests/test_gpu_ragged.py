@@ -144,3 +144,68 @@ def test_ragged_equal_lengths_match_uniform(kq):
     err = float((a - b).abs().max())
     _say(f"[ragged == uniform] max abs diff {err:.3e}")
     assert err <= 5e-5
+
+
+def test_ragged_gqa70b_32k_sampled(kq):
+    """The bench's ragged workload at full size: the 32K GQA layer (B = 16,
+    64 query / 8 KV heads) with sequence b holding 32768 - 1920·b tokens,
+    KIVI 2-bit; prefill, then 130 appends (every sequence flushes at its own
+    step) with decodes. Sampled (b, h) blocks, each an oracle batch of one
+    over its own sequence: state bit-exact, their query heads' outputs within
+    the bound, in both tile orders."""
+    from oracle import attention
+    cfg = synth.CONFIGS["gqa70b_32k"]
+    B, H, Hq, S = cfg["batch"], cfg["num_kv_heads"], cfg["num_q_heads"], cfg["seq_len"]
+    steps = 130
+    C = S + steps
+    nq = Hq // H
+    lens = [S - 1920 * b for b in range(B)]
+    blocks = [(0, 0), (6, 5), (15, 7)]
+    _say(f"[ragged 32K] lens {lens[0]}..{lens[-1]} steps={steps}")
+    k = synth.make_k(B, H, 0, C, D, device="cuda")
+    v = synth.make_v(B, H, 0, C, D, device="cuda")
+    caches = {}
+    for det in (0, 1):
+        dc = kq.DeviceCache(kq.make_config("kivi", bits=2, batch=B, num_kv_heads=H, capacity=C,
+                                           deterministic=det), ragged=True)
+        dc.prefill_ragged(k[:, :, :S].contiguous(), v[:, :, :S].contiguous(), lens)
+        caches[det] = dc
+    ocs = []
+    for b, h in blocks:
+        oc = ocache.KiviCache(1, 1, D, 2, 32, 128, C)
+        oc.prefill(_np(k[b:b + 1, h:h + 1, :lens[b]]), _np(v[b:b + 1, h:h + 1, :lens[b]]))
+        ocs.append(oc)
+    ws = caches[0].make_workspace(Hq)
+    worst = 0.0
+    for i in range(steps + 1):
+        if i > 0:
+            pos = [lens[b] + i - 1 for b in range(B)]
+            k1 = torch.stack([k[b, :, pos[b]] for b in range(B)]).contiguous()
+            v1 = torch.stack([v[b, :, pos[b]] for b in range(B)]).contiguous()
+            for dc in caches.values():
+                dc.append(k1, v1)
+            for (b, h), oc in zip(blocks, ocs):
+                oc.append(_np(k1[b:b + 1, h:h + 1]), _np(v1[b:b + 1, h:h + 1]))
+        if i in (0, 1, 65, 129, 130):
+            q = synth.make_q(B, Hq, D, step=i, device="cuda")
+            qn = _np(q)
+            for dc in caches.values():
+                on = _np(dc.decode(q, workspace=ws))
+                for (b, h), oc in zip(blocks, ocs):
+                    Kh, Vh = oc.dequantized()
+                    ref = attention.decode_attention(qn[b:b + 1, h * nq:(h + 1) * nq], Kh, Vh)
+                    worst = max(worst, float(np.max(np.abs(
+                        on[b:b + 1, h * nq:(h + 1) * nq].astype(np.float64) - ref))))
+    torch.cuda.synchronize()
+    for det, dc in caches.items():
+        for (b, h), oc in zip(blocks, ocs):
+            assert dc.seq_n_quant[b] == oc.n_quant and dc.seq_n_resid[b] == oc.n_resid
+            for name in NAMES:
+                g = _np(dc.view(name))[b, h]
+                o = getattr(oc, name)[0, 0]
+                if name.endswith("codes"):
+                    g = g.view(np.uint32)
+                assert np.array_equal(g.view(np.uint8), o.view(np.uint8)), (det, name, b, h)
+    assert all(oc.flush_steps for oc in ocs)
+    _say(f"  worst sampled max abs err {worst:.3e}, flushes {[oc.flush_steps for oc in ocs]}")
+    assert worst <= ATOL
