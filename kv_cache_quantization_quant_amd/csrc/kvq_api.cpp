@@ -736,6 +736,13 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q, int32_t 
   a.vbits = int(d.vbits);
   a.nvs = int(d.nvs);
   a.qfp8 = is_fp8(cache->cfg.format) && cache->cfg.fp8_attention ? 1 : 0;
+  // KIVI: unit-sized workgroups when every (b, h, head chunk) block can have
+  // a compute unit to itself, four-wavefront ones otherwise
+  if (kivi) {
+    const int64_t x = d.B * d.H * (nq / heads_per_chunk(nq));
+    const int cus = kvq::device_compute_units();
+    a.unit = cus > 0 && x <= cus ? 1 : 0;
+  }
   const int64_t target = int64_t(kvq::decode_resident_workgroups(a)) * KVQ_SPLIT_ROUNDS;
   const Plan p = ragged ? make_plan_ragged(d, nq, cache, target)
                         : make_plan(d, nq, cache->n_quant, n_win, target);

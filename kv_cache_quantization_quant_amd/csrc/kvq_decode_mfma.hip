@@ -881,30 +881,32 @@ __device__ __forceinline__ void wait_groups(int ahead) {
 // early and leave their SIMDs one wavefront deep for the rest of the launch
 // (measured: three equal workgroups per unit ended at 46, 67 and 88 µs of a
 // 91 µs launch).
+// Wavefronts per SIMD: what registers and LDS allow (2-bit K and V, or one of
+// them 4-bit: 3 at up to 170 VGPRs; 4-bit K and V, and every instance with V
+// scales per 32 channels: 2).
 template <int BITS, int VB, int NVS>
 constexpr int kivi_waves_per_simd() {
-  return (BITS == 2 && VB == 2 && NVS == 1) ? KVQ_DECODE_WAVES_PER_SIMD : 2;
+  return (BITS == 2 && VB == 2 && NVS == 1) ? KVQ_DECODE_WAVES_PER_SIMD
+         : (NVS == 1 && !(BITS == 4 && VB == 4)) ? 3
+                                                 : 2;
 }
-// The 2-bit instance holds three wavefronts per SIMD, the whole unit in one
-// workgroup; the others keep four-wavefront workgroups (two per unit), since
-// a unit-sized workgroup of theirs leaves the unit idle between workgroups
-// when a launch has more (b, h) blocks than units.
-#ifndef KVQ_KIVI_UNIT_WORKGROUP
-#define KVQ_KIVI_UNIT_WORKGROUP 1
-#endif
-template <int BITS, int VB, int NVS>
+// Each instance comes in two workgroup shapes: UNIT = the whole compute unit
+// in one workgroup (that many wavefronts on each SIMD, tiles shared), for
+// launches with at most one (b, h) block per unit; otherwise four-wavefront
+// workgroups with a fixed tile order, which keep a unit busy across the many
+// rounds of a launch with more blocks than units (a unit-sized workgroup
+// leaves the unit idle between rounds: 7 % on the 4-bit B = 64 layer).
+template <int BITS, int VB, int NVS, bool UNIT>
 constexpr int kivi_waves() {
-  return (KVQ_KIVI_UNIT_WORKGROUP && BITS == 2 && VB == 2 && NVS == 1)
-             ? 4 * kivi_waves_per_simd<BITS, VB, NVS>()
-             : 4;
+  return UNIT ? 4 * kivi_waves_per_simd<BITS, VB, NVS>() : 4;
 }
 
-template <int BITS, int VB, int NVS>
-__global__ __launch_bounds__((64 * kivi_waves<BITS, VB, NVS>()))
+template <int BITS, int VB, int NVS, bool UNIT>
+__global__ __launch_bounds__((64 * kivi_waves<BITS, VB, NVS, UNIT>()))
 __attribute__((amdgpu_waves_per_eu((kivi_waves_per_simd<BITS, VB, NVS>())))) void kivi_mfma_split_kernel(
     DecodeArgs a) {
   using S = Stage<BITS, VB, NVS>;
-  constexpr int NW = kivi_waves<BITS, VB, NVS>();
+  constexpr int NW = kivi_waves<BITS, VB, NVS, UNIT>();
   __shared__ __attribute__((aligned(16))) uint8_t ring[NW][S::kDepth][S::kBytes];
   __shared__ uint32_t next_tile;   // tiles of this split handed out so far
 
@@ -994,7 +996,7 @@ __attribute__((amdgpu_waves_per_eu((kivi_waves_per_simd<BITS, VB, NVS>())))) voi
     // from the shared counter (unit-sized workgroups; four-wavefront ones
     // share a unit with others, so balancing inside them gains little), or
     // wave, wave + NW, ... in fixed order
-    constexpr bool kShare = NW > 4;
+    constexpr bool kShare = UNIT;
     uint32_t taken = 0;
     auto take = [&]() -> uint32_t {
       if (!kShare || a.fixed_order) return uint32_t(wave) + uint32_t(NW) * taken++;
@@ -1391,20 +1393,22 @@ hipError_t launch_dense_mfma(const DecodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// launches the (K bits, V bits) instance with NVS V scales per token
+// launches the (K bits, V bits) instance with NVS V scales per token, in the
+// workgroup shape a.unit selects
+template <int KB, int VB, int NVS>
+static void launch_kivi_shape(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+  if (a.unit)
+    kivi_mfma_split_kernel<KB, VB, NVS, true><<<grid, 64 * kivi_waves<KB, VB, NVS, true>(), 0, s>>>(a);
+  else
+    kivi_mfma_split_kernel<KB, VB, NVS, false><<<grid, 64 * kivi_waves<KB, VB, NVS, false>(), 0, s>>>(a);
+}
 template <int NVS>
 static hipError_t launch_kivi_nvs(const DecodeArgs& a, dim3 grid, hipStream_t s) {
-  if (a.kbits == 2 && a.vbits == 2) {
-    kivi_mfma_split_kernel<2, 2, NVS><<<grid, 64 * kivi_waves<2, 2, NVS>(), 0, s>>>(a);
-  } else if (a.kbits == 4 && a.vbits == 4) {
-    kivi_mfma_split_kernel<4, 4, NVS><<<grid, 64 * kivi_waves<4, 4, NVS>(), 0, s>>>(a);
-  } else if (a.kbits == 4 && a.vbits == 2) {
-    kivi_mfma_split_kernel<4, 2, NVS><<<grid, 64 * kivi_waves<4, 2, NVS>(), 0, s>>>(a);
-  } else if (a.kbits == 2 && a.vbits == 4) {
-    kivi_mfma_split_kernel<2, 4, NVS><<<grid, 64 * kivi_waves<2, 4, NVS>(), 0, s>>>(a);
-  } else {
-    return hipErrorInvalidValue;
-  }
+  if (a.kbits == 2 && a.vbits == 2) launch_kivi_shape<2, 2, NVS>(a, grid, s);
+  else if (a.kbits == 4 && a.vbits == 4) launch_kivi_shape<4, 4, NVS>(a, grid, s);
+  else if (a.kbits == 4 && a.vbits == 2) launch_kivi_shape<4, 2, NVS>(a, grid, s);
+  else if (a.kbits == 2 && a.vbits == 4) launch_kivi_shape<2, 4, NVS>(a, grid, s);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -1420,24 +1424,41 @@ static int blocks_per_cu(Kernel kernel, std::atomic<int>& slot, int threads = kT
   return n;
 }
 
+template <int KB, int VB, int NVS>
+static int kivi_blocks_per_cu(bool unit, std::atomic<int>* slot) {
+  return unit ? blocks_per_cu(kivi_mfma_split_kernel<KB, VB, NVS, true>, slot[1],
+                              64 * kivi_waves<KB, VB, NVS, true>())
+              : blocks_per_cu(kivi_mfma_split_kernel<KB, VB, NVS, false>, slot[0],
+                              64 * kivi_waves<KB, VB, NVS, false>());
+}
+
+int device_compute_units() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return cus;
+}
+
 int decode_resident_workgroups(const DecodeArgs& a) {
-  static std::atomic<int> slots[16];
+  static std::atomic<int> slots[32];
   int per_cu = 0;
   switch (a.src) {
     case kSrcKivi2:
     case kSrcKivi4: {
-      const int k = (a.kbits == 4 ? 1 : 0) + (a.vbits == 4 ? 2 : 0) + (a.nvs == 4 ? 4 : 0);
       if (a.nvs != 1 && a.nvs != 4) return 0;
-      if (a.nvs == 1) {
-        if (k == 0) per_cu = blocks_per_cu(kivi_mfma_split_kernel<2, 2, 1>, slots[k], 64 * kivi_waves<2, 2, 1>());
-        else if (k == 1) per_cu = blocks_per_cu(kivi_mfma_split_kernel<4, 2, 1>, slots[k], 64 * kivi_waves<4, 2, 1>());
-        else if (k == 2) per_cu = blocks_per_cu(kivi_mfma_split_kernel<2, 4, 1>, slots[k], 64 * kivi_waves<2, 4, 1>());
-        else per_cu = blocks_per_cu(kivi_mfma_split_kernel<4, 4, 1>, slots[k], 64 * kivi_waves<4, 4, 1>());
-      } else {
-        if (k == 4) per_cu = blocks_per_cu(kivi_mfma_split_kernel<2, 2, 4>, slots[k], 64 * kivi_waves<2, 2, 4>());
-        else if (k == 5) per_cu = blocks_per_cu(kivi_mfma_split_kernel<4, 2, 4>, slots[k], 64 * kivi_waves<4, 2, 4>());
-        else if (k == 6) per_cu = blocks_per_cu(kivi_mfma_split_kernel<2, 4, 4>, slots[k], 64 * kivi_waves<2, 4, 4>());
-        else per_cu = blocks_per_cu(kivi_mfma_split_kernel<4, 4, 4>, slots[k], 64 * kivi_waves<4, 4, 4>());
+      const int k = (a.kbits == 4 ? 1 : 0) + (a.vbits == 4 ? 2 : 0) + (a.nvs == 4 ? 4 : 0);
+      std::atomic<int>* slot = &slots[16 + 2 * k];
+      const bool u = a.unit != 0;
+      switch (k) {
+        case 0: per_cu = kivi_blocks_per_cu<2, 2, 1>(u, slot); break;
+        case 1: per_cu = kivi_blocks_per_cu<4, 2, 1>(u, slot); break;
+        case 2: per_cu = kivi_blocks_per_cu<2, 4, 1>(u, slot); break;
+        case 3: per_cu = kivi_blocks_per_cu<4, 4, 1>(u, slot); break;
+        case 4: per_cu = kivi_blocks_per_cu<2, 2, 4>(u, slot); break;
+        case 5: per_cu = kivi_blocks_per_cu<4, 2, 4>(u, slot); break;
+        case 6: per_cu = kivi_blocks_per_cu<2, 4, 4>(u, slot); break;
+        default: per_cu = kivi_blocks_per_cu<4, 4, 4>(u, slot); break;
       }
       break;
     }
@@ -1456,10 +1477,7 @@ int decode_resident_workgroups(const DecodeArgs& a) {
       return 0;
   }
   if (per_cu <= 0) return 0;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
+  const int cus = device_compute_units();
   return cus > 0 ? cus * per_cu : 0;
 }
 

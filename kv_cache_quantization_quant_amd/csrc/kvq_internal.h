@@ -150,6 +150,8 @@ struct DecodeArgs {
   int win_split;          // split that runs the window tiles (-1: empty window)
   int fixed_order;        // KIVI: 1 = wavefront w takes tiles w, w + NW, ... of its
                           // split (deterministic); 0 = tiles from a shared counter
+  int unit;               // KIVI: 1 = one workgroup per compute unit (tiles shared
+                          // unless fixed_order), 0 = four-wavefront workgroups
   int split_offset;       // first split index a launch covers (grid.x from here)
   const float* q;         // [B][Hq][D]
   float* out;             // [B][Hq][D]
@@ -181,6 +183,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 // workgroups per unit, from the kernel's register and LDS use); 0 if the
 // runtime cannot tell.
 int decode_resident_workgroups(const DecodeArgs& a);
+// Compute units of the current device (0 if the runtime cannot tell).
+int device_compute_units();
 hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_dense_mfma(const DecodeArgs& a, hipStream_t s);
 
