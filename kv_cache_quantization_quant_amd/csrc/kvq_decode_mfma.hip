@@ -611,14 +611,30 @@ __device__ __forceinline__ void process_window_tile(const DecodeArgs& a, WaveAcc
   }
   const u32x4 bp = p_operand(pp);
   // V^T tiles: lane (r, u) needs channel 16n + r at tokens 4u + j (j < 4) and
-  // 16 + 4u + j - 4; masked tokens read as 0.
+  // 16 + 4u + j - 4. Every slot of a window tile lies inside the window buffer
+  // (its capacity is a whole number of tiles), so the loads are issued
+  // unconditionally, those of two channel tiles at a time in flight together;
+  // masked tokens become 0 after the load (a slot past the last token may hold
+  // anything, even a NaN).
+  __half vh[2][8];
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
+    if (n % 2 == 0) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int t = (j < 4) ? 4 * u + j : 16 + 4 * u + (j - 4);
+          vh[m][j] = vwp[t * kHeadDim + 16 * (n + m) + r];
+        }
+      }
+    }
     float v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int t = (j < 4) ? 4 * u + j : 16 + 4 * u + (j - 4);
-      v[j] = t < n_in ? __half2float(vwp[t * kHeadDim + 16 * n + r]) : 0.0f;
+      const float x = __half2float(vh[n % 2][j]);
+      v[j] = t < n_in ? x : 0.0f;
     }
     uint32_t hi[4], lo[4];
 #pragma unroll
