@@ -36,7 +36,7 @@ BENCH_STATS = ["python3", os.path.join(ROOT, "bench.py"), "--steps", "256", "--w
 BENCH = ["python3", os.path.join(ROOT, "bench.py"), "--steps", "16", "--warmup", "4",
          "--no-cpu-baseline", "--no-extra", "--no-cold"]
 COPY_MIB = 1024
-DECODE = "kivi_mfma_split_kernel<2, 2, 1>"
+DECODE = "kivi_mfma_split_kernel<2, 2, 1, true>"   # the unit-sized workgroup shape
 MERGE = "decode_merge_kernel"
 
 
