@@ -764,3 +764,35 @@ def test_gqa_128k_fp16_sampled(kq, kv_128k):
         worst = max(worst, _att_err(out[b:b + 1, h * nq:(h + 1) * nq], ref))
     _say(f"[gqa_128k fp16] sampled max abs err {worst:.3e}")
     assert worst <= ATOL
+
+
+@pytest.mark.parametrize("bits,vbits,gc,det", [(2, 0, 0, 0), (2, 0, 0, 1), (4, 2, 0, 0),
+                                               (2, 0, 32, 0)])
+def test_kivi_many_blocks_shape(kq, bits, vbits, gc, det):
+    """More (b, h) blocks than compute units (B·H = 320 here): the decode
+    takes its four-wavefront workgroup shape with a fixed tile order. State
+    bit-exact, attention within the bound, over a prefill and appends that
+    flush."""
+    B, H, Hq, S, steps = 40, 8, 16, 300, 40
+    C = S + steps
+    _say(f"[many blocks] bits={bits} v_bits={vbits} gc={gc} det={det} B={B} H={H}")
+    k, v = _kv(B, H, C)
+    dc = kq.DeviceCache(kq.make_config("kivi", bits=bits, batch=B, num_kv_heads=H, capacity=C,
+                                       v_bits=vbits, v_group_channels=gc, deterministic=det))
+    oc = ocache.KiviCache(B, H, D, bits, 32, 128, C, v_bits=vbits or None,
+                          v_group_channels=gc or None)
+    dc.prefill(k[:, :, :S].contiguous(), v[:, :, :S].contiguous())
+    oc.prefill(_np(k[:, :, :S]), _np(v[:, :, :S]))
+    kn, vn = _np(k), _np(v)
+    worst = 0.0
+    for i in range(steps):
+        t = S + i
+        dc.append(k[:, :, t].contiguous(), v[:, :, t].contiguous())
+        oc.append(kn[:, :, t], vn[:, :, t])
+        if i in (0, steps - 1):
+            q = synth.make_q(B, Hq, D, step=i, device="cuda")
+            worst = max(worst, _att_err(_np(dc.decode(q)), oc.attention(_np(q))))
+    torch.cuda.synchronize()
+    _compare_kivi_state(dc, oc)
+    _say(f"  worst max abs err {worst:.3e}, flushes at {oc.flush_steps}")
+    assert oc.flush_steps and worst <= ATOL
