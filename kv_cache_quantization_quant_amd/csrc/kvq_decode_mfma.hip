@@ -69,6 +69,9 @@ constexpr int kWaves = kThreads / 64;
 #ifndef KVQ_RING_STAGES_4BIT
 #define KVQ_RING_STAGES_4BIT 3
 #endif
+#ifndef KVQ_TAKE_AHEAD
+#define KVQ_TAKE_AHEAD 1   // take a split's next tile one iteration before it is issued
+#endif
 #ifndef KVQ_RING_STAGES_UNIT
 #define KVQ_RING_STAGES_UNIT 3
 #endif
@@ -1068,10 +1071,11 @@ __attribute__((amdgpu_waves_per_eu((kivi_waves_per_simd<BITS, VB, NVS>())))) voi
       // steady state: a group is loaded every iteration, one fixed wait,
       // until the split runs out of tiles; each iteration takes the tile of
       // the next one, so the counter's round trip overlaps the arithmetic
-      uint32_t t_next = n_mine < 0 ? take() : n_blk;
+      uint32_t t_next = (KVQ_TAKE_AHEAD && n_mine < 0) ? take() : n_blk;
       while (n_mine < 0) {
         // the refilled stage was last read two groups ago; its reads are done
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (!KVQ_TAKE_AHEAD) t_next = take();
         if (t_next >= n_blk) {
           n_mine = i + kAhead;
           break;
@@ -1081,7 +1085,7 @@ __attribute__((amdgpu_waves_per_eu((kivi_waves_per_simd<BITS, VB, NVS>())))) voi
         wait_vmem<kAhead * S::kLoads>();
         load_v<BITS, VB, NVS>(ring_w + ((i - 1) % kDepth) * S::kBytes, r, u, V);
         load_k<BITS, VB, NVS>(ring_w + (i % kDepth) * S::kBytes, r, u, low, K);
-        t_next = take();
+        if (KVQ_TAKE_AHEAD) t_next = take();
         // keep every LDS read of the iteration ahead of the arithmetic
         __builtin_amdgcn_sched_barrier(0);
         group_scores<BITS, NVS>(K, low, q16, low ? 0.0f : W.m_ref, sc);
