@@ -34,7 +34,15 @@ __device__ __forceinline__ float wave_sum(float x) {
 // every lane reads its two channels of up to kBatch partial outputs at once,
 // so a head costs about one memory round trip per kBatch splits.
 constexpr int kBatch = 32;
-__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
+// The merge's own launch arguments (a few bytes instead of the split
+// kernels' block with its ragged-batch table).
+struct MergeArgs {
+  const float* ws;        // [rows][n_split][D + 2] partials
+  float* out;             // [rows][D]
+  int n_split;
+};
+
+__global__ __launch_bounds__(64) void decode_merge_kernel(MergeArgs a) {
   const int64_t row = blockIdx.x;   // b·Hq + hq
   const int lane = threadIdx.x;
   const float* part = a.ws + row * a.n_split * kPart;
@@ -71,8 +79,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
 
 // The split kernel of the cache's format, then the merge.
 hipError_t launch_decode(const DecodeArgs& a_in, hipStream_t s) {
-  DecodeArgs a = a_in;
-  a.split_offset = 0;
+  const DecodeArgs& a = a_in;
   hipError_t e = hipSuccess;
   switch (a.src) {
     case kSrcKivi2:
@@ -88,7 +95,11 @@ hipError_t launch_decode(const DecodeArgs& a_in, hipStream_t s) {
       return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  decode_merge_kernel<<<a.B * a.Hq, 64, 0, s>>>(a);
+  MergeArgs m;
+  m.ws = a.ws;
+  m.out = a.out;
+  m.n_split = a.n_split;
+  decode_merge_kernel<<<a.B * a.Hq, 64, 0, s>>>(m);
   return hipGetLastError();
 }
 

@@ -152,7 +152,6 @@ struct DecodeArgs {
                           // split (deterministic); 0 = tiles from a shared counter
   int unit;               // KIVI: 1 = one workgroup per compute unit (tiles shared
                           // unless fixed_order), 0 = four-wavefront workgroups
-  int split_offset;       // first split index a launch covers (grid.x from here)
   const float* q;         // [B][Hq][D]
   float* out;             // [B][Hq][D]
   float* ws;              // [B][Hq][n_split][D + 2]
