@@ -216,9 +216,15 @@ def _check(status: int, what: str):
         raise KvqError(status, what)
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream_handle(stream) -> int:
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return s.cuda_stream
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None:          # the current stream's handle, no Stream object
+        return _raw_stream(torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 # ------------------------------------------ torch-owned cache (plumbing) ---

@@ -1461,10 +1461,14 @@ static int kivi_blocks_per_cu(bool unit, std::atomic<int>* slot) {
 }
 
 int device_compute_units() {
+  // per device, queried once (a fixed property of the device)
+  static std::atomic<int> known[64];
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64 && (cus = known[dev].load(std::memory_order_relaxed)) > 0) return cus;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
+  if (dev >= 0 && dev < 64 && cus > 0) known[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 
