@@ -12,7 +12,10 @@
 // Data movement. Each wavefront owns a ring of LDS stages, one 32-token group
 // per stage (K codes, V codes, K scale | zero, V scale | zero: 3328 bytes at
 // 2 bits, 5376 at 4 bits), filled by global_load_lds (one instruction moves
-// 1 KiB, no VGPRs involved) up to three groups ahead of the group in work.
+// 1 KiB, no VGPRs involved) one or two groups ahead of the group in work.
+// Work is split over (b, h, head chunk) blocks and, within one, over splits of
+// its 32-token tiles; the wavefronts of a split's workgroup take its tiles
+// from a shared LDS counter (unit-sized workgroups) or in a fixed order.
 //
 // One wavefront processes one group at a time; lane l has r = l%16, u = l/16,
 // head slot hs = r%8 (up to 8 query heads of one KV head) and part = r/8.
