@@ -180,14 +180,15 @@ typedef struct {
   int32_t v_group_channels; /* KIVI: 0 = one V scale / zero-point per token;
                               32 = one per token and run of 32 channels
                               (D/32 per token); ignored else                  */
-  int32_t deterministic;   /* 0 or 1. KIVI decode: 0 = the wavefronts of a
-                              split take its 32-token tiles from a shared
-                              counter as they go (fastest; which wavefront
-                              sums which tile varies, so outputs can differ
-                              from run to run in the last bits, always
-                              within the accuracy bound); 1 = a fixed tile
-                              order per wavefront (bitwise identical runs).
-                              FP8 / FP16 decodes are always deterministic.  */
+  int32_t deterministic;   /* 0 or 1. KIVI and FP8 decode: 0 = the
+                              wavefronts of a split may take its 32-token
+                              tiles from a shared counter as they go
+                              (fastest; which wavefront sums which tile
+                              varies, so outputs can differ from run to run
+                              in the last bits, always within the accuracy
+                              bound); 1 = a fixed tile order per wavefront
+                              (bitwise identical runs). FP16 decodes are
+                              always deterministic.                          */
 } kvq_config;
 
 /* Bytes the caller must allocate for each device buffer (0 = unused). */

@@ -189,9 +189,9 @@ def make_config(fmt: str = "kivi", bits: int | None = None, group_size: int = 32
     """v_bits: KIVI V bit width (0 = same as bits); scale_per_head: FP8 scales
     per KV head (1) or per tensor (0); fp8_attention: FP8 decode with the
     query quantized to E4M3 (1); v_group_channels: KIVI V scales per run of
-    32 channels (32) or per token (0); deterministic: KIVI decode with a fixed
-    tile order per wavefront (1, bitwise reproducible) or tiles shared as the
-    wavefronts go (0, fastest)."""
+    32 channels (32) or per token (0); deterministic: KIVI and FP8 decode with
+    a fixed tile order per wavefront (1, bitwise reproducible) or tiles shared
+    as the wavefronts go (0, fastest)."""
     if bits is None:
         bits = {"kivi": 2, "fp8": 8, "fp8_e5m2": 8, "fp16": 16}[fmt]
     return KvqConfig(FORMATS[fmt], bits, group_size, residual_length, batch, num_kv_heads,

@@ -736,9 +736,11 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q, int32_t 
   a.vbits = int(d.vbits);
   a.nvs = int(d.nvs);
   a.qfp8 = is_fp8(cache->cfg.format) && cache->cfg.fp8_attention ? 1 : 0;
-  // KIVI: unit-sized workgroups when every (b, h, head chunk) block can have
-  // a compute unit to itself, four-wavefront ones otherwise
-  if (kivi) {
+  // Unit-sized workgroups when every (b, h, head chunk) block can have a
+  // compute unit to itself, four-wavefront ones otherwise. KIVI: either
+  // order of tiles; FP8: only for caches that need not be deterministic (the
+  // unit shape pays only with tiles shared); FP16: four wavefronts always.
+  if (kivi || (is_fp8(cache->cfg.format) && !cache->cfg.deterministic)) {
     const int64_t x = d.B * d.H * (nq / heads_per_chunk(nq));
     const int cus = kvq::device_compute_units();
     a.unit = cus > 0 && x <= cus ? 1 : 0;

@@ -1274,10 +1274,21 @@ __device__ __forceinline__ void process_dense_tile(const uint8_t* st, WaveAcc& W
   }
 }
 
-template <int SRC, bool QF8>
-__global__ __launch_bounds__(kThreads) void dense_mfma_split_kernel(DecodeArgs a) {
+// Wavefronts of a dense decode workgroup. UNIT (FP8 caches, tiles shared,
+// chosen only when the cache is not deterministic): the whole compute unit in
+// one workgroup, two wavefronts per SIMD on two 8 KiB stages each; otherwise
+// four wavefronts with a fixed tile order (the FP16 caches' 16 KiB stages fit
+// no more). Same-box A/B of the 128K FP8 decode: the unit shape with shared
+// tiles 2-4 % faster, with a fixed order 7-8 % slower.
+template <int SRC, bool UNIT>
+constexpr int dense_waves() { return (UNIT && SRC != kSrcFp16) ? 8 : 4; }
+
+template <int SRC, bool QF8, bool UNIT>
+__global__ __launch_bounds__((64 * dense_waves<SRC, UNIT>())) void dense_mfma_split_kernel(DecodeArgs a) {
   using S = DenseStage<SRC>;
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][S::kDepth][S::kBytes];
+  constexpr int NW = dense_waves<SRC, UNIT>();
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NW][S::kDepth][S::kBytes];
+  __shared__ uint32_t next_tile;   // tiles of this split handed out so far
 
   const BlockCoord bc = block_coord(a);
   const int split = bc.split;
@@ -1375,51 +1386,74 @@ __global__ __launch_bounds__(kThreads) void dense_mfma_split_kernel(DecodeArgs a
   for (int n = 0; n < 8; ++n) W.cv[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   W.cones[0] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  if (tid == 0) next_tile = 0;
+  __syncthreads();
   const int64_t n_tiles = (a.n_main + kGroup - 1) / kGroup;
   const int64_t g0 = int64_t(split) * a.tiles_per_split;
   const int64_t g1 = min(g0 + int64_t(a.tiles_per_split), n_tiles);
-  // this wavefront's tiles: g0 + wave + kWaves·i, i < n_mine
-  const int n_mine = g1 - g0 > wave ? int((g1 - g0 - wave + kWaves - 1) / kWaves) : 0;
-  constexpr int kAhead = S::kDepth - 1;
+  const uint32_t n_blk = g1 > g0 ? uint32_t(g1 - g0) : 0u;   // tiles of this split
+  static_assert(S::kDepth == 2, "one tile in flight ahead of the one in work");
   const uint32_t v16 = 16u * lane;
   uint8_t* ring_w = &ring[wave][0][0];
-#pragma unroll
-  for (int j = 0; j < kAhead; ++j)
-    if (j < n_mine) issue_tile<SRC>(ring_w + j * S::kBytes, a, bh, g0 + wave + int64_t(kWaves) * j, v16);
-  for (int i = 0; i < n_mine; ++i) {
-    if (i + kAhead < n_mine) {
+  // the next tile of the split (n_blk and above: none left), from the shared
+  // counter (UNIT) or in fixed order wave, wave + NW, ...
+  uint32_t taken = 0;
+  auto take = [&]() -> uint32_t {
+    if (!UNIT) return uint32_t(wave) + uint32_t(NW) * taken++;
+    uint32_t t = 0;
+    if (lane == 0) t = atomicAdd(&next_tile, 1u);
+    return __builtin_amdgcn_readfirstlane(t);
+  };
+  // tile i of this wavefront sits in stage i % 2; cur: the tile in work,
+  // t_next: the one after it (taken a tile ahead)
+  const uint32_t t0 = take();
+  bool have = t0 < n_blk;
+  int64_t cur = g0 + t0;
+  if (have) issue_tile<SRC>(ring_w, a, bh, cur, v16);
+  uint32_t t_next = have ? take() : n_blk;
+  for (int i = 0; have; ++i) {
+    const bool more = t_next < n_blk;
+    const int64_t nxt = g0 + t_next;
+    if (more) {
       // the refilled stage was read by the previous tile; its reads are done
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      const int j = i + kAhead;
-      issue_tile<SRC>(ring_w + (j % S::kDepth) * S::kBytes, a, bh, g0 + wave + int64_t(kWaves) * j,
-                      v16);
+      issue_tile<SRC>(ring_w + ((i + 1) % S::kDepth) * S::kBytes, a, bh, nxt, v16);
+      wait_vmem<S::kLoads>();
+      t_next = take();
+    } else {
+      wait_vmem<0>();
     }
-    const int ahead = min(kAhead, n_mine - 1 - i);
-    if (ahead >= 2) wait_vmem<2 * S::kLoads>();
-    else if (ahead == 1) wait_vmem<S::kLoads>();
-    else wait_vmem<0>();
-    const int64_t tile = g0 + wave + int64_t(kWaves) * i;
-    const int n_in = int(min<int64_t>(kGroup, a.n_main - tile * kGroup));
+    const int n_in = int(min<int64_t>(kGroup, a.n_main - cur * kGroup));
     process_dense_tile<SRC, QF8>(ring_w + (i % S::kDepth) * S::kBytes, W, n_in, bq, smul, r,
                                  u, low);
+    have = more;
+    cur = nxt;
   }
 
-  wave_epilogue_and_merge(a, W, &ring[0][0][0], sizeof(ring[0]), wave, lane, hs, u, low, tid,
-                          b, hq0, nh, split, sv);
+  wave_epilogue_and_merge<1, NW>(a, W, &ring[0][0][0], sizeof(ring[0]), wave, lane, hs, u, low,
+                                 tid, b, hq0, nh, split, sv);
 }
 
 }  // namespace
 
+template <int SRC, bool QF8>
+static void launch_dense_shape(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+  if (a.unit)
+    dense_mfma_split_kernel<SRC, QF8, true><<<grid, 64 * dense_waves<SRC, true>(), 0, s>>>(a);
+  else
+    dense_mfma_split_kernel<SRC, QF8, false><<<grid, 64 * dense_waves<SRC, false>(), 0, s>>>(a);
+}
+
 hipError_t launch_dense_mfma(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid = split_grid(a);
   if (a.src == kSrcFp16) {
-    dense_mfma_split_kernel<kSrcFp16, false><<<grid, kThreads, 0, s>>>(a);
+    dense_mfma_split_kernel<kSrcFp16, false, false><<<grid, 64 * dense_waves<kSrcFp16, false>(), 0, s>>>(a);
   } else if (a.src == kSrcE5M2) {
-    if (a.qfp8) dense_mfma_split_kernel<kSrcE5M2, true><<<grid, kThreads, 0, s>>>(a);
-    else dense_mfma_split_kernel<kSrcE5M2, false><<<grid, kThreads, 0, s>>>(a);
+    if (a.qfp8) launch_dense_shape<kSrcE5M2, true>(a, grid, s);
+    else launch_dense_shape<kSrcE5M2, false>(a, grid, s);
   } else {
-    if (a.qfp8) dense_mfma_split_kernel<kSrcFp8, true><<<grid, kThreads, 0, s>>>(a);
-    else dense_mfma_split_kernel<kSrcFp8, false><<<grid, kThreads, 0, s>>>(a);
+    if (a.qfp8) launch_dense_shape<kSrcFp8, true>(a, grid, s);
+    else launch_dense_shape<kSrcFp8, false>(a, grid, s);
   }
   return hipGetLastError();
 }
@@ -1463,6 +1497,14 @@ static int kivi_blocks_per_cu(bool unit, std::atomic<int>* slot) {
                               64 * kivi_waves<KB, VB, NVS, false>());
 }
 
+template <int SRC, bool QF8>
+static int dense_blocks_per_cu(bool unit, std::atomic<int>* slot) {
+  return unit ? blocks_per_cu(dense_mfma_split_kernel<SRC, QF8, true>, slot[1],
+                              64 * dense_waves<SRC, true>())
+              : blocks_per_cu(dense_mfma_split_kernel<SRC, QF8, false>, slot[0],
+                              64 * dense_waves<SRC, false>());
+}
+
 int device_compute_units() {
   // per device, queried once (a fixed property of the device)
   static std::atomic<int> known[64];
@@ -1498,15 +1540,16 @@ int decode_resident_workgroups(const DecodeArgs& a) {
       break;
     }
     case kSrcFp16:
-      per_cu = blocks_per_cu(dense_mfma_split_kernel<kSrcFp16, false>, slots[8]);
+      per_cu = blocks_per_cu(dense_mfma_split_kernel<kSrcFp16, false, false>, slots[8],
+                             64 * dense_waves<kSrcFp16, false>());
       break;
     case kSrcFp8:
-      per_cu = a.qfp8 ? blocks_per_cu(dense_mfma_split_kernel<kSrcFp8, true>, slots[9])
-                      : blocks_per_cu(dense_mfma_split_kernel<kSrcFp8, false>, slots[10]);
+      per_cu = a.qfp8 ? dense_blocks_per_cu<kSrcFp8, true>(a.unit != 0, &slots[0])
+                      : dense_blocks_per_cu<kSrcFp8, false>(a.unit != 0, &slots[2]);
       break;
     case kSrcE5M2:
-      per_cu = a.qfp8 ? blocks_per_cu(dense_mfma_split_kernel<kSrcE5M2, true>, slots[11])
-                      : blocks_per_cu(dense_mfma_split_kernel<kSrcE5M2, false>, slots[12]);
+      per_cu = a.qfp8 ? dense_blocks_per_cu<kSrcE5M2, true>(a.unit != 0, &slots[4])
+                      : dense_blocks_per_cu<kSrcE5M2, false>(a.unit != 0, &slots[6]);
       break;
     default:
       return 0;

@@ -273,20 +273,23 @@ def test_append_at_capacity_is_rejected(kq):
     assert (dc.n_quant, dc.n_resid) == (32, 8)
 
 
-@pytest.mark.parametrize("bits", [2, 4])
-def test_deterministic(kq, bits):
+@pytest.mark.parametrize("fmt,bits,fp8_attention", [("kivi", 2, 0), ("kivi", 4, 0),
+                                                    ("fp8", None, 0), ("fp8", None, 1),
+                                                    ("fp8_e5m2", None, 0)])
+def test_deterministic(kq, fmt, bits, fp8_attention):
     """deterministic = 1: bitwise identical quantization and decode across
-    caches and calls. deterministic = 0 (tiles shared between wavefronts as
-    they go): the same codes, and outputs within 2e-5 of the fixed order (the
-    fp32 sums of one wavefront's tiles add up in another order; measured
-    4e-6 on outputs of magnitude up to about 10)."""
+    caches and calls. deterministic = 0 (KIVI and FP8: tiles shared between
+    wavefronts as they go): the same codes, and outputs within 2e-5 of the
+    fixed order (the fp32 sums of one wavefront's tiles add up in another
+    order; measured 4e-6 on outputs of magnitude up to about 10)."""
     B, H, Hq, S = 2, 2, 8, 6000
     k, v = _kv(B, H, S)
     q = synth.make_q(B, Hq, D, device="cuda")
     outs = []
     for det in (1, 1, 0, 0):
-        dc = kq.DeviceCache(kq.make_config("kivi", bits=bits, batch=B, num_kv_heads=H,
-                                           capacity=S, deterministic=det))
+        dc = kq.DeviceCache(kq.make_config(fmt, bits=bits, batch=B, num_kv_heads=H,
+                                           capacity=S, fp8_attention=fp8_attention,
+                                           deterministic=det))
         dc.prefill(k, v)
         outs.append((_np(dc.view("k_codes")), _np(dc.decode(q)), _np(dc.decode(q))))
     for o in outs[1:]:
