@@ -135,7 +135,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 7
+#define KVQ_ABI_VERSION 8
 
 typedef enum {
   KVQ_OK = 0,
@@ -303,6 +303,26 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q,
                                 void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/* One decode over the attention layers of a model, layer by layer in index
+ * order, for callers that hold every layer's query at once. Each layer keeps
+ * its own cache ([Tutorial] §四.4: a layer has its own cache length and KV
+ * head count, e.g. sliding-window layers that keep only their last tokens):
+ * caches[l] may differ in format, capacity, fill state, num_kv_heads and
+ * raggedness; a layer left unquantized ([KIVI-page] §7.1, sensitive layers
+ * kept at full precision) is an FP16 cache. All layers share the batch size
+ * and num_q_heads (a multiple of each layer's num_kv_heads).
+ * q: device fp32 [n_layers][B][Hq][D]; out: same shape (written); workspace:
+ * device, ≥ the largest kvq_decode_workspace_bytes of the layers (the
+ * layers' launches run one after another on the stream and reuse it).
+ * Every layer is checked as kvq_decode_attention checks it, and planned,
+ * before anything is enqueued: on error nothing is enqueued and the status
+ * is the first failing layer's (INVALID_ARG also for a null caches array,
+ * n_layers < 1, a null layer or a batch size unlike layer 0's). */
+kvq_status kvq_decode_attention_layers(const kvq_cache* const* caches, int32_t n_layers,
+                                       const float* q, int32_t num_q_heads, float* out,
+                                       void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
 /* Per-query-head E4M3 quantization of decode queries, the first step of
  * attention in the FP8 domain ([Tutorial] §十八.7; [KIVI-page] §6): one scale
  * per (b, query head) as q_scale has one entry per head ([Tutorial] §十八.6),
@@ -332,6 +352,14 @@ int64_t kvq_decode_bytes(const kvq_cache* cache, int32_t num_q_heads);
 double kvq_theoretical_bytes(int32_t num_layers, int32_t batch, int64_t seq_len,
                              int32_t num_kv_heads, int32_t head_dim,
                              double bytes_per_elem);
+
+/* The pages' mixed-layer KV byte formula 2·B·bytes_per_elem·Σ_l S_l·H_kv,l·D_l
+ * ([Tutorial] §四.4), for layers with their own cache length seq_len[l], KV
+ * heads num_kv_heads[l] and head dim head_dim[l] (host arrays of n_layers).
+ * −1 on invalid input (n_layers < 1, null arrays, negative sizes). */
+double kvq_theoretical_bytes_layers(int32_t n_layers, int32_t batch, const int64_t* seq_len,
+                                    const int32_t* num_kv_heads, const int32_t* head_dim,
+                                    double bytes_per_elem);
 
 /* Static description of a status code (never NULL). */
 const char* kvq_status_str(kvq_status status);

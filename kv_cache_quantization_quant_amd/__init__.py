@@ -11,7 +11,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import POINTER, byref, c_double, c_int32, c_int64, c_size_t, c_void_p
+from ctypes import POINTER, byref, c_double, c_int32, c_int64, c_size_t, c_void_p, pointer
 
 import torch
 
@@ -28,7 +28,7 @@ KVQ_ERR_STATE = 4
 KVQ_ERR_DEVICE = 5
 KVQ_ERR_WORKSPACE = 6
 
-ABI_VERSION = 7        # KVQ_ABI_VERSION of include/kvq.h
+ABI_VERSION = 8        # KVQ_ABI_VERSION of include/kvq.h
 
 KVQ_FMT_FP16 = 0
 KVQ_FMT_FP8_E4M3 = 1
@@ -92,11 +92,17 @@ def _load():
         "kvq_decode_workspace_bytes": (c_size_t, [POINTER(KvqConfig), c_int32]),
         "kvq_decode_attention": (c_int32, [POINTER(KvqCache), c_void_p, c_int32, c_void_p,
                                            c_void_p, c_size_t, c_void_p]),
+        "kvq_decode_attention_layers": (c_int32, [POINTER(POINTER(KvqCache)), c_int32,
+                                                  c_void_p, c_int32, c_void_p, c_void_p,
+                                                  c_size_t, c_void_p]),
         "kvq_decode_bytes": (c_int64, [POINTER(KvqCache), c_int32]),
         "kvq_quantize_query_fp8": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p,
                                              c_void_p, c_void_p]),
         "kvq_theoretical_bytes": (c_double, [c_int32, c_int32, c_int64, c_int32, c_int32,
                                              c_double]),
+        "kvq_theoretical_bytes_layers": (c_double, [c_int32, c_int32, POINTER(c_int64),
+                                                    POINTER(c_int32), POINTER(c_int32),
+                                                    c_double]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -114,7 +120,8 @@ ABI_SYMBOLS = ("kvq_abi_version", "kvq_status_str", "kvq_layout_query", "kvq_cac
                "kvq_cache_reset", "kvq_prefill_quantize", "kvq_prefill_quantize_ragged",
                "kvq_append_token",
                "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_bytes",
-               "kvq_quantize_query_fp8", "kvq_theoretical_bytes")
+               "kvq_quantize_query_fp8", "kvq_theoretical_bytes",
+               "kvq_decode_attention_layers", "kvq_theoretical_bytes_layers")
 
 
 # ------------------------------------------------- one-to-one ABI wrappers ---
@@ -165,6 +172,16 @@ def kvq_decode_attention(cache: KvqCache, q_ptr: int, num_q_heads: int, out_ptr:
                                     ws_bytes, stream)
 
 
+def kvq_decode_attention_layers(caches, q_ptr: int, num_q_heads: int, out_ptr: int,
+                                ws_ptr: int, ws_bytes: int, stream: int | None) -> int:
+    """caches: a sequence of KvqCache (None entries pass a null pointer)."""
+    arr = (POINTER(KvqCache) * max(1, len(caches)))()
+    for i, c in enumerate(caches):
+        arr[i] = pointer(c) if c is not None else POINTER(KvqCache)()
+    return lib.kvq_decode_attention_layers(arr, len(caches), q_ptr, num_q_heads, out_ptr,
+                                           ws_ptr, ws_bytes, stream)
+
+
 def kvq_decode_bytes(cache: KvqCache, num_q_heads: int) -> int:
     return lib.kvq_decode_bytes(byref(cache), num_q_heads)
 
@@ -179,6 +196,36 @@ def kvq_theoretical_bytes(num_layers, batch, seq_len, num_kv_heads, head_dim,
                           bytes_per_elem) -> float:
     return lib.kvq_theoretical_bytes(num_layers, batch, seq_len, num_kv_heads, head_dim,
                                      bytes_per_elem)
+
+
+def kvq_theoretical_bytes_layers(batch, seq_lens, num_kv_heads, head_dims,
+                                 bytes_per_elem) -> float:
+    n = len(seq_lens)
+    if not (len(num_kv_heads) == len(head_dims) == n):
+        raise ValueError("one seq_len, num_kv_heads and head_dim per layer")
+    return lib.kvq_theoretical_bytes_layers(n, batch, (c_int64 * max(1, n))(*seq_lens),
+                                            (c_int32 * max(1, n))(*num_kv_heads),
+                                            (c_int32 * max(1, n))(*head_dims), bytes_per_elem)
+
+
+def decode_layers(caches, q: torch.Tensor, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """One decode per layer (kvq_decode_attention_layers). caches: DeviceCache
+    per layer; q: contiguous fp32 [L, B, Hq, D] → out fp32 [L, B, Hq, D]."""
+    assert q.dtype == torch.float32 and q.is_contiguous() and q.dim() == 4
+    assert q.shape[0] == len(caches)
+    hq = q.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        n = max(c.workspace_bytes(hq) for c in caches)
+        if n == 0:
+            raise KvqError(KVQ_ERR_INVALID_ARG, "kvq_decode_workspace_bytes")
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    _check(kvq_decode_attention_layers([c.cache for c in caches], q.data_ptr(), hq,
+                                       out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                       _stream_handle(stream)), "kvq_decode_attention_layers")
+    return out
 
 
 def make_config(fmt: str = "kivi", bits: int | None = None, group_size: int = 32,

@@ -701,9 +701,11 @@ size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t num_q_heads) {
   return size_t(d.B) * num_q_heads * max_splits(d, nq) * (kHeadDim + 2) * sizeof(float);
 }
 
-kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q, int32_t num_q_heads,
-                                float* out, void* workspace, size_t workspace_bytes,
-                                void* stream) {
+}  // extern "C"
+
+// Every check of one decode call, before anything is enqueued.
+static kvq_status decode_check(const kvq_cache* cache, const float* q, int32_t num_q_heads,
+                               float* out, void* workspace, size_t workspace_bytes) {
   if (cache == nullptr || q == nullptr || out == nullptr) return KVQ_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(out)) return KVQ_ERR_INVALID_ARG;
   const kvq_status vs = validate_config(&cache->cfg);
@@ -722,6 +724,13 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q, int32_t 
   const size_t need = kvq_decode_workspace_bytes(&cache->cfg, num_q_heads);
   if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
     return KVQ_ERR_WORKSPACE;
+  return KVQ_OK;
+}
+
+// The launches of one checked decode call (dry: plan only, enqueue nothing).
+static kvq_status decode_enqueue(const kvq_cache* cache, const float* q, int32_t num_q_heads,
+                                 float* out, void* workspace, void* stream, bool dry) {
+  const bool ragged = is_ragged(cache);
 
   const Dims d = dims_of(cache->cfg);
   const int nq = num_q_heads / int(d.H);
@@ -749,6 +758,7 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q, int32_t 
   const Plan p = ragged ? make_plan_ragged(d, nq, cache, target)
                         : make_plan(d, nq, cache->n_quant, n_win, target);
   if (p.n_split > max_splits(d, nq)) return KVQ_ERR_WORKSPACE;
+  if (dry) return KVQ_OK;
 
   a.B = int(d.B);
   a.H = int(d.H);
@@ -789,6 +799,45 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q, int32_t 
   a.ws = static_cast<float*>(workspace);
   a.qscale = float(1.4426950408889634 / sqrt(double(kHeadDim)));
   return device_status(kvq::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" {
+
+kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q, int32_t num_q_heads,
+                                float* out, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  const kvq_status st = decode_check(cache, q, num_q_heads, out, workspace, workspace_bytes);
+  if (st != KVQ_OK) return st;
+  return decode_enqueue(cache, q, num_q_heads, out, workspace, stream, false);
+}
+
+kvq_status kvq_decode_attention_layers(const kvq_cache* const* caches, int32_t n_layers,
+                                       const float* q, int32_t num_q_heads, float* out,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (caches == nullptr || n_layers < 1 || q == nullptr || out == nullptr)
+    return KVQ_ERR_INVALID_ARG;
+  // every layer checked and planned before the first launch
+  int64_t row = 0;   // floats of one layer's q / out: B·Hq·D
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const kvq_cache* c = caches[l];
+    if (c == nullptr) return KVQ_ERR_INVALID_ARG;
+    if (l > 0 && c->cfg.batch != caches[0]->cfg.batch) return KVQ_ERR_INVALID_ARG;
+    const kvq_status st = decode_check(c, q + l * row, num_q_heads, out + l * row, workspace,
+                                       workspace_bytes);
+    if (st != KVQ_OK) return st;
+    if (l == 0) row = int64_t(c->cfg.batch) * num_q_heads * kHeadDim;
+  }
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const kvq_status st = decode_enqueue(caches[l], q + l * row, num_q_heads, out + l * row,
+                                         workspace, stream, true);
+    if (st != KVQ_OK) return st;
+  }
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const kvq_status st = decode_enqueue(caches[l], q + l * row, num_q_heads, out + l * row,
+                                         workspace, stream, false);
+    if (st != KVQ_OK) return st;
+  }
+  return KVQ_OK;
 }
 
 kvq_status kvq_quantize_query_fp8(const float* q, int32_t batch, int32_t num_q_heads,
@@ -840,6 +889,20 @@ double kvq_theoretical_bytes(int32_t num_layers, int32_t batch, int64_t seq_len,
                              int32_t num_kv_heads, int32_t head_dim, double bytes_per_elem) {
   return 2.0 * num_layers * double(batch) * double(seq_len) * num_kv_heads * head_dim *
          bytes_per_elem;
+}
+
+double kvq_theoretical_bytes_layers(int32_t n_layers, int32_t batch, const int64_t* seq_len,
+                                    const int32_t* num_kv_heads, const int32_t* head_dim,
+                                    double bytes_per_elem) {
+  if (n_layers < 1 || batch < 0 || seq_len == nullptr || num_kv_heads == nullptr ||
+      head_dim == nullptr || !(bytes_per_elem >= 0.0))
+    return -1.0;
+  double tokens = 0.0;   // Σ_l S_l·H_kv,l·D_l
+  for (int32_t l = 0; l < n_layers; ++l) {
+    if (seq_len[l] < 0 || num_kv_heads[l] < 0 || head_dim[l] < 0) return -1.0;
+    tokens += double(seq_len[l]) * num_kv_heads[l] * head_dim[l];
+  }
+  return 2.0 * double(batch) * bytes_per_elem * tokens;
 }
 
 }  // extern "C"

@@ -60,7 +60,7 @@ def test_struct_sizes_match_header(tmp_path):
         assert int(got[st]) == ctypes.sizeof(cls), st
         for f in fields[st]:
             assert int(got[f"{st}.{f}"]) == getattr(cls, f).offset, (st, f)
-    assert int(got["abi"]) == kq.kvq_abi_version() == kq.ABI_VERSION == 7
+    assert int(got["abi"]) == kq.kvq_abi_version() == kq.ABI_VERSION == 8
 
 
 def test_status_strings():
@@ -395,3 +395,41 @@ def test_ragged_decode_bytes_sum_sequences():
     c, _, _ = _ragged_host_cache(cfg, nq=nq, nr=nr)
     want = sum(bytes_model.decode_bytes_kivi(1, 8, 128, 2, 32, q, r) for q, r in zip(nq, nr))
     assert kq.kvq_decode_bytes(c, 64) == want
+
+
+def test_theoretical_bytes_layers_pins():
+    """The mixed-layer formula 2·B·b·Σ_l S_l·H_kv,l·D_l (the KV Cache
+    quantization page, §四.4), pinned by hand-worked values."""
+    # a 4096-token sliding-window layer and a 131072-token global layer,
+    # 8 KV heads of 128, fp16: 2·1·2·(4096 + 131072)·8·128 = 553648128
+    assert kq.kvq_theoretical_bytes_layers(1, [4096, 131072], [8, 8], [128, 128], 2.0) == 553648128
+    # layers with their own KV heads and head dims: 2·3·0.5·(100·4·128 + 50·2·64) = 172800
+    assert kq.kvq_theoretical_bytes_layers(3, [100, 50], [4, 2], [128, 64], 0.5) == 172800
+    # equal layers reduce to the uniform formula 2·L·B·S·H·D·b
+    assert (kq.kvq_theoretical_bytes_layers(1, [131072] * 32, [32] * 32, [128] * 32, 2.0)
+            == kq.kvq_theoretical_bytes(32, 1, 131072, 32, 128, 2.0) == 64 * 2 ** 30)
+    assert kq.kvq_theoretical_bytes_layers(1, [], [], [], 2.0) == -1.0
+    assert kq.kvq_theoretical_bytes_layers(1, [-1], [8], [128], 2.0) == -1.0
+    assert kq.kvq_theoretical_bytes_layers(1, [1], [8], [128], -2.0) == -1.0
+
+
+def test_decode_layers_checks_every_layer_before_any_launch():
+    """Each layer is checked before the first launch: a failing later layer
+    returns its own status (on this host a launch would report DEVICE)."""
+    P = 0x100000
+    cfg = kq.make_config("kivi", batch=2, num_kv_heads=4, capacity=512)
+    ok = _host_cache(cfg, 64, 10)
+    need = kq.kvq_decode_workspace_bytes(cfg, 8)
+    empty = _host_cache(cfg)
+    assert kq.kvq_decode_attention_layers([ok, empty], P, 8, P, P, need, None) == kq.KVQ_ERR_STATE
+    assert kq.kvq_decode_attention_layers([ok, None], P, 8, P, P, need, None) == kq.KVQ_ERR_INVALID_ARG
+    assert kq.kvq_decode_attention_layers([], P, 8, P, P, need, None) == kq.KVQ_ERR_INVALID_ARG
+    other_b = _host_cache(kq.make_config("kivi", batch=3, num_kv_heads=4, capacity=512), 64, 10)
+    assert kq.kvq_decode_attention_layers([ok, other_b], P, 8, P, P, need, None) == kq.KVQ_ERR_INVALID_ARG
+    big_cfg = kq.make_config("kivi", batch=2, num_kv_heads=4, capacity=8192)
+    big = _host_cache(big_cfg, 4096, 10)
+    assert kq.kvq_decode_workspace_bytes(big_cfg, 8) > need
+    assert kq.kvq_decode_attention_layers([ok, big], P, 8, P, P, need, None) == kq.KVQ_ERR_WORKSPACE
+    three = _host_cache(kq.make_config("kivi", batch=2, num_kv_heads=3, capacity=512), 64, 10)
+    assert kq.kvq_decode_attention_layers([ok, three], P, 8, P, P, need, None) == kq.KVQ_ERR_UNSUPPORTED
+    assert kq.kvq_decode_attention_layers([ok, ok], None, 8, P, P, need, None) == kq.KVQ_ERR_INVALID_ARG
