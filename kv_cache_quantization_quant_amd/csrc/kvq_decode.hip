@@ -5,7 +5,8 @@
 // kernels (kvq_decode_mfma.hip: KIVI groups and window on the matrix cores,
 // FP8 / FP16 tiles on the matrix cores) each write one partial (o[D], m, l)
 // per (b, query head, split), with m a log2-domain maximum and o, l relative
-// to it; this file merges them (log-sum-exp) into the output.
+// to it; this file merges them (log-sum-exp) into the output. With one split
+// per row the split kernels write o / l to the output themselves.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -77,7 +78,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(MergeArgs a) {
 
 }  // namespace
 
-// The split kernel of the cache's format, then the merge.
+// The split kernel of the cache's format, then the merge (none with one split
+// per row: the split kernel writes the output).
 hipError_t launch_decode(const DecodeArgs& a_in, hipStream_t s) {
   const DecodeArgs& a = a_in;
   hipError_t e = hipSuccess;
@@ -95,6 +97,7 @@ hipError_t launch_decode(const DecodeArgs& a_in, hipStream_t s) {
       return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
+  if (KVQ_DIRECT_SINGLE_SPLIT && a.n_split == 1) return hipSuccess;   // written by the split
   MergeArgs m;
   m.ws = a.ws;
   m.out = a.out;

@@ -760,6 +760,12 @@ __device__ __forceinline__ void wave_epilogue_and_merge(const DecodeArgs& a, con
         L = fmaf(f, mlw[2 * h + 1], L);
       }
     }
+    if (KVQ_DIRECT_SINGLE_SPLIT && a.n_split == 1) {
+      // one split per row: the merge would compute exactly O / L (its one
+      // weight is 2^0 = 1), so the output is written here and no merge runs
+      a.out[(int64_t(b) * a.Hq + hq0 + h) * kHeadDim + d] = O / L;
+      continue;
+    }
     float* part = a.ws + ((int64_t(b) * a.Hq + hq0 + h) * a.n_split + split) * kPart;
     part[d] = O;
     if (d == 0) {

@@ -116,6 +116,12 @@ enum SrcFormat : int { kSrcFp16 = 0, kSrcFp8 = 1, kSrcKivi2 = 2, kSrcKivi4 = 3, 
 
 // Split-K decode attention. Grid: n_split · B·H · head_chunks blocks in one
 // dimension, main-region splits first and window splits last.
+// 1: a decode with one split per row writes its output from the split
+// kernel, without the merge launch.
+#ifndef KVQ_DIRECT_SINGLE_SPLIT
+#define KVQ_DIRECT_SINGLE_SPLIT 1
+#endif
+
 struct DecodeArgs {
   int src;                // SrcFormat of the main region
   int kbits, vbits;       // KIVI K and V bit widths

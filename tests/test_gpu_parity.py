@@ -799,3 +799,27 @@ def test_kivi_many_blocks_shape(kq, bits, vbits, gc, det):
     _compare_kivi_state(dc, oc)
     _say(f"  worst max abs err {worst:.3e}, flushes at {oc.flush_steps}")
     assert oc.flush_steps and worst <= ATOL
+
+
+@pytest.mark.parametrize("fmt", ["kivi", "fp16"])
+def test_one_split_per_row_writes_output_directly(kq, fmt):
+    """1024 (b, KV head) blocks of one query head each, more than the device
+    holds at once, so the decode plan has one split per row and the split
+    kernel writes o / l to the output itself (no merge launch): attention
+    within the bound of the oracle, KIVI (with its FP16 window) and FP16."""
+    B, H, Hq, S = 64, 16, 16, 1000
+    _say(f"[one split per row] fmt={fmt} B={B} H={H} Hq={Hq} S={S}")
+    k, v = _kv(B, H, S)
+    dc = kq.DeviceCache(kq.make_config(fmt, batch=B, num_kv_heads=H, capacity=S))
+    dc.prefill(k, v)
+    if fmt == "kivi":
+        oc = ocache.KiviCache(B, H, D, 2, 32, 128, S)
+    else:
+        oc = ocache.Fp16Cache(B, H, D, S)
+    oc.prefill(_np(k), _np(v))
+    q = synth.make_q(B, Hq, D, device="cuda")
+    out = dc.decode(q)
+    torch.cuda.synchronize()
+    err = _att_err(_np(out), oc.attention(_np(q)))
+    _say(f"  max abs err {err:.3e}")
+    assert err <= ATOL
