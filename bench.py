@@ -290,6 +290,33 @@ def run_extra(torch, kq, synth):
         _log(f"[bench] extra {key}: {out[key]}")
     kv_cache.clear()
     torch.cuda.empty_cache()
+    # one call over four layers of the 32K GQA shape, three KIVI 2-bit and one
+    # left unquantized (FP16), as a model with a sensitive layer kept at full
+    # precision would hold them; the same K/V in every layer
+    c = synth.CONFIGS["gqa70b_32k"]
+    B, H, Hq, S = c["batch"], c["num_kv_heads"], c["num_q_heads"], c["seq_len"]
+    k = synth.make_k(B, H, 0, S, D, device="cuda")
+    v = synth.make_v(B, H, 0, S, D, device="cuda")
+    layers = []
+    for fmt in ("kivi", "kivi", "fp16", "kivi"):
+        lc = kq.DeviceCache(kq.make_config(fmt, bits=2 if fmt == "kivi" else None, batch=B,
+                                           num_kv_heads=H, capacity=S))
+        lc.prefill(k, v)
+        layers.append(lc)
+    del k, v
+    ql = synth.make_q(len(layers) * B, Hq, D, device="cuda").view(len(layers), B, Hq, D)
+    ol = torch.empty_like(ql)
+    wsl = max((lc.make_workspace(Hq) for lc in layers), key=lambda t: t.numel())
+    dec = statistics.median(time_launches(
+        torch, lambda: kq.decode_layers(layers, ql, out=ol, workspace=wsl), 10, scrub))
+    nbytes = sum(lc.decode_bytes(Hq) for lc in layers)
+    key = "gqa70b_32k/layers_kivi3_fp16_1"
+    out[key] = {"decode_us": round(dec, 2), "decode_bytes": nbytes,
+                "decode_gbs": round(nbytes / (dec * 1e-6) / 1e9, 1),
+                "decode_frac_hbm": round(nbytes / (dec * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    _log(f"[bench] extra {key}: {out[key]}")
+    del layers, ql, ol, wsl
+    torch.cuda.empty_cache()
     # accuracy side report: FP8 and KIVI attention against FP16 attention
     ref = outs["fp16"]
     acc = {}
