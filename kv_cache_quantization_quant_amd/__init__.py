@@ -212,16 +212,26 @@ def decode_layers(caches, q: torch.Tensor, out: torch.Tensor | None = None,
                   workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """One decode per layer (kvq_decode_attention_layers). caches: DeviceCache
     per layer; q: contiguous fp32 [L, B, Hq, D] → out fp32 [L, B, Hq, D]."""
-    assert q.dtype == torch.float32 and q.is_contiguous() and q.dim() == 4
-    assert q.shape[0] == len(caches)
+    if len(caches) < 1:
+        raise ValueError("decode_layers: at least one layer")
+    c0 = caches[0]
+    if q.dim() != 4:
+        raise ValueError(f"q: shape {tuple(q.shape)}, expected [layers, batch, Hq, D]")
     hq = q.shape[2]
+    shape = (len(caches), c0.cfg.batch, hq, c0.cfg.head_dim)
+    for c in caches:
+        if c.cfg.batch != c0.cfg.batch or c.cfg.head_dim != c0.cfg.head_dim:
+            raise ValueError("decode_layers: every layer needs the same batch and head_dim")
+    _require(q, "q", torch.float32, shape, c0.device)
     if out is None:
         out = torch.empty_like(q)
+    _require(out, "out", torch.float32, shape, c0.device)
     if workspace is None:
         n = max(c.workspace_bytes(hq) for c in caches)
         if n == 0:
             raise KvqError(KVQ_ERR_INVALID_ARG, "kvq_decode_workspace_bytes")
         workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    _require(workspace, "workspace", torch.uint8, (workspace.numel(),), c0.device)
     _check(kvq_decode_attention_layers([c.cache for c in caches], q.data_ptr(), hq,
                                        out.data_ptr(), workspace.data_ptr(), workspace.numel(),
                                        _stream_handle(stream)), "kvq_decode_attention_layers")
@@ -249,8 +259,10 @@ def make_config(fmt: str = "kivi", bits: int | None = None, group_size: int = 32
 def quantize_query_fp8(q: torch.Tensor, stream=None) -> tuple[torch.Tensor, torch.Tensor]:
     """q: contiguous fp32 [B, Hq, D] on the device → (E4M3 codes uint8
     [B, Hq, D], scales fp32 [B, Hq])."""
-    assert q.dtype == torch.float32 and q.is_contiguous() and q.dim() == 3
+    if q.dim() != 3:
+        raise ValueError(f"q: shape {tuple(q.shape)}, expected [batch, Hq, D]")
     B, Hq, D = q.shape
+    _require(q, "q", torch.float32, (B, Hq, D))
     codes = torch.empty(q.shape, dtype=torch.uint8, device=q.device)
     scales = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     _check(kvq_quantize_query_fp8(q.data_ptr(), B, Hq, D, codes.data_ptr(), scales.data_ptr(),
@@ -261,6 +273,25 @@ def quantize_query_fp8(q: torch.Tensor, stream=None) -> tuple[torch.Tensor, torc
 def _check(status: int, what: str):
     if status != KVQ_OK:
         raise KvqError(status, what)
+
+
+def _require(t, name: str, dtype: torch.dtype, shape, device: torch.device | None = None):
+    """Raises ValueError unless t is a contiguous device tensor of this dtype
+    and shape (and on `device`, when given). The C ABI takes bare pointers, so
+    a tensor of the wrong shape would let the kernels read or write outside
+    it: every tensor is checked here, before its pointer goes to the library."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor, got device {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, the cache is on {device}")
 
 
 _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
@@ -304,7 +335,8 @@ class DeviceCache:
                 t = torch.zeros(nbytes, dtype=torch.uint8, device=device)
                 self.buffers[name] = t
                 setattr(self.cache, name, t.data_ptr())
-        self.device = device
+        # the device every buffer sits on ("cuda" resolved to its index)
+        self.device = next(iter(self.buffers.values())).device
 
     # fill state
     @property
@@ -329,9 +361,18 @@ class DeviceCache:
     def prefill_ragged(self, k: torch.Tensor, v: torch.Tensor, seq_lens, stream=None):
         """k, v: contiguous fp16 [B, H, max_len, D] on the device, sequence b in
         its first seq_lens[b] tokens."""
-        assert self.ragged
-        assert k.dtype == torch.float16 and v.dtype == torch.float16
-        assert k.is_contiguous() and v.is_contiguous() and k.shape == v.shape
+        if not self.ragged:
+            raise ValueError("prefill_ragged needs a cache made with ragged=True")
+        c = self.cfg
+        if k.dim() != 4:
+            raise ValueError(f"k: shape {tuple(k.shape)}, expected [B, H, max_len, D]")
+        if len(seq_lens) != c.batch:
+            raise ValueError(f"seq_lens: {len(seq_lens)} entries, expected batch = {c.batch}")
+        if tuple(v.shape) != tuple(k.shape):
+            raise ValueError(f"v: shape {tuple(v.shape)}, k has {tuple(k.shape)}")
+        shape = (c.batch, c.num_kv_heads, k.shape[2], c.head_dim)
+        _require(k, "k", torch.float16, shape, self.device)
+        _require(v, "v", torch.float16, shape, self.device)
         lens = (c_int64 * len(seq_lens))(*[int(x) for x in seq_lens])
         _check(kvq_prefill_quantize_ragged(self.cache, k.data_ptr(), v.data_ptr(), k.shape[2],
                                            lens, _stream_handle(stream)),
@@ -339,14 +380,23 @@ class DeviceCache:
 
     def prefill(self, k: torch.Tensor, v: torch.Tensor, stream=None):
         """k, v: contiguous fp16 [B, H, S, D] on the device."""
-        assert k.dtype == torch.float16 and v.dtype == torch.float16
-        assert k.is_contiguous() and v.is_contiguous() and k.shape == v.shape
+        c = self.cfg
+        if k.dim() != 4:
+            raise ValueError(f"k: shape {tuple(k.shape)}, expected [B, H, S, D]")
+        if tuple(v.shape) != tuple(k.shape):
+            raise ValueError(f"v: shape {tuple(v.shape)}, k has {tuple(k.shape)}")
+        shape = (c.batch, c.num_kv_heads, k.shape[2], c.head_dim)
+        _require(k, "k", torch.float16, shape, self.device)
+        _require(v, "v", torch.float16, shape, self.device)
         _check(kvq_prefill_quantize(self.cache, k.data_ptr(), v.data_ptr(), k.shape[2],
                                     _stream_handle(stream)), "kvq_prefill_quantize")
 
     def append(self, k1: torch.Tensor, v1: torch.Tensor, stream=None):
         """k1, v1: contiguous fp16 [B, H, D] on the device."""
-        assert k1.dtype == torch.float16 and k1.is_contiguous() and v1.is_contiguous()
+        c = self.cfg
+        shape = (c.batch, c.num_kv_heads, c.head_dim)
+        _require(k1, "k1", torch.float16, shape, self.device)
+        _require(v1, "v1", torch.float16, shape, self.device)
         _check(kvq_append_token(self.cache, k1.data_ptr(), v1.data_ptr(),
                                 _stream_handle(stream)), "kvq_append_token")
 
@@ -362,12 +412,18 @@ class DeviceCache:
     def decode(self, q: torch.Tensor, out: torch.Tensor | None = None,
                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
         """q: contiguous fp32 [B, Hq, D] → out fp32 [B, Hq, D]."""
-        assert q.dtype == torch.float32 and q.is_contiguous()
+        c = self.cfg
+        if q.dim() != 3:
+            raise ValueError(f"q: shape {tuple(q.shape)}, expected [B, Hq, D]")
         hq = q.shape[1]
+        shape = (c.batch, hq, c.head_dim)
+        _require(q, "q", torch.float32, shape, self.device)
         if out is None:
             out = torch.empty_like(q)
+        _require(out, "out", torch.float32, shape, self.device)
         if workspace is None:
             workspace = self.make_workspace(hq)
+        _require(workspace, "workspace", torch.uint8, (workspace.numel(),), self.device)
         _check(kvq_decode_attention(self.cache, q.data_ptr(), hq, out.data_ptr(),
                                     workspace.data_ptr(), workspace.numel(),
                                     _stream_handle(stream)), "kvq_decode_attention")

@@ -219,6 +219,22 @@ def test_decode_bytes_match_oracle(fmt, bits, vbits, per_head):
     assert kq.kvq_decode_bytes(_host_cache(cfg), 12) == -1          # 12 % 8 != 0
 
 
+@pytest.mark.parametrize("fmt,bits,B,H,S,nq,nr,per_head,want", [
+    # the benchmark workloads' step-0 totals, worked out term by term in
+    # tests/test_oracle_bytes.py
+    ("kivi", 2, 8, 32, 4096, 3968, 128, 0, 122421248),
+    ("kivi", 2, 16, 8, 32768, 32640, 128, 0, 442892288),
+    ("kivi", 4, 64, 32, 8192, 8064, 128, 0, 2908749824),
+    ("kivi", 2, 4, 8, 131072, 130944, 128, 0, 437878784),
+    ("fp8", 8, 4, 8, 131072, 131072, 0, 0, 1073741832),
+    ("fp8", 8, 4, 8, 131072, 131072, 0, 1, 1073741888),
+    ("fp16", 16, 4, 8, 131072, 131072, 0, 0, 2147483648)])
+def test_decode_bytes_workload_totals(fmt, bits, B, H, S, nq, nr, per_head, want):
+    cfg = kq.make_config(fmt, bits=bits, batch=B, num_kv_heads=H, capacity=S,
+                         scale_per_head=per_head)
+    assert kq.kvq_decode_bytes(_host_cache(cfg, nq, nr), 8 * H) == want
+
+
 def test_theoretical_bytes_pages():
     # 512 KiB/token and 64 GiB at 128K for 32 layers, 32 KV heads, D = 128, BF16
     assert kq.kvq_theoretical_bytes(32, 1, 1, 32, 128, 2.0) == 524288

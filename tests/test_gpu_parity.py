@@ -488,9 +488,10 @@ def test_query_fp8_codes(kq):
     ("fp8_e5m2", 0, 2, 2, 16, 500, 20), ("fp8", 0, 1, 1, 2, 31, 3),
 ])
 def test_fp8_attention_in_fp8_domain(kq, fmt, per_head, B, H, Hq, S, steps):
-    """Decode with the query quantized to E4M3 and the scores on the FP8
-    matrix cores (E4M3 × E4M3, or E5M2 K × E4M3 q): attention within the bound
-    of the oracle's attention over the dequantized query and cache."""
+    """Decode with the query quantized to E4M3 and the scores taken in the
+    FP8 domain (E4M3 × E4M3, or E5M2 K × E4M3 q: exact fp8 × fp8 products,
+    summed on the f16 matrix cores): attention within the bound of the
+    oracle's attention over the dequantized query and cache."""
     C = S + steps
     k, v = _kv(B, H, C)
     dc = kq.DeviceCache(kq.make_config(fmt, batch=B, num_kv_heads=H, capacity=C,
@@ -818,8 +819,14 @@ def test_one_split_per_row_writes_output_directly(kq, fmt):
         oc = ocache.Fp16Cache(B, H, D, S)
     oc.prefill(_np(k), _np(v))
     q = synth.make_q(B, Hq, D, device="cuda")
-    out = dc.decode(q)
+    # the workspace only ever holds split partials: with one split per row
+    # nothing may be written there (a plan with more splits would write them
+    # and fail here instead of silently testing the merge path)
+    ws = dc.make_workspace(Hq)
+    ws.fill_(0xFF)
+    out = dc.decode(q, workspace=ws)
     torch.cuda.synchronize()
+    assert bool((ws == 0xFF).all()), "split partials written: the plan has more than one split"
     err = _att_err(_np(out), oc.attention(_np(q)))
     _say(f"  max abs err {err:.3e}")
     assert err <= ATOL

@@ -99,3 +99,80 @@ def test_kivi_decode_bytes_decomposition(bits):
 def test_fp8_fp16_decode_bytes():
     assert bm.decode_bytes_fp16(2, 3, 128, 10) == bm.kv_cache_bytes(1, 2, 10, 3, 128, 2)
     assert bm.decode_bytes_fp8(2, 3, 128, 10) == bm.kv_cache_bytes(1, 2, 10, 3, 128, 1) + 8
+
+
+# ---- decode step bytes of the benchmark workloads, worked out by hand ----
+# Each total below is written out term by term from the workload's shape
+# (prefill split: the newest 128 tokens stay in the fp16 window, the rest are
+# whole 32-token groups), so a dropped, doubled or mis-scaled term of the
+# byte model fails one of them. Per (b, KV head) block, with n = grouped
+# tokens, r = window tokens, D = 128:
+#   K codes n·D·b/8, K scale + zero (n/G)·D·4·2, V codes n·D·b_V/8,
+#   V scale + zero n·4·2 (per run of channels with V sub-groups),
+#   window 2·r·D·2.
+
+def test_decode_bytes_llama2_7b_layer():
+    # B=8, 32 MHA heads, S=4096, 2-bit: n = 3968, r = 128
+    per = (3968 * 32          # K codes: 126,976
+           + 124 * 1024       # K scale + zero: 126,976
+           + 3968 * 32        # V codes: 126,976
+           + 3968 * 8         # V scale + zero: 31,744
+           + 65536)           # window: 65,536
+    assert per == 478208
+    assert bm.decode_bytes_kivi(8, 32, 128, 2, 32, 3968, 128) == 256 * per == 122421248
+
+
+def test_decode_bytes_gqa_32k_layer():
+    # B=16, 8 KV heads, S=32768, 2-bit, before the first append: n = 32640, r = 128
+    per = 1044480 + 1044480 + 1044480 + 261120 + 65536
+    assert per == 3460096
+    assert bm.decode_bytes_kivi(16, 8, 128, 2, 32, 32640, 128) == 128 * per == 442892288
+    # after the first append flushed the window: n = 32768, r = 1
+    per1 = 1048576 + 1048576 + 1048576 + 262144 + 512
+    assert bm.decode_bytes_kivi(16, 8, 128, 2, 32, 32768, 1) == 128 * per1 == 436273152
+
+
+def test_decode_bytes_large_batch_4bit():
+    # B=64, 32 heads, S=8192, 4-bit: n = 8064, r = 128
+    per = (8064 * 64          # K codes: 516,096
+           + 252 * 1024       # K scale + zero: 258,048
+           + 8064 * 64        # V codes: 516,096
+           + 8064 * 8         # V scale + zero: 64,512
+           + 65536)
+    assert per == 1420288
+    assert bm.decode_bytes_kivi(64, 32, 128, 4, 32, 8064, 128) == 2048 * per == 2908749824
+
+
+def test_decode_bytes_long_context_three_formats():
+    # B=4, 8 KV heads, S=131072
+    B, H, S = 4, 8, 131072
+    # KIVI 2-bit: n = 130944, r = 128
+    per = 4190208 + 4190208 + 4190208 + 1047552 + 65536
+    assert per == 13683712
+    assert bm.decode_bytes_kivi(B, H, 128, 2, 32, 130944, 128) == 32 * per == 437878784
+    # FP8: one byte per K and V element, plus s_K and s_V (fp32)
+    assert bm.decode_bytes_fp8(B, H, 128, S) == 1073741824 + 8 == 1073741832
+    # FP8 with one (s_K, s_V) pair per KV head: 8 pairs
+    assert bm.decode_bytes_fp8(B, H, 128, S, per_head=True) == 1073741824 + 64
+    # FP16: two bytes per K and V element
+    assert bm.decode_bytes_fp16(B, H, 128, S) == 2147483648
+
+
+def test_decode_bytes_variant_terms():
+    """The V width and V channel sub-group terms on the 32K GQA layer
+    (n = 32640, r = 128), against hand-computed per-block bytes."""
+    # K 4-bit / V 2-bit: K codes double, V codes stay
+    per = 2088960 + 1044480 + 1044480 + 261120 + 65536
+    assert bm.decode_bytes_kivi(16, 8, 128, 4, 32, 32640, 128, v_bits=2) == 128 * per == 576585728
+    # K 2-bit / V 4-bit: the same total, the other side doubled
+    per = 1044480 + 1044480 + 2088960 + 261120 + 65536
+    assert bm.decode_bytes_kivi(16, 8, 128, 2, 32, 32640, 128, v_bits=4) == 128 * per
+    # V scale and zero per run of 32 channels: four pairs per token
+    per = 1044480 + 1044480 + 1044480 + 4 * 261120 + 65536
+    assert bm.decode_bytes_kivi(16, 8, 128, 2, 32, 32640, 128, v_group_channels=32) \
+        == 128 * per == 543162368
+    # G = 64 and 128: K metadata halves / quarters, nothing else moves
+    per64 = 1044480 + 1044480 // 2 + 1044480 + 261120 + 65536
+    per128 = 1044480 + 1044480 // 4 + 1044480 + 261120 + 65536
+    assert bm.decode_bytes_kivi(16, 8, 128, 2, 64, 32640, 128) == 128 * per64 == 376045568
+    assert bm.decode_bytes_kivi(16, 8, 128, 2, 128, 32640, 128) == 128 * per128 == 342622208
