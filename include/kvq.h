@@ -25,8 +25,10 @@
  * ---------------------------------------------------------------------------
  * - Memory. The caller allocates and frees every device buffer (sizes from
  *   kvq_layout_query / kvq_decode_workspace_bytes). The library never
- *   allocates device memory, keeps no global state, and never synchronizes
- *   the device. Pointers marked "device" must point to device memory of the
+ *   allocates device memory and never synchronizes the device; its only
+ *   global state is the per-GPU partials array of kvq_decode_attention_static
+ *   (KVQ_STATIC_WORKSPACE_BYTES, part of its loaded device code) and cached
+ *   device properties. Pointers marked "device" must point to device memory of the
  *   current HIP device; "host" pointers to host memory. Every device pointer
  *   (cache buffers, inputs, outputs, workspace) must be 16-byte aligned
  *   (else KVQ_ERR_INVALID_ARG, or KVQ_ERR_WORKSPACE for the workspace).
@@ -135,7 +137,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 8
+#define KVQ_ABI_VERSION 9
 
 typedef enum {
   KVQ_OK = 0,
@@ -322,6 +324,32 @@ kvq_status kvq_decode_attention_layers(const kvq_cache* const* caches, int32_t n
                                        const float* q, int32_t num_q_heads, float* out,
                                        void* workspace, size_t workspace_bytes,
                                        void* stream);
+
+/* Size in bytes of the device array kvq_decode_attention_static keeps its
+ * split partials in (one array per GPU the library runs on, reserved when
+ * the library's device code is loaded on that GPU and held until the
+ * process ends). */
+#define KVQ_STATIC_WORKSPACE_BYTES (32u << 20)
+
+/* kvq_decode_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops or harnesses that forbid
+ * allocation): the same decode with the same arguments, semantics and errors,
+ * but no workspace argument. The split partials go to the library's own
+ * device array of KVQ_STATIC_WORKSPACE_BYTES on the current GPU; the call
+ * allocates nothing (no hipMalloc, no library allocation).
+ * Limit: KVQ_ERR_WORKSPACE, with nothing enqueued, when the partials of the
+ * decode as planned (B · Hq · splits · (D + 2) · 4 bytes) would not fit;
+ * a configuration with kvq_decode_workspace_bytes(cfg, Hq) ≤
+ * KVQ_STATIC_WORKSPACE_BYTES always fits. KVQ_ERR_DEVICE if the array's
+ * address cannot be found on the current GPU.
+ * Sharing: every call on one GPU uses that GPU's one array, and the array
+ * keeps the last call's contents. Calls in stream order on one stream are
+ * safe; calls that may run at the same time on one GPU (several streams,
+ * several host threads without ordering) race on the array and must be
+ * ordered by the caller. Nothing in the array needs clearing: each partial
+ * is written before it is read. */
+kvq_status kvq_decode_attention_static(const kvq_cache* cache, const float* q,
+                                       int32_t num_q_heads, float* out, void* stream);
 
 /* Per-query-head E4M3 quantization of decode queries, the first step of
  * attention in the FP8 domain ([Tutorial] §十八.7; [KIVI-page] §6): one scale

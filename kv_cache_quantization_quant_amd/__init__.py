@@ -28,7 +28,8 @@ KVQ_ERR_STATE = 4
 KVQ_ERR_DEVICE = 5
 KVQ_ERR_WORKSPACE = 6
 
-ABI_VERSION = 8        # KVQ_ABI_VERSION of include/kvq.h
+ABI_VERSION = 9        # KVQ_ABI_VERSION of include/kvq.h
+STATIC_WORKSPACE_BYTES = 32 << 20   # KVQ_STATIC_WORKSPACE_BYTES
 
 KVQ_FMT_FP16 = 0
 KVQ_FMT_FP8_E4M3 = 1
@@ -92,6 +93,8 @@ def _load():
         "kvq_decode_workspace_bytes": (c_size_t, [POINTER(KvqConfig), c_int32]),
         "kvq_decode_attention": (c_int32, [POINTER(KvqCache), c_void_p, c_int32, c_void_p,
                                            c_void_p, c_size_t, c_void_p]),
+        "kvq_decode_attention_static": (c_int32, [POINTER(KvqCache), c_void_p, c_int32,
+                                                  c_void_p, c_void_p]),
         "kvq_decode_attention_layers": (c_int32, [POINTER(POINTER(KvqCache)), c_int32,
                                                   c_void_p, c_int32, c_void_p, c_void_p,
                                                   c_size_t, c_void_p]),
@@ -121,7 +124,8 @@ ABI_SYMBOLS = ("kvq_abi_version", "kvq_status_str", "kvq_layout_query", "kvq_cac
                "kvq_append_token",
                "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_bytes",
                "kvq_quantize_query_fp8", "kvq_theoretical_bytes",
-               "kvq_decode_attention_layers", "kvq_theoretical_bytes_layers")
+               "kvq_decode_attention_layers", "kvq_theoretical_bytes_layers",
+               "kvq_decode_attention_static")
 
 
 # ------------------------------------------------- one-to-one ABI wrappers ---
@@ -170,6 +174,11 @@ def kvq_decode_attention(cache: KvqCache, q_ptr: int, num_q_heads: int, out_ptr:
                          ws_ptr: int, ws_bytes: int, stream: int | None) -> int:
     return lib.kvq_decode_attention(byref(cache), q_ptr, num_q_heads, out_ptr, ws_ptr,
                                     ws_bytes, stream)
+
+
+def kvq_decode_attention_static(cache: KvqCache, q_ptr: int, num_q_heads: int, out_ptr: int,
+                                stream: int | None) -> int:
+    return lib.kvq_decode_attention_static(byref(cache), q_ptr, num_q_heads, out_ptr, stream)
 
 
 def kvq_decode_attention_layers(caches, q_ptr: int, num_q_heads: int, out_ptr: int,
@@ -427,6 +436,19 @@ class DeviceCache:
         _check(kvq_decode_attention(self.cache, q.data_ptr(), hq, out.data_ptr(),
                                     workspace.data_ptr(), workspace.numel(),
                                     _stream_handle(stream)), "kvq_decode_attention")
+        return out
+
+    def decode_static(self, q: torch.Tensor, out: torch.Tensor, stream=None) -> torch.Tensor:
+        """kvq_decode_attention_static: the decode with the library's own
+        per-GPU partials array, allocating nothing (out must be given)."""
+        c = self.cfg
+        if q.dim() != 3:
+            raise ValueError(f"q: shape {tuple(q.shape)}, expected [B, Hq, D]")
+        shape = (c.batch, q.shape[1], c.head_dim)
+        _require(q, "q", torch.float32, shape, self.device)
+        _require(out, "out", torch.float32, shape, self.device)
+        _check(kvq_decode_attention_static(self.cache, q.data_ptr(), q.shape[1], out.data_ptr(),
+                                           _stream_handle(stream)), "kvq_decode_attention_static")
         return out
 
     def decode_bytes(self, num_q_heads: int) -> int:

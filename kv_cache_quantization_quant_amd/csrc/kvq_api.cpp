@@ -703,9 +703,10 @@ size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t num_q_heads) {
 
 }  // extern "C"
 
-// Every check of one decode call, before anything is enqueued.
-static kvq_status decode_check(const kvq_cache* cache, const float* q, int32_t num_q_heads,
-                               float* out, void* workspace, size_t workspace_bytes) {
+// Every check of one decode call but the workspace's, before anything is
+// enqueued.
+static kvq_status decode_check_args(const kvq_cache* cache, const float* q, int32_t num_q_heads,
+                                    float* out) {
   if (cache == nullptr || q == nullptr || out == nullptr) return KVQ_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(out)) return KVQ_ERR_INVALID_ARG;
   const kvq_status vs = validate_config(&cache->cfg);
@@ -721,6 +722,14 @@ static kvq_status decode_check(const kvq_cache* cache, const float* q, int32_t n
   } else if (cache->n_quant + cache->n_resid <= 0) {
     return KVQ_ERR_STATE;
   }
+  return KVQ_OK;
+}
+
+// Every check of one decode call with a caller's workspace.
+static kvq_status decode_check(const kvq_cache* cache, const float* q, int32_t num_q_heads,
+                               float* out, void* workspace, size_t workspace_bytes) {
+  const kvq_status st = decode_check_args(cache, q, num_q_heads, out);
+  if (st != KVQ_OK) return st;
   const size_t need = kvq_decode_workspace_bytes(&cache->cfg, num_q_heads);
   if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
     return KVQ_ERR_WORKSPACE;
@@ -728,8 +737,10 @@ static kvq_status decode_check(const kvq_cache* cache, const float* q, int32_t n
 }
 
 // The launches of one checked decode call (dry: plan only, enqueue nothing).
+// WORKSPACE when the plan's partials do not fit in workspace_bytes.
 static kvq_status decode_enqueue(const kvq_cache* cache, const float* q, int32_t num_q_heads,
-                                 float* out, void* workspace, void* stream, bool dry) {
+                                 float* out, void* workspace, size_t workspace_bytes,
+                                 void* stream, bool dry) {
   const bool ragged = is_ragged(cache);
 
   const Dims d = dims_of(cache->cfg);
@@ -758,6 +769,9 @@ static kvq_status decode_enqueue(const kvq_cache* cache, const float* q, int32_t
   const Plan p = ragged ? make_plan_ragged(d, nq, cache, target)
                         : make_plan(d, nq, cache->n_quant, n_win, target);
   if (p.n_split > max_splits(d, nq)) return KVQ_ERR_WORKSPACE;
+  const double part_bytes =
+      double(d.B) * num_q_heads * p.n_split * (kHeadDim + 2) * sizeof(float);
+  if (part_bytes > double(workspace_bytes)) return KVQ_ERR_WORKSPACE;
   if (dry) return KVQ_OK;
 
   a.B = int(d.B);
@@ -808,7 +822,17 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q, int32_t 
                                 void* stream) {
   const kvq_status st = decode_check(cache, q, num_q_heads, out, workspace, workspace_bytes);
   if (st != KVQ_OK) return st;
-  return decode_enqueue(cache, q, num_q_heads, out, workspace, stream, false);
+  return decode_enqueue(cache, q, num_q_heads, out, workspace, workspace_bytes, stream, false);
+}
+
+kvq_status kvq_decode_attention_static(const kvq_cache* cache, const float* q,
+                                       int32_t num_q_heads, float* out, void* stream) {
+  const kvq_status st = decode_check_args(cache, q, num_q_heads, out);
+  if (st != KVQ_OK) return st;
+  void* ws = nullptr;
+  if (kvq::static_workspace(&ws) != hipSuccess) return KVQ_ERR_DEVICE;
+  return decode_enqueue(cache, q, num_q_heads, out, ws, KVQ_STATIC_WORKSPACE_BYTES, stream,
+                        false);
 }
 
 kvq_status kvq_decode_attention_layers(const kvq_cache* const* caches, int32_t n_layers,
@@ -829,12 +853,12 @@ kvq_status kvq_decode_attention_layers(const kvq_cache* const* caches, int32_t n
   }
   for (int32_t l = 0; l < n_layers; ++l) {
     const kvq_status st = decode_enqueue(caches[l], q + l * row, num_q_heads, out + l * row,
-                                         workspace, stream, true);
+                                         workspace, workspace_bytes, stream, true);
     if (st != KVQ_OK) return st;
   }
   for (int32_t l = 0; l < n_layers; ++l) {
     const kvq_status st = decode_enqueue(caches[l], q + l * row, num_q_heads, out + l * row,
-                                         workspace, stream, false);
+                                         workspace, workspace_bytes, stream, false);
     if (st != KVQ_OK) return st;
   }
   return KVQ_OK;

@@ -12,6 +12,9 @@
 
 #include <math.h>
 
+#include <mutex>
+
+#include "../../include/kvq.h"
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -76,7 +79,32 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(MergeArgs a) {
   *reinterpret_cast<float2*>(a.out + row * kHeadDim + 2 * lane) = make_float2(o0 / L, o1 / L);
 }
 
+// Split partials of kvq_decode_attention_static: one array per GPU (each
+// device that loads this code object gets its own copy), never passed to a
+// kernel by name — host code takes its device address from static_workspace.
+static __device__ __align__(256) unsigned char scratch[KVQ_STATIC_WORKSPACE_BYTES];
+
 }  // namespace
+
+hipError_t static_workspace(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 // The split kernel of the cache's format, then the merge (none with one split
 // per row: the split kernel writes the output).

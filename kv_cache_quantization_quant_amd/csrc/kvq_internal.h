@@ -183,6 +183,10 @@ struct QueryQuantArgs {
 
 hipError_t launch_query_fp8(const QueryQuantArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// Device address of the current GPU's split-partial array of
+// kvq_decode_attention_static (KVQ_STATIC_WORKSPACE_BYTES), looked up once per
+// device with that device current.
+hipError_t static_workspace(void** ptr);
 // Workgroups of the split kernel that a.src, a.kbits, a.vbits, a.nvs and a.qfp8
 // select that the current device holds at once (compute units × resident
 // workgroups per unit, from the kernel's register and LDS use); 0 if the

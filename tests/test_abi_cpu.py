@@ -60,7 +60,7 @@ def test_struct_sizes_match_header(tmp_path):
         assert int(got[st]) == ctypes.sizeof(cls), st
         for f in fields[st]:
             assert int(got[f"{st}.{f}"]) == getattr(cls, f).offset, (st, f)
-    assert int(got["abi"]) == kq.kvq_abi_version() == kq.ABI_VERSION == 8
+    assert int(got["abi"]) == kq.kvq_abi_version() == kq.ABI_VERSION == 9
 
 
 def test_status_strings():
@@ -293,6 +293,14 @@ def test_decode_errors_before_any_launch():
     assert kq.kvq_decode_attention(c, P + 4, 8, P, P, need, None) == kq.KVQ_ERR_INVALID_ARG
     empty = _host_cache(cfg)
     assert kq.kvq_decode_attention(empty, P, 8, P, P, need, None) == kq.KVQ_ERR_STATE
+    # the allocation-free variant checks the same arguments before it looks
+    # up its device array
+    assert kq.kvq_decode_attention_static(c, P, 6, P, None) == kq.KVQ_ERR_UNSUPPORTED
+    assert kq.kvq_decode_attention_static(c, P, 0, P, None) == kq.KVQ_ERR_INVALID_ARG
+    assert kq.kvq_decode_attention_static(c, None, 8, P, None) == kq.KVQ_ERR_INVALID_ARG
+    assert kq.kvq_decode_attention_static(c, P + 4, 8, P, None) == kq.KVQ_ERR_INVALID_ARG
+    assert kq.kvq_decode_attention_static(c, P, 8, P + 4, None) == kq.KVQ_ERR_INVALID_ARG
+    assert kq.kvq_decode_attention_static(empty, P, 8, P, None) == kq.KVQ_ERR_STATE
 
 
 def test_workspace_bound_covers_every_state():
