@@ -316,3 +316,112 @@ class Fp16Cache:
     def attention(self, q):
         Kh, Vh = self.dequantized()
         return attention.decode_attention(q, Kh, Vh)
+
+
+class PagedKiviCache:
+    """A ragged KIVI batch whose grouped region lives in a pool of pages
+    ([Tutorial] §十三.1: paged attention maps each sequence's logical token
+    blocks onto discrete physical blocks, and quantization and paging
+    compose).
+
+    Reading (the pages give no page layout): a page holds P consecutive
+    tokens of every KV head of one sequence — P a power of two, a multiple of
+    the group size G and of the 32-token V tile, so pages hold whole groups —
+    laid out as one sequence's contiguous buffers restricted to those tokens:
+      k_codes [NP][H][P][D·b/32],  v_codes [NP][H][P/32][D][32·b_V/32],
+      k_scale, k_zero [NP][H][P/G][D],  v_scale, v_zero [NP][H][P] (or
+      [NP][H][P][D/Gc] with V channel sub-groups).
+    Logical page j of sequence b (its tokens [jP, jP + P)) is physical page
+    table[b][j]. Only the grouped region is paged; the FP16 window stays per
+    sequence (k_resid, v_resid [B][H][Rcap][D]). Quantization, flushes and
+    attention are those of the ragged cache (each sequence alone, as a batch
+    of one): paging changes where the grouped data sits, not what it is.
+    Pages that no sequence has written stay zero."""
+
+    def __init__(self, batch, num_kv_heads, head_dim, bits, group, residual, capacity,
+                 page_tokens, num_pages, table, v_bits=None, v_group_channels=None):
+        P = page_tokens
+        assert P >= VT and P & (P - 1) == 0 and P % group == 0
+        self.ragged = RaggedKiviCache(batch, num_kv_heads, head_dim, bits, group, residual,
+                                      capacity, v_bits=v_bits, v_group_channels=v_group_channels)
+        self.B, self.H, self.D, self.G, self.P, self.NP = (batch, num_kv_heads, head_dim, group,
+                                                           P, num_pages)
+        self.max_pages = -(-capacity // P)
+        self.table = np.asarray(table, np.int64)
+        assert self.table.shape == (batch, self.max_pages)
+        c0 = self.ragged.seqs[0]
+        H, D = num_kv_heads, head_dim
+        self.k_codes = np.zeros((num_pages, H, P) + c0.k_codes.shape[3:], np.uint32)
+        self.v_codes = np.zeros((num_pages, H, P // VT) + c0.v_codes.shape[3:], np.uint32)
+        self.k_scale = np.zeros((num_pages, H, P // group, D), np.float32)
+        self.k_zero = np.zeros_like(self.k_scale)
+        self.v_scale = np.zeros((num_pages, H, P) + c0.v_scale.shape[3:], np.float32)
+        self.v_zero = np.zeros_like(self.v_scale)
+
+    @property
+    def seq_n_quant(self):
+        return self.ragged.seq_n_quant
+
+    @property
+    def seq_n_resid(self):
+        return self.ragged.seq_n_resid
+
+    def _store(self):
+        """Writes every sequence's grouped tokens [0, n_quant) into its pages:
+        logical page j's tokens go to page table[b][j] at slots t − jP."""
+        P, G = self.P, self.G
+        for b, c in enumerate(self.ragged.seqs):
+            for j in range(-(-c.n_quant // P)):
+                p = self.table[b, j]
+                t0, t1 = j * P, min(c.n_quant, j * P + P)
+                n = t1 - t0
+                self.k_codes[p, :, :n] = c.k_codes[0, :, t0:t1]
+                self.v_codes[p, :, :n // VT] = c.v_codes[0, :, t0 // VT:t1 // VT]
+                self.k_scale[p, :, :n // G] = c.k_scale[0, :, t0 // G:t1 // G]
+                self.k_zero[p, :, :n // G] = c.k_zero[0, :, t0 // G:t1 // G]
+                self.v_scale[p, :, :n] = c.v_scale[0, :, t0:t1]
+                self.v_zero[p, :, :n] = c.v_zero[0, :, t0:t1]
+
+    def prefill(self, k, v, seq_lens):
+        self.ragged.prefill(k, v, seq_lens)
+        self._store()
+
+    def append(self, k1, v1):
+        self.ragged.append(k1, v1)
+        self._store()
+
+    def window(self, name):
+        """k_resid or v_resid of the whole batch, [B][H][Rcap][D]."""
+        return self.ragged.array(name)
+
+    def dequantized_seq(self, b):
+        """Sequence b's K̂, V̂ [1, H, n, D] read back from the pool through
+        its block table, then its FP16 window."""
+        c = self.ragged.seqs[b]
+        P, G, nq = self.P, self.G, c.n_quant
+        pages = [self.table[b, j] for j in range(-(-nq // P))]
+        ntok = [min(P, nq - j * P) for j in range(len(pages))]
+        Kh = np.empty((1, self.H, nq + c.n_resid, self.D), np.float32)
+        Vh = np.empty_like(Kh)
+        for h in range(self.H):
+            if nq:
+                kc = np.concatenate([self.k_codes[p, h, :n] for p, n in zip(pages, ntok)])
+                vc = np.concatenate([self.v_codes[p, h, :n // VT] for p, n in zip(pages, ntok)])
+                ks = np.concatenate([self.k_scale[p, h, :n // G] for p, n in zip(pages, ntok)])
+                kz = np.concatenate([self.k_zero[p, h, :n // G] for p, n in zip(pages, ntok)])
+                vs = np.concatenate([self.v_scale[p, h, :n] for p, n in zip(pages, ntok)])
+                vz = np.concatenate([self.v_zero[p, h, :n] for p, n in zip(pages, ntok)])
+                Kh[0, h, :nq] = kivi.dequantize_k(kivi.unpack_k(kc, c.bits, self.D), ks, kz, G)
+                Vh[0, h, :nq] = kivi.dequantize_v(kivi.unpack_v(vc, c.v_bits, VT), vs, vz)
+        Kh[0, :, nq:] = c.k_resid[0, :, :c.n_resid].astype(np.float32)
+        Vh[0, :, nq:] = c.v_resid[0, :, :c.n_resid].astype(np.float32)
+        return Kh, Vh
+
+    def attention(self, q):
+        """q: fp32 [B, Hq, D] → fp64 [B, Hq, D], each row over its own
+        sequence as read from the pool."""
+        out = []
+        for b in range(self.B):
+            Kh, Vh = self.dequantized_seq(b)
+            out.append(attention.decode_attention(q[b:b + 1], Kh, Vh))
+        return np.concatenate(out, axis=0)
