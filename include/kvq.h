@@ -114,6 +114,13 @@
  *            with v_group_channels = 32 (run m of token t at [t][m])
  *   k_resid, v_resid fp16 [B][H][Rcap][D] the FP16 residual window; slot i
  *            holds token n_quant + i.
+ * Paged KIVI (page_tokens = P > 0, NP = num_pages): the grouped-region
+ *   arrays are pools of pages, each page holding tokens of one sequence for
+ *   every KV head in the layout above restricted to P tokens:
+ *   k_codes uint32 [NP][H][P][D·b/32], v_codes uint32 [NP][H][P/32][D][32·b_V/32],
+ *   k_scale, k_zero fp32 [NP][H][P/G][D], v_scale, v_zero fp32 [NP][H][P]
+ *   (or [NP][H][P][D/32]); token t of sequence b is slot t mod P of page
+ *   block_table[b][t / P]. The window stays [B][H][Rcap][D].
  * FP8 and FP16 (baseline, no quantization) use tiles of T = 32 tokens,
  * NT = ceil(C / T), CTT = NT · T:
  *   k_codes  [B][H][CTT][D]   token rows (uint8 FP8 codes, or fp16 values);
@@ -137,7 +144,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 9
+#define KVQ_ABI_VERSION 10
 
 typedef enum {
   KVQ_OK = 0,
@@ -191,6 +198,15 @@ typedef struct {
                               bound); 1 = a fixed tile order per wavefront
                               (bitwise identical runs). FP16 decodes are
                               always deterministic.                          */
+  int32_t page_tokens;     /* KIVI: 0 = each sequence's grouped region is
+                              contiguous; P > 0 = it lives in a pool of pages
+                              of P tokens (a power of two ≥ 32 and a multiple
+                              of group_size) of every KV head, reached through
+                              the cache's block table ([Tutorial] §十三.1,
+                              paged attention); the cache must be ragged.
+                              Must be 0 for the other formats.                */
+  int32_t num_pages;       /* KIVI with page_tokens > 0: pages in the pool
+                              (≥ 1); ignored otherwise                        */
 } kvq_config;
 
 /* Bytes the caller must allocate for each device buffer (0 = unused). */
@@ -225,6 +241,15 @@ typedef struct {
    * NULL (both): every sequence has the scalar fill levels above. */
   int64_t* seq_n_quant;
   int32_t* seq_n_resid;
+  /* Paged KIVI cache (cfg.page_tokens = P > 0): device int32
+   * [batch][max_pages], max_pages = ceil(capacity / P), 4-byte aligned; entry
+   * [b][j] is the pool page holding tokens [jP, jP + P) of sequence b. The
+   * caller fills it before any call that writes or reads those tokens (a
+   * prefill, an append whose flush reaches them, a decode over them); the
+   * pages of different sequences must be distinct. Entries are read on the
+   * device only; one outside [0, num_pages) is clamped into it (the results
+   * are then undefined, but no access leaves the pool). NULL otherwise. */
+  const int32_t* block_table;
 } kvq_cache;
 
 /* Largest batch of a ragged cache (the per-sequence fill levels travel to

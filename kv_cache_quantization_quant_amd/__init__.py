@@ -28,7 +28,7 @@ KVQ_ERR_STATE = 4
 KVQ_ERR_DEVICE = 5
 KVQ_ERR_WORKSPACE = 6
 
-ABI_VERSION = 9        # KVQ_ABI_VERSION of include/kvq.h
+ABI_VERSION = 10       # KVQ_ABI_VERSION of include/kvq.h
 STATIC_WORKSPACE_BYTES = 32 << 20   # KVQ_STATIC_WORKSPACE_BYTES
 
 KVQ_FMT_FP16 = 0
@@ -46,7 +46,8 @@ class KvqConfig(ctypes.Structure):
                 ("residual_length", c_int32), ("batch", c_int32),
                 ("num_kv_heads", c_int32), ("head_dim", c_int32), ("capacity", c_int32),
                 ("v_bits", c_int32), ("scale_per_head", c_int32), ("fp8_attention", c_int32),
-                ("v_group_channels", c_int32), ("deterministic", c_int32)]
+                ("v_group_channels", c_int32), ("deterministic", c_int32),
+                ("page_tokens", c_int32), ("num_pages", c_int32)]
 
 
 class KvqLayout(ctypes.Structure):
@@ -62,7 +63,8 @@ class KvqCache(ctypes.Structure):
                 ("k_resid", c_void_p), ("v_resid", c_void_p),
                 ("tensor_scale", c_void_p),
                 ("n_quant", c_int64), ("n_resid", c_int32), ("reserved", c_int32),
-                ("seq_n_quant", POINTER(c_int64)), ("seq_n_resid", POINTER(c_int32))]
+                ("seq_n_quant", POINTER(c_int64)), ("seq_n_resid", POINTER(c_int32)),
+                ("block_table", c_void_p)]
 
 
 MAX_RAGGED_BATCH = 128   # KVQ_MAX_RAGGED_BATCH
@@ -251,18 +253,21 @@ def make_config(fmt: str = "kivi", bits: int | None = None, group_size: int = 32
                 residual_length: int = 128, batch: int = 1, num_kv_heads: int = 1,
                 head_dim: int = 128, capacity: int = 256, v_bits: int = 0,
                 scale_per_head: int = 0, fp8_attention: int = 0,
-                v_group_channels: int = 0, deterministic: int = 0) -> KvqConfig:
+                v_group_channels: int = 0, deterministic: int = 0, page_tokens: int = 0,
+                num_pages: int = 0) -> KvqConfig:
     """v_bits: KIVI V bit width (0 = same as bits); scale_per_head: FP8 scales
     per KV head (1) or per tensor (0); fp8_attention: FP8 decode with the
     query quantized to E4M3 (1); v_group_channels: KIVI V scales per run of
     32 channels (32) or per token (0); deterministic: KIVI and FP8 decode with
     a fixed tile order per wavefront (1, bitwise reproducible) or tiles shared
-    as the wavefronts go (0, fastest)."""
+    as the wavefronts go (0, fastest); page_tokens, num_pages: KIVI grouped
+    region in a pool of num_pages pages of page_tokens tokens (0: contiguous;
+    the cache is then ragged and needs a block table)."""
     if bits is None:
         bits = {"kivi": 2, "fp8": 8, "fp8_e5m2": 8, "fp16": 16}[fmt]
     return KvqConfig(FORMATS[fmt], bits, group_size, residual_length, batch, num_kv_heads,
                      head_dim, capacity, v_bits, scale_per_head, fp8_attention,
-                     v_group_channels, deterministic)
+                     v_group_channels, deterministic, page_tokens, num_pages)
 
 
 def quantize_query_fp8(q: torch.Tensor, stream=None) -> tuple[torch.Tensor, torch.Tensor]:
@@ -323,13 +328,33 @@ class DeviceCache:
     _BUFFERS = ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero",
                 "k_resid", "v_resid", "tensor_scale")
 
-    def __init__(self, cfg: KvqConfig, device="cuda", ragged: bool = False):
-        """ragged: per-sequence fill levels (KIVI; prefill with prefill_ragged)."""
+    def __init__(self, cfg: KvqConfig, device="cuda", ragged: bool = False,
+                 block_table: torch.Tensor | None = None):
+        """ragged: per-sequence fill levels (KIVI; prefill with prefill_ragged).
+        A paged configuration (page_tokens > 0) is ragged and takes its block
+        table: int32 [batch, ceil(capacity / page_tokens)] on the device
+        (kept here; the caller may update its entries between calls)."""
         self.cfg = cfg
         st, self.layout = kvq_layout_query(cfg)
         _check(st, "kvq_layout_query")
         self.cache = KvqCache()
         _check(kvq_cache_init(self.cache, cfg), "kvq_cache_init")
+        self.paged = cfg.format == KVQ_FMT_KIVI and cfg.page_tokens > 0
+        if self.paged:
+            ragged = True
+            if block_table is None:
+                raise ValueError("a paged cache needs its block table")
+            max_pages = -(-cfg.capacity // cfg.page_tokens)
+            if block_table.device.type != "cuda" and torch.device(device).type == "cuda":
+                raise ValueError("block_table: must be a GPU tensor")
+            if (block_table.dtype != torch.int32 or tuple(block_table.shape) !=
+                    (cfg.batch, max_pages) or not block_table.is_contiguous()):
+                raise ValueError(f"block_table: contiguous int32 [{cfg.batch}, {max_pages}] "
+                                 f"expected, got {block_table.dtype} {tuple(block_table.shape)}")
+            self.block_table = block_table
+            self.cache.block_table = block_table.data_ptr()
+        elif block_table is not None:
+            raise ValueError("block_table given for a cache that is not paged")
         self.ragged = ragged
         if ragged:
             # host arrays the library reads and updates (kept alive here)
@@ -465,11 +490,13 @@ class DeviceCache:
         if c.format == KVQ_FMT_KIVI:
             b = c.bits
             bv = c.v_bits if c.v_bits > 0 else c.bits
-            vsh = (B, H, CT) if c.v_group_channels == 0 else (B, H, CT, D // c.v_group_channels)
-            shapes = {"k_codes": (torch.int32, (B, H, CT, D * b // 32)),
-                      "v_codes": (torch.int32, (B, H, CT // 32, D, 32 * bv // 32)),
-                      "k_scale": (torch.float32, (B, H, NG, D)),
-                      "k_zero": (torch.float32, (B, H, NG, D)),
+            # blocks of token slots: (b, h) of CT slots, or (page, h) of P slots
+            NB, T = (c.num_pages, c.page_tokens) if self.paged else (B, CT)
+            vsh = (NB, H, T) if c.v_group_channels == 0 else (NB, H, T, D // c.v_group_channels)
+            shapes = {"k_codes": (torch.int32, (NB, H, T, D * b // 32)),
+                      "v_codes": (torch.int32, (NB, H, T // 32, D, 32 * bv // 32)),
+                      "k_scale": (torch.float32, (NB, H, T // G, D)),
+                      "k_zero": (torch.float32, (NB, H, T // G, D)),
                       "v_scale": (torch.float32, vsh),
                       "v_zero": (torch.float32, vsh),
                       "k_resid": (torch.float16, (B, H, Rcap, D)),

@@ -78,6 +78,17 @@ kvq_status validate_config(const kvq_config* c) {
     default:
       if (c->bits != 16) return KVQ_ERR_UNSUPPORTED;
   }
+  // paged grouped region (KIVI): P a power of two ≥ 32, whole groups per page
+  if (c->page_tokens < 0) return KVQ_ERR_INVALID_ARG;
+  if (c->page_tokens > 0) {
+    const int32_t P = c->page_tokens;
+    if (c->format != KVQ_FMT_KIVI) return KVQ_ERR_UNSUPPORTED;
+    if (P < kGroup || P > (1 << 24) || (P & (P - 1)) != 0 || P % c->group_size != 0)
+      return KVQ_ERR_UNSUPPORTED;
+    if (c->num_pages <= 0) return KVQ_ERR_INVALID_ARG;
+    if (double(c->num_pages) * c->num_kv_heads * P * c->head_dim > 9.0e15)
+      return KVQ_ERR_UNSUPPORTED;
+  }
   // grid dimension y carries B·H
   if (int64_t(c->batch) * c->num_kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
   // keep every element index well inside int64
@@ -91,7 +102,15 @@ kvq_status validate_config(const kvq_config* c) {
 // NG = ⌈C/G⌉ group slots, CT = NG·G token slots, NT = CT/32 tiles of 32 tokens.
 struct Dims {
   int64_t B, H, D, C, G, NG, CT, NT, Rcap, bits, vbits, nvs;
+  // paged KIVI: P tokens per page, NP pages, max_pages table entries per sequence
+  int64_t P, NP, max_pages;
 };
+
+int ilog2(int64_t x) {
+  int n = 0;
+  while ((int64_t(1) << (n + 1)) <= x) ++n;
+  return n;
+}
 
 Dims dims_of(const kvq_config& c) {
   Dims d;
@@ -108,6 +127,9 @@ Dims dims_of(const kvq_config& c) {
   d.vbits = (c.format == KVQ_FMT_KIVI && c.v_bits > 0) ? c.v_bits : c.bits;
   d.nvs = (c.format == KVQ_FMT_KIVI && c.v_group_channels > 0) ? c.head_dim / c.v_group_channels
                                                               : 1;
+  d.P = c.format == KVQ_FMT_KIVI ? c.page_tokens : 0;
+  d.NP = d.P > 0 ? c.num_pages : 0;
+  d.max_pages = d.P > 0 ? ceil_div(c.capacity, d.P) : 0;
   return d;
 }
 
@@ -116,6 +138,10 @@ kvq_status device_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_E
 // Kernels use 16-byte vector loads and stores.
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+bool is_paged(const kvq_cache* c) {
+  return c->cfg.format == KVQ_FMT_KIVI && c->cfg.page_tokens > 0;
+}
+
 bool buffers_set(const kvq_cache* c) {
   if (c->k_codes == nullptr || c->v_codes == nullptr) return false;
   if (!aligned16(c->k_codes) || !aligned16(c->v_codes)) return false;
@@ -123,6 +149,10 @@ bool buffers_set(const kvq_cache* c) {
     const void* p[6] = {c->k_scale, c->k_zero, c->v_scale, c->v_zero, c->k_resid, c->v_resid};
     for (const void* x : p)
       if (x == nullptr || !aligned16(x)) return false;
+    // a paged cache has its block table, and per-sequence fill levels
+    if (is_paged(c))
+      return c->block_table != nullptr && (reinterpret_cast<uintptr_t>(c->block_table) & 3u) == 0 &&
+             c->seq_n_quant != nullptr && c->seq_n_resid != nullptr;
     return true;
   }
   if (is_fp8(c->cfg.format)) return c->tensor_scale != nullptr && aligned16(c->tensor_scale);
@@ -173,6 +203,15 @@ kvq::KiviQuantArgs kivi_quant_args(const kvq_cache* c, const Dims& d) {
   qa.vbits = int(d.vbits);
   qa.NG = d.NG;
   qa.NT = d.NT;
+  if (d.P > 0) {            // a block is one (page, h): a page's groups and tiles
+    qa.paged = 1;
+    qa.NG = d.P / d.G;
+    qa.NT = d.P / kGroup;
+    qa.block_table = c->block_table;
+    qa.max_pages = int(d.max_pages);
+    qa.page_group_shift = ilog2(d.P / d.G);
+    qa.num_pages = int(d.NP);
+  }
   qa.group = int(d.G);
   qa.nvs = int(d.nvs);
   qa.H = int(d.H);
@@ -336,13 +375,18 @@ kvq_status kvq_layout_query(const kvq_config* cfg, kvq_layout* out) {
   const Dims d = dims_of(*cfg);
   const size_t bh = size_t(d.B * d.H);
   switch (cfg->format) {
-    case KVQ_FMT_KIVI:
-      out->k_codes = bh * d.CT * (d.D * d.bits / 32) * 4;
-      out->v_codes = bh * d.NT * d.D * (kGroup * d.vbits / 32) * 4;
-      out->k_scale = out->k_zero = bh * d.NG * d.D * 4;
-      out->v_scale = out->v_zero = bh * d.CT * d.nvs * 4;
+    case KVQ_FMT_KIVI: {
+      // blocks of token slots: one per (b, h) of CT slots, or one per
+      // (page, h) of P slots in a paged pool
+      const size_t blocks = d.P > 0 ? size_t(d.NP * d.H) : bh;
+      const size_t CT = d.P > 0 ? size_t(d.P) : size_t(d.CT);
+      out->k_codes = blocks * CT * (d.D * d.bits / 32) * 4;
+      out->v_codes = blocks * (CT / kGroup) * d.D * (kGroup * d.vbits / 32) * 4;
+      out->k_scale = out->k_zero = blocks * (CT / d.G) * d.D * 4;
+      out->v_scale = out->v_zero = blocks * CT * d.nvs * 4;
       out->k_resid = out->v_resid = bh * d.Rcap * d.D * 2;
       break;
+    }
     case KVQ_FMT_FP8_E4M3:
     case KVQ_FMT_FP8_E5M2:
       out->k_codes = out->v_codes = bh * d.CT * d.D;
@@ -791,6 +835,16 @@ static kvq_status decode_enqueue(const kvq_cache* cache, const float* q, int32_t
   a.NT = d.NT;
   a.gshift = d.G == 128 ? 2 : d.G == 64 ? 1 : 0;
   a.main_bh_tokens = d.CT;
+  if (d.P > 0) {            // blocks are (page, h): a page's groups, tiles, slots
+    a.paged = 1;
+    a.NG = d.P / d.G;
+    a.NT = d.P / kGroup;
+    a.main_bh_tokens = d.P;
+    a.block_table = cache->block_table;
+    a.max_pages = int(d.max_pages);
+    a.page_tile_shift = ilog2(d.P / kGroup);
+    a.num_pages = int(d.NP);
+  }
   a.n_main = cache->n_quant;
   a.k_win = static_cast<const __half*>(cache->k_resid);
   a.v_win = static_cast<const __half*>(cache->v_resid);

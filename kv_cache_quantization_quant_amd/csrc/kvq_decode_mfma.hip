@@ -809,17 +809,26 @@ struct GroupSrc {
   const uint8_t* vz;   // V zero-points, lanes 32..63
 };
 
-// Sources of 32-token tile g; its K scales and zero-points are those of
-// group g >> gshift (G = 32 << gshift tokens share them).
-template <int BITS, int VB, int NVS>
-__device__ __forceinline__ GroupSrc group_src(const DecodeArgs& a, int bh, int64_t g) {
+// Sources of 32-token tile g of (b, h); its K scales and zero-points are
+// those of group g >> gshift (G = 32 << gshift tokens share them). A paged
+// cache's tile sits in the (page, h) block of the page its sequence's block
+// table names (clamped into the pool), as tile g mod (page tiles) of it.
+template <int BITS, int VB, int NVS, bool PAGED>
+__device__ __forceinline__ GroupSrc group_src(const DecodeArgs& a, int bh, int b, int h,
+                                              int64_t g) {
   using S = Stage<BITS, VB, NVS>;
-  const int64_t kg = (int64_t(bh) * a.NG + (g >> a.gshift)) * kHeadDim * 4;   // bytes
-  const int64_t vg = (int64_t(bh) * a.main_bh_tokens + g * kGroup) * 4 * NVS;
+  int64_t blk = bh;
+  if constexpr (PAGED) {
+    const int e = a.block_table[int64_t(b) * a.max_pages + (g >> a.page_tile_shift)];
+    blk = int64_t(min(max(e, 0), a.num_pages - 1)) * a.H + h;
+    g &= (int64_t(1) << a.page_tile_shift) - 1;
+  }
+  const int64_t kg = (blk * a.NG + (g >> a.gshift)) * kHeadDim * 4;   // bytes
+  const int64_t vg = (blk * a.main_bh_tokens + g * kGroup) * 4 * NVS;
   GroupSrc P;
   P.kc = static_cast<const uint8_t*>(a.k_main) +
-         (int64_t(bh) * a.main_bh_tokens + g * kGroup) * (kHeadDim * BITS / 8) - S::kKc;
-  P.vc = static_cast<const uint8_t*>(a.v_main) + (int64_t(bh) * a.NT + g) * S::kVBytes -
+         (blk * a.main_bh_tokens + g * kGroup) * (kHeadDim * BITS / 8) - S::kKc;
+  P.vc = static_cast<const uint8_t*>(a.v_main) + (blk * a.NT + g) * S::kVBytes -
          (S::kVc - S::kSecond);
   P.ks = reinterpret_cast<const uint8_t*>(a.k_scale) + kg - (S::kKsz - S::kSecond);
   P.kz = reinterpret_cast<const uint8_t*>(a.k_zero) + kg - (S::kKsz - S::kSecond);
@@ -932,7 +941,7 @@ constexpr int kivi_waves() {
   return UNIT ? 4 * kivi_waves_per_simd<BITS, VB, NVS>() : 4;
 }
 
-template <int BITS, int VB, int NVS, bool UNIT>
+template <int BITS, int VB, int NVS, bool UNIT, bool PAGED>
 __global__ __launch_bounds__((64 * kivi_waves<BITS, VB, NVS, UNIT>()))
 __attribute__((amdgpu_waves_per_eu((kivi_waves_per_simd<BITS, VB, NVS>())))) void kivi_mfma_split_kernel(
     DecodeArgs a) {
@@ -1046,7 +1055,7 @@ __attribute__((amdgpu_waves_per_eu((kivi_waves_per_simd<BITS, VB, NVS>())))) voi
       if (n_mine < 0) {
         const uint32_t t = take();
         if (t < n_blk) {
-          issue_group<BITS, VB, NVS>(ring_w + j * S::kBytes, group_src<BITS, VB, NVS>(a, bh, g0 + t),
+          issue_group<BITS, VB, NVS>(ring_w + j * S::kBytes, group_src<BITS, VB, NVS, PAGED>(a, bh, b, h_kv, g0 + t),
                                      v16, h16, h4);
         } else {
           n_mine = j;
@@ -1063,7 +1072,7 @@ __attribute__((amdgpu_waves_per_eu((kivi_waves_per_simd<BITS, VB, NVS>())))) voi
         const uint32_t t = take();
         if (t < n_blk) {
           issue_group<BITS, VB, NVS>(ring_w + kAhead * S::kBytes,
-                                     group_src<BITS, VB, NVS>(a, bh, g0 + t), v16, h16, h4);
+                                     group_src<BITS, VB, NVS, PAGED>(a, bh, b, h_kv, g0 + t), v16, h16, h4);
           wait_vmem<kAhead * S::kLoads>();
         } else {
           n_mine = kAhead;
@@ -1090,7 +1099,7 @@ __attribute__((amdgpu_waves_per_eu((kivi_waves_per_simd<BITS, VB, NVS>())))) voi
           break;
         }
         issue_group<BITS, VB, NVS>(ring_w + ((i + kAhead) % kDepth) * S::kBytes,
-                                   group_src<BITS, VB, NVS>(a, bh, g0 + t_next), v16, h16, h4);
+                                   group_src<BITS, VB, NVS, PAGED>(a, bh, b, h_kv, g0 + t_next), v16, h16, h4);
         wait_vmem<kAhead * S::kLoads>();
         load_v<BITS, VB, NVS>(ring_w + ((i - 1) % kDepth) * S::kBytes, r, u, V);
         load_k<BITS, VB, NVS>(ring_w + (i % kDepth) * S::kBytes, r, u, low, K);
@@ -1466,12 +1475,19 @@ hipError_t launch_dense_mfma(const DecodeArgs& a, hipStream_t s) {
 
 // launches the (K bits, V bits) instance with NVS V scales per token, in the
 // workgroup shape a.unit selects
+template <int KB, int VB, int NVS, bool PAGED>
+static void launch_kivi_paging(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+  if (a.unit)
+    kivi_mfma_split_kernel<KB, VB, NVS, true, PAGED>
+        <<<grid, 64 * kivi_waves<KB, VB, NVS, true>(), 0, s>>>(a);
+  else
+    kivi_mfma_split_kernel<KB, VB, NVS, false, PAGED>
+        <<<grid, 64 * kivi_waves<KB, VB, NVS, false>(), 0, s>>>(a);
+}
 template <int KB, int VB, int NVS>
 static void launch_kivi_shape(const DecodeArgs& a, dim3 grid, hipStream_t s) {
-  if (a.unit)
-    kivi_mfma_split_kernel<KB, VB, NVS, true><<<grid, 64 * kivi_waves<KB, VB, NVS, true>(), 0, s>>>(a);
-  else
-    kivi_mfma_split_kernel<KB, VB, NVS, false><<<grid, 64 * kivi_waves<KB, VB, NVS, false>(), 0, s>>>(a);
+  if (a.paged) launch_kivi_paging<KB, VB, NVS, true>(a, grid, s);
+  else launch_kivi_paging<KB, VB, NVS, false>(a, grid, s);
 }
 template <int NVS>
 static hipError_t launch_kivi_nvs(const DecodeArgs& a, dim3 grid, hipStream_t s) {
@@ -1495,11 +1511,13 @@ static int blocks_per_cu(Kernel kernel, std::atomic<int>& slot, int threads = kT
   return n;
 }
 
+// (the paged instances have the same occupancy: both are built for the same
+// wavefronts per SIMD, and a kernel that would spill fails the build)
 template <int KB, int VB, int NVS>
 static int kivi_blocks_per_cu(bool unit, std::atomic<int>* slot) {
-  return unit ? blocks_per_cu(kivi_mfma_split_kernel<KB, VB, NVS, true>, slot[1],
+  return unit ? blocks_per_cu(kivi_mfma_split_kernel<KB, VB, NVS, true, false>, slot[1],
                               64 * kivi_waves<KB, VB, NVS, true>())
-              : blocks_per_cu(kivi_mfma_split_kernel<KB, VB, NVS, false>, slot[0],
+              : blocks_per_cu(kivi_mfma_split_kernel<KB, VB, NVS, false, false>, slot[0],
                               64 * kivi_waves<KB, VB, NVS, false>());
 }
 

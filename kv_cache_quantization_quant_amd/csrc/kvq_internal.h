@@ -47,6 +47,15 @@ struct KiviQuantArgs {
   // into cache groups [seq.y[b], seq.y[b] + seq.x[b]) (n_groups, g0 unused)
   int ragged;
   int H;
+  // paged cache: group gg of sequence b goes to page
+  // block_table[b·max_pages + (gg >> page_group_shift)] (clamped to the pool),
+  // group gg mod 2^page_group_shift of that page's (page, h) block; NG, NT
+  // are then a page's groups and tiles
+  int paged;
+  const int32_t* block_table;
+  int max_pages;
+  int page_group_shift;
+  int num_pages;
   RaggedTable seq;
 };
 
@@ -165,6 +174,14 @@ struct DecodeArgs {
   // ragged KIVI batch: sequence b has seq.x[b] 32-token tiles in its grouped
   // region and seq.y[b] window tokens (n_main, n_win, win_split unused)
   int ragged;
+  // paged KIVI cache: tile g of sequence b is tile g mod 2^page_tile_shift of
+  // the (page, h) block of page block_table[b·max_pages + (g >> page_tile_shift)]
+  // (clamped to the pool); NG, NT and main_bh_tokens are then a page's
+  int paged;
+  const int32_t* block_table;
+  int max_pages;
+  int page_tile_shift;
+  int num_pages;
   RaggedTable seq;
 };
 

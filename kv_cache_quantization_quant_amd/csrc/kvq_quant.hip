@@ -139,7 +139,18 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
     if (g >= a.seq.x[b]) return;
     gg = int64_t(a.seq.y[b]) + g;
   }
-  const int64_t CT = a.NG * G;
+  // destination (b, h) block of the cache arrays, and the group within it: a
+  // paged cache's group lives in the (page, h) block of the page its
+  // sequence's block table names for it (clamped into the pool)
+  int64_t blk = bh;
+  if (a.paged) {
+    const int b = bh / a.H;
+    const int h = bh - b * a.H;
+    const int e = a.block_table[int64_t(b) * a.max_pages + (gg >> a.page_group_shift)];
+    blk = int64_t(min(max(e, 0), a.num_pages - 1)) * a.H + h;
+    gg &= (int64_t(1) << a.page_group_shift) - 1;
+  }
+  const int64_t CT = a.NG * G;             // token slots of one block
 
   uint4 kr[NS][2];                         // the thread's K values of each sub-tile
 #pragma unroll
@@ -176,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
     const float vs = (vmx - vmn) / VQMAX;
     // one thread per token (nvs = 1) or per run of 32 channels (nvs = 4)
     if (a.nvs == 1 ? j == 0 : (j & 1) == 0) {
-      const int64_t o = (bh * CT + gg * G + tr) * a.nvs + (a.nvs == 1 ? 0 : j / 2);
+      const int64_t o = (blk * CT + gg * G + tr) * a.nvs + (a.nvs == 1 ? 0 : j / 2);
       a.v_scale[o] = vs;
       a.v_zero[o] = vmn;
     }
@@ -231,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
     const float s0 = (float(kmx[0]) - mn0) / KQMAX;
     const float s1 = (float(kmx[1]) - mn1) / KQMAX;
     if (u == 0) {
-      const int64_t o = (bh * a.NG + gg) * kHeadDim + d0;
+      const int64_t o = (blk * a.NG + gg) * kHeadDim + d0;
       *reinterpret_cast<float2*>(a.k_scale + o) = make_float2(s0, s1);
       *reinterpret_cast<float2*>(a.k_zero + o) = make_float2(mn0, mn1);
       *reinterpret_cast<float2*>(&s_k[d0]) = make_float2(s0, s1);
@@ -245,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
   // the high.
 #pragma unroll
   for (int sub = 0; sub < NS; ++sub) {
-    uint32_t* vdst = a.v_codes + (bh * a.NT + gg * NS + sub) * kHeadDim * VW;
+    uint32_t* vdst = a.v_codes + (blk * a.NT + gg * NS + sub) * kHeadDim * VW;
 #pragma unroll
     for (int rep = 0; rep < (kHeadDim * VW) / kThreads; ++rep) {
       const int idx = rep * kThreads + tid;
@@ -296,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
     }
     uint32_t w[KTW];
     pack16<KB>(c, w);
-    uint32_t* kdst = a.k_codes + (bh * CT + gg * G + sub * kGroup + t) * KW;
+    uint32_t* kdst = a.k_codes + (blk * CT + gg * G + sub * kGroup + t) * KW;
     if (KB == 2) {
       kdst[j] = w[0];
     } else {

@@ -60,7 +60,7 @@ def test_struct_sizes_match_header(tmp_path):
         assert int(got[st]) == ctypes.sizeof(cls), st
         for f in fields[st]:
             assert int(got[f"{st}.{f}"]) == getattr(cls, f).offset, (st, f)
-    assert int(got["abi"]) == kq.kvq_abi_version() == kq.ABI_VERSION == 9
+    assert int(got["abi"]) == kq.kvq_abi_version() == kq.ABI_VERSION == 10
 
 
 def test_status_strings():
@@ -95,6 +95,14 @@ def test_status_strings():
     (dict(residual_length=48), kq.KVQ_ERR_UNSUPPORTED),
     (dict(residual_length=-32), kq.KVQ_ERR_INVALID_ARG),
     (dict(batch=300, num_kv_heads=300), kq.KVQ_ERR_UNSUPPORTED),
+    (dict(page_tokens=64, num_pages=10), 0),
+    (dict(page_tokens=32, num_pages=1), 0),
+    (dict(page_tokens=128, num_pages=3, group_size=128), 0),
+    (dict(page_tokens=-64, num_pages=10), kq.KVQ_ERR_INVALID_ARG),
+    (dict(page_tokens=64, num_pages=0), kq.KVQ_ERR_INVALID_ARG),
+    (dict(page_tokens=16, num_pages=4), kq.KVQ_ERR_UNSUPPORTED),
+    (dict(page_tokens=96, num_pages=4), kq.KVQ_ERR_UNSUPPORTED),
+    (dict(page_tokens=32, num_pages=4, group_size=64), kq.KVQ_ERR_UNSUPPORTED),
 ])
 def test_config_validation(fields, expect):
     cfg = kq.make_config("kivi", batch=2, num_kv_heads=2, capacity=256)
@@ -274,6 +282,49 @@ def test_append_errors_before_any_launch():
     assert kq.kvq_append_token(fp16, P, P, None) == kq.KVQ_ERR_CAPACITY
     assert kq.kvq_append_token(_host_cache(kq.make_config("fp16", capacity=10), 3, 1),
                                P, P, None) == kq.KVQ_ERR_STATE
+
+
+def test_paged_layout_and_refusals():
+    """Pool sizes of a paged KIVI cache (pages of every KV head), the window
+    per sequence; page_tokens only for KIVI; calls on a paged cache without a
+    block table or per-sequence fill levels are refused before any launch."""
+    B, H, C, P, NP = 3, 2, 1000, 64, 40
+    for bits, vbits, gc in ((2, 0, 0), (4, 2, 0), (2, 0, 32)):
+        cfg = kq.make_config("kivi", bits=bits, v_bits=vbits, v_group_channels=gc, batch=B,
+                             num_kv_heads=H, capacity=C, page_tokens=P, num_pages=NP)
+        st, lay = kq.kvq_layout_query(cfg)
+        assert st == 0
+        vb = vbits or bits
+        nvs = 4 if gc else 1
+        assert lay.k_codes == NP * H * P * 128 * bits // 8
+        assert lay.v_codes == NP * H * P * 128 * vb // 8
+        assert lay.k_scale == lay.k_zero == NP * H * (P // 32) * 128 * 4
+        assert lay.v_scale == lay.v_zero == NP * H * P * nvs * 4
+        assert lay.k_resid == lay.v_resid == B * H * 128 * 128 * 2
+    for fmt in ("fp8", "fp16", "fp8_e5m2"):
+        st, _ = kq.kvq_layout_query(kq.make_config(fmt, capacity=C, page_tokens=P, num_pages=NP))
+        assert st == kq.KVQ_ERR_UNSUPPORTED
+    P_ = 0x100000
+    cfg = kq.make_config("kivi", batch=B, num_kv_heads=H, capacity=C, page_tokens=P,
+                         num_pages=NP)
+    nq = (ctypes.c_int64 * B)(64, 0, 32)
+    nr = (ctypes.c_int32 * B)(3, 5, 128)
+    lens = (ctypes.c_int64 * B)(100, 100, 100)
+    c = _host_cache(cfg)            # buffers set, no block table, not ragged
+    assert kq.kvq_prefill_quantize(c, P_, P_, 100, None) == kq.KVQ_ERR_INVALID_ARG
+    c.seq_n_quant = ctypes.cast(nq, ctypes.POINTER(ctypes.c_int64))
+    c.seq_n_resid = ctypes.cast(nr, ctypes.POINTER(ctypes.c_int32))
+    assert kq.kvq_decode_attention(c, P_, 4, P_, P_, 1 << 30, None) == kq.KVQ_ERR_INVALID_ARG
+    assert kq.kvq_append_token(c, P_, P_, None) == kq.KVQ_ERR_INVALID_ARG
+    c.block_table = P_ + 2                      # misaligned
+    assert kq.kvq_decode_attention(c, P_, 4, P_, P_, 1 << 30, None) == kq.KVQ_ERR_INVALID_ARG
+    c.block_table = P_
+    # the contiguous prefill is not for ragged (hence paged) caches
+    assert kq.kvq_prefill_quantize(c, P_, P_, 100, None) == kq.KVQ_ERR_INVALID_ARG
+    # the byte count is the ragged one: paging moves no extra bytes
+    want = sum(bytes_model.decode_bytes_kivi(1, H, 128, 2, 32, q, r) for q, r in zip(nq, nr))
+    assert kq.kvq_decode_bytes(c, 4) == want
+    del lens
 
 
 def test_decode_errors_before_any_launch():

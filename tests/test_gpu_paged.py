@@ -1,0 +1,176 @@
+"""Parity of paged KIVI caches (the grouped region in a pool of pages reached
+through a block table; "大模型量化从0到1（十三）：KV Cache 量化", §十三.1) against
+the oracle's paged cache and against the contiguous ragged path.
+
+Bar: the whole page pools (every page, including the ones no sequence uses)
+and the windows bit-exact; fill levels equal; attention within max-abs 2e-3
+of the oracle's fp64 attention read back through the table; and with a fixed
+tile order, the paged decode bitwise equal to the contiguous ragged decode of
+the same tokens (paging changes addresses only).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import cache as ocache
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 2e-3
+D = 128
+POOL = ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero")
+
+
+@pytest.fixture(scope="module")
+def kq():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import kv_cache_quantization_quant_amd as m
+    return m
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _table(B, max_pages, spare, seed):
+    """A shuffled block table: distinct pages for every (sequence, logical
+    page), drawn from a pool with `spare` pages left over."""
+    NP = B * max_pages + spare
+    perm = np.random.default_rng(seed).permutation(NP)[:B * max_pages]
+    return NP, perm.reshape(B, max_pages).astype(np.int32)
+
+
+def _compare(dc, oc):
+    for name in POOL:
+        g = _np(dc.view(name))
+        o = getattr(oc, name)
+        if name.endswith("codes"):
+            g = g.view(np.uint32)
+        assert g.shape == o.shape, (name, g.shape, o.shape)
+        assert np.array_equal(g.view(np.uint8), o.view(np.uint8)), name
+    for name in ("k_resid", "v_resid"):
+        assert np.array_equal(_np(dc.view(name)).view(np.uint8), oc.window(name).view(np.uint8))
+    assert dc.seq_n_quant == oc.seq_n_quant and dc.seq_n_resid == oc.seq_n_resid
+
+
+def _err(out, ref):
+    return float(np.max(np.abs(_np(out).astype(np.float64) - ref)))
+
+
+@pytest.mark.parametrize("P,G,bits,vbits,gc,R,H,Hq,lens,steps", [
+    (64, 32, 2, 0, 0, 128, 2, 8, [600, 130, 257], 70),     # flushes cross page edges
+    (32, 32, 2, 0, 0, 0, 2, 2, [97, 1, 32], 35),            # R = 0, one tile per page
+    (128, 64, 4, 2, 0, 64, 1, 4, [500, 63, 200], 70),
+    (256, 128, 2, 4, 0, 128, 2, 8, [1000, 129, 640], 20),
+    (64, 32, 2, 0, 32, 128, 2, 16, [257, 700, 96], 30),     # V scales per 32 channels
+    (512, 32, 2, 0, 0, 128, 4, 32, [4096, 1000, 3000, 77, 2048, 333], 5),   # many splits
+])
+def test_paged_prefill_append_decode(kq, P, G, bits, vbits, gc, R, H, Hq, lens, steps):
+    B = len(lens)
+    Smax = max(lens)
+    C = Smax + steps
+    max_pages = -(-C // P)
+    NP, table = _table(B, max_pages, 5, seed=len(lens) + P)
+    _say(f"[paged] P={P} NP={NP} G={G} bits={bits} v_bits={vbits} gc={gc} R={R} H={H} "
+         f"Hq={Hq} lens={lens} steps={steps}")
+    k = synth.make_k(B, H, 0, C, D, device="cuda")
+    v = synth.make_v(B, H, 0, C, D, device="cuda")
+    cfg = kq.make_config("kivi", bits=bits, group_size=G, residual_length=R, batch=B,
+                         num_kv_heads=H, capacity=C, v_bits=vbits, v_group_channels=gc,
+                         page_tokens=P, num_pages=NP)
+    dc = kq.DeviceCache(cfg, block_table=torch.from_numpy(table).cuda())
+    oc = ocache.PagedKiviCache(B, H, D, bits, G, R, C, P, NP, table, v_bits=vbits or None,
+                               v_group_channels=gc or None)
+    kp, vp = k[:, :, :Smax].clone(), v[:, :, :Smax].clone()
+    for b, S in enumerate(lens):          # padding the kernels must not read
+        kp[b, :, S:] = 30000.0
+        vp[b, :, S:] = -30000.0
+    dc.prefill_ragged(kp, vp, lens)
+    oc.prefill(_np(kp), _np(vp), lens)
+    torch.cuda.synchronize()
+    _compare(dc, oc)
+    ws = dc.make_workspace(Hq)
+    q = synth.make_q(B, Hq, D, device="cuda")
+    worst = _err(dc.decode(q, workspace=ws), oc.attention(_np(q)))
+    nxt = list(lens)
+    for i in range(steps):
+        k1 = torch.stack([k[b, :, nxt[b]] for b in range(B)]).contiguous()
+        v1 = torch.stack([v[b, :, nxt[b]] for b in range(B)]).contiguous()
+        dc.append(k1, v1)
+        oc.append(_np(k1), _np(v1))
+        nxt = [t + 1 for t in nxt]
+        if i % 10 == 9 or i == steps - 1:
+            q = synth.make_q(B, Hq, D, step=i, device="cuda")
+            worst = max(worst, _err(dc.decode(q, workspace=ws), oc.attention(_np(q))))
+    torch.cuda.synchronize()
+    _compare(dc, oc)
+    _say(f"  worst max abs err {worst:.3e}, flushes {[s.flush_steps for s in oc.ragged.seqs]}")
+    assert worst <= ATOL
+
+
+def test_paged_gqa70b_32k_equals_contiguous(kq):
+    """The bench's ragged 32K GQA workload (B = 16, 64 query / 8 KV heads,
+    sequence b holding 32768 - 1920·b tokens, KIVI 2-bit) in pages of 256
+    tokens under a shuffled table, next to the same batch in contiguous
+    ragged buffers, both with a fixed tile order: after the prefill and 130
+    appends (a flush in every sequence), every page holds exactly its
+    sequence's tokens of the contiguous buffers, and the decodes are bitwise
+    equal at every checked step."""
+    cfg0 = synth.CONFIGS["gqa70b_32k"]
+    B, H, Hq, S = cfg0["batch"], cfg0["num_kv_heads"], cfg0["num_q_heads"], cfg0["seq_len"]
+    steps, P = 130, 256
+    C = S + steps
+    lens = [S - 1920 * b for b in range(B)]
+    max_pages = -(-C // P)
+    NP, table = _table(B, max_pages, 7, seed=32)
+    _say(f"[paged 32K] P={P} NP={NP} lens {lens[0]}..{lens[-1]} steps={steps}")
+    k = synth.make_k(B, H, 0, C, D, device="cuda")
+    v = synth.make_v(B, H, 0, C, D, device="cuda")
+    base = dict(bits=2, batch=B, num_kv_heads=H, capacity=C, deterministic=1)
+    rag = kq.DeviceCache(kq.make_config("kivi", **base), ragged=True)
+    tab = torch.from_numpy(table).cuda()
+    pag = kq.DeviceCache(kq.make_config("kivi", page_tokens=P, num_pages=NP, **base),
+                         block_table=tab)
+    for dc in (rag, pag):
+        dc.prefill_ragged(k[:, :, :S].contiguous(), v[:, :, :S].contiguous(), lens)
+    ws = rag.make_workspace(Hq)
+    worst = 0.0
+    for i in range(steps + 1):
+        if i > 0:
+            pos = [lens[b] + i - 1 for b in range(B)]
+            k1 = torch.stack([k[b, :, pos[b]] for b in range(B)]).contiguous()
+            v1 = torch.stack([v[b, :, pos[b]] for b in range(B)]).contiguous()
+            rag.append(k1, v1)
+            pag.append(k1, v1)
+        if i in (0, 1, 64, 129, 130):
+            q = synth.make_q(B, Hq, D, step=i, device="cuda")
+            a, b_ = rag.decode(q, workspace=ws), pag.decode(q, workspace=ws)
+            torch.cuda.synchronize()
+            worst = max(worst, float((a - b_).abs().max()))
+            assert torch.equal(a, b_), f"paged decode differs from contiguous at step {i}"
+    assert rag.seq_n_quant == pag.seq_n_quant and rag.seq_n_resid == pag.seq_n_resid
+    assert all(nq > lens[b] - 128 for b, nq in enumerate(rag.seq_n_quant))
+    # every page holds its logical tokens of the contiguous buffers
+    G = 32
+    for name in POOL:
+        cont = rag.view(name)                       # [B, H, CT, ...]
+        pool = pag.view(name)                       # [NP, H, P', ...]
+        per = {"k_codes": P, "v_codes": P // 32, "k_scale": P // G, "k_zero": P // G,
+               "v_scale": P, "v_zero": P}[name]
+        unit = {"k_codes": 1, "v_codes": 32, "k_scale": G, "k_zero": G, "v_scale": 1,
+                "v_zero": 1}[name]
+        for b in range(B):
+            nq = rag.seq_n_quant[b]
+            n_units = nq // unit
+            for j in range(-(-n_units // per)):
+                lo, hi = j * per, min(n_units, j * per + per)
+                assert torch.equal(pool[table[b, j], :, :hi - lo], cont[b, :, lo:hi]), (name, b, j)
+    for name in ("k_resid", "v_resid"):
+        assert torch.equal(rag.view(name), pag.view(name))
