@@ -20,10 +20,12 @@ workload; extra per-workload figures for the other configurations.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
 import statistics
+import subprocess
 import sys
 import time
 
@@ -48,6 +50,11 @@ def decode_source_hash() -> str:
         with open(os.path.join(ROOT, "kv_cache_quantization_quant_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def _file_hash() -> str:
+    with open(os.path.abspath(__file__), "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
 def traffic_from_counters():
@@ -102,21 +109,40 @@ def quantize_traffic_bytes(B, H, S, bits, n_quant, n_resid):
     return read + write
 
 
+def _bytes_at(kq, cache, n_quant, n_resid, hq):
+    """kvq_decode_bytes of `cache` at another fill state (a host-side copy of
+    its struct; nothing is enqueued)."""
+    c = kq.KvqCache.from_buffer_copy(cache)
+    c.n_quant, c.n_resid = n_quant, n_resid
+    return kq.kvq_decode_bytes(c, hq)
+
+
 def run_main(torch, kq, synth, args):
     cfg = synth.CONFIGS["gqa70b_32k"]
     B, H, Hq, S, bits = (cfg["batch"], cfg["num_kv_heads"], cfg["num_q_heads"],
                          cfg["seq_len"], cfg["bits"])
-    n_steps = args.warmup + args.steps
-    C = S + -(-n_steps // LAYERS)
+    R = cfg["residual_length"]
+    # Layer l enters the timed steps with a window of 1 + 32·l tokens (setup
+    # appends after the prefill; the first one flushes the full prefill
+    # window), so that even a short run decodes over every part of the window
+    # cycle and a long one crosses flushes in the timed region.
+    stagger = [1 + (R // LAYERS) * l for l in range(LAYERS)]
+    # the timed steps run twice: once with events around each decode (the
+    # roofline pass), once with only the region's two events (the value)
+    per_layer = -(-(args.warmup + 2 * args.steps) // LAYERS)
+    n_new = max(stagger) + per_layer
+    C = S + n_new
     _log(f"[bench] gqa70b_32k: B={B} Hq={Hq} H={H} S={S} KIVI {bits}-bit, "
-         f"{LAYERS} layer caches, warmup={args.warmup} steps={args.steps}")
+         f"{LAYERS} layer caches (windows {stagger}), warmup {args.warmup_s}s + "
+         f"{args.warmup} steps, steps={args.steps}")
     t0 = time.time()
-    k = synth.make_k(B, H, 0, S + n_steps, D, device="cuda")
-    v = synth.make_v(B, H, 0, S + n_steps, D, device="cuda")
+    k = synth.make_k(B, H, 0, C, D, device="cuda")
+    v = synth.make_v(B, H, 0, C, D, device="cuda")
     kp, vp = k[:, :, :S].contiguous(), v[:, :, :S].contiguous()
-    k_new = [k[:, :, S + i].contiguous() for i in range(n_steps)]
-    v_new = [v[:, :, S + i].contiguous() for i in range(n_steps)]
-    qs = [synth.make_q(B, Hq, D, step=i, device="cuda") for i in range(n_steps)]
+    k_new = [k[:, :, S + i].contiguous() for i in range(n_new)]
+    v_new = [v[:, :, S + i].contiguous() for i in range(n_new)]
+    n_q = args.warmup + 2 * args.steps
+    qs = [synth.make_q(B, Hq, D, step=i, device="cuda") for i in range(n_q)]
     del k, v
     torch.cuda.synchronize()
     _log(f"[bench] inputs generated in {time.time() - t0:.1f}s")
@@ -138,84 +164,138 @@ def run_main(torch, kq, synth, args):
         c.prefill(kp, vp)
     del kp, vp
 
-    # step i works on layer i % LAYERS; with every layer prefilled to a full
-    # window, the first append of each layer flushes 128 tokens into 4 groups
-    warm_flush = []
-    for i in range(args.warmup):
-        c = layers[i % LAYERS]
-        flushes = c.n_resid == c.cfg.residual_length
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        c.append(k_new[i], v_new[i])
-        e1.record()
-        if flushes:
-            warm_flush.append((e0, e1))
-        c.decode(qs[i], out=out, workspace=ws)
-    torch.cuda.synchronize()
-    warm_flush_us = [a.elapsed_time(b) * 1e3 for a, b in warm_flush]
+    # setup appends (untimed as steps): the first append of each layer finds
+    # the prefill window full and flushes it (timed here on its own), the
+    # next ones are plain window writes
+    # (each behind a cache scrub, so that the GPU is busy while the host
+    # enqueues it and the events time the append's kernels alone)
+    pos = [0] * LAYERS                     # next streamed token of each layer
+    flush_us, plain_us = [], []
+    scrub = Scrub(torch)
+    for l, c in enumerate(layers):
+        for j in range(stagger[l]):
+            flushes = c.n_resid == c.cfg.residual_length
+            (flush_us if flushes else plain_us).extend(time_launches(
+                torch, lambda: c.append(k_new[pos[l]], v_new[pos[l]]), 1, scrub))
+            pos[l] += 1
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    ev_app = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    flush_step = []
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    step_bytes = []
+    # time-based warm-up: decodes cycling through the layers until the clocks
+    # have settled under this load, then the requested warm-up steps
+    t_w = time.perf_counter()
+    n_warm = 0
+    while time.perf_counter() - t_w < args.warmup_s:
+        for c in layers:
+            c.decode(qs[0], out=out, workspace=ws)
+        n_warm += LAYERS
+        torch.cuda.synchronize()
+    qi = 0
+    for i in range(args.warmup):
+        l = i % LAYERS
+        layers[l].append(k_new[pos[l]], v_new[pos[l]])
+        pos[l] += 1
+        layers[l].decode(qs[qi], out=out, workspace=ws)
+        qi += 1
     torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    start.record()
-    for j in range(args.steps):
-        i = args.warmup + j
-        c = layers[i % LAYERS]
-        flush_step.append(c.n_resid == c.cfg.residual_length)   # this append flushes
-        ev_app[j].record()
-        c.append(k_new[i], v_new[i])
-        step_bytes.append(c.decode_bytes(Hq))
-        ev[j][0].record()
-        c.decode(qs[i], out=out, workspace=ws)
-        ev[j][1].record()
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = start.elapsed_time(end)
-    dec_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
-    app_us = [a.elapsed_time(b[0]) * 1e3 for a, b in zip(ev_app, ev)]
-    plain_app = [u for u, f in zip(app_us, flush_step) if not f]
-    flush_app = [u for u, f in zip(app_us, flush_step) if f] + warm_flush_us
+
+    def timed(per_decode_events):
+        """K steps (append + decode, layer i % LAYERS); returns the region's
+        time (us), the fill state each decode saw, the decodes' event times."""
+        nonlocal qi
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)] if per_decode_events else None
+        state = []
+        host = []
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        # no garbage collection pass inside the region (a pass over this
+        # process's many tensors and events holds the host for milliseconds)
+        gc.collect()
+        gc.disable()
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        start.record()
+        for j in range(args.steps):
+            host.append(time.perf_counter())
+            l = j % LAYERS
+            c = layers[l]
+            c.append(k_new[pos[l]], v_new[pos[l]])
+            pos[l] += 1
+            state.append((l, c.cache.n_quant, c.cache.n_resid))
+            if ev:
+                ev[j][0].record()
+            c.decode(qs[qi], out=out, workspace=ws)
+            qi += 1
+            if ev:
+                ev[j][1].record()
+        end.record()
+        wall_enqueue = time.perf_counter() - wall0
+        torch.cuda.synchronize()
+        gc.enable()
+        total_us = start.elapsed_time(end) * 1e3
+        dec = [a.elapsed_time(b) * 1e3 for a, b in ev] if ev else None
+        host.append(wall0 + wall_enqueue)
+        step_host_max = max(b - a for a, b in zip(host, host[1:])) * 1e6
+        return total_us, state, dec, wall_enqueue, step_host_max
+
+    # value: the steps with nothing but the region's two events
+    total_us, state, _, wall_enq, host_max = timed(False)
+    step_bytes = [_bytes_at(kq, layers[l].cache, nq, nr, Hq) for l, nq, nr in state]
     total_bytes = sum(step_bytes)
-    value = total_bytes / (total_ms * 1e-3) / 1e9
+    value = total_bytes / (total_us * 1e-6) / 1e9
+    # roofline: the same steps with events around each decode
+    total_us2, state2, dec_us, _, _ = timed(True)
+    bytes2 = [_bytes_at(kq, layers[l].cache, nq, nr, Hq) for l, nq, nr in state2]
     mean_dec_us = sum(dec_us) / len(dec_us)
-    achieved = (total_bytes / len(step_bytes)) / (mean_dec_us * 1e-6) / 1e9
+    mean_bytes = sum(bytes2) / len(bytes2)
+    achieved = mean_bytes / (mean_dec_us * 1e-6) / 1e9
 
     # decode launches with the Infinity Cache scrubbed before each one
     cold_med = None
     bytes_now = dc.decode_bytes(Hq)
     if not args.no_cold:
-        scrub = Scrub(torch)
         cold = time_launches(torch, lambda: dc.decode(qs[-1], out=out, workspace=ws), 20, scrub)
         cold_med = statistics.median(cold)
 
+    windows = [nr for _, _, nr in state]
     res = {
         "B": B, "Hq": Hq, "H": H, "S": S, "bits": bits,
-        "total_ms": total_ms, "wall_s": wall, "ms_per_step": total_ms / args.steps,
-        "value": value, "mean_decode_us": mean_dec_us,
+        "total_ms": total_us * 1e-3, "ms_per_step": total_us * 1e-3 / args.steps,
+        "host_enqueue_us_per_step": wall_enq / args.steps * 1e6,
+        "host_enqueue_us_max_step": host_max,
+        "value": value,
+        "decode_bytes_per_step_mean": total_bytes / len(step_bytes),
+        "window_tokens_min_max": [min(windows), max(windows)],
+        "flushes_in_timed_steps": sum(1 for _, _, nr in state if nr == 1),
+        "roofline_pass_ms_per_step": total_us2 * 1e-3 / args.steps,
+        "mean_decode_us": mean_dec_us,
         "p50_decode_us": statistics.median(dec_us),
         "p95_decode_us": sorted(dec_us)[int(0.95 * (len(dec_us) - 1))],
-        "decode_bytes_per_launch": total_bytes / len(step_bytes),
+        "decode_bytes_per_launch": mean_bytes,
         "achieved_gbs": achieved,
         "cold_decode_us_p50": cold_med,
         "cold_decode_gbs": None if cold_med is None else bytes_now / (cold_med * 1e-6) / 1e9,
-        "append_us_p50": statistics.median(plain_app) if plain_app else None,
-        "flush_append_us_mean": statistics.mean(flush_app) if flush_app else None,
-        "flush_steps": len(flush_app),
-        "append_plus_decode_us_mean": statistics.mean(a + d for a, d in zip(app_us, dec_us)),
+        "append_us_p50": statistics.median(plain_us) if plain_us else None,
+        "flush_append_us_mean": statistics.mean(flush_us) if flush_us else None,
+        "warmup_decodes": n_warm,
         "prefill_quantize_us": pre_us,
         "prefill_quantize_gbs": q_bytes / (pre_us * 1e-6) / 1e9,
         "layers": LAYERS,
         "final_state": [[c.n_quant, c.n_resid] for c in layers],
     }
     return res
+
+
+def copy_peak_gbs(torch, mib=1024, iters=10):
+    """Device-to-device copy rate on this machine (read + write bytes / time),
+    median of `iters` copies of `mib` MiB: a measured peak beside the
+    published 8 TB/s."""
+    n = mib << 18
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    t = time_launches(torch, lambda: dst.copy_(src), iters)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * (mib << 20) / (statistics.median(t) * 1e-6) / 1e9
 
 
 def run_extra(torch, kq, synth):
@@ -233,6 +313,8 @@ def run_extra(torch, kq, synth):
             dict(name="gqa70b_32k", fmt="kivi", v_group_channels=32),
             # ragged batch: sequence b holds 32768 - 1920·b tokens (32768 .. 3968)
             dict(name="gqa70b_32k", fmt="kivi", ragged=True),
+            # the same ragged batch in pages of 256 tokens under a shuffled table
+            dict(name="gqa70b_32k", fmt="kivi", ragged=True, paged=256),
             dict(name="gqa_128k", fmt="fp16"), dict(name="gqa_128k", fmt="fp8"),
             dict(name="gqa_128k", fmt="fp8", per_head=1), dict(name="gqa_128k", fmt="fp8_e5m2"),
             dict(name="gqa_128k", fmt="fp8", fp8_attention=1),
@@ -256,10 +338,19 @@ def run_extra(torch, kq, synth):
         bits = (kbits or c["bits"]) if fmt == "kivi" else None
         ragged = item.get("ragged", False)
         lens = [S - 1920 * b for b in range(B)] if ragged else None
+        P = item.get("paged", 0)
+        table, NP = None, 0
+        if P:
+            import numpy as np
+            max_pages = -(-S // P)
+            NP = B * max_pages
+            perm = np.random.default_rng(0).permutation(NP).astype(np.int32)
+            table = torch.from_numpy(perm.reshape(B, max_pages)).cuda()
         dc = kq.DeviceCache(kq.make_config(fmt, bits=bits, group_size=G, batch=B,
                                            num_kv_heads=H, capacity=S, v_bits=vbits or 0,
                                            scale_per_head=per_head, fp8_attention=qf8,
-                                           v_group_channels=gc), ragged=ragged)
+                                           v_group_channels=gc, page_tokens=P, num_pages=NP),
+                            ragged=ragged, block_table=table)
 
         def prefill():
             dc.reset()
@@ -277,7 +368,7 @@ def run_extra(torch, kq, synth):
         key = (f"{name}/{fmt}" + (f"_g{G}" if G != 32 else "") +
                (f"_k{kbits}v{vbits}" if vbits else "") + ("_per_head" if per_head else "") +
                ("_fp8_attention" if qf8 else "") + (f"_vgc{gc}" if gc else "") +
-               ("_ragged" if ragged else ""))
+               ("_ragged" if ragged else "") + (f"_paged{P}" if P else ""))
         if name == "gqa_128k":
             outs[key.split("/")[1]] = o.double().cpu()
         nbytes = dc.decode_bytes(Hq)
@@ -334,28 +425,31 @@ def _cuda_ok():
     return torch.cuda.is_available()
 
 
-def run_cpu_baseline(synth):
-    """The oracle on a bounded sample of the same workload: 8 of the 128
-    (b, KV head) blocks, prefill-quantized, then 8 decode steps each
-    (append + dequantize + fp64 attention of the block's 8 query heads), on one
-    host thread."""
+def _cpu_worker(arg):
+    """One host process of the CPU baseline: its (b, KV head) blocks of the 32K
+    GQA layer, drawn on the CPU, prefill-quantized, then `steps` decode steps
+    (append + dequantize + fp64 attention of the block's query heads), on one
+    thread. Returns (algorithmic decode bytes, prefill s, decode s)."""
+    blocks, steps, in_dir = arg
     import numpy as np
+    import torch
     from threadpoolctl import threadpool_limits
 
-    from oracle import bytes_model, cache as ocache
+    import synth
+    from oracle import attention, bytes_model, cache as ocache
 
+    torch.set_num_threads(1)
     cfg = synth.CONFIGS["gqa70b_32k"]
     B, H, Hq, S = cfg["batch"], cfg["num_kv_heads"], cfg["num_q_heads"], cfg["seq_len"]
     nq = Hq // H
-    blocks = [(b, h) for b in (0, 5, 10, 15) for h in (0, 7)]
-    steps = 8
     with threadpool_limits(limits=1):
-        dev = "cuda" if _cuda_ok() else "cpu"
-        kb = np.stack([synth.make_k(1, H, 0, S + steps, D, device=dev, b0=b)[0, h].cpu().numpy()
-                       for b, h in blocks])
-        vb = np.stack([synth.make_v(1, H, 0, S + steps, D, device=dev, b0=b)[0, h].cpu().numpy()
-                       for b, h in blocks])
-        q = synth.make_q(B, Hq, D, step=0).numpy()
+        # each block's K, V (tokens [0, S + steps)) and queries as drawn by the
+        # parent (seeded synth; plain .npy arrays)
+        kb = np.stack([np.load(os.path.join(in_dir, f"k_{b}_{h}.npy")) for b, h in blocks])
+        vb = np.stack([np.load(os.path.join(in_dir, f"v_{b}_{h}.npy")) for b, h in blocks])
+        q_all = np.load(os.path.join(in_dir, "q.npy"))                 # [steps, B, Hq, D]
+        qs = [np.stack([q_all[i, b, h * nq:(h + 1) * nq] for b, h in blocks])
+              for i in range(steps)]
         t0 = time.perf_counter()
         oc = ocache.KiviCache(len(blocks), 1, D, 2, 32, 128, S + steps)
         oc.prefill(kb[:, None, :S], vb[:, None, :S])
@@ -364,21 +458,93 @@ def run_cpu_baseline(synth):
         t0 = time.perf_counter()
         for i in range(steps):
             oc.append(kb[:, None, S + i], vb[:, None, S + i])
-            qs = np.stack([q[b, h * nq:(h + 1) * nq] for b, h in blocks])   # [8 blocks, nq, D]
             Kh, Vh = oc.dequantized()
-            from oracle import attention
             for j in range(len(blocks)):
-                attention.decode_attention(qs[j:j + 1], Kh[j:j + 1], Vh[j:j + 1])
+                attention.decode_attention(qs[i][j:j + 1], Kh[j:j + 1], Vh[j:j + 1])
             nbytes += bytes_model.decode_bytes_kivi(len(blocks), 1, D, 2, 32, oc.n_quant,
                                                     oc.n_resid)
         t_dec = time.perf_counter() - t0
-    return {"value": round(nbytes / t_dec / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": (f"{len(blocks)} of {B * H} (b, KV head) blocks of the 32K GQA layer, "
-                       f"{steps} decode steps each (append + dequantize + fp64 attention of "
-                       f"{nq} query heads); prefill quantize of those blocks took "
-                       f"{t_pre:.2f}s; decode {t_dec:.2f}s"),
-            "decode_s_per_block_step": round(t_dec / (steps * len(blocks)), 4)}
+    return nbytes, t_pre, t_dec
+
+
+def _cpu_blocks(n):
+    """The (b, KV head) blocks of the CPU baseline sample, spread over batch
+    elements and heads."""
+    return [((5 * j) % 16, (j + j // 16) % 8) for j in range(n)]
+
+
+def cpu_baseline_child(workers, per_worker, steps, in_dir):
+    """Runs in a child process that never touches the GPU: `workers` host
+    processes (one thread each) of _cpu_worker over `per_worker` blocks each,
+    started together; prints one JSON line."""
+    import multiprocessing as mp
+
+    n = workers * per_worker
+    blocks = _cpu_blocks(n)
+    chunks = [(blocks[w * per_worker:(w + 1) * per_worker], steps, in_dir)
+              for w in range(workers)]
+    t0 = time.perf_counter()
+    if workers == 1:
+        res = [_cpu_worker(chunks[0])]
+    else:
+        with mp.get_context("fork").Pool(workers) as pool:
+            res = pool.map(_cpu_worker, chunks)
+    wall = time.perf_counter() - t0
+    nbytes = sum(r[0] for r in res)
+    t_dec = max(r[2] for r in res)          # the workers decode side by side
+    print(json.dumps({"bytes": nbytes, "decode_s": t_dec, "prefill_s": max(r[1] for r in res),
+                      "blocks": n, "steps": steps, "workers": workers, "wall_s": wall}),
+          flush=True)
+
+
+def run_cpu_baseline(torch, synth):
+    """The oracle, unmodified, on a bounded sample of the same workload, in a
+    child process: once on one thread (8 blocks), once on N host cores (N
+    processes of one thread, 2 blocks each; N = the cores this process may
+    run on, at most 16). The blocks' inputs are drawn here (on the GPU when
+    there is one: the same seeded values) and handed over as .npy files."""
+    import shutil
+    import tempfile
+
+    import numpy as np
+
+    cfg = synth.CONFIGS["gqa70b_32k"]
+    B, H, Hq, S = cfg["batch"], cfg["num_kv_heads"], cfg["num_q_heads"], cfg["seq_len"]
+    steps = 8
+    n_all = min(16, len(os.sched_getaffinity(0)))
+    dev = "cuda" if torch.cuda.is_available() else "cpu"
+    in_dir = tempfile.mkdtemp(prefix="kvq_cpu_baseline_")
+    try:
+        for b, h in sorted(set(_cpu_blocks(max(8, 2 * n_all)))):
+            np.save(os.path.join(in_dir, f"k_{b}_{h}.npy"),
+                    synth.make_k(1, H, 0, S + steps, D, device=dev, b0=b, heads=[h])[0, 0].cpu().numpy())
+            np.save(os.path.join(in_dir, f"v_{b}_{h}.npy"),
+                    synth.make_v(1, H, 0, S + steps, D, device=dev, b0=b, heads=[h])[0, 0].cpu().numpy())
+        np.save(os.path.join(in_dir, "q.npy"), np.stack(
+            [synth.make_q(B, Hq, D, step=i, device=dev).cpu().numpy() for i in range(steps)]))
+        runs = {}
+        for workers, per in ((1, 8), (n_all, 2)):
+            r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-child",
+                                str(workers), str(per), str(steps), in_dir], capture_output=True,
+                               text=True, timeout=900, cwd=ROOT)
+            if r.returncode != 0:
+                raise RuntimeError(f"cpu baseline child failed:\n{r.stderr[-2000:]}")
+            runs[workers] = json.loads(r.stdout.strip().splitlines()[-1])
+            _log(f"[bench] cpu baseline {workers} core(s): {runs[workers]}")
+    finally:
+        shutil.rmtree(in_dir, ignore_errors=True)
+    one, alln = runs[1], runs[n_all]
+    gbs = lambda r: r["bytes"] / r["decode_s"] / 1e9
+    return {"value": round(gbs(alln), 4), "unit": "GB/s", "cores": n_all, "kind": "oracle",
+            "sample": (f"{alln['blocks']} of 128 (b, KV head) blocks of the 32K GQA layer, "
+                       f"{alln['steps']} decode steps each (append + dequantize + fp64 "
+                       f"attention of 8 query heads), {n_all} host processes of one thread "
+                       f"side by side (2 blocks each), decode {alln['decode_s']:.2f}s"),
+            "single_thread": {"value": round(gbs(one), 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"{one['blocks']} blocks x {one['steps']} steps, "
+                                        f"decode {one['decode_s']:.2f}s, prefill quantize "
+                                        f"{one['prefill_s']:.2f}s"},
+            "decode_s_per_block_step_1_thread": round(one["decode_s"] / (8 * one["blocks"]), 4)}
 
 
 def main():
@@ -393,7 +559,16 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the run, copy a device buffer of this many MiB (a known-size "
                          "transfer that calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--warmup-s", type=float, default=0.5,
+                    help="seconds of decodes before the warm-up steps (clocks settle under "
+                         "the load)")
+    ap.add_argument("--cpu-baseline-child", nargs=4, metavar=("WORKERS", "BLOCKS", "STEPS", "DIR"),
+                    help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.cpu_baseline_child:
+        w, blk, st, d = args.cpu_baseline_child
+        cpu_baseline_child(int(w), int(blk), int(st), d)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark measures one GPU only; the path runs on a "
@@ -411,7 +586,9 @@ def main():
     torch.cuda.set_device(0)
     main_res = run_main(torch, kq, synth, args)
     extra = None if args.no_extra else run_extra(torch, kq, synth)
-    cpu = None if args.no_cpu_baseline else run_cpu_baseline(synth)
+    copy_gbs = copy_peak_gbs(torch)
+    cpu = None if args.no_cpu_baseline else run_cpu_baseline(torch, synth)
+    props = torch.cuda.get_device_properties(0)
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 18                      # float32 elements
         src = torch.full((n,), 1.0, device="cuda")
@@ -448,10 +625,15 @@ def main():
                      "traffic": traffic,
                      "kernel": "decode attention (split + merge launches)",
                      "bytes_per_launch": int(main_res["decode_bytes_per_launch"]),
-                     "mean_launch_us": round(main_res["mean_decode_us"], 3)},
+                     "mean_launch_us": round(main_res["mean_decode_us"], 3),
+                     "measured_copy_gbs": round(copy_gbs, 1),
+                     "frac_of_measured_copy": round(achieved / copy_gbs, 4)},
         "cpu_baseline": cpu,
         "details": {k: (round(v, 3) if isinstance(v, float) else v)
                     for k, v in main_res.items()},
+        "env": {"device": props.name, "compute_units": props.multi_processor_count,
+                "torch": torch.__version__, "hip": torch.version.hip,
+                "decode_source_hash": decode_source_hash(), "bench_sha256_16": _file_hash()},
         "extra": extra,
     }
     print(json.dumps(line), flush=True)

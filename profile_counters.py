@@ -1,17 +1,25 @@
 #!/usr/bin/env python
 """rocprofv3 evidence for the decode kernel of bench.py's gqa70b_32k workload.
 
-Three profiler runs of a short bench (each its own process, the program right
-after `--`):
-  1. --kernel-trace --stats: per-kernel launch counts and average durations;
-  2. --pmc FETCH_SIZE and 3. --pmc WRITE_SIZE (KiB per dispatch), both with a
-     1 GiB device-to-device copy at the end (--copy-probe-mib 1024), whose
-     known size calibrates the two counters.
-Writes decode_gqa70b_32k_kernel_stats.txt, decode_gqa70b_32k_counters.txt and
+Profiler runs of a short bench (each its own process, the program right
+after `--`), chosen by name on the command line (default: all):
+  stats    --kernel-trace --stats: per-kernel launch counts and average
+           durations over the bench's default steps;
+  traffic  --pmc FETCH_SIZE, then --pmc WRITE_SIZE (KiB per dispatch), both
+           with a 1 GiB device-to-device copy at the end
+           (--copy-probe-mib 1024), whose known size calibrates the counters;
+  sq       three --pmc passes of SQ_* / GRBM_* counters over the split kernel
+           (instructions per 32-token group, VALU and MFMA busy, LDS bank
+           conflicts, shader clock);
+  gaps     --kernel-trace of the short run the round-end benchmark makes
+           (--steps 20 --warmup 5): kernel durations and the idle gaps
+           between the kernels of its timed steps.
+Writes decode_gqa70b_32k_kernel_stats.txt, decode_gqa70b_32k_counters.txt,
 decode_gqa70b_32k_counters.json (read by bench.py for roofline.traffic, keyed by
-a hash of the decode sources) to OUT/profiles/ (OUT below), to be copied into
-profiles/; raw profiler output stays under OUT/prof_*.
-Run on a machine with the GPU: python profile_counters.py
+a hash of the decode sources), decode_gqa70b_32k_sq_counters.txt and
+decode_gqa70b_32k_step_gaps.txt to OUT/profiles/ (OUT below), to be copied
+into profiles/; raw profiler output stays under OUT/prof_*.
+Run on a machine with the GPU: python profile_counters.py [stats traffic sq gaps]
 """
 from __future__ import annotations
 
@@ -35,7 +43,22 @@ BENCH_STATS = ["python3", os.path.join(ROOT, "bench.py"), "--steps", "256", "--w
                "--no-cpu-baseline", "--no-extra", "--no-cold"]
 BENCH = ["python3", os.path.join(ROOT, "bench.py"), "--steps", "16", "--warmup", "4",
          "--no-cpu-baseline", "--no-extra", "--no-cold"]
+BENCH_DRIVER = ["python3", os.path.join(ROOT, "bench.py"), "--gpus", "1", "--steps", "20",
+                "--warmup", "5", "--no-cpu-baseline", "--no-extra"]
 COPY_MIB = 1024
+# SQ / GRBM counter passes (at most 8 SQ and 2 GRBM counters per pass)
+SQ_PASSES = [
+    ["SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU",
+     "SQ_INSTS_VMEM_RD", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE", "GRBM_COUNT"],
+    ["SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_LDS",
+     "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_INST_CYCLES_VMEM_RD",
+     "SQ_INSTS_SMEM"],
+    ["SQ_INSTS_VALU_CVT", "SQ_INSTS_VALU_INT32", "SQ_INSTS_VALU_FMA_F32", "SQ_INSTS_VALU_MUL_F32",
+     "SQ_INSTS_VALU_ADD_F32", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_VALU_MFMA_MOPS_F16",
+     "SQ_INSTS_VALU_MFMA_MOPS_BF16"],
+]
+N_SIMD = 1024          # 256 compute units x 4 SIMDs
+N_XCD = 8
 DECODE = "kivi_mfma_split_kernel<2, 2, 1, true>"   # the unit-sized workgroup shape
 MERGE = "decode_merge_kernel"
 
@@ -111,13 +134,129 @@ def copy_reading(by):
     return max(vals)
 
 
+def split_stats_avg_us():
+    """The split kernel's average duration from the stats pass (written by it)."""
+    f = glob.glob(os.path.join(OUT, "prof_stats", "**", "*kernel_stats.csv"), recursive=True)
+    if not f:
+        return None
+    with open(f[0]) as fh:
+        for r in csv.DictReader(fh):
+            if DECODE in short(r["Name"]):
+                return float(r["AverageNs"]) / 1e3
+    return None
+
+
+def sq_pass():
+    """Counters of the split kernel, median per dispatch, and what they give
+    per 32-token group; the group count of a dispatch is the bench's grouped
+    tiles (16·8 (b, KV head) blocks × 1024 tiles after the first flush)."""
+    vals, cmds = {}, []
+    for i, ctrs in enumerate(SQ_PASSES):
+        d, c = run(f"sq{i}", ["--pmc", *ctrs, "--kernel-include-regex", "kivi_mfma_split_kernel"])
+        cmds.append(rel(c))
+        rows = counter_rows(d)
+        for ctr in ctrs:
+            v = pick(per_kernel(rows, ctr), DECODE)
+            vals[ctr] = statistics.median(v)
+    tiles = 16 * 8 * 1024
+    waves = vals["SQ_WAVES"]
+    dur_us = split_stats_avg_us()
+    lines = ["# rocprofv3 SQ / GRBM counters of the split kernel, gqa70b_32k decode "
+             "(bench.py --steps 16 --warmup 4, 4 layer caches); median per dispatch"]
+    lines += [f"# command (pass {i}): {c}" for i, c in enumerate(cmds)]
+    lines += [f"{k:32s} {v:16.0f}" for k, v in vals.items()]
+    per = lambda k: vals[k] / tiles
+    lines.append(f"groups (32-token tiles) per dispatch: {tiles}; wavefronts: {waves:.0f}")
+    for k in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD",
+              "SQ_INSTS_SMEM", "SQ_INSTS_VALU_CVT", "SQ_INSTS_VALU_INT32", "SQ_INSTS_VALU_FMA_F32",
+              "SQ_INSTS_VALU_MUL_F32", "SQ_INSTS_VALU_ADD_F32", "SQ_INSTS_VALU_TRANS_F32"):
+        lines.append(f"{k} per group: {per(k):8.1f}")
+    if dur_us:
+        cyc = vals["GRBM_GUI_ACTIVE"] / N_XCD
+        clk = cyc / (dur_us * 1e-6) / 1e9
+        lines.append(f"split kernel average duration (stats pass): {dur_us:.2f} us; "
+                     f"GRBM_GUI_ACTIVE / {N_XCD} XCDs = {cyc:.0f} cycles -> shader clock "
+                     f"{clk:.2f} GHz")
+        # SQ_ACTIVE_INST_VALU counts quad-cycles per wave; one VALU issue per SIMD per cycle
+        lines.append(f"VALU busy = 4*SQ_ACTIVE_INST_VALU / (SIMDs * GUI cycles) = "
+                     f"{4 * vals['SQ_ACTIVE_INST_VALU'] / (N_SIMD * cyc):.3f}")
+        lines.append(f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs * GUI cycles) = "
+                     f"{vals['SQ_VALU_MFMA_BUSY_CYCLES'] / (N_SIMD * cyc):.3f}")
+        lines.append(f"VALU issue time at that clock: 4 cycles x SQ_INSTS_VALU / SIMDs = "
+                     f"{4 * vals['SQ_INSTS_VALU'] / N_SIMD / (clk * 1e3):.1f} us")
+    lines.append(f"LDS bank conflict cycles per LDS instruction: "
+                 f"{vals['SQ_LDS_BANK_CONFLICT'] / max(1.0, vals['SQ_INSTS_LDS']):.3f}")
+    with open(os.path.join(PROF, "decode_gqa70b_32k_sq_counters.txt"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines), flush=True)
+
+
+def gaps_pass():
+    """Kernel durations and idle gaps of the timed steps of the short bench
+    run. A step is an append (its copy kernel, after the flush's quantize
+    kernel when one is due) followed by the decode's split and merge kernels;
+    the bench runs 5 warm-up steps, then the 20 steps its value is taken
+    from, then the same 20 steps with events around each decode (its
+    roofline pass)."""
+    d, c = run("gaps", ["--kernel-trace"], bench=BENCH_DRIVER)
+    f = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)[0]
+    with open(f) as fh:
+        rows = list(csv.DictReader(fh))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    names = [short(r["Kernel_Name"]) for r in rows]
+    t0 = [int(r["Start_Timestamp"]) for r in rows]
+    t1 = [int(r["End_Timestamp"]) for r in rows]
+    splits = [i for i in range(1, len(rows))
+              if DECODE in names[i] and "copy_tokens_kernel" in names[i - 1]]
+    lines = ["# rocprofv3 kernel trace of the round-end benchmark command: per timed step, "
+             "the append's kernels, the decode's split and merge, and the idle time on the "
+             "GPU between them", f"# command: {rel(c)}"]
+    summary = {}
+    # the first step of each pass follows a host synchronization: left out
+    for tag, sel in (("value pass (region events only)", splits[6:25]),
+                     ("roofline pass (events around each decode)", splits[26:45])):
+        step_us, idle_us, split_us, merge_us, app_us = [], [], [], [], []
+        for i in sel:
+            first = i - 1
+            if first > 0 and "kivi_quantize_kernel" in names[first - 1]:
+                first -= 1
+            last = i + 1 if i + 1 < len(rows) and MERGE in names[i + 1] else i
+            busy = sum(t1[k] - t0[k] for k in range(first, last + 1))
+            # the step runs from the end of the previous kernel to its last kernel's end
+            span = t1[last] - t1[first - 1]
+            step_us.append(span / 1e3)
+            idle_us.append((span - busy) / 1e3)
+            split_us.append((t1[i] - t0[i]) / 1e3)
+            if last != i:
+                merge_us.append((t1[last] - t0[last]) / 1e3)
+            app_us.append(sum(t1[k] - t0[k] for k in range(first, i)) / 1e3)
+        m = statistics.mean
+        summary[tag] = (m(step_us), m(idle_us), m(split_us), m(merge_us) if merge_us else 0.0,
+                        m(app_us), len(sel))
+        lines.append(f"{tag}: {len(sel)} steps; step {m(step_us):.2f} us = append kernels "
+                     f"{m(app_us):.2f} + split {m(split_us):.2f} + merge "
+                     f"{m(merge_us) if merge_us else 0:.2f} + idle {m(idle_us):.2f}")
+    with open(os.path.join(PROF, "decode_gqa70b_32k_step_gaps.txt"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines), flush=True)
+
+
 def main():
     os.makedirs(PROF, exist_ok=True)
     from bench import decode_source_hash
+    passes = sys.argv[1:] or ["stats", "traffic", "sq", "gaps"]
 
-    d1, c1 = run("stats", ["--kernel-trace", "--stats"], bench=BENCH_STATS)
-    stats = glob.glob(os.path.join(d1, "**", "*kernel_stats.csv"), recursive=True)[0]
-    write_stats_summary(stats, rel(c1), os.path.join(PROF, "decode_gqa70b_32k_kernel_stats.txt"))
+    if "stats" in passes:
+        d1, c1 = run("stats", ["--kernel-trace", "--stats"], bench=BENCH_STATS)
+        stats = glob.glob(os.path.join(d1, "**", "*kernel_stats.csv"), recursive=True)[0]
+        write_stats_summary(stats, rel(c1),
+                            os.path.join(PROF, "decode_gqa70b_32k_kernel_stats.txt"))
+    if "sq" in passes:
+        sq_pass()
+    if "gaps" in passes:
+        gaps_pass()
+    if "traffic" not in passes:
+        return
 
     res = {}
     cmds = {}

@@ -107,40 +107,47 @@ def k_channel_factors(num_kv_heads: int, head_dim: int, seed: int = 0,
     return f
 
 
-def _token_index(b: int, H: int, t0: int, t1: int, device):
-    """Counter base of tokens [t0, t1) of every KV head of batch element b:
-    int64 [H, t1 - t0]."""
-    h = torch.arange(H, dtype=torch.int64, device=device)
+def _token_index(b: int, H: int, t0: int, t1: int, device, heads=None):
+    """Counter base of tokens [t0, t1) of the KV heads `heads` (default: all
+    H) of batch element b: int64 [len(heads), t1 - t0]."""
+    if heads is None:
+        h = torch.arange(H, dtype=torch.int64, device=device)
+    else:
+        h = torch.tensor(list(heads), dtype=torch.int64, device=device)
     t = torch.arange(t0, t1, dtype=torch.int64, device=device)
     return ((b * H + h[:, None]) << _TOKEN_BITS) + t[None, :]
 
 
 def make_k(batch: int, num_kv_heads: int, t0: int, t1: int, head_dim: int,
-           seed: int = 0, device="cpu", b0: int = 0) -> torch.Tensor:
+           seed: int = 0, device="cpu", b0: int = 0, heads=None) -> torch.Tensor:
     """fp16 K for tokens [t0, t1) of batch elements [b0, b0 + B):
-    shape [B, H, t1 - t0, D]."""
+    shape [B, H, t1 - t0, D]; with `heads` (KV head indices), only those
+    heads: [B, len(heads), t1 - t0, D], each equal to its slice of the full
+    tensor."""
     assert 0 <= t0 <= t1 < (1 << _TOKEN_BITS)
     f = k_channel_factors(num_kv_heads, head_dim, seed, device)
-    out = torch.empty(batch, num_kv_heads, t1 - t0, head_dim,
+    hs = list(range(num_kv_heads)) if heads is None else list(heads)
+    out = torch.empty(batch, len(hs), t1 - t0, head_dim,
                       dtype=torch.float16, device=device)
     d = torch.arange(head_dim, dtype=torch.int64, device=device)
     for b in range(batch):
-        tok = _token_index(b0 + b, num_kv_heads, t0, t1, device)
+        tok = _token_index(b0 + b, num_kv_heads, t0, t1, device, hs)
         idx = tok[:, :, None] * head_dim + d
-        out[b] = _to_fp16(normal(seed, STREAM_K, idx) * f[:, None, :])
+        out[b] = _to_fp16(normal(seed, STREAM_K, idx) * f[hs][:, None, :])
     return out
 
 
 def make_v(batch: int, num_kv_heads: int, t0: int, t1: int, head_dim: int,
-           seed: int = 0, device="cpu", b0: int = 0) -> torch.Tensor:
+           seed: int = 0, device="cpu", b0: int = 0, heads=None) -> torch.Tensor:
     """fp16 V for tokens [t0, t1) of batch elements [b0, b0 + B):
-    shape [B, H, t1 - t0, D]."""
+    shape [B, H, t1 - t0, D] (only the KV heads `heads` when given)."""
     assert 0 <= t0 <= t1 < (1 << _TOKEN_BITS)
-    out = torch.empty(batch, num_kv_heads, t1 - t0, head_dim,
+    hs = list(range(num_kv_heads)) if heads is None else list(heads)
+    out = torch.empty(batch, len(hs), t1 - t0, head_dim,
                       dtype=torch.float16, device=device)
     d = torch.arange(head_dim, dtype=torch.int64, device=device)
     for b in range(batch):
-        tok = _token_index(b0 + b, num_kv_heads, t0, t1, device)
+        tok = _token_index(b0 + b, num_kv_heads, t0, t1, device, hs)
         g = torch.exp(0.5 * normal(seed, STREAM_VF, tok))
         idx = tok[:, :, None] * head_dim + d
         out[b] = _to_fp16(normal(seed, STREAM_V, idx) * g[:, :, None])

@@ -32,3 +32,11 @@ def test_threefry_counter_chunking():
     full = synth.normal(0, synth.STREAM_K, idx)
     for i in (0, 1, 499, 999):
         assert float(synth.normal(0, synth.STREAM_K, idx[i:i + 1])[0]) == float(full[i])
+
+
+def test_head_selection_is_a_slice():
+    """Drawing only some KV heads gives exactly those heads' slices."""
+    k = synth.make_k(2, 8, 5, 40, 128, b0=3)
+    v = synth.make_v(2, 8, 5, 40, 128, b0=3)
+    assert torch.equal(synth.make_k(1, 8, 5, 40, 128, b0=4, heads=[6, 2])[0], k[1, [6, 2]])
+    assert torch.equal(synth.make_v(1, 8, 5, 40, 128, b0=4, heads=[7])[0], v[1, [7]])
