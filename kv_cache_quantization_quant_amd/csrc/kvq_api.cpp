@@ -15,6 +15,7 @@
 
 #include <algorithm>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "../../include/kvq.h"
@@ -809,7 +810,14 @@ static kvq_status decode_enqueue(const kvq_cache* cache, const float* q, int32_t
     const int cus = kvq::device_compute_units();
     a.unit = cus > 0 && x <= cus ? 1 : 0;
   }
-  const int64_t target = int64_t(kvq::decode_resident_workgroups(a)) * KVQ_SPLIT_ROUNDS;
+  int64_t target = int64_t(kvq::decode_resident_workgroups(a)) * KVQ_SPLIT_ROUNDS;
+  // KVQ_DECODE_TARGET_WORKGROUPS (environment, read per call) replaces the
+  // workgroup target: the same cache can then be decoded under other split
+  // plans (a test of the split merge) or the plan tuned without a rebuild
+  if (const char* env = getenv("KVQ_DECODE_TARGET_WORKGROUPS")) {
+    const long t = strtol(env, nullptr, 10);
+    if (t > 0) target = t;
+  }
   const Plan p = ragged ? make_plan_ragged(d, nq, cache, target)
                         : make_plan(d, nq, cache->n_quant, n_win, target);
   if (p.n_split > max_splits(d, nq)) return KVQ_ERR_WORKSPACE;
