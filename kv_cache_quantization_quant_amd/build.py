@@ -52,9 +52,17 @@ def _scratch_kernels(remarks: str) -> list[str]:
     return bad
 
 
+# Per-source flags. The decode kernels' only atomics are the LDS tile counters,
+# taken by one lane per wavefront: the atomic optimizer's wave-wide
+# reduction around them (lane counts, prefix, broadcast) is pure overhead in
+# the steady-state loop.
+EXTRA = {"kvq_decode_mfma.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src),
+           "-o", obj]
     if src.endswith(".hip"):
         cmd.append("-Rpass-analysis=kernel-resource-usage")
     r = subprocess.run(cmd, capture_output=True, text=True)

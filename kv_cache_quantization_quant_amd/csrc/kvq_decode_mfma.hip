@@ -55,6 +55,7 @@
 #include <math.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "kvq_fp8.h"
 #include "kvq_internal.h"
@@ -1090,19 +1091,25 @@ __attribute__((amdgpu_waves_per_eu((kivi_waves_per_simd<BITS, VB, NVS>())))) voi
       // until the split runs out of tiles; each iteration takes the tile of
       // the next one, so the counter's round trip overlaps the arithmetic
       uint32_t t_next = (KVQ_TAKE_AHEAD && n_mine < 0) ? take() : n_blk;
-      while (n_mine < 0) {
+      // One steady-state iteration for group i, whose stage i % kDepth is the
+      // compile-time PH: every LDS address of the ring is then a constant
+      // offset from the wavefront's ring base. Returns false once the split
+      // has no tile left (n_mine is then known).
+      auto step = [&](auto ph) -> bool {
+        constexpr int PH = decltype(ph)::value;
         // the refilled stage was last read two groups ago; its reads are done
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (!KVQ_TAKE_AHEAD) t_next = take();
         if (t_next >= n_blk) {
           n_mine = i + kAhead;
-          break;
+          return false;
         }
-        issue_group<BITS, VB, NVS>(ring_w + ((i + kAhead) % kDepth) * S::kBytes,
-                                   group_src<BITS, VB, NVS, PAGED>(a, bh, b, h_kv, g0 + t_next), v16, h16, h4);
+        issue_group<BITS, VB, NVS>(ring_w + ((PH + kAhead) % kDepth) * S::kBytes,
+                                   group_src<BITS, VB, NVS, PAGED>(a, bh, b, h_kv, g0 + t_next),
+                                   v16, h16, h4);
         wait_vmem<kAhead * S::kLoads>();
-        load_v<BITS, VB, NVS>(ring_w + ((i - 1) % kDepth) * S::kBytes, r, u, V);
-        load_k<BITS, VB, NVS>(ring_w + (i % kDepth) * S::kBytes, r, u, low, K);
+        load_v<BITS, VB, NVS>(ring_w + ((PH + kDepth - 1) % kDepth) * S::kBytes, r, u, V);
+        load_k<BITS, VB, NVS>(ring_w + PH * S::kBytes, r, u, low, K);
         if (KVQ_TAKE_AHEAD) t_next = take();
         // keep every LDS read of the iteration ahead of the arithmetic
         __builtin_amdgcn_sched_barrier(0);
@@ -1110,6 +1117,20 @@ __attribute__((amdgpu_waves_per_eu((kivi_waves_per_simd<BITS, VB, NVS>())))) voi
         group_values<VB, NVS>(V, W, bp_prev, vsh, vm0, vm1, magic, magic32);
         group_probs<BITS, true, NVS>(W, sc, K.vs, K.vz, bp_prev);
         ++i;
+        return true;
+      };
+      // group 1 is in stage 1: the stages then follow 2, .., kDepth - 1, 0, 1, ..
+      if (n_mine < 0) {
+        using std::integral_constant;
+        if constexpr (kDepth == 3) {
+          while (step(integral_constant<int, 1>{}) && step(integral_constant<int, 2>{}) &&
+                 step(integral_constant<int, 0>{})) {
+          }
+        } else {
+          while (step(integral_constant<int, 1>{}) && step(integral_constant<int, 2>{}) &&
+                 step(integral_constant<int, 3>{}) && step(integral_constant<int, 0>{})) {
+          }
+        }
       }
       // the last kAhead groups (fewer for a wavefront with fewer groups):
       // nothing left to load

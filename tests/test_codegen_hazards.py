@@ -70,7 +70,8 @@ def _operand_gaps(body):
 @pytest.fixture(scope="module")
 def decode_asm(tmp_path_factory):
     out = tmp_path_factory.mktemp("asm") / "dec.s"
-    cmd = [kbuild.HIPCC, *[f for f in kbuild.COMMON if f != "-fPIC"], "--cuda-device-only", "-S",
+    cmd = [kbuild.HIPCC, *[f for f in kbuild.COMMON if f != "-fPIC"],
+           *kbuild.EXTRA.get(os.path.basename(SRC), []), "--cuda-device-only", "-S",
            "-x", "hip", SRC, "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
