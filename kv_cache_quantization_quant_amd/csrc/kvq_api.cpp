@@ -274,6 +274,9 @@ Plan make_plan(const Dims& d, int nq, int64_t n_main, int n_win, int64_t target)
   // no more splits per (b, h) than whole rounds of the target allow
   if (x <= target && tiles > 0) tps = std::max(tps, ceil_div(tiles, target / x));
   if (tps < kMinTilesPerSplit) tps = kMinTilesPerSplit;
+  // whole K groups per split (G > 32: the decode keeps a group's score
+  // operands across its tiles)
+  tps = ceil_div(tps, d.G / kGroup) * (d.G / kGroup);
   p.tiles_per_split = int(tps);
   p.n_split_main = int(ceil_div(tiles, tps));
   if (fold) {
@@ -342,6 +345,7 @@ Plan make_plan_ragged(const Dims& d, int nq, const kvq_cache* c, int64_t target)
     }
     tps = hi;
   }
+  tps = ceil_div(tps, d.G / kGroup) * (d.G / kGroup);   // whole K groups per split
   p.tiles_per_split = int(tps);
   p.n_split_main = int(ceil_div(max_tiles, tps));
   p.n_split = std::max(p.n_split_main, 1);

@@ -382,7 +382,7 @@ struct VLoad {
 
 template <int BITS, int VB, int NVS>
 __device__ __forceinline__ void load_k(const uint8_t* st, int r, int u, bool low,
-                                       KLoad<BITS, NVS>& K) {
+                                       KLoad<BITS, NVS>& K, bool kscale = true) {
   using S = Stage<BITS, VB, NVS>;
   const uint8_t* kc = st + S::kKc;
   constexpr int kRow = kHeadDim * BITS / 8;
@@ -396,11 +396,15 @@ __device__ __forceinline__ void load_k(const uint8_t* st, int r, int u, bool low
     K.w0[0] = x.x; K.w0[1] = x.y; K.w0[2] = x.z; K.w0[3] = x.w;
     K.w1[0] = y.x; K.w1[1] = y.y; K.w1[2] = y.z; K.w1[3] = y.w;
   }
-  const float4* ksz = reinterpret_cast<const float4*>(st + S::kKsz) + 8 * u + (low ? 4 : 0);
+  // K scales and zero-points (read apart, once per K group, when a group's
+  // operands are kept across its tiles)
+  if (kscale) {
+    const float4* ksz = reinterpret_cast<const float4*>(st + S::kKsz) + 8 * u + (low ? 4 : 0);
 #pragma unroll
-  for (int c4 = 0; c4 < 4; ++c4) K.kz[c4] = ksz[kHeadDim / 4 + c4];
+    for (int c4 = 0; c4 < 4; ++c4) K.kz[c4] = ksz[kHeadDim / 4 + c4];
 #pragma unroll
-  for (int c4 = 0; c4 < 4; ++c4) K.ks[c4] = ksz[c4];
+    for (int c4 = 0; c4 < 4; ++c4) K.ks[c4] = ksz[c4];
+  }
   if (NVS == 1) {
     const float4* vsz = reinterpret_cast<const float4*>(st + S::kVsz) + (low ? 4 : 0) + u;
     K.vs[0] = vsz[0];
@@ -414,6 +418,18 @@ __device__ __forceinline__ void load_k(const uint8_t* st, int r, int u, bool low
       K.vz[i] = vsz[kGroup * NVS / 4 + i];
     }
   }
+}
+
+// K scales and zero-points of a stage alone (the kscale part of load_k)
+template <int BITS, int VB, int NVS>
+__device__ __forceinline__ void load_kscale(const uint8_t* st, int u, bool low,
+                                            KLoad<BITS, NVS>& K) {
+  using S = Stage<BITS, VB, NVS>;
+  const float4* ksz = reinterpret_cast<const float4*>(st + S::kKsz) + 8 * u + (low ? 4 : 0);
+#pragma unroll
+  for (int c4 = 0; c4 < 4; ++c4) K.kz[c4] = ksz[kHeadDim / 4 + c4];
+#pragma unroll
+  for (int c4 = 0; c4 < 4; ++c4) K.ks[c4] = ksz[c4];
 }
 
 template <int KB, int BITS, int NVS>
@@ -480,6 +496,66 @@ __device__ __forceinline__ void group_scores(const KLoad<BITS, NVS>& K, bool low
     s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(k_operand<BITS>(m1, 2 + h)), as_f16x8(bl), s1, 0, 0, 0);
   }
   // ---- both columns of the head; part 0 keeps tile 0, part 1 tile 1
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float t0 = s0[i] + xor8(s0[i]);
+    const float t1 = s1[i] + xor8(s1[i]);
+    sc[i] = low ? t1 : t0;
+  }
+}
+
+// With G > 32 (the K scales and zero-points shared by G / 32 tiles) the
+// score-side operands of a K group are built once, on its first tile, and
+// kept across the group's tiles: Q' as the B operands of both halves of the
+// k-steps (high and low terms already exchanged) and the z-term.
+struct GroupQ {
+  u32x4 bh[2], bl[2];
+  float zt;
+};
+
+// The first half of group_scores: Q' and the z-term of a K group.
+template <int BITS, int NVS>
+__device__ __forceinline__ void group_q(const KLoad<BITS, NVS>& K, const float (&q16)[16],
+                                        GroupQ& Q) {
+  float zp[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float4 z = K.kz[j];
+    zp[j] = fmaf(q16[4 * j + 3], z.w, fmaf(q16[4 * j + 2], z.z,
+                 fmaf(q16[4 * j + 1], z.y, q16[4 * j] * z.x)));
+  }
+  Q.zt = sum_x16_x32((zp[0] + zp[1]) + (zp[2] + zp[3]));
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int c0 = 8 * h + kslot_channel(2 * p), c1 = 8 * h + kslot_channel(2 * p + 1);
+      split_pair(q16[c0] * f4_at(K.ks, c0), q16[c1] * f4_at(K.ks, c1), hi[p], lo[p]);
+    }
+    swap_halves4(hi, lo);
+    Q.bh[h] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+    Q.bl[h] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+  }
+}
+
+// The second half of group_scores: the scores of one tile from its K codes
+// and its group's operands.
+template <int BITS, int NVS>
+__device__ __forceinline__ void tile_scores(const KLoad<BITS, NVS>& K, bool low, const GroupQ& Q,
+                                            float m_part, float (&sc)[4]) {
+  uint32_t m0[2 * BITS], m1[2 * BITS];
+  k_masks<BITS>(K.w0, m0);
+  k_masks<BITS>(K.w1, m1);
+  const float zt = Q.zt - m_part;
+  f32x4 s0 = f32x4{zt, zt, zt, zt}, s1 = s0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(k_operand<BITS>(m0, h)), as_f16x8(Q.bh[h]), s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(k_operand<BITS>(m1, h)), as_f16x8(Q.bh[h]), s1, 0, 0, 0);
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(k_operand<BITS>(m0, 2 + h)), as_f16x8(Q.bl[h]), s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(k_operand<BITS>(m1, 2 + h)), as_f16x8(Q.bl[h]), s1, 0, 0, 0);
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float t0 = s0[i] + xor8(s0[i]);
@@ -942,10 +1018,14 @@ constexpr int kivi_waves() {
   return UNIT ? 4 * kivi_waves_per_simd<BITS, VB, NVS>() : 4;
 }
 
-template <int BITS, int VB, int NVS, bool UNIT, bool PAGED>
+// GRP (G > 32, one V scale per token, contiguous cache): a wavefront takes
+// whole K groups of G / 32 tiles and keeps the group's score operands across
+// them (K scales read, Q' split and z-term summed once per group).
+template <int BITS, int VB, int NVS, bool UNIT, bool PAGED, bool GRP = false>
 __global__ __launch_bounds__((64 * kivi_waves<BITS, VB, NVS, UNIT>()))
 __attribute__((amdgpu_waves_per_eu((kivi_waves_per_simd<BITS, VB, NVS>())))) void kivi_mfma_split_kernel(
     DecodeArgs a) {
+  static_assert(!GRP || (NVS == 1 && !PAGED), "group operands kept on the contiguous layout");
   using S = Stage<BITS, VB, NVS>;
   constexpr int NW = kivi_waves<BITS, VB, NVS, UNIT>();
   // ring stages per wavefront: the unit-sized workgroup keeps one group in
@@ -1044,11 +1124,40 @@ __attribute__((amdgpu_waves_per_eu((kivi_waves_per_simd<BITS, VB, NVS>())))) voi
     // wave, wave + NW, ... in fixed order
     constexpr bool kShare = UNIT;
     uint32_t taken = 0;
-    auto take = [&]() -> uint32_t {
+    // GRP: the counter and the fixed order hand out K groups, whose tiles the
+    // wavefront then takes one by one (a split holds whole groups)
+    auto take_unit = [&]() -> uint32_t {
       if (!kShare || a.fixed_order) return uint32_t(wave) + uint32_t(NW) * taken++;
       uint32_t t = 0;
       if (lane == 0) t = atomicAdd(&next_tile, 1u);
       return __builtin_amdgcn_readfirstlane(t);
+    };
+    const uint32_t gs_mask = GRP ? (1u << a.gshift) - 1u : 0u;   // tiles per K group - 1
+    uint32_t grp_next = 0;                                        // GRP: next tile to hand out
+    auto take = [&]() -> uint32_t {
+      if constexpr (GRP) {
+        if ((grp_next & gs_mask) == 0) grp_next = take_unit() << a.gshift;
+        return grp_next++;
+      }
+      return take_unit();
+    };
+    // The wavefront's i-th tile is the first of its K group when i is a
+    // multiple of G / 32 (it takes whole groups, in order). Its operands are
+    // built from the stage before the iteration's other LDS reads, while the
+    // previous tile's V codes are not yet in registers.
+    GroupQ Qg;
+    auto group_ops = [&](const uint8_t* st, int idx) {
+      if constexpr (GRP) {
+        if ((uint32_t(idx) & gs_mask) == 0) {
+          KLoad<BITS, NVS> KS;
+          load_kscale<BITS, VB, NVS>(st, u, low, KS);
+          group_q<BITS, NVS>(KS, q16, Qg);
+        }
+      }
+    };
+    auto scores = [&](const KLoad<BITS, NVS>& K, float m_part, float (&sc_out)[4]) {
+      if constexpr (GRP) tile_scores<BITS, NVS>(K, low, Qg, m_part, sc_out);
+      else group_scores<BITS, NVS>(K, low, q16, m_part, sc_out);
     };
     int n_mine = -1;
 #pragma unroll
@@ -1082,8 +1191,9 @@ __attribute__((amdgpu_waves_per_eu((kivi_waves_per_simd<BITS, VB, NVS>())))) voi
       if (n_mine >= 0) wait_groups<BITS, VB, NVS>(n_mine - 1);
       KLoad<BITS, NVS> K;
       VLoad V;
-      load_k<BITS, VB, NVS>(ring_w, r, u, low, K);
-      group_scores<BITS, NVS>(K, low, q16, 0.0f, sc);
+      group_ops(ring_w, 0);
+      load_k<BITS, VB, NVS>(ring_w, r, u, low, K, !GRP);
+      scores(K, 0.0f, sc);
       u32x4 bp_prev[NVS];
       group_probs<BITS, false, NVS>(W, sc, K.vs, K.vz, bp_prev);
       int i = 1;
@@ -1108,12 +1218,13 @@ __attribute__((amdgpu_waves_per_eu((kivi_waves_per_simd<BITS, VB, NVS>())))) voi
                                    group_src<BITS, VB, NVS, PAGED>(a, bh, b, h_kv, g0 + t_next),
                                    v16, h16, h4);
         wait_vmem<kAhead * S::kLoads>();
+        group_ops(ring_w + PH * S::kBytes, i);
         load_v<BITS, VB, NVS>(ring_w + ((PH + kDepth - 1) % kDepth) * S::kBytes, r, u, V);
-        load_k<BITS, VB, NVS>(ring_w + PH * S::kBytes, r, u, low, K);
+        load_k<BITS, VB, NVS>(ring_w + PH * S::kBytes, r, u, low, K, !GRP);
         if (KVQ_TAKE_AHEAD) t_next = take();
         // keep every LDS read of the iteration ahead of the arithmetic
         __builtin_amdgcn_sched_barrier(0);
-        group_scores<BITS, NVS>(K, low, q16, low ? 0.0f : W.m_ref, sc);
+        scores(K, low ? 0.0f : W.m_ref, sc);
         group_values<VB, NVS>(V, W, bp_prev, vsh, vm0, vm1, magic, magic32);
         group_probs<BITS, true, NVS>(W, sc, K.vs, K.vz, bp_prev);
         ++i;
@@ -1136,11 +1247,12 @@ __attribute__((amdgpu_waves_per_eu((kivi_waves_per_simd<BITS, VB, NVS>())))) voi
       // nothing left to load
       for (; i < n_mine; ++i) {
         wait_groups<BITS, VB, NVS>(n_mine - 1 - i);
+        group_ops(ring_w + (i % kDepth) * S::kBytes, i);
         load_v<BITS, VB, NVS>(ring_w + ((i - 1) % kDepth) * S::kBytes, r, u, V);
-        load_k<BITS, VB, NVS>(ring_w + (i % kDepth) * S::kBytes, r, u, low, K);
+        load_k<BITS, VB, NVS>(ring_w + (i % kDepth) * S::kBytes, r, u, low, K, !GRP);
         // keep every LDS read of the iteration ahead of the arithmetic
         __builtin_amdgcn_sched_barrier(0);
-        group_scores<BITS, NVS>(K, low, q16, low ? 0.0f : W.m_ref, sc);
+        scores(K, low ? 0.0f : W.m_ref, sc);
         group_values<VB, NVS>(V, W, bp_prev, vsh, vm0, vm1, magic, magic32);
         group_probs<BITS, true, NVS>(W, sc, K.vs, K.vz, bp_prev);
       }
@@ -1496,19 +1608,30 @@ hipError_t launch_dense_mfma(const DecodeArgs& a, hipStream_t s) {
 
 // launches the (K bits, V bits) instance with NVS V scales per token, in the
 // workgroup shape a.unit selects
-template <int KB, int VB, int NVS, bool PAGED>
+template <int KB, int VB, int NVS, bool PAGED, bool GRP>
 static void launch_kivi_paging(const DecodeArgs& a, dim3 grid, hipStream_t s) {
   if (a.unit)
-    kivi_mfma_split_kernel<KB, VB, NVS, true, PAGED>
+    kivi_mfma_split_kernel<KB, VB, NVS, true, PAGED, GRP>
         <<<grid, 64 * kivi_waves<KB, VB, NVS, true>(), 0, s>>>(a);
   else
-    kivi_mfma_split_kernel<KB, VB, NVS, false, PAGED>
+    kivi_mfma_split_kernel<KB, VB, NVS, false, PAGED, GRP>
         <<<grid, 64 * kivi_waves<KB, VB, NVS, false>(), 0, s>>>(a);
 }
+// Contiguous caches with G > 32 and one V scale per token keep each K
+// group's score operands across its tiles (the split plan holds whole groups).
 template <int KB, int VB, int NVS>
 static void launch_kivi_shape(const DecodeArgs& a, dim3 grid, hipStream_t s) {
-  if (a.paged) launch_kivi_paging<KB, VB, NVS, true>(a, grid, s);
-  else launch_kivi_paging<KB, VB, NVS, false>(a, grid, s);
+  if (a.paged) {
+    launch_kivi_paging<KB, VB, NVS, true, false>(a, grid, s);
+    return;
+  }
+  if constexpr (NVS == 1) {
+    if (a.gshift > 0) {
+      launch_kivi_paging<KB, VB, NVS, false, true>(a, grid, s);
+      return;
+    }
+  }
+  launch_kivi_paging<KB, VB, NVS, false, false>(a, grid, s);
 }
 template <int NVS>
 static hipError_t launch_kivi_nvs(const DecodeArgs& a, dim3 grid, hipStream_t s) {

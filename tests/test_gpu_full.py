@@ -131,19 +131,24 @@ def _splits_written(ws, rows, sentinel_bits=0xFFFFFFFF):
     return int((m != -1).sum()) // rows
 
 
-@pytest.mark.parametrize("fmt,det", [("kivi", 0), ("kivi", 1), ("fp8", 0), ("fp16", 0)])
-def test_split_count_invariance(kq, fmt, det, monkeypatch):
+@pytest.mark.parametrize("fmt,det,G", [("kivi", 0, 32), ("kivi", 1, 32), ("kivi", 0, 64),
+                                       ("kivi", 0, 128), ("kivi", 1, 128), ("fp8", 0, 32),
+                                       ("fp16", 0, 32)])
+def test_split_count_invariance(kq, fmt, det, G, monkeypatch):
+    """G = 64 and 128 run the decode that keeps a K group's score operands
+    across its tiles (a split then holds whole groups)."""
     B, H, Hq, S, steps = 2, 4, 32, 8000, 70
     C = S + steps
     k = synth.make_k(B, H, 0, C, D, device="cuda")
     v = synth.make_v(B, H, 0, C, D, device="cuda")
+    extra = dict(group_size=G) if fmt == "kivi" else {}
     dc = kq.DeviceCache(kq.make_config(fmt, batch=B, num_kv_heads=H, capacity=C,
-                                       deterministic=det))
+                                       deterministic=det, **extra))
     dc.prefill(k[:, :, :S].contiguous(), v[:, :, :S].contiguous())
     for t in range(S, C):                       # a flush, and a 70-token window (KIVI)
         dc.append(k[:, :, t].contiguous(), v[:, :, t].contiguous())
     if fmt == "kivi":
-        oc = ocache.KiviCache(B, H, D, 2, 32, 128, C)
+        oc = ocache.KiviCache(B, H, D, 2, G, 128, C)
     elif fmt == "fp8":
         oc = ocache.Fp8Cache(B, H, D, C)
     else:
@@ -170,7 +175,7 @@ def test_split_count_invariance(kq, fmt, det, monkeypatch):
         assert errs[-1] <= ATOL, (target, errs[-1])
     monkeypatch.delenv("KVQ_DECODE_TARGET_WORKGROUPS", raising=False)
     spread = max(float((o - outs[0]).abs().max()) for o in outs)
-    _say(f"[split invariance] {fmt} det={det}: splits per row {splits}, "
+    _say(f"[split invariance] {fmt} det={det} G={G}: splits per row {splits}, "
          f"max |difference| {spread:.2e}, errors vs oracle {[f'{e:.1e}' for e in errs]}")
     assert len(set(splits)) >= 3, splits
     # each plan sums the same products in another fp32 order (and the P

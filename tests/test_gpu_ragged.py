@@ -57,6 +57,7 @@ def _compare(dc, oc):
     (32, 2, 0, 32, 128, 2, 16, [257, 700, 96], 30),         # V scales per 32 channels
     (128, 2, 4, 0, 128, 2, 8, [1000, 129, 640], 20),
     (32, 2, 0, 0, 128, 4, 32, [4096, 1000, 3000, 77, 2048, 333], 5),   # many splits
+    (128, 2, 0, 0, 128, 4, 32, [4096, 1000, 3000, 77, 2048, 333], 5),  # whole K groups per split
 ])
 def test_ragged_prefill_append_decode(kq, G, bits, vbits, gc, R, H, Hq, lens, steps):
     B = len(lens)
