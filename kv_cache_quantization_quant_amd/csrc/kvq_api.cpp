@@ -614,14 +614,24 @@ kvq_status append_ragged(kvq_cache* cache, const Dims& d, const __half* kh, cons
     any_flush = any_flush || full;
   }
   if (any_flush) {
+    // one launch: the flushing sequences' groups, and every sequence's new
+    // token (slot 0 after a flush, else after its window's last token)
     qa.n_groups = int(d.Rcap / d.G);
+    qa.k_new = kh;
+    qa.v_new = vh;
+    qa.k_win = static_cast<__half*>(cache->k_resid);
+    qa.v_win = static_cast<__half*>(cache->v_resid);
+    qa.win_bh_stride = d.Rcap * d.D;
+    for (int64_t b = 0; b < d.B; ++b) qa.seq.z[b] = qa.seq.x[b] > 0 ? 0 : cache->seq_n_resid[b];
     if (kvq::launch_kivi_quantize(qa, s) != hipSuccess) return KVQ_ERR_DEVICE;
     for (int64_t b = 0; b < d.B; ++b) {
       if (qa.seq.x[b] > 0) {
         cache->seq_n_quant[b] += d.Rcap;
         cache->seq_n_resid[b] = 0;
       }
+      cache->seq_n_resid[b] += 1;
     }
+    return KVQ_OK;
   }
   kvq::CopyTokensArgs ca{};
   ca.k_src = kh;
@@ -684,9 +694,16 @@ kvq_status kvq_append_token(kvq_cache* cache, const void* k_new, const void* v_n
       qa.k_zero = cache->k_zero;
       qa.v_scale = cache->v_scale;
       qa.v_zero = cache->v_zero;
+      // the new token goes to window slot 0 in the same launch
+      qa.k_new = kh;
+      qa.v_new = vh;
+      qa.k_win = static_cast<__half*>(cache->k_resid);
+      qa.v_win = static_cast<__half*>(cache->v_resid);
+      qa.win_bh_stride = d.Rcap * d.D;
       if (kvq::launch_kivi_quantize(qa, s) != hipSuccess) return KVQ_ERR_DEVICE;
       cache->n_quant += d.Rcap;
-      cache->n_resid = 0;
+      cache->n_resid = 1;
+      return KVQ_OK;
     }
     kvq::CopyTokensArgs ca{};
     ca.k_src = kh;

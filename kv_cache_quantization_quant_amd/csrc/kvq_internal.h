@@ -56,6 +56,16 @@ struct KiviQuantArgs {
   int max_pages;
   int page_group_shift;
   int num_pages;
+  // a window flush folds in the append that triggered it: the new token
+  // (fp16 [B·H][D]) goes to window slot 0 of each (b, h) block (a ragged
+  // batch: slot seq.z[b], and sequences that do not flush only take the new
+  // token), written by the block's group-0 workgroup once it holds its loads
+  // of that slot (null k_new: no token)
+  const __half* k_new;
+  const __half* v_new;
+  __half* k_win;
+  __half* v_win;
+  int64_t win_bh_stride;  // elements between window blocks
   RaggedTable seq;
 };
 

@@ -94,6 +94,17 @@ __device__ __forceinline__ void pack16(const float (&c)[16], uint32_t (&w)[BITS 
   }
 }
 
+// The appended token of (b, h) block bh into window slot `slot`: 16 threads
+// copy K, 16 copy V (16 bytes each).
+__device__ __forceinline__ void write_new_token(const KiviQuantArgs& a, int bh, int64_t slot,
+                                                int tid) {
+  if (tid >= 32) return;
+  const int c = tid & 15;
+  const __half* src = (tid < 16 ? a.k_new : a.v_new) + int64_t(bh) * kHeadDim + 8 * c;
+  __half* dst = (tid < 16 ? a.k_win : a.v_win) + bh * a.win_bh_stride + slot * kHeadDim + 8 * c;
+  *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+}
+
 // One workgroup quantizes one group of G = 32·NS tokens (NS sub-tiles of 32
 // tokens × 128 channels) of K and of V for one (b, h). Loads: thread
 // (t = tid / 8, j = tid % 8) holds channels [16j, 16j + 16) of token t of each
@@ -134,9 +145,15 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
   const int t = tid >> 3;
   const int j = tid & 7;
   int64_t gg = a.g0 + g;                   // cache group
+  int64_t new_slot = 0;                    // window slot of the appended token
   if (a.ragged) {                          // block-uniform: the whole block leaves
     const int b = bh / a.H;
-    if (g >= a.seq.x[b]) return;
+    new_slot = a.seq.z[b];
+    if (g >= a.seq.x[b]) {
+      // a sequence that does not flush only takes the appended token
+      if (g == 0 && a.k_new != nullptr) write_new_token(a, bh, new_slot, tid);
+      return;
+    }
     gg = int64_t(a.seq.y[b]) + g;
   }
   // destination (b, h) block of the cache arrays, and the group within it: a
@@ -210,6 +227,8 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
     for (int k = 0; k < VTW; ++k) vt[sub][VTW * j + k][t] = w[k];
   }
   __syncthreads();
+  // every load of the group has been consumed: slot 0 may take the new token
+  if (g == 0 && a.k_new != nullptr) write_new_token(a, bh, new_slot, tid);
 
   // ---- K statistics over the G rows: wavefront w, channels 32w + 2c, +1
   {

@@ -56,6 +56,21 @@ hipError_t launch_kivi_quantize(const KiviQuantArgs& a, hipStream_t) {
   } else {
     require(group_range_ok(a, a.g0, a.n_groups), "quantize: group range");
   }
+  if (a.k_new != nullptr) {
+    // the folded append: one token per (b, h) block into a window slot
+    require(a.v_new != nullptr && a.k_win != nullptr && a.v_win != nullptr,
+            "quantize: new token buffers");
+    require(a.n_groups >= 1, "quantize: a group-0 workgroup per block writes the new token");
+    require(a.win_bh_stride % kHeadDim == 0, "quantize: window rows");
+    const int64_t cap = a.win_bh_stride / kHeadDim;
+    if (a.ragged) {
+      for (int b = 0; b < a.bh_count / a.H; ++b)
+        require(a.seq.z[b] >= 0 && a.seq.z[b] < cap && (a.seq.x[b] == 0 || a.seq.z[b] == 0),
+                "quantize: new token slot");
+    } else {
+      require(cap >= 1, "quantize: new token slot");
+    }
+  }
   return hipSuccess;
 }
 
