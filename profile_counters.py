@@ -13,13 +13,18 @@ after `--`), chosen by name on the command line (default: all):
            conflicts, shader clock);
   gaps     --kernel-trace of the short run the round-end benchmark makes
            (--steps 20 --warmup 5): kernel durations and the idle gaps
-           between the kernels of its timed steps.
+           between the kernels of its timed steps;
+  quant    the prefill quantize kernel of the same short bench (its 32K
+           prefills, the dispatches with the largest grid): durations from a
+           kernel trace, the SQ / GRBM passes, FETCH_SIZE / WRITE_SIZE
+           calibrated by the 1 GiB copy, against the bytes it must move.
 Writes decode_gqa70b_32k_kernel_stats.txt, decode_gqa70b_32k_counters.txt,
 decode_gqa70b_32k_counters.json (read by bench.py for roofline.traffic, keyed by
-a hash of the decode sources), decode_gqa70b_32k_sq_counters.txt and
-decode_gqa70b_32k_step_gaps.txt to OUT/profiles/ (OUT below), to be copied
+a hash of the decode sources), decode_gqa70b_32k_sq_counters.txt,
+decode_gqa70b_32k_step_gaps.txt and prefill_quantize_gqa70b_32k_counters.txt
+to OUT/profiles/ (OUT below), to be copied
 into profiles/; raw profiler output stays under OUT/prof_*.
-Run on a machine with the GPU: python profile_counters.py [stats traffic sq gaps]
+Run on a machine with the GPU: python profile_counters.py [stats traffic sq gaps quant]
 """
 from __future__ import annotations
 
@@ -59,8 +64,12 @@ SQ_PASSES = [
 ]
 N_SIMD = 1024          # 256 compute units x 4 SIMDs
 N_XCD = 8
-DECODE = "kivi_mfma_split_kernel<2, 2, 1, true>"   # the unit-sized workgroup shape
+DECODE = "kivi_mfma_split_kernel<2, 2, 1, true, false, false>"   # unit-sized workgroups, contiguous, G = 32
 MERGE = "decode_merge_kernel"
+QUANT = "kivi_quantize_kernel<2, 2, 1>"
+# the 32K prefill: B = 16, 8 KV heads, 32768 tokens of which 32640 are grouped
+# (R = 128 stay in the window), D = 128, 2-bit K and V, G = 32
+PRE_B, PRE_H, PRE_NQ, PRE_D, PRE_BITS, PRE_G = 16, 8, 32640, 128, 2, 32
 
 
 def run(tag, prof_args, extra=(), bench=BENCH):
@@ -236,7 +245,90 @@ def gaps_pass():
         lines.append(f"{tag}: {len(sel)} steps; step {m(step_us):.2f} us = append kernels "
                      f"{m(app_us):.2f} + split {m(split_us):.2f} + merge "
                      f"{m(merge_us) if merge_us else 0:.2f} + idle {m(idle_us):.2f}")
+    lines.append("idle: the GPU waiting for the host, which under --kernel-trace pays the "
+                 "tracer's work on every launch; the bench's own host_enqueue_us_max_step (no "
+                 "tracer) is the host time of the untraced command. The kernel durations are "
+                 "the figures to set against the bench line's per-decode events.")
     with open(os.path.join(PROF, "decode_gqa70b_32k_step_gaps.txt"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines), flush=True)
+
+
+def prefill_values(rows, counter):
+    """`counter` of the prefill quantize dispatches: the quantize dispatches
+    with the largest grid (the flushes of a full window have 4 groups per
+    (b, h) block, the 32K prefills 1020)."""
+    q = [r for r in rows if QUANT in short(r["Kernel_Name"]) and r["Counter_Name"] == counter]
+    assert q, f"no {QUANT} dispatch with {counter}"
+    g = max(int(r["Grid_Size"]) for r in q)
+    return [float(r["Counter_Value"]) for r in q if int(r["Grid_Size"]) == g]
+
+
+def quant_pass():
+    """Evidence for the prefill quantize kernel: what it moves and how busy
+    its units are."""
+    d, c_trace = run("qtrace", ["--kernel-trace"])
+    f = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)[0]
+    with open(f) as fh:
+        rows = [r for r in csv.DictReader(fh) if QUANT in short(r["Kernel_Name"])]
+    durs = sorted((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows)
+    pre = [x for x in durs if x > 20 * durs[0]]          # the prefills, not the flushes
+    dur_us = statistics.median(pre)
+    cmds = {"trace": rel(c_trace)}
+    vals = {}
+    for i, ctrs in enumerate(SQ_PASSES):
+        d, c = run(f"qsq{i}", ["--pmc", *ctrs, "--kernel-include-regex", "kivi_quantize_kernel"])
+        cmds[f"sq{i}"] = rel(c)
+        rows = counter_rows(d)
+        for ctr in ctrs:
+            vals[ctr] = statistics.median(prefill_values(rows, ctr))
+    traffic = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        d, c = run(f"q{ctr.lower()}", ["--pmc", ctr, "--kernel-include-regex",
+                                       "kivi_quantize_kernel|[Cc]opy"],
+                   ["--copy-probe-mib", str(COPY_MIB)])
+        cmds[ctr] = rel(c)
+        rows = counter_rows(d)
+        kib = statistics.median(prefill_values(rows, ctr))
+        scale = COPY_MIB * 1024.0 / copy_reading(per_kernel(rows, ctr))
+        traffic[ctr] = (kib, scale, kib * scale * 1024)
+    bh = PRE_B * PRE_H
+    read = 2 * bh * PRE_NQ * PRE_D * 2
+    write = bh * (2 * PRE_NQ * PRE_D * PRE_BITS // 8 + (PRE_NQ // PRE_G) * PRE_D * 8 + PRE_NQ * 8)
+    groups = bh * (PRE_NQ // PRE_G)
+    cyc = vals["GRBM_GUI_ACTIVE"] / N_XCD
+    lines = ["# prefill quantize kernel (KIVI 2-bit, G = 32) of the 32K GQA layer: "
+             "B = 16, 8 KV heads, 32640 grouped tokens per (b, h) block",
+             *[f"# command ({k}): {v}" for k, v in cmds.items()],
+             f"prefill dispatches timed: {len(pre)}; median duration {dur_us:.1f} us "
+             f"(kernel trace, no counters)",
+             f"bytes it must move: read {read / 1e6:.1f} MB (fp16 K and V), write "
+             f"{write / 1e6:.1f} MB (codes, K scale / zero per group and channel, V scale / "
+             f"zero per token); {(read + write) / 1e6:.1f} MB",
+             f"achieved: {(read + write) / (dur_us * 1e-6) / 1e9:.0f} GB/s = "
+             f"{(read + write) / (dur_us * 1e-6) / 8e12:.3f} of 8 TB/s"]
+    for ctr, (kib, scale, b) in traffic.items():
+        lines.append(f"{ctr}: {kib:.0f} KiB per prefill dispatch x copy scale {scale:.4f} = "
+                     f"{b / 1e6:.1f} MB")
+    lines.append(f"HBM traffic / bytes it must move: "
+                 f"{(traffic['FETCH_SIZE'][2] + traffic['WRITE_SIZE'][2]) / (read + write):.3f}")
+    lines += [f"{k:32s} {v:16.0f}" for k, v in vals.items()]
+    lines.append(f"groups (32 tokens of one (b, h) block) per dispatch: {groups}; "
+                 f"wavefronts: {vals['SQ_WAVES']:.0f}")
+    for k in ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD",
+              "SQ_INSTS_VALU_CVT", "SQ_INSTS_VALU_FMA_F32", "SQ_INSTS_VALU_MUL_F32",
+              "SQ_INSTS_VALU_ADD_F32"):
+        lines.append(f"{k} per group: {vals[k] / groups:8.1f}")
+    clk = cyc / (dur_us * 1e-6) / 1e9
+    lines.append(f"GRBM_GUI_ACTIVE / {N_XCD} XCDs = {cyc:.0f} cycles (counter pass, dispatches "
+                 f"serialized) -> {clk:.2f} GHz at the trace duration")
+    lines.append(f"VALU busy = 4*SQ_ACTIVE_INST_VALU / (SIMDs * GUI cycles) = "
+                 f"{4 * vals['SQ_ACTIVE_INST_VALU'] / (N_SIMD * cyc):.3f}")
+    lines.append(f"VALU issue time: 4 cycles x SQ_INSTS_VALU / SIMDs at that clock = "
+                 f"{4 * vals['SQ_INSTS_VALU'] / N_SIMD / (clk * 1e3):.1f} us of {dur_us:.1f} us")
+    lines.append(f"LDS bank conflict cycles per LDS instruction: "
+                 f"{vals['SQ_LDS_BANK_CONFLICT'] / max(1.0, vals['SQ_INSTS_LDS']):.3f}")
+    with open(os.path.join(PROF, "prefill_quantize_gqa70b_32k_counters.txt"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines), flush=True)
 
@@ -244,7 +336,7 @@ def gaps_pass():
 def main():
     os.makedirs(PROF, exist_ok=True)
     from bench import decode_source_hash
-    passes = sys.argv[1:] or ["stats", "traffic", "sq", "gaps"]
+    passes = sys.argv[1:] or ["stats", "traffic", "sq", "gaps", "quant"]
 
     if "stats" in passes:
         d1, c1 = run("stats", ["--kernel-trace", "--stats"], bench=BENCH_STATS)
@@ -255,6 +347,8 @@ def main():
         sq_pass()
     if "gaps" in passes:
         gaps_pass()
+    if "quant" in passes:
+        quant_pass()
     if "traffic" not in passes:
         return
 
