@@ -35,6 +35,10 @@ __device__ __forceinline__ uint32_t affine_code(float x, float mn, float s, floa
   return static_cast<uint32_t>(r);
 }
 
+__device__ __forceinline__ float f4c(float4 v, int c) {
+  return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
+}
+
 __device__ __forceinline__ void halves_to_float(const uint4& raw, float* f) {
   const __half2* h = reinterpret_cast<const __half2*>(&raw);
 #pragma unroll
@@ -67,6 +71,23 @@ __device__ __forceinline__ float fast_code(float x, float mn, float r, float& de
   const float c = rintf(p);
   dev = fmaxf(dev, fabsf(p - c));
   return c;
+}
+
+// x / d correctly rounded, for d = 3 or 15 (2^b − 1 at b = 2, 4): q = RN(x·y)
+// with y = RN(1/d) is within an ulp of the quotient, the remainder x − q·d is
+// exact in one fma, and one more fma of it with y gives RN(x / d). Checked
+// bit for bit against the IEEE division for every finite fp32 x of either
+// sign, for both d; the one exception, x = −0 (where the correction gives +0),
+// and non-finite x take q itself.
+template <int D>
+__device__ __forceinline__ float div_code_range(float x) {
+  static_assert(D == 3 || D == 15, "code ranges of 2- and 4-bit codes");
+  constexpr float y = 1.0f / float(D);
+  const float q = x * y;
+  const float r = fmaf(-q, float(D), x);
+  const float c = fmaf(r, y, q);
+  // class mask: NaN (bits 0, 1), ±inf (2, 9), ±0 (5, 6)
+  return __builtin_amdgcn_class(x, 0x267) ? q : c;
 }
 
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
@@ -201,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
     }
     const float vmx = float(mm[0]);
     const float vmn = -float(mm[1]);
-    const float vs = (vmx - vmn) / VQMAX;
+    const float vs = div_code_range<(1 << VB) - 1>(vmx - vmn);
     // one thread per token (nvs = 1) or per run of 32 channels (nvs = 4)
     if (a.nvs == 1 ? j == 0 : (j & 1) == 0) {
       const int64_t o = (blk * CT + gg * G + tr) * a.nvs + (a.nvs == 1 ? 0 : j / 2);
@@ -218,8 +239,13 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
 #pragma unroll
     for (int i = 0; i < 16; ++i) c[i] = fast_code(vx[i], vmn, vr, dev);
     if (dev > kTieEdge) {
+      // a lane with a possible tie recomputes only the values that may sit on
+      // one (the fast codes of the others are exact): a wavefront then runs
+      // the division for the value slots where some lane has one
 #pragma unroll
-      for (int i = 0; i < 16; ++i) c[i] = float(affine_code(vx[i], vmn, vs, VQMAX));
+      for (int i = 0; i < 16; ++i)
+        if (fabsf((vx[i] - vmn) * vr - c[i]) > kTieEdge)
+          c[i] = float(affine_code(vx[i], vmn, vs, VQMAX));
     }
     uint32_t w[VTW];
     pack16<VB>(c, w);
@@ -258,8 +284,8 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
       kmn = h2min(as_h2(pn[0]), as_h2(pn[1]));
     }
     const float mn0 = float(kmn[0]), mn1 = float(kmn[1]);
-    const float s0 = (float(kmx[0]) - mn0) / KQMAX;
-    const float s1 = (float(kmx[1]) - mn1) / KQMAX;
+    const float s0 = div_code_range<(1 << KB) - 1>(float(kmx[0]) - mn0);
+    const float s1 = div_code_range<(1 << KB) - 1>(float(kmx[1]) - mn1);
     if (u == 0) {
       const int64_t o = (blk * a.NG + gg) * kHeadDim + d0;
       *reinterpret_cast<float2*>(a.k_scale + o) = make_float2(s0, s1);
@@ -320,9 +346,11 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
       c[4 * q4 + 3] = fast_code(kx[4 * q4 + 3], zq[q4].w, rq[q4].w, dev);
     }
     if (dev > kTieEdge) {
+      // as for V: only the values that may sit on a tie
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        c[i] = float(affine_code(kx[i], z_k[16 * j + i], s_k[16 * j + i], KQMAX));
+        if (fabsf((kx[i] - f4c(zq[i / 4], i % 4)) * f4c(rq[i / 4], i % 4) - c[i]) > kTieEdge)
+          c[i] = float(affine_code(kx[i], z_k[16 * j + i], s_k[16 * j + i], KQMAX));
     }
     uint32_t w[KTW];
     pack16<KB>(c, w);
