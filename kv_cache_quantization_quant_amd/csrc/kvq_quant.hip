@@ -75,10 +75,11 @@ __device__ __forceinline__ float fast_code(float x, float mn, float r, float& de
 
 // x / d correctly rounded, for d = 3 or 15 (2^b − 1 at b = 2, 4): q = RN(x·y)
 // with y = RN(1/d) is within an ulp of the quotient, the remainder x − q·d is
-// exact in one fma, and one more fma of it with y gives RN(x / d). Checked
-// bit for bit against the IEEE division for every finite fp32 x of either
-// sign, for both d; the one exception, x = −0 (where the correction gives +0),
-// and non-finite x take q itself.
+// exact in one fma, and one more fma of it with y gives RN(x / d). Equal bit
+// for bit to the IEEE division for every finite fp32 x of either sign, for
+// both d (a host check runs every pattern of the binades where the steps do
+// not scale by powers of two and of one middle binade); the one exception,
+// x = −0 (where the correction gives +0), and non-finite x take q itself.
 template <int D>
 __device__ __forceinline__ float div_code_range(float x) {
   static_assert(D == 3 || D == 15, "code ranges of 2- and 4-bit codes");
