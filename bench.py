@@ -6,7 +6,8 @@ Workload (the 70B-style GQA layer at 32K context): B=16, 64 query heads,
 quantized once before timing; a step is one streamed decode step of one layer:
 append one token per (b, KV head) — with the lazy window flush when due, every
 128 appends — then decode attention of one query per head over the whole
-cache. The steps cycle through LAYERS independent layer caches of that shape,
+cache: one kvq_append_decode call in the pass the value is taken from, the two
+calls with events around the decode in the roofline pass. The steps cycle through LAYERS independent layer caches of that shape,
 as consecutive layers of a model do, so that no step finds its cache in the
 256 MB Infinity Cache. Inputs are seeded synthetic tensors (synth), resident
 in HBM before timing.
@@ -191,9 +192,8 @@ def run_main(torch, kq, synth, args):
     qi = 0
     for i in range(args.warmup):
         l = i % LAYERS
-        layers[l].append(k_new[pos[l]], v_new[pos[l]])
+        layers[l].append_decode(k_new[pos[l]], v_new[pos[l]], qs[qi], out=out, workspace=ws)
         pos[l] += 1
-        layers[l].decode(qs[qi], out=out, workspace=ws)
         qi += 1
     torch.cuda.synchronize()
 
@@ -218,15 +218,19 @@ def run_main(torch, kq, synth, args):
             host.append(time.perf_counter())
             l = j % LAYERS
             c = layers[l]
-            c.append(k_new[pos[l]], v_new[pos[l]])
-            pos[l] += 1
-            state.append((l, c.cache.n_quant, c.cache.n_resid))
             if ev:
+                # roofline pass: the append, then events around the decode alone
+                c.append(k_new[pos[l]], v_new[pos[l]])
                 ev[j][0].record()
-            c.decode(qs[qi], out=out, workspace=ws)
-            qi += 1
-            if ev:
+                c.decode(qs[qi], out=out, workspace=ws)
                 ev[j][1].record()
+            else:
+                # value pass: the step as one call (one launch unless a flush
+                # is due: the decode stores the new token itself)
+                c.append_decode(k_new[pos[l]], v_new[pos[l]], qs[qi], out=out, workspace=ws)
+            pos[l] += 1
+            qi += 1
+            state.append((l, c.cache.n_quant, c.cache.n_resid))
         end.record()
         wall_enqueue = time.perf_counter() - wall0
         torch.cuda.synchronize()

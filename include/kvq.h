@@ -144,7 +144,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 10
+#define KVQ_ABI_VERSION 11
 
 typedef enum {
   KVQ_OK = 0,
@@ -329,6 +329,20 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q,
                                 int32_t num_q_heads, float* out,
                                 void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/* kvq_append_token, then kvq_decode_attention, on the same stream: one
+ * streamed decode step ([Tutorial] §八.4: the new token's K/V enter the cache,
+ * then attention reads it). Every check of both calls runs first (the decode's
+ * on the fill state after the append), so on error nothing is enqueued and
+ * the cache is unchanged. A KIVI cache with no flush due (ragged: no sequence
+ * whose window is full) takes one launch: the decode stores the new token
+ * into its window slot and reads it from k_new / v_new. A flush, and every
+ * FP8 or FP16 cache, takes the append's launches, then the decode's. The
+ * results equal the two calls' (bitwise with deterministic = 1).
+ * Arguments as for the two calls; errors as theirs. */
+kvq_status kvq_append_decode(kvq_cache* cache, const void* k_new, const void* v_new,
+                             const float* q, int32_t num_q_heads, float* out,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* One decode over the attention layers of a model, layer by layer in index
  * order, for callers that hold every layer's query at once. Each layer keeps

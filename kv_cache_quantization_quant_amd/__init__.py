@@ -28,7 +28,7 @@ KVQ_ERR_STATE = 4
 KVQ_ERR_DEVICE = 5
 KVQ_ERR_WORKSPACE = 6
 
-ABI_VERSION = 10       # KVQ_ABI_VERSION of include/kvq.h
+ABI_VERSION = 11       # KVQ_ABI_VERSION of include/kvq.h
 STATIC_WORKSPACE_BYTES = 32 << 20   # KVQ_STATIC_WORKSPACE_BYTES
 
 KVQ_FMT_FP16 = 0
@@ -97,6 +97,8 @@ def _load():
                                            c_void_p, c_size_t, c_void_p]),
         "kvq_decode_attention_static": (c_int32, [POINTER(KvqCache), c_void_p, c_int32,
                                                   c_void_p, c_void_p]),
+        "kvq_append_decode": (c_int32, [POINTER(KvqCache), c_void_p, c_void_p, c_void_p, c_int32,
+                                        c_void_p, c_void_p, c_size_t, c_void_p]),
         "kvq_decode_attention_layers": (c_int32, [POINTER(POINTER(KvqCache)), c_int32,
                                                   c_void_p, c_int32, c_void_p, c_void_p,
                                                   c_size_t, c_void_p]),
@@ -127,7 +129,7 @@ ABI_SYMBOLS = ("kvq_abi_version", "kvq_status_str", "kvq_layout_query", "kvq_cac
                "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_bytes",
                "kvq_quantize_query_fp8", "kvq_theoretical_bytes",
                "kvq_decode_attention_layers", "kvq_theoretical_bytes_layers",
-               "kvq_decode_attention_static")
+               "kvq_decode_attention_static", "kvq_append_decode")
 
 
 # ------------------------------------------------- one-to-one ABI wrappers ---
@@ -176,6 +178,12 @@ def kvq_decode_attention(cache: KvqCache, q_ptr: int, num_q_heads: int, out_ptr:
                          ws_ptr: int, ws_bytes: int, stream: int | None) -> int:
     return lib.kvq_decode_attention(byref(cache), q_ptr, num_q_heads, out_ptr, ws_ptr,
                                     ws_bytes, stream)
+
+
+def kvq_append_decode(cache: KvqCache, k_ptr: int, v_ptr: int, q_ptr: int, num_q_heads: int,
+                      out_ptr: int, ws_ptr: int, ws_bytes: int, stream: int | None) -> int:
+    return lib.kvq_append_decode(byref(cache), k_ptr, v_ptr, q_ptr, num_q_heads, out_ptr, ws_ptr,
+                                 ws_bytes, stream)
 
 
 def kvq_decode_attention_static(cache: KvqCache, q_ptr: int, num_q_heads: int, out_ptr: int,
@@ -461,6 +469,31 @@ class DeviceCache:
         _check(kvq_decode_attention(self.cache, q.data_ptr(), hq, out.data_ptr(),
                                     workspace.data_ptr(), workspace.numel(),
                                     _stream_handle(stream)), "kvq_decode_attention")
+        return out
+
+    def append_decode(self, k1: torch.Tensor, v1: torch.Tensor, q: torch.Tensor,
+                      out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor:
+        """kvq_append_decode: append(k1, v1) then decode(q) as one call.
+        k1, v1: contiguous fp16 [B, H, D]; q: contiguous fp32 [B, Hq, D]."""
+        c = self.cfg
+        kv_shape = (c.batch, c.num_kv_heads, c.head_dim)
+        _require(k1, "k1", torch.float16, kv_shape, self.device)
+        _require(v1, "v1", torch.float16, kv_shape, self.device)
+        if q.dim() != 3:
+            raise ValueError(f"q: shape {tuple(q.shape)}, expected [B, Hq, D]")
+        hq = q.shape[1]
+        shape = (c.batch, hq, c.head_dim)
+        _require(q, "q", torch.float32, shape, self.device)
+        if out is None:
+            out = torch.empty_like(q)
+        _require(out, "out", torch.float32, shape, self.device)
+        if workspace is None:
+            workspace = self.make_workspace(hq)
+        _require(workspace, "workspace", torch.uint8, (workspace.numel(),), self.device)
+        _check(kvq_append_decode(self.cache, k1.data_ptr(), v1.data_ptr(), q.data_ptr(), hq,
+                                 out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                 _stream_handle(stream)), "kvq_append_decode")
         return out
 
     def decode_static(self, q: torch.Tensor, out: torch.Tensor, stream=None) -> torch.Tensor:

@@ -656,8 +656,8 @@ kvq_status append_ragged(kvq_cache* cache, const Dims& d, const __half* kh, cons
 
 }  // namespace
 
-kvq_status kvq_append_token(kvq_cache* cache, const void* k_new, const void* v_new,
-                            void* stream) {
+// Every check of kvq_append_token, before anything is enqueued.
+static kvq_status append_check(const kvq_cache* cache, const void* k_new, const void* v_new) {
   if (cache == nullptr || k_new == nullptr || v_new == nullptr) return KVQ_ERR_INVALID_ARG;
   if (!aligned16(k_new) || !aligned16(v_new)) return KVQ_ERR_INVALID_ARG;
   const kvq_status vs = validate_config(&cache->cfg);
@@ -665,6 +665,21 @@ kvq_status kvq_append_token(kvq_cache* cache, const void* k_new, const void* v_n
   if (!buffers_set(cache)) return KVQ_ERR_INVALID_ARG;
   const Dims d = dims_of(cache->cfg);
   if (!state_ok(cache, d)) return KVQ_ERR_STATE;
+  if (is_ragged(cache)) {
+    for (int64_t b = 0; b < d.B; ++b)
+      if (cache->seq_n_quant[b] + cache->seq_n_resid[b] >= d.C) return KVQ_ERR_CAPACITY;
+    return KVQ_OK;
+  }
+  if (cache->n_quant + cache->n_resid >= d.C) return KVQ_ERR_CAPACITY;
+  if (is_fp8(cache->cfg.format) && cache->n_quant == 0) return KVQ_ERR_STATE;
+  return KVQ_OK;
+}
+
+kvq_status kvq_append_token(kvq_cache* cache, const void* k_new, const void* v_new,
+                            void* stream) {
+  const kvq_status st = append_check(cache, k_new, v_new);
+  if (st != KVQ_OK) return st;
+  const Dims d = dims_of(cache->cfg);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int bh = int(d.B * d.H);
   const __half* kh = static_cast<const __half*>(k_new);
@@ -806,7 +821,8 @@ static kvq_status decode_check(const kvq_cache* cache, const float* q, int32_t n
 // WORKSPACE when the plan's partials do not fit in workspace_bytes.
 static kvq_status decode_enqueue(const kvq_cache* cache, const float* q, int32_t num_q_heads,
                                  float* out, void* workspace, size_t workspace_bytes,
-                                 void* stream, bool dry) {
+                                 void* stream, bool dry, const __half* k_new = nullptr,
+                                 const __half* v_new = nullptr) {
   const bool ragged = is_ragged(cache);
 
   const Dims d = dims_of(cache->cfg);
@@ -891,6 +907,12 @@ static kvq_status decode_enqueue(const kvq_cache* cache, const float* q, int32_t
       a.seq.y[b] = cache->seq_n_resid[b];
     }
   }
+  if (k_new != nullptr) {   // the token just appended, stored by this launch
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_win_store = static_cast<__half*>(cache->k_resid);
+    a.v_win_store = static_cast<__half*>(cache->v_resid);
+  }
   a.q = q;
   a.out = out;
   a.ws = static_cast<float*>(workspace);
@@ -906,6 +928,59 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const float* q, int32_t 
   const kvq_status st = decode_check(cache, q, num_q_heads, out, workspace, workspace_bytes);
   if (st != KVQ_OK) return st;
   return decode_enqueue(cache, q, num_q_heads, out, workspace, workspace_bytes, stream, false);
+}
+
+kvq_status kvq_append_decode(kvq_cache* cache, const void* k_new, const void* v_new,
+                             const float* q, int32_t num_q_heads, float* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  kvq_status st = append_check(cache, k_new, v_new);
+  if (st != KVQ_OK) return st;
+  // the fill state after the append, on a copy (a ragged cache's levels in
+  // local arrays): the decode is checked and planned on it before anything
+  // is enqueued
+  const Dims d = dims_of(cache->cfg);
+  const bool ragged = is_ragged(cache);
+  const bool kivi = cache->cfg.format == KVQ_FMT_KIVI;
+  kvq_cache after = *cache;
+  int64_t nq_after[kvq::kMaxRagged];
+  int32_t nr_after[kvq::kMaxRagged];
+  bool flush = false;
+  if (ragged) {
+    for (int64_t b = 0; b < d.B; ++b) {
+      const bool full = cache->seq_n_resid[b] == d.Rcap;
+      flush = flush || full;
+      nq_after[b] = cache->seq_n_quant[b] + (full ? d.Rcap : 0);
+      nr_after[b] = (full ? 0 : cache->seq_n_resid[b]) + 1;
+    }
+    after.seq_n_quant = nq_after;
+    after.seq_n_resid = nr_after;
+  } else if (kivi) {
+    flush = cache->n_resid == d.Rcap;
+    after.n_quant = cache->n_quant + (flush ? d.Rcap : 0);
+    after.n_resid = (flush ? 0 : cache->n_resid) + 1;
+  } else {
+    after.n_quant = cache->n_quant + 1;
+  }
+  st = decode_check(&after, q, num_q_heads, out, workspace, workspace_bytes);
+  if (st != KVQ_OK) return st;
+  st = decode_enqueue(&after, q, num_q_heads, out, workspace, workspace_bytes, stream, true,
+                      nullptr, nullptr);
+  if (st != KVQ_OK) return st;
+  if (!kivi || flush) {
+    // a flush (or an FP8 / FP16 append) goes first in launches of its own
+    st = kvq_append_token(cache, k_new, v_new, stream);
+    if (st != KVQ_OK) return st;
+    return decode_enqueue(cache, q, num_q_heads, out, workspace, workspace_bytes, stream, false,
+                          nullptr, nullptr);
+  }
+  // one launch: the decode stores the token into its window slot itself
+  if (ragged) {
+    for (int64_t b = 0; b < d.B; ++b) cache->seq_n_resid[b] += 1;
+  } else {
+    cache->n_resid += 1;
+  }
+  return decode_enqueue(cache, q, num_q_heads, out, workspace, workspace_bytes, stream, false,
+                        static_cast<const __half*>(k_new), static_cast<const __half*>(v_new));
 }
 
 kvq_status kvq_decode_attention_static(const kvq_cache* cache, const float* q,

@@ -667,11 +667,19 @@ __device__ __forceinline__ void process_window_tile(const DecodeArgs& a, WaveAcc
   const __half* kw = a.k_win + (int64_t(bh) * a.win_cap + tile * kGroup) * kHeadDim;
   const __half* vwp = a.v_win + (int64_t(bh) * a.win_cap + tile * kGroup) * kHeadDim;
   const int n_in = int(min<int64_t>(kGroup, n_win - tile * kGroup));
+  // a folded append: the newest token (slot n_win − 1) comes from the
+  // caller's buffer, not from the window it is being stored into
+  const bool here = a.k_new != nullptr && n_win - tile * kGroup <= kGroup;
+  const int t_new = here ? n_in - 1 : -1;                  // its slot in this tile
+  const __half* k_new = here ? a.k_new + int64_t(bh) * kHeadDim : kw;
+  const __half* v_new = here ? a.v_new + int64_t(bh) * kHeadDim : vwp;
+  const __half* k_row0 = r == t_new ? k_new : kw + r * kHeadDim;
+  const __half* k_row1 = 16 + r == t_new ? k_new : kw + (16 + r) * kHeadDim;
   f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
   for (int sl = 0; sl < 4; ++sl) {
-    const uint4 k0 = *reinterpret_cast<const uint4*>(kw + r * kHeadDim + 32 * sl + 8 * u);
-    const uint4 k1 = *reinterpret_cast<const uint4*>(kw + (16 + r) * kHeadDim + 32 * sl + 8 * u);
+    const uint4 k0 = *reinterpret_cast<const uint4*>(k_row0 + 32 * sl + 8 * u);
+    const uint4 k1 = *reinterpret_cast<const uint4*>(k_row1 + 32 * sl + 8 * u);
     s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(u32x4{k0.x, k0.y, k0.z, k0.w}),
                                                 as_f16x8(bqw[sl]), s0, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(u32x4{k1.x, k1.y, k1.z, k1.w}),
@@ -711,7 +719,7 @@ __device__ __forceinline__ void process_window_tile(const DecodeArgs& a, WaveAcc
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int t = (j < 4) ? 4 * u + j : 16 + 4 * u + (j - 4);
-          vh[m][j] = vwp[t * kHeadDim + 16 * (n + m) + r];
+          vh[m][j] = (t == t_new ? v_new : vwp + t * kHeadDim)[16 * (n + m) + r];
         }
       }
     }
@@ -764,6 +772,19 @@ __device__ __forceinline__ void run_window(const DecodeArgs& a, WaveAccT<NVS>& W
     }
   }
   const int64_t n_tiles = (n_win + kGroup - 1) / kGroup;
+  // a folded append: wavefront 0 of head chunk 0 stores the appended token
+  // into its window slot (16 lanes for K, 16 for V, 16 bytes each); no
+  // wavefront of this launch reads that slot from the window
+  if (a.k_new != nullptr && wave == 0 && hq0 % a.nq == 0 && n_win > 0) {
+    const int lane = u * 16 + r;
+    if (lane < 32) {
+      const int c = lane & 15;
+      const __half* src = (lane < 16 ? a.k_new : a.v_new) + int64_t(bh) * kHeadDim + 8 * c;
+      __half* dst = (lane < 16 ? a.k_win_store : a.v_win_store) +
+                    (int64_t(bh) * a.win_cap + n_win - 1) * kHeadDim + 8 * c;
+      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+    }
+  }
   for (int64_t tile = wave; tile < n_tiles; tile += NW)
     process_window_tile(a, W, bh, tile, bqw, r, u, low, n_win);
 }

@@ -177,6 +177,14 @@ struct DecodeArgs {
                           // split (deterministic); 0 = tiles from a shared counter
   int unit;               // KIVI: 1 = one workgroup per compute unit (tiles shared
                           // unless fixed_order), 0 = four-wavefront workgroups
+  // an append folded into the decode (KIVI, no flush due): the appended token
+  // (fp16 [B·H][D]) is window slot n_win − 1 (ragged: seq.y[b] − 1); the
+  // workgroups that run the window read it from here, and those of head
+  // chunk 0 store it into the window buffers (null k_new: no append)
+  const __half* k_new;
+  const __half* v_new;
+  __half* k_win_store;
+  __half* v_win_store;
   const float* q;         // [B][Hq][D]
   float* out;             // [B][Hq][D]
   float* ws;              // [B][Hq][n_split][D + 2]

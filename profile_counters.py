@@ -202,11 +202,11 @@ def sq_pass():
 
 def gaps_pass():
     """Kernel durations and idle gaps of the timed steps of the short bench
-    run. A step is an append (its copy kernel, after the flush's quantize
-    kernel when one is due) followed by the decode's split and merge kernels;
-    the bench runs 5 warm-up steps, then the 20 steps its value is taken
-    from, then the same 20 steps with events around each decode (its
-    roofline pass)."""
+    run. The bench runs 5 warm-up steps, then the 20 steps its value is
+    taken from (one kvq_append_decode call each: the split and merge
+    launches, after the flush's quantize launch when one is due), then the
+    same 20 steps as an append's copy launch followed by the decode, with
+    events around each decode (its roofline pass)."""
     d, c = run("gaps", ["--kernel-trace"], bench=BENCH_DRIVER)
     f = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)[0]
     with open(f) as fh:
@@ -215,19 +215,23 @@ def gaps_pass():
     names = [short(r["Kernel_Name"]) for r in rows]
     t0 = [int(r["Start_Timestamp"]) for r in rows]
     t1 = [int(r["End_Timestamp"]) for r in rows]
-    splits = [i for i in range(1, len(rows))
-              if DECODE in names[i] and "copy_tokens_kernel" in names[i - 1]]
+    splits = [i for i in range(1, len(rows)) if DECODE in names[i]]
+    # the roofline pass: the 20 splits right after an append's copy launch
+    roof = [i for i in splits if "copy_tokens_kernel" in names[i - 1]][-20:]
+    # the value pass: the 20 splits before the roofline pass's first step
+    value = [i for i in splits if i < roof[0] - 1][-20:]
     lines = ["# rocprofv3 kernel trace of the round-end benchmark command: per timed step, "
-             "the append's kernels, the decode's split and merge, and the idle time on the "
-             "GPU between them", f"# command: {rel(c)}"]
-    summary = {}
+             "the append's kernels (none in a fused step without a flush), the decode's "
+             "split and merge, and the idle time on the GPU between them",
+             f"# command: {rel(c)}"]
     # the first step of each pass follows a host synchronization: left out
-    for tag, sel in (("value pass (region events only)", splits[6:25]),
-                     ("roofline pass (events around each decode)", splits[26:45])):
+    for tag, sel in (("value pass (kvq_append_decode, region events only)", value[1:]),
+                     ("roofline pass (append, then events around each decode)", roof[1:])):
         step_us, idle_us, split_us, merge_us, app_us = [], [], [], [], []
         for i in sel:
-            first = i - 1
-            if first > 0 and "kivi_quantize_kernel" in names[first - 1]:
+            first = i
+            while first > 0 and ("copy_tokens_kernel" in names[first - 1] or
+                                 "kivi_quantize_kernel" in names[first - 1]):
                 first -= 1
             last = i + 1 if i + 1 < len(rows) and MERGE in names[i + 1] else i
             busy = sum(t1[k] - t0[k] for k in range(first, last + 1))
@@ -240,8 +244,6 @@ def gaps_pass():
                 merge_us.append((t1[last] - t0[last]) / 1e3)
             app_us.append(sum(t1[k] - t0[k] for k in range(first, i)) / 1e3)
         m = statistics.mean
-        summary[tag] = (m(step_us), m(idle_us), m(split_us), m(merge_us) if merge_us else 0.0,
-                        m(app_us), len(sel))
         lines.append(f"{tag}: {len(sel)} steps; step {m(step_us):.2f} us = append kernels "
                      f"{m(app_us):.2f} + split {m(split_us):.2f} + merge "
                      f"{m(merge_us) if merge_us else 0:.2f} + idle {m(idle_us):.2f}")

@@ -80,8 +80,18 @@ static void uniform_kivi(int bits, int G, int R, int B, int H, int hq, int S, in
   const int64_t rcap = R > 0 ? R : G;
   CHECK(c.n_quant == nq && c.n_resid == nr);
   CHECK(decode_ok(&c, hq));
+  const size_t ws = kvq_decode_workspace_bytes(&c.cfg, hq);
+  /* the fused step with a short workspace is refused before it appends */
+  CHECK(kvq_append_decode(&c, P(32), P(33), (const float*)P(20), hq, (float*)P(21), P(22), 64,
+                          NULL) == KVQ_ERR_WORKSPACE);
+  CHECK(c.n_quant == nq && c.n_resid == nr);
   for (int i = 0; i < steps; ++i) {
-    CHECK(kvq_append_token(&c, P(32), P(33), NULL) == KVQ_OK);
+    /* odd steps: append and decode in one call */
+    if (i % 2)
+      CHECK(kvq_append_decode(&c, P(32), P(33), (const float*)P(20), hq, (float*)P(21), P(22), ws,
+                              NULL) == KVQ_OK);
+    else
+      CHECK(kvq_append_token(&c, P(32), P(33), NULL) == KVQ_OK);
     if (nr == rcap) {
       nq += rcap;
       nr = 0;
@@ -92,6 +102,8 @@ static void uniform_kivi(int bits, int G, int R, int B, int H, int hq, int S, in
   }
   /* full: one more append is refused and changes nothing */
   CHECK(kvq_append_token(&c, P(32), P(33), NULL) == KVQ_ERR_CAPACITY);
+  CHECK(kvq_append_decode(&c, P(32), P(33), (const float*)P(20), hq, (float*)P(21), P(22), ws,
+                          NULL) == KVQ_ERR_CAPACITY);
   CHECK(c.n_quant == nq && c.n_resid == nr);
   /* the allocation-free decode plans the same call */
   CHECK(kvq_decode_attention_static(&c, (const float*)P(20), hq, (float*)P(21), NULL) == KVQ_OK);
@@ -141,7 +153,11 @@ static void ragged_kivi(int paged, int B, int H, int hq, int steps) {
       want_q[b] = nq[b] + (nr[b] == R ? R : 0);
       want_r[b] = (nr[b] == R ? 0 : nr[b]) + 1;
     }
-    CHECK(kvq_append_token(&c, P(32), P(33), NULL) == KVQ_OK);
+    if (i % 3 == 1)
+      CHECK(kvq_append_decode(&c, P(32), P(33), (const float*)P(20), hq, (float*)P(21), P(22),
+                              kvq_decode_workspace_bytes(&c.cfg, hq), NULL) == KVQ_OK);
+    else
+      CHECK(kvq_append_token(&c, P(32), P(33), NULL) == KVQ_OK);
     for (int b = 0; b < B; ++b) CHECK(nq[b] == want_q[b] && nr[b] == want_r[b]);
     if (i % 29 == 0) CHECK(decode_ok(&c, hq));
   }
@@ -164,7 +180,11 @@ static void dense(int fmt, int B, int H, int hq, int S, int steps, int per_head,
   CHECK(kvq_prefill_quantize(&c, P(30), P(31), S, NULL) == KVQ_OK);
   CHECK(c.n_quant == S && c.n_resid == 0);
   for (int i = 0; i < steps; ++i) {
-    CHECK(kvq_append_token(&c, P(32), P(33), NULL) == KVQ_OK);
+    if (i % 2)
+      CHECK(kvq_append_decode(&c, P(32), P(33), (const float*)P(20), hq, (float*)P(21), P(22),
+                              kvq_decode_workspace_bytes(&c.cfg, hq), NULL) == KVQ_OK);
+    else
+      CHECK(kvq_append_token(&c, P(32), P(33), NULL) == KVQ_OK);
     CHECK(c.n_quant == S + i + 1);
     if (i % 7 == 0) CHECK(decode_ok(&c, hq));
   }

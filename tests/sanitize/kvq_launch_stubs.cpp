@@ -130,6 +130,18 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t) {
           "decode: split counts");
   require(a.win_split >= -1 && a.win_split < a.n_split, "decode: window split");
   require(a.n_split == 1 || a.ws != nullptr, "decode: workspace");
+  if (a.k_new != nullptr) {
+    // a folded append: KIVI, its token in window slot n_win - 1 of each block
+    require(a.src == kSrcKivi2 || a.src == kSrcKivi4, "decode: folded append format");
+    require(a.v_new != nullptr && a.k_win_store != nullptr && a.v_win_store != nullptr,
+            "decode: folded append buffers");
+    if (a.ragged) {
+      for (int b = 0; b < a.B; ++b)
+        require(a.seq.y[b] >= 1 && a.seq.y[b] <= a.win_cap, "decode: folded append slot");
+    } else {
+      require(a.n_win >= 1 && a.n_win <= a.win_cap, "decode: folded append slot");
+    }
+  }
   const int64_t per_block = a.paged ? int64_t(a.max_pages) * a.main_bh_tokens : a.main_bh_tokens;
   if (a.paged)
     require(a.main_bh_tokens == (int64_t(32) << a.page_tile_shift) && a.num_pages >= 1 &&

@@ -60,7 +60,7 @@ def test_struct_sizes_match_header(tmp_path):
         assert int(got[st]) == ctypes.sizeof(cls), st
         for f in fields[st]:
             assert int(got[f"{st}.{f}"]) == getattr(cls, f).offset, (st, f)
-    assert int(got["abi"]) == kq.kvq_abi_version() == kq.ABI_VERSION == 10
+    assert int(got["abi"]) == kq.kvq_abi_version() == kq.ABI_VERSION == 11
 
 
 def test_status_strings():
