@@ -167,6 +167,8 @@ def sq_pass():
         for ctr in ctrs:
             v = pick(per_kernel(rows, ctr), DECODE)
             vals[ctr] = statistics.median(v)
+        if i == 0:   # the pass that counts GRBM_GUI_ACTIVE: its own dispatch time
+            ctr_us = dispatch_us(rows, DECODE)
     tiles = 16 * 8 * 1024
     waves = vals["SQ_WAVES"]
     dur_us = split_stats_avg_us()
@@ -180,19 +182,20 @@ def sq_pass():
               "SQ_INSTS_SMEM", "SQ_INSTS_VALU_CVT", "SQ_INSTS_VALU_INT32", "SQ_INSTS_VALU_FMA_F32",
               "SQ_INSTS_VALU_MUL_F32", "SQ_INSTS_VALU_ADD_F32", "SQ_INSTS_VALU_TRANS_F32"):
         lines.append(f"{k} per group: {per(k):8.1f}")
+    cyc = vals["GRBM_GUI_ACTIVE"] / N_XCD
+    clk = cyc / (ctr_us * 1e-6) / 1e9
     if dur_us:
-        cyc = vals["GRBM_GUI_ACTIVE"] / N_XCD
-        clk = cyc / (dur_us * 1e-6) / 1e9
-        lines.append(f"split kernel average duration (stats pass): {dur_us:.2f} us; "
-                     f"GRBM_GUI_ACTIVE / {N_XCD} XCDs = {cyc:.0f} cycles -> shader clock "
-                     f"{clk:.2f} GHz")
-        # SQ_ACTIVE_INST_VALU counts quad-cycles per wave; one VALU issue per SIMD per cycle
-        lines.append(f"VALU busy = 4*SQ_ACTIVE_INST_VALU / (SIMDs * GUI cycles) = "
-                     f"{4 * vals['SQ_ACTIVE_INST_VALU'] / (N_SIMD * cyc):.3f}")
-        lines.append(f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs * GUI cycles) = "
-                     f"{vals['SQ_VALU_MFMA_BUSY_CYCLES'] / (N_SIMD * cyc):.3f}")
-        lines.append(f"VALU issue time at that clock: 4 cycles x SQ_INSTS_VALU / SIMDs = "
-                     f"{4 * vals['SQ_INSTS_VALU'] / N_SIMD / (clk * 1e3):.1f} us")
+        lines.append(f"split kernel average duration (stats pass): {dur_us:.2f} us")
+    lines.append(f"split kernel in the counter pass: {ctr_us:.2f} us (median), "
+                 f"GRBM_GUI_ACTIVE / {N_XCD} XCDs = {cyc:.0f} cycles -> shader clock "
+                 f"{clk:.2f} GHz")
+    # SQ_ACTIVE_INST_VALU counts quad-cycles per wave; one VALU issue per SIMD per cycle
+    lines.append(f"VALU busy = 4*SQ_ACTIVE_INST_VALU / (SIMDs * GUI cycles) = "
+                 f"{4 * vals['SQ_ACTIVE_INST_VALU'] / (N_SIMD * cyc):.3f}")
+    lines.append(f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs * GUI cycles) = "
+                 f"{vals['SQ_VALU_MFMA_BUSY_CYCLES'] / (N_SIMD * cyc):.3f}")
+    lines.append(f"VALU issue time at that clock: 4 cycles x SQ_INSTS_VALU / SIMDs = "
+                 f"{4 * vals['SQ_INSTS_VALU'] / N_SIMD / (clk * 1e3):.1f} us of {ctr_us:.1f} us")
     lines.append(f"LDS bank conflict cycles per LDS instruction: "
                  f"{vals['SQ_LDS_BANK_CONFLICT'] / max(1.0, vals['SQ_INSTS_LDS']):.3f}")
     with open(os.path.join(PROF, "decode_gqa70b_32k_sq_counters.txt"), "w") as fh:
@@ -256,6 +259,17 @@ def gaps_pass():
     print("\n".join(lines), flush=True)
 
 
+def dispatch_us(rows, needle, grid=None):
+    """Median duration (us) of the counted dispatches of a kernel, from the
+    counter pass's own timestamps (one row per counter: deduplicated by
+    dispatch); `grid`: only dispatches of that grid size."""
+    seen = {}
+    for r in rows:
+        if needle in short(r["Kernel_Name"]) and (grid is None or int(r["Grid_Size"]) == grid):
+            seen[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    return statistics.median(seen.values())
+
+
 def prefill_values(rows, counter):
     """`counter` of the prefill quantize dispatches: the quantize dispatches
     with the largest grid (the flushes of a full window have 4 groups per
@@ -284,6 +298,9 @@ def quant_pass():
         rows = counter_rows(d)
         for ctr in ctrs:
             vals[ctr] = statistics.median(prefill_values(rows, ctr))
+        if i == 0:   # the pass that counts GRBM_GUI_ACTIVE: its own dispatch time
+            g = max(int(r["Grid_Size"]) for r in rows if QUANT in short(r["Kernel_Name"]))
+            ctr_us = dispatch_us(rows, QUANT, g)
     traffic = {}
     for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
         d, c = run(f"q{ctr.lower()}", ["--pmc", ctr, "--kernel-include-regex",
@@ -321,13 +338,13 @@ def quant_pass():
               "SQ_INSTS_VALU_CVT", "SQ_INSTS_VALU_FMA_F32", "SQ_INSTS_VALU_MUL_F32",
               "SQ_INSTS_VALU_ADD_F32"):
         lines.append(f"{k} per group: {vals[k] / groups:8.1f}")
-    clk = cyc / (dur_us * 1e-6) / 1e9
-    lines.append(f"GRBM_GUI_ACTIVE / {N_XCD} XCDs = {cyc:.0f} cycles (counter pass, dispatches "
-                 f"serialized) -> {clk:.2f} GHz at the trace duration")
+    clk = cyc / (ctr_us * 1e-6) / 1e9
+    lines.append(f"GRBM_GUI_ACTIVE / {N_XCD} XCDs = {cyc:.0f} cycles over the counter pass's "
+                 f"own dispatch time {ctr_us:.1f} us (dispatches serialized) -> {clk:.2f} GHz")
     lines.append(f"VALU busy = 4*SQ_ACTIVE_INST_VALU / (SIMDs * GUI cycles) = "
                  f"{4 * vals['SQ_ACTIVE_INST_VALU'] / (N_SIMD * cyc):.3f}")
     lines.append(f"VALU issue time: 4 cycles x SQ_INSTS_VALU / SIMDs at that clock = "
-                 f"{4 * vals['SQ_INSTS_VALU'] / N_SIMD / (clk * 1e3):.1f} us of {dur_us:.1f} us")
+                 f"{4 * vals['SQ_INSTS_VALU'] / N_SIMD / (clk * 1e3):.1f} us of {ctr_us:.1f} us")
     lines.append(f"LDS bank conflict cycles per LDS instruction: "
                  f"{vals['SQ_LDS_BANK_CONFLICT'] / max(1.0, vals['SQ_INSTS_LDS']):.3f}")
     with open(os.path.join(PROF, "prefill_quantize_gqa70b_32k_counters.txt"), "w") as fh:
