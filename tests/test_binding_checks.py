@@ -17,7 +17,7 @@ def no_calls(monkeypatch):
         raise AssertionError("a C entry point was reached")
     for name in ("kvq_prefill_quantize", "kvq_prefill_quantize_ragged", "kvq_append_token",
                  "kvq_decode_attention", "kvq_decode_attention_layers",
-                 "kvq_quantize_query_fp8"):
+                 "kvq_quantize_query_fp8", "kvq_append_decode", "kvq_decode_attention_static"):
         monkeypatch.setattr(kq, name, boom)
 
 
@@ -102,6 +102,27 @@ def test_decode_out_and_workspace_checks(no_calls):
             dc.decode(ok, out=out, workspace=_t((1 << 20,), torch.uint8))
     with pytest.raises(ValueError):
         dc.decode(ok, out=ok, workspace=_t((1 << 18,), torch.float32))
+
+
+def test_append_decode_checks(no_calls):
+    """kvq_append_decode takes every check of the append and of the decode."""
+    dc = _cache()
+    kv_ok = (B, H, D)
+    q_ok = _t((B, HQ, D), torch.float32)
+    ws = _t((1 << 20,), torch.uint8)
+    for kv_shape, kv_dtype in (((B, H, D), torch.float32), ((B, H + 1, D), torch.float16),
+                               ((B * H, D), torch.float16), (kv_ok, torch.float16)):
+        with pytest.raises(ValueError):
+            dc.append_decode(_t(kv_shape, kv_dtype), _t(kv_shape, kv_dtype), q_ok, out=q_ok,
+                             workspace=ws)
+    for q in (_t((B, HQ, D), torch.float16), _t((B + 1, HQ, D), torch.float32),
+              _t((B, HQ), torch.float32), q_ok):
+        with pytest.raises(ValueError):
+            dc.append_decode(_t(kv_ok, torch.float16), _t(kv_ok, torch.float16), q, out=q_ok,
+                             workspace=ws)
+    with pytest.raises(ValueError):
+        dc.append_decode(_t(kv_ok, torch.float16), _t(kv_ok, torch.float16), q_ok,
+                         out=_t((B, HQ, D - 1), torch.float32), workspace=ws)
 
 
 def test_decode_layers_checks(no_calls):
