@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libkvq.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["kvq_api.cpp", "kvq_quant.hip", "kvq_decode.hip", "kvq_decode_mfma.hip"]
+SOURCES = ["kvq_api.cpp", "kvq_quant.hip", "kvq_quant_kivi.hip", "kvq_decode.hip",
+           "kvq_decode_mfma.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 
@@ -56,7 +57,12 @@ def _scratch_kernels(remarks: str) -> list[str]:
 # taken by one lane per wavefront: the atomic optimizer's wave-wide
 # reduction around them (lane counts, prefix, broadcast) is pure overhead in
 # the steady-state loop.
-EXTRA = {"kvq_decode_mfma.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+EXTRA = {
+    "kvq_decode_mfma.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
+    # IEEE mode off for the KIVI quantizer: its fp16 min / max need no quieting
+    # of every loaded value first (the flag requires relaxed NaN handling)
+    "kvq_quant_kivi.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"],
+}
 
 
 def _compile(src: str) -> str:
