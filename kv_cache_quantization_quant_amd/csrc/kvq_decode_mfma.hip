@@ -90,7 +90,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+__device__ __forceinline__ f16x4 as_f16x4(u32x2 v) { return __builtin_bit_cast(f16x4, v); }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // LDS stage of one 32-token tile (byte offsets), K codes at KB bits, V
@@ -472,10 +475,23 @@ __device__ __forceinline__ void group_scores(const KLoad<BITS, NVS>& K, bool low
     zp[j] = fmaf(q16[4 * j + 3], z.w, fmaf(q16[4 * j + 2], z.z,
                  fmaf(q16[4 * j + 1], z.y, q16[4 * j] * z.x)));
   }
-  // part 0 also carries −m_ref (m_part), so that the scores come out relative
-  // to the reference maximum
-  const float zt = sum_x16_x32((zp[0] + zp[1]) + (zp[2] + zp[3])) - m_part;
-  f32x4 s0 = f32x4{zt, zt, zt, zt}, s1 = s0;
+  // The z-term summed over the four lane groups by the matrix cores (one
+  // 16×16×16 product instead of two lane swaps and the accumulator fills):
+  // B holds the lane's partial, less −m_ref once per head (lane group 0 of
+  // part 0, the m_part the caller passes there), times 2^-8, as an fp16
+  // high/low pair in k-slots 0 and 1 (slots 2 and 3 zero); A is 256 in every
+  // slot. Each column's sum over the lane groups then lands in every row of
+  // that column, the accumulator the scores build on. The 2^-8 (undone
+  // exactly by A) keeps partials up to 2^24 inside fp16's range; the pair
+  // carries 22 significant bits, and fp16's subnormal step adds at most
+  // 2^-16 per partial (2^-13 over the 8 partials of a score, in log2 units).
+  const float zs = (((zp[0] + zp[1]) + (zp[2] + zp[3])) - m_part) * 0.00390625f;
+  const float zr = zs - __uint_as_float(__float_as_uint(zs) & 0xFFFFE000u);
+  const u32x2 bz = u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(zs, zr)), 0u};
+  const u32x2 a256 = u32x2{0x5C005C00u, 0x5C005C00u};
+  f32x4 s0 = __builtin_amdgcn_mfma_f32_16x16x16f16(as_f16x4(a256), as_f16x4(bz),
+                                                   f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  f32x4 s1 = s0;
   // ---- scores: local k-step h is global k-step h (part 0) or 2 + h (part 1)
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -1176,6 +1192,13 @@ __attribute__((amdgpu_waves_per_eu((kivi_waves_per_simd<BITS, VB, NVS>())))) voi
         }
       }
     };
+    // −m_ref enters each head's scores once: from every lane of part 0 when
+    // the z-term is broadcast from one lane-group sum (G > 32), from lane
+    // group 0 of part 0 when the matrix cores add the lane groups' partials
+    auto m_part_of = [&](float m_ref) -> float {
+      if constexpr (GRP) return low ? 0.0f : m_ref;
+      return (low || u != 0) ? 0.0f : m_ref;
+    };
     auto scores = [&](const KLoad<BITS, NVS>& K, float m_part, float (&sc_out)[4]) {
       if constexpr (GRP) tile_scores<BITS, NVS>(K, low, Qg, m_part, sc_out);
       else group_scores<BITS, NVS>(K, low, q16, m_part, sc_out);
@@ -1245,7 +1268,7 @@ __attribute__((amdgpu_waves_per_eu((kivi_waves_per_simd<BITS, VB, NVS>())))) voi
         if (KVQ_TAKE_AHEAD) t_next = take();
         // keep every LDS read of the iteration ahead of the arithmetic
         __builtin_amdgcn_sched_barrier(0);
-        scores(K, low ? 0.0f : W.m_ref, sc);
+        scores(K, m_part_of(W.m_ref), sc);
         group_values<VB, NVS>(V, W, bp_prev, vsh, vm0, vm1, magic, magic32);
         group_probs<BITS, true, NVS>(W, sc, K.vs, K.vz, bp_prev);
         ++i;
@@ -1273,7 +1296,7 @@ __attribute__((amdgpu_waves_per_eu((kivi_waves_per_simd<BITS, VB, NVS>())))) voi
         load_k<BITS, VB, NVS>(ring_w + (i % kDepth) * S::kBytes, r, u, low, K, !GRP);
         // keep every LDS read of the iteration ahead of the arithmetic
         __builtin_amdgcn_sched_barrier(0);
-        scores(K, low ? 0.0f : W.m_ref, sc);
+        scores(K, m_part_of(W.m_ref), sc);
         group_values<VB, NVS>(V, W, bp_prev, vsh, vm0, vm1, magic, magic32);
         group_probs<BITS, true, NVS>(W, sc, K.vs, K.vz, bp_prev);
       }
