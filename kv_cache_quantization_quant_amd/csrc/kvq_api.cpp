@@ -38,9 +38,12 @@ constexpr int64_t kMaxTargetWorkgroups = 4096;
 // Time of one FP16 window tile in grouped-region tiles: the last main split
 // of each (b, h) runs the window too and gets that much less of the grouped
 // region (the wavefronts of a split share its tiles as they go, so the
-// window's cost spreads over all of them).
+// window's cost spreads over all of them). A window tile's wavefront waits on
+// several dependent memory round trips while the others stream: in a traced
+// 32K decode the last split still ended about 2.4 µs after the first at 4,
+// and 8 measured faster than 4, 12 and 16.
 #ifndef KVQ_WINDOW_TILE_COST
-#define KVQ_WINDOW_TILE_COST 4
+#define KVQ_WINDOW_TILE_COST 8
 #endif
 constexpr int64_t kFallbackWorkgroups = 2048;
 constexpr int64_t kMinTilesPerSplit = 4;   // one tile per wavefront at least
