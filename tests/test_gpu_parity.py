@@ -92,6 +92,36 @@ def test_kivi_prefill_and_decode(kq, B, H, Hq, S, bits, R, C):
     assert err <= ATOL
 
 
+@pytest.mark.parametrize("k_scale,k_offset", [(30.0, 0.0), (200.0, 0.0), (2.0, 1000.0)])
+def test_kivi_wide_key_ranges(kq, k_scale, k_offset):
+    """Keys far wider than the synthetic ones (up to about 14500 in magnitude)
+    and keys with a common per-channel offset: the score operands q·s and the
+    z-term enter the matrix cores as fp16 high/low pairs (22 significant bits,
+    the z-term scaled by 2^-8 into fp16's range), and the output must stay
+    within the bound of the oracle. (Offsets of thousands put every score
+    thousands of log2 units from zero, where fp32 scores themselves resolve
+    only about 1e-3; the bound then no longer holds for any fp32 kernel.)"""
+    B, H, Hq, S, bits, R, C = 2, 2, 16, 1100, 2, 128, 1200
+    _say(f"[kivi wide keys] scale={k_scale} offset={k_offset}")
+    k, v = _kv(B, H, S)
+    k = (k.float() * k_scale + k_offset).clamp(-65504.0, 65504.0).half()
+    dc = kq.DeviceCache(kq.make_config("kivi", bits=bits, residual_length=R, batch=B,
+                                       num_kv_heads=H, capacity=C))
+    dc.prefill(k, v)
+    oc = ocache.KiviCache(B, H, D, bits, 32, R, C)
+    oc.prefill(_np(k), _np(v))
+    torch.cuda.synchronize()
+    _compare_kivi_state(dc, oc)
+    q = synth.make_q(B, Hq, D, device="cuda")
+    out = dc.decode(q)
+    torch.cuda.synchronize()
+    got = _np(out)
+    assert np.isfinite(got).all()
+    err = _att_err(got, oc.attention(_np(q)))
+    _say(f"  max abs err {err:.3e}")
+    assert err <= ATOL
+
+
 def _tie_heavy(B, H, S, bits, seed):
     """fp16 K/V whose groups and tokens put many values exactly on, or one
     fp16 step beside, the rounding ties (k + 1/2)·s of the quantizer, plus
