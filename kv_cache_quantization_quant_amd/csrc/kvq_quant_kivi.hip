@@ -38,12 +38,21 @@ __device__ __forceinline__ float f4c(float4 v, int c) {
   return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
 }
 
-// ---- fast exact quotient. The code is rint(RN((x − min) / s)). With r within
-// about one ulp of 1/s, p = RN((x − min)·r) lies within 1.5·2⁻²³·Q of the exact
-// quotient Q ≤ 2^b − 1 < 16, so |p − RN(Q)| < 2⁻¹⁸. Unless p is within 2⁻¹⁶ of
-// a half-integer (a possible rounding tie), rint(p) is the code; the rare lanes
-// with such a value redo their codes with the correctly rounded division.
+// ---- fast exact quotient. The code is rint(q), q = RN(RN(x − min) / s), with
+// x and min fp16 values. The kernel takes p = RN(x·r + n) in one fma, with r
+// within about an ulp of 1/s and n = RN(−min·r), per channel (K) or token (V).
+// Against the real quotient Q = RN(x − min) / s ≤ 2^b − 1 < 16, the errors are
+// r's (2⁻²³·Q), the rounding of x − min that the fma does not make (2⁻²⁴·Q),
+// the fma's own rounding (2⁻²⁴·Q) and n's rounding (2⁻²⁴·|min·r|); with q's
+// own 2⁻²⁴·Q, |p − q| < 1.25·2⁻²²·Q + 2⁻²⁴·|min·r| < 2⁻¹⁶ + 2⁻²³·|n|. Unless
+// p lies that close to a half-integer (a possible rounding tie), rint(p) is
+// the code; the rare lanes with such a value redo those values' codes with
+// the correctly rounded division. The edge below is the threshold on
+// |p − rint(p)| for n = 0, less 2⁻²³·|n| per channel block (K) or token (V).
+// When min·r is large against the codes (a group far from zero with a tiny
+// range) every value takes the division, which is still exact.
 constexpr float kTieEdge = 0.5f - 1.0f / 65536.0f;
+__device__ __forceinline__ float tie_edge(float n_abs) { return kTieEdge - n_abs * 0x1p-23f; }
 
 // 1/s to within about an ulp (one Newton step on the hardware estimate);
 // 0 when s == 0, which makes every code 0 as the quantizer requires.
@@ -53,10 +62,10 @@ __device__ __forceinline__ float quant_recip(float s) {
   return fmaf(r, fmaf(-s, r, 1.0f), r);
 }
 
-// rint((x − mn)·r) as a float (0 ≤ code ≤ 2^b − 1); `dev` keeps the largest
-// |p − rint(p)| seen, so that dev > kTieEdge flags a possible rounding tie.
-__device__ __forceinline__ float fast_code(float x, float mn, float r, float& dev) {
-  const float p = (x - mn) * r;
+// rint(x·r + n) as a float (0 ≤ code ≤ 2^b − 1); `dev` keeps the largest
+// |p − rint(p)| seen, so that dev above the edge flags a possible rounding tie.
+__device__ __forceinline__ float fast_code(float x, float r, float n, float& dev) {
+  const float p = fmaf(x, r, n);
   const float c = rintf(p);
   dev = fmaxf(dev, fabsf(p - c));
   return c;
@@ -144,6 +153,8 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
   __shared__ __attribute__((aligned(16))) float s_k[kHeadDim];
   __shared__ __attribute__((aligned(16))) float z_k[kHeadDim];
   __shared__ __attribute__((aligned(16))) float r_k[kHeadDim];
+  __shared__ __attribute__((aligned(16))) float n_k[kHeadDim];       // RN(−min·r) per channel
+  __shared__ float edge_k[kHeadDim / 16];                            // tie edge per 16 channels
   __shared__ __attribute__((aligned(16))) uint32_t vt[NS][VTR][kRow];  // [sub][channel word][token]
 
   const int g = int(__builtin_amdgcn_workgroup_id_x());
@@ -246,16 +257,18 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
     halves_to_float(v0, vx);
     halves_to_float(v1, vx + 8);
     const float vr = quant_recip(vs);
+    const float vn = -(vmn * vr);
+    const float vedge = tie_edge(fabsf(vn));
     float dev = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) c[i] = fast_code(vx[i], vmn, vr, dev);
-    if (dev > kTieEdge) {
+    for (int i = 0; i < 16; ++i) c[i] = fast_code(vx[i], vr, vn, dev);
+    if (dev > vedge) {
       // a lane with a possible tie recomputes only the values that may sit on
       // one (the fast codes of the others are exact): a wavefront then runs
       // the division for the value slots where some lane has one
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (fabsf((vx[i] - vmn) * vr - c[i]) > kTieEdge)
+        if (fabsf(fmaf(vx[i], vr, vn) - c[i]) > vedge)
           c[i] = float(affine_code(vx[i], vmn, vs, VQMAX));
     }
     uint32_t w[VTW];
@@ -297,13 +310,23 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
     const float mn0 = float(kmn[0]), mn1 = float(kmn[1]);
     const float s0 = div_code_range<(1 << KB) - 1>(float(kmx[0]) - mn0);
     const float s1 = div_code_range<(1 << KB) - 1>(float(kmx[1]) - mn1);
+    const float r0 = quant_recip(s0), r1 = quant_recip(s1);
+    const float n0 = -(mn0 * r0), n1 = -(mn1 * r1);
+    // the largest |n| of each block of 16 channels (8 lanes of a row: xor 1,
+    // xor 2, then the half-row mirror)
+    float nm = fmaxf(fabsf(n0), fabsf(n1));
+    nm = fmaxf(nm, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(nm), 0xB1, 0xF, 0xF, false)));
+    nm = fmaxf(nm, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(nm), 0x4E, 0xF, 0xF, false)));
+    nm = fmaxf(nm, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(nm), 0x141, 0xF, 0xF, false)));
     if (u == 0) {
       const int64_t o = (blk * a.NG + gg) * kHeadDim + d0;
       *reinterpret_cast<float2*>(a.k_scale + o) = make_float2(s0, s1);
       *reinterpret_cast<float2*>(a.k_zero + o) = make_float2(mn0, mn1);
       *reinterpret_cast<float2*>(&s_k[d0]) = make_float2(s0, s1);
       *reinterpret_cast<float2*>(&z_k[d0]) = make_float2(mn0, mn1);
-      *reinterpret_cast<float2*>(&r_k[d0]) = make_float2(quant_recip(s0), quant_recip(s1));
+      *reinterpret_cast<float2*>(&r_k[d0]) = make_float2(r0, r1);
+      *reinterpret_cast<float2*>(&n_k[d0]) = make_float2(n0, n1);
+      if ((c & 7) == 0) edge_k[d0 / 16] = tie_edge(nm);
     }
   }
 
@@ -337,12 +360,13 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
   __syncthreads();
 
   // ---- K codes: token 32·sub + t, channels [16j, 16j + 16), packed along channels.
-  float4 zq[4], rq[4];
+  float4 nq[4], rq[4];
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
-    zq[q4] = *reinterpret_cast<const float4*>(&z_k[16 * j + 4 * q4]);
+    nq[q4] = *reinterpret_cast<const float4*>(&n_k[16 * j + 4 * q4]);
     rq[q4] = *reinterpret_cast<const float4*>(&r_k[16 * j + 4 * q4]);
   }
+  const float kedge = edge_k[j];
 #pragma unroll
   for (int sub = 0; sub < NS; ++sub) {
     float kx[16], c[16];
@@ -351,16 +375,16 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
     float dev = 0.0f;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      c[4 * q4 + 0] = fast_code(kx[4 * q4 + 0], zq[q4].x, rq[q4].x, dev);
-      c[4 * q4 + 1] = fast_code(kx[4 * q4 + 1], zq[q4].y, rq[q4].y, dev);
-      c[4 * q4 + 2] = fast_code(kx[4 * q4 + 2], zq[q4].z, rq[q4].z, dev);
-      c[4 * q4 + 3] = fast_code(kx[4 * q4 + 3], zq[q4].w, rq[q4].w, dev);
+      c[4 * q4 + 0] = fast_code(kx[4 * q4 + 0], rq[q4].x, nq[q4].x, dev);
+      c[4 * q4 + 1] = fast_code(kx[4 * q4 + 1], rq[q4].y, nq[q4].y, dev);
+      c[4 * q4 + 2] = fast_code(kx[4 * q4 + 2], rq[q4].z, nq[q4].z, dev);
+      c[4 * q4 + 3] = fast_code(kx[4 * q4 + 3], rq[q4].w, nq[q4].w, dev);
     }
-    if (dev > kTieEdge) {
+    if (dev > kedge) {
       // as for V: only the values that may sit on a tie
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (fabsf((kx[i] - f4c(zq[i / 4], i % 4)) * f4c(rq[i / 4], i % 4) - c[i]) > kTieEdge)
+        if (fabsf(fmaf(kx[i], f4c(rq[i / 4], i % 4), f4c(nq[i / 4], i % 4)) - c[i]) > kedge)
           c[i] = float(affine_code(kx[i], z_k[16 * j + i], s_k[16 * j + i], KQMAX));
     }
     uint32_t w[KTW];
