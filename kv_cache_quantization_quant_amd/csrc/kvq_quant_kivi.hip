@@ -86,7 +86,7 @@ __device__ __forceinline__ float div_code_range(float x) {
   const float r = fmaf(-q, float(D), x);
   const float c = fmaf(r, y, q);
   // class mask: NaN (bits 0, 1), ±inf (2, 9), ±0 (5, 6)
-  return __builtin_amdgcn_class(x, 0x267) ? q : c;
+  return __builtin_amdgcn_classf(x, 0x267) ? q : c;
 }
 
 // pack 16 codes (floats 0..2^b−1) of consecutive channels into 32-bit words,
@@ -128,9 +128,10 @@ __device__ __forceinline__ void write_new_token(const KiviQuantArgs& a, int bh, 
 //      bits) of 16 channel codes per thread into an LDS transpose, from which
 //      each thread assembles the sub-tile's V words along tokens.
 //   K (per channel over the G tokens): wavefront w takes channels [32w, 32w + 32), lane (pair c = l % 16, quarter
-//      u = l / 16) reduces rows [u·G/4, (u+1)·G/4) of channels 32w + 2c, +1,
-//      then the four quarters are combined; codes of the thread's 16 channels
-//      follow from the per-channel scale and zero.
+//      u = l / 16) reduces rows [u·G/4, (u+1)·G/4) of channels 32w + 2c, +1
+//      into LDS; wavefront 0 then combines the four quarters of every channel
+//      pair and derives the per-channel scale and zero, from which the codes
+//      of each thread's 16 channels follow.
 template <int KB, int VB, int NS>
 __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a) {
   constexpr int G = NS * kGroup;           // tokens per group
@@ -155,6 +156,7 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
   __shared__ __attribute__((aligned(16))) float r_k[kHeadDim];
   __shared__ __attribute__((aligned(16))) float n_k[kHeadDim];       // RN(−min·r) per channel
   __shared__ float edge_k[kHeadDim / 16];                            // tie edge per 16 channels
+  __shared__ __attribute__((aligned(16))) uint2 k_part[4][kHeadDim / 2];  // [quarter][pair] (max, min)
   __shared__ __attribute__((aligned(16))) uint32_t vt[NS][VTR][kRow];  // [sub][channel word][token]
 
   const int g = int(__builtin_amdgcn_workgroup_id_x());
@@ -276,11 +278,9 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
 #pragma unroll
     for (int k = 0; k < VTW; ++k) vt[sub][VTW * j + k][t] = w[k];
   }
-  __syncthreads();
-  // every load of the group has been consumed: slot 0 may take the new token
-  if (g == 0 && a.k_new != nullptr) write_new_token(a, bh, new_slot, tid);
-
-  // ---- K statistics over the G rows: wavefront w, channels 32w + 2c, +1
+  // ---- K statistics over the G rows, first half: lane (pair c = l % 16,
+  // quarter u = l / 16) of wavefront w takes the minimum and maximum of rows
+  // [u·G/4, (u+1)·G/4) of channels 32w + 2c and 32w + 2c + 1
   {
     const int wv = tid >> 6;
     const int c = tid & 15;
@@ -295,39 +295,41 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
       kmx = h2max(kmx, x);
       kmn = h2min(kmn, x);
     }
-    // combine the four quarters (lanes l ^ 16, l ^ 32)
-#pragma unroll
-    for (int step = 0; step < 2; ++step) {
-      const auto px = step == 0
-          ? __builtin_amdgcn_permlane16_swap(as_u(kmx), as_u(kmx), false, false)
-          : __builtin_amdgcn_permlane32_swap(as_u(kmx), as_u(kmx), false, false);
-      const auto pn = step == 0
-          ? __builtin_amdgcn_permlane16_swap(as_u(kmn), as_u(kmn), false, false)
-          : __builtin_amdgcn_permlane32_swap(as_u(kmn), as_u(kmn), false, false);
-      kmx = h2max(as_h2(px[0]), as_h2(px[1]));
-      kmn = h2min(as_h2(pn[0]), as_h2(pn[1]));
-    }
+    k_part[u][16 * wv + c] = make_uint2(as_u(kmx), as_u(kmn));
+  }
+  __syncthreads();
+  // every load of the group has been consumed: slot 0 may take the new token
+  if (g == 0 && a.k_new != nullptr) write_new_token(a, bh, new_slot, tid);
+
+  // ---- K statistics, second half, in wavefront 0 alone (the other three
+  // would repeat the same scalar work): lane p combines the four quarters of
+  // channels 2p and 2p + 1 and derives their scale, zero, reciprocal, −min·r
+  // and the tie edge of their block of 16 channels
+  if (tid < 64) {
+    const int p = tid;
+    const int d0 = 2 * p;
+    const uint2 q0 = k_part[0][p], q1 = k_part[1][p], q2 = k_part[2][p], q3 = k_part[3][p];
+    const h2v kmx = h2max(h2max(as_h2(q0.x), as_h2(q1.x)), h2max(as_h2(q2.x), as_h2(q3.x)));
+    const h2v kmn = h2min(h2min(as_h2(q0.y), as_h2(q1.y)), h2min(as_h2(q2.y), as_h2(q3.y)));
     const float mn0 = float(kmn[0]), mn1 = float(kmn[1]);
     const float s0 = div_code_range<(1 << KB) - 1>(float(kmx[0]) - mn0);
     const float s1 = div_code_range<(1 << KB) - 1>(float(kmx[1]) - mn1);
     const float r0 = quant_recip(s0), r1 = quant_recip(s1);
     const float n0 = -(mn0 * r0), n1 = -(mn1 * r1);
-    // the largest |n| of each block of 16 channels (8 lanes of a row: xor 1,
-    // xor 2, then the half-row mirror)
+    // the largest |n| of each block of 16 channels (8 lanes: xor 1, xor 2,
+    // then the half-row mirror)
     float nm = fmaxf(fabsf(n0), fabsf(n1));
     nm = fmaxf(nm, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(nm), 0xB1, 0xF, 0xF, false)));
     nm = fmaxf(nm, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(nm), 0x4E, 0xF, 0xF, false)));
     nm = fmaxf(nm, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(nm), 0x141, 0xF, 0xF, false)));
-    if (u == 0) {
-      const int64_t o = (blk * a.NG + gg) * kHeadDim + d0;
-      *reinterpret_cast<float2*>(a.k_scale + o) = make_float2(s0, s1);
-      *reinterpret_cast<float2*>(a.k_zero + o) = make_float2(mn0, mn1);
-      *reinterpret_cast<float2*>(&s_k[d0]) = make_float2(s0, s1);
-      *reinterpret_cast<float2*>(&z_k[d0]) = make_float2(mn0, mn1);
-      *reinterpret_cast<float2*>(&r_k[d0]) = make_float2(r0, r1);
-      *reinterpret_cast<float2*>(&n_k[d0]) = make_float2(n0, n1);
-      if ((c & 7) == 0) edge_k[d0 / 16] = tie_edge(nm);
-    }
+    const int64_t o = (blk * a.NG + gg) * kHeadDim + d0;
+    *reinterpret_cast<float2*>(a.k_scale + o) = make_float2(s0, s1);
+    *reinterpret_cast<float2*>(a.k_zero + o) = make_float2(mn0, mn1);
+    *reinterpret_cast<float2*>(&s_k[d0]) = make_float2(s0, s1);
+    *reinterpret_cast<float2*>(&z_k[d0]) = make_float2(mn0, mn1);
+    *reinterpret_cast<float2*>(&r_k[d0]) = make_float2(r0, r1);
+    *reinterpret_cast<float2*>(&n_k[d0]) = make_float2(n0, n1);
+    if ((p & 7) == 0) edge_k[p >> 3] = tie_edge(nm);
   }
 
   // ---- V words: per (tile, channel), the tile's 32 token codes packed along
@@ -351,7 +353,7 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * q4 + e;
-          word |= ((xs[e] >> sh) & ((1u << VB) - 1)) << (VB * (i / 2) + 16 * (i % 2));
+          word |= __builtin_amdgcn_ubfe(xs[e], sh, VB) << (VB * (i / 2) + 16 * (i % 2));
         }
       }
       vdst[idx] = word;
