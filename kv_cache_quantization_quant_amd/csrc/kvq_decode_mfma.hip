@@ -466,14 +466,16 @@ __device__ __forceinline__ void group_scores(const KLoad<BITS, NVS>& K, bool low
   uint32_t m0[2 * BITS], m1[2 * BITS];
   k_masks<BITS>(K.w0, m0);
   k_masks<BITS>(K.w1, m1);
-  // ---- z-term of this lane's 16 channels, summed over the four lane groups u
-  // (four independent partial sums: a 16-long dependent chain would stall)
-  float zp[4];
+  // ---- z-term of this lane's 16 channels less its share of the reference
+  // maximum, as one chain of fused multiply-adds
+  float zacc = -m_part;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const float4 z = K.kz[j];
-    zp[j] = fmaf(q16[4 * j + 3], z.w, fmaf(q16[4 * j + 2], z.z,
-                 fmaf(q16[4 * j + 1], z.y, q16[4 * j] * z.x)));
+    zacc = fmaf(q16[4 * j], z.x, zacc);
+    zacc = fmaf(q16[4 * j + 1], z.y, zacc);
+    zacc = fmaf(q16[4 * j + 2], z.z, zacc);
+    zacc = fmaf(q16[4 * j + 3], z.w, zacc);
   }
   // The z-term summed over the four lane groups by the matrix cores (one
   // 16×16×16 product instead of two lane swaps and the accumulator fills):
@@ -485,7 +487,7 @@ __device__ __forceinline__ void group_scores(const KLoad<BITS, NVS>& K, bool low
   // exactly by A) keeps partials up to 2^24 inside fp16's range; the pair
   // carries 22 significant bits, and fp16's subnormal step adds at most
   // 2^-16 per partial (2^-13 over the 8 partials of a score, in log2 units).
-  const float zs = (((zp[0] + zp[1]) + (zp[2] + zp[3])) - m_part) * 0.00390625f;
+  const float zs = zacc * 0.00390625f;
   const float zr = zs - __uint_as_float(__float_as_uint(zs) & 0xFFFFE000u);
   const u32x2 bz = u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(zs, zr)), 0u};
   const u32x2 a256 = u32x2{0x5C005C00u, 0x5C005C00u};
@@ -641,18 +643,22 @@ __device__ __forceinline__ void group_values(const VLoad& V, WaveAccT<NVS>& W,
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
     uint32_t d[4];
+    // both words shifted at once: the bits of the second word that enter the
+    // first (at 20 and above for shifts up to 12) lie outside the masks
+    const uint64_t pair = (uint64_t(V.w[n][1]) << 32) | V.w[n][0];
     if (BITS == 2) {
-      const uint32_t v0 = V.w[n][0] >> vsh, v1 = V.w[n][1] >> vsh;
+      const uint64_t x = pair >> vsh;
+      const uint32_t v0 = uint32_t(x), v1 = uint32_t(x >> 32);
       d[0] = bfi(vm0, v0, magic);
       d[1] = bfi(vm1, v0, magic32);
       d[2] = bfi(vm0, v1, magic);
       d[3] = bfi(vm1, v1, magic32);
     } else {
-      const uint32_t v0 = V.w[n][0], v1 = V.w[n][1];
-      d[0] = bfi(vm0, v0 >> vsh, magic);
-      d[1] = bfi(vm0, v0 >> (vsh + 4), magic);
-      d[2] = bfi(vm0, v1 >> vsh, magic);
-      d[3] = bfi(vm0, v1 >> (vsh + 4), magic);
+      const uint64_t x = pair >> vsh, y = pair >> (vsh + 4);
+      d[0] = bfi(vm0, uint32_t(x), magic);
+      d[1] = bfi(vm0, uint32_t(y), magic);
+      d[2] = bfi(vm0, uint32_t(x >> 32), magic);
+      d[3] = bfi(vm0, uint32_t(y >> 32), magic);
     }
     // channels 16n..16n+15 lie in run n·NVS/8
     W.cv[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{d[0], d[1], d[2], d[3]}),
@@ -1195,10 +1201,8 @@ __attribute__((amdgpu_waves_per_eu((kivi_waves_per_simd<BITS, VB, NVS>())))) voi
     // −m_ref enters each head's scores once: from every lane of part 0 when
     // the z-term is broadcast from one lane-group sum (G > 32), from lane
     // group 0 of part 0 when the matrix cores add the lane groups' partials
-    auto m_part_of = [&](float m_ref) -> float {
-      if constexpr (GRP) return low ? 0.0f : m_ref;
-      return (low || u != 0) ? 0.0f : m_ref;
-    };
+    const bool m_lane = GRP ? !low : (!low && u == 0);
+    auto m_part_of = [&](float m_ref) -> float { return m_lane ? m_ref : 0.0f; };
     auto scores = [&](const KLoad<BITS, NVS>& K, float m_part, float (&sc_out)[4]) {
       if constexpr (GRP) tile_scores<BITS, NVS>(K, low, Qg, m_part, sc_out);
       else group_scores<BITS, NVS>(K, low, q16, m_part, sc_out);
