@@ -939,7 +939,11 @@ __device__ __forceinline__ GroupSrc group_src(const DecodeArgs& a, int bh, int b
   using S = Stage<BITS, VB, NVS>;
   int64_t blk = bh;
   if constexpr (PAGED) {
-    const int e = a.block_table[int64_t(b) * a.max_pages + (g >> a.page_tile_shift)];
+    // a scalar load (the table is read-only for the launch): a vector load's
+    // wait would also drain the copies in flight, every tile
+    typedef __attribute__((address_space(4))) const int32_t ConstI32;
+    const ConstI32* table = (const ConstI32*)(a.block_table);
+    const int e = table[int64_t(b) * a.max_pages + (g >> a.page_tile_shift)];
     blk = int64_t(min(max(e, 0), a.num_pages - 1)) * a.H + h;
     g &= (int64_t(1) << a.page_tile_shift) - 1;
   }

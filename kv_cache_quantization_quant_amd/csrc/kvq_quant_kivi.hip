@@ -183,7 +183,9 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
   if (a.paged) {
     const int b = bh / a.H;
     const int h = bh - b * a.H;
-    const int e = a.block_table[int64_t(b) * a.max_pages + (gg >> a.page_group_shift)];
+    typedef __attribute__((address_space(4))) const int32_t ConstI32;   // scalar load
+    const ConstI32* table = (const ConstI32*)(a.block_table);
+    const int e = table[int64_t(b) * a.max_pages + (gg >> a.page_group_shift)];
     blk = int64_t(min(max(e, 0), a.num_pages - 1)) * a.H + h;
     gg &= (int64_t(1) << a.page_group_shift) - 1;
   }
