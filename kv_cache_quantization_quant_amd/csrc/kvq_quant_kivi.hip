@@ -34,25 +34,6 @@ __device__ __forceinline__ uint32_t affine_code(float x, float mn, float s, floa
   return static_cast<uint32_t>(r);
 }
 
-// Stores of the cache's codes, scales and zero-points, non-temporal: the
-// decode reads them much later, so they need not stay in the caches (and a
-// prefill leaves no dirty lines behind for the next kernel to write back).
-// The empty asm keeps the optimizer from merging a store with its copy on
-// another path, which drops the non-temporal mark.
-template <typename T>
-__device__ __forceinline__ void out_store(T* p, T x) {
-  asm volatile("" ::: "memory");
-  __builtin_nontemporal_store(x, p);
-}
-template <typename T>
-__device__ __forceinline__ void out_store2(T* p, T x0, T x1) {
-  static_assert(sizeof(T) == 4, "pairs of 32-bit words");
-  const uint64_t v = uint64_t(__builtin_bit_cast(uint32_t, x0)) |
-                     (uint64_t(__builtin_bit_cast(uint32_t, x1)) << 32);
-  asm volatile("" ::: "memory");
-  __builtin_nontemporal_store(v, reinterpret_cast<uint64_t*>(p));
-}
-
 __device__ __forceinline__ float f4c(float4 v, int c) {
   return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
 }
@@ -271,8 +252,8 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
     // one thread per token (nvs = 1) or per run of 32 channels (nvs = 4)
     if (a.nvs == 1 ? j == 0 : (j & 1) == 0) {
       const int64_t o = (blk * CT + gg * G + tr) * a.nvs + (a.nvs == 1 ? 0 : j / 2);
-      out_store(a.v_scale + o, vs);
-      out_store(a.v_zero + o, vmn);
+      store_nt(a.v_scale + o, vs);
+      store_nt(a.v_zero + o, vmn);
     }
 
     // ---- V codes of the thread's 16 channels → the LDS transpose
@@ -344,8 +325,8 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
     nm = fmaxf(nm, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(nm), 0x4E, 0xF, 0xF, false)));
     nm = fmaxf(nm, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(nm), 0x141, 0xF, 0xF, false)));
     const int64_t o = (blk * a.NG + gg) * kHeadDim + d0;
-    out_store2(a.k_scale + o, s0, s1);
-    out_store2(a.k_zero + o, mn0, mn1);
+    store_nt2(a.k_scale + o, __float_as_uint(s0), __float_as_uint(s1));
+    store_nt2(a.k_zero + o, __float_as_uint(mn0), __float_as_uint(mn1));
     *reinterpret_cast<float2*>(&s_k[d0]) = make_float2(s0, s1);
     *reinterpret_cast<float2*>(&z_k[d0]) = make_float2(mn0, mn1);
     *reinterpret_cast<float2*>(&r_k[d0]) = make_float2(r0, r1);
@@ -377,7 +358,7 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
           word |= __builtin_amdgcn_ubfe(xs[e], sh, VB) << (VB * (i / 2) + 16 * (i % 2));
         }
       }
-      out_store(vdst + idx, word);
+      store_nt(vdst + idx, word);
     }
   }
   __syncthreads();
@@ -414,9 +395,9 @@ __global__ __launch_bounds__(kThreads) void kivi_quantize_kernel(KiviQuantArgs a
     pack16<KB>(c, w);
     uint32_t* kdst = a.k_codes + (blk * CT + gg * G + sub * kGroup + t) * KW;
     if (KB == 2) {
-      out_store(kdst + j, w[0]);
+      store_nt(kdst + j, w[0]);
     } else {
-      out_store2(kdst + 2 * j, w[0], w[KTW - 1]);
+      store_nt2(kdst + 2 * j, w[0], w[KTW - 1]);
     }
   }
 }
