@@ -714,9 +714,13 @@ def test_gqa70b_32k_stream_sampled(kq):
 
 
 def test_mha_large_batch_4bit_sampled(kq):
+    """B = 64, 32 MHA heads, S = 8192, KIVI 4-bit: 2048 (b, h) blocks, more
+    than the device holds at once (four-wavefront workgroups, one split per
+    row). One block of every sequence, its head stepping through all 32, is
+    checked bit-exact and against the oracle's attention."""
     cfg = synth.CONFIGS["mha_large_batch_4bit"]
     B, H, Hq, S = cfg["batch"], cfg["num_kv_heads"], cfg["num_q_heads"], cfg["seq_len"]
-    blocks = [(0, 0), (31, 17), (63, 31)]
+    blocks = [(b, (7 * b + 3) % H) for b in range(B)] + [(B - 1, H - 1)]
     _say(f"[mha_large_batch_4bit] B={B} H={H} S={S}")
     k, v = _kv(B, H, S)
     dc = kq.DeviceCache(kq.make_config("kivi", bits=4, batch=B, num_kv_heads=H, capacity=S))
@@ -768,7 +772,7 @@ def test_gqa_128k_fp8_sampled(kq, kv_128k):
     out = _np(dc.decode(q))
     from oracle import attention
     worst = 0.0
-    for b, h in [(0, 0), (1, 4), (3, 7)]:
+    for b, h in [(0, 0), (0, 7), (1, 4), (2, 2), (3, 5), (3, 7)]:
         kc = ofp8.quantize(_np(k[b, h]), sk)
         vc = ofp8.quantize(_np(v[b, h]), sv)
         assert np.array_equal(_np(dc.view("k_codes")[b, h, :S]), kc)
