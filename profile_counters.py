@@ -11,7 +11,7 @@ after `--`), chosen by name on the command line (default: all):
   sq       three --pmc passes of SQ_* / GRBM_* counters over the split kernel
            (instructions per 32-token group, VALU and MFMA busy, LDS bank
            conflicts, shader clock);
-  gaps     --kernel-trace of the short run the round-end benchmark makes
+  gaps     --kernel-trace of a short benchmark run
            (--steps 20 --warmup 5): kernel durations and the idle gaps
            between the kernels of its timed steps;
   quant    the prefill quantize kernel of the same short bench (its 32K
@@ -223,7 +223,7 @@ def gaps_pass():
     roof = [i for i in splits if "copy_tokens_kernel" in names[i - 1]][-20:]
     # the value pass: the 20 splits before the roofline pass's first step
     value = [i for i in splits if i < roof[0] - 1][-20:]
-    lines = ["# rocprofv3 kernel trace of the round-end benchmark command: per timed step, "
+    lines = ["# rocprofv3 kernel trace of a short benchmark run: per timed step, "
              "the append's kernels (none in a fused step without a flush), the decode's "
              "split and merge, and the idle time on the GPU between them",
              f"# command: {rel(c)}"]
