@@ -25,9 +25,12 @@ import gc
 import hashlib
 import json
 import os
+import re
+import shutil
 import statistics
 import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -260,6 +263,17 @@ def run_main(torch, kq, synth, args):
         cold = time_launches(torch, lambda: dc.decode(qs[-1], out=out, workspace=ws), 20, scrub)
         cold_med = statistics.median(cold)
 
+    # the shader clock while the layers' decodes run back to back (the chip's
+    # power limit sets it under this load)
+    sclk = None
+    if not args.no_clock:
+        li = [0]
+
+        def one():
+            layers[li[0] % LAYERS].decode(qs[-1], out=out, workspace=ws)
+            li[0] += 1
+        sclk = sustained_sclk_mhz(torch, one)
+
     windows = [nr for _, _, nr in state]
     res = {
         "B": B, "Hq": Hq, "H": H, "S": S, "bits": bits,
@@ -281,12 +295,47 @@ def run_main(torch, kq, synth, args):
         "append_us_p50": statistics.median(plain_us) if plain_us else None,
         "flush_append_us_mean": statistics.mean(flush_us) if flush_us else None,
         "warmup_decodes": n_warm,
+        "sclk_mhz_back_to_back_decodes": sclk,
         "prefill_quantize_us": pre_us,
         "prefill_quantize_gbs": q_bytes / (pre_us * 1e-6) / 1e9,
         "layers": LAYERS,
         "final_state": [[c.n_quant, c.n_resid] for c in layers],
     }
     return res
+
+
+def sustained_sclk_mhz(torch, fn, secs=1.5):
+    """Shader clock (MHz) sampled with `rocm-smi --showclocks` from another
+    thread while `fn` runs back to back for `secs`; the first and last
+    samples, which may fall outside the load, are dropped. None where
+    rocm-smi is missing or fails."""
+    exe = shutil.which("rocm-smi")
+    if exe is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                r = subprocess.run([exe, "--showclocks", "--json"], capture_output=True,
+                                   text=True, timeout=10)
+            except (OSError, subprocess.SubprocessError):
+                return
+            m = re.search(r'sclk clock speed:": "\((\d+)Mhz\)', r.stdout)
+            if m:
+                samples.append(int(m.group(1)))
+            stop.wait(0.2)
+
+    t = threading.Thread(target=sampler, daemon=True)
+    t.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < secs:
+        for _ in range(32):
+            fn()
+        torch.cuda.synchronize()
+    stop.set()
+    t.join(timeout=15)
+    return samples[1:-1] or None
 
 
 def copy_peak_gbs(torch, mib=1024, iters=10):
@@ -558,6 +607,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip sampling the shader clock (rocm-smi) during back-to-back decodes")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the scrubbed single-launch decode timing (profiling runs)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,

@@ -45,11 +45,11 @@ PROF = os.path.join(OUT, "profiles")          # copied into profiles/ afterwards
 # average decode duration compares with the bench line); the counter passes,
 # which serialize every dispatch they count, use a short run
 BENCH_STATS = ["python3", os.path.join(ROOT, "bench.py"), "--steps", "256", "--warmup", "16",
-               "--no-cpu-baseline", "--no-extra", "--no-cold"]
+               "--no-cpu-baseline", "--no-extra", "--no-cold", "--no-clock"]
 BENCH = ["python3", os.path.join(ROOT, "bench.py"), "--steps", "16", "--warmup", "4",
-         "--no-cpu-baseline", "--no-extra", "--no-cold"]
+         "--no-cpu-baseline", "--no-extra", "--no-cold", "--no-clock"]
 BENCH_DRIVER = ["python3", os.path.join(ROOT, "bench.py"), "--gpus", "1", "--steps", "20",
-                "--warmup", "5", "--no-cpu-baseline", "--no-extra"]
+                "--warmup", "5", "--no-cpu-baseline", "--no-extra", "--no-clock"]
 COPY_MIB = 1024
 # SQ / GRBM counter passes (at most 8 SQ and 2 GRBM counters per pass)
 SQ_PASSES = [
