@@ -293,7 +293,9 @@ def run_main(torch, kq, synth, args):
         "cold_decode_us_p50": cold_med,
         "cold_decode_gbs": None if cold_med is None else bytes_now / (cold_med * 1e-6) / 1e9,
         "append_us_p50": statistics.median(plain_us) if plain_us else None,
-        "flush_append_us_mean": statistics.mean(flush_us) if flush_us else None,
+        # median: the first flushing append is the flush kernel's first launch
+        # in this process
+        "flush_append_us_p50": statistics.median(flush_us) if flush_us else None,
         "warmup_decodes": n_warm,
         "sclk_mhz_back_to_back_decodes": sclk,
         "prefill_quantize_us": pre_us,
