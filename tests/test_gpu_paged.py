@@ -71,6 +71,7 @@ def _err(out, ref):
     (256, 128, 2, 4, 0, 128, 2, 8, [1000, 129, 640], 20),
     (64, 32, 2, 0, 32, 128, 2, 16, [257, 700, 96], 30),     # V scales per 32 channels
     (512, 32, 2, 0, 0, 128, 4, 32, [4096, 1000, 3000, 77, 2048, 333], 5),   # many splits
+    (64, 32, 2, 0, 0, 128, 1, 2, [1 + (37 * i) % 300 for i in range(128)], 3),  # the largest batch
 ])
 def test_paged_prefill_append_decode(kq, P, G, bits, vbits, gc, R, H, Hq, lens, steps):
     B = len(lens)

@@ -58,6 +58,7 @@ def _compare(dc, oc):
     (128, 2, 4, 0, 128, 2, 8, [1000, 129, 640], 20),
     (32, 2, 0, 0, 128, 4, 32, [4096, 1000, 3000, 77, 2048, 333], 5),   # many splits
     (128, 2, 0, 0, 128, 4, 32, [4096, 1000, 3000, 77, 2048, 333], 5),  # whole K groups per split
+    (32, 2, 0, 0, 128, 1, 2, [1 + (37 * i) % 300 for i in range(128)], 3),  # the largest batch
 ])
 def test_ragged_prefill_append_decode(kq, G, bits, vbits, gc, R, H, Hq, lens, steps):
     B = len(lens)
