@@ -219,6 +219,47 @@ def test_kivi_streaming(kq, bits, R):
     assert worst <= ATOL
 
 
+@pytest.mark.parametrize("fmt,bits,R", [("kivi", 2, 128), ("kivi", 4, 64), ("kivi", 2, 0),
+                                         ("fp16", None, None)])
+def test_cache_built_by_appends_alone(kq, fmt, bits, R):
+    """No prefill: every token arrives by an append into an empty cache, from
+    a one-token cache through the first lazy flushes (KIVI) or across tile
+    edges (FP16). Fill state, stored values and attention match the oracle."""
+    B, H, Hq, steps = 2, 2, 8, 170
+    C = steps
+    _say(f"[appends alone] fmt={fmt} bits={bits} R={R}")
+    k, v = _kv(B, H, C)
+    if fmt == "kivi":
+        dc = kq.DeviceCache(kq.make_config("kivi", bits=bits, residual_length=R, batch=B,
+                                           num_kv_heads=H, capacity=C))
+        oc = ocache.KiviCache(B, H, D, bits, 32, R, C)
+    else:
+        dc = kq.DeviceCache(kq.make_config("fp16", batch=B, num_kv_heads=H, capacity=C))
+        oc = ocache.Fp16Cache(B, H, D, C)
+    ws = dc.make_workspace(Hq)
+    kn, vn = _np(k), _np(v)
+    check_at = {1, 2, 31, 32, 33, 64, 65, 128, 129, 130, 161, steps}
+    worst = 0.0
+    for i in range(1, steps + 1):
+        dc.append(k[:, :, i - 1].contiguous(), v[:, :, i - 1].contiguous())
+        oc.append(kn[:, :, i - 1], vn[:, :, i - 1])
+        if fmt == "kivi":
+            assert (dc.n_quant, dc.n_resid) == (oc.n_quant, oc.n_resid), i
+        if i in check_at:
+            q = synth.make_q(B, Hq, D, step=i, device="cuda")
+            worst = max(worst, _att_err(_np(dc.decode(q, workspace=ws)), oc.attention(_np(q))))
+    torch.cuda.synchronize()
+    if fmt == "kivi":
+        _compare_kivi_state(dc, oc)
+        assert oc.flush_steps and dc.n_quant > 0
+        _say(f"  flushes at {oc.flush_steps}")
+    else:
+        assert np.array_equal(_np(dc.view("k_codes")), oc.k)
+        assert np.array_equal(_np(dc.view("v_codes")), oc.v)
+    _say(f"  worst max abs err {worst:.3e}")
+    assert worst <= ATOL
+
+
 @pytest.mark.parametrize("G,bits,R,B,H,Hq,S0,steps", [
     (64, 2, 64, 2, 2, 8, 300, 140),       # flushes of one 64-token group
     (128, 4, 128, 1, 3, 6, 500, 140),     # GQA 2, 4-bit
