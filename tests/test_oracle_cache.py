@@ -292,3 +292,36 @@ def test_v_subgroup_cache_layout_and_reduction():
     assert np.array_equal(Kh, Kp)
     x = v[:, :, :160].astype(np.float32)
     assert np.abs(Vh[:, :, :160] - x).max() <= np.abs(Vp[:, :, :160] - x).max()
+
+
+@pytest.mark.parametrize("G,R,T,state", [
+    (32, 128, 256, (128, 128)),   # flush at append 129
+    (32, 64, 192, (128, 64)),     # flushes at 65 and 129
+    (64, 128, 384, (256, 128)),   # flushes of two 64-token groups
+    (32, 0, 97, (96, 1)),         # R = 0: the window is the open group
+])
+def test_appends_alone_equal_the_prefill(G, R, T, state):
+    """A cache that receives every token by an append into an empty cache
+    ends, once its fill state is the one a prefill of the same T tokens gives,
+    with the same stored arrays as that prefill: every flush quantizes whole
+    groups at the positions the prefill puts them, and the window holds the
+    newest tokens."""
+    B, H, D = 2, 2, 128
+    k = synth.make_k(B, H, 0, T, D).numpy()
+    v = synth.make_v(B, H, 0, T, D).numpy()
+    pre = cache.KiviCache(B, H, D, 2, G, R, T)
+    pre.prefill(k, v)
+    app = cache.KiviCache(B, H, D, 2, G, R, T)
+    for t in range(T):
+        app.append(k[:, :, t], v[:, :, t])
+    assert (pre.n_quant, pre.n_resid) == (app.n_quant, app.n_resid) == state
+    # a flush empties a full window: R tokens, or the open group when R = 0
+    w = R or G
+    assert app.flush_steps == [1 + w * (i + 1) for i in range(T // w - (T % w == 0))]
+    for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero"):
+        assert np.array_equal(getattr(pre, name), getattr(app, name)), name
+    n = state[1]
+    assert np.array_equal(pre.k_resid[:, :, :n], app.k_resid[:, :, :n])
+    assert np.array_equal(pre.v_resid[:, :, :n], app.v_resid[:, :, :n])
+    q = synth.make_q(B, 8, D).numpy()
+    assert np.array_equal(pre.attention(q), app.attention(q))
